@@ -1,0 +1,372 @@
+"""CPU oracle for TurboQuant KV-cache compression and compressed decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only the tests, the smoke check of the build entry point and the CPU-baseline
+leg of the benchmark may use it.  It shares no code with the HIP library.
+
+Everything here is plain and slow on purpose: fp64 throughout, a dense rotation
+matrix, brute-force nearest-codeword search, a bit loop for packing and a full
+(two-pass) softmax.  Each function names the passage of the source pages it
+follows.  Page keys used in citations:
+
+  [inferrs]  "inferrs & TurboQuant：本地 LLM 推理的内存革命"
+  [tq-80]    "TurboQuant：让大模型本地推理内存占用降低80%的KV缓存压缩技术"
+  [tq-plus]  "TurboQuant+：跨平台KV缓存压缩技术助力本地LLM高效推理"
+  [tq-fwht]  "TurboQuant：用Rust核心与FWHT预处理实现LLM推理的4-bit KV缓存量化"
+  [google]   "Google 最新極限壓縮算法，砸碎大模型本地部署的內存墻，8 倍提升！"
+
+Readings of points the pages leave open (each is listed in the design notes):
+  * rotation R = H diag(s) / sqrt(d), H the Sylvester-ordered Hadamard matrix;
+  * codebook = Lloyd-Max quantizer of the density (1 - x^2)^((d-3)/2) on [-1, 1]
+    (the marginal of one coordinate of a uniformly random unit vector, which the
+    [tq-80] page describes as a Beta law), centroids ascending;
+  * code index = number of boundaries strictly below u (ties go to the lower
+    index), boundaries are the midpoints of adjacent centroids;
+  * u is normalised by the full-precision norm; the stored norm is its fp16
+    round-to-nearest-even value; a zero vector gives u = 0;
+  * packing is an LSB-first bit stream (see `code_bit_positions`);
+  * Sparse V keeps row t for head h iff the final normalised softmax weight
+    p_{h,t} >= tau, without renormalisation.
+
+Parity status: every function here is pinned by a test in tests/ against
+closed forms, a library routine or brute force, except the end-to-end outputs
+on the synthetic workloads, which no page prints (parity unpinned beyond the
+oracle for those values).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Codebook: Lloyd iteration on a known density  ([tq-80] §核心创新, §tqai项目)
+# ---------------------------------------------------------------------------
+
+_GL_NODES, _GL_WEIGHTS = np.polynomial.legendre.leggauss(20)
+
+
+def rotated_coordinate_density(d: int):
+    """Unnormalised density of one coordinate of a random unit vector in R^d.
+
+    [tq-80] §核心创新 states that after the random orthogonal rotation the
+    coordinates follow a concentrated Beta law.  For a uniform point on the
+    sphere S^{d-1} one coordinate x has density proportional to
+    (1 - x^2)^((d-3)/2) on [-1, 1] (that is, (x+1)/2 ~ Beta((d-1)/2, (d-1)/2)).
+    """
+    alpha = (d - 3) / 2.0
+
+    def f(x):
+        x = np.asarray(x, dtype=np.float64)
+        return np.power(np.clip(1.0 - x * x, 0.0, None), alpha)
+
+    return f
+
+
+def cell_integrals(f, edges, max_piece=0.01):
+    """Mass and first moment of density f over consecutive cells [edges[k], edges[k+1]].
+
+    Plain composite Gauss-Legendre quadrature: every cell is split into pieces of
+    width at most `max_piece`, 20 nodes per piece.
+    """
+    edges = np.asarray(edges, dtype=np.float64)
+    a, b = edges[:-1], edges[1:]
+    width = b - a
+    npieces = np.maximum(1, np.ceil(width / max_piece).astype(np.int64))
+    cell_of_piece = np.repeat(np.arange(len(a)), npieces)
+    first_piece = np.concatenate(([0], np.cumsum(npieces)[:-1]))
+    j = np.arange(cell_of_piece.size) - np.repeat(first_piece, npieces)
+    pw = (width / npieces)[cell_of_piece]
+    pa = a[cell_of_piece] + j * pw
+    mid = pa + 0.5 * pw
+    half = 0.5 * pw
+    x = mid[:, None] + half[:, None] * _GL_NODES[None, :]
+    fx = f(x)
+    w = half[:, None] * _GL_WEIGHTS[None, :]
+    mass_p = (fx * w).sum(axis=1)
+    mom_p = (x * fx * w).sum(axis=1)
+    mass = np.add.reduceat(mass_p, first_piece)
+    mom = np.add.reduceat(mom_p, first_piece)
+    return mass, mom
+
+
+def lloyd_max(f, lo: float, hi: float, init, tol: float, max_iter: int = 1_000_000,
+              max_piece: float = 0.01):
+    """Lloyd's algorithm for the scalar quantizer minimising E (x - Q(x))^2 under f.
+
+    Alternates the two Lloyd-Max optimality conditions:
+      boundaries t_j = (c_j + c_{j+1}) / 2          (nearest-neighbour cells)
+      centroids  c_k = E[x | t_{k-1} < x < t_k]     (centroid condition)
+    until the largest centroid move is below `tol`.
+    Returns (centroids, boundaries, iterations).
+    """
+    c = np.array(init, dtype=np.float64)
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = np.concatenate(([lo], t, [hi]))
+        mass, mom = cell_integrals(f, edges, max_piece)
+        c_new = mom / mass
+        step = float(np.max(np.abs(c_new - c)))
+        c = c_new
+        if step < tol:
+            break
+    return c, 0.5 * (c[:-1] + c[1:]), it
+
+
+def gaussian_quantile_init(d: int, levels: int):
+    """Initial centroids: quantiles of N(0, 1/d) at (k + 1/2) / L."""
+    from scipy.special import ndtri
+
+    k = np.arange(levels, dtype=np.float64)
+    return ndtri((k + 0.5) / levels) / math.sqrt(d)
+
+
+def make_codebook(d: int, bits: int, init: str = "gauss"):
+    """Data-independent Lloyd-Max codebook for b-bit codes at head dim d.
+
+    [tq-80] §核心创新 and §tqai项目: the codebook is derived from the known
+    distribution of the rotated coordinates, precomputed, and shared by every
+    model.  The result is symmetrised (c_k = -c_{L-1-k}), which is exact for the
+    even density and makes the middle boundary exactly 0.
+    """
+    levels = 1 << bits
+    f = rotated_coordinate_density(d)
+    if init == "gauss":
+        c0 = gaussian_quantile_init(d, levels)
+    elif init == "uniform":
+        c0 = (np.arange(levels) + 0.5) / levels * 2.0 - 1.0
+        c0 *= 4.0 / math.sqrt(d)
+    else:
+        raise ValueError(init)
+    tol = 1e-13 if bits >= 8 else 1e-14
+    c, _, it = lloyd_max(f, -1.0, 1.0, c0, tol)
+    c = 0.5 * (c - c[::-1])
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t, it
+
+
+def codebook_distortion(d: int, centroids) -> float:
+    """d * E (u_i - Q(u_i))^2 = expected squared error of a whole unit vector.
+
+    Quadrature over the Lloyd cells of the normalised density.
+    """
+    c = np.asarray(centroids, dtype=np.float64)
+    f = rotated_coordinate_density(d)
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    z, _ = cell_integrals(f, np.array([-1.0, 1.0]))
+    total = 0.0
+    for k in range(len(c)):
+        g = lambda x, ck=c[k]: (np.asarray(x) - ck) ** 2 * f(x)
+        m, _ = cell_integrals(g, edges[k:k + 2])
+        total += float(m[0])
+    return d * total / float(z[0])
+
+
+# ---------------------------------------------------------------------------
+# Rotation  ([inferrs] §核心技术; [tq-fwht] §2 FWHT 预处理)
+# ---------------------------------------------------------------------------
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester-ordered Hadamard matrix, H[i, j] = (-1)^popcount(i & j)."""
+    h = np.empty((d, d), dtype=np.float64)
+    for i in range(d):
+        for j in range(d):
+            h[i, j] = -1.0 if bin(i & j).count("1") % 2 else 1.0
+    return h
+
+
+def rotation_matrix(signs) -> np.ndarray:
+    """Dense random-sign Walsh-Hadamard rotation R = H diag(s) / sqrt(d).
+
+    [inferrs] §核心技术 names a Walsh-Hadamard rotation applied before
+    quantization; [tq-fwht] §2 says it is orthogonal and exactly invertible.
+    The random signs s are an input (drawn by the caller from a seed).
+    """
+    s = np.asarray(signs, dtype=np.float64)
+    d = s.size
+    return hadamard(d) * s[None, :] / math.sqrt(d)
+
+
+def rotate(x, signs) -> np.ndarray:
+    """y = R x for row vectors x[..., d], applying the factors of R in order:
+    sign flip, integer Hadamard product, then 1/sqrt(d).  (Applying them in this
+    order keeps exact zeros exact, e.g. for x = all-ones.)"""
+    s = np.asarray(signs, dtype=np.float64)
+    d = s.size
+    return ((np.asarray(x, dtype=np.float64) * s) @ hadamard(d).T) / math.sqrt(d)
+
+
+def unrotate(y, signs) -> np.ndarray:
+    """x = R^T y = diag(s) H y / sqrt(d) for row vectors y[..., d]."""
+    s = np.asarray(signs, dtype=np.float64)
+    d = s.size
+    return s * ((np.asarray(y, dtype=np.float64) @ hadamard(d)) / math.sqrt(d))
+
+
+# ---------------------------------------------------------------------------
+# Quantization  ([tq-80] §核心创新; [inferrs] §压缩格式对比)
+# ---------------------------------------------------------------------------
+
+def fp16_round(x) -> np.ndarray:
+    """IEEE binary16 round-to-nearest-even of fp64 values (returned as float16)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+def nearest_code_bruteforce(u, centroids) -> np.ndarray:
+    """argmin_k |u - c_k|, ties to the lower index (brute force over all levels)."""
+    u = np.asarray(u, dtype=np.float64)
+    c = np.asarray(centroids, dtype=np.float64)
+    dist = np.abs(u[..., None] - c)
+    best = dist.min(axis=-1, keepdims=True)
+    return np.argmax(dist <= best, axis=-1).astype(np.int64)
+
+
+def code_by_boundaries(u, boundaries) -> np.ndarray:
+    """Number of boundaries strictly below u (nearest centroid, ties low)."""
+    return np.searchsorted(np.asarray(boundaries, dtype=np.float64),
+                           np.asarray(u, dtype=np.float64), side="left").astype(np.int64)
+
+
+def quantize(x, signs, centroids, boundaries, method: str = "boundaries"):
+    """Quantize head vectors x[..., d] (fp64 values).
+
+    Steps ([tq-80] §核心创新): n = ||x||_2; the norm is kept as fp16; the
+    direction u = R x / n is rotated and each coordinate is mapped to its nearest
+    codeword.  Returns (codes int64 [..., d], norms float16 [...], u fp64 [..., d]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1))
+    y = rotate(x, signs)
+    safe = np.where(n > 0, n, 1.0)
+    u = np.where((n > 0)[..., None], y / safe[..., None], 0.0)
+    if method == "bruteforce":
+        codes = nearest_code_bruteforce(u, centroids)
+    else:
+        codes = code_by_boundaries(u, boundaries)
+    return codes, fp16_round(n), u
+
+
+def near_boundary_mask(u, boundaries, band: float = 1e-6) -> np.ndarray:
+    """Coordinates whose rotated value lies within `band` of a boundary."""
+    u = np.asarray(u, dtype=np.float64)
+    t = np.asarray(boundaries, dtype=np.float64)
+    return (np.abs(u[..., None] - t) <= band).any(axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Bit packing  ([google] mlx-vlm kernel list: pack / unpack of low-bit codes)
+# ---------------------------------------------------------------------------
+
+LAYOUT_ROWS = 0     # token-major: one contiguous LSB-first row per vector
+LAYOUT_GROUP8 = 1   # groups of 8 tokens, coordinate-major inside a group
+
+
+def code_bit_positions(n_tokens: int, d: int, bits: int, layout: int) -> np.ndarray:
+    """Bit offset of bit k of code (t, i) inside one (batch, kv-head) code plane.
+
+    LAYOUT_ROWS:   t*d*b + i*b + k                 (vector t is one LSB-first row)
+    LAYOUT_GROUP8: (t//8)*d*8*b + (i*8 + t%8)*b + k (codes of 8 consecutive tokens
+                   for one coordinate are adjacent)
+    Returns int64 array [n_tokens, d, bits].
+    """
+    t = np.arange(n_tokens)[:, None, None]
+    i = np.arange(d)[None, :, None]
+    k = np.arange(bits)[None, None, :]
+    if layout == LAYOUT_ROWS:
+        return t * d * bits + i * bits + k
+    if layout == LAYOUT_GROUP8:
+        return (t // 8) * d * 8 * bits + (i * 8 + t % 8) * bits + k
+    raise ValueError(layout)
+
+
+def pack(codes, bits: int, layout: int = LAYOUT_ROWS) -> np.ndarray:
+    """Pack codes [T, d] into T*d*b/8 bytes: bit k of a code goes to its bit offset,
+    byte = offset >> 3, bit-in-byte = offset & 7 (LSB first)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    n_tokens, d = codes.shape
+    if layout == LAYOUT_GROUP8 and n_tokens % 8:
+        raise ValueError("LAYOUT_GROUP8 needs a multiple of 8 tokens")
+    pos = code_bit_positions(n_tokens, d, bits, layout)
+    bitval = (codes[:, :, None] >> np.arange(bits)[None, None, :]) & 1
+    out = np.zeros(n_tokens * d * bits // 8, dtype=np.uint8)
+    on = pos[bitval == 1]
+    np.bitwise_or.at(out, on >> 3, (1 << (on & 7)).astype(np.uint8))
+    return out
+
+
+def unpack(packed, n_tokens: int, d: int, bits: int, layout: int = LAYOUT_ROWS) -> np.ndarray:
+    """Inverse of `pack`: codes [T, d] (int64)."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    pos = code_bit_positions(n_tokens, d, bits, layout)
+    bitval = (packed[pos >> 3] >> (pos & 7)) & 1
+    return (bitval.astype(np.int64) << np.arange(bits)[None, None, :]).sum(axis=-1)
+
+
+def packed_bytes_per_vector(d: int, bits: int) -> int:
+    """Bytes per cached vector: d*b/8 code bytes plus a 2-byte fp16 norm."""
+    return d * bits // 8 + 2
+
+
+# ---------------------------------------------------------------------------
+# Dequantization and attention
+# ---------------------------------------------------------------------------
+
+def dequantize(codes, norms16, signs, centroids) -> np.ndarray:
+    """x_hat = n16 * R^T c[idx]  (the exact inverse rotation, [tq-fwht] §2)."""
+    c = np.asarray(centroids, dtype=np.float64)[np.asarray(codes)]
+    n = np.asarray(norms16, dtype=np.float64)
+    return n[..., None] * unrotate(c, signs)
+
+
+def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 0.0):
+    """Decode attention over a dequantized cache, one query per (batch, head).
+
+    q: [B, Hq, d]; k_hat, v_hat: [B, Hkv, T, d]; query head h reads kv head
+    h // (Hq // Hkv).  For each (b, h) with length T_b:
+      s_t = scale * q . k_hat_t,  M = max s,  LSE = M + log sum exp(s - M),
+      p_t = exp(s_t - LSE),       o = sum_t keep_t p_t v_hat_t,
+    with keep_t = (p_t >= tau) for Sparse V ([inferrs] §Sparse V: V rows of
+    low attention weight are skipped) and keep_t = 1 when tau == 0.  The
+    denominator always counts every row (no renormalisation).
+    Returns (out [B, Hq, d], lse [B, Hq], scores [B, Hq, T] with -inf past T_b).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kh = np.asarray(k_hat, dtype=np.float64)
+    vh = np.asarray(v_hat, dtype=np.float64)
+    bsz, hq, d = q.shape
+    hkv, t_max = kh.shape[1], kh.shape[2]
+    g = hq // hkv
+    out = np.zeros((bsz, hq, d))
+    lse = np.full((bsz, hq), -np.inf)
+    scores = np.full((bsz, hq, t_max), -np.inf)
+    for b in range(bsz):
+        tb = t_max if seq_lens is None else int(seq_lens[b])
+        for h in range(hq):
+            j = h // g
+            if tb == 0:
+                continue
+            s = scale * (kh[b, j, :tb] @ q[b, h])
+            m = s.max()
+            ssum = np.exp(s - m).sum()
+            l_ = m + math.log(ssum)
+            p = np.exp(s - l_)
+            keep = p >= tau if tau > 0 else np.ones(tb, dtype=bool)
+            out[b, h] = (p[keep, None] * vh[b, j, :tb][keep]).sum(axis=0)
+            lse[b, h] = l_
+            scores[b, h, :tb] = s
+    return out, lse, scores
+
+
+def sparse_v_borderline(scores, lse, tau: float, rel: float = 1e-3) -> np.ndarray:
+    """Rows whose keep decision is within the score tolerance of the threshold.
+
+    |s_t - (LSE + ln tau)| <= rel * max|s| for the (b, h) row; either decision
+    is acceptable there.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    finite = np.isfinite(s)
+    smax = np.where(finite, np.abs(s), 0.0).max(axis=-1, keepdims=True)
+    thr = np.asarray(lse)[..., None] + math.log(tau)
+    return finite & (np.abs(s - thr) <= rel * smax)

@@ -1,0 +1,369 @@
+"""Pins for the CPU oracle: closed forms, library routines, textbook cases, brute force.
+
+None of these re-type the oracle's own formula; each compares it with something
+the mathematics or an independent routine fixes.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import linalg, special
+
+from oracle import tq_oracle as o
+
+D = 128
+ALPHA = (D - 3) / 2.0
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- codebook
+
+
+def _beta_mass(a, b):
+    """Closed-form cell mass of (1-x^2)^alpha / Z via the regularized incomplete beta."""
+    p = ALPHA + 1.0
+    return special.betainc(p, p, (b + 1) / 2) - special.betainc(p, p, (a + 1) / 2)
+
+
+def _first_moment(a, b):
+    """Closed-form int_a^b x (1-x^2)^alpha dx / Z."""
+    z = special.beta(0.5, ALPHA + 1.0)
+    p = ALPHA + 1.0
+    return ((1 - a * a) ** p - (1 - b * b) ** p) / (2 * p * z)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_quadrature_matches_closed_form_moments(bits, golden_codebooks):
+    c, t = golden_codebooks[bits]
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    f = o.rotated_coordinate_density(D)
+    mass, mom = o.cell_integrals(f, edges)
+    z = special.beta(0.5, ALPHA + 1.0)
+    mass_cf = _beta_mass(edges[:-1], edges[1:])
+    mom_cf = _first_moment(edges[:-1], edges[1:])
+    assert np.allclose(mass / z, mass_cf, rtol=1e-11, atol=1e-16)
+    assert np.allclose(mom / z, mom_cf, rtol=1e-10, atol=1e-17)
+    # the stored table satisfies the centroid condition with closed-form moments
+    assert np.allclose(mom_cf / mass_cf, c, rtol=0, atol=5e-10)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_midpoint_condition_and_symmetry(bits, golden_codebooks):
+    c, t = golden_codebooks[bits]
+    assert len(c) == 1 << bits and len(t) == (1 << bits) - 1
+    assert np.all(np.diff(c) > 0)
+    assert np.array_equal(t, 0.5 * (c[:-1] + c[1:]))
+    assert np.array_equal(c, -c[::-1])
+    assert t[(1 << bits) // 2 - 1] == 0.0
+
+
+def test_one_bit_closed_form():
+    # optimal 1-bit quantizer of a symmetric density: +/- E|x|
+    c, _, _ = o.make_codebook(D, 1)
+    e_abs = math.exp(special.gammaln(D / 2) - special.gammaln((D + 1) / 2)) / math.sqrt(math.pi)
+    assert abs(e_abs - 0.0706616) < 1e-7
+    assert np.allclose(c, [-e_abs, e_abs], rtol=1e-13)
+
+
+def _max_table():
+    rows = {}
+    with open(os.path.join(GOLDEN, "max1960_gaussian.txt")) as fh:
+        for ln in fh:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            head, outs, bnds, mse = [s.strip() for s in ln.split("|")]
+            n = int(head.split()[1])
+            rows[n] = ([float(x) for x in outs.split()],
+                       [float(x) for x in bnds.split()] if bnds else [], float(mse))
+    return rows
+
+
+@pytest.mark.parametrize("levels", [2, 4, 8, 16])
+def test_lloyd_routine_reproduces_max_gaussian_table(levels):
+    """Textbook special case: the same Lloyd routine on N(0,1) gives Max's table."""
+    outs, bnds, mse = _max_table()[levels]
+    f = lambda x: np.exp(-0.5 * np.asarray(x) ** 2)
+    init = o.gaussian_quantile_init(1, levels)
+    c, t, _ = o.lloyd_max(f, -12.0, 12.0, init, 1e-13, max_piece=0.05)
+    pos_c = c[levels // 2:]
+    pos_t = t[levels // 2:]
+    assert np.allclose(pos_c, outs, atol=6e-4, rtol=6e-4)
+    assert np.allclose(pos_t, bnds, atol=6e-4, rtol=6e-4)
+    # distortion of the result vs the table's mse
+    edges = np.concatenate(([-12.0], t, [12.0]))
+    tot = 0.0
+    for k in range(levels):
+        g = lambda x, ck=c[k]: (np.asarray(x) - ck) ** 2 * f(x)
+        m, _ = o.cell_integrals(g, edges[k:k + 2], 0.05)
+        tot += m[0]
+    tot /= math.sqrt(2 * math.pi)
+    assert abs(tot - mse) <= 6e-4 * mse + 5e-6
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_scaled_codebook_near_gaussian_limit(bits):
+    outs, _, _ = _max_table()[1 << bits]
+    c, _, _ = o.make_codebook(D, bits)
+    ratio = math.sqrt(D) * c[(1 << bits) // 2:] / np.array(outs)
+    assert np.all(np.abs(ratio - 1) < 0.02)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_optimum_is_unique(bits):
+    c1, _, _ = o.make_codebook(D, bits, init="gauss")
+    c2, _, _ = o.make_codebook(D, bits, init="uniform")
+    assert np.allclose(c1, c2, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_stored_tables_match_fresh_lloyd(bits, golden_codebooks):
+    c, t, _ = o.make_codebook(D, bits)
+    assert np.array_equal(c, golden_codebooks[bits][0])
+    assert np.array_equal(t, golden_codebooks[bits][1])
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_distortion_matches_monte_carlo_and_bound(bits, golden_codebooks):
+    c, t = golden_codebooks[bits]
+    d_quad = o.codebook_distortion(D, c)
+    rng = np.random.default_rng(1234)
+    x = rng.standard_normal((20000, D))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)   # uniform on the sphere
+    idx = o.code_by_boundaries(u, t)
+    err = ((u - c[idx]) ** 2).sum(axis=1)
+    se = err.std() / math.sqrt(err.size)
+    assert abs(err.mean() - d_quad) < 4 * se
+    # the pages' "about 2.7x the information-theoretic bound" read with the
+    # 4^-b lower bound: D_b * 4^b stays below sqrt(3)*pi/2
+    assert d_quad * 4 ** bits < math.sqrt(3) * math.pi / 2
+    assert d_quad * 4 ** bits > 1.0
+
+
+# ----------------------------------------------------------------- rotation
+
+
+def _signs(seed=1):
+    rng = np.random.default_rng(seed)
+    return 1 - 2 * rng.integers(0, 2, D)
+
+
+def test_rotation_matches_scipy_hadamard():
+    s = _signs()
+    r = o.rotation_matrix(s)
+    ref = linalg.hadamard(D).astype(np.float64) * s[None, :] / math.sqrt(D)
+    assert np.array_equal(r, ref)
+    assert np.abs(r @ r.T - np.eye(D)).max() < 1e-14
+    x = np.random.default_rng(0).standard_normal((10, D))
+    y = x @ r.T
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    assert np.allclose(y @ r, x, atol=1e-13)
+    assert np.allclose(o.rotate(x, s), y, atol=1e-13)
+    assert np.allclose(o.unrotate(o.rotate(x, s), s), x, atol=1e-13)
+
+
+# ----------------------------------------------------------------- quantize
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_quantize_basis_vectors(bits, golden_codebooks):
+    """x = e_j: every u_i = H[i, j] s_j / sqrt(d) = +/- 1/sqrt(d)."""
+    c, t = golden_codebooks[bits]
+    s = _signs()
+    h = linalg.hadamard(D)
+    expect_pos = int(np.argmin(np.abs(c - 1 / math.sqrt(D))))
+    expect_neg = int(np.argmin(np.abs(c + 1 / math.sqrt(D))))
+    assert expect_pos + expect_neg == len(c) - 1
+    assert expect_pos == {2: 3, 3: 5, 4: 11, 8: 184}[bits]
+    for j in (0, 5, 77, 127):
+        x = np.zeros(D)
+        x[j] = 3.0
+        codes, n16, u = o.quantize(x[None], s, c, t)
+        sign = h[:, j] * s[j]
+        assert np.array_equal(codes[0], np.where(sign > 0, expect_pos, expect_neg))
+        assert float(n16[0]) == 3.0
+        assert np.abs(np.abs(u[0][:, None] - t[None, :])).min() > 7.5e-4
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_quantize_ties_and_zero_vector(bits, golden_codebooks):
+    c, t = golden_codebooks[bits]
+    levels = 1 << bits
+    plus = np.ones(D, dtype=np.int64)
+    codes, _, u = o.quantize(np.ones((1, D)), plus, c, t)
+    assert abs(u[0, 0] - 1.0) < 1e-15 and np.all(u[0, 1:] == 0.0)
+    assert codes[0, 0] == levels - 1
+    assert np.all(codes[0, 1:] == levels // 2 - 1)          # ties go to the lower code
+    codes0, n0, u0 = o.quantize(np.zeros((1, D)), _signs(), c, t)
+    assert float(n0[0]) == 0.0 and np.all(u0 == 0.0)
+    assert np.all(codes0 == levels // 2 - 1)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_bruteforce_equals_boundary_search(bits, golden_codebooks):
+    c, t = golden_codebooks[bits]
+    rng = np.random.default_rng(bits)
+    u = np.concatenate([rng.standard_normal(5000) * 0.12, c, [-1.0, 1.0, 0.0]])
+    assert np.array_equal(o.nearest_code_bruteforce(u, c), o.code_by_boundaries(u, t))
+    # exactly on a boundary both neighbours are nearest (up to the rounding of
+    # |u - c|); the boundary rule takes the lower one
+    at = o.code_by_boundaries(t, t)
+    assert np.array_equal(at, np.arange(len(t)))
+    assert np.all(np.abs(o.nearest_code_bruteforce(t, c) - at) <= 1)
+
+
+def test_fp16_norm_is_round_to_nearest_even():
+    vals = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2048 + 1, 65504.0, 1e-8])
+    r = o.fp16_round(vals).astype(np.float64)
+    assert r[0] == 1.0 and r[1] == 1 + 2 ** -9 and r[2] == 2048.0 and r[3] == 65504.0
+    assert r[4] == 0.0
+
+
+# ----------------------------------------------------------------- packing
+
+
+def _pack_bit_loop(codes, bits, layout):
+    n_tokens, d = codes.shape
+    out = bytearray(n_tokens * d * bits // 8)
+    for tok in range(n_tokens):
+        for i in range(d):
+            for k in range(bits):
+                if (int(codes[tok, i]) >> k) & 1:
+                    if layout == o.LAYOUT_ROWS:
+                        pos = (tok * d + i) * bits + k
+                    else:
+                        grp, r = divmod(tok, 8)
+                        pos = grp * d * 8 * bits + (i * 8 + r) * bits + k
+                    out[pos // 8] |= 1 << (pos % 8)
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_pack_two_routes_and_roundtrip(bits, layout):
+    rng = np.random.default_rng(bits * 10 + layout)
+    codes = rng.integers(0, 1 << bits, size=(16, D))
+    a = o.pack(codes, bits, layout)
+    b = _pack_bit_loop(codes, bits, layout)
+    assert np.array_equal(a, b)
+    assert np.array_equal(o.unpack(a, 16, D, bits, layout), codes)
+    if layout == o.LAYOUT_ROWS:
+        bitmat = ((codes[:, :, None] >> np.arange(bits)) & 1).astype(np.uint8).reshape(-1)
+        assert np.array_equal(np.packbits(bitmat, bitorder="little"), a)
+        # one row per vector, d*b/8 bytes
+        assert np.array_equal(a.reshape(16, -1)[3], o.pack(codes[3:4], bits))
+
+
+# ----------------------------------------------------------------- dequantize / attention
+
+
+def test_dequantize_norm_and_inverse(golden_codebooks):
+    s = _signs()
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, D)) * 3
+    for bits in (2, 4, 8):
+        c, t = golden_codebooks[bits]
+        codes, n16, u = o.quantize(x, s, c, t)
+        xh = o.dequantize(codes, n16, s, c)
+        assert np.allclose(np.linalg.norm(xh, axis=1),
+                           n16.astype(np.float64) * np.linalg.norm(c[codes], axis=1), rtol=1e-13)
+        rel = np.linalg.norm(xh - x, axis=1) / np.linalg.norm(x, axis=1)
+        assert rel.mean() < 1.5 * math.sqrt(o.codebook_distortion(D, c))
+
+
+def _small_cache(bits_k=4, bits_v=2, b=2, hkv=2, hq=4, T=37, seed=0, golden=None):
+    s = _signs()
+    rng = np.random.default_rng(seed)
+    ck, tk = golden[bits_k]
+    cv, tv = golden[bits_v]
+    k = rng.standard_normal((b, hkv, T, D))
+    v = rng.standard_normal((b, hkv, T, D))
+    kc, kn, _ = o.quantize(k, s, ck, tk)
+    vc, vn, _ = o.quantize(v, s, cv, tv)
+    kh = o.dequantize(kc, kn, s, ck)
+    vh = o.dequantize(vc, vn, s, cv)
+    q = rng.standard_normal((b, hq, D))
+    return s, q, kc, kn, vc, vn, kh, vh, ck, cv
+
+
+def test_attention_rotated_domain_identity(golden_codebooks):
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(golden=golden_codebooks)
+    scale = 1 / math.sqrt(D)
+    out, lse, scores = o.decode_attention(q, kh, vh, scale)
+    r = o.rotation_matrix(s)
+    g = q.shape[1] // kh.shape[1]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            qt = scale * (r @ q[b, h])
+            s_rot = kn[b, h // g].astype(np.float64) * (ck[kc[b, h // g]] @ qt)
+            assert np.allclose(scores[b, h], s_rot, rtol=1e-12, atol=1e-12)
+            assert abs(lse[b, h] - special.logsumexp(s_rot)) < 1e-12
+            p = special.softmax(s_rot)
+            o_rot = (p[:, None] * vn[b, h // g].astype(np.float64)[:, None] * cv[vc[b, h // g]]).sum(0)
+            assert np.allclose(out[b, h], r.T @ o_rot, atol=1e-12)
+
+
+def test_attention_special_cases(golden_codebooks):
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(golden=golden_codebooks)
+    scale = 1 / math.sqrt(D)
+    out1, lse1, _ = o.decode_attention(q, kh[:, :, :1], vh[:, :, :1], scale)
+    assert np.allclose(out1, np.repeat(vh[:, :, 0], 2, axis=1))
+    out0, _, _ = o.decode_attention(np.zeros_like(q), kh, vh, scale)
+    assert np.allclose(out0, np.repeat(vh.mean(axis=2), 2, axis=1))
+    vsame = np.broadcast_to(vh[:, :, :1], vh.shape)
+    out_same, _, _ = o.decode_attention(q, kh, vsame, scale)
+    assert np.allclose(out_same, np.repeat(vh[:, :, 0], 2, axis=1))
+    # GQA: query head h reads kv head h // g
+    _, lse, scores = o.decode_attention(q, kh, vh, scale)
+    for h in range(4):
+        assert np.allclose(scores[1, h, :], scale * kh[1, h // 2] @ q[1, h])
+    assert np.allclose(np.exp(scores - lse[..., None]).sum(-1), 1.0)
+    # per-sequence lengths
+    lens = np.array([5, 37])
+    out_l, lse_l, sc_l = o.decode_attention(q, kh, vh, scale, seq_lens=lens)
+    ref, _, _ = o.decode_attention(q[:1], kh[:1, :, :5], vh[:1, :, :5], scale)
+    assert np.allclose(out_l[0], ref[0]) and np.all(np.isneginf(sc_l[0, :, 5:]))
+
+
+def test_sparse_v_limits_and_bound(golden_codebooks):
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=200, golden=golden_codebooks)
+    q = q * 6.0     # sharpen the attention so some rows fall under the threshold
+    scale = 1 / math.sqrt(D)
+    dense, lse, scores = o.decode_attention(q, kh, vh, scale)
+    same, _, _ = o.decode_attention(q, kh, vh, scale, tau=1e-300)
+    assert np.allclose(same, dense)
+    none, _, _ = o.decode_attention(q, kh, vh, scale, tau=1.01)
+    assert np.all(none == 0.0)
+    tau = 1e-2
+    sparse, _, _ = o.decode_attention(q, kh, vh, scale, tau=tau)
+    p = np.exp(scores - lse[..., None])
+    dropped = p < tau
+    g = q.shape[1] // kh.shape[1]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            bound = (p[b, h] * dropped[b, h] * np.linalg.norm(vh[b, h // g], axis=1)).sum()
+            assert np.linalg.norm(sparse[b, h] - dense[b, h]) <= bound + 1e-12
+    assert dropped.any() and (~dropped).any()
+
+
+def _page_figures():
+    out = {}
+    with open(os.path.join(GOLDEN, "pages_format_figures.txt")) as fh:
+        for ln in fh:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            key, val, _ = [x.strip() for x in ln.split("|")]
+            out[key] = float(val)
+    return out
+
+
+def test_byte_accounting_against_pages():
+    fig = _page_figures()
+    fp16 = 2 * D
+    per = {b: o.packed_bytes_per_vector(D, b) for b in (2, 3, 4, 8)}
+    assert per == {2: 34, 3: 50, 4: 66, 8: 130}
+    assert round(fp16 / per[4], 1) == pytest.approx(3.9, abs=0.01) and fp16 / per[4] >= fig["turbo4_ratio_vs_fp16"]
+    assert abs(fp16 / per[3] - fig["turbo3_ratio_vs_fp16_max"]) < 0.05
+    assert 1 - (per[4] + per[2]) / (2 * fp16) > fig["k4v2_saving_min"]
+    assert abs(1 - (per[3] + per[2]) / (2 * fp16) - fig["k3v2_saving"]) < 0.005
+    assert (D * 4 // 8) / fp16 == fig["four_bit_cache_fraction"]
