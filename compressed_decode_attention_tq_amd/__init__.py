@@ -1,0 +1,214 @@
+"""TurboQuant compressed-KV quantize and decode attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of libtq.so (declared in include/tq.h).  It only
+marshals arguments: every step of quantize, decode attention and dequantize runs in the
+HIP kernels of the library.  PyTorch provides device memory and the current stream.
+There is no CPU fallback: if libtq.so has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+LAYOUT_ROWS, LAYOUT_GROUP8 = 0, 1
+D = 128
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
+        ("boundaries", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m compressed_decode_attention_tq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.tq_make_codebook_table.argtypes = [i32, i32, vp, vp]
+        L.tq_quantize_append.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, vp]
+        L.tq_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, i32,
+                                     i32, vp, i32, f32, f32, vp, vp, vp, vp, sz, vp]
+        L.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
+        L.tq_decode_workspace_bytes.restype = sz
+        L.tq_dequantize.argtypes = [ctypes.POINTER(CacheStruct), i32, i32, vp, i32, vp]
+        L.tq_code_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.tq_code_bytes.restype = sz
+        L.tq_status_string.argtypes = [i32]
+        L.tq_status_string.restype = ctypes.c_char_p
+        for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_decode_attn", "tq_dequantize"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != TQ_OK:
+        raise TQError(status, what)
+
+
+def make_codebook_table(d: int, bits: int):
+    """Host call: fp32 (centroids[2^bits], boundaries[2^bits - 1]) as numpy arrays."""
+    c = np.zeros(1 << bits, dtype=np.float32)
+    t = np.zeros(max((1 << bits) - 1, 1), dtype=np.float32)
+    _check(lib().tq_make_codebook_table(d, bits, c.ctypes.data, t.ctypes.data), "tq_make_codebook_table")
+    return c, t[: (1 << bits) - 1]
+
+
+def code_bytes(d: int, bits: int, batch: int, n_kv_heads: int, capacity: int) -> int:
+    return int(lib().tq_code_bytes(d, bits, batch, n_kv_heads, capacity))
+
+
+def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, ctx_len: int, tau: float) -> int:
+    return int(lib().tq_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, ctx_len, tau))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return TQ_F32
+    if dt == torch.bfloat16:
+        return TQ_BF16
+    if dt == torch.float16:
+        return TQ_F16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class PackedCache:
+    """One K or V cache of one layer: packed codes + fp16 norms + codebook + signs (device)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, capacity: int, bits: int, layout: int,
+                 signs, device="cuda", d: int = D):
+        torch = _torch()
+        self.d, self.bits, self.layout = d, bits, layout
+        self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
+        nbytes = batch * n_kv_heads * capacity * d * bits // 8
+        self.codes = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.norms = torch.zeros(batch * n_kv_heads * capacity, dtype=torch.float16, device=device)
+        c, t = make_codebook_table(d, bits)
+        self.centroids = torch.from_numpy(c).to(device)
+        self.boundaries = torch.from_numpy(np.concatenate([t, [0.0]]).astype(np.float32)).to(device)
+        if signs.is_cuda and signs.dtype == torch.int8 and signs.is_contiguous():
+            self.signs = signs          # shared: the K and V caches of a layer use one sign vector
+        else:
+            self.signs = signs.to(device=device, dtype=torch.int8).contiguous()
+
+    def struct(self) -> CacheStruct:
+        return CacheStruct(self.d, self.bits, self.layout, self.batch, self.n_kv_heads, self.capacity,
+                           self.codes.data_ptr(), self.norms.data_ptr(), self.centroids.data_ptr(),
+                           self.boundaries.data_ptr(), self.signs.data_ptr())
+
+    def plane_codes(self, b: int, h: int):
+        per = self.capacity * self.d * self.bits // 8
+        i = b * self.n_kv_heads + h
+        return self.codes[i * per:(i + 1) * per]
+
+    def plane_norms(self, b: int, h: int):
+        i = b * self.n_kv_heads + h
+        return self.norms[i * self.capacity:(i + 1) * self.capacity]
+
+
+def quantize_append(cache: PackedCache, x, start_pos: int, stream=None):
+    """Quantize x [batch, n_tokens, n_kv_heads, d] into positions start_pos .. start_pos+n_tokens."""
+    if x.dim() != 4 or x.shape[0] != cache.batch or x.shape[2] != cache.n_kv_heads or x.shape[3] != cache.d:
+        raise ValueError(f"x has shape {tuple(x.shape)}")
+    st = cache.struct()
+    _check(lib().tq_quantize_append(ctypes.byref(st), _dev(x, "x"), _dtype_code(x.dtype), start_pos,
+                                    x.shape[1], _stream_ptr(stream)), "tq_quantize_append")
+
+
+def dequantize(cache: PackedCache, start_pos: int, n_tokens: int, dtype=None, stream=None):
+    """x_hat [batch, n_tokens, n_kv_heads, d] for cache positions start_pos .. start_pos+n_tokens."""
+    torch = _torch()
+    dtype = torch.float32 if dtype is None else dtype
+    out = torch.empty((cache.batch, n_tokens, cache.n_kv_heads, cache.d), dtype=dtype,
+                      device=cache.codes.device)
+    st = cache.struct()
+    _check(lib().tq_dequantize(ctypes.byref(st), start_pos, n_tokens, _dev(out, "out"),
+                               _dtype_code(dtype), _stream_ptr(stream)), "tq_dequantize")
+    return out
+
+
+class DecodeBuffers:
+    """Caller-owned outputs and workspace of one decode problem shape."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, ctx_len, tau, device="cuda", d=D,
+                 want_lse=True, want_scores=False):
+        torch = _torch()
+        self.out = torch.empty((batch, n_q_heads, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=device) if want_lse else None
+        self.scores = (torch.empty((batch, n_q_heads, ctx_len), dtype=torch.float32, device=device)
+                       if want_scores else None)
+        nbytes = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, ctx_len, tau)
+        if nbytes == 0:
+            raise TQError(TQ_ERR_INVALID_ARG, "tq_decode_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.ws_bytes = nbytes
+
+
+def decode_attn(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: int, scale: float,
+                tau: float = 0.0, seq_lens=None, buffers: DecodeBuffers | None = None,
+                want_scores: bool = False, stream=None):
+    """Decode attention; returns the DecodeBuffers holding out [B, Hq, d], lse and scores."""
+    bsz, hq, d = q.shape
+    if buffers is None:
+        buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, tau, device=q.device,
+                                d=d, want_scores=want_scores)
+    ks, vs = k_cache.struct(), v_cache.struct()
+    sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
+    _check(lib().tq_decode_attn(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len,
+        float(scale), float(tau), _dev(buffers.out, "out"),
+        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        _dev(buffers.scores, "scores") if buffers.scores is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn")
+    return buffers

@@ -1,0 +1,201 @@
+// C-ABI entry points: argument validation (before any HIP call), split planning,
+// workspace layout and kernel launches.  See include/tq.h for the contract.
+#include <cmath>
+#include <cstdint>
+
+#include "tq_launch.h"
+
+namespace tq {
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+bool valid_dtype(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+
+// Largest capacity accepted: keeps every plane offset far inside 64-bit and every token
+// index inside int32 arithmetic in the kernels.
+constexpr int kMaxCapacity = 1 << 26;
+
+int check_cache(const tq_cache *c) {
+  if (c == nullptr) return TQ_ERR_INVALID_ARG;
+  if (c->codes == nullptr || c->norms == nullptr || c->centroids == nullptr ||
+      c->boundaries == nullptr || c->signs == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned(c->codes, 16) || !aligned(c->norms, 16) || !aligned(c->centroids, 4) ||
+      !aligned(c->boundaries, 4))
+    return TQ_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->capacity < 1) return TQ_ERR_INVALID_ARG;
+  if (c->layout != TQ_LAYOUT_ROWS && c->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;
+  if (c->d != kD) return TQ_ERR_UNSUPPORTED;
+  if (!valid_bits(c->bits)) return TQ_ERR_UNSUPPORTED;
+  if (c->capacity % kChunk != 0 || c->capacity > kMaxCapacity) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+CacheView view_of(const tq_cache *c) {
+  CacheView v;
+  v.codes = c->codes;
+  v.norms = c->norms;
+  v.centroids = c->centroids;
+  v.boundaries = c->boundaries;
+  v.signs = c->signs;
+  v.bits = c->bits;
+  v.layout = c->layout;
+  v.n_kv_heads = c->n_kv_heads;
+  v.capacity = c->capacity;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len) {
+  const long units = (long)batch * n_kv_heads;
+  const long target_blocks = 2048;
+  long s_target = (target_blocks + units - 1) / units;
+  if (s_target < 1) s_target = 1;
+  long len = (ctx_len + s_target - 1) / s_target;
+  len = (len + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  if (len < kSplitAlign) len = kSplitAlign;
+  long n = (ctx_len + len - 1) / len;
+  if (n < 1) n = 1;
+  return SplitPlan{(int)n, (int)len};
+}
+
+WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
+                                 bool sparse) {
+  const SplitPlan p = plan_splits(batch, n_kv_heads, ctx_len);
+  const size_t heads = (size_t)batch * n_q_heads * p.n_splits;
+  WorkspaceLayout w{};
+  size_t off = 0;
+  w.part_ml = off;
+  off = align_up(off + heads * sizeof(float2), 256);
+  w.part_o = off;
+  off = align_up(off + heads * kD * sizeof(float), 256);
+  w.cand_count = off;
+  w.cand = off;
+  if (sparse) {
+    const size_t units = (size_t)batch * n_kv_heads * p.n_splits;
+    const int g = n_q_heads / n_kv_heads;
+    off = align_up(off + units * sizeof(int), 256);
+    w.cand = off;
+    off = align_up(off + units * (size_t)p.split_len * (1 + g) * sizeof(float), 256);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char *tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t tq_code_bytes(int d, int bits, int batch, int n_kv_heads, int capacity) {
+  if (d < 1 || batch < 1 || n_kv_heads < 1 || capacity < 1 || bits < 1 || bits > 8) return 0;
+  return (size_t)batch * n_kv_heads * capacity * (size_t)d * bits / 8;
+}
+
+size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
+                                 float sparse_v_tau) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads != 0 ||
+      ctx_len < 0 || !(sparse_v_tau >= 0.f && sparse_v_tau < 1.f))
+    return 0;
+  return workspace_layout(batch, n_q_heads, n_kv_heads, ctx_len, sparse_v_tau > 0.f).total;
+}
+
+int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_pos,
+                       int n_tokens, void *hip_stream) {
+  int st = check_cache(c);
+  if (st != TQ_OK) return st;
+  if (x == nullptr || !aligned(x, 16) || !valid_dtype(x_dtype)) return TQ_ERR_INVALID_ARG;
+  if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if ((long)start_pos + n_tokens > c->capacity) return TQ_ERR_CAPACITY;
+  if (n_tokens == 0) return TQ_OK;
+  return hip_status(launch_quantize(view_of(c), c->batch, x, x_dtype, start_pos, n_tokens,
+                                    static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_dequantize(const tq_cache *c, int start_pos, int n_tokens, void *out, int out_dtype,
+                  void *hip_stream) {
+  int st = check_cache(c);
+  if (st != TQ_OK) return st;
+  if (out == nullptr || !aligned(out, 16) || !valid_dtype(out_dtype)) return TQ_ERR_INVALID_ARG;
+  if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if ((long)start_pos + n_tokens > c->capacity) return TQ_ERR_CAPACITY;
+  if (n_tokens == 0) return TQ_OK;
+  return hip_status(launch_dequantize(view_of(c), c->batch, out, out_dtype, start_pos, n_tokens,
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
+                   int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
+                   float sparse_v_tau, float *out, float *lse, float *scores, void *workspace,
+                   size_t workspace_bytes, void *hip_stream) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
+      k->signs != v->signs)
+    return TQ_ERR_INVALID_ARG;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (scores != nullptr && !aligned(scores, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / k->n_kv_heads;
+  if (group > 16) return TQ_ERR_UNSUPPORTED;
+  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
+  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if (!(sparse_v_tau >= 0.f && sparse_v_tau < 1.f)) return TQ_ERR_INVALID_ARG;
+  const bool sparse = sparse_v_tau > 0.f;
+  const WorkspaceLayout w = workspace_layout(k->batch, n_q_heads, k->n_kv_heads, ctx_len, sparse);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+
+  DecodeArgs a{};
+  a.k = view_of(k);
+  a.v = view_of(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = ctx_len;
+  a.scale = scale;
+  a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
+  a.sparse = sparse ? 1 : 0;
+  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len);
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  char *ws = static_cast<char *>(workspace);
+  a.part_ml = reinterpret_cast<float2 *>(ws + w.part_ml);
+  a.part_o = reinterpret_cast<float *>(ws + w.part_o);
+  a.cand_count = reinterpret_cast<int *>(ws + w.cand_count);
+  a.cand = reinterpret_cast<float *>(ws + w.cand);
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,349 @@
+// Generic decode attention over the packed cache (any code width, any GQA group <= 16).
+//
+// Scoring in the rotated domain ([google] "Google 最新極限壓縮算法…": scores computed
+// directly against quantized keys; weighted V sums kept in the rotated domain and rotated
+// back once), online softmax per split of the context, an LSE merge of the splits, and the
+// exact Sparse-V rule of [inferrs] "inferrs & TurboQuant：本地 LLM 推理的内存革命", §Sparse V
+// (rows whose final softmax weight is below tau are not decoded).
+//
+// Sparse V is exact although the final log-sum-exp is only known at the end: pass 1 keeps a
+// row as a candidate unless its score is below (running LSE of the split) + ln tau; the
+// running LSE never exceeds the final one, so no row the exact rule keeps is dropped.
+// Pass 2 applies the exact rule to the candidates with the merged LSE and reads only the
+// V codes of kept rows.
+#include "tq_common.h"
+#include "tq_launch.h"
+
+namespace tq {
+namespace {
+
+constexpr float kInvSqrtD = 0.08838834764831845f;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int seq_len_of(const DecodeArgs &a, int b) {
+  if (a.seq_lens == nullptr) return a.ctx_len;
+  return min(max(a.seq_lens[b], 0), a.ctx_len);
+}
+
+// Rotated, scaled queries of the g heads of one kv head: qt[j] = scale * R q_{kvh*g+j}.
+__device__ void load_rotated_queries(const DecodeArgs &a, int b, int kvh, float (*qt)[kD]) {
+  const int g = a.group;
+  for (int e = threadIdx.x; e < g * kD; e += blockDim.x) {
+    const int j = e / kD, i = e % kD;
+    const float x = load_elem(a.q, ((size_t)b * a.n_q_heads + kvh * g + j) * kD + i, a.q_dtype);
+    qt[j][i] = a.k.signs[i] < 0 ? -x : x;
+  }
+  block_fwht128(&qt[0][0], g);
+  const float qs = a.scale * kInvSqrtD;
+  for (int e = threadIdx.x; e < g * kD; e += blockDim.x) qt[e / kD][e % kD] *= qs;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int g = a.group, S = a.plan.n_splits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool sparse = a.sparse != 0;
+
+  __shared__ float qt[16][kD];
+  __shared__ float lutK[256], lutV[256];
+  __shared__ float pbuf[16][256];
+  __shared__ float nvs[256];
+  __shared__ float stat_s[16];
+  __shared__ int wave_cnt[4];
+
+  const int T = seq_len_of(a, b);
+  const int t_begin = s * a.plan.split_len;
+  const int t_end = min(t_begin + a.plan.split_len, T);
+  const int bk = a.k.bits, bv = a.v.bits;
+  for (int i = tid; i < (1 << bk); i += blockDim.x) lutK[i] = a.k.centroids[i];
+  for (int i = tid; i < (1 << bv); i += blockDim.x) lutV[i] = a.v.centroids[i];
+  load_rotated_queries(a, b, kvh, qt);
+
+  if (a.scores != nullptr) {  // positions past the sequence length read -inf
+    const int pad_end = min(t_begin + a.plan.split_len, a.ctx_len);
+    for (int e = max(t_begin, T) * g + tid; e < pad_end * g; e += blockDim.x) {
+      const int t = e / g, j = e % g;
+      a.scores[((size_t)b * a.n_q_heads + kvh * g + j) * a.ctx_len + t] = -INFINITY;
+    }
+  }
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+  const int ci = tid & (kD - 1), jj = tid >> 7;
+  float acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+
+  const uint8_t *kplane = a.k.plane(b, kvh);
+  const uint16_t *knorm = a.k.norm_plane(b, kvh);
+  const uint8_t *vplane = a.v.plane(b, kvh);
+  const uint16_t *vnorm = a.v.norm_plane(b, kvh);
+  float *cand_base = nullptr;
+  if (sparse)
+    cand_base = a.cand + (((size_t)b * a.n_kv_heads + kvh) * S + s) * (size_t)a.plan.split_len * (1 + g);
+  int cand_written = 0;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += 256) {
+    const int t = t0 + tid;
+    const bool valid = t < t_end;
+    float d[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = 0.f;
+    if (valid) {
+      const uint8_t *row = kplane + (size_t)t * 16 * bk;
+      for (int i0 = 0; i0 < kD; i0 += 8) {
+        float cv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cv[e] = lutK[read_field(row, (uint64_t)(i0 + e) * bk, bk)];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (j < g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[j] = fmaf(qt[j][i0 + e], cv[e], d[j]);
+          }
+        }
+      }
+      const float nk = half_bits_to_float(knorm[t]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) d[j] *= nk;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < g) pbuf[j][tid] = valid ? d[j] : -INFINITY;
+    if (a.scores != nullptr && valid) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < g) a.scores[((size_t)b * a.n_q_heads + kvh * g + j) * a.ctx_len + t] = d[j];
+    }
+    nvs[tid] = valid ? half_bits_to_float(vnorm[t]) : 0.f;
+    __syncthreads();
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = wave + 4 * r;
+      if (j < g) {
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = pbuf[j][lane + 64 * k];
+        const float cm = wave_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float m_new = fmaxf(m_run[r], cm);
+        float alpha = 1.f, psum = 0.f;
+        if (m_new != -INFINITY) {
+          alpha = m_run[r] == -INFINITY ? 0.f : __expf(m_run[r] - m_new);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[k] = x[k] == -INFINITY ? 0.f : __expf(x[k] - m_new);
+            psum += x[k];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = 0.f;
+        }
+        psum = wave_sum(psum);
+        l_run[r] = l_run[r] * alpha + psum;
+        m_run[r] = m_new;
+        if (!sparse) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pbuf[j][lane + 64 * k] = x[k];
+          if (lane == 0) stat_s[j] = alpha;
+        } else if (lane == 0) {
+          stat_s[j] = m_new == -INFINITY ? INFINITY : m_new + __logf(l_run[r]);
+        }
+      }
+    }
+    __syncthreads();
+
+    if (!sparse) {
+      const int nvalid = min(256, t_end - t0);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (jj + 2 * r < g) acc[r] *= stat_s[jj + 2 * r];
+      const uint64_t fmask = (1ull << bv) - 1ull;
+      for (int gi = 0; gi < (nvalid + 7) / 8; ++gi) {
+        const uint8_t *chunk = vplane + (size_t)((t0 >> 3) + gi) * kD * bv + (size_t)ci * bv;
+        uint64_t w = 0;
+        for (int by = 0; by < bv; ++by) w |= (uint64_t)chunk[by] << (8 * by);
+        for (int rr = 0; rr < 8; ++rr) {
+          const int tt = 8 * gi + rr;
+          if (tt >= nvalid) break;
+          const float val = lutV[(w >> (rr * bv)) & fmask] * nvs[tt];
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (jj + 2 * r < g) acc[r] = fmaf(pbuf[jj + 2 * r][tt], val, acc[r]);
+        }
+      }
+    } else {
+      bool flag = false;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < g && pbuf[j][tid] >= stat_s[j] + a.ln_tau) flag = true;
+      }
+      const uint64_t bal = __ballot(flag);
+      const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int off = cand_written;
+      for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+      if (flag) {
+        float *rec = cand_base + (size_t)(off + rank) * (1 + g);
+        rec[0] = __int_as_float(t);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < g) rec[1 + j] = pbuf[j][tid];
+      }
+      cand_written += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = wave + 4 * r;
+    if (j < g && lane == 0)
+      a.part_ml[((size_t)b * a.n_q_heads + kvh * g + j) * S + s] = make_float2(m_run[r], l_run[r]);
+  }
+  if (!sparse) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int j = jj + 2 * r;
+      if (j < g) a.part_o[(((size_t)b * a.n_q_heads + kvh * g + j) * S + s) * kD + ci] = acc[r];
+    }
+  } else if (tid == 0) {
+    a.cand_count[((size_t)b * a.n_kv_heads + kvh) * S + s] = cand_written;
+  }
+}
+
+// Pass 2 of Sparse V: exact keep rule with the merged LSE, V rows read only when kept.
+__global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int g = a.group, S = a.plan.n_splits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float lse_s[16];
+  __shared__ float lutV[256];
+  __shared__ float pbuf[16][256];
+  __shared__ int toks[256];
+  __shared__ float nvs[256];
+  __shared__ int keep_any[256];
+
+  const int bv = a.v.bits;
+  for (int i = tid; i < (1 << bv); i += blockDim.x) lutV[i] = a.v.centroids[i];
+  for (int j = wave; j < g; j += 4) {
+    const float2 *ml = a.part_ml + ((size_t)b * a.n_q_heads + kvh * g + j) * S;
+    float mx = -INFINITY;
+    for (int k = lane; k < S; k += 64) mx = fmaxf(mx, ml[k].x);
+    mx = wave_max(mx);
+    float l = 0.f;
+    if (mx != -INFINITY)
+      for (int k = lane; k < S; k += 64)
+        if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - mx);
+    l = wave_sum(l);
+    if (lane == 0) lse_s[j] = mx == -INFINITY ? INFINITY : mx + __logf(l);
+  }
+  __syncthreads();
+
+  const int count = a.cand_count[((size_t)b * a.n_kv_heads + kvh) * S + s];
+  const float *base =
+      a.cand + (((size_t)b * a.n_kv_heads + kvh) * S + s) * (size_t)a.plan.split_len * (1 + g);
+  const uint8_t *vplane = a.v.plane(b, kvh);
+  const uint16_t *vnorm = a.v.norm_plane(b, kvh);
+  const int ci = tid & (kD - 1), jj = tid >> 7;
+  float acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+
+  for (int c0 = 0; c0 < count; c0 += 256) {
+    const int r_idx = c0 + tid;
+    if (r_idx < count) {
+      const float *rec = base + (size_t)r_idx * (1 + g);
+      const int t = __float_as_int(rec[0]);
+      toks[tid] = t;
+      nvs[tid] = half_bits_to_float(vnorm[t]);
+      int any = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j < g) {
+          const float z = rec[1 + j] - lse_s[j];
+          const float p = z >= a.ln_tau ? __expf(z) : 0.f;
+          pbuf[j][tid] = p;
+          any |= p > 0.f;
+        }
+      }
+      keep_any[tid] = any;
+    }
+    __syncthreads();
+    const int n = min(256, count - c0);
+    for (int tt = 0; tt < n; ++tt) {
+      if (!keep_any[tt]) continue;
+      const int t = toks[tt];
+      const float val =
+          lutV[read_field(vplane, code_bit_offset(TQ_LAYOUT_GROUP8, bv, t, ci), bv)] * nvs[tt];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (jj + 2 * r < g) acc[r] = fmaf(pbuf[jj + 2 * r][tt], val, acc[r]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int j = jj + 2 * r;
+    if (j < g) a.part_o[(((size_t)b * a.n_q_heads + kvh * g + j) * S + s) * kD + ci] = acc[r];
+  }
+}
+
+// LSE merge of the split partials, normalisation and the inverse rotation R^T.
+__global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
+  const int hq = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const int S = a.plan.n_splits;
+  const float2 *ml = a.part_ml + ((size_t)b * a.n_q_heads + hq) * S;
+  const float *po = a.part_o + ((size_t)b * a.n_q_heads + hq) * S * kD;
+  __shared__ float buf[kD];
+  float mx = -INFINITY;
+  for (int k = 0; k < S; ++k) mx = fmaxf(mx, ml[k].x);
+  float o = 0.f, l = 0.f;
+  if (mx != -INFINITY) {
+    for (int k = 0; k < S; ++k) {
+      const float2 p = ml[k];
+      const float w = p.x == -INFINITY ? 0.f : __expf(p.x - mx);
+      l += p.y * w;
+      o += a.sparse ? po[(size_t)k * kD + i] : po[(size_t)k * kD + i] * w;
+    }
+    if (!a.sparse) o /= l;
+  }
+  buf[i] = o;
+  block_fwht128(buf, 1);
+  const float r = buf[i] * kInvSqrtD;
+  a.out[((size_t)b * a.n_q_heads + hq) * kD + i] = a.k.signs[i] < 0 ? -r : r;
+  if (i == 0 && a.lse != nullptr)
+    a.lse[(size_t)b * a.n_q_heads + hq] = mx == -INFINITY ? -INFINITY : mx + __logf(l);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
+  decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.sparse) {
+    decode_sparse_v<<<grid_split, 256, 0, stream>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  decode_merge<<<dim3(a.n_q_heads, a.batch), 128, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

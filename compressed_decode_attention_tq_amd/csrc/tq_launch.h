@@ -1,0 +1,56 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include "tq_common.h"
+
+namespace tq {
+
+// Split-context geometry of one decode call.  Every split covers `split_len` tokens
+// (a multiple of kSplitAlign) of one (batch, kv head); the number of splits is chosen
+// so the grid has enough blocks for the chip.  The same function sizes the workspace.
+constexpr int kSplitAlign = 256;
+
+struct SplitPlan {
+  int n_splits;
+  int split_len;
+};
+
+SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len);
+
+// Workspace layout (byte offsets, 256-byte aligned sections).
+struct WorkspaceLayout {
+  size_t part_ml;     // float2 [batch][n_q_heads][n_splits]      (m, l) per split
+  size_t part_o;      // float  [batch][n_q_heads][n_splits][128] rotated-domain sums
+  size_t cand_count;  // int    [batch][n_kv_heads][n_splits]      Sparse-V candidates
+  size_t cand;        // float  [batch][n_kv_heads][n_splits][split_len][1 + g]
+  size_t total;
+};
+
+WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
+                                 bool sparse);
+
+struct DecodeArgs {
+  CacheView k, v;
+  const void *q;
+  int q_dtype;
+  int batch, n_q_heads, n_kv_heads, group;
+  const int32_t *seq_lens;
+  int ctx_len;
+  float scale;
+  float ln_tau;  // log(tau), only read when sparse
+  int sparse;
+  SplitPlan plan;
+  float *out, *lse, *scores;
+  float2 *part_ml;
+  float *part_o;
+  int *cand_count;
+  float *cand;
+};
+
+hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
+                           int start_pos, int n_tokens, hipStream_t stream);
+hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
+                             int start_pos, int n_tokens, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace tq

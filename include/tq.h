@@ -1,0 +1,174 @@
+/*
+ * tq.h - C ABI of the TurboQuant compressed-KV library for AMD Instinct MI355X (gfx950).
+ *
+ * Two halves of one data-parallel hot path:
+ *   - quantize: every K or V head vector x (d = 128) is rotated by a random-sign
+ *     Walsh-Hadamard transform R = H diag(s) / sqrt(d), its L2 norm is split off and
+ *     stored as fp16, and each coordinate of the unit direction u = R x / ||x|| is
+ *     mapped to the nearest entry of a data-independent Lloyd-Max codebook of
+ *     2^bits levels; the codes are bit-packed.
+ *   - decode attention: one query per (batch, query head) is scored directly
+ *     against the packed keys in the rotated domain,
+ *         s_t = scale * ||k_t|| * (R q) . c_K[idx_t],
+ *     followed by a softmax, optional Sparse-V row skipping, accumulation of
+ *     p_t * ||v_t|| * c_V[idx_v_t] in the rotated domain and one inverse rotation.
+ *
+ * Source pages (cited by title and section):
+ *   [inferrs]  "inferrs & TurboQuant：本地 LLM 推理的内存革命" - §核心技术 (Walsh-Hadamard
+ *              rotation before quantization), table §压缩格式对比 (2/3/4-bit formats),
+ *              §三个反直觉的关键发现 (K/V asymmetry, boundary layers), §Sparse V (skip the
+ *              decode of V positions with low attention weight).
+ *   [tq-80]    "TurboQuant：让大模型本地推理内存占用降低80%的KV缓存压缩技术" - §核心创新
+ *              (random orthogonal rotation, Beta-distributed coordinates, precomputed
+ *              Lloyd-Max codebooks, norm kept as fp16), §tqai项目 (bits_k / bits_v),
+ *              §配置策略与质量权衡 (K4/V2, K3/V2, K4/V3).
+ *   [tq-plus]  "TurboQuant+：跨平台KV缓存压缩技术助力本地LLM高效推理" - §KV缓存的作用与开销
+ *              (cache size = 2 * layers * heads * head_dim * length * bytes).
+ *   [tq-fwht]  "TurboQuant：用Rust核心与FWHT预处理实现LLM推理的4-bit KV缓存量化" - §2 FWHT
+ *              (orthogonal, exactly invertible transform before 4-bit quantization).
+ *   [google]   "Google 最新極限壓縮算法，砸碎大模型本地部署的內存墻，8 倍提升！" - the list of
+ *              mlx-vlm kernels (score against quantized keys, pack / unpack low-bit codes,
+ *              multi-head weighted sum in the rotated domain) and the 4-bit-key speed-up.
+ *
+ * Conventions shared by every call:
+ *   - Status: 0 = TQ_OK, negative = error (enum tq_status).  Nothing throws across
+ *     the ABI.  All argument validation happens before any HIP call, so invalid
+ *     arguments are reported without touching the GPU.
+ *   - Memory: every buffer is allocated and owned by the caller.  Pointers named
+ *     "device" must be device memory of the current HIP device.  The library keeps
+ *     no global state and allocates nothing.
+ *   - Asynchrony: device work is enqueued on `hip_stream` (a hipStream_t, NULL =
+ *     the null stream) and the call returns without waiting.  Only launch errors
+ *     are returned (TQ_ERR_HIP); faults surface at the caller's next sync.
+ *   - Head dim d must be 128.  Code widths: bits in {2, 3, 4, 8}.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* null or misaligned pointer, negative size, bad enum, NaN */
+  TQ_ERR_UNSUPPORTED = -2, /* valid in principle but not implemented (d != 128, bits, group) */
+  TQ_ERR_CAPACITY = -3,    /* token range or context longer than the cache capacity */
+  TQ_ERR_WORKSPACE = -4,   /* workspace smaller than tq_decode_workspace_bytes() */
+  TQ_ERR_HIP = -5          /* a HIP launch failed */
+};
+
+enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 };
+
+/* Packed-code layouts inside one (batch, kv head) plane of `capacity` tokens.
+ * Bit k of the code of (token t, rotated coordinate i) sits at bit offset
+ *   TQ_LAYOUT_ROWS:   t*d*bits + i*bits + k
+ *   TQ_LAYOUT_GROUP8: (t/8)*d*8*bits + (i*8 + t%8)*bits + k
+ * of the plane, byte = offset >> 3, bit within byte = offset & 7 (LSB first).
+ * ROWS keeps one vector's codes in one d*bits/8-byte row (how the keys are read);
+ * GROUP8 puts the codes of 8 consecutive tokens for one coordinate next to each
+ * other (how the values are read when they are summed over tokens).  Both use
+ * exactly d*bits/8 bytes per vector.  Decode attention needs K in ROWS and V in
+ * GROUP8; quantize and dequantize accept either. */
+enum tq_layout { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_GROUP8 = 1 };
+
+/* One K or V cache of one layer.  Every pointer is device memory owned by the caller.
+ *   codes       [batch][n_kv_heads][capacity * d * bits / 8] bytes, 16-byte aligned
+ *   norms       [batch][n_kv_heads][capacity] IEEE fp16 bit patterns, 16-byte aligned
+ *   centroids   [1 << bits] fp32, ascending (from tq_make_codebook_table)
+ *   boundaries  [(1 << bits) - 1] fp32 midpoints (from tq_make_codebook_table)
+ *   signs       [d] int8, each +1 or -1: the diagonal of the rotation (shared by the
+ *               K and V caches of a layer)
+ * capacity must be a positive multiple of 64. */
+typedef struct tq_cache {
+  int32_t d;
+  int32_t bits;
+  int32_t layout;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t capacity;
+  uint8_t *codes;
+  uint16_t *norms;
+  const float *centroids;
+  const float *boundaries;
+  const int8_t *signs;
+} tq_cache;
+
+/* Lloyd-Max codebook for the marginal density of one coordinate of a random unit
+ * vector in R^d, f(x) proportional to (1 - x^2)^((d-3)/2) on [-1, 1] ([tq-80] §核心创新:
+ * rotated coordinates are Beta distributed; the codebook is data-independent and
+ * precomputed).  Host-only, no GPU: computed in fp64 (Lloyd iterations refined by
+ * Newton steps on the Lloyd fixed point), symmetrised, rounded to fp32.
+ *   centroids   host out [1 << bits], ascending
+ *   boundaries  host out [(1 << bits) - 1], midpoints of adjacent centroids
+ * Errors: TQ_ERR_INVALID_ARG (null pointer, d < 4), TQ_ERR_UNSUPPORTED (bits outside 1..8). */
+int tq_make_codebook_table(int d, int bits, float *centroids, float *boundaries);
+
+/* Quantize n_tokens new tokens of every (batch, kv head) into cache positions
+ * [start_pos, start_pos + n_tokens) ([tq-80] §核心创新; [inferrs] §核心技术):
+ *   n = ||x||_2 (fp32), norm stored as fp16 (round to nearest even),
+ *   u = R x / n (u = 0 for a zero vector), code = #{ j : boundaries[j] < u_i },
+ *   codes packed in the cache's layout.
+ *   x      device in [batch][n_tokens][n_kv_heads][d] of x_dtype (TQ_F32/TQ_BF16/TQ_F16),
+ *          16-byte aligned
+ * Positions outside the range are left untouched (a GROUP8 cache is read-modified-
+ * written at the edges of the range).  Calls that overlap on one cache race.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
+ * (start_pos < 0 or start_pos + n_tokens > capacity), TQ_ERR_HIP. */
+int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_pos,
+                       int n_tokens, void *hip_stream);
+
+/* Decode attention against the packed cache, one query per (batch, query head).
+ * Query head h reads kv head h / (n_q_heads / n_kv_heads).  For each (b, h) with
+ * T = seq_lens ? clamp(seq_lens[b], 0, ctx_len) : ctx_len tokens:
+ *   s_t  = scale * ||k_t||_fp16 * (R q) . c_K[idx_t]                    ([google] score kernel)
+ *   LSE  = log sum_t exp(s_t),  p_t = exp(s_t - LSE)
+ *   o    = R^T sum_t keep_t p_t ||v_t||_fp16 c_V[idx_v_t]                 ([google] weighted
+ *                                                                        rotated sum; [tq-fwht] §2)
+ * with keep_t = 1 when sparse_v_tau == 0 and keep_t = (p_t >= sparse_v_tau) otherwise
+ * ([inferrs] §Sparse V; no renormalisation, o = 0 when every row is dropped).
+ *   k, v       caches of one layer; k in TQ_LAYOUT_ROWS, v in TQ_LAYOUT_GROUP8; they must
+ *              agree on d, batch, n_kv_heads, capacity and signs (bits may differ)
+ *   q          device in [batch][n_q_heads][d] of q_dtype, 16-byte aligned
+ *   n_q_heads  a multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16
+ *   seq_lens   device int32 [batch] or NULL
+ *   ctx_len    0 <= ctx_len <= capacity
+ *   scale      finite softmax scale (1/sqrt(d) in the usual case)
+ *   sparse_v_tau  0 (dense) or a threshold in (0, 1)
+ *   out        device out [batch][n_q_heads][d] fp32, 16-byte aligned
+ *   lse        device out [batch][n_q_heads] fp32 or NULL (-inf when T = 0)
+ *   scores     device out [batch][n_q_heads][ctx_len] fp32 or NULL (s_t; -inf past T)
+ *   workspace  device scratch of at least tq_decode_workspace_bytes(...) bytes,
+ *              256-byte aligned; contents on entry are ignored
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
+                   int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
+                   float sparse_v_tau, float *out, float *lse, float *scores, void *workspace,
+                   size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes tq_decode_attn needs for this problem (0 for invalid arguments). */
+size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
+                                 float sparse_v_tau);
+
+/* Reconstruct x_hat = ||x||_fp16 * R^T c[idx] for cache positions
+ * [start_pos, start_pos + n_tokens) ([google] unpack kernel; [tq-fwht] §2 invertibility).
+ *   out  device out [batch][n_tokens][n_kv_heads][d] of out_dtype, 16-byte aligned
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+int tq_dequantize(const tq_cache *c, int start_pos, int n_tokens, void *out, int out_dtype,
+                  void *hip_stream);
+
+/* Bytes of the packed-code buffer of a cache: batch * n_kv_heads * capacity * d * bits / 8
+ * ([tq-plus] §KV缓存的作用与开销 with d*bits/8 bytes per vector); 0 for invalid arguments. */
+size_t tq_code_bytes(int d, int bits, int batch, int n_kv_heads, int capacity);
+
+/* Static description of a status code. */
+const char *tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,131 @@
+"""CPU-only checks of the C-ABI library: it loads, exports what include/tq.h declares,
+its host codebook equals the oracle's, and argument validation rejects bad calls
+before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_decode_attention_tq_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tq.lib()
+    names = _declared_symbols()
+    assert {"tq_make_codebook_table", "tq_quantize_append", "tq_decode_attn", "tq_dequantize",
+            "tq_decode_workspace_bytes", "tq_status_string", "tq_code_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_host_codebook_equals_oracle_table(bits, golden_codebooks):
+    c, t = tq.make_codebook_table(128, bits)
+    gc, gt = golden_codebooks[bits]
+    assert np.array_equal(c, gc.astype(np.float32))
+    assert np.array_equal(t, gt.astype(np.float32))
+
+
+def test_codebook_argument_errors():
+    c = np.zeros(16, np.float32)
+    L = tq.lib()
+    assert L.tq_make_codebook_table(128, 9, c.ctypes.data, c.ctypes.data) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_make_codebook_table(128, 4, None, c.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_make_codebook_table(2, 4, c.ctypes.data, c.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_status_strings_and_sizes():
+    assert tq.status_string(0) == "ok"
+    assert "workspace" in tq.status_string(tq.TQ_ERR_WORKSPACE)
+    assert tq.code_bytes(128, 4, 2, 8, 1024) == 2 * 8 * 1024 * 64
+    assert tq.code_bytes(128, 3, 1, 1, 64) == 64 * 48
+    assert tq.decode_workspace_bytes(1, 32, 8, 8192, 0.0) > 0
+    assert tq.decode_workspace_bytes(1, 32, 8, 8192, 1e-4) > tq.decode_workspace_bytes(1, 32, 8, 8192, 0.0)
+    assert tq.decode_workspace_bytes(1, 30, 8, 8192, 0.0) == 0       # group not integral
+    assert tq.decode_workspace_bytes(1, 32, 8, -1, 0.0) == 0
+    assert tq.decode_workspace_bytes(1, 32, 8, 8192, 1.0) == 0
+    assert tq.decode_workspace_bytes(1, 32, 8, 8192, float("nan")) == 0
+
+
+# Fake, suitably aligned addresses: validation fails before anything dereferences them.
+FAKE = 0x7F0000000000
+
+
+def _cache(**kw):
+    base = dict(d=128, bits=4, layout=0, batch=1, n_kv_heads=2, capacity=1024,
+                codes=FAKE, norms=FAKE + 0x100000, centroids=FAKE + 0x200000,
+                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000)
+    base.update(kw)
+    return tq.CacheStruct(base["d"], base["bits"], base["layout"], base["batch"], base["n_kv_heads"],
+                          base["capacity"], base["codes"], base["norms"], base["centroids"],
+                          base["boundaries"], base["signs"])
+
+
+def _quant(cache, x=FAKE + 0x500000, dtype=1, start=0, n=16):
+    return tq.lib().tq_quantize_append(ctypes.byref(cache), x, dtype, start, n, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(bits=5), tq.TQ_ERR_UNSUPPORTED),
+    (dict(bits=1), tq.TQ_ERR_UNSUPPORTED),
+    (dict(layout=7), tq.TQ_ERR_INVALID_ARG),
+    (dict(batch=0), tq.TQ_ERR_INVALID_ARG),
+    (dict(capacity=1000), tq.TQ_ERR_UNSUPPORTED),
+    (dict(codes=0), tq.TQ_ERR_INVALID_ARG),
+    (dict(codes=FAKE + 4), tq.TQ_ERR_INVALID_ARG),
+    (dict(norms=FAKE + 2), tq.TQ_ERR_INVALID_ARG),
+    (dict(signs=0), tq.TQ_ERR_INVALID_ARG),
+])
+def test_quantize_rejects_bad_cache(kw, status):
+    assert _quant(_cache(**kw)) == status
+
+
+def test_quantize_rejects_bad_ranges():
+    c = _cache()
+    assert _quant(c, start=-1) == tq.TQ_ERR_INVALID_ARG
+    assert _quant(c, n=-3) == tq.TQ_ERR_INVALID_ARG
+    assert _quant(c, start=1000, n=25) == tq.TQ_ERR_CAPACITY
+    assert _quant(c, dtype=9) == tq.TQ_ERR_INVALID_ARG
+    assert _quant(c, x=0) == tq.TQ_ERR_INVALID_ARG
+    assert _quant(c, x=FAKE + 0x500008) == tq.TQ_ERR_INVALID_ARG
+    assert _quant(c, n=0) == tq.TQ_OK            # nothing to do, no launch
+    assert tq.lib().tq_dequantize(ctypes.byref(c), 1020, 8, FAKE, 0, None) == tq.TQ_ERR_CAPACITY
+    assert tq.lib().tq_dequantize(ctypes.byref(c), 0, 8, FAKE, 5, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def _decode(k, v, q=FAKE + 0x600000, hq=8, seq=None, ctx=512, scale=0.088, tau=0.0,
+            out=FAKE + 0x700000, ws=FAKE + 0x800000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = tq.decode_workspace_bytes(k.batch, hq, k.n_kv_heads, max(ctx, 0), tau) or 1
+    return tq.lib().tq_decode_attn(ctypes.byref(k), ctypes.byref(v), q, 1, hq, seq, ctx, scale, tau,
+                                   out, None, None, ws, ws_bytes, None)
+
+
+def test_decode_argument_validation():
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+    assert _decode(k, v, hq=7) == tq.TQ_ERR_INVALID_ARG            # not a multiple of n_kv_heads
+    assert _decode(k, v, hq=64) == tq.TQ_ERR_UNSUPPORTED           # group 32 > 16
+    assert _decode(k, v, ctx=2048) == tq.TQ_ERR_CAPACITY
+    assert _decode(k, v, ctx=-1) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, tau=1.5) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, tau=float("nan")) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, scale=float("inf")) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    assert _decode(k, v, ws=FAKE + 0x800010) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, out=0) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, q=FAKE + 0x600002) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, _cache(layout=0, bits=2)) == tq.TQ_ERR_UNSUPPORTED   # V must be GROUP8
+    assert _decode(k, _cache(layout=1, bits=2, capacity=2048)) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, _cache(layout=1, bits=2, signs=FAKE + 0x400100)) == tq.TQ_ERR_INVALID_ARG
+    assert _decode(k, v, seq=FAKE + 0x900002) == tq.TQ_ERR_INVALID_ARG

@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes are ones the oracle finishes in seconds but that still span several 64-token chunks,
+several 256-token decode steps and splits, and ragged tails.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import compressed_decode_attention_tq_amd as tq  # noqa: E402
+from compressed_decode_attention_tq_amd import inputs  # noqa: E402
+from oracle import tq_oracle as o  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def signs():
+    return inputs.rotation_signs()
+
+
+def _table(golden, bits):
+    return golden[bits]
+
+
+_SIGNS_DEV = {}
+
+
+def _new_cache(batch, hkv, cap, bits, layout, signs):
+    key = tuple(signs.tolist())
+    if key not in _SIGNS_DEV:
+        _SIGNS_DEV[key] = signs.to(DEV)
+    return tq.PackedCache(batch, hkv, cap, bits, layout, _SIGNS_DEV[key], device=DEV)
+
+
+def _fill(cache, x, start=0):
+    tq.quantize_append(cache, x, start)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ quantize
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_quantize_matches_oracle(bits, layout, dtype, signs, golden_codebooks):
+    _say("quantize", bits, layout, dtype)
+    w = inputs.WORKLOADS["llama8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=200, n_kv_heads=3, with_query=False)
+    x = g["k"].to({"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[dtype])
+    cache = _new_cache(2, 3, 256, bits, layout, signs)
+    _fill(cache, x.to(DEV))
+    s64 = signs.numpy().astype(np.float64)
+    parity.check_quantize(cache, parity.to_f64(x), 0, s64, _table(golden_codebooks, bits))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_append_in_pieces_keeps_earlier_tokens(layout, bits, signs, golden_codebooks):
+    """Ragged appends (including single tokens inside an 8-token group) read-modify-write
+    the edges of the range and leave every other position untouched."""
+    _say("append pieces", layout, bits)
+    w = inputs.WORKLOADS["batch32k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=203, n_kv_heads=2, with_query=False)
+    x = g["v"]
+    cache = _new_cache(2, 2, 256, bits, layout, signs)
+    for a, e in [(0, 37), (37, 38), (38, 101), (101, 190), (190, 191), (191, 203)]:
+        tq.quantize_append(cache, x[:, a:e].contiguous().to(DEV), a)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    parity.check_quantize(cache, parity.to_f64(x), 0, s64, _table(golden_codebooks, bits))
+
+
+def test_quantize_special_vectors(signs, golden_codebooks):
+    """Basis vectors, the all-ones vector (exact ties on the middle boundary) and zeros."""
+    _say("special vectors")
+    x = torch.zeros((1, 64, 1, 128), dtype=torch.float32)
+    for j in range(60):
+        x[0, j, 0, (j * 37) % 128] = 1.0 + j
+    x[0, 60, 0, :] = 1.0
+    x[0, 62, 0, :] = -2.0
+    plus = torch.ones(128, dtype=torch.int8)
+    for bits in (2, 3, 4, 8):
+        cache = _new_cache(1, 1, 64, bits, 0, plus)
+        _fill(cache, x.to(DEV))
+        codes, _ = parity.gpu_plane_codes(cache, 0, 0, 64)
+        c, t = _table(golden_codebooks, bits)
+        ref, n16, _ = o.quantize(parity.to_f64(x)[0, :, 0], np.ones(128), c, t)
+        assert np.array_equal(codes, ref)          # no value is near a boundary except exact ties
+        levels = 1 << bits
+        assert codes[60, 0] == levels - 1 and np.all(codes[60, 1:] == levels // 2 - 1)
+        assert np.all(codes[61] == levels // 2 - 1)      # zero vector
+        norms = parity.gpu_plane_norms(cache, 0, 0, 64).astype(np.float64)
+        assert norms[61] == 0.0 and norms[60] == float(np.float16(math.sqrt(128)))
+        assert np.array_equal(norms[:60], 1.0 + np.arange(60))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_dequantize_matches_oracle(layout, signs, golden_codebooks):
+    _say("dequantize", layout)
+    w = inputs.WORKLOADS["llama8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=150, n_kv_heads=2, with_query=False)
+    for bits in (2, 4, 8):
+        cache = _new_cache(2, 2, 192, bits, layout, signs)
+        _fill(cache, g["k"].to(DEV))
+        got = tq.dequantize(cache, 10, 130)
+        torch.cuda.synchronize()
+        ref = parity.oracle_cache_view(cache, signs.numpy().astype(np.float64),
+                                       _table(golden_codebooks, bits), 140)[:, :, 10:140]
+        parity.check_rows(parity.to_f64(got).transpose(0, 2, 1, 3), ref, f"dequantize b{bits}")
+
+
+# ------------------------------------------------------------------ decode
+
+
+def _decode_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, tau=0.0,
+                 seq_lens=None, q_dtype=None, scale=None):
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
+    kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
+    vc = _new_cache(batch, hkv, cap, bits_v, 1, signs)
+    _fill(kc, g["k"].to(DEV))
+    _fill(vc, g["v"].to(DEV))
+    q = g["q"] if q_dtype is None else g["q"].to(q_dtype)
+    scale = 1.0 / math.sqrt(128) if scale is None else scale
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    buf = tq.decode_attn(kc, vc, q.to(DEV).contiguous(), ctx, scale, tau=tau, seq_lens=sl,
+                         want_scores=True)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    kh = parity.oracle_cache_view(kc, s64, golden[bits_k], ctx)
+    vh = parity.oracle_cache_view(vc, s64, golden[bits_v], ctx)
+    out, lse, scores = o.decode_attention(parity.to_f64(q), kh, vh, scale, seq_lens=seq_lens, tau=tau)
+    got_scores = buf.scores.cpu().numpy()
+    parity.check_scores(got_scores, scores, seq_lens)
+    fin = np.isfinite(lse)
+    assert np.all(np.isneginf(buf.lse.cpu().numpy()[~fin]))
+    assert np.allclose(buf.lse.cpu().numpy()[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    allowance, nb = None, 0
+    if tau > 0:
+        allowance, nb = parity.sparse_allowance(scores, lse, vh, tau, hq // hkv)
+    worst = parity.check_rows(buf.out.cpu().numpy(), out, "decode out", allowance=allowance)
+    _say(f"  worst rel err {worst:.2e} borderline {nb}")
+    return buf, out
+
+
+def test_decode_tiny_workload(signs, golden_codebooks):
+    """The smallest workload exactly as stated: 1 kv head, 1 query head, 1024 fp32 tokens."""
+    _say("decode tiny")
+    w = inputs.WORKLOADS["tiny"]
+    _decode_case(w, signs, golden_codebooks, 1, 1, 1, 1024, 1024, 4, 2)
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, bits_v)
+    ("llama8k", 1, 32, 8, 700, 768, 4, 2),
+    ("llama8k", 2, 8, 2, 1000, 1024, 4, 2),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 2),
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 2),
+    ("ctx131k", 1, 16, 1, 600, 640, 4, 3),
+    ("llama8k", 1, 2, 2, 333, 384, 8, 8),
+    ("llama8k", 1, 4, 2, 64, 64, 2, 4),
+    ("llama8k", 1, 16, 1, 500, 512, 4, 2),
+])
+def test_decode_dense_matches_oracle(case, signs, golden_codebooks):
+    name, *shape = case
+    _say("decode dense", case)
+    _decode_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape)
+
+
+def test_decode_seq_lens_and_query_dtypes(signs, golden_codebooks):
+    _say("decode seq_lens")
+    w = inputs.WORKLOADS["llama8k"]
+    _decode_case(w, signs, golden_codebooks, 4, 8, 2, 900, 960, 4, 2, seq_lens=[900, 0, 1, 513])
+    _decode_case(w, signs, golden_codebooks, 2, 8, 2, 300, 320, 4, 2, q_dtype=torch.float32)
+    _decode_case(w, signs, golden_codebooks, 2, 8, 2, 300, 320, 4, 2, q_dtype=torch.float16, scale=0.3)
+
+
+def test_decode_empty_context(signs, golden_codebooks):
+    _say("decode empty")
+    kc = _new_cache(1, 2, 64, 4, 0, signs)
+    vc = _new_cache(1, 2, 64, 2, 1, signs)
+    q = torch.randn((1, 4, 128), device=DEV)
+    buf = tq.decode_attn(kc, vc, q, 0, 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(buf.out == 0) and torch.all(torch.isneginf(buf.lse))
+
+
+@pytest.mark.parametrize("case", [
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 2, 1e-4),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 2, 1e-4),
+    ("llama8k", 1, 8, 2, 777, 832, 4, 2, 1e-2),
+    ("ctx131k", 1, 16, 1, 700, 704, 4, 2, 0.3),
+])
+def test_decode_sparse_v_matches_oracle(case, signs, golden_codebooks):
+    name, *shape, tau = case
+    _say("decode sparse", case)
+    _decode_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, tau=tau)
+
+
+def test_decode_is_deterministic(signs):
+    _say("determinism")
+    w = inputs.WORKLOADS["llama8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=900, n_kv_heads=2, n_q_heads=8)
+    kc = _new_cache(2, 2, 960, 4, 0, signs)
+    vc = _new_cache(2, 2, 960, 2, 1, signs)
+    _fill(kc, g["k"].to(DEV))
+    _fill(vc, g["v"].to(DEV))
+    q = g["q"].to(DEV)
+    for tau in (0.0, 1e-3):
+        a = tq.decode_attn(kc, vc, q, 900, 0.0884, tau=tau).out.clone()
+        b = tq.decode_attn(kc, vc, q, 900, 0.0884, tau=tau).out.clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
