@@ -70,14 +70,6 @@ __global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
   for (int i = tid; i < (1 << bv); i += blockDim.x) lutV[i] = a.v.centroids[i];
   load_rotated_queries(a, b, kvh, qt);
 
-  if (a.scores != nullptr) {  // positions past the sequence length read -inf
-    const int pad_end = min(t_begin + a.plan.split_len, a.ctx_len);
-    for (int e = max(t_begin, T) * g + tid; e < pad_end * g; e += blockDim.x) {
-      const int t = e / g, j = e % g;
-      a.scores[((size_t)b * a.n_q_heads + kvh * g + j) * a.ctx_len + t] = -INFINITY;
-    }
-  }
-
   float m_run[4], l_run[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
@@ -304,45 +296,115 @@ __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
 }
 
 // LSE merge of the split partials, normalisation and the inverse rotation R^T.
-__global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+// Block (query head, batch) of 512 threads: 4 groups of 128 (one coordinate per thread)
+// take every 4th split, with independent loads unrolled so the latency overlaps.
+constexpr int kMergeGroups = 4;
+
+__global__ __launch_bounds__(128 * kMergeGroups) void decode_merge(DecodeArgs a) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int i = threadIdx.x & (kD - 1), grp = threadIdx.x >> 7;
   const int S = a.plan.n_splits;
   const float2 *ml = a.part_ml + ((size_t)b * a.n_q_heads + hq) * S;
   const float *po = a.part_o + ((size_t)b * a.n_q_heads + hq) * S * kD;
+  __shared__ float red_m[kMergeGroups * 2];
+  __shared__ float red_l[kMergeGroups];
+  __shared__ float red_o[kMergeGroups][kD];
   __shared__ float buf[kD];
+
   float mx = -INFINITY;
-  for (int k = 0; k < S; ++k) mx = fmaxf(mx, ml[k].x);
+  for (int k = threadIdx.x; k < S; k += blockDim.x) mx = fmaxf(mx, ml[k].x);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  if ((threadIdx.x & 63) == 0) red_m[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kMergeGroups * 2; ++w) mx = fmaxf(mx, red_m[w]);
+
   float o = 0.f, l = 0.f;
   if (mx != -INFINITY) {
-    for (int k = 0; k < S; ++k) {
+    int k = grp;
+    for (; k + 3 * kMergeGroups < S; k += 4 * kMergeGroups) {
+      float2 p[4];
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = ml[k + u * kMergeGroups];
+        v[u] = po[(size_t)(k + u * kMergeGroups) * kD + i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = p[u].x == -INFINITY ? 0.f : __expf(p[u].x - mx);
+        l += p[u].y * w;
+        o += a.sparse ? v[u] : v[u] * w;
+      }
+    }
+    for (; k < S; k += kMergeGroups) {
       const float2 p = ml[k];
       const float w = p.x == -INFINITY ? 0.f : __expf(p.x - mx);
       l += p.y * w;
       o += a.sparse ? po[(size_t)k * kD + i] : po[(size_t)k * kD + i] * w;
     }
-    if (!a.sparse) o /= l;
   }
-  buf[i] = o;
+  red_o[grp][i] = o;
+  if (i == 0) red_l[grp] = l;
+  __syncthreads();
+  if (grp == 0) {
+    float ot = red_o[0][i], lt = red_l[0];
+#pragma unroll
+    for (int q = 1; q < kMergeGroups; ++q) {
+      ot += red_o[q][i];
+      lt += red_l[q];
+    }
+    if (mx != -INFINITY && !a.sparse) ot /= lt;
+    if (mx == -INFINITY) ot = 0.f;
+    buf[i] = ot;
+    if (i == 0 && a.lse != nullptr)
+      a.lse[(size_t)b * a.n_q_heads + hq] = mx == -INFINITY ? -INFINITY : mx + __logf(lt);
+  }
+  if (a.scores != nullptr) {  // positions past the sequence length read -inf
+    const int T = seq_len_of(a, b);
+    float *row = a.scores + ((size_t)b * a.n_q_heads + hq) * a.ctx_len;
+    for (int t = T + (int)threadIdx.x; t < a.ctx_len; t += blockDim.x) row[t] = -INFINITY;
+  }
   block_fwht128(buf, 1);
-  const float r = buf[i] * kInvSqrtD;
-  a.out[((size_t)b * a.n_q_heads + hq) * kD + i] = a.k.signs[i] < 0 ? -r : r;
-  if (i == 0 && a.lse != nullptr)
-    a.lse[(size_t)b * a.n_q_heads + hq] = mx == -INFINITY ? -INFINITY : mx + __logf(l);
+  if (grp == 0) {
+    const float r = buf[i] * kInvSqrtD;
+    a.out[((size_t)b * a.n_q_heads + hq) * kD + i] = a.k.signs[i] < 0 ? -r : r;
+  }
 }
 
 }  // namespace
 
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
-  decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (decode_mfma_supported(a)) {
+    e = launch_decode_mfma(a, compute_units(), stream);
+  } else {
+    decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   if (a.sparse) {
     decode_sparse_v<<<grid_split, 256, 0, stream>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  decode_merge<<<dim3(a.n_q_heads, a.batch), 128, 0, stream>>>(a);
+  decode_merge<<<dim3(a.n_q_heads, a.batch), 128 * kMergeGroups, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@ namespace tq {
 // Split-context geometry of one decode call.  Every split covers `split_len` tokens
 // (a multiple of kSplitAlign) of one (batch, kv head); the number of splits is chosen
 // so the grid has enough blocks for the chip.  The same function sizes the workspace.
-constexpr int kSplitAlign = 256;
+constexpr int kSplitAlign = 64;
 
 struct SplitPlan {
   int n_splits;
@@ -52,5 +52,7 @@ hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_d
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+bool decode_mfma_supported(const DecodeArgs &a);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int n_cu, hipStream_t stream);
 
 }  // namespace tq
