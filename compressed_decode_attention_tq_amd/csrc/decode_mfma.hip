@@ -1,22 +1,24 @@
 // Decode attention on matrix cores (gfx950 v_mfma_f32_16x16x32_f16) for the common code
-// widths: keys 3 or 4 bits (TQ_LAYOUT_ROWS), values 2 bits (TQ_LAYOUT_GROUP8).
+// widths: keys 3 or 4 bits (TQ_LAYOUT_ROWS), values 2 bits (TQ_LAYOUT_GROUP8), query group
+// up to 8 heads per kv head.
 //
 // What is computed is the same as the generic kernels ([google] "Google 最新極限壓縮算法…":
 // scores taken directly against the quantized keys, values summed in the rotated domain);
 // only the schedule differs:
 //   * Codes become fp16 operands through lookup tables in LDS.  A key byte (two 4-bit codes,
-//     or a 6-bit pair of 3-bit codes) gives the two centroids as fp16 hi parts plus fp16 lo
-//     parts; a value byte (four 2-bit codes of one coordinate, four
-//     consecutive tokens) gives four fp16 centroids.  Tables are replicated 32 times so the
-//     32 lanes of one LDS pass never share a bank; one v_perm builds a lookup address.
-//   * Scores: S[head][token] = Qrot . K per 16-token sub-tile with the rotated query and the
-//     centroids each split into fp16 hi + lo parts: hi*hi + lo*hi + hi*lo, three matrix-core
-//     products into one fp32 accumulator, about 22 significant bits, which keeps large-norm
-//     scores accurate enough for the exponentials (the lo parts are often fp16 subnormals,
-//     which the matrix cores take as they are).  Scores are then compacted through LDS to
-//     one token per lane.
-//   * Values: O[head][coord] += P'[head][token] V[token][coord] with P' = p * ||v|| in fp16;
-//     the GROUP8 layout gives each lane 8 consecutive tokens of 8 coordinates in 16 bytes.
+//     or a 6-bit pair of 3-bit codes) gives {hi(c_a), hi(c_b), lo(c_a), lo(c_b)}, the two
+//     centroids split into an fp16 hi part and the fp16 remainder; a value byte (four 2-bit
+//     codes of one coordinate, four consecutive tokens) gives four fp16 centroids.  Tables
+//     are replicated 32 times so the 32 lanes of one LDS pass never share a bank; one
+//     v_perm builds a lookup address; two lookups form one 8-half operand as loaded.
+//   * Scores, about 22 significant bits: the query rows of the score product hold the
+//     rotated query's fp16 hi part (rows 0..G-1) and its remainder (rows G..2G-1), each
+//     repeated to match the {hi, hi, lo, lo} key operand, so one product gives
+//     (q_hi + q_lo) . (c_hi + c_lo) for 16 coordinates; the two row halves are summed when
+//     the scores are compacted through LDS to one token per lane.
+//   * Values: O[row][coord] += P'[row][token] V[token][coord] with P' = p * ||v|| split the
+//     same way into rows 0..G-1 (fp16 hi) and G..2G-1 (remainder); the GROUP8 layout gives
+//     each lane 8 consecutive tokens of 8 coordinates in 16 bytes.
 //   * Online softmax with a stale reference: p = exp(s - m_ref); m_ref only moves when a
 //     tile would push p * ||v|| past the fp16 range, so the accumulator is rarely rescaled.
 //   * Persistent workgroups, one per CU (160 KB of LDS), 8 waves each; a wave owns whole
@@ -35,13 +37,14 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 64;
 constexpr float kInvSqrtD = 0.08838834764831845f;
-constexpr float kAMax = 30000.f;        // largest p * ||v|| kept in an fp16 operand
+constexpr float kAMax = 30000.f;  // largest p * ||v|| kept in an fp16 operand
 
 // LDS map (bytes):
-//   [0, 64K)      K table: entry e at e*256 + copy*8 (copy < 32): {hi pair, lo pair}
-//   [64K, 128K)   V table: entry e at 64K + e*256 + copy*8 (copy < 32): 4 fp16
-//   [128K, 160K)  per-wave 4 KB buffer: scores [64 tokens][16 heads] fp32, then P'
-//                 [16 heads][64 tokens] fp16 (rows of 128 bytes)
+//   [0, 64K)      K table: entry e at e*256 + copy*8 (copy < 32)
+//   [64K, 128K)   V table: entry e at 64K + e*256 + copy*8 (copy < 32)
+//   [128K, 160K)  per-wave 4 KB buffer: scores [64 tokens][16 rows] fp32, then P'
+//                 [16 rows][64 tokens] fp16; both with XOR-swizzled 16-byte units so the
+//                 16 lanes of one LDS pass hit 16 different bank groups
 constexpr int kLdsBytes = 160 * 1024;
 constexpr uint32_t kVBase = 64 * 1024;
 constexpr uint32_t kWBase = 128 * 1024;
@@ -49,9 +52,17 @@ constexpr uint32_t kWBase = 128 * 1024;
 __device__ __forceinline__ uint2 lds_u64(const uint8_t *lds, uint32_t addr) {
   return *reinterpret_cast<const uint2 *>(lds + addr);
 }
-
 __device__ __forceinline__ uint16_t h16(float x) { return __half_as_ushort(__float2half_rn(x)); }
 __device__ __forceinline__ float f16(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// byte offset of score (token, 4-row group) inside the wave buffer
+__device__ __forceinline__ uint32_t score_off(int tok, int grp) {
+  return (uint32_t)tok * 64u + ((uint32_t)(grp ^ ((tok >> 2) & 3)) << 4);
+}
+// byte offset of the 16-byte unit (row, unit = tokens 8u .. 8u+7) of the P' staging
+__device__ __forceinline__ uint32_t pst_off(int row, int unit) {
+  return (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
+}
 
 template <int BK>
 __device__ void build_tables(uint8_t *lds, const float *kc, const float *vc) {
@@ -60,10 +71,9 @@ __device__ void build_tables(uint8_t *lds, const float *kc, const float *vc) {
     const float c0 = BK == 4 ? kc[e & 15] : kc[e & 7];
     const float c1 = BK == 4 ? kc[e >> 4] : kc[(e >> 3) & 7];
     const uint16_t h0 = h16(c0), h1 = h16(c1);
-    const uint16_t l0 = h16(c0 - f16(h0)), l1 = h16(c1 - f16(h1));
     uint2 kv;
     kv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    kv.y = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    kv.y = (uint32_t)h16(c0 - f16(h0)) | ((uint32_t)h16(c1 - f16(h1)) << 16);
     *reinterpret_cast<uint2 *>(lds + e * 256 + copy * 8) = kv;
     uint2 vv;
     vv.x = (uint32_t)h16(vc[e & 3]) | ((uint32_t)h16(vc[(e >> 2) & 3]) << 16);
@@ -83,10 +93,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// NH = query heads handled per lane (group padded to 4, 8 or 16); BK = key bits (3 or 4);
-// value bits are 2.
+// NH = query heads per kv head padded to 4 or 8; BK = key bits (3 or 4); value bits 2.
 template <int BK, int NH, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(NH == 4 || NH == 8, "two row halves of NH rows must fit 16 rows");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   build_tables<BK>(lds, a.k.centroids, a.v.centroids);
   __syncthreads();
@@ -97,7 +107,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const uint32_t kc8 = (uint32_t)(lane & 31) << 3;
   const uint32_t vc8 = ((uint32_t)(lane & 31) << 3) | 0x00010000u;  // + 64K table base
   uint8_t *wbuf = lds + kWBase + wave * 4096;
-  float *sbuf = reinterpret_cast<float *>(wbuf);                     // [64][16] fp32
+  // query row this lane feeds: hi part of head m_row, remainder of head m_row - NH, or 0
+  const int q_head = m_row < NH ? m_row : m_row - NH;
+  const bool q_is_lo = m_row >= NH;
+  const bool q_live = m_row < 2 * NH && q_head < g;
 
   const int n_items = a.batch * a.n_kv_heads * S;
   const int wave_id = blockIdx.x * kWaves + wave, n_waves = gridDim.x * kWaves;
@@ -111,15 +124,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int t_begin = split * a.plan.split_len;
     const int t_end = min(t_begin + a.plan.split_len, T);
 
-    // ---- rotated, scaled query of head m_row (rows >= g are zero), split hi + lo
-    half8 qhi[4], qlo[4];
+    // ---- rotated, scaled query (hi or lo part), each value repeated for {hi, hi, lo, lo}
+    half8 qop[8];
     {
       float v[32];
-      const bool hv = m_row < g;
-      const size_t qbase = ((size_t)b * a.n_q_heads + kvh * g + (hv ? m_row : 0)) * kD + 32 * quarter;
+      const size_t qbase = ((size_t)b * a.n_q_heads + kvh * g + (q_live ? q_head : 0)) * kD + 32 * quarter;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        const float x = hv ? load_elem(a.q, qbase + e, a.q_dtype) : 0.f;
+        const float x = q_live ? load_elem(a.q, qbase + e, a.q_dtype) : 0.f;
         v[e] = a.k.signs[32 * quarter + e] < 0 ? -x : x;
       }
 #pragma unroll
@@ -142,15 +154,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         }
       }
       const float qs = a.scale * kInvSqrtD;
+      _Float16 part[32];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int e = 0; e < 32; ++e) {
+        const float x = v[e] * qs;
+        const _Float16 hi = (_Float16)x;
+        part[e] = q_is_lo ? (_Float16)(x - (float)hi) : hi;
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = v[8 * r + e] * qs;
-          const _Float16 hi = (_Float16)x;
-          qhi[r][e] = hi;
-          qlo[r][e] = (_Float16)(x - (float)hi);
-        }
+      for (int m = 0; m < 8; ++m) {
+        qop[m][0] = part[4 * m];     qop[m][1] = part[4 * m + 1];
+        qop[m][2] = part[4 * m];     qop[m][3] = part[4 * m + 1];
+        qop[m][4] = part[4 * m + 2]; qop[m][5] = part[4 * m + 3];
+        qop[m][6] = part[4 * m + 2]; qop[m][7] = part[4 * m + 3];
+      }
     }
 
     float m_ref[NH], l_part[NH];
@@ -168,93 +185,95 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     int cand_written = 0;
     if (SPARSE) cand_base = a.cand + ((size_t)item) * (size_t)a.plan.split_len * (1 + g);
 
-    // ---- loads of one tile: key quarter rows (token 16s + m_row, coordinates
-    //      32q..32q+31), value groups, norms of token `lane`
-    uint32_t kw[4][4], kw_n[4][4];
-    uint4 vw[2], vw_n[2];
-    uint16_t nk_h = 0, nv_h = 0, nk_n = 0, nv_n = 0;
-    auto load_tile = [&](int tl, uint32_t (&kd)[4][4], uint4 (&vd)[2], uint16_t &nkh, uint16_t &nvh) {
+    // ---- tile loads: key quarter rows (token 16s + m_row, coordinates 32q..32q+31) and
+    //      key norms are fetched one tile ahead (issued as soon as the score products of
+    //      the previous tile have consumed them); value groups and value norms at the top of
+    //      the tile they belong to, ahead of the score products
+    uint32_t kw[4][4];
+    uint16_t nk_h = 0;
+    auto load_keys = [&](int t0) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint8_t *src = kplane + (size_t)(tl + 16 * s + m_row) * (16 * BK) + quarter * (4 * BK);
+        const uint8_t *src = kplane + (size_t)(t0 + 16 * s + m_row) * (16 * BK) + quarter * (4 * BK);
         if (BK == 4) {
           const uint4 w = *reinterpret_cast<const uint4 *>(src);
-          kd[s][0] = w.x; kd[s][1] = w.y; kd[s][2] = w.z; kd[s][3] = w.w;
+          kw[s][0] = w.x; kw[s][1] = w.y; kw[s][2] = w.z; kw[s][3] = w.w;
         } else {
           const uint32_t *pp = reinterpret_cast<const uint32_t *>(src);
-          kd[s][0] = pp[0]; kd[s][1] = pp[1]; kd[s][2] = pp[2]; kd[s][3] = 0u;
+          kw[s][0] = pp[0]; kw[s][1] = pp[1]; kw[s][2] = pp[2]; kw[s][3] = 0u;
         }
       }
+      nk_h = knorm[t0 + lane];
+    };
+    if (t_begin < t_end) load_keys(t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+      uint4 vw[2];
+      uint16_t nv_h = 0;
       if (!SPARSE) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const size_t grp8 = (size_t)(tl >> 3) + 4 * c + quarter;
-          vd[c] = *reinterpret_cast<const uint4 *>(vplane + grp8 * (kD * 2) + m_row * 16);
+          const size_t grp8 = (size_t)(t0 >> 3) + 4 * c + quarter;
+          vw[c] = *reinterpret_cast<const uint4 *>(vplane + grp8 * (kD * 2) + m_row * 16);
         }
-        nvh = vnorm[tl + lane];
-      }
-      nkh = knorm[tl + lane];
-    };
-    if (t_begin < t_end) load_tile(t_begin, kw, vw, nk_h, nv_h);
-
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-      if (t0 + kTile < t_end) load_tile(t0 + kTile, kw_n, vw_n, nk_n, nv_n);
-      if (BK == 3) {  // four 24-bit chunks of 8 codes each
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t p0 = kw[s][0], p1 = kw[s][1], p2 = kw[s][2];
-          kw[s][0] = p0 & 0xFFFFFFu;
-          kw[s][1] = ((p0 >> 24) | (p1 << 8)) & 0xFFFFFFu;
-          kw[s][2] = ((p1 >> 16) | (p2 << 16)) & 0xFFFFFFu;
-          kw[s][3] = p2 >> 8;
-        }
+        nv_h = vnorm[t0 + lane];
       }
       const bool tv = t0 + lane < t_end;
-      const float nk = half_bits_to_float(nk_h);
-      const float nv = SPARSE ? 1.f : half_bits_to_float(nv_h);
 
-      // ---- scores on matrix cores: four 16-token sub-tiles as independent accumulator
-      //      chains; per 32-coordinate chunk r, all lookups first, then hi*hi, lo*hi, hi*lo
+      // ---- scores: sub-tile s, 16-coordinate chunk m -> key fields 2m, 2m+1 of the quarter
+      auto key_operands = [&](int m, half8 (&dst)[4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint2 t2[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int f = 2 * m + p;  // field index within the quarter row
+            uint32_t addr;
+            if (BK == 4) {
+              addr = __builtin_amdgcn_perm(kw[s][f >> 2], kc8, 0x0C0C0000u | ((4u + (f & 3)) << 8));
+            } else {
+              const int bit = 6 * f;
+              uint32_t fld;
+              if ((bit & 31) <= 26) fld = (kw[s][bit >> 5] >> (bit & 31)) & 63u;
+              else fld = ((kw[s][bit >> 5] >> (bit & 31)) | (kw[s][(bit >> 5) + 1] << (32 - (bit & 31)))) & 63u;
+              addr = (fld << 8) | kc8;
+            }
+            t2[p] = lds_u64(lds, addr);
+          }
+          __builtin_memcpy(&dst[s], t2, 16);
+        }
+      };
       floatx4 acc[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+      half8 bop[2][4];
+      key_operands(0, bop[0]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        half8 bh[4], bl[4];
+      for (int m = 0; m < 8; ++m) {
+        // lookups of step m+1 go out before the products of step m, so their LDS latency
+        // hides behind four matrix instructions; the fence keeps the scheduler to this order
+        if (m + 1 < 8) key_operands(m + 1, bop[(m + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint2 t4[4];
-          const uint32_t w = kw[s][r];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            uint32_t addr;
-            if (BK == 4) addr = __builtin_amdgcn_perm(w, kc8, 0x0C0C0000u | ((4u + p) << 8));
-            else addr = (((w >> (6 * p)) & 63u) << 8) | kc8;
-            t4[p] = lds_u64(lds, addr);
-          }
-          const uint32_t hv[4] = {t4[0].x, t4[1].x, t4[2].x, t4[3].x};
-          const uint32_t lv[4] = {t4[0].y, t4[1].y, t4[2].y, t4[3].y};
-          __builtin_memcpy(&bh[s], hv, 16);
-          __builtin_memcpy(&bl[s], lv, 16);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[r], bh[s], acc[s], 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[r], bh[s], acc[s], 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[r], bl[s], acc[s], 0, 0, 0);
+        for (int s = 0; s < 4; ++s)
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[m], bop[m & 1][s], acc[s], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // lane holds heads 4q..4q+3 of token 16s + m_row (rows >= NH are unused padding)
+      const float nk = half_bits_to_float(nk_h);
+      if (t0 + kTile < t_end) load_keys(t0 + kTile);
+      const float nv = SPARSE ? 1.f : half_bits_to_float(nv_h);
+      // lane holds rows 4q..4q+3 of token 16s + m_row
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<floatx4 *>(sbuf + (16 * s + m_row) * 16 + 4 * quarter) = acc[s];
+        *reinterpret_cast<floatx4 *>(wbuf + score_off(16 * s + m_row, quarter)) = acc[s];
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
       float sc[NH];
 #pragma unroll
       for (int k = 0; k < NH / 4; ++k) {
-        const float4 d = *reinterpret_cast<const float4 *>(sbuf + lane * 16 + 4 * k);
-        sc[4 * k] = d.x; sc[4 * k + 1] = d.y; sc[4 * k + 2] = d.z; sc[4 * k + 3] = d.w;
+        const floatx4 hi = *reinterpret_cast<const floatx4 *>(wbuf + score_off(lane, k));
+        const floatx4 lo = *reinterpret_cast<const floatx4 *>(wbuf + score_off(lane, k + NH / 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[4 * k + j] = hi[j] + lo[j];
       }
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
@@ -270,8 +289,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         const float pe = ok ? __expf(s - m_ref[j]) : 0.f;
         p[j] = pe;
         if (ok && !(pe * nv <= kAMax)) need = true;
-        if (a.scores != nullptr && ok)
-          a.scores[((size_t)b * a.n_q_heads + kvh * g + j) * a.ctx_len + t0 + lane] = s;
+      }
+      if (a.scores != nullptr) {
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+          if (j < g && tv) a.scores[((size_t)b * a.n_q_heads + kvh * g + j) * a.ctx_len + t0 + lane] = sc[j];
       }
       if (__any(need)) {
         // move the reference to the tile's largest s + ln||v|| (per head), rescale
@@ -289,10 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         if (!SPARSE) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            float al = alpha[jj];
-            if (NH > 4 && quarter == 1) al = alpha[(4 + jj) % NH];
-            if (NH > 8 && quarter == 2) al = alpha[(8 + jj) % NH];
-            if (NH > 8 && quarter == 3) al = alpha[(12 + jj) % NH];
+            const float al = (NH == 8 && (quarter & 1)) ? alpha[(4 + jj) % NH] : alpha[jj];
 #pragma unroll
             for (int n = 0; n < 8; ++n) oacc[n][jj] *= al;
           }
@@ -302,33 +321,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       for (int j = 0; j < NH; ++j) l_part[j] += p[j];
 
       if (!SPARSE) {
-        // ---- P' to LDS as [head][token] fp16, read back as the PV operand
-        _Float16 *pst = reinterpret_cast<_Float16 *>(wbuf);
+        // ---- P' (hi rows 0..NH-1, remainder rows NH..2NH-1) to LDS, read back as operand
 #pragma unroll
-        for (int j = 0; j < NH; ++j) pst[j * 64 + lane] = (_Float16)(p[j] * nv);
+        for (int j = 0; j < NH; ++j) {
+          const float pv = p[j] * nv;
+          const _Float16 hi = (_Float16)pv;
+          const _Float16 lo = (_Float16)(pv - (float)hi);
+          *reinterpret_cast<_Float16 *>(wbuf + pst_off(j, lane >> 3) + 2 * (lane & 7)) = hi;
+          *reinterpret_cast<_Float16 *>(wbuf + pst_off(NH + j, lane >> 3) + 2 * (lane & 7)) = lo;
+        }
         __builtin_amdgcn_wave_barrier();
         __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+          uint4 pa = *reinterpret_cast<const uint4 *>(wbuf + pst_off(m_row, 4 * c + quarter));
+          if (m_row >= 2 * NH) pa = make_uint4(0u, 0u, 0u, 0u);
           half8 aop;
-          if (m_row < NH) {
-            const uint4 pa = *reinterpret_cast<const uint4 *>(wbuf + m_row * 128 + 64 * c + 16 * quarter);
-            __builtin_memcpy(&aop, &pa, 16);
-          } else {
-            aop = half8{0, 0, 0, 0, 0, 0, 0, 0};
-          }
+          __builtin_memcpy(&aop, &pa, 16);
           const uint32_t vwd[4] = {vw[c].x, vw[c].y, vw[c].z, vw[c].w};
-#pragma unroll
-          for (int n = 0; n < 8; ++n) {
+          auto value_operand = [&](int n) {
             const uint32_t w = vwd[n >> 1];
             const uint32_t sel_lo = 0x0C020000u | ((4u + 2u * (n & 1)) << 8);
             const uint32_t sel_hi = 0x0C020000u | ((5u + 2u * (n & 1)) << 8);
-            const uint2 lo = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_lo));
-            const uint2 hi = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_hi));
-            const uint32_t hv[4] = {lo.x, lo.y, hi.x, hi.y};
-            half8 bop;
-            __builtin_memcpy(&bop, hv, 16);
-            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, oacc[n], 0, 0, 0);
+            uint2 t2[2];
+            t2[0] = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_lo));
+            t2[1] = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_hi));
+            half8 bo;
+            __builtin_memcpy(&bo, t2, 16);
+            return bo;
+          };
+          half8 vb[2];
+          vb[0] = value_operand(0);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            if (n + 1 < 8) vb[(n + 1) & 1] = value_operand(n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, vb[n & 1], oacc[n], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -353,14 +382,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         }
         cand_written += __popcll(bal);
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kw[s][r] = kw_n[s][r];
-      vw[0] = vw_n[0];
-      vw[1] = vw_n[1];
-      nk_h = nk_n;
-      nv_h = nv_n;
     }
 
     // ---- partials of this item
@@ -371,10 +392,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         a.part_ml[((size_t)b * a.n_q_heads + kvh * g + j) * S + split] = make_float2(m_ref[j], lt);
     }
     if (!SPARSE) {
+      // add the remainder rows onto the hi rows: rows NH.. live 16*NH/4 lanes further on
+      constexpr int kLoLanes = NH == 4 ? 16 : 32;
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) oacc[n][jj] += __shfl_xor(oacc[n][jj], kLoLanes);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int head = 4 * quarter + jj;
-        if (head < g) {
+        if (head < g && quarter < NH / 4) {
           float *dst = a.part_o + (((size_t)b * a.n_q_heads + kvh * g + head) * S + split) * kD + 8 * m_row;
           *reinterpret_cast<float4 *>(dst) = make_float4(oacc[0][jj], oacc[1][jj], oacc[2][jj], oacc[3][jj]);
           *reinterpret_cast<float4 *>(dst + 4) = make_float4(oacc[4][jj], oacc[5][jj], oacc[6][jj], oacc[7][jj]);
@@ -389,15 +416,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 template <int BK, bool SPARSE>
 hipError_t launch_g(const DecodeArgs &a, int grid, hipStream_t stream) {
   if (a.group <= 4) decode_mfma_kernel<BK, 4, SPARSE><<<grid, kThreads, 0, stream>>>(a);
-  else if (a.group <= 8) decode_mfma_kernel<BK, 8, SPARSE><<<grid, kThreads, 0, stream>>>(a);
-  else decode_mfma_kernel<BK, 16, SPARSE><<<grid, kThreads, 0, stream>>>(a);
+  else decode_mfma_kernel<BK, 8, SPARSE><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs &a) {
-  return (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.group <= 16 &&
+  return (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.group <= 8 &&
          a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
          a.plan.split_len % kTile == 0;
 }
