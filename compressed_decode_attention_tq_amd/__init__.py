@@ -189,7 +189,8 @@ class DecodeBuffers:
         nbytes = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, ctx_len, tau)
         if nbytes == 0:
             raise TQError(TQ_ERR_INVALID_ARG, "tq_decode_workspace_bytes")
-        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        # zero once: the decode call's arrival counters live here and return to zero
+        self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.workspace.data_ptr()) % 256
         self.ws_ptr = self.workspace.data_ptr() + off
         self.ws_bytes = nbytes

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["api.hip", "quantize.hip", "decode_generic.hip", "decode_mfma.hip", "codebook.cpp"]
+SOURCES = ["api.hip", "quantize.hip", "decode_generic.hip", "decode_mfma.hip", "decode_fused.hip",
+           "codebook.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [

@@ -65,12 +65,36 @@ SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len) {
   return SplitPlan{(int)n, (int)len};
 }
 
+SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len) {
+  const long units = (long)batch * n_kv_heads;
+  const long target_groups = 256;       // about one workgroup per CU
+  const long max_len = 1L << 20;        // keeps in-split byte offsets within 32 bits
+  const long min_len = 8 * kSplitAlign;  // one tile for each of the 8 waves of a workgroup
+  long s_target = (target_groups + units - 1) / units;
+  if (s_target < 1) s_target = 1;
+  long len = (ctx_len + s_target - 1) / s_target;
+  len = (len + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  if (len < min_len) len = min_len;
+  if (len > max_len) len = max_len;
+  long n = (ctx_len + len - 1) / len;
+  if (n < 1) n = 1;
+  return SplitPlan{(int)n, (int)len};
+}
+
 WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  bool sparse) {
   const SplitPlan p = plan_splits(batch, n_kv_heads, ctx_len);
+  const SplitPlan fp = plan_fused(batch, n_kv_heads, ctx_len);
   const size_t heads = (size_t)batch * n_q_heads * p.n_splits;
+  const size_t fheads = (size_t)batch * n_q_heads * fp.n_splits;
   WorkspaceLayout w{};
   size_t off = 0;
+  w.counters = off;  // first, so no other section of any layout ever overlaps it
+  off = align_up(off + (size_t)batch * n_kv_heads * sizeof(unsigned), 256);
+  w.fpart_ml = off;
+  off = align_up(off + fheads * sizeof(float2), 256);
+  w.fpart_o = off;
+  off = align_up(off + fheads * kD * sizeof(float), 256);
   w.part_ml = off;
   off = align_up(off + heads * sizeof(float2), 256);
   w.part_o = off;
@@ -187,6 +211,7 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
   a.sparse = sparse ? 1 : 0;
   a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len);
+  a.fplan = plan_fused(k->batch, k->n_kv_heads, ctx_len);
   a.out = out;
   a.lse = lse;
   a.scores = scores;
@@ -195,6 +220,9 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.part_o = reinterpret_cast<float *>(ws + w.part_o);
   a.cand_count = reinterpret_cast<int *>(ws + w.cand_count);
   a.cand = reinterpret_cast<float *>(ws + w.cand);
+  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
+  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
+  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
   return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -1,0 +1,609 @@
+// Dense decode attention in one launch on matrix cores (gfx950 v_mfma_f32_16x16x32_f16), for
+// keys of 3 or 4 bits (TQ_LAYOUT_ROWS), values of 2 bits (TQ_LAYOUT_GROUP8) and a query
+// group of up to 8 heads per kv head.
+//
+// What is computed follows [google] "Google 最新極限壓縮算法…" (scores taken directly
+// against the quantized keys as ||k|| (Rq).c[idx], values summed in the rotated domain and
+// rotated back once) and [tq-plus] "turboquant_plus" §Sparse V / attention (online softmax
+// over the context).  The schedule is this file's own:
+//
+//   * Work unit: one workgroup (8 waves, 160 KB of LDS, one per CU) owns a contiguous split
+//     of one (batch, kv head) context; its waves take the split's 64-token tiles in turn.
+//   * The query group is rotated once per split: wave h applies the signs and the
+//     Walsh-Hadamard butterflies to head h (two coordinates per lane, lane exchanges for the
+//     upper six stages) and leaves R q in LDS for all waves.
+//   * Codes become fp16 matrix operands through lookup tables in LDS, replicated 32 times
+//     so the 32 lanes of one LDS pass never share a bank.  A key byte (two 4-bit codes, or a
+//     6-bit pair of 3-bit codes) gives {hi(c_a), hi(c_b), lo(c_a), lo(c_b)}: each centroid
+//     split into its fp16 value and the fp16 remainder.  A value byte (four 2-bit codes of
+//     one coordinate, four consecutive tokens) gives four fp16 centroids.
+//   * Scores keep about 22 significant bits: query row 2h holds the fp16 part of head h,
+//     row 2h+1 its remainder, each value repeated to meet the {hi, hi, lo, lo} key operand,
+//     so one product sums (q_hi + q_lo).(c_hi + c_lo) over 16 coordinates; the two rows of a
+//     head land in the same lane and are added there.
+//   * Softmax in base 2 (log2 e is folded into the query) with a stale reference: the
+//     reference of a head only moves when a tile would push p * ||v|| past the fp16 range,
+//     so the value accumulator is rarely rescaled.  The value product takes P' = p * ||v||
+//     split the same way into a fp16 row and a remainder row.
+//   * End of split: the 8 waves combine (m, l, O) through LDS; the workgroup writes one
+//     partial per query head and bumps a per-(batch, kv head) arrival counter.  The last
+//     workgroup to arrive merges the partials, applies the inverse rotation and writes the
+//     output and log-sum-exp, then clears the counter for the next call.
+#include "tq_common.h"
+#include "tq_launch.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 64;
+constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kAMax = 30000.f;   // largest p * ||v|| kept in an fp16 operand
+constexpr float kNvFloor = 1e-20f;  // ||v|| used for the range test of an all-zero value
+constexpr int kRsrcWord3 = 0x00020000;
+
+// LDS map (bytes):
+//   [0, 64K)      K table: entry e at e*256 + copy*8 (copy < 32)
+//   [64K, 128K)   V table: entry e at 64K + e*256 + copy*8
+//   [128K, 160K)  one 4 KB buffer per wave:
+//                   [0, 2K)  scores of the tile, [32 token pairs][2 head halves][2][NH/2]
+//                            fp32, 16-byte units XOR-swizzled
+//                   [2K, 4K) P' [16 rows][64 tokens] fp16, 16-byte units XOR-swizzled
+//                 and, between tiles, the rotated query group (rows of 128 fp32) and the
+//                 end-of-split combine.
+constexpr int kLdsBytes = 160 * 1024;
+constexpr uint32_t kVBase = 64 * 1024;
+constexpr uint32_t kWBase = 128 * 1024;
+constexpr uint32_t kPBase = 2048;
+
+__device__ __forceinline__ uint2 lds_u64(const uint8_t *lds, uint32_t addr) {
+  return *reinterpret_cast<const uint2 *>(lds + addr);
+}
+__device__ __forceinline__ uint16_t h16(float x) { return __half_as_ushort(__float2half_rn(x)); }
+__device__ __forceinline__ float f16(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Score staging: 16-byte unit `u` (0 .. 2*NH/4 - 1 per token pair) of token pair `pr`.
+template <int NH>
+__device__ __forceinline__ uint32_t score_unit(int pr, int u) {
+  if (NH == 4) return (uint32_t)pr * 32u + ((uint32_t)(u ^ ((pr >> 3) & 1)) << 4);
+  return (uint32_t)pr * 64u + ((uint32_t)(u ^ ((pr >> 2) & 3)) << 4);
+}
+// P' staging: 16-byte unit `unit` (tokens 8*unit .. 8*unit+7) of row `row`.
+__device__ __forceinline__ uint32_t pst_off(int row, int unit) {
+  return kPBase + (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
+}
+
+template <int BK>
+__device__ void build_tables(uint8_t *lds, const float *kc, const float *vc) {
+  for (int idx = threadIdx.x; idx < 256 * 32; idx += blockDim.x) {
+    const int e = idx >> 5, copy = idx & 31;
+    const float c0 = BK == 4 ? kc[e & 15] : kc[e & 7];
+    const float c1 = BK == 4 ? kc[e >> 4] : kc[(e >> 3) & 7];
+    const uint16_t h0 = h16(c0), h1 = h16(c1);
+    uint2 kv;
+    kv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    kv.y = (uint32_t)h16(c0 - f16(h0)) | ((uint32_t)h16(c1 - f16(h1)) << 16);
+    *reinterpret_cast<uint2 *>(lds + e * 256 + copy * 8) = kv;
+    uint2 vv;
+    vv.x = (uint32_t)h16(vc[e & 3]) | ((uint32_t)h16(vc[(e >> 2) & 3]) << 16);
+    vv.y = (uint32_t)h16(vc[(e >> 4) & 3]) | ((uint32_t)h16(vc[(e >> 6) & 3]) << 16);
+    *reinterpret_cast<uint2 *>(lds + kVBase + e * 256 + copy * 8) = vv;
+  }
+}
+
+// Butterfly stages 1..6 of a 128-point Walsh-Hadamard transform whose coordinates 2l, 2l+1
+// sit in lane l (stage 0, inside the lane, is done by the caller).
+__device__ __forceinline__ void wave_fwht_upper(float &x0, float &x1, int lane) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m);
+    x0 = upper ? o0 - x0 : x0 + o0;
+    x1 = upper ? o1 - x1 : x1 + o1;
+  }
+}
+
+__device__ __forceinline__ float half_max(float v) {  // over the 32 lanes of a half wave
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+// Partials cross workgroups (and the per-XCD L2 caches) as agent-scope relaxed atomics: the
+// stores write through to the coherent level and the loads bypass stale L2 lines, so no
+// cache-wide writeback or invalidate is needed around the arrival counter.
+__device__ __forceinline__ void store_coherent(float2 *p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2 *p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float exp2_or_zero(float x, float ref) {
+  return (x == -INFINITY || ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - ref);
+}
+
+template <int BK, int NH>
+__global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
+  static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
+  constexpr int NH2 = NH / 2;      // heads per softmax lane
+  constexpr int KROW = 16 * BK;    // key bytes per token
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
+  const int g = a.group, S = a.fplan.n_splits, L = a.fplan.split_len;
+  const int m_row = lane & 15, quarter = lane >> 4;
+  const int pr = lane & 31, half_id = lane >> 5;  // softmax mapping: tokens 2pr, 2pr+1
+  const uint32_t kc8 = (uint32_t)(lane & 31) << 3;
+  const uint32_t vc8 = ((uint32_t)(lane & 31) << 3) | kVBase;
+  uint8_t *wbuf = lds + kWBase + wave * 4096;
+  float *qrot = reinterpret_cast<float *>(lds + kWBase);  // [NH][128] between tiles
+
+  build_tables<BK>(lds, a.k.centroids, a.v.centroids);
+  if (NH == 4) {  // P' rows 8..15 stay zero for the whole launch
+    *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  const int n_items = a.batch * a.n_kv_heads * S;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int split = item % S;
+    const int kvh = (item / S) % a.n_kv_heads;
+    const int b = item / (S * a.n_kv_heads);
+    int T = a.ctx_len;
+    if (a.seq_lens != nullptr) T = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.ctx_len));
+    const int t_begin = split * L;
+    const int t_end = min(t_begin + L, T);
+    const int qh0 = kvh * g;  // first query head of the group
+
+    // ---- rotated query group: wave h rotates head h into qrot[h]
+    if (wave < NH) {
+      float x0 = 0.f, x1 = 0.f;
+      if (wave < g) {
+        const size_t base = ((size_t)b * a.n_q_heads + qh0 + wave) * kD + 2 * lane;
+        x0 = load_elem(a.q, base, a.q_dtype);
+        x1 = load_elem(a.q, base + 1, a.q_dtype);
+        if (a.k.signs[2 * lane] < 0) x0 = -x0;
+        if (a.k.signs[2 * lane + 1] < 0) x1 = -x1;
+      }
+      const float y0 = x0 + x1, y1 = x0 - x1;
+      x0 = y0;
+      x1 = y1;
+      wave_fwht_upper(x0, x1, lane);
+      const float qs = a.scale * kInvSqrtD * kLog2e;
+      *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
+    }
+    __syncthreads();
+    // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
+    half8 qop[8];
+    {
+      const int head = m_row >> 1;
+      const bool lo_row = (m_row & 1) != 0;
+      const bool live = head < NH && head < g;
+      float v[32];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float4 f = live ? *reinterpret_cast<const float4 *>(qrot + head * kD + 32 * quarter + 4 * r)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
+      }
+      _Float16 part[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const _Float16 hi = (_Float16)v[e];
+        part[e] = lo_row ? (_Float16)(v[e] - (float)hi) : hi;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        qop[m][0] = part[4 * m];     qop[m][1] = part[4 * m + 1];
+        qop[m][2] = part[4 * m];     qop[m][3] = part[4 * m + 1];
+        qop[m][4] = part[4 * m + 2]; qop[m][5] = part[4 * m + 3];
+        qop[m][6] = part[4 * m + 2]; qop[m][7] = part[4 * m + 3];
+      }
+    }
+    __syncthreads();  // qrot (wave buffers 0..1) is free for staging from here
+
+    // ---- per-lane softmax state: heads half_id*NH2 + hh
+    float mr[NH2], lsum[NH2];
+#pragma unroll
+    for (int hh = 0; hh < NH2; ++hh) { mr[hh] = -INFINITY; lsum[hh] = 0.f; }
+    floatx4 oacc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+    const uint32_t span_tok = (uint32_t)n_tiles * kTile;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v.plane(b, kvh) + (size_t)t_begin * 32, span_tok * 32);
+    const __amdgpu_buffer_rsrc_t knrs = make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    const __amdgpu_buffer_rsrc_t vnrs = make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    const uint32_t k_voff = (uint32_t)m_row * KROW + (uint32_t)quarter * (4 * BK);
+    const uint32_t v_voff = (uint32_t)quarter * 256u + (uint32_t)m_row * 16u;
+    const uint32_t n_voff = (uint32_t)pr * 4u;
+
+    uint32_t kw[4][4];
+    uint32_t nkw = 0;
+    auto load_keys = [&](int tile) {
+      const int so = tile * kTile * KROW;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (BK == 4) {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + s * 16 * KROW, so, 0);
+          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = w[3];
+        } else {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b96(krs, k_voff + s * 16 * KROW, so, 0);
+          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = 0u;
+        }
+      }
+      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff, tile * kTile * 2, 0);
+    };
+    if (wave < n_tiles) load_keys(wave);
+
+    for (int tile = wave; tile < n_tiles; tile += kWaves) {
+      const int t0 = t_begin + tile * kTile;
+      uint32_t vw[2][4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + c * 1024, tile * kTile * 32, 0);
+        vw[c][0] = w[0]; vw[c][1] = w[1]; vw[c][2] = w[2]; vw[c][3] = w[3];
+      }
+      const uint32_t nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff, tile * kTile * 2, 0);
+
+      // ---- scores: sub-tile s, 16-coordinate chunk m -> key fields 2m, 2m+1 of the quarter
+      auto key_operands = [&](int m, half8 (&dst)[4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint2 t2[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int f = 2 * m + p;
+            uint32_t addr;
+            if (BK == 4) {
+              addr = __builtin_amdgcn_perm(kw[s][f >> 2], kc8, 0x0C0C0000u | ((4u + (f & 3)) << 8));
+            } else {
+              const int bit = 6 * f;
+              uint32_t fld;
+              if ((bit & 31) <= 26) fld = (kw[s][bit >> 5] >> (bit & 31)) & 63u;
+              else fld = ((kw[s][bit >> 5] >> (bit & 31)) | (kw[s][(bit >> 5) + 1] << (32 - (bit & 31)))) & 63u;
+              addr = (fld << 8) | kc8;
+            }
+            t2[p] = lds_u64(lds, addr);
+          }
+          __builtin_memcpy(&dst[s], t2, 16);
+        }
+      };
+      floatx4 acc[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+      half8 bop[2][4];
+      key_operands(0, bop[0]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        // lookups of step m+1 go out before the products of step m; the fences keep the
+        // scheduler to this order so LDS latency hides behind four matrix instructions
+        if (m + 1 < 8) key_operands(m + 1, bop[(m + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[m], bop[m & 1][s], acc[s], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint32_t nk_pair = nkw;
+      if (tile + kWaves < n_tiles) load_keys(tile + kWaves);
+
+      // lane holds rows 4q..4q+3 (heads 2q, 2q+1; fp16 and remainder rows) of token 16s+m_row
+      if (NH == 8 || quarter < 2) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int tok = 16 * s + m_row, p2 = tok >> 1, tb = tok & 1;
+          const float2 sv = make_float2(acc[s][0] + acc[s][1], acc[s][2] + acc[s][3]);
+          uint32_t off;
+          if (NH == 4) off = score_unit<4>(p2, quarter) + tb * 8;
+          else off = score_unit<8>(p2, 2 * (quarter >> 1) + tb) + (quarter & 1) * 8;
+          *reinterpret_cast<float2 *>(wbuf + off) = sv;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      float sc[2][NH2];  // [token bit][head slot]
+      if (NH == 4) {
+        const float4 r = *reinterpret_cast<const float4 *>(wbuf + score_unit<4>(pr, half_id));
+        sc[0][0] = r.x; sc[0][1] = r.y; sc[1][0] = r.z; sc[1][1] = r.w;
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const float4 r = *reinterpret_cast<const float4 *>(wbuf + score_unit<8>(pr, 2 * half_id + tb));
+          sc[tb][0] = r.x; sc[tb][1] = r.y; sc[tb][2] = r.z; sc[tb][3] = r.w;
+        }
+      }
+
+      // ---- online softmax (base 2) for tokens t0 + 2pr + tb, heads half_id*NH2 + hh
+      float nk[2], nv[2];
+      nk[0] = f16((uint16_t)(nk_pair & 0xffffu));
+      nk[1] = f16((uint16_t)(nk_pair >> 16));
+      nv[0] = fmaxf(f16((uint16_t)(nvw & 0xffffu)), kNvFloor);
+      nv[1] = fmaxf(f16((uint16_t)(nvw >> 16)), kNvFloor);
+      const bool tail = t0 + kTile > t_end;
+      float p[2][NH2];
+      float vmax = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const bool ok = !tail || (t0 + 2 * pr + tb < t_end);
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) {
+          const float s2 = ok ? sc[tb][hh] * nk[tb] : -INFINITY;
+          sc[tb][hh] = s2;
+          p[tb][hh] = __builtin_amdgcn_exp2f(s2 - mr[hh]);
+          vmax = fmaxf(vmax, p[tb][hh] * nv[tb]);
+        }
+      }
+      if (__any(!(vmax <= kAMax))) {
+        // move each head's reference to the tile's largest s + log2||v||, rescale
+        float alpha[NH2];
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) {
+          float z = fmaxf(sc[0][hh] == -INFINITY ? -INFINITY : sc[0][hh] + __log2f(nv[0]),
+                          sc[1][hh] == -INFINITY ? -INFINITY : sc[1][hh] + __log2f(nv[1]));
+          z = half_max(z);
+          const float m_new = fmaxf(mr[hh], z);
+          alpha[hh] = exp2_or_zero(mr[hh], m_new);
+          mr[hh] = m_new;
+          lsum[hh] *= alpha[hh];
+          p[0][hh] = exp2_or_zero(sc[0][hh], m_new);
+          p[1][hh] = exp2_or_zero(sc[1][hh], m_new);
+        }
+        // value rows 4q..4q+3 belong to heads 2q, 2q+1
+        float al[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h % NH2]), (h / NH2) * 32));
+        float a0 = al[0], a1 = al[1];
+#pragma unroll
+        for (int q = 1; q < NH / 2; ++q)
+          if (quarter == q) { a0 = al[2 * q]; a1 = al[2 * q + 1]; }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          oacc[n][0] *= a0; oacc[n][1] *= a0;
+          oacc[n][2] *= a1; oacc[n][3] *= a1;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < NH2; ++hh) lsum[hh] += p[0][hh] + p[1][hh];
+
+      if (a.scores != nullptr) {
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) {
+          const int h = half_id * NH2 + hh;
+          if (h < g) {
+            float *row = a.scores + ((size_t)b * a.n_q_heads + qh0 + h) * a.ctx_len;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              if (t0 + 2 * pr + tb < t_end) row[t0 + 2 * pr + tb] = sc[tb][hh] * kLn2;
+          }
+        }
+      }
+
+      // ---- P' = p * ||v||: fp16 row 2h and remainder row 2h+1, token pair per 32-bit write
+#pragma unroll
+      for (int hh = 0; hh < NH2; ++hh) {
+        const int h = half_id * NH2 + hh;
+        const float v0 = p[0][hh] * nv[0], v1 = p[1][hh] * nv[1];
+        half2v hi, lo;
+        hi[0] = (_Float16)v0;
+        hi[1] = (_Float16)v1;
+        lo[0] = (_Float16)(v0 - (float)hi[0]);
+        lo[1] = (_Float16)(v1 - (float)hi[1]);
+        const uint32_t sub = (uint32_t)(pr & 3) * 4u;
+        *reinterpret_cast<half2v *>(wbuf + pst_off(2 * h, pr >> 2) + sub) = hi;
+        *reinterpret_cast<half2v *>(wbuf + pst_off(2 * h + 1, pr >> 2) + sub) = lo;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+
+      // ---- O[row][coord] += P'[row][token] V[token][coord]
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 pa = *reinterpret_cast<const uint4 *>(wbuf + pst_off(m_row, 4 * c + quarter));
+        half8 aop;
+        __builtin_memcpy(&aop, &pa, 16);
+        auto value_operand = [&](int n) {
+          const uint32_t w = vw[c][n >> 1];
+          const uint32_t sel_lo = 0x0C020000u | ((4u + 2u * (n & 1)) << 8);
+          const uint32_t sel_hi = 0x0C020000u | ((5u + 2u * (n & 1)) << 8);
+          uint2 t2[2];
+          t2[0] = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_lo));
+          t2[1] = lds_u64(lds, __builtin_amdgcn_perm(w, vc8, sel_hi));
+          half8 bo;
+          __builtin_memcpy(&bo, t2, 16);
+          return bo;
+        };
+        half8 vb[2];
+        vb[0] = value_operand(0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          if (n + 1 < 8) vb[(n + 1) & 1] = value_operand(n + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, vb[n & 1], oacc[n], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+    }
+
+    // ---- combine the 8 waves of the split.  Round 1: (m, l) per head.
+    float ltot[NH2];
+#pragma unroll
+    for (int hh = 0; hh < NH2; ++hh) ltot[hh] = half_sum(lsum[hh]);
+    __syncthreads();  // every wave is done with its staging buffers
+    if (pr == 0) {
+#pragma unroll
+      for (int hh = 0; hh < NH2; ++hh)
+        *reinterpret_cast<float2 *>(wbuf + (half_id * NH2 + hh) * 8) = make_float2(mr[hh], ltot[hh]);
+    }
+    __syncthreads();
+    // scale of this wave's value rows (heads 2q, 2q+1) and, for the summing phase, the
+    // split's reference and sum of head `wave` (thread (wave, lane) sums coords 2l, 2l+1)
+    float f0 = 0.f, f1 = 0.f, Mh = -INFINITY, Lh = 0.f;
+    {
+      const int h0 = NH == 8 ? 2 * quarter : 2 * (quarter & 1);
+      float M0 = -INFINITY, M1 = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float *src = reinterpret_cast<const float *>(lds + kWBase + w * 4096);
+        M0 = fmaxf(M0, src[2 * h0]);
+        M1 = fmaxf(M1, src[2 * (h0 + 1)]);
+        if (wave < NH) Mh = fmaxf(Mh, src[2 * wave]);
+      }
+      const float *own = reinterpret_cast<const float *>(wbuf);
+      f0 = exp2_or_zero(own[2 * h0], M0);
+      f1 = exp2_or_zero(own[2 * (h0 + 1)], M1);
+      if (wave < NH) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float *src = reinterpret_cast<const float *>(lds + kWBase + w * 4096);
+          Lh += src[2 * wave + 1] * exp2_or_zero(src[2 * wave], Mh);
+        }
+      }
+    }
+    __syncthreads();
+    // Round 2: scaled O rows of this wave, [head][128] fp32 (hi and remainder rows summed)
+    if (NH == 8 || quarter < 2) {
+      const int h0 = 2 * quarter;
+      float *dst0 = reinterpret_cast<float *>(wbuf) + h0 * kD + 8 * m_row;
+      float *dst1 = dst0 + kD;
+      *reinterpret_cast<float4 *>(dst0) = make_float4((oacc[0][0] + oacc[0][1]) * f0, (oacc[1][0] + oacc[1][1]) * f0,
+                                                      (oacc[2][0] + oacc[2][1]) * f0, (oacc[3][0] + oacc[3][1]) * f0);
+      *reinterpret_cast<float4 *>(dst0 + 4) = make_float4((oacc[4][0] + oacc[4][1]) * f0, (oacc[5][0] + oacc[5][1]) * f0,
+                                                          (oacc[6][0] + oacc[6][1]) * f0, (oacc[7][0] + oacc[7][1]) * f0);
+      *reinterpret_cast<float4 *>(dst1) = make_float4((oacc[0][2] + oacc[0][3]) * f1, (oacc[1][2] + oacc[1][3]) * f1,
+                                                      (oacc[2][2] + oacc[2][3]) * f1, (oacc[3][2] + oacc[3][3]) * f1);
+      *reinterpret_cast<float4 *>(dst1 + 4) = make_float4((oacc[4][2] + oacc[4][3]) * f1, (oacc[5][2] + oacc[5][3]) * f1,
+                                                          (oacc[6][2] + oacc[6][3]) * f1, (oacc[7][2] + oacc[7][3]) * f1);
+    }
+    __syncthreads();
+    const size_t part_row = ((size_t)b * a.n_q_heads + qh0 + wave) * S;  // valid for wave < g
+    if (wave < NH && wave < g) {
+      float2 o = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float2 x = *reinterpret_cast<const float2 *>(lds + kWBase + w * 4096 + (wave * kD + 2 * lane) * 4);
+        o.x += x.x;
+        o.y += x.y;
+      }
+      store_coherent(reinterpret_cast<float2 *>(a.fpart_o + (part_row + split) * kD) + lane, o);
+      if (lane == 0) store_coherent(a.fpart_ml + part_row + split, make_float2(Mh, Lh));
+    }
+
+    // ---- arrival; the last workgroup of this (batch, kv head) merges its splits.  The wait
+    //      makes this wave's partial stores complete before the counter moves.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    int *flag = reinterpret_cast<int *>(lds + kWBase);
+    unsigned *counter = a.counters + (size_t)b * a.n_kv_heads + kvh;
+    if (threadIdx.x == 0) {
+      const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = old == (unsigned)(S - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    if (last) {
+      if (wave < NH && wave < g) {
+        // lane s of a chunk holds partial s's (m, l); every lane then sums its two
+        // coordinates over the partials, 16 loads in flight at a time
+        const float2 *pml = a.fpart_ml + part_row;
+        const float2 *pof = reinterpret_cast<const float2 *>(a.fpart_o + part_row * kD) + lane;
+        float M = -INFINITY;
+        for (int s0 = 0; s0 < S; s0 += 64)
+          if (s0 + lane < S) M = fmaxf(M, load_coherent(pml + s0 + lane).x);
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+        float l = 0.f, o0 = 0.f, o1 = 0.f;
+        if (M != -INFINITY) {
+          for (int s0 = 0; s0 < S; s0 += 64) {
+            float w = 0.f;
+            if (s0 + lane < S) {
+              const float2 ml = load_coherent(pml + s0 + lane);
+              w = exp2_or_zero(ml.x, M);
+              l += ml.y * w;
+            }
+            const int n = min(64, S - s0);
+            for (int s = 0; s < n; s += 16) {
+              float2 o[16];
+#pragma unroll
+              for (int u = 0; u < 16; ++u)
+                o[u] = s + u < n ? load_coherent(pof + (size_t)(s0 + s + u) * (kD / 2)) : make_float2(0.f, 0.f);
+#pragma unroll
+              for (int u = 0; u < 16; ++u) {
+                const float wu = __shfl(w, s + u);
+                o0 += o[u].x * wu;
+                o1 += o[u].y * wu;
+              }
+            }
+          }
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) l += __shfl_xor(l, m);
+          o0 /= l;
+          o1 /= l;
+        }
+        // inverse rotation: x = s * (H y) / sqrt(128)
+        float y0 = o0 + o1, y1 = o0 - o1;
+        wave_fwht_upper(y0, y1, lane);
+        y0 *= kInvSqrtD;
+        y1 *= kInvSqrtD;
+        if (a.k.signs[2 * lane] < 0) y0 = -y0;
+        if (a.k.signs[2 * lane + 1] < 0) y1 = -y1;
+        const size_t orow = (size_t)b * a.n_q_heads + qh0 + wave;
+        *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
+        if (lane == 0 && a.lse != nullptr) a.lse[orow] = M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
+        if (a.scores != nullptr) {
+          float *row = a.scores + orow * a.ctx_len;
+          for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;
+        }
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // LDS (flag, query rows) is reused by the next item
+  }
+}
+
+template <int BK>
+hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
+  if (a.group <= 4) decode_fused_kernel<BK, 4><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_fused_supported(const DecodeArgs &a) {
+  return !a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.group <= 8 &&
+         a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
+         a.fplan.split_len % kTile == 0 && a.counters != nullptr;
+}
+
+hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream) {
+  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  int grid = (int)std::min<long>(n_cu, items);
+  if (grid < 1) grid = 1;
+  return a.k.bits == 4 ? launch_bk<4>(a, grid, stream) : launch_bk<3>(a, grid, stream);
+}
+
+}  // namespace tq

@@ -390,6 +390,7 @@ int compute_units() {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (decode_fused_supported(a)) return launch_decode_fused(a, compute_units(), stream);
   dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
   hipError_t e;
   if (decode_mfma_supported(a)) {

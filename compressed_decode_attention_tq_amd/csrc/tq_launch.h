@@ -16,9 +16,14 @@ struct SplitPlan {
 };
 
 SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len);
+// Splits of the single-launch dense path: about one workgroup per CU, whole 64-token tiles.
+SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len);
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WorkspaceLayout {
+  size_t counters;    // unsigned [batch][n_kv_heads]   zero between calls
+  size_t fpart_ml;    // float2 [batch][n_q_heads][fused splits]
+  size_t fpart_o;     // float  [batch][n_q_heads][fused splits][128]
   size_t part_ml;     // float2 [batch][n_q_heads][n_splits]      (m, l) per split
   size_t part_o;      // float  [batch][n_q_heads][n_splits][128] rotated-domain sums
   size_t cand_count;  // int    [batch][n_kv_heads][n_splits]      Sparse-V candidates
@@ -45,6 +50,12 @@ struct DecodeArgs {
   float *part_o;
   int *cand_count;
   float *cand;
+  // single-launch dense path: one partial per (batch, query head, split of fplan) and an
+  // arrival counter per (batch, kv head) that the last workgroup clears
+  SplitPlan fplan;
+  float2 *fpart_ml;
+  float *fpart_o;
+  unsigned *counters;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
@@ -53,6 +64,8 @@ hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_d
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supported(const DecodeArgs &a);
+bool decode_fused_supported(const DecodeArgs &a);
+hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int n_cu, hipStream_t stream);
 
 }  // namespace tq

@@ -142,7 +142,10 @@ int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_
  *   lse        device out [batch][n_q_heads] fp32 or NULL (-inf when T = 0)
  *   scores     device out [batch][n_q_heads][ctx_len] fp32 or NULL (s_t; -inf past T)
  *   workspace  device scratch of at least tq_decode_workspace_bytes(...) bytes,
- *              256-byte aligned; contents on entry are ignored
+ *              256-byte aligned, owned by the caller.  Zero-fill it once before the first
+ *              call that uses it: it holds per-(batch, kv head) arrival counters that every
+ *              completed call leaves at zero again.  Calls that share one workspace must not
+ *              overlap in time (same stream, or ordered by events).
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
                    int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
