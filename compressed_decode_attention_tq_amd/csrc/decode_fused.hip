@@ -32,6 +32,8 @@
 #include "tq_common.h"
 #include "tq_launch.h"
 
+#include <type_traits>
+
 namespace tq {
 namespace {
 
@@ -256,7 +258,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     };
     if (wave < n_tiles) load_keys(wave);
 
-    for (int tile = wave; tile < n_tiles; tile += kWaves) {
+    // one tile; PREFETCH issues the key loads of the wave's next tile.  The last tile is
+    // peeled off so that the loads are never conditional inside the loop body: a load
+    // issued on one path only would make every later wait cover it as well.
+    auto tile_body = [&](int tile, auto prefetch_tag) {
+      constexpr bool PREFETCH = decltype(prefetch_tag)::value;
       const int t0 = t_begin + tile * kTile;
       uint32_t vw[2][4];
 #pragma unroll
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         __builtin_amdgcn_sched_barrier(0);
       }
       const uint32_t nk_pair = nkw;
-      if (tile + kWaves < n_tiles) load_keys(tile + kWaves);
+      if (PREFETCH) load_keys(tile + kWaves);
 
       // lane holds rows 4q..4q+3 (heads 2q, 2q+1; fp16 and remainder rows) of token 16s+m_row
       if (NH == 8 || quarter < 2) {
@@ -340,20 +346,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       nk[1] = f16((uint16_t)(nk_pair >> 16));
       nv[0] = fmaxf(f16((uint16_t)(nvw & 0xffffu)), kNvFloor);
       nv[1] = fmaxf(f16((uint16_t)(nvw >> 16)), kNvFloor);
-      const bool tail = t0 + kTile > t_end;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] *= nk[tb];
+      if (t0 + kTile > t_end) {  // ragged last tile of the split (uniform branch)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          if (t0 + 2 * pr + tb >= t_end) {
+#pragma unroll
+            for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] = -INFINITY;
+          }
+      }
       float p[2][NH2];
       float vmax = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const bool ok = !tail || (t0 + 2 * pr + tb < t_end);
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int hh = 0; hh < NH2; ++hh) {
-          const float s2 = ok ? sc[tb][hh] * nk[tb] : -INFINITY;
-          sc[tb][hh] = s2;
-          p[tb][hh] = __builtin_amdgcn_exp2f(s2 - mr[hh]);
+          p[tb][hh] = __builtin_amdgcn_exp2f(sc[tb][hh] - mr[hh]);
           vmax = fmaxf(vmax, p[tb][hh] * nv[tb]);
         }
-      }
       if (__any(!(vmax <= kAMax))) {
         // move each head's reference to the tile's largest s + log2||v||, rescale
         float alpha[NH2];
@@ -446,7 +459,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       }
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
-    }
+    };
+    int tile = wave;
+    for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, std::true_type{});
+    if (tile < n_tiles) tile_body(tile, std::false_type{});
 
     // ---- combine the 8 waves of the split.  Round 1: (m, l) per head.
     float ltot[NH2];
