@@ -9,14 +9,26 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   prefill:          quantize a 32-layer cache of 32768 tokens (K and V of every layer).
 Inputs are resident in HBM before the timed region.  Decode workloads rotate over enough
 copies of the cache (one per step, like the layers of a model) that the reads come from
-HBM rather than the 256 MB Infinity Cache.
+HBM rather than the 256 MB Infinity Cache.  The steps are recorded once into a HIP graph
+and the graph is replayed, so the timed region holds GPU work only (no Python launch
+overhead between kernels); --eager times plain launches instead.
 
-Prints one JSON line (rank 0): the throughput, the roofline of the dominant kernel
-(decode attention, or quantize for prefill), and the CPU oracle timed on this host.
+Prints one JSON line: the throughput, the roofline of the dominant kernel (the single
+decode-attention kernel, or quantize for prefill) timed with HIP events on the stream the
+kernels run on, and the CPU oracle timed on this host.
+
+Two helper modes turn rocprofv3 output into the short summaries kept under profiles/:
+    python bench.py --summarize-stats DIR --name NAME --command "CMD"
+    python bench.py --summarize-traffic --fetch DIR --write DIR --workload W --kernel K \
+        --command "CMD"
+(--calibrate-copy makes a timed run end with plain 512 MiB device copies: the FETCH_SIZE
+and WRITE_SIZE they read scale the counters to bytes.)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -31,6 +43,11 @@ if ROOT not in sys.path:
 METRIC = "compressed-KV decode attention KV-tokens/s & HBM GB/s; quantize tokens/s"
 HBM_PEAK_GBS = 8000.0
 D = 128
+COPY_BYTES = 512 << 20
+CALIBRATION_COPIES = 5
+CALIBRATION_KERNEL = "copyBuffer"   # the HIP runtime's device-to-device copy kernel
+DECODE_KERNEL = "decode_fused_kernel"
+QUANTIZE_KERNEL = "quantize_kernel"
 
 
 def parse():
@@ -43,7 +60,15 @@ def parse():
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-iters", type=int, default=None)
+    p.add_argument("--eager", action="store_true", help="time plain launches, no HIP graph")
+    p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--summarize-stats", default=None)
+    p.add_argument("--summarize-traffic", action="store_true")
+    p.add_argument("--fetch", default=None)
+    p.add_argument("--write", default=None)
+    p.add_argument("--kernel", default=DECODE_KERNEL)
+    p.add_argument("--name", default=None)
+    p.add_argument("--command", default="")
     return p.parse_args()
 
 
@@ -58,8 +83,8 @@ def kernel_sources_digest() -> str:
 
 
 def traffic_from_profiles(workload: str, kernel: str, digest: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """Calibrated HBM bytes per launch from rocprofv3 counters, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -86,9 +111,15 @@ def cpu_cores():
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path would shard by "
-              "batch / kv head with no exchange, which this build does not launch.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): it measures the single-GPU "
+              "kernel; the path would shard by (batch, kv head) with no exchange.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -104,7 +135,6 @@ def main():
     if args.workload == "batch32k" and args.tau is None:
         tau = 0.0          # reported dense by default; pass --tau 1e-4 for Sparse V
     signs = inputs.rotation_signs().to(dev)
-    stream = torch.cuda.current_stream()
     digest = kernel_sources_digest()
 
     def log(*a):
@@ -116,19 +146,47 @@ def main():
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
     result["roofline"]["traffic"] = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
     result["sources_digest"] = digest
+    if args.calibrate_copy:
+        calibrate_copy(torch, log)
     print(json.dumps(result), flush=True)
 
 
-def _timed(fn, iters, torch, stream):
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(iters):
-        fn(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end)  # ms
+class Timer:
+    """Time of one iteration of a callable, with HIP events on the current stream.  Exactly
+    `n` iterations are timed: they are recorded once into a HIP graph, the graph is replayed
+    once untimed, then once between the events; or (eager) launched directly."""
+
+    def __init__(self, torch, eager):
+        self.torch = torch
+        self.eager = eager
+
+    def per_iteration_ms(self, fn, n, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            stream = torch.cuda.current_stream()
+            start.record(stream)
+            for i in range(n):
+                fn(i)
+            end.record(stream)
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / n
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return start.elapsed_time(end) / n
 
 
 def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
@@ -137,7 +195,8 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     cap = ctx
     per_copy = tq.code_bytes(D, bk, batch, hkv, cap) + tq.code_bytes(D, bv, batch, hkv, cap) + 4 * batch * hkv * cap
     copies = args.copies or max(1, math.ceil(600e6 / per_copy))
-    log(f"[bench] workload={w.name} tau={tau} copies={copies} cache/copy={per_copy / 1e6:.1f} MB")
+    log(f"[bench] workload={w.name} tau={tau} copies={copies} cache/copy={per_copy / 1e6:.1f} MB "
+        f"({'eager launches' if args.eager else 'HIP graph replay'})")
     g = inputs.generate(w, device=dev)
     k_all, v_all, q = g["k"], g["v"], g["q"].contiguous()
     caches = []
@@ -156,46 +215,48 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     scale = 1.0 / math.sqrt(D)
     torch.cuda.synchronize()
 
-    def step(i):
+    def append(i):
         kc, vc = caches[i % copies]
         tq.quantize_append(kc, k_new, ctx - 1)
         tq.quantize_append(vc, v_new, ctx - 1)
-        tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
 
     def decode_only(i):
         kc, vc = caches[i % copies]
         tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
 
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        step(i)
-    ms = _timed(step, args.steps, torch, stream)
-    ms_per_step = ms / args.steps
+    def step(i):
+        append(i)
+        decode_only(i)
+
+    timer = Timer(torch, args.eager)
+    steps = args.steps
+    ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     kv_tokens = batch * ctx
     value = kv_tokens / (ms_per_step / 1e3)
-    kiters = args.kernel_iters or max(args.steps, 50)
-    for i in range(5):
-        decode_only(i)
-    ms_k = _timed(decode_only, kiters, torch, stream) / kiters
+    ms_k = timer.per_iteration_ms(decode_only, max(args.steps, 2 * copies), 2)
+    ms_a = timer.per_iteration_ms(append, max(args.steps, 2 * copies), 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
     achieved = nbytes / (ms_k / 1e3) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, decode call {ms_k * 1e3:.1f} us, "
-        f"{achieved:.0f} GB/s algorithmic")
+        f"append (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic")
 
+    dense_single = tau == 0.0 and bk in (3, 4) and bv == 2 and w.group <= 8
     result = {
         "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16+f32",
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D,
                    "ctx": ctx, "bits_k": bk, "bits_v": bv, "sparse_v_tau": tau,
-                   "step": "append 1 token (K,V) + decode attention", "cache_copies": copies},
+                   "step": "append 1 token (K,V) + decode attention", "cache_copies": copies,
+                   "timing": "eager" if args.eager else "hip graph replay"},
         "decode_call_us": ms_k * 1e3,
-        "decode_gbs": achieved,
+        "append_kv_us": ms_a * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode attention call (split + merge kernels)",
-                     "bytes_per_launch": nbytes},
+                     "kernel": DECODE_KERNEL if dense_single
+                     else "decode attention call (split, Sparse-V and merge kernels)",
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3},
         "_kernel": "decode",
     }
     if not args.no_cpu_baseline:
@@ -263,12 +324,9 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
             tq.quantize_append(kc, k, 0)
             tq.quantize_append(vc, v, 0)
 
-    stream = torch.cuda.current_stream()
+    timer = Timer(torch, args.eager)
     steps = max(1, args.steps // 20)
-    for i in range(max(1, args.warmup // 20)):
-        step(i)
-    ms = _timed(step, steps, torch, stream)
-    ms_per_step = ms / steps
+    ms_per_step = timer.per_iteration_ms(step, steps, max(1, args.warmup // 20))
     tokens = layers * ctx
     value = tokens / (ms_per_step / 1e3)
     achieved = (in_bytes + out_bytes) / (ms_per_step / 1e3) / 1e9
@@ -278,10 +336,12 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": w.name, "layers": layers, "n_kv_heads": hkv, "d": D, "tokens": ctx,
-                   "bits": "K4/V3, layers 0,1,30,31 at 8/8", "packed_vs_bf16": in_bytes / out_bytes},
+                   "bits": "K4/V3, layers 0,1,30,31 at 8/8", "packed_vs_bf16": in_bytes / out_bytes,
+                   "timing": "eager" if args.eager else "hip graph replay"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "quantize (64 launches per step)", "bytes_per_launch": (in_bytes + out_bytes) / (2 * layers)},
+                     "kernel": QUANTIZE_KERNEL + " (64 launches per step)",
+                     "bytes_per_launch": (in_bytes + out_bytes) / (2 * layers)},
         "_kernel": "quantize",
     }
     if not args.no_cpu_baseline:
@@ -305,6 +365,93 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
                                   "kind": "oracle",
                                   "sample": f"layer 5, 1024 positions x {hkv} kv heads, K4/V3, quantize+pack, {reps} reps"}
     return result
+
+
+def calibrate_copy(torch, log):
+    """Plain device-to-device copies of COPY_BYTES each (read COPY_BYTES, write COPY_BYTES)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(CALIBRATION_COPIES):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration: 5 copies of {COPY_BYTES} bytes")
+
+
+# ---- rocprofv3 summaries -------------------------------------------------------------------
+
+def _short(name: str) -> str:
+    n = name.replace("void ", "").replace("tq::(anonymous namespace)::", "")
+    return n.split("(")[0][:60]
+
+
+def summarize_stats(args):
+    """Kernel table of a `rocprofv3 --kernel-trace --stats --output-format csv` run."""
+    files = glob.glob(os.path.join(args.summarize_stats, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {args.summarize_stats}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# {args.name}", "", f"command: {args.command}", "",
+             f"{'kernel':60s} {'calls':>7s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} {'total %':>8s}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name']):60s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+    out = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"{args.name}.txt"), "w") as fh:
+        fh.write(out)
+    print(out)
+
+
+def _counter_means(d, counter):
+    """Mean per-dispatch value of `counter` per kernel (short name) in a rocprofv3 --pmc run."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (_short(r["Kernel_Name"]), r.get("Dispatch_Id", ""))
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    per_kernel = {}
+    for (name, _), v in acc.items():
+        per_kernel.setdefault(name, []).append(v)
+    means = {k: sum(v) / len(v) for k, v in per_kernel.items()}
+    # the calibration copies are the largest dispatches of the runtime's copy kernel (it also
+    # serves the small host-to-device uploads of the run)
+    for k, v in per_kernel.items():
+        if CALIBRATION_KERNEL in k:
+            top = sorted(v)[-CALIBRATION_COPIES:]
+            means[k] = sum(top) / len(top)
+    return means, {k: len(v) for k, v in per_kernel.items()}
+
+
+def summarize_traffic(args):
+    """HBM bytes per launch of `--kernel`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by bytes / counter of the calibration copies of the same runs."""
+    fetch, nf = _counter_means(args.fetch, "FETCH_SIZE")
+    write, nw = _counter_means(args.write, "WRITE_SIZE")
+
+    def pick(table, pat):
+        keys = [k for k in table if pat in k]
+        if not keys:
+            sys.exit(f"no kernel matching {pat!r} in {sorted(table)}")
+        return keys[0]
+
+    kf, cf = pick(fetch, args.kernel), pick(fetch, CALIBRATION_KERNEL)
+    kw, cw = pick(write, args.kernel), pick(write, CALIBRATION_KERNEL)
+    scale_f = COPY_BYTES / (fetch[cf] * 1024.0)
+    scale_w = COPY_BYTES / (write[cw] * 1024.0)
+    fb = fetch[kf] * 1024.0 * scale_f
+    wb = write[kw] * 1024.0 * scale_w
+    rec = {"kernel": kf, "workload": args.workload, "fetch_kib_per_dispatch": fetch[kf],
+           "write_kib_per_dispatch": write[kw], "copy_fetch_kib": fetch[cf], "copy_write_kib": write[cw],
+           "copy_bytes": COPY_BYTES, "fetch_scale": scale_f, "write_scale": scale_w,
+           "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+           "dispatches": {"fetch": nf[kf], "write": nw[kw]}, "sources_digest": kernel_sources_digest(),
+           "command": args.command}
+    kname = "decode" if args.kernel == DECODE_KERNEL else "quantize"
+    with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{args.workload}.txt"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 if __name__ == "__main__":
