@@ -24,7 +24,7 @@ int check_cache(const tq_cache *c) {
       c->boundaries == nullptr || c->signs == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (!aligned(c->codes, 16) || !aligned(c->norms, 16) || !aligned(c->centroids, 4) ||
-      !aligned(c->boundaries, 4))
+      !aligned(c->boundaries, 4) || !aligned(c->signs, 16))
     return TQ_ERR_INVALID_ARG;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->capacity < 1) return TQ_ERR_INVALID_ARG;
   if (c->layout != TQ_LAYOUT_ROWS && c->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;

@@ -6,11 +6,15 @@
 // codebook, vector norm stored separately as fp16.  [inferrs] "inferrs & TurboQuant：本地
 // LLM 推理的内存革命", §核心技术: the rotation is a Walsh-Hadamard transform.
 //
-// Thread mapping: a block of 256 threads owns one 64-token chunk of one (batch, kv head)
-// plane; 4 consecutive lanes own one vector, 32 coordinates each.  The Walsh-Hadamard
-// transform runs 5 butterfly stages inside a lane and 2 across the lane quad.  Codes are
-// staged in LDS and written out in the cache layout, so a GROUP8 group (8 tokens) is always
-// produced by one block.
+// Quantize mapping: a block of 256 threads covers one 64-token chunk of one (batch, kv head)
+// plane and each of its waves owns 16 consecutive tokens (two 8-token value groups), so the
+// waves never wait for each other.  4 lanes hold one vector, 32 coordinates each: the
+// Walsh-Hadamard transform runs 5 butterfly stages inside a lane and 2 across the lane quad.
+// The code of u is found without a search loop: the codebook is symmetric (t_{L-2-j} = -t_j,
+// t_{L/2-1} = 0), so code = L/2 + #{positive t < u} for u > 0 and L/2 - 1 - #{positive t <= |u|}
+// otherwise, a count of compares against the L/2 - 1 positive boundaries held in scalar
+// registers (8-bit codebooks use a binary search over the boundaries in LDS).  Row-layout
+// codes are packed inside the lane; value-group codes go through a per-wave LDS transpose.
 #include "tq_common.h"
 #include "tq_launch.h"
 
@@ -36,13 +40,12 @@ __device__ __forceinline__ void load32(const void *x, size_t base, float v[32]) 
       uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        uint16_t lo = ws[e] & 0xffff, hi = ws[e] >> 16;
         if (DTYPE == TQ_BF16) {
-          v[8 * r + 2 * e] = __uint_as_float((uint32_t)lo << 16);
-          v[8 * r + 2 * e + 1] = __uint_as_float((uint32_t)hi << 16);
+          v[8 * r + 2 * e] = __uint_as_float(ws[e] << 16);
+          v[8 * r + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
         } else {
-          v[8 * r + 2 * e] = half_bits_to_float(lo);
-          v[8 * r + 2 * e + 1] = half_bits_to_float(hi);
+          v[8 * r + 2 * e] = half_bits_to_float((uint16_t)(ws[e] & 0xffffu));
+          v[8 * r + 2 * e + 1] = half_bits_to_float((uint16_t)(ws[e] >> 16));
         }
       }
     }
@@ -74,25 +77,61 @@ __device__ __forceinline__ void quad_fwht(float v[32], int q) {
   }
 }
 
-template <int DTYPE>
+// code = #{j : t_j < u} for a symmetric codebook of 2^BITS levels (BITS <= 4); `pos` holds
+// the positive boundaries t_{L/2} .. t_{L-2}.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(float u, const float *pos) {
+  constexpr int L = 1 << BITS;
+  // for u < 0 count the boundaries <= |u|: compare against the next float above |u|
+  float a = fabsf(u);
+  if (u < 0.f) a = __uint_as_float(__float_as_uint(a) + 1u);
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int k = 0; k < L / 2 - 1; ++k) cnt += pos[k] < a ? 1u : 0u;
+  return u > 0.f ? (uint32_t)(L / 2) + cnt : (uint32_t)(L / 2 - 1) - cnt;
+}
+
+// code = #{j : t_j < u} by binary search over 255 boundaries in LDS.
+__device__ __forceinline__ uint32_t code_of_8(float u, const float *bnd) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (int step = 128; step >= 1; step >>= 1)
+    if (bnd[idx + step - 1] < u) idx += step;
+  return idx;
+}
+
+template <int DTYPE, int BITS, int LAYOUT>
 __global__ __launch_bounds__(256) void quantize_kernel(CacheView c, const void *__restrict__ x,
                                                        int start_pos, int n_tokens) {
+  constexpr int L = 1 << BITS;
   const int h = blockIdx.y, b = blockIdx.z;
   const int chunk0 = (start_pos / kChunk + (int)blockIdx.x) * kChunk;
   const int lo = max(chunk0, start_pos), hi = min(chunk0 + kChunk, start_pos + n_tokens);
-  const int bits = c.bits, levels = 1 << bits;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wt0 = chunk0 + 16 * wave;
+  if (wt0 + 16 <= lo || wt0 >= hi) return;  // no token of this wave is in the range
 
-  __shared__ uint8_t codes[kChunk][kD];
-  __shared__ float bnd[256];
-  for (int i = threadIdx.x; i < levels - 1; i += blockDim.x) bnd[i] = c.boundaries[i];
-  __syncthreads();
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][16][kD];  // value-group transpose
+  __shared__ float bnd8[4][256];                                     // 8-bit boundaries
 
-  const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const int t = chunk0 + j;
+  const int j = lane >> 2, q = lane & 3;
+  const int t = wt0 + j;
   const bool valid = t >= lo && t < hi;
+
+  float pos[L / 2 > 1 ? L / 2 - 1 : 1];
+  if (BITS <= 4) {
+#pragma unroll
+    for (int k = 0; k < L / 2 - 1; ++k) pos[k] = c.boundaries[L / 2 + k];
+  } else {
+    for (int k = lane; k < L - 1; k += 64) bnd8[wave][k] = c.boundaries[k];
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
+
   float v[32];
   if (valid) {
-    size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
+    const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
     load32<DTYPE>(x, row * kD + 32 * q, v);
   } else {
 #pragma unroll
@@ -103,54 +142,98 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheView c, const void *
   for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
   ss += __shfl_xor(ss, 1);
   ss += __shfl_xor(ss, 2);
+  {
+    const int4 sw0 = *reinterpret_cast<const int4 *>(c.signs + 32 * q);
+    const int4 sw1 = *reinterpret_cast<const int4 *>(c.signs + 32 * q + 16);
+    const int sw[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = c.signs[32 * q + e] < 0 ? -v[e] : v[e];
+    for (int e = 0; e < 32; ++e) {  // flip the sign bit where s_i = -1 (byte 0xff)
+      const uint32_t neg = ((uint32_t)sw[e >> 2] >> (8 * (e & 3) + 7)) & 1u;
+      v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (neg << 31));
+    }
+  }
   quad_fwht(v, q);
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
+  uint32_t code[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     const float u = v[e] * inv;
-    int idx = 0;
-    for (int step = levels >> 1; step >= 1; step >>= 1)
-      if (u > bnd[idx + step - 1]) idx += step;
-    codes[j][32 * q + e] = (uint8_t)idx;
+    code[e] = BITS <= 4 ? code_of<BITS <= 4 ? BITS : 4>(u, pos) : code_of_8(u, bnd8[wave]);
   }
   if (valid && q == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
-  __syncthreads();
 
   uint8_t *plane = c.plane(b, h);
-  if (c.layout == TQ_LAYOUT_ROWS) {
-    const int words = 4 * bits;  // 16*bits bytes per row
-    for (int idx = threadIdx.x; idx < kChunk * words; idx += blockDim.x) {
-      const int jj = idx / words, w = idx % words, tt = chunk0 + jj;
-      if (tt < lo || tt >= hi) continue;
-      uint64_t acc = 0;
-      for (int i = (32 * w) / bits; i < kD; ++i) {
-        const int sh = bits * i - 32 * w;
-        if (sh >= 32) break;
-        const uint64_t cv = codes[jj][i];
-        acc |= sh >= 0 ? (cv << sh) : (cv >> (-sh));
-      }
-      reinterpret_cast<uint32_t *>(plane + (size_t)tt * 16 * bits)[w] = (uint32_t)acc;
+  if (LAYOUT == TQ_LAYOUT_ROWS) {
+    // the lane's 32 codes are bits [32*BITS*q, 32*BITS*(q+1)) of the token's row
+    uint32_t w[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int bit = e * BITS;
+      w[bit >> 5] |= code[e] << (bit & 31);
+      if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+    }
+    if (valid) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)t * 16 * BITS + 4 * BITS * q);
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) dst[k] = w[k];
     }
   } else {
-    for (int idx = threadIdx.x; idx < (kChunk / 8) * kD; idx += blockDim.x) {
-      const int grp = idx / kD, i = idx % kD, tg = chunk0 + 8 * grp;
-      uint64_t val = 0, mask = 0;
-      const uint64_t field = (1ull << bits) - 1ull;
-      for (int r = 0; r < 8; ++r) {
-        const int tt = tg + r;
-        if (tt < lo || tt >= hi) continue;
-        val |= (uint64_t)codes[8 * grp + r][i] << (r * bits);
-        mask |= field << (r * bits);
+    // stage codes [token][coord] as bytes, then lane r of a group builds coordinates
+    // 4r .. 4r+3 of its group: 8 tokens x BITS bits per coordinate, BITS bytes each
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pk[k] = code[16 * r + 4 * k] | (code[16 * r + 4 * k + 1] << 8) | (code[16 * r + 4 * k + 2] << 16) |
+                (code[16 * r + 4 * k + 3] << 24);
+      *reinterpret_cast<uint4 *>(&stage[wave][j][32 * q + 16 * r]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int gi = lane >> 5, r = lane & 31;
+    const int tg = wt0 + 8 * gi;  // first token of the group
+    uint64_t chunk[4] = {0, 0, 0, 0}, mask = 0;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const uint32_t cw = *reinterpret_cast<const uint32_t *>(&stage[wave][8 * gi + tt][4 * r]);
+      const bool in = tg + tt >= lo && tg + tt < hi;
+      if (in) mask |= (uint64_t)(L - 1) << (tt * BITS);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) chunk[k] |= (uint64_t)((cw >> (8 * k)) & 0xffu) << (tt * BITS);
+    }
+    if (mask != 0) {
+      // the 4 coordinate chunks are 4*BITS consecutive bytes: pack them into BITS dwords
+      uint32_t out[BITS], msk[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) { out[k] = 0u; msk[k] = 0u; }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int bit = k * 8 * BITS;  // bit offset of chunk k
+        const uint64_t cv = chunk[k] & mask;
+#pragma unroll
+        for (int part = 0; part < (8 * BITS + 31) / 32 + 1; ++part) {
+          const int wb = (bit >> 5) + part;  // destination dword
+          if (wb >= BITS) break;
+          const int sh = 32 * wb - bit;     // chunk bit that lands at bit 0 of dword wb
+          if (sh >= 8 * BITS) break;
+          if (sh >= 0) {
+            out[wb] |= (uint32_t)(cv >> sh);
+            msk[wb] |= (uint32_t)(mask >> sh);
+          } else {
+            out[wb] |= (uint32_t)(cv << (-sh));
+            msk[wb] |= (uint32_t)(mask << (-sh));
+          }
+        }
       }
-      if (mask == 0) continue;
-      uint8_t *dst = plane + (size_t)(tg >> 3) * kD * bits + (size_t)i * bits;
-      for (int by = 0; by < bits; ++by) {
-        const uint8_t m = (uint8_t)(mask >> (8 * by)), nv = (uint8_t)(val >> (8 * by));
-        if (m == 0xff) dst[by] = nv;
-        else if (m != 0) dst[by] = (uint8_t)((dst[by] & ~m) | (nv & m));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)(tg >> 3) * kD * BITS + 4 * BITS * r);
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) {
+        if (msk[k] == 0xffffffffu) dst[k] = out[k];
+        else if (msk[k] != 0u) dst[k] = (dst[k] & ~msk[k]) | out[k];
       }
     }
   }
@@ -186,18 +269,34 @@ __global__ __launch_bounds__(256) void dequantize_kernel(CacheView c, void *__re
   }
 }
 
+
+template <int DTYPE, int BITS>
+void launch_q(const CacheView &c, dim3 grid, const void *x, int start_pos, int n_tokens, hipStream_t stream) {
+  if (c.layout == TQ_LAYOUT_ROWS)
+    quantize_kernel<DTYPE, BITS, TQ_LAYOUT_ROWS><<<grid, 256, 0, stream>>>(c, x, start_pos, n_tokens);
+  else
+    quantize_kernel<DTYPE, BITS, TQ_LAYOUT_GROUP8><<<grid, 256, 0, stream>>>(c, x, start_pos, n_tokens);
+}
+
+template <int DTYPE>
+void launch_qd(const CacheView &c, dim3 grid, const void *x, int start_pos, int n_tokens, hipStream_t stream) {
+  switch (c.bits) {
+    case 2: launch_q<DTYPE, 2>(c, grid, x, start_pos, n_tokens, stream); break;
+    case 3: launch_q<DTYPE, 3>(c, grid, x, start_pos, n_tokens, stream); break;
+    case 4: launch_q<DTYPE, 4>(c, grid, x, start_pos, n_tokens, stream); break;
+    default: launch_q<DTYPE, 8>(c, grid, x, start_pos, n_tokens, stream); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
                            int start_pos, int n_tokens, hipStream_t stream) {
   const int first = start_pos / kChunk, last = (start_pos + n_tokens - 1) / kChunk;
   dim3 grid(last - first + 1, c.n_kv_heads, batch);
-  if (x_dtype == TQ_F32)
-    quantize_kernel<TQ_F32><<<grid, 256, 0, stream>>>(c, x, start_pos, n_tokens);
-  else if (x_dtype == TQ_BF16)
-    quantize_kernel<TQ_BF16><<<grid, 256, 0, stream>>>(c, x, start_pos, n_tokens);
-  else
-    quantize_kernel<TQ_F16><<<grid, 256, 0, stream>>>(c, x, start_pos, n_tokens);
+  if (x_dtype == TQ_F32) launch_qd<TQ_F32>(c, grid, x, start_pos, n_tokens, stream);
+  else if (x_dtype == TQ_BF16) launch_qd<TQ_BF16>(c, grid, x, start_pos, n_tokens, stream);
+  else launch_qd<TQ_F16>(c, grid, x, start_pos, n_tokens, stream);
   return hipGetLastError();
 }
 

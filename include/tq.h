@@ -79,9 +79,11 @@ enum tq_layout { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_GROUP8 = 1 };
  *   codes       [batch][n_kv_heads][capacity * d * bits / 8] bytes, 16-byte aligned
  *   norms       [batch][n_kv_heads][capacity] IEEE fp16 bit patterns, 16-byte aligned
  *   centroids   [1 << bits] fp32, ascending (from tq_make_codebook_table)
- *   boundaries  [(1 << bits) - 1] fp32 midpoints (from tq_make_codebook_table)
- *   signs       [d] int8, each +1 or -1: the diagonal of the rotation (shared by the
- *               K and V caches of a layer)
+ *   boundaries  [(1 << bits) - 1] fp32 midpoints (from tq_make_codebook_table); the
+ *               kernels rely on the symmetry that table has: boundaries[L-2-j] =
+ *               -boundaries[j] and boundaries[L/2-1] = 0 (L = 1 << bits)
+ *   signs       [d] int8, each +1 or -1, 16-byte aligned: the diagonal of the rotation
+ *               (shared by the K and V caches of a layer)
  * capacity must be a positive multiple of 64. */
 typedef struct tq_cache {
   int32_t d;
