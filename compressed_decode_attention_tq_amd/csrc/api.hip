@@ -52,13 +52,17 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
 }  // namespace
 
-SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len) {
+SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len, int group) {
   const long units = (long)batch * n_kv_heads;
   const long target_blocks = 2048;
+  // a split's softmax weights [split_len][group] fit the Sparse-V pass's LDS
+  const long padded = group <= 4 ? 4 : group <= 8 ? 8 : 16;
+  const long max_len = (kSparseWeights / padded) / kSplitAlign * kSplitAlign;
   long s_target = (target_blocks + units - 1) / units;
   if (s_target < 1) s_target = 1;
   long len = (ctx_len + s_target - 1) / s_target;
   len = (len + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  if (len > max_len) len = max_len;
   if (len < kSplitAlign) len = kSplitAlign;
   long n = (ctx_len + len - 1) / len;
   if (n < 1) n = 1;
@@ -83,7 +87,7 @@ SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len) {
 
 WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  bool sparse) {
-  const SplitPlan p = plan_splits(batch, n_kv_heads, ctx_len);
+  const SplitPlan p = plan_splits(batch, n_kv_heads, ctx_len, n_q_heads / n_kv_heads);
   const SplitPlan fp = plan_fused(batch, n_kv_heads, ctx_len);
   const size_t heads = (size_t)batch * n_q_heads * p.n_splits;
   const size_t fheads = (size_t)batch * n_q_heads * fp.n_splits;
@@ -210,7 +214,7 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.scale = scale;
   a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
   a.sparse = sparse ? 1 : 0;
-  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len);
+  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
   a.fplan = plan_fused(k->batch, k->n_kv_heads, ctx_len);
   a.out = out;
   a.lse = lse;

@@ -86,20 +86,32 @@ __device__ __forceinline__ uint32_t pst_off(int row, int unit) {
   return kPBase + (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
 }
 
+// Codebook staging: word k < 16 holds the K centroid k as {fp16 value, fp16 remainder},
+// word 16 + k the fp16 V centroid k; c is the centroid this thread loaded.
 template <int BK>
-__device__ void build_tables(uint8_t *lds, const float *kc, const float *vc) {
+__device__ void stage_codebooks(uint32_t *st, float c) {
+  const int t = threadIdx.x;
+  if (t < (1 << BK)) {
+    const uint16_t h = h16(c);
+    st[t] = (uint32_t)h | ((uint32_t)h16(c - f16(h)) << 16);
+  } else if (t >= 16 && t < 20) {
+    st[t] = h16(c);
+  }
+}
+
+template <int BK>
+__device__ void build_tables(uint8_t *lds, const uint32_t *st) {
   for (int idx = threadIdx.x; idx < 256 * 32; idx += blockDim.x) {
     const int e = idx >> 5, copy = idx & 31;
-    const float c0 = BK == 4 ? kc[e & 15] : kc[e & 7];
-    const float c1 = BK == 4 ? kc[e >> 4] : kc[(e >> 3) & 7];
-    const uint16_t h0 = h16(c0), h1 = h16(c1);
+    const uint32_t c0 = st[BK == 4 ? (e & 15) : (e & 7)];
+    const uint32_t c1 = st[BK == 4 ? (e >> 4) : ((e >> 3) & 7)];
     uint2 kv;
-    kv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    kv.y = (uint32_t)h16(c0 - f16(h0)) | ((uint32_t)h16(c1 - f16(h1)) << 16);
+    kv.x = (c0 & 0xffffu) | (c1 << 16);
+    kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
     *reinterpret_cast<uint2 *>(lds + e * 256 + copy * 8) = kv;
     uint2 vv;
-    vv.x = (uint32_t)h16(vc[e & 3]) | ((uint32_t)h16(vc[(e >> 2) & 3]) << 16);
-    vv.y = (uint32_t)h16(vc[(e >> 4) & 3]) | ((uint32_t)h16(vc[(e >> 6) & 3]) << 16);
+    vv.x = st[16 + (e & 3)] | (st[16 + ((e >> 2) & 3)] << 16);
+    vv.y = st[16 + ((e >> 4) & 3)] | (st[16 + ((e >> 6) & 3)] << 16);
     *reinterpret_cast<uint2 *>(lds + kVBase + e * 256 + copy * 8) = vv;
   }
 }
@@ -158,11 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   uint8_t *wbuf = lds + kWBase + wave * 4096;
   float *qrot = reinterpret_cast<float *>(lds + kWBase);  // [NH][128] between tiles
 
-  build_tables<BK>(lds, a.k.centroids, a.v.centroids);
-  if (NH == 4) {  // P' rows 8..15 stay zero for the whole launch
+  if (NH == 4)  // P' rows 8..15 stay zero for the whole launch
     *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
-  }
-  __syncthreads();
 
   const int n_items = a.batch * a.n_kv_heads * S;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -175,15 +184,86 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     const int t_end = min(t_begin + L, T);
     const int qh0 = kvh * g;  // first query head of the group
 
+    const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+    const uint32_t span_tok = (uint32_t)n_tiles * kTile;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v.plane(b, kvh) + (size_t)t_begin * 32, span_tok * 32);
+    const __amdgpu_buffer_rsrc_t knrs = make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    const __amdgpu_buffer_rsrc_t vnrs = make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    const uint32_t k_voff = (uint32_t)m_row * KROW + (uint32_t)quarter * (4 * BK);
+    const uint32_t v_voff = (uint32_t)quarter * 256u + (uint32_t)m_row * 16u;
+    const uint32_t n_voff = (uint32_t)pr * 4u;
+
+    uint32_t kw[4][4];
+    uint32_t nkw = 0;
+    auto load_keys = [&](int tile) {
+      // the whole offset is in the vector offset: a tile past the split's end lies outside
+      // the buffer's range and reads as zeros without touching memory
+      const uint32_t so = (uint32_t)tile * (kTile * KROW);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (BK == 4) {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + so + s * 16 * KROW, 0, 0);
+          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = w[3];
+        } else {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b96(krs, k_voff + so + s * 16 * KROW, 0, 0);
+          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = 0u;
+        }
+      }
+      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
+    };
+
+    // the small loads the setup needs go out first, then the wave's first key tile; nothing
+    // is used until all of them are in flight (a use would make the wave wait right there)
+    const bool first_item = item == (int)blockIdx.x;
+    float kcs[1 << BK], vcs[4];
+    if (first_item) {
+#pragma unroll
+      for (int i = 0; i < (1 << BK); ++i) kcs[i] = a.k.centroids[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vcs[i] = a.v.centroids[i];
+    }
+    const int qhead = qh0 + min(wave, g - 1);
+    const size_t qbase = ((size_t)b * a.n_q_heads + qhead) * kD + 2 * lane;
+    uint32_t qw0 = 0u, qw1 = 0u;
+    if (a.q_dtype == TQ_F32) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(a.q) + qbase);
+      qw0 = w.x;
+      qw1 = w.y;
+    } else {
+      qw0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qbase);
+    }
+    const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
+    load_keys(wave);
+    if (first_item) {  // the code tables, once per workgroup
+      float cent = 0.f;
+      const int t = threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < (1 << BK); ++i) cent = t == i ? kcs[i] : cent;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cent = t == 16 + i ? vcs[i] : cent;
+      uint32_t *st = reinterpret_cast<uint32_t *>(lds + kWBase + 7 * 4096);
+      stage_codebooks<BK>(st, cent);
+      __syncthreads();
+      build_tables<BK>(lds, st);
+    }
+
     // ---- rotated query group: wave h rotates head h into qrot[h]
     if (wave < NH) {
       float x0 = 0.f, x1 = 0.f;
       if (wave < g) {
-        const size_t base = ((size_t)b * a.n_q_heads + qh0 + wave) * kD + 2 * lane;
-        x0 = load_elem(a.q, base, a.q_dtype);
-        x1 = load_elem(a.q, base + 1, a.q_dtype);
-        if (a.k.signs[2 * lane] < 0) x0 = -x0;
-        if (a.k.signs[2 * lane + 1] < 0) x1 = -x1;
+        if (a.q_dtype == TQ_F32) {
+          x0 = __uint_as_float(qw0);
+          x1 = __uint_as_float(qw1);
+        } else if (a.q_dtype == TQ_BF16) {
+          x0 = __uint_as_float(qw0 << 16);
+          x1 = __uint_as_float(qw0 & 0xffff0000u);
+        } else {
+          x0 = f16((uint16_t)(qw0 & 0xffffu));
+          x1 = f16((uint16_t)(qw0 >> 16));
+        }
+        if (sgn & 0x80u) x0 = -x0;
+        if (sgn & 0x8000u) x1 = -x1;
       }
       const float y0 = x0 + x1, y1 = x0 - x1;
       x0 = y0;
@@ -230,33 +310,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 #pragma unroll
     for (int n = 0; n < 8; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-    const uint32_t span_tok = (uint32_t)n_tiles * kTile;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v.plane(b, kvh) + (size_t)t_begin * 32, span_tok * 32);
-    const __amdgpu_buffer_rsrc_t knrs = make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
-    const __amdgpu_buffer_rsrc_t vnrs = make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
-    const uint32_t k_voff = (uint32_t)m_row * KROW + (uint32_t)quarter * (4 * BK);
-    const uint32_t v_voff = (uint32_t)quarter * 256u + (uint32_t)m_row * 16u;
-    const uint32_t n_voff = (uint32_t)pr * 4u;
-
-    uint32_t kw[4][4];
-    uint32_t nkw = 0;
-    auto load_keys = [&](int tile) {
-      const int so = tile * kTile * KROW;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (BK == 4) {
-          const auto w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + s * 16 * KROW, so, 0);
-          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = w[3];
-        } else {
-          const auto w = __builtin_amdgcn_raw_buffer_load_b96(krs, k_voff + s * 16 * KROW, so, 0);
-          kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = 0u;
-        }
-      }
-      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff, tile * kTile * 2, 0);
-    };
-    if (wave < n_tiles) load_keys(wave);
 
     // one tile; PREFETCH issues the key loads of the wave's next tile.  The last tile is
     // peeled off so that the loads are never conditional inside the loop body: a load
@@ -267,10 +320,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       uint32_t vw[2][4];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + c * 1024, tile * kTile * 32, 0);
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + (uint32_t)tile * (kTile * 32) + c * 1024, 0, 0);
         vw[c][0] = w[0]; vw[c][1] = w[1]; vw[c][2] = w[2]; vw[c][3] = w[3];
       }
-      const uint32_t nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff, tile * kTile * 2, 0);
+      const uint32_t nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
 
       // ---- scores: sub-tile s, 16-coordinate chunk m -> key fields 2m, 2m+1 of the quarter
       auto key_operands = [&](int m, half8 (&dst)[4]) {

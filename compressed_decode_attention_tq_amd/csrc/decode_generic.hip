@@ -218,20 +218,50 @@ __global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
   }
 }
 
-// Pass 2 of Sparse V: exact keep rule with the merged LSE, V rows read only when kept.
+// Sparse V, second pass, one block per split.  The exact weights p = exp(s - LSE) of the
+// candidate rows (zero where p < tau), times the row's value norm, go to an LDS table
+// w[split_len][GP] (GP = the group size padded to 4, 8 or 16; padding heads stay 0); then
+// the block reads only the split's 8-token value groups that hold a kept row.  A group is
+// 128 coordinates of BV contiguous bytes, so one wave reads a whole group with lane l
+// taking coordinates 2l and 2l+1 (2*BV bytes, one coalesced access), and adds
+// w[t][j] * c_V[code] for every head j; the four waves take every fourth group, a batch of
+// groups in flight at a time, and are summed through LDS at the end.
+template <int BV>
+__device__ __forceinline__ void load_coord_pair(const uint8_t *src, uint64_t &lo, uint64_t &hi) {
+  if constexpr (BV == 2) {
+    const uint32_t x = *reinterpret_cast<const uint32_t *>(src);
+    lo = x & 0xFFFFu;
+    hi = x >> 16;
+  } else if constexpr (BV == 3) {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(src);
+    const uint32_t u0 = h[0], u1 = h[1], u2 = h[2];
+    lo = u0 | (uint64_t)(u1 & 0xFFu) << 16;
+    hi = (u1 >> 8) | (uint64_t)u2 << 8;
+  } else if constexpr (BV == 4) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(src);
+    lo = x.x;
+    hi = x.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4 *>(src);
+    lo = x.x | (uint64_t)x.y << 32;
+    hi = x.z | (uint64_t)x.w << 32;
+  }
+}
+
+template <int GP, int BV>
 __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int g = a.group, S = a.plan.n_splits;
+  const int g = a.group, S = a.plan.n_splits, L = a.plan.split_len;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float lse_s[16];
-  __shared__ float lutV[256];
-  __shared__ float pbuf[16][256];
-  __shared__ int toks[256];
-  __shared__ float nvs[256];
-  __shared__ int keep_any[256];
+  __shared__ float lutV[1 << BV];
+  __shared__ __align__(16) float w[kSparseWeights];  // [token in split][GP]; then [wave][GP][kD]
+  __shared__ int gflag[kSparseWeights / 32];         // 8-token groups holding a kept row
+  static_assert(4 * GP * kD <= kSparseWeights, "wave sums fit the weight table");
 
-  const int bv = a.v.bits;
-  for (int i = tid; i < (1 << bv); i += blockDim.x) lutV[i] = a.v.centroids[i];
+  for (int i = tid; i < (1 << BV); i += blockDim.x) lutV[i] = a.v.centroids[i];
+  for (int i = tid; i < L * GP; i += blockDim.x) w[i] = 0.f;
+  for (int i = tid; i < L / 8; i += blockDim.x) gflag[i] = 0;
   for (int j = wave; j < g; j += 4) {
     const float2 *ml = a.part_ml + ((size_t)b * a.n_q_heads + kvh * g + j) * S;
     float mx = -INFINITY;
@@ -246,52 +276,88 @@ __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
   }
   __syncthreads();
 
+  const int t_begin = s * L;
   const int count = a.cand_count[((size_t)b * a.n_kv_heads + kvh) * S + s];
   const float *base =
-      a.cand + (((size_t)b * a.n_kv_heads + kvh) * S + s) * (size_t)a.plan.split_len * (1 + g);
-  const uint8_t *vplane = a.v.plane(b, kvh);
+      a.cand + (((size_t)b * a.n_kv_heads + kvh) * S + s) * (size_t)L * (1 + g);
   const uint16_t *vnorm = a.v.norm_plane(b, kvh);
-  const int ci = tid & (kD - 1), jj = tid >> 7;
-  float acc[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+  for (int r = tid; r < count; r += blockDim.x) {
+    const float *rec = base + (size_t)r * (1 + g);
+    const int t = __float_as_int(rec[0]);
+    const float nv = half_bits_to_float(vnorm[t]);
+    const int tl = t - t_begin;
+    bool any = false;
+    for (int j = 0; j < g; ++j) {
+      const float z = rec[1 + j] - lse_s[j];
+      const bool keep = z >= a.ln_tau;
+      w[tl * GP + j] = keep ? __expf(z) * nv : 0.f;
+      any |= keep;
+    }
+    if (any) gflag[tl >> 3] = 1;
+  }
+  __syncthreads();
 
-  for (int c0 = 0; c0 < count; c0 += 256) {
-    const int r_idx = c0 + tid;
-    if (r_idx < count) {
-      const float *rec = base + (size_t)r_idx * (1 + g);
-      const int t = __float_as_int(rec[0]);
-      toks[tid] = t;
-      nvs[tid] = half_bits_to_float(vnorm[t]);
-      int any = 0;
+  const uint8_t *vgroups = a.v.plane(b, kvh) + (size_t)(t_begin >> 3) * kD * BV + 2 * lane * BV;
+  float acc_a[GP], acc_b[GP];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < g) {
-          const float z = rec[1 + j] - lse_s[j];
-          const float p = z >= a.ln_tau ? __expf(z) : 0.f;
-          pbuf[j][tid] = p;
-          any |= p > 0.f;
+  for (int j = 0; j < GP; ++j) acc_a[j] = acc_b[j] = 0.f;
+  const int n_groups = L / 8;
+  constexpr uint32_t kMask = (1u << BV) - 1u;
+  constexpr int kBatch = BV == 8 ? 8 : 16;
+  for (int g0 = wave; g0 < n_groups; g0 += 4 * kBatch) {
+    uint64_t lo[kBatch], hi[kBatch];
+    bool on[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int gi = g0 + 4 * u;
+      on[u] = gi < n_groups && gflag[gi];
+      lo[u] = hi[u] = 0;
+      if (on[u]) load_coord_pair<BV>(vgroups + (size_t)gi * kD * BV, lo[u], hi[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (!on[u]) continue;
+      const float4 *wr = reinterpret_cast<const float4 *>(w + (size_t)(8 * (g0 + 4 * u)) * GP);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float va = lutV[(uint32_t)(lo[u] >> (r * BV)) & kMask];
+        const float vb = lutV[(uint32_t)(hi[u] >> (r * BV)) & kMask];
+#pragma unroll
+        for (int q = 0; q < GP / 4; ++q) {
+          const float4 ww = wr[r * (GP / 4) + q];
+          acc_a[4 * q + 0] = fmaf(ww.x, va, acc_a[4 * q + 0]);
+          acc_a[4 * q + 1] = fmaf(ww.y, va, acc_a[4 * q + 1]);
+          acc_a[4 * q + 2] = fmaf(ww.z, va, acc_a[4 * q + 2]);
+          acc_a[4 * q + 3] = fmaf(ww.w, va, acc_a[4 * q + 3]);
+          acc_b[4 * q + 0] = fmaf(ww.x, vb, acc_b[4 * q + 0]);
+          acc_b[4 * q + 1] = fmaf(ww.y, vb, acc_b[4 * q + 1]);
+          acc_b[4 * q + 2] = fmaf(ww.z, vb, acc_b[4 * q + 2]);
+          acc_b[4 * q + 3] = fmaf(ww.w, vb, acc_b[4 * q + 3]);
         }
       }
-      keep_any[tid] = any;
     }
-    __syncthreads();
-    const int n = min(256, count - c0);
-    for (int tt = 0; tt < n; ++tt) {
-      if (!keep_any[tt]) continue;
-      const int t = toks[tt];
-      const float val =
-          lutV[read_field(vplane, code_bit_offset(TQ_LAYOUT_GROUP8, bv, t, ci), bv)] * nvs[tt];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (jj + 2 * r < g) acc[r] = fmaf(pbuf[jj + 2 * r][tt], val, acc[r]);
-    }
-    __syncthreads();
   }
+  __syncthreads();  // weights no longer read: the table now holds the wave sums
+  float2 *red = reinterpret_cast<float2 *>(w);
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int j = jj + 2 * r;
-    if (j < g) a.part_o[(((size_t)b * a.n_q_heads + kvh * g + j) * S + s) * kD + ci] = acc[r];
+  for (int j = 0; j < GP; ++j) red[(wave * GP + j) * (kD / 2) + lane] = make_float2(acc_a[j], acc_b[j]);
+  __syncthreads();
+  for (int e = tid; e < g * kD; e += blockDim.x) {
+    const int j = e / kD, c = e % kD;
+    float o = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) o += w[(wv * GP + j) * kD + c];
+    a.part_o[(((size_t)b * a.n_q_heads + kvh * g + j) * S + s) * kD + c] = o;
+  }
+}
+
+template <int GP>
+void launch_sparse_v(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  switch (a.v.bits) {
+    case 2: decode_sparse_v<GP, 2><<<grid, 256, 0, stream>>>(a); break;
+    case 3: decode_sparse_v<GP, 3><<<grid, 256, 0, stream>>>(a); break;
+    case 4: decode_sparse_v<GP, 4><<<grid, 256, 0, stream>>>(a); break;
+    default: decode_sparse_v<GP, 8><<<grid, 256, 0, stream>>>(a); break;
   }
 }
 
@@ -401,7 +467,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   }
   if (e != hipSuccess) return e;
   if (a.sparse) {
-    decode_sparse_v<<<grid_split, 256, 0, stream>>>(a);
+    if (a.group <= 4) launch_sparse_v<4>(a, grid_split, stream);
+    else if (a.group <= 8) launch_sparse_v<8>(a, grid_split, stream);
+    else launch_sparse_v<16>(a, grid_split, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

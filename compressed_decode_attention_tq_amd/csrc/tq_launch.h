@@ -9,13 +9,14 @@ namespace tq {
 // (a multiple of kSplitAlign) of one (batch, kv head); the number of splits is chosen
 // so the grid has enough blocks for the chip.  The same function sizes the workspace.
 constexpr int kSplitAlign = 64;
+constexpr int kSparseWeights = 8192;  // floats of the Sparse-V pass's per-split weight table
 
 struct SplitPlan {
   int n_splits;
   int split_len;
 };
 
-SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len);
+SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len, int group);
 // Splits of the single-launch dense path: about one workgroup per CU, whole 64-token tiles.
 SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len);
 

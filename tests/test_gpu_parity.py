@@ -202,11 +202,21 @@ def test_decode_empty_context(signs, golden_codebooks):
     ("batch32k", 2, 8, 2, 1300, 1344, 3, 2, 1e-4),
     ("llama8k", 1, 8, 2, 777, 832, 4, 2, 1e-2),
     ("ctx131k", 1, 16, 1, 700, 704, 4, 2, 0.3),
+    ("llama8k", 1, 2, 2, 333, 384, 8, 8, 1e-3),
+    ("ctx131k", 1, 16, 1, 600, 640, 4, 3, 1e-3),
+    ("llama8k", 1, 6, 2, 500, 512, 4, 4, 1e-3),
 ])
 def test_decode_sparse_v_matches_oracle(case, signs, golden_codebooks):
     name, *shape, tau = case
     _say("decode sparse", case)
     _decode_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, tau=tau)
+
+
+def test_decode_sparse_v_ragged_lengths(signs, golden_codebooks):
+    _say("decode sparse seq_lens")
+    w = inputs.WORKLOADS["llama8k"]
+    _decode_case(w, signs, golden_codebooks, 4, 8, 2, 900, 960, 4, 2, seq_lens=[900, 0, 1, 513],
+                 tau=1e-3)
 
 
 def test_decode_is_deterministic(signs):
