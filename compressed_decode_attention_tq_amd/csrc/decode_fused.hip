@@ -86,33 +86,44 @@ __device__ __forceinline__ uint32_t pst_off(int row, int unit) {
   return kPBase + (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
 }
 
-// Codebook staging: word k < 16 holds the K centroid k as {fp16 value, fp16 remainder},
-// word 16 + k the fp16 V centroid k; c is the centroid this thread loaded.
+// Code tables, built from the centroids each thread holds in registers.  Thread (w, copy),
+// w = threadIdx.x / 32, writes copy `copy` of entries e = 16k + w, k = 0..15:
+//   K entry e: fp16 {c_K[a], c_K[b]} then their fp16 remainders, a = e & (2^BK - 1) and
+//              b the next BK bits of e (two codes of one key byte);
+//   V entry e: the fp16 centroids of the four 2-bit codes of value byte e.
 template <int BK>
-__device__ void stage_codebooks(uint32_t *st, float c) {
-  const int t = threadIdx.x;
-  if (t < (1 << BK)) {
-    const uint16_t h = h16(c);
-    st[t] = (uint32_t)h | ((uint32_t)h16(c - f16(h)) << 16);
-  } else if (t >= 16 && t < 20) {
-    st[t] = h16(c);
+__device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 << BK], const float (&vcs)[4]) {
+  constexpr int NK = 1 << BK;
+  uint32_t khl[NK];  // {fp16 value, fp16 remainder}
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const uint16_t h = h16(kcs[i]);
+    khl[i] = (uint32_t)h | ((uint32_t)h16(kcs[i] - f16(h)) << 16);
   }
-}
-
-template <int BK>
-__device__ void build_tables(uint8_t *lds, const uint32_t *st) {
-  for (int idx = threadIdx.x; idx < 256 * 32; idx += blockDim.x) {
-    const int e = idx >> 5, copy = idx & 31;
-    const uint32_t c0 = st[BK == 4 ? (e & 15) : (e & 7)];
-    const uint32_t c1 = st[BK == 4 ? (e >> 4) : ((e >> 3) & 7)];
+  uint32_t vh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vh[i] = h16(vcs[i]);
+  const int w = threadIdx.x >> 5, copy = threadIdx.x & 31;
+  uint32_t c0 = 0u, vlo0 = 0u, vlo1 = 0u;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) c0 = (w & (NK - 1)) == i ? khl[i] : c0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vlo0 = (w & 3) == i ? vh[i] : vlo0;
+    vlo1 = ((w >> 2) & 3) == i ? vh[i] : vlo1;
+  }
+  const uint32_t vlo = vlo0 | (vlo1 << 16);
+  uint8_t *row = lds + w * 256 + copy * 8;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    uint32_t c1;
+    if (BK == 4) c1 = khl[k];
+    else c1 = (w >> 3) ? khl[(2 * k + 1) & 7] : khl[(2 * k) & 7];
     uint2 kv;
     kv.x = (c0 & 0xffffu) | (c1 << 16);
     kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
-    *reinterpret_cast<uint2 *>(lds + e * 256 + copy * 8) = kv;
-    uint2 vv;
-    vv.x = st[16 + (e & 3)] | (st[16 + ((e >> 2) & 3)] << 16);
-    vv.y = st[16 + ((e >> 4) & 3)] | (st[16 + ((e >> 6) & 3)] << 16);
-    *reinterpret_cast<uint2 *>(lds + kVBase + e * 256 + copy * 8) = vv;
+    *reinterpret_cast<uint2 *>(row + k * 4096) = kv;
+    *reinterpret_cast<uint2 *>(row + kVBase + k * 4096) = make_uint2(vlo, vh[k & 3] | (vh[(k >> 2) & 3] << 16));
   }
 }
 
@@ -173,8 +184,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   if (NH == 4)  // P' rows 8..15 stay zero for the whole launch
     *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 
-  const int n_items = a.batch * a.n_kv_heads * S;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  {  // one split of one (batch, kv head) per workgroup
+    const int item = blockIdx.x;
     const int split = item % S;
     const int kvh = (item / S) % a.n_kv_heads;
     const int b = item / (S * a.n_kv_heads);
@@ -215,14 +226,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
     // is used until all of them are in flight (a use would make the wave wait right there)
-    const bool first_item = item == (int)blockIdx.x;
     float kcs[1 << BK], vcs[4];
-    if (first_item) {
 #pragma unroll
-      for (int i = 0; i < (1 << BK); ++i) kcs[i] = a.k.centroids[i];
+    for (int i = 0; i < (1 << BK); ++i) kcs[i] = a.k.centroids[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vcs[i] = a.v.centroids[i];
-    }
+    for (int i = 0; i < 4; ++i) vcs[i] = a.v.centroids[i];
     const int qhead = qh0 + min(wave, g - 1);
     const size_t qbase = ((size_t)b * a.n_q_heads + qhead) * kD + 2 * lane;
     uint32_t qw0 = 0u, qw1 = 0u;
@@ -235,18 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
     load_keys(wave);
-    if (first_item) {  // the code tables, once per workgroup
-      float cent = 0.f;
-      const int t = threadIdx.x;
-#pragma unroll
-      for (int i = 0; i < (1 << BK); ++i) cent = t == i ? kcs[i] : cent;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cent = t == 16 + i ? vcs[i] : cent;
-      uint32_t *st = reinterpret_cast<uint32_t *>(lds + kWBase + 7 * 4096);
-      stage_codebooks<BK>(st, cent);
-      __syncthreads();
-      build_tables<BK>(lds, st);
-    }
+    build_tables<BK>(lds, kcs, vcs);  // read only after the barriers below
 
     // ---- rotated query group: wave h rotates head h into qrot[h]
     if (wave < NH) {
@@ -649,7 +646,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       }
       if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();  // LDS (flag, query rows) is reused by the next item
   }
 }
 
@@ -669,9 +665,10 @@ bool decode_fused_supported(const DecodeArgs &a) {
 }
 
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream) {
+  (void)n_cu;
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
-  int grid = (int)std::min<long>(n_cu, items);
-  if (grid < 1) grid = 1;
+  if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  const int grid = (int)items;
   return a.k.bits == 4 ? launch_bk<4>(a, grid, stream) : launch_bk<3>(a, grid, stream);
 }
 
