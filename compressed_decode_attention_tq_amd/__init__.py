@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.tq_make_codebook_table.argtypes = [i32, i32, vp, vp]
         L.tq_quantize_append.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, vp]
+        L.tq_quantize_append_kv.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp,
+                                            i32, i32, i32, vp]
         L.tq_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, i32,
                                      i32, vp, i32, f32, f32, vp, vp, vp, vp, sz, vp]
         L.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
@@ -60,7 +62,8 @@ def lib() -> ctypes.CDLL:
         L.tq_code_bytes.restype = sz
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
-        for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_decode_attn", "tq_dequantize"):
+        for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
+                     "tq_dequantize"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -162,6 +165,20 @@ def quantize_append(cache: PackedCache, x, start_pos: int, stream=None):
     st = cache.struct()
     _check(lib().tq_quantize_append(ctypes.byref(st), _dev(x, "x"), _dtype_code(x.dtype), start_pos,
                                     x.shape[1], _stream_ptr(stream)), "tq_quantize_append")
+
+
+def quantize_append_kv(k_cache: PackedCache, v_cache: PackedCache, k, v, start_pos: int, stream=None):
+    """quantize_append of k into k_cache and v into v_cache, one launch (row-layout keys,
+    value-group values; same batch, kv heads and capacity)."""
+    for name, cache, x in (("k", k_cache, k), ("v", v_cache, v)):
+        if x.dim() != 4 or x.shape[0] != cache.batch or x.shape[2] != cache.n_kv_heads or x.shape[3] != cache.d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    ks, vs = k_cache.struct(), v_cache.struct()
+    _check(lib().tq_quantize_append_kv(ctypes.byref(ks), ctypes.byref(vs), _dev(k, "k"), _dev(v, "v"),
+                                       _dtype_code(k.dtype), start_pos, k.shape[1], _stream_ptr(stream)),
+           "tq_quantize_append_kv")
 
 
 def dequantize(cache: PackedCache, start_pos: int, n_tokens: int, dtype=None, stream=None):

@@ -159,6 +159,24 @@ int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_
                                     static_cast<hipStream_t>(hip_stream)));
 }
 
+int tq_quantize_append_kv(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,
+                          int x_dtype, int start_pos, int n_tokens, void *hip_stream) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity)
+    return TQ_ERR_INVALID_ARG;
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if ((long)start_pos + n_tokens > k->capacity) return TQ_ERR_CAPACITY;
+  if (n_tokens == 0) return TQ_OK;
+  return hip_status(launch_quantize_kv(view_of(k), view_of(v), k->batch, xk, xv, x_dtype, start_pos,
+                                       n_tokens, static_cast<hipStream_t>(hip_stream)));
+}
+
 int tq_dequantize(const tq_cache *c, int start_pos, int n_tokens, void *out, int out_dtype,
                   void *hip_stream) {
   int st = check_cache(c);

@@ -61,6 +61,9 @@ struct DecodeArgs {
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
                            int start_pos, int n_tokens, hipStream_t stream);
+hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
+                              const void *xv, int x_dtype, int start_pos, int n_tokens,
+                              hipStream_t stream);
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -123,6 +123,18 @@ int tq_make_codebook_table(int d, int bits, float *centroids, float *boundaries)
 int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_pos,
                        int n_tokens, void *hip_stream);
 
+/* tq_quantize_append on a key cache and a value cache of one layer in a single launch
+ * (same operation and references as tq_quantize_append, applied to both).
+ *   k          cache in TQ_LAYOUT_ROWS;  v  cache in TQ_LAYOUT_GROUP8; they must agree on
+ *              batch, n_kv_heads and capacity (bits, codebooks and signs may differ)
+ *   xk, xv     device in [batch][n_tokens][n_kv_heads][d] of x_dtype, 16-byte aligned
+ * Results are bit-identical to two tq_quantize_append calls.  Calls that overlap on one
+ * cache race.
+ * Errors: TQ_ERR_INVALID_ARG (also for other layouts or mismatched shapes),
+ * TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+int tq_quantize_append_kv(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,
+                          int x_dtype, int start_pos, int n_tokens, void *hip_stream);
+
 /* Decode attention against the packed cache, one query per (batch, query head).
  * Query head h reads kv head h / (n_q_heads / n_kv_heads).  For each (b, h) with
  * T = seq_lens ? clamp(seq_lens[b], 0, ctx_len) : ctx_len tokens:

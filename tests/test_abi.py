@@ -104,6 +104,25 @@ def test_quantize_rejects_bad_ranges():
     assert tq.lib().tq_dequantize(ctypes.byref(c), 0, 8, FAKE, 5, None) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_quantize_kv_rejects_mismatched_caches():
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+
+    def qkv(k, v, xk=FAKE + 0x500000, xv=FAKE + 0x580000, dtype=1, start=0, n=16):
+        return tq.lib().tq_quantize_append_kv(ctypes.byref(k), ctypes.byref(v), xk, xv, dtype, start, n, None)
+
+    assert qkv(k, v, n=0) == tq.TQ_OK                                     # nothing to do, no launch
+    assert qkv(v, k) == tq.TQ_ERR_INVALID_ARG                             # layouts swapped
+    assert qkv(k, _cache(layout=1, bits=2, batch=2)) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, _cache(layout=1, bits=2, n_kv_heads=1)) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, _cache(layout=1, bits=2, capacity=2048)) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, _cache(layout=1, bits=5)) == tq.TQ_ERR_UNSUPPORTED
+    assert qkv(k, v, xv=0) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, v, xk=FAKE + 0x500004) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, v, dtype=9) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, v, start=-1) == tq.TQ_ERR_INVALID_ARG
+    assert qkv(k, v, start=1000, n=25) == tq.TQ_ERR_CAPACITY
+
+
 def _decode(k, v, q=FAKE + 0x600000, hq=8, seq=None, ctx=512, scale=0.088, tau=0.0,
             out=FAKE + 0x700000, ws=FAKE + 0x800000, ws_bytes=None):
     if ws_bytes is None:

@@ -83,6 +83,36 @@ def test_append_in_pieces_keeps_earlier_tokens(layout, bits, signs, golden_codeb
     parity.check_quantize(cache, parity.to_f64(x), 0, s64, _table(golden_codebooks, bits))
 
 
+@pytest.mark.parametrize("bits_k,bits_v,dtype", [(4, 2, "bf16"), (3, 2, "f16"), (4, 3, "f32"), (8, 8, "bf16"),
+                                                (2, 4, "f16")])
+def test_quantize_append_kv_equals_two_appends(bits_k, bits_v, dtype, signs, golden_codebooks):
+    """The one-launch key-and-value append writes exactly what two single-cache appends write,
+    over ragged ranges that start and end inside 8-token groups and 64-token chunks."""
+    _say("append kv", bits_k, bits_v, dtype)
+    w = inputs.WORKLOADS["llama8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=150, n_kv_heads=3, with_query=False)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    k, v = g["k"].to(tdt), g["v"].to(tdt)
+    one = (_new_cache(2, 3, 192, bits_k, 0, signs), _new_cache(2, 3, 192, bits_v, 1, signs))
+    two = (_new_cache(2, 3, 192, bits_k, 0, signs), _new_cache(2, 3, 192, bits_v, 1, signs))
+    for c in one + two:  # the same stale contents outside the written ranges
+        c.codes.fill_(0xA5)
+        c.norms.fill_(0x3C00)
+    for a, e in [(0, 5), (5, 70), (70, 71), (71, 150)]:
+        ks, vs = k[:, a:e].contiguous().to(DEV), v[:, a:e].contiguous().to(DEV)
+        tq.quantize_append_kv(one[0], one[1], ks, vs, a)
+        tq.quantize_append(two[0], ks, a)
+        tq.quantize_append(two[1], vs, a)
+    torch.cuda.synchronize()
+    for c1, c2 in zip(one, two):
+        assert torch.equal(c1.codes, c2.codes)
+        assert torch.equal(c1.norms, c2.norms)
+    s64 = signs.numpy().astype(np.float64)
+    if dtype == "f32":
+        parity.check_quantize(one[0], parity.to_f64(g["k"]), 0, s64, _table(golden_codebooks, bits_k))
+        parity.check_quantize(one[1], parity.to_f64(g["v"]), 0, s64, _table(golden_codebooks, bits_v))
+
+
 def test_quantize_special_vectors(signs, golden_codebooks):
     """Basis vectors, the all-ones vector (exact ties on the middle boundary) and zeros."""
     _say("special vectors")
