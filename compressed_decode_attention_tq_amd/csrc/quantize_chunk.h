@@ -53,8 +53,17 @@ __device__ __forceinline__ void load32(const void *x, size_t base, float v[32]) 
   }
 }
 
+// Value of the same register in lane (lane ^ m) of the quad, m = 1 (quad_perm 1,0,3,2:
+// control 0xB1) or m = 2 (quad_perm 2,3,0,1: control 0x4E), through a DPP move.
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 // Unnormalised Walsh-Hadamard transform of 128 values held 32 per lane by a lane quad
-// (lane q of the quad holds coordinates 32q .. 32q+31).
+// (lane q of the quad holds coordinates 32q .. 32q+31): five butterfly stages inside the
+// lane, then two across the quad, where the upper lane of a pair keeps partner - own and
+// the lower one partner + own (one multiply-add by a per-lane sign of +-1, exact).
 __device__ __forceinline__ void quad_fwht(float v[32], int q) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
@@ -67,15 +76,11 @@ __device__ __forceinline__ void quad_fwht(float v[32], int q) {
       }
     }
   }
+  const float s1 = (q & 1) ? -1.f : 1.f, s2 = (q & 2) ? -1.f : 1.f;
 #pragma unroll
-  for (int m = 1; m <= 2; m <<= 1) {
-    const bool upper = (q & m) != 0;
+  for (int e = 0; e < 32; ++e) v[e] = fmaf(s1, v[e], quad_swap<0xB1>(v[e]));
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      float o = __shfl_xor(v[e], m);
-      v[e] = upper ? (o - v[e]) : (v[e] + o);
-    }
-  }
+  for (int e = 0; e < 32; ++e) v[e] = fmaf(s2, v[e], quad_swap<0x4E>(v[e]));
 }
 
 // code = #{j : t_j < u} for a symmetric codebook of 2^BITS levels (BITS <= 4); `pos` holds
@@ -101,10 +106,75 @@ __device__ __forceinline__ uint32_t code_of_8(float u, const float *bnd) {
   return idx;
 }
 
+constexpr int kGridCells = 64;
+
 struct QuantLds {
   __attribute__((aligned(16))) uint8_t stage[4][16][kD];  // value-group transpose
   float bnd8[4][256];                                      // 8-bit boundaries
+  uint2 grid[4][kGridCells];                               // per-wave code grid
 };
+
+// Code search by a uniform grid over the boundaries (codebooks of up to 16 levels).  Cell
+// c = trunc(clamp(u * scale + offset, 0, cells - 1)) holds at most one boundary; its entry is
+// {#{t_j < lower edge of c}, that boundary or +inf}, so code = entry.x + (u > entry.y).
+// Cell 0 reaches down to -inf and the last cell up to +inf.  A u that rounds into a
+// neighbouring cell can only change its code when a boundary lies between u and the cell
+// edge, i.e. within the rounding of u (far below 1e-6).
+struct CodeGrid {
+  float scale, offset, last_cell;
+  int cells;
+  bool ok;
+};
+
+// Builds the wave's grid from the L/2 - 1 positive boundaries (the codebook is symmetric:
+// t = -pos reversed, 0, pos).  ok is false when the grid would need more than kGridCells
+// cells or a cell would hold two boundaries; the caller then counts compares instead.
+template <int BITS>
+__device__ CodeGrid build_code_grid(const float *pos, uint2 *grid, int lane) {
+  constexpr int L = 1 << BITS, NP = L / 2 - 1;
+  float gap = pos[0];
+#pragma unroll
+  for (int k = 0; k + 1 < NP; ++k) gap = fminf(gap, pos[k + 1] - pos[k]);
+  const float w = 0.75f * gap;
+  const float lo = -pos[NP - 1] - 0.5f * w;
+  CodeGrid gd;
+  gd.cells = (int)ceilf((2.f * pos[NP - 1] + w) / w) + 1;
+  gd.last_cell = (float)(gd.cells - 1);
+  gd.scale = 1.f / w;
+  gd.offset = -lo / w;
+  gd.ok = gap > 0.f && gd.cells <= kGridCells;
+  if (!gd.ok) return gd;
+  const int cidx = lane;
+  const float e0 = lo + (float)cidx * w;        // lower edge (cell 0: -inf)
+  const float e1 = lo + (float)(cidx + 1) * w;  // upper edge (last cell: +inf)
+  const bool first = cidx == 0, last = cidx == gd.cells - 1;
+  uint32_t base = 0, inside = 0;
+  float bnd = INFINITY;
+  auto visit = [&](float t) {
+    const bool below = !first && t < e0;
+    const bool in = !below && (last || t < e1);
+    base += below ? 1u : 0u;
+    inside += in ? 1u : 0u;
+    if (in) bnd = fminf(bnd, t);
+  };
+#pragma unroll
+  for (int k = NP - 1; k >= 0; --k) visit(-pos[k]);
+  visit(0.f);
+#pragma unroll
+  for (int k = 0; k < NP; ++k) visit(pos[k]);
+  const bool bad = cidx < gd.cells && inside > 1u;
+  gd.ok = __ballot(bad) == 0ull;
+  if (cidx < gd.cells) grid[cidx] = make_uint2(base, __float_as_uint(bnd));
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  return gd;
+}
+
+__device__ __forceinline__ uint32_t code_by_grid(float u, const CodeGrid &gd, const uint2 *grid) {
+  const int cidx = (int)__builtin_amdgcn_fmed3f(fmaf(u, gd.scale, gd.offset), 0.f, gd.last_cell);
+  const uint2 e = grid[cidx];
+  return e.x + (u > __uint_as_float(e.y) ? 1u : 0u);
+}
 
 // One 64-token chunk (chunk index bx counted from the chunk of start_pos) of the plane of
 // (batch b, kv head h).
@@ -125,9 +195,11 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
   const bool valid = t >= lo && t < hi;
 
   float pos[L / 2 > 1 ? L / 2 - 1 : 1];
+  CodeGrid gd{0.f, 0.f, 0.f, 0, false};
   if (BITS <= 4) {
 #pragma unroll
     for (int k = 0; k < L / 2 - 1; ++k) pos[k] = c.boundaries[L / 2 + k];
+    gd = build_code_grid<BITS <= 4 ? BITS : 4>(pos, sh.grid[wave], lane);
   } else {
     for (int k = lane; k < L - 1; k += 64) sh.bnd8[wave][k] = c.boundaries[k];
     __builtin_amdgcn_wave_barrier();
@@ -161,10 +233,15 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
   uint32_t code[32];
+  if (BITS <= 4 && gd.ok) {
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const float u = v[e] * inv;
-    code[e] = BITS <= 4 ? code_of<BITS <= 4 ? BITS : 4>(u, pos) : code_of_8(u, sh.bnd8[wave]);
+    for (int e = 0; e < 32; ++e) code[e] = code_by_grid(v[e] * inv, gd, sh.grid[wave]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float u = v[e] * inv;
+      code[e] = BITS <= 4 ? code_of<BITS <= 4 ? BITS : 4>(u, pos) : code_of_8(u, sh.bnd8[wave]);
+    }
   }
   if (valid && q == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
 
