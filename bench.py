@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -73,12 +74,17 @@ def parse():
 
 
 def kernel_sources_digest() -> str:
+    """Digest of the kernel sources' code: comments and blank space are left out, so that a
+    counter record stays valid across comment edits and goes stale on any code change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "compressed_decode_attention_tq_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode())
-            h.update(fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -144,7 +150,9 @@ def main():
         result = bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log)
     else:
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
-    result["roofline"]["traffic"] = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
+    traffic = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
+    launches = result.pop("_launches", 1)  # traffic per step when a step is several launches
+    result["roofline"]["traffic"] = None if traffic is None else traffic * launches
     result["sources_digest"] = digest
     if args.calibrate_copy:
         calibrate_copy(torch, log)
@@ -256,7 +264,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
                      "kernel": DECODE_KERNEL if dense_single
                      else "decode attention call (split, Sparse-V and merge kernels)",
                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3},
-        "_kernel": "decode",
+        "_kernel": "decode" if dense_single else "decode_sparse",
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(w, tau, caches[0], host_k, host_v, q, signs, np, torch, log)
@@ -341,6 +349,7 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
                      "kernel": QUANTIZE_KERNEL + " (32 launches per step, K and V of one layer each)",
                      "bytes_per_launch": (in_bytes + out_bytes) / (2 * layers)},
         "_kernel": "quantize",
+        "_launches": layers,
     }
     if not args.no_cpu_baseline:
         from oracle import tq_oracle as o
@@ -434,17 +443,29 @@ def summarize_traffic(args):
             sys.exit(f"no kernel matching {pat!r} in {sorted(table)}")
         return keys[0]
 
-    kf, cf = pick(fetch, args.kernel), pick(fetch, CALIBRATION_KERNEL)
-    kw, cw = pick(write, args.kernel), pick(write, CALIBRATION_KERNEL)
+    def weighted(table, counts):
+        # every instance of the kernel (e.g. the bit widths of the prefill layers), weighted
+        # by its number of dispatches
+        keys = sorted(k for k in table if args.kernel in k and CALIBRATION_KERNEL not in k)
+        if not keys:
+            sys.exit(f"no kernel matching {args.kernel!r} in {sorted(table)}")
+        n = sum(counts[k] for k in keys)
+        return keys, sum(table[k] * counts[k] for k in keys) / n, {k: counts[k] for k in keys}
+
+    kf, mf, df = weighted(fetch, nf)
+    kw, mw, dw = weighted(write, nw)
+    cf, cw = pick(fetch, CALIBRATION_KERNEL), pick(write, CALIBRATION_KERNEL)
     scale_f = COPY_BYTES / (fetch[cf] * 1024.0)
     scale_w = COPY_BYTES / (write[cw] * 1024.0)
-    fb = fetch[kf] * 1024.0 * scale_f
-    wb = write[kw] * 1024.0 * scale_w
-    rec = {"kernel": kf, "workload": args.workload, "fetch_kib_per_dispatch": fetch[kf],
-           "write_kib_per_dispatch": write[kw], "copy_fetch_kib": fetch[cf], "copy_write_kib": write[cw],
+    fb = mf * 1024.0 * scale_f
+    wb = mw * 1024.0 * scale_w
+    rec = {"kernel": kf, "workload": args.workload, "fetch_kib_per_dispatch": mf,
+           "write_kib_per_dispatch": mw,
+           "per_instance_kib": {k: {"fetch": fetch[k], "write": write.get(k)} for k in kf},
+           "copy_fetch_kib": fetch[cf], "copy_write_kib": write[cw],
            "copy_bytes": COPY_BYTES, "fetch_scale": scale_f, "write_scale": scale_w,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
-           "dispatches": {"fetch": nf[kf], "write": nw[kw]}, "sources_digest": kernel_sources_digest(),
+           "dispatches": {"fetch": df, "write": dw}, "sources_digest": kernel_sources_digest(),
            "command": args.command}
     kname = "decode" if args.kernel == DECODE_KERNEL else "quantize"
     with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{args.workload}.txt"), "w") as fh:

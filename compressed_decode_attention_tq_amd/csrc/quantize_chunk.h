@@ -9,12 +9,13 @@
 // Quantize mapping: a block of 256 threads covers one 64-token chunk of one (batch, kv head)
 // plane and each of its waves owns 16 consecutive tokens (two 8-token value groups), so the
 // waves never wait for each other.  4 lanes hold one vector, 32 coordinates each: the
-// Walsh-Hadamard transform runs 5 butterfly stages inside a lane and 2 across the lane quad.
-// The code of u is found without a search loop: the codebook is symmetric (t_{L-2-j} = -t_j,
-// t_{L/2-1} = 0), so code = L/2 + #{positive t < u} for u > 0 and L/2 - 1 - #{positive t <= |u|}
-// otherwise, a count of compares against the L/2 - 1 positive boundaries held in scalar
-// registers (8-bit codebooks use a binary search over the boundaries in LDS).  Row-layout
-// codes are packed inside the lane; value-group codes go through a per-wave LDS transpose.
+// Walsh-Hadamard transform runs 5 butterfly stages inside a lane and 2 across the lane quad
+// (DPP moves).  Codes of codebooks with up to 16 levels come from a per-wave uniform grid in
+// LDS (one lookup, one compare); when a codebook does not fit the grid, the code is counted
+// with compares against the L/2 - 1 positive boundaries (the codebook is symmetric:
+// t_{L-2-j} = -t_j, t_{L/2-1} = 0).  256-level codebooks use a binary search over the
+// boundaries in LDS.  Row-layout codes are packed inside the lane; value-group codes go
+// through a per-wave LDS transpose.
 #pragma once
 #include "tq_common.h"
 #include "tq_launch.h"
