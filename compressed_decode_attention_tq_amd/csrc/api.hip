@@ -85,10 +85,22 @@ SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len) {
   return SplitPlan{(int)n, (int)len};
 }
 
+SplitPlan plan_fused_sparse(int batch, int n_kv_heads, int ctx_len, const SplitPlan &p) {
+  const SplitPlan d = plan_fused(batch, n_kv_heads, ctx_len);
+  long k = (d.split_len + p.split_len / 2) / p.split_len;
+  if (k < 1) k = 1;
+  if (k > kMaxChunksPerSplit) k = kMaxChunksPerSplit;
+  const long len = k * p.split_len;
+  long n = (ctx_len + len - 1) / len;
+  if (n < 1) n = 1;
+  return SplitPlan{(int)n, (int)len};
+}
+
 WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  bool sparse) {
   const SplitPlan p = plan_splits(batch, n_kv_heads, ctx_len, n_q_heads / n_kv_heads);
-  const SplitPlan fp = plan_fused(batch, n_kv_heads, ctx_len);
+  const SplitPlan fp = sparse ? plan_fused_sparse(batch, n_kv_heads, ctx_len, p)
+                              : plan_fused(batch, n_kv_heads, ctx_len);
   const size_t heads = (size_t)batch * n_q_heads * p.n_splits;
   const size_t fheads = (size_t)batch * n_q_heads * fp.n_splits;
   WorkspaceLayout w{};
@@ -233,7 +245,8 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
   a.sparse = sparse ? 1 : 0;
   a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
-  a.fplan = plan_fused(k->batch, k->n_kv_heads, ctx_len);
+  a.fplan = sparse ? plan_fused_sparse(k->batch, k->n_kv_heads, ctx_len, a.plan)
+                   : plan_fused(k->batch, k->n_kv_heads, ctx_len);
   a.out = out;
   a.lse = lse;
   a.scores = scores;

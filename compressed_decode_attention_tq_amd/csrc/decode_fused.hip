@@ -91,7 +91,7 @@ __device__ __forceinline__ uint32_t pst_off(int row, int unit) {
 //   K entry e: fp16 {c_K[a], c_K[b]} then their fp16 remainders, a = e & (2^BK - 1) and
 //              b the next BK bits of e (two codes of one key byte);
 //   V entry e: the fp16 centroids of the four 2-bit codes of value byte e.
-template <int BK>
+template <int BK, bool VTAB>
 __device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 << BK], const float (&vcs)[4]) {
   constexpr int NK = 1 << BK;
   uint32_t khl[NK];  // {fp16 value, fp16 remainder}
@@ -123,7 +123,7 @@ __device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 
     kv.x = (c0 & 0xffffu) | (c1 << 16);
     kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
     *reinterpret_cast<uint2 *>(row + k * 4096) = kv;
-    *reinterpret_cast<uint2 *>(row + kVBase + k * 4096) = make_uint2(vlo, vh[k & 3] | (vh[(k >> 2) & 3] << 16));
+    if (VTAB) *reinterpret_cast<uint2 *>(row + kVBase + k * 4096) = make_uint2(vlo, vh[k & 3] | (vh[(k >> 2) & 3] << 16));
   }
 }
 
@@ -164,7 +164,7 @@ __device__ __forceinline__ float exp2_or_zero(float x, float ref) {
   return (x == -INFINITY || ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - ref);
 }
 
-template <int BK, int NH>
+template <int BK, int NH, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
@@ -243,7 +243,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
     load_keys(wave);
-    build_tables<BK>(lds, kcs, vcs);  // read only after the barriers below
+    build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
+    // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
+    // the value-table region is free in that mode)
+    int *chunk_count = reinterpret_cast<int *>(lds + kVBase);
+    const int c_first = SPARSE ? t_begin / a.plan.split_len : 0;
+    const int n_chunks = SPARSE ? a.fplan.split_len / a.plan.split_len : 0;
+    if (SPARSE && (int)threadIdx.x < n_chunks) chunk_count[threadIdx.x] = 0;
 
     // ---- rotated query group: wave h rotates head h into qrot[h]
     if (wave < NH) {
@@ -315,12 +321,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       constexpr bool PREFETCH = decltype(prefetch_tag)::value;
       const int t0 = t_begin + tile * kTile;
       uint32_t vw[2][4];
+      uint32_t nvw = 0u;
+      if constexpr (!SPARSE) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + (uint32_t)tile * (kTile * 32) + c * 1024, 0, 0);
-        vw[c][0] = w[0]; vw[c][1] = w[1]; vw[c][2] = w[2]; vw[c][3] = w[3];
+        for (int c = 0; c < 2; ++c) {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + (uint32_t)tile * (kTile * 32) + c * 1024, 0, 0);
+          vw[c][0] = w[0]; vw[c][1] = w[1]; vw[c][2] = w[2]; vw[c][3] = w[3];
+        }
+        nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
       }
-      const uint32_t nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
 
       // ---- scores: sub-tile s, 16-coordinate chunk m -> key fields 2m, 2m+1 of the quarter
       auto key_operands = [&](int m, half8 (&dst)[4]) {
@@ -407,6 +416,69 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 #pragma unroll
             for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] = -INFINITY;
           }
+      }
+      if constexpr (SPARSE) {
+        // exact running maximum of the wave per head, sum relative to it; a token is a
+        // candidate when some head's score reaches that maximum + log2(tau).  The maximum
+        // only grows and never exceeds the final LSE, so every row the final weight keeps is
+        // among the candidates.  (A bound shared by the workgroup's waves halves the
+        // candidates but costs more per tile than the records it saves.)
+        const float log2_tau = a.ln_tau * kLog2e;
+        bool cand0 = false, cand1 = false;
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) {
+          const float z = half_max(fmaxf(sc[0][hh], sc[1][hh]));
+          const float m_new = fmaxf(mr[hh], z);
+          lsum[hh] = lsum[hh] * exp2_or_zero(mr[hh], m_new) + exp2_or_zero(sc[0][hh], m_new) +
+                     exp2_or_zero(sc[1][hh], m_new);
+          mr[hh] = m_new;
+          if (half_id * NH2 + hh < g) {
+            cand0 |= sc[0][hh] != -INFINITY && sc[0][hh] >= m_new + log2_tau;
+            cand1 |= sc[1][hh] != -INFINITY && sc[1][hh] >= m_new + log2_tau;
+          }
+        }
+        // token 2pr + tb is a candidate if either head half flags it; records are
+        // {token, g scores (natural log)} at consecutive slots of the tile's second-pass split
+        const uint64_t b0 = __ballot(cand0), b1 = __ballot(cand1);
+        const uint32_t c0 = (uint32_t)b0 | (uint32_t)(b0 >> 32);
+        const uint32_t c1 = (uint32_t)b1 | (uint32_t)(b1 >> 32);
+        const int n0 = __popc(c0), n = n0 + __popc(c1);
+        if (n > 0) {
+          const int chunk = t0 / a.plan.split_len;
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&chunk_count[chunk - c_first], n);
+          base = __builtin_amdgcn_readfirstlane(base);
+          float *cbase = a.cand + (((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + chunk) *
+                                      (size_t)a.plan.split_len * (1 + g);
+          const uint32_t below = (1u << pr) - 1u;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const uint32_t cm = tb ? c1 : c0;
+            if ((cm >> pr) & 1u) {
+              const int slot = base + (tb ? n0 : 0) + __popc(cm & below);
+              float *rec = cbase + (size_t)slot * (1 + g);
+              if (half_id == 0) rec[0] = __int_as_float(t0 + 2 * pr + tb);
+#pragma unroll
+              for (int hh = 0; hh < NH2; ++hh) {
+                const int h = half_id * NH2 + hh;
+                if (h < g) rec[1 + h] = sc[tb][hh] * kLn2;
+              }
+            }
+          }
+        }
+        if (a.scores != nullptr) {
+#pragma unroll
+          for (int hh = 0; hh < NH2; ++hh) {
+            const int h = half_id * NH2 + hh;
+            if (h < g) {
+              float *row = a.scores + ((size_t)b * a.n_q_heads + qh0 + h) * a.ctx_len;
+#pragma unroll
+              for (int tb = 0; tb < 2; ++tb)
+                if (t0 + 2 * pr + tb < t_end) row[t0 + 2 * pr + tb] = sc[tb][hh] * kLn2;
+            }
+          }
+        }
+        return;
       }
       float p[2][NH2];
       float vmax = 0.f;
@@ -549,6 +621,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         }
       }
     }
+    if constexpr (SPARSE) {
+      // the split's (m, l) per query head in natural-log units, and the candidate counts;
+      // the value pass and the merge are separate kernels
+      if (wave < NH && wave < g && lane == 0)
+        a.fpart_ml[((size_t)b * a.n_q_heads + qh0 + wave) * S + split] =
+            make_float2(Mh == -INFINITY ? -INFINITY : Mh * kLn2, Lh);
+      for (int i = threadIdx.x; i < n_chunks; i += blockDim.x)
+        if (c_first + i < a.plan.n_splits)
+          a.cand_count[((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + c_first + i] = chunk_count[i];
+      return;
+    }
     __syncthreads();
     // Round 2: scaled O rows of this wave, [head][128] fp32 (hi and remainder rows summed)
     if (NH == 8 || quarter < 2) {
@@ -649,10 +732,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
-template <int BK>
+template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.group <= 4) decode_fused_kernel<BK, 4><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8><<<grid, kThreads, 0, stream>>>(a);
+  if (a.group <= 4) decode_fused_kernel<BK, 4, SPARSE><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8, SPARSE><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -669,7 +752,20 @@ hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   const int grid = (int)items;
-  return a.k.bits == 4 ? launch_bk<4>(a, grid, stream) : launch_bk<3>(a, grid, stream);
+  return a.k.bits == 4 ? launch_bk<4, false>(a, grid, stream) : launch_bk<3, false>(a, grid, stream);
+}
+
+bool decode_fused_sparse_supported(const DecodeArgs &a) {
+  return a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.group <= 8 &&
+         a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
+         a.plan.split_len % kTile == 0 && a.fplan.split_len % a.plan.split_len == 0 &&
+         a.fplan.split_len / a.plan.split_len <= kMaxChunksPerSplit;
+}
+
+hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream) {
+  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  return a.k.bits == 4 ? launch_bk<4, true>(a, (int)items, stream) : launch_bk<3, true>(a, (int)items, stream);
 }
 
 }  // namespace tq

@@ -263,13 +263,14 @@ __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
   for (int i = tid; i < L * GP; i += blockDim.x) w[i] = 0.f;
   for (int i = tid; i < L / 8; i += blockDim.x) gflag[i] = 0;
   for (int j = wave; j < g; j += 4) {
-    const float2 *ml = a.part_ml + ((size_t)b * a.n_q_heads + kvh * g + j) * S;
+    const int SL = a.lse_splits;
+    const float2 *ml = a.lse_ml + ((size_t)b * a.n_q_heads + kvh * g + j) * SL;
     float mx = -INFINITY;
-    for (int k = lane; k < S; k += 64) mx = fmaxf(mx, ml[k].x);
+    for (int k = lane; k < SL; k += 64) mx = fmaxf(mx, ml[k].x);
     mx = wave_max(mx);
     float l = 0.f;
     if (mx != -INFINITY)
-      for (int k = lane; k < S; k += 64)
+      for (int k = lane; k < SL; k += 64)
         if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - mx);
     l = wave_sum(l);
     if (lane == 0) lse_s[j] = mx == -INFINITY ? INFINITY : mx + __logf(l);
@@ -377,8 +378,12 @@ __global__ __launch_bounds__(128 * kMergeGroups) void decode_merge(DecodeArgs a)
   __shared__ float red_o[kMergeGroups][kD];
   __shared__ float buf[kD];
 
+  // Sparse V: the LSE comes from the first pass's partials, and the second pass's partials
+  // are already normalised, so they are plain sums
+  const int SL = a.sparse ? a.lse_splits : S;
+  const float2 *lml = a.sparse ? a.lse_ml + ((size_t)b * a.n_q_heads + hq) * SL : ml;
   float mx = -INFINITY;
-  for (int k = threadIdx.x; k < S; k += blockDim.x) mx = fmaxf(mx, ml[k].x);
+  for (int k = threadIdx.x; k < SL; k += blockDim.x) mx = fmaxf(mx, lml[k].x);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
   if ((threadIdx.x & 63) == 0) red_m[threadIdx.x >> 6] = mx;
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(128 * kMergeGroups) void decode_merge(DecodeArgs a)
   for (int w = 1; w < kMergeGroups * 2; ++w) mx = fmaxf(mx, red_m[w]);
 
   float o = 0.f, l = 0.f;
-  if (mx != -INFINITY) {
+  if (mx != -INFINITY && !a.sparse) {
     int k = grp;
     for (; k + 3 * kMergeGroups < S; k += 4 * kMergeGroups) {
       float2 p[4];
@@ -402,15 +407,28 @@ __global__ __launch_bounds__(128 * kMergeGroups) void decode_merge(DecodeArgs a)
       for (int u = 0; u < 4; ++u) {
         const float w = p[u].x == -INFINITY ? 0.f : __expf(p[u].x - mx);
         l += p[u].y * w;
-        o += a.sparse ? v[u] : v[u] * w;
+        o += v[u] * w;
       }
     }
     for (; k < S; k += kMergeGroups) {
       const float2 p = ml[k];
       const float w = p.x == -INFINITY ? 0.f : __expf(p.x - mx);
       l += p.y * w;
-      o += a.sparse ? po[(size_t)k * kD + i] : po[(size_t)k * kD + i] * w;
+      o += po[(size_t)k * kD + i] * w;
     }
+  } else if (mx != -INFINITY) {
+    for (int k = grp; k < SL; k += kMergeGroups) {
+      const float2 p = lml[k];
+      if (p.x != -INFINITY) l += p.y * __expf(p.x - mx);
+    }
+    int k = grp;
+    for (; k + 3 * kMergeGroups < S; k += 4 * kMergeGroups) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = po[(size_t)(k + u * kMergeGroups) * kD + i];
+      o += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    for (; k < S; k += kMergeGroups) o += po[(size_t)k * kD + i];
   }
   red_o[grp][i] = o;
   if (i == 0) red_l[grp] = l;
@@ -455,15 +473,24 @@ int compute_units() {
   return cached[dev];
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  if (decode_fused_supported(a)) return launch_decode_fused(a, compute_units(), stream);
+hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
+  if (decode_fused_supported(args)) return launch_decode_fused(args, compute_units(), stream);
+  DecodeArgs a = args;
   dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
   hipError_t e;
-  if (decode_mfma_supported(a)) {
-    e = launch_decode_mfma(a, compute_units(), stream);
+  if (decode_fused_sparse_supported(a)) {  // key-only fused first pass
+    a.lse_ml = a.fpart_ml;
+    a.lse_splits = a.fplan.n_splits;
+    e = launch_decode_fused_sparse(a, stream);
   } else {
-    decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
-    e = hipGetLastError();
+    a.lse_ml = a.part_ml;
+    a.lse_splits = a.plan.n_splits;
+    if (decode_mfma_supported(a)) {
+      e = launch_decode_mfma(a, compute_units(), stream);
+    } else {
+      decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
+      e = hipGetLastError();
+    }
   }
   if (e != hipSuccess) return e;
   if (a.sparse) {

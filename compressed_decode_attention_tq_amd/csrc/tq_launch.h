@@ -19,6 +19,10 @@ struct SplitPlan {
 SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len, int group);
 // Splits of the single-launch dense path: about one workgroup per CU, whole 64-token tiles.
 SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len);
+// Sparse V's fused first pass: splits of a whole number (<= kMaxChunksPerSplit) of the
+// second pass's splits `p`, about as long as the dense plan's.
+SplitPlan plan_fused_sparse(int batch, int n_kv_heads, int ctx_len, const SplitPlan &p);
+constexpr int kMaxChunksPerSplit = 64;
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WorkspaceLayout {
@@ -57,6 +61,11 @@ struct DecodeArgs {
   float2 *fpart_ml;
   float *fpart_o;
   unsigned *counters;
+  // Sparse V: the (m, l) partials (natural log) the LSE is merged from, per (batch, query
+  // head): lse_splits of them.  The per-wave first pass writes part_ml (plan splits), the
+  // fused first pass fpart_ml (fplan splits).
+  const float2 *lse_ml;
+  int lse_splits;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
@@ -69,6 +78,8 @@ hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_d
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supported(const DecodeArgs &a);
 bool decode_fused_supported(const DecodeArgs &a);
+bool decode_fused_sparse_supported(const DecodeArgs &a);
+hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int n_cu, hipStream_t stream);
 
