@@ -37,43 +37,55 @@ def gpu_plane_norms(cache, b, h, n_tokens):
     return cache.plane_norms(b, h)[:n_tokens].cpu().numpy()
 
 
+def check_plane(cache, b, h, x64, start, signs, table, end=None):
+    """Codes and norms of plane (b, h) at positions [start, start + n) against the oracle's
+    quantization of x64 [n, d]; returns the number of near-boundary coordinates."""
+    c, t = table
+    n = x64.shape[0]
+    end = start + n if end is None else end
+    pad = (end + 7) // 8 * 8
+    codes_g, raw = gpu_plane_codes(cache, b, h, pad)
+    # packing is bit-exact: re-packing the GPU's own codes gives the GPU bytes
+    assert np.array_equal(o.pack(codes_g, cache.bits, cache.layout), raw), (b, h)
+    codes_o, n16_o, u = o.quantize(x64, signs, c, t)
+    near = o.near_boundary_mask(u, t, BAND)
+    got = codes_g[start:start + n]
+    mism = (got != codes_o) & ~near
+    assert not mism.any(), (b, h, np.argwhere(mism)[:5])
+    n16_g = gpu_plane_norms(cache, b, h, end)[start:start + n].astype(np.float64)
+    ref = n16_o.astype(np.float64)
+    assert np.all(np.abs(n16_g - ref) <= REL * np.abs(ref) + 1e-30), (b, h)
+    return int(near.sum())
+
+
 def check_quantize(cache, x64, start, signs, table, written_upto=None, report=None):
     """x64: fp64 [batch, n, n_kv_heads, d] quantized into [start, start + n)."""
-    c, t = table
     bsz, n, hkv, d = x64.shape
-    end = start + n if written_upto is None else written_upto
-    pad = (end + 7) // 8 * 8
     near_total = 0
     for b in range(bsz):
         for h in range(hkv):
-            codes_g, raw = gpu_plane_codes(cache, b, h, pad)
-            # packing is bit-exact: re-packing the GPU's own codes gives the GPU bytes
-            assert np.array_equal(o.pack(codes_g, cache.bits, cache.layout), raw), (b, h)
-            codes_o, n16_o, u = o.quantize(x64[b, :, h], signs, c, t)
-            near = o.near_boundary_mask(u, t, BAND)
-            got = codes_g[start:start + n]
-            mism = (got != codes_o) & ~near
-            assert not mism.any(), (b, h, np.argwhere(mism)[:5])
-            near_total += int(near.sum())
-            n16_g = gpu_plane_norms(cache, b, h, end)[start:start + n].astype(np.float64)
-            ref = n16_o.astype(np.float64)
-            assert np.all(np.abs(n16_g - ref) <= REL * np.abs(ref) + 1e-30), (b, h)
+            near_total += check_plane(cache, b, h, x64[b, :, h], start, signs, table, written_upto)
     if report is not None:
         report["near_boundary"] = report.get("near_boundary", 0) + near_total
     return near_total
 
 
+def oracle_plane(cache, b, h, signs, table, n_tokens):
+    """Dequantized plane (b, h) [n_tokens, d] computed by the oracle from the GPU codes."""
+    c, _ = table
+    pad = (n_tokens + 7) // 8 * 8
+    codes, _ = gpu_plane_codes(cache, b, h, pad)
+    n16 = gpu_plane_norms(cache, b, h, n_tokens).astype(np.float16)
+    return o.dequantize(codes[:n_tokens], n16, signs, c)
+
+
 def oracle_cache_view(cache, signs, table, n_tokens):
     """Dequantized cache [batch, n_kv_heads, n_tokens, d] computed by the oracle from the
     GPU-produced codes and norms."""
-    c, _ = table
     out = np.zeros((cache.batch, cache.n_kv_heads, n_tokens, cache.d))
-    pad = (n_tokens + 7) // 8 * 8
     for b in range(cache.batch):
         for h in range(cache.n_kv_heads):
-            codes, _ = gpu_plane_codes(cache, b, h, pad)
-            n16 = gpu_plane_norms(cache, b, h, n_tokens).astype(np.float16)
-            out[b, h] = o.dequantize(codes[:n_tokens], n16, signs, c)
+            out[b, h] = oracle_plane(cache, b, h, signs, table, n_tokens)
     return out
 
 

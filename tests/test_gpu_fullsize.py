@@ -1,0 +1,94 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle cannot take whole outputs at these sizes, so sampled outputs are compared:
+  decode    a few (batch, query head) rows of attention (output and LSE) against the
+            oracle's attention over its dequantization of the GPU-written planes, and the
+            codes and norms of those planes against the oracle's quantizer;
+  prefill   a boundary (8/8-bit) layer and a middle (K4/V3) layer of the 32768-token
+            cache, two kv-head planes each, against the oracle's quantizer.
+Caches, queries and launches are those of the benchmark: the context minus one token is
+appended, the last token goes through the key-and-value append, then one decode call.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import compressed_decode_attention_tq_amd as tq  # noqa: E402
+from compressed_decode_attention_tq_amd import inputs  # noqa: E402
+from oracle import tq_oracle as o  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("workload,tau", [("llama8k", 0.0), ("batch32k", 0.0), ("batch32k", 1e-4),
+                                          ("ctx131k", 0.0), ("ctx131k", 1e-4)])
+def test_decode_full_size_sampled(workload, tau, golden_codebooks):
+    w = inputs.WORKLOADS[workload]
+    _say("full-size decode", workload, tau)
+    batch, hq, hkv, ctx, g = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.group
+    signs = inputs.rotation_signs()
+    sd = signs.to(DEV)
+    x = inputs.generate(w, device=DEV)
+    kc = tq.PackedCache(batch, hkv, ctx, w.bits_k, tq.LAYOUT_ROWS, sd, device=DEV)
+    vc = tq.PackedCache(batch, hkv, ctx, w.bits_v, tq.LAYOUT_GROUP8, sd, device=DEV)
+    tq.quantize_append(kc, x["k"][:, : ctx - 1].contiguous(), 0)
+    tq.quantize_append(vc, x["v"][:, : ctx - 1].contiguous(), 0)
+    tq.quantize_append_kv(kc, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(), ctx - 1)
+    q = x["q"].contiguous()
+    scale = 1.0 / math.sqrt(128)
+    bufs = tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=DEV)
+    tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
+    torch.cuda.synchronize()
+    out_g, lse_g = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
+    s64 = signs.numpy().astype(np.float64)
+    rows = sorted({(0, 0), (batch - 1, hq - 1), (batch // 2, min(hq - 1, hq // 2 + 1))})
+    checked = set()
+    for b, h in rows:
+        kvh = h // g
+        kh = parity.oracle_plane(kc, b, kvh, s64, golden_codebooks[w.bits_k], ctx)
+        vh = parity.oracle_plane(vc, b, kvh, s64, golden_codebooks[w.bits_v], ctx)
+        q64 = parity.to_f64(q[b, h])
+        out, lse, scores = o.decode_attention(q64[None, None], kh[None, None], vh[None, None], scale, tau=tau)
+        allowance, nb = (None, 0)
+        if tau > 0:
+            allowance, nb = parity.sparse_allowance(scores, lse, vh[None, None], tau, 1)
+        worst = parity.check_rows(out_g[b, h][None, None], out, f"out[{b},{h}]", allowance=allowance)
+        assert abs(lse_g[b, h] - lse[0, 0]) <= 1e-3 * max(1.0, abs(lse[0, 0])), (b, h, lse_g[b, h], lse[0, 0])
+        _say(f"  row ({b},{h}): rel err {worst:.2e}, borderline rows {nb}")
+        if (b, kvh) in checked:
+            continue
+        checked.add((b, kvh))
+        for cache, xx, bits in ((kc, x["k"], w.bits_k), (vc, x["v"], w.bits_v)):
+            near = parity.check_plane(cache, b, kvh, parity.to_f64(xx[b, :, kvh]), 0, s64, golden_codebooks[bits])
+            _say(f"  plane ({b},{kvh}) {bits}-bit: near-boundary coordinates {near}")
+
+
+@pytest.mark.parametrize("layer", [0, 5])
+def test_prefill_layer_full_size_sampled(layer, golden_codebooks):
+    w = inputs.WORKLOADS["prefill"]
+    bk, bv = inputs.layer_bits(w, layer)
+    _say("full-size prefill layer", layer, bk, bv)
+    signs = inputs.rotation_signs()
+    sd = signs.to(DEV)
+    x = inputs.generate(w, device=DEV, layer=layer, with_query=False)
+    k, v = x["k"].contiguous(), x["v"].contiguous()
+    kc = tq.PackedCache(1, w.n_kv_heads, w.ctx, bk, tq.LAYOUT_ROWS, sd, device=DEV)
+    vc = tq.PackedCache(1, w.n_kv_heads, w.ctx, bv, tq.LAYOUT_GROUP8, sd, device=DEV)
+    tq.quantize_append_kv(kc, vc, k, v, 0)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    for h in (0, w.n_kv_heads - 1):
+        for cache, xx, bits in ((kc, k, bk), (vc, v, bv)):
+            near = parity.check_plane(cache, 0, h, parity.to_f64(xx[0, :, h]), 0, s64, golden_codebooks[bits])
+            _say(f"  plane (0,{h}) {bits}-bit: near-boundary coordinates {near}")
