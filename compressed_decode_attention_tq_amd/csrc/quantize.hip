@@ -66,7 +66,7 @@ void launch_qd(const CacheView &c, dim3 grid, const void *x, int start_pos, int 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
                            int start_pos, int n_tokens, hipStream_t stream) {
   const int first = start_pos / kChunk, last = (start_pos + n_tokens - 1) / kChunk;
-  dim3 grid(last - first + 1, c.n_kv_heads, batch);
+  dim3 grid((last - first + kChunksPerBlock) / kChunksPerBlock, c.n_kv_heads, batch);
   if (x_dtype == TQ_F32) launch_qd<TQ_F32>(c, grid, x, start_pos, n_tokens, stream);
   else if (x_dtype == TQ_BF16) launch_qd<TQ_BF16>(c, grid, x, start_pos, n_tokens, stream);
   else launch_qd<TQ_F16>(c, grid, x, start_pos, n_tokens, stream);

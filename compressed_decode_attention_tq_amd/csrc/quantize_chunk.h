@@ -25,35 +25,6 @@ namespace {
 
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
-template <int DTYPE>
-__device__ __forceinline__ void load32(const void *x, size_t base, float v[32]) {
-  if (DTYPE == TQ_F32) {
-    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + base);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float4 f = p[r];
-      v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
-    }
-  } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + base);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint4 w = p[r];
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (DTYPE == TQ_BF16) {
-          v[8 * r + 2 * e] = __uint_as_float(ws[e] << 16);
-          v[8 * r + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
-        } else {
-          v[8 * r + 2 * e] = half_bits_to_float((uint16_t)(ws[e] & 0xffffu));
-          v[8 * r + 2 * e + 1] = half_bits_to_float((uint16_t)(ws[e] >> 16));
-        }
-      }
-    }
-  }
-}
-
 // Value of the same register in lane (lane ^ m) of the quad, m = 1 (quad_perm 1,0,3,2:
 // control 0xB1) or m = 2 (quad_perm 2,3,0,1: control 0x4E), through a DPP move.
 template <int CTRL>
@@ -107,23 +78,27 @@ __device__ __forceinline__ uint32_t code_of_8(float u, const float *bnd) {
   return idx;
 }
 
-constexpr int kGridCells = 64;
+constexpr int kGridCells = 128;
 
 struct QuantLds {
   __attribute__((aligned(16))) uint8_t stage[4][16][kD];  // value-group transpose
-  float bnd8[4][256];                                      // 8-bit boundaries
-  uint2 grid[4][kGridCells];                               // per-wave code grid
+  float bnd8[256];                                         // 256-level boundaries
+  uint2 grid[4][kGridCells];                               // per-wave code grid (<= 16 levels)
+  uint2 grid8[1024];                                       // block code grid (256 levels)
+  float red[4];
+  int flag;
 };
 
-// Code search by a uniform grid over the boundaries (codebooks of up to 16 levels).  Cell
-// c = trunc(clamp(u * scale + offset, 0, cells - 1)) holds at most one boundary; its entry is
-// {#{t_j < lower edge of c}, that boundary or +inf}, so code = entry.x + (u > entry.y).
-// Cell 0 reaches down to -inf and the last cell up to +inf.  A u that rounds into a
-// neighbouring cell can only change its code when a boundary lies between u and the cell
-// edge, i.e. within the rounding of u (far below 1e-6).
+// Code search by a uniform grid over u in [-1.01, 1.01) (codebooks of up to 16 levels).  In
+// cell coordinates f = (u + 1.01) / w, cell c = trunc(f) holds at most one boundary; its
+// entry is {#{t_j < lower edge of c}, f of that boundary (+inf if none)}, so
+// code = entry.x + (f > entry.y): one multiply-add, one conversion, one lookup, one compare.
+// A unit vector's coordinates satisfy |u| <= 1 (the fp32 norm makes it 1 + 1e-5 at most), so
+// f stays inside the table without a clamp; a NaN converts to cell 0.  A u that rounds into
+// a neighbouring cell, or a comparison rounded in cell coordinates, can only change a code
+// within the rounding of u (far below 1e-6) of a boundary.
 struct CodeGrid {
-  float scale, offset, last_cell;
-  int cells;
+  float scale, offset;  // f = u * scale + offset
   bool ok;
 };
 
@@ -133,191 +108,334 @@ struct CodeGrid {
 template <int BITS>
 __device__ CodeGrid build_code_grid(const float *pos, uint2 *grid, int lane) {
   constexpr int L = 1 << BITS, NP = L / 2 - 1;
+  constexpr float kLo = -1.01f, kHi = 1.01f;
   float gap = pos[0];
 #pragma unroll
   for (int k = 0; k + 1 < NP; ++k) gap = fminf(gap, pos[k + 1] - pos[k]);
   const float w = 0.75f * gap;
-  const float lo = -pos[NP - 1] - 0.5f * w;
   CodeGrid gd;
-  gd.cells = (int)ceilf((2.f * pos[NP - 1] + w) / w) + 1;
-  gd.last_cell = (float)(gd.cells - 1);
   gd.scale = 1.f / w;
-  gd.offset = -lo / w;
-  gd.ok = gap > 0.f && gd.cells <= kGridCells;
+  gd.offset = -kLo / w;
+  gd.ok = gap > 0.f && pos[NP - 1] < kHi && (kHi - kLo) / w <= (float)kGridCells;
   if (!gd.ok) return gd;
-  const int cidx = lane;
-  const float e0 = lo + (float)cidx * w;        // lower edge (cell 0: -inf)
-  const float e1 = lo + (float)(cidx + 1) * w;  // upper edge (last cell: +inf)
-  const bool first = cidx == 0, last = cidx == gd.cells - 1;
-  uint32_t base = 0, inside = 0;
-  float bnd = INFINITY;
-  auto visit = [&](float t) {
-    const bool below = !first && t < e0;
-    const bool in = !below && (last || t < e1);
-    base += below ? 1u : 0u;
-    inside += in ? 1u : 0u;
-    if (in) bnd = fminf(bnd, t);
-  };
+  bool bad = false;
 #pragma unroll
-  for (int k = NP - 1; k >= 0; --k) visit(-pos[k]);
-  visit(0.f);
+  for (int half = 0; half < 2; ++half) {
+    const int cidx = lane + 64 * half;
+    const float e0 = kLo + (float)cidx * w;  // lower edge
+    const float e1 = e0 + w;                 // upper edge
+    uint32_t base = 0, inside = 0;
+    float bnd = INFINITY;
+    auto visit = [&](float t) {
+      base += t < e0 ? 1u : 0u;
+      const bool in = t >= e0 && t < e1;
+      inside += in ? 1u : 0u;
+      if (in) bnd = fminf(bnd, (t - kLo) * gd.scale);
+    };
 #pragma unroll
-  for (int k = 0; k < NP; ++k) visit(pos[k]);
-  const bool bad = cidx < gd.cells && inside > 1u;
+    for (int k = NP - 1; k >= 0; --k) visit(-pos[k]);
+    visit(0.f);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) visit(pos[k]);
+    bad |= inside > 1u;
+    grid[cidx] = make_uint2(base, __float_as_uint(bnd));
+  }
   gd.ok = __ballot(bad) == 0ull;
-  if (cidx < gd.cells) grid[cidx] = make_uint2(base, __float_as_uint(bnd));
   __builtin_amdgcn_wave_barrier();
   __asm__ volatile("" ::: "memory");
   return gd;
 }
 
-__device__ __forceinline__ uint32_t code_by_grid(float u, const CodeGrid &gd, const uint2 *grid) {
-  const int cidx = (int)__builtin_amdgcn_fmed3f(fmaf(u, gd.scale, gd.offset), 0.f, gd.last_cell);
-  const uint2 e = grid[cidx];
-  return e.x + (u > __uint_as_float(e.y) ? 1u : 0u);
+// code of coordinate v of a vector whose u = v * inv; sinv = inv * gd.scale
+__device__ __forceinline__ uint32_t code_by_grid(float v, float sinv, const CodeGrid &gd, const uint2 *grid) {
+  const float f = fmaf(v, sinv, gd.offset);
+  const uint2 e = grid[(int)f];
+  return e.x + (f > __uint_as_float(e.y) ? 1u : 0u);
 }
 
-// One 64-token chunk (chunk index bx counted from the chunk of start_pos) of the plane of
-// (batch b, kv head h).
+// The grid for 256-level codebooks, shared by the block and built by all its threads (the
+// caller synchronises before and after): cells of 0.75 x the smallest boundary gap over
+// [t_0 - w/2, t_254 + w/2), at most 1024 of them; cell 0 reaches down to -inf and the last
+// cell up to +inf, so lookups clamp the cell index.  Entry and check as for the wave grid;
+// the boundaries are copied to sh.bnd8 for the entries' binary searches and the fallback.
+struct CodeGrid8 {
+  float scale, offset, last_cell;
+  bool ok;
+};
+
+__device__ CodeGrid8 build_code_grid8(const float *boundaries, QuantLds &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float gmin = INFINITY;
+  if (tid < 255) sh.bnd8[tid] = boundaries[tid];
+  __syncthreads();
+  if (tid < 254) gmin = sh.bnd8[tid + 1] - sh.bnd8[tid];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) gmin = fminf(gmin, __shfl_xor(gmin, m));
+  if (lane == 0) sh.red[wave] = gmin;
+  if (tid == 0) sh.flag = 0;
+  __syncthreads();
+  gmin = fminf(fminf(sh.red[0], sh.red[1]), fminf(sh.red[2], sh.red[3]));
+  const float w = 0.75f * gmin;
+  const float lo = sh.bnd8[0] - 0.5f * w;
+  CodeGrid8 gd;
+  const float span = (sh.bnd8[254] + 0.5f * w - lo) / w;
+  gd.ok = gmin > 0.f && span < 1023.f;
+  if (!gd.ok) return gd;  // uniform: every thread sees the same values
+  const int cells = (int)ceilf(span) + 1;
+  gd.scale = 1.f / w;
+  gd.offset = -lo / w;
+  gd.last_cell = (float)(cells - 1);
+  bool bad = false;
+  for (int cidx = tid; cidx < cells; cidx += blockDim.x) {
+    const float e0 = lo + (float)cidx * w, e1 = e0 + w;
+    // base = #{t < e0} (0 for the first cell, which reaches down to -inf)
+    uint32_t base = 0;
+    if (cidx > 0) {
+#pragma unroll
+      for (int step = 128; step >= 1; step >>= 1)
+        if (base + step - 1 < 255 && sh.bnd8[base + step - 1] < e0) base += step;
+    }
+    const bool last = cidx == cells - 1;
+    float bnd = INFINITY;
+    if (base < 255 && (last || sh.bnd8[base] < e1)) {
+      bnd = (sh.bnd8[base] - lo) * gd.scale;
+      if (base + 1 < 255 && (last || sh.bnd8[base + 1] < e1)) bad = true;
+    }
+    sh.grid8[cidx] = make_uint2(base, __float_as_uint(bnd));
+  }
+  if (bad) sh.flag = 1;
+  __syncthreads();
+  gd.ok = sh.flag == 0;
+  return gd;
+}
+
+__device__ __forceinline__ uint32_t code_by_grid8(float v, float sinv, const CodeGrid8 &gd, const uint2 *grid) {
+  const float f = fmaf(v, sinv, gd.offset);
+  const uint2 e = grid[(int)__builtin_amdgcn_fmed3f(f, 0.f, gd.last_cell)];
+  return e.x + (f > __uint_as_float(e.y) ? 1u : 0u);
+}
+
+// Packs the 32 codes of coordinates 32q .. 32q+31 of token t into bits
+// [32*BITS*q, 32*BITS*(q+1)) of the token's row.
+template <int BITS>
+__device__ __forceinline__ void store_row_quarter(uint8_t *plane, int t, int q, const uint32_t (&code)[32]) {
+  uint32_t w[BITS];
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int bit = e * BITS;
+    w[bit >> 5] |= code[e] << (bit & 31);
+    if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+  }
+  uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)t * 16 * BITS + 4 * BITS * q);
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+}
+
+// Value groups from the wave's staged codes stage[16 tokens][128] (bytes): lane r of a
+// group builds coordinates 4r .. 4r+3 of its group, 8 tokens x BITS bits per coordinate,
+// BITS bytes each; bytes of tokens outside [lo, hi) are read-modified-written.
+template <int BITS>
+__device__ __forceinline__ void store_groups_from_stage(const uint8_t (*stage)[kD], uint8_t *plane, int lane,
+                                                        int wt0, int lo, int hi) {
+  constexpr int L = 1 << BITS;
+  const int gi = lane >> 5, r = lane & 31;
+  const int tg = wt0 + 8 * gi;  // first token of the group
+  uint64_t chunk[4] = {0, 0, 0, 0}, mask = 0;
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const uint32_t cw = *reinterpret_cast<const uint32_t *>(&stage[8 * gi + tt][4 * r]);
+    const bool in = tg + tt >= lo && tg + tt < hi;
+    if (in) mask |= (uint64_t)(L - 1) << (tt * BITS);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) chunk[k] |= (uint64_t)((cw >> (8 * k)) & 0xffu) << (tt * BITS);
+  }
+  if (mask == 0) return;
+  // the 4 coordinate chunks are 4*BITS consecutive bytes: pack them into BITS dwords
+  uint32_t out[BITS], msk[BITS];
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) { out[k] = 0u; msk[k] = 0u; }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bit = k * 8 * BITS;  // bit offset of chunk k
+    const uint64_t cv = chunk[k] & mask;
+#pragma unroll
+    for (int part = 0; part < (8 * BITS + 31) / 32 + 1; ++part) {
+      const int wb = (bit >> 5) + part;  // destination dword
+      if (wb >= BITS) break;
+      const int sh = 32 * wb - bit;     // chunk bit that lands at bit 0 of dword wb
+      if (sh >= 8 * BITS) break;
+      if (sh >= 0) {
+        out[wb] |= (uint32_t)(cv >> sh);
+        msk[wb] |= (uint32_t)(mask >> sh);
+      } else {
+        out[wb] |= (uint32_t)(cv << (-sh));
+        msk[wb] |= (uint32_t)(mask << (-sh));
+      }
+    }
+  }
+  uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)(tg >> 3) * kD * BITS + 4 * BITS * r);
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) {
+    if (msk[k] == 0xffffffffu) dst[k] = out[k];
+    else if (msk[k] != 0u) dst[k] = (dst[k] & ~msk[k]) | out[k];
+  }
+}
+
+// Code search set-up shared by both paths: the positive boundaries and the code grid
+// (codebooks of up to 16 levels), or the 255 boundaries in LDS (256 levels).
+template <int BITS>
+__device__ __forceinline__ CodeGrid setup_code_search(const CacheView &c, QuantLds &sh, int wave, int lane,
+                                                      float (&pos)[(1 << BITS) / 2 > 1 ? (1 << BITS) / 2 - 1 : 1]) {
+  constexpr int L = 1 << BITS;
+  CodeGrid gd{0.f, 0.f, false};
+  if (BITS <= 4) {
+#pragma unroll
+    for (int k = 0; k < L / 2 - 1; ++k) pos[k] = c.boundaries[L / 2 + k];
+    gd = build_code_grid<BITS <= 4 ? BITS : 4>(pos, sh.grid[wave], lane);
+  }
+  return gd;
+}
+
+// Code without the grid: compare count (up to 16 levels) or binary search (256 levels).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_by_search(float u, const QuantLds &sh, int wave, const float *pos) {
+  return BITS <= 4 ? code_of<BITS <= 4 ? BITS : 4>(u, pos) : code_of_8(u, sh.bnd8);
+}
+
+constexpr int kChunksPerBlock = 4;  // chunks one block quantizes, reusing the set-up
+
+// Loads the lane's 32 coordinates with the rotation signs applied: the sign masks m (0 or the
+// sign bit) are folded into the conversion, (w << 16) + m and (w & 0xffff0000) ^ m for bf16.
+template <int DTYPE>
+__device__ __forceinline__ void load32_signed(const void *x, size_t base, const uint32_t (&m)[32], float v[32]) {
+  if (DTYPE == TQ_F32) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + base);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint4 f = p[r];
+      v[4 * r] = __uint_as_float(f.x ^ m[4 * r]);
+      v[4 * r + 1] = __uint_as_float(f.y ^ m[4 * r + 1]);
+      v[4 * r + 2] = __uint_as_float(f.z ^ m[4 * r + 2]);
+      v[4 * r + 3] = __uint_as_float(f.w ^ m[4 * r + 3]);
+    }
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + base);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 w = p[r];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * r + 2 * e;
+        if (DTYPE == TQ_BF16) {
+          v[i] = __uint_as_float((ws[e] << 16) + m[i]);  // + flips bit 31 only: low bits are 0
+          v[i + 1] = __uint_as_float((ws[e] & 0xffff0000u) ^ m[i + 1]);
+        } else {
+          v[i] = __uint_as_float(__float_as_uint(half_bits_to_float((uint16_t)(ws[e] & 0xffffu))) ^ m[i]);
+          v[i + 1] = __uint_as_float(__float_as_uint(half_bits_to_float((uint16_t)(ws[e] >> 16))) ^ m[i + 1]);
+        }
+      }
+    }
+  }
+}
+
+// Up to kChunksPerBlock 64-token chunks (block bx takes chunks kChunksPerBlock * bx .. counted
+// from the chunk of start_pos) of the plane of (batch b, kv head h).  Each wave owns 16
+// tokens of every chunk; the code search set-up and the sign masks are made once.
 template <int DTYPE, int BITS, int LAYOUT>
 __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *__restrict__ x,
                                                int start_pos, int n_tokens, int h, int b, int bx,
                                                QuantLds &sh) {
   constexpr int L = 1 << BITS;
-  const int chunk0 = (start_pos / kChunk + bx) * kChunk;
-  const int lo = max(chunk0, start_pos), hi = min(chunk0 + kChunk, start_pos + n_tokens);
+  const int first = start_pos / kChunk + bx * kChunksPerBlock;
+  const int last = min(first + kChunksPerBlock - 1, (start_pos + n_tokens - 1) / kChunk);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wt0 = chunk0 + 16 * wave;
-  if (wt0 + 16 <= lo || wt0 >= hi) return;  // no token of this wave is in the range
-
+  CodeGrid8 gd8{0.f, 0.f, 0.f, false};
+  if (BITS == 8) gd8 = build_code_grid8(c.boundaries, sh);  // whole block, before any wave leaves
+  // tokens of this wave: [first*64 + 16 wave, +16), ... ; none in range -> done
+  {
+    bool any = false;
+    for (int ch = first; ch <= last; ++ch) {
+      const int wt0 = ch * kChunk + 16 * wave;
+      any |= wt0 + 16 > start_pos && wt0 < start_pos + n_tokens;
+    }
+    if (!any) return;
+  }
   const int j = lane >> 2, q = lane & 3;
-  const int t = wt0 + j;
-  const bool valid = t >= lo && t < hi;
 
   float pos[L / 2 > 1 ? L / 2 - 1 : 1];
-  CodeGrid gd{0.f, 0.f, 0.f, 0, false};
-  if (BITS <= 4) {
-#pragma unroll
-    for (int k = 0; k < L / 2 - 1; ++k) pos[k] = c.boundaries[L / 2 + k];
-    gd = build_code_grid<BITS <= 4 ? BITS : 4>(pos, sh.grid[wave], lane);
-  } else {
-    for (int k = lane; k < L - 1; k += 64) sh.bnd8[wave][k] = c.boundaries[k];
-    __builtin_amdgcn_wave_barrier();
-    __asm__ volatile("" ::: "memory");
-  }
-
-  float v[32];
-  if (valid) {
-    const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
-    load32<DTYPE>(x, row * kD + 32 * q, v);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) v[e] = 0.f;
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
+  const CodeGrid gd = setup_code_search<BITS>(c, sh, wave, lane, pos);
+  uint32_t smask[32];  // sign bit of s_(32q + e), bit 7 of its byte
   {
     const int4 sw0 = *reinterpret_cast<const int4 *>(c.signs + 32 * q);
     const int4 sw1 = *reinterpret_cast<const int4 *>(c.signs + 32 * q + 16);
-    const int sw[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
+    const uint32_t sw[8] = {(uint32_t)sw0.x, (uint32_t)sw0.y, (uint32_t)sw0.z, (uint32_t)sw0.w,
+                            (uint32_t)sw1.x, (uint32_t)sw1.y, (uint32_t)sw1.z, (uint32_t)sw1.w};
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {  // flip the sign bit where s_i = -1 (byte 0xff)
-      const uint32_t neg = ((uint32_t)sw[e >> 2] >> (8 * (e & 3) + 7)) & 1u;
-      v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (neg << 31));
-    }
+    for (int e = 0; e < 32; ++e) smask[e] = (sw[e >> 2] << (24 - 8 * (e & 3))) & 0x80000000u;
   }
-  quad_fwht(v, q);
-  const float n = sqrtf(ss);
-  const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
-  uint32_t code[32];
-  if (BITS <= 4 && gd.ok) {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) code[e] = code_by_grid(v[e] * inv, gd, sh.grid[wave]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float u = v[e] * inv;
-      code[e] = BITS <= 4 ? code_of<BITS <= 4 ? BITS : 4>(u, pos) : code_of_8(u, sh.bnd8[wave]);
-    }
-  }
-  if (valid && q == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
-
   uint8_t *plane = c.plane(b, h);
-  if (LAYOUT == TQ_LAYOUT_ROWS) {
-    // the lane's 32 codes are bits [32*BITS*q, 32*BITS*(q+1)) of the token's row
-    uint32_t w[BITS];
-#pragma unroll
-    for (int k = 0; k < BITS; ++k) w[k] = 0u;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int bit = e * BITS;
-      w[bit >> 5] |= code[e] << (bit & 31);
-      if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
-    }
+
+  for (int ch = first; ch <= last; ++ch) {
+    const int chunk0 = ch * kChunk;
+    const int lo = max(chunk0, start_pos), hi = min(chunk0 + kChunk, start_pos + n_tokens);
+    const int wt0 = chunk0 + 16 * wave;
+    if (wt0 + 16 <= lo || wt0 >= hi) continue;  // no token of this wave in this chunk
+    const int t = wt0 + j;
+    const bool valid = t >= lo && t < hi;
+
+    float v[32];
     if (valid) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)t * 16 * BITS + 4 * BITS * q);
+      const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
+      load32_signed<DTYPE>(x, row * kD + 32 * q, smask, v);
+    } else {
 #pragma unroll
-      for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+      for (int e = 0; e < 32; ++e) v[e] = 0.f;
     }
-  } else {
-    // stage codes [token][coord] as bytes, then lane r of a group builds coordinates
-    // 4r .. 4r+3 of its group: 8 tokens x BITS bits per coordinate, BITS bytes each
+    float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      uint32_t pk[4];
+    for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    quad_fwht(v, q);
+    const float n = sqrtf(ss);
+    const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
+    uint32_t code[32];
+    if (BITS <= 4 && gd.ok) {
+      const float sinv = inv * gd.scale;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        pk[k] = code[16 * r + 4 * k] | (code[16 * r + 4 * k + 1] << 8) | (code[16 * r + 4 * k + 2] << 16) |
-                (code[16 * r + 4 * k + 3] << 24);
-      *reinterpret_cast<uint4 *>(&sh.stage[wave][j][32 * q + 16 * r]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      for (int e = 0; e < 32; ++e) code[e] = code_by_grid(v[e], sinv, gd, sh.grid[wave]);
+    } else if (BITS == 8 && gd8.ok) {
+      const float sinv = inv * gd8.scale;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) code[e] = code_by_grid8(v[e], sinv, gd8, sh.grid8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) code[e] = code_by_search<BITS>(v[e] * inv, sh, wave, pos);
     }
-    __builtin_amdgcn_wave_barrier();
-    __asm__ volatile("" ::: "memory");
-    const int gi = lane >> 5, r = lane & 31;
-    const int tg = wt0 + 8 * gi;  // first token of the group
-    uint64_t chunk[4] = {0, 0, 0, 0}, mask = 0;
+    if (valid && q == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
+
+    if (LAYOUT == TQ_LAYOUT_ROWS) {
+      if (valid) store_row_quarter<BITS>(plane, t, q, code);
+    } else {
+      // stage codes [token][coord] as bytes for the value-group packing
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t cw = *reinterpret_cast<const uint32_t *>(&sh.stage[wave][8 * gi + tt][4 * r]);
-      const bool in = tg + tt >= lo && tg + tt < hi;
-      if (in) mask |= (uint64_t)(L - 1) << (tt * BITS);
+      for (int r = 0; r < 2; ++r) {
+        uint32_t pk[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) chunk[k] |= (uint64_t)((cw >> (8 * k)) & 0xffu) << (tt * BITS);
-    }
-    if (mask != 0) {
-      // the 4 coordinate chunks are 4*BITS consecutive bytes: pack them into BITS dwords
-      uint32_t out[BITS], msk[BITS];
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) { out[k] = 0u; msk[k] = 0u; }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int bit = k * 8 * BITS;  // bit offset of chunk k
-        const uint64_t cv = chunk[k] & mask;
-#pragma unroll
-        for (int part = 0; part < (8 * BITS + 31) / 32 + 1; ++part) {
-          const int wb = (bit >> 5) + part;  // destination dword
-          if (wb >= BITS) break;
-          const int sh = 32 * wb - bit;     // chunk bit that lands at bit 0 of dword wb
-          if (sh >= 8 * BITS) break;
-          if (sh >= 0) {
-            out[wb] |= (uint32_t)(cv >> sh);
-            msk[wb] |= (uint32_t)(mask >> sh);
-          } else {
-            out[wb] |= (uint32_t)(cv << (-sh));
-            msk[wb] |= (uint32_t)(mask << (-sh));
-          }
-        }
+        for (int k = 0; k < 4; ++k)
+          pk[k] = code[16 * r + 4 * k] | (code[16 * r + 4 * k + 1] << 8) | (code[16 * r + 4 * k + 2] << 16) |
+                  (code[16 * r + 4 * k + 3] << 24);
+        *reinterpret_cast<uint4 *>(&sh.stage[wave][j][32 * q + 16 * r]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
-      uint32_t *dst = reinterpret_cast<uint32_t *>(plane + (size_t)(tg >> 3) * kD * BITS + 4 * BITS * r);
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) {
-        if (msk[k] == 0xffffffffu) dst[k] = out[k];
-        else if (msk[k] != 0u) dst[k] = (dst[k] & ~msk[k]) | out[k];
-      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      store_groups_from_stage<BITS>(sh.stage[wave], plane, lane, wt0, lo, hi);
+      __builtin_amdgcn_wave_barrier();  // the stage is rewritten by the next chunk
+      __asm__ volatile("" ::: "memory");
     }
   }
 }

@@ -49,7 +49,7 @@ hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batc
                               const void *xv, int x_dtype, int start_pos, int n_tokens,
                               hipStream_t stream) {
   const int first = start_pos / kChunk, last = (start_pos + n_tokens - 1) / kChunk;
-  dim3 grid(last - first + 1, kc.n_kv_heads, 2 * batch);
+  dim3 grid((last - first + kChunksPerBlock) / kChunksPerBlock, kc.n_kv_heads, 2 * batch);
   if (x_dtype == TQ_F32) launch_kv<TQ_F32>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
   else if (x_dtype == TQ_BF16) launch_kv<TQ_BF16>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
   else launch_kv<TQ_F16>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
