@@ -54,7 +54,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
 SplitPlan plan_splits(int batch, int n_kv_heads, int ctx_len, int group) {
   const long units = (long)batch * n_kv_heads;
-  const long target_blocks = 2048;
+  const long target_blocks = 1024;
   // a split's softmax weights [split_len][group] fit the Sparse-V pass's LDS
   const long padded = group <= 4 ? 4 : group <= 8 ? 8 : 16;
   const long max_len = (kSparseWeights / padded) / kSplitAlign * kSplitAlign;

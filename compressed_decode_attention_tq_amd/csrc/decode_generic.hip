@@ -257,8 +257,15 @@ __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
   __shared__ float lutV[1 << BV];
   __shared__ __align__(16) float w[kSparseWeights];  // [token in split][GP]; then [wave][GP][kD]
   __shared__ int gflag[kSparseWeights / 32];         // 8-token groups holding a kept row
+  __shared__ uint16_t nvs[kSparseWeights / 4];       // fp16 value norms of the split
   static_assert(4 * GP * kD <= kSparseWeights, "wave sums fit the weight table");
 
+  const int t_begin = s * L;
+  {  // the split's value norms go to LDS with the other set-up loads
+    const uint16_t *vnorm = a.v.norm_plane(b, kvh) + t_begin;
+    const int n_valid = min(L, seq_len_of(a, b) - t_begin);
+    for (int i = tid; i < L; i += blockDim.x) nvs[i] = i < n_valid ? vnorm[i] : (uint16_t)0;
+  }
   for (int i = tid; i < (1 << BV); i += blockDim.x) lutV[i] = a.v.centroids[i];
   for (int i = tid; i < L * GP; i += blockDim.x) w[i] = 0.f;
   for (int i = tid; i < L / 8; i += blockDim.x) gflag[i] = 0;
@@ -277,24 +284,36 @@ __global__ __launch_bounds__(256) void decode_sparse_v(DecodeArgs a) {
   }
   __syncthreads();
 
-  const int t_begin = s * L;
   const int count = a.cand_count[((size_t)b * a.n_kv_heads + kvh) * S + s];
   const float *base =
       a.cand + (((size_t)b * a.n_kv_heads + kvh) * S + s) * (size_t)L * (1 + g);
-  const uint16_t *vnorm = a.v.norm_plane(b, kvh);
-  for (int r = tid; r < count; r += blockDim.x) {
-    const float *rec = base + (size_t)r * (1 + g);
-    const int t = __float_as_int(rec[0]);
-    const float nv = half_bits_to_float(vnorm[t]);
-    const int tl = t - t_begin;
-    bool any = false;
-    for (int j = 0; j < g; ++j) {
-      const float z = rec[1 + j] - lse_s[j];
-      const bool keep = z >= a.ln_tau;
-      w[tl * GP + j] = keep ? __expf(z) * nv : 0.f;
-      any |= keep;
+  // two records per thread per round, their loads issued together
+  for (int r0 = 0; r0 < count; r0 += 2 * 256) {
+    float rec[2][1 + GP];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = r0 + k * 256 + tid;
+      const float *src = base + (size_t)min(r, count - 1) * (1 + g);
+#pragma unroll
+      for (int jj = 0; jj <= GP; ++jj) rec[k][jj] = jj <= g ? src[jj] : 0.f;
     }
-    if (any) gflag[tl >> 3] = 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (r0 + k * 256 + tid >= count) continue;
+      const int tl = __float_as_int(rec[k][0]) - t_begin;
+      const float nv = half_bits_to_float(nvs[tl]);
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < GP; ++j) {
+        if (j < g) {
+          const float z = rec[k][1 + j] - lse_s[j];
+          const bool keep = z >= a.ln_tau;
+          w[tl * GP + j] = keep ? __expf(z) * nv : 0.f;
+          any |= keep;
+        }
+      }
+      if (any) gflag[tl >> 3] = 1;
+    }
   }
   __syncthreads();
 
@@ -422,11 +441,12 @@ __global__ __launch_bounds__(128 * kMergeGroups) void decode_merge(DecodeArgs a)
       if (p.x != -INFINITY) l += p.y * __expf(p.x - mx);
     }
     int k = grp;
-    for (; k + 3 * kMergeGroups < S; k += 4 * kMergeGroups) {
-      float v[4];
+    for (; k + 15 * kMergeGroups < S; k += 16 * kMergeGroups) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = po[(size_t)(k + u * kMergeGroups) * kD + i];
-      o += (v[0] + v[1]) + (v[2] + v[3]);
+      for (int u = 0; u < 16; ++u) v[u] = po[(size_t)(k + u * kMergeGroups) * kD + i];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) o += v[u];
     }
     for (; k < S; k += kMergeGroups) o += po[(size_t)k * kD + i];
   }
