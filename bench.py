@@ -150,6 +150,9 @@ def main():
         result = bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log)
     else:
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
+    stream = stream_read_gbs(torch, tq, log)
+    result["roofline"]["stream_read_gbs"] = stream
+    result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
     traffic = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
     launches = result.pop("_launches", 1)  # traffic per step when a step is several launches
     result["roofline"]["traffic"] = None if traffic is None else traffic * launches
@@ -169,32 +172,66 @@ class Timer:
         self.eager = eager
 
     def per_iteration_ms(self, fn, n, warmup):
+        return self.per_iteration_stats(fn, n, warmup, batches=1)[0]
+
+    def per_iteration_stats(self, fn, n, warmup, batches):
+        """(median, min, max) per-iteration ms over `batches` timed runs of the same n
+        iterations (graph replays, or eager loops)."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if self.eager:
-            stream = torch.cuda.current_stream()
-            start.record(stream)
-            for i in range(n):
-                fn(i)
-            end.record(stream)
-            torch.cuda.synchronize()
-            return start.elapsed_time(end) / n
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n):
-                fn(i)
-        graph.replay()
-        torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
+        times = []
+        if self.eager:
+            for _ in range(batches):
+                start.record(stream)
+                for i in range(n):
+                    fn(i)
+                end.record(stream)
+                torch.cuda.synchronize()
+                times.append(start.elapsed_time(end) / n)
+        else:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(n):
+                    fn(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            for _ in range(batches):
+                start.record(stream)
+                graph.replay()
+                end.record(stream)
+                torch.cuda.synchronize()
+                times.append(start.elapsed_time(end) / n)
+            del graph
+        times.sort()
+        return times[len(times) // 2], times[0], times[-1]
+
+
+def stream_read_gbs(torch, tq, log):
+    """Streaming-read bandwidth of the device: the library's plain read kernel over three
+    512 MiB buffers in turn (more than the 256 MB last-level cache), best of 5 rounds."""
+    bufs = [torch.ones(512 << 20, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        tq.probe_stream_read(b, sink)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    best = float("inf")
+    for _ in range(5):
         start.record(stream)
-        graph.replay()
+        for b in bufs:
+            tq.probe_stream_read(b, sink)
         end.record(stream)
         torch.cuda.synchronize()
-        del graph
-        return start.elapsed_time(end) / n
+        best = min(best, start.elapsed_time(end))
+    gbs = 3 * (512 << 20) / (best * 1e-3) / 1e9
+    log(f"[bench] streaming-read probe: {gbs:.0f} GB/s")
+    del bufs
+    return gbs
 
 
 def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
@@ -240,7 +277,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     kv_tokens = batch * ctx
     value = kv_tokens / (ms_per_step / 1e3)
-    ms_k = timer.per_iteration_ms(decode_only, max(args.steps, 2 * copies), 2)
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(decode_only, max(args.steps, 2 * copies), 2, batches=5)
     ms_a = timer.per_iteration_ms(append, max(args.steps, 2 * copies), 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
     achieved = nbytes / (ms_k / 1e3) / 1e9
@@ -258,6 +295,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
                    "step": "append 1 token (K,V) + decode attention", "cache_copies": copies,
                    "timing": "eager" if args.eager else "hip graph replay"},
         "decode_call_us": ms_k * 1e3,
+        "decode_call_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
         "append_kv_us": ms_a * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,

@@ -58,12 +58,13 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
         L.tq_decode_workspace_bytes.restype = sz
         L.tq_dequantize.argtypes = [ctypes.POINTER(CacheStruct), i32, i32, vp, i32, vp]
+        L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.tq_code_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.tq_code_bytes.restype = sz
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_dequantize"):
+                     "tq_dequantize", "tq_probe_stream_read"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -179,6 +180,13 @@ def quantize_append_kv(k_cache: PackedCache, v_cache: PackedCache, k, v, start_p
     _check(lib().tq_quantize_append_kv(ctypes.byref(ks), ctypes.byref(vs), _dev(k, "k"), _dev(v, "v"),
                                        _dtype_code(k.dtype), start_pos, k.shape[1], _stream_ptr(stream)),
            "tq_quantize_append_kv")
+
+
+def probe_stream_read(buf, sink, stream=None):
+    """One launch of the streaming-read probe over the device tensor `buf` (measurement
+    only); `sink` is a device int32 tensor of at least one element."""
+    _check(lib().tq_probe_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                                      _stream_ptr(stream)), "tq_probe_stream_read")
 
 
 def dequantize(cache: PackedCache, start_pos: int, n_tokens: int, dtype=None, stream=None):

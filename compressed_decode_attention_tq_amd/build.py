@@ -15,7 +15,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
 SOURCES = ["api.hip", "quantize.hip", "quantize_kv.hip", "decode_generic.hip", "decode_mfma.hip", "decode_fused.hip",
-           "codebook.cpp"]
+           "probe.hip", "codebook.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [

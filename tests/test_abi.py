@@ -2,6 +2,7 @@
 its host codebook equals the oracle's, and argument validation rejects bad calls
 before any HIP call (so these run without a GPU)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -14,16 +15,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "tq.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     L = tq.lib()
     names = _declared_symbols()
-    assert {"tq_make_codebook_table", "tq_quantize_append", "tq_decode_attn", "tq_dequantize",
-            "tq_decode_workspace_bytes", "tq_status_string", "tq_code_bytes"} <= set(names)
+    assert {"tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
+            "tq_dequantize", "tq_decode_workspace_bytes", "tq_status_string", "tq_code_bytes",
+            "tq_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -148,3 +152,12 @@ def test_decode_argument_validation():
     assert _decode(k, _cache(layout=1, bits=2, capacity=2048)) == tq.TQ_ERR_INVALID_ARG
     assert _decode(k, _cache(layout=1, bits=2, signs=FAKE + 0x400100)) == tq.TQ_ERR_INVALID_ARG
     assert _decode(k, v, seq=FAKE + 0x900002) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_probe_rejects_bad_arguments():
+    f = tq.lib().tq_probe_stream_read
+    assert f(None, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert f(FAKE, 1 << 20, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert f(FAKE + 8, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert f(FAKE, 1000, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, None) == tq.TQ_ERR_INVALID_ARG

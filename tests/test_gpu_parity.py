@@ -263,3 +263,14 @@ def test_decode_is_deterministic(signs):
         b = tq.decode_attn(kc, vc, q, 900, 0.0884, tau=tau).out.clone()
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+def test_stream_read_probe_runs():
+    """The measurement probe reads a buffer and leaves it untouched (it only loads)."""
+    _say("stream-read probe")
+    buf = torch.arange(1 << 18, dtype=torch.int32, device=DEV)
+    ref = buf.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    tq.probe_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
