@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--summarize-stats", default=None)
     p.add_argument("--summarize-traffic", action="store_true")
+    p.add_argument("--summarize-instmix", default=None,
+                   help="rocprofv3 --pmc directory with SQ_WAVES and SQ_INSTS_* counters")
+    p.add_argument("--kernel-us", type=float, default=None, help="average launch time of --kernel")
     p.add_argument("--fetch", default=None)
     p.add_argument("--write", default=None)
     p.add_argument("--kernel", default=DECODE_KERNEL)
@@ -122,6 +125,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args)
+        return
+    if args.summarize_instmix:
+        summarize_instmix(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): it measures the single-GPU "
@@ -507,6 +513,35 @@ def summarize_traffic(args):
            "command": args.command}
     kname = "decode" if args.kernel == DECODE_KERNEL else "quantize"
     with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{args.workload}.txt"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_instmix(args):
+    """Instructions per wave of `--kernel` (all its instances, dispatch-weighted) from
+    SQ_WAVES and SQ_INSTS_{VALU,MFMA,LDS,SALU,VMEM}, and the vector-ALU issue fraction: a wave64
+    VALU instruction occupies a 16-lane SIMD for 4 cycles, so the fraction is
+    4 x (VALU - MFMA instructions) / (SIMDs x clock x launch time) (256 CUs x 4 SIMDs, 2.4 GHz)."""
+    names = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"]
+    got = {}
+    for n in names:
+        means, counts = _counter_means(args.summarize_instmix, n)
+        keys = [k for k in means if args.kernel in k]
+        if keys:
+            tot = sum(counts[k] for k in keys)
+            got[n] = sum(means[k] * counts[k] for k in keys) / tot
+    if "SQ_WAVES" not in got or "SQ_INSTS_VALU" not in got:
+        sys.exit(f"no SQ_WAVES / SQ_INSTS_VALU for {args.kernel!r}")
+    waves = got["SQ_WAVES"]
+    rec = {"kernel": args.kernel, "workload": args.workload, "waves_per_launch": waves,
+           "per_wave": {n[9:].lower(): got[n] / waves for n in names[1:] if n in got},
+           "command": args.command}
+    if args.kernel_us:
+        cycles = args.kernel_us * 1e-6 * 2.4e9
+        rec["launch_us"] = args.kernel_us
+        # SQ_INSTS_VALU includes the matrix instructions, which run on their own unit
+        rec["valu_issue_fraction"] = 4.0 * (got["SQ_INSTS_VALU"] - got.get("SQ_INSTS_MFMA", 0.0)) / (1024 * cycles)
+    with open(os.path.join(ROOT, "profiles", f"instmix_{args.kernel}_{args.workload}.txt"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
 
