@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(CacheView c, void *__re
   }
   quad_fwht(v, q);
   if (!valid) return;
-  const float scale = half_bits_to_float(c.norm_plane(b, h)[t]) * kInvSqrtD;
+  const float scale = half_bits_to_float(c.norm_plane(b, h)[t]) * kInvSqrtD * quad_fwht_sign(q);
   const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {

@@ -32,10 +32,12 @@ __device__ __forceinline__ float quad_swap(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Unnormalised Walsh-Hadamard transform of 128 values held 32 per lane by a lane quad
-// (lane q of the quad holds coordinates 32q .. 32q+31): five butterfly stages inside the
-// lane, then two across the quad, where the upper lane of a pair keeps partner - own and
-// the lower one partner + own (one multiply-add by a per-lane sign of +-1, exact).
+// Walsh-Hadamard transform (unnormalised) of 128 values held 32 per lane by a lane quad (lane
+// q of the quad holds coordinates 32q .. 32q+31): five butterfly stages inside the lane,
+// then two across the quad as v += s * partner (s = +1 for the lower lane of a pair, -1 for
+// the upper), one DPP multiply-add each.  The upper lane thereby holds own - partner, the
+// negative of its butterfly output, so the lane ends with (-1)^popcount(q) times the
+// transform: quad_fwht_sign(q) gives that factor, which the caller folds into its scale.
 __device__ __forceinline__ void quad_fwht(float v[32], int q) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
@@ -48,12 +50,99 @@ __device__ __forceinline__ void quad_fwht(float v[32], int q) {
       }
     }
   }
-  const float s1 = (q & 1) ? -1.f : 1.f, s2 = (q & 2) ? -1.f : 1.f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = fmaf(s1, v[e], quad_swap<0xB1>(v[e]));
-#pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = fmaf(s2, v[e], quad_swap<0x4E>(v[e]));
+  // v += s * partner as v_fmac_f32_dpp (the compiler does not fold the DPP move into a
+  // multiply-accumulate).  A DPP read needs two wait states after a vector write of its
+  // source: the s_nop covers the instructions before each block, and inside a block no
+  // instruction reads a register the two before it wrote.
+  {
+    const float s = (q & 1) ? -1.f : 1.f;
+    asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %0, %0, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %1, %1, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %2, %2, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %3, %3, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %4, %4, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %5, %5, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %6, %6, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %7, %7, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %8, %8, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %9, %9, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %10, %10, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %11, %11, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %12, %12, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %13, %13, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %14, %14, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %15, %15, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      : "+v"(v[0+0]), "+v"(v[0+1]), "+v"(v[0+2]), "+v"(v[0+3]), "+v"(v[0+4]), "+v"(v[0+5]), "+v"(v[0+6]), "+v"(v[0+7]), "+v"(v[0+8]), "+v"(v[0+9]), "+v"(v[0+10]), "+v"(v[0+11]), "+v"(v[0+12]), "+v"(v[0+13]), "+v"(v[0+14]), "+v"(v[0+15])
+      : "v"(s));
+    asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %0, %0, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %1, %1, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %2, %2, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %3, %3, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %4, %4, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %5, %5, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %6, %6, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %7, %7, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %8, %8, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %9, %9, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %10, %10, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %11, %11, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %12, %12, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %13, %13, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %14, %14, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %15, %15, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      : "+v"(v[16+0]), "+v"(v[16+1]), "+v"(v[16+2]), "+v"(v[16+3]), "+v"(v[16+4]), "+v"(v[16+5]), "+v"(v[16+6]), "+v"(v[16+7]), "+v"(v[16+8]), "+v"(v[16+9]), "+v"(v[16+10]), "+v"(v[16+11]), "+v"(v[16+12]), "+v"(v[16+13]), "+v"(v[16+14]), "+v"(v[16+15])
+      : "v"(s));
+  }
+  {
+    const float s = (q & 2) ? -1.f : 1.f;
+    asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %0, %0, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %1, %1, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %2, %2, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %3, %3, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %4, %4, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %5, %5, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %6, %6, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %7, %7, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %8, %8, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %9, %9, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %10, %10, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %11, %11, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %12, %12, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %13, %13, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %14, %14, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %15, %15, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      : "+v"(v[0+0]), "+v"(v[0+1]), "+v"(v[0+2]), "+v"(v[0+3]), "+v"(v[0+4]), "+v"(v[0+5]), "+v"(v[0+6]), "+v"(v[0+7]), "+v"(v[0+8]), "+v"(v[0+9]), "+v"(v[0+10]), "+v"(v[0+11]), "+v"(v[0+12]), "+v"(v[0+13]), "+v"(v[0+14]), "+v"(v[0+15])
+      : "v"(s));
+    asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %0, %0, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %1, %1, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %2, %2, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %3, %3, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %4, %4, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %5, %5, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %6, %6, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %7, %7, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %8, %8, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %9, %9, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %10, %10, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %11, %11, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %12, %12, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %13, %13, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %14, %14, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "v_fmac_f32_dpp %15, %15, %16 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      : "+v"(v[16+0]), "+v"(v[16+1]), "+v"(v[16+2]), "+v"(v[16+3]), "+v"(v[16+4]), "+v"(v[16+5]), "+v"(v[16+6]), "+v"(v[16+7]), "+v"(v[16+8]), "+v"(v[16+9]), "+v"(v[16+10]), "+v"(v[16+11]), "+v"(v[16+12]), "+v"(v[16+13]), "+v"(v[16+14]), "+v"(v[16+15])
+      : "v"(s));
+  }
 }
+
+__device__ __forceinline__ float quad_fwht_sign(int q) { return ((q ^ (q >> 1)) & 1) ? -1.f : 1.f; }
 
 // code = #{j : t_j < u} for a symmetric codebook of 2^BITS levels (BITS <= 4); `pos` holds
 // the positive boundaries t_{L/2} .. t_{L-2}.
@@ -402,7 +491,7 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
     ss += __shfl_xor(ss, 2);
     quad_fwht(v, q);
     const float n = sqrtf(ss);
-    const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
+    const float inv = (n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f) * quad_fwht_sign(q);
     uint32_t code[32];
     if (BITS <= 4 && gd.ok) {
       const float sinv = inv * gd.scale;
