@@ -1,20 +1,22 @@
-// Dense decode attention in one launch on matrix cores (gfx950 v_mfma_f32_16x16x32_f16), for
-// keys of 3 or 4 bits (TQ_LAYOUT_ROWS), values of 2 bits (TQ_LAYOUT_GROUP8) and a query
-// group of up to 8 heads per kv head.
+// Decode attention on matrix cores (gfx950 v_mfma_f32_16x16x32_f16) for keys of 3 or 4 bits
+// (TQ_LAYOUT_ROWS) and a query group of up to 8 heads per kv head: dense attention over
+// 2-bit values (TQ_LAYOUT_GROUP8) in one launch, or the key-only first pass of Sparse V.
 //
 // What is computed follows [google] "Google 最新極限壓縮算法…" (scores taken directly
 // against the quantized keys as ||k|| (Rq).c[idx], values summed in the rotated domain and
-// rotated back once) and [tq-plus] "turboquant_plus" §Sparse V / attention (online softmax
-// over the context).  The schedule is this file's own:
+// rotated back once) and, for the gate, [inferrs] "inferrs & TurboQuant：本地 LLM 推理的内存革命"
+// §Sparse V.  The schedule is this file's own:
 //
-//   * Work unit: one workgroup (8 waves, 160 KB of LDS, one per CU) owns a contiguous split
-//     of one (batch, kv head) context; its waves take the split's 64-token tiles in turn.
+//   * Work unit: one workgroup (8 waves, all 160 KB of LDS, so one resident per CU) owns one
+//     contiguous split of one (batch, kv head) context; the plan makes about one split per
+//     CU.  The waves take the split's 64-token tiles in turn.
 //   * The query group is rotated once per split: wave h applies the signs and the
 //     Walsh-Hadamard butterflies to head h (two coordinates per lane, lane exchanges for the
 //     upper six stages) and leaves R q in LDS for all waves.
 //   * Codes become fp16 matrix operands through lookup tables in LDS, replicated 32 times
-//     so the 32 lanes of one LDS pass never share a bank.  A key byte (two 4-bit codes, or a
-//     6-bit pair of 3-bit codes) gives {hi(c_a), hi(c_b), lo(c_a), lo(c_b)}: each centroid
+//     so the 32 lanes of one LDS pass never share a bank; every thread builds its part of
+//     the tables from the centroids it holds in registers.  A key byte (two 4-bit codes, or
+//     a 6-bit pair of 3-bit codes) gives {hi(c_a), hi(c_b), lo(c_a), lo(c_b)}: each centroid
 //     split into its fp16 value and the fp16 remainder.  A value byte (four 2-bit codes of
 //     one coordinate, four consecutive tokens) gives four fp16 centroids.
 //   * Scores keep about 22 significant bits: query row 2h holds the fp16 part of head h,
@@ -29,6 +31,10 @@
 //     partial per query head and bumps a per-(batch, kv head) arrival counter.  The last
 //     workgroup to arrive merges the partials, applies the inverse rotation and writes the
 //     output and log-sum-exp, then clears the counter for the next call.
+//   * Sparse V first pass (SPARSE): no value loads or products.  Each wave keeps an exact
+//     running maximum per head and writes every token whose score reaches it + log2(tau)
+//     as a candidate record of the second pass's split; the split's (m, l) become partials
+//     for the second pass and the merge (separate kernels).
 #include "tq_common.h"
 #include "tq_launch.h"
 
