@@ -38,9 +38,12 @@ __device__ __forceinline__ float quad_swap(float x) {
 // the upper), one DPP multiply-add each.  The upper lane thereby holds own - partner, the
 // negative of its butterfly output, so the lane ends with (-1)^popcount(q) times the
 // transform: quad_fwht_sign(q) gives that factor, which the caller folds into its scale.
+// FIRST = 2 skips the in-lane stage of distance 1, for a caller that has done it already
+// (the stages commute).
+template <int FIRST = 1>
 __device__ __forceinline__ void quad_fwht(float v[32], int q) {
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
+  for (int h = FIRST; h < 32; h <<= 1) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       if ((e & h) == 0) {
@@ -397,37 +400,40 @@ constexpr int kChunksPerBlock = 4;  // chunks one block quantizes, reusing the s
 
 // Loads the lane's 32 coordinates with the rotation signs applied: the sign masks m (0 or the
 // sign bit) are folded into the conversion, (w << 16) + m and (w & 0xffff0000) ^ m for bf16.
-template <int DTYPE>
-__device__ __forceinline__ void load32_signed(const void *x, size_t base, const uint32_t (&m)[32], float v[32]) {
-  if (DTYPE == TQ_F32) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + base);
+// 32 fp32 coordinates with the sign bits of s applied (XOR masks m).
+__device__ __forceinline__ void load32_f32_signed(const float *x, const uint32_t (&m)[32], float v[32]) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(x);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint4 f = p[r];
-      v[4 * r] = __uint_as_float(f.x ^ m[4 * r]);
-      v[4 * r + 1] = __uint_as_float(f.y ^ m[4 * r + 1]);
-      v[4 * r + 2] = __uint_as_float(f.z ^ m[4 * r + 2]);
-      v[4 * r + 3] = __uint_as_float(f.w ^ m[4 * r + 3]);
-    }
-  } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + base);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint4 w = p[r];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * r + 2 * e;
-        if (DTYPE == TQ_BF16) {
-          v[i] = __uint_as_float((ws[e] << 16) + m[i]);  // + flips bit 31 only: low bits are 0
-          v[i + 1] = __uint_as_float((ws[e] & 0xffff0000u) ^ m[i + 1]);
-        } else {
-          v[i] = __uint_as_float(__float_as_uint(half_bits_to_float((uint16_t)(ws[e] & 0xffffu))) ^ m[i]);
-          v[i + 1] = __uint_as_float(__float_as_uint(half_bits_to_float((uint16_t)(ws[e] >> 16))) ^ m[i + 1]);
-        }
-      }
-    }
+  for (int r = 0; r < 8; ++r) {
+    const uint4 f = p[r];
+    v[4 * r] = __uint_as_float(f.x ^ m[4 * r]);
+    v[4 * r + 1] = __uint_as_float(f.y ^ m[4 * r + 1]);
+    v[4 * r + 2] = __uint_as_float(f.z ^ m[4 * r + 2]);
+    v[4 * r + 3] = __uint_as_float(f.w ^ m[4 * r + 3]);
   }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c for two 16-bit values per word (bf16 or fp16), fp32 result:
+// the products are exact, so with b = {+-1, +-1} this is a signed sum of two inputs rounded
+// once, and with b = a a sum of squares.
+template <int DTYPE>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (DTYPE == TQ_BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+// The same with c = 0, as the three-operand instruction with an inline zero: the builtin
+// above becomes the accumulating two-operand form plus a move of 0 for every call.
+template <int DTYPE>
+__device__ __forceinline__ float dot2_0(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (DTYPE == TQ_BF16) asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  else asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Up to kChunksPerBlock 64-token chunks (block bx takes chunks kChunksPerBlock * bx .. counted
@@ -457,7 +463,11 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
 
   float pos[L / 2 > 1 ? L / 2 - 1 : 1];
   const CodeGrid gd = setup_code_search<BITS>(c, sh, wave, lane, pos);
-  uint32_t smask[32];  // sign bit of s_(32q + e), bit 7 of its byte
+  // Signs s_(32q + e) of this lane's coordinates.  fp32 input: sign-bit XOR masks.  16-bit
+  // input: the load does the first butterfly stage as two dot products of each input word
+  // (coordinates 2e, 2e+1) with the +-1 pairs {s_2e, s_2e+1} and {s_2e, -s_2e+1} written in
+  // the input's format.
+  uint32_t smask[32], spair[16], sdiff[16];
   {
     const int4 sw0 = *reinterpret_cast<const int4 *>(c.signs + 32 * q);
     const int4 sw1 = *reinterpret_cast<const int4 *>(c.signs + 32 * q + 16);
@@ -465,6 +475,12 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
                             (uint32_t)sw1.x, (uint32_t)sw1.y, (uint32_t)sw1.z, (uint32_t)sw1.w};
 #pragma unroll
     for (int e = 0; e < 32; ++e) smask[e] = (sw[e >> 2] << (24 - 8 * (e & 3))) & 0x80000000u;
+    const uint32_t one = DTYPE == TQ_BF16 ? 0x3F80u : 0x3C00u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      spair[e] = (one | (smask[2 * e] >> 16)) | ((one << 16) | smask[2 * e + 1]);
+      sdiff[e] = spair[e] ^ 0x80000000u;
+    }
   }
   uint8_t *plane = c.plane(b, h);
 
@@ -477,19 +493,45 @@ __device__ __forceinline__ void quantize_chunk(const CacheView &c, const void *_
     const bool valid = t >= lo && t < hi;
 
     float v[32];
-    if (valid) {
-      const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
-      load32_signed<DTYPE>(x, row * kD + 32 * q, smask, v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) v[e] = 0.f;
-    }
     float ss = 0.f;
+    if constexpr (DTYPE == TQ_F32) {
+      if (valid) {
+        const size_t row = ((size_t)b * n_tokens + (t - start_pos)) * c.n_kv_heads + h;
+        load32_f32_signed(reinterpret_cast<const float *>(x) + row * kD + 32 * q, smask, v);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
+        for (int e = 0; e < 32; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
+      quad_fwht(v, q);
+    } else {
+      // Buffer loads over the rows of tokens lo .. hi-1: a lane of a token outside that range
+      // reads past the end and gets zeros, so no branch and no clearing.  The range is at
+      // most 64 rows of n_kv_heads * 256 bytes (n_kv_heads < 65536, the grid's y limit).
+      // (Prefetching the next chunk's words into registers cost a wave per SIMD and was
+      // slower.)
+      const uint32_t row_bytes = (uint32_t)c.n_kv_heads * (kD * 2);
+      const uint32_t range = (uint32_t)(hi - lo) * row_bytes;
+      const size_t row_lo = ((size_t)b * n_tokens + (lo - start_pos)) * c.n_kv_heads + h;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(reinterpret_cast<const uint16_t *>(x) + row_lo * kD), (short)0, (int)range, 0x00020000);
+      const uint32_t off = valid ? (uint32_t)(t - lo) * row_bytes + 64u * q : range;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * r, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = 4 * r + k;
+          v[2 * e] = dot2_0<DTYPE>(w[k], spair[e]);
+          v[2 * e + 1] = dot2_0<DTYPE>(w[k], sdiff[e]);
+          ss = dot2<DTYPE>(w[k], w[k], ss);
+        }
+      }
+      quad_fwht<2>(v, q);
+    }
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
-    quad_fwht(v, q);
     const float n = sqrtf(ss);
     const float inv = (n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f) * quad_fwht_sign(q);
     uint32_t code[32];

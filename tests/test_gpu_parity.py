@@ -137,6 +137,30 @@ def test_quantize_special_vectors(signs, golden_codebooks):
         assert np.array_equal(norms[:60], 1.0 + np.arange(60))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_quantize_tiny_and_wide_range_inputs(dtype, signs, golden_codebooks):
+    """16-bit inputs whose entries span many orders of magnitude: fp16 vectors with half of
+    the entries in the subnormal range (below 6.1e-5), fp16 vectors that are subnormal
+    throughout, and bf16 vectors with entries from 1e-30 to 1e3.  Every input value must
+    reach the rotation unchanged (no flushing of subnormal inputs)."""
+    _say("tiny inputs", dtype)
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((2, 128, 3, 128), generator=g, dtype=torch.float64)
+    if dtype == "f16":
+        x[:, :64, :, 64:] *= 3e-6            # subnormal halves next to normal values
+        x[:, 64:96] *= 2e-6                  # subnormal throughout
+        x[:, 96:] *= 1e-4 * torch.rand((2, 32, 3, 128), generator=g, dtype=torch.float64)
+        tx = x.to(torch.float16)
+    else:
+        e = torch.randint(-30, 4, (2, 128, 3, 128), generator=g).to(torch.float64)
+        tx = (x * torch.pow(10.0, e)).to(torch.bfloat16)
+    for bits, layout in ((4, 0), (3, 1), (2, 0), (8, 1)):
+        cache = _new_cache(2, 3, 128, bits, layout, signs)
+        _fill(cache, tx.to(DEV))
+        s64 = signs.numpy().astype(np.float64)
+        parity.check_quantize(cache, parity.to_f64(tx), 0, s64, _table(golden_codebooks, bits))
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_dequantize_matches_oracle(layout, signs, golden_codebooks):
     _say("dequantize", layout)
