@@ -361,6 +361,43 @@ def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 
     return out, lse, scores
 
 
+def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None):
+    """Attention of n_q new query positions per sequence over a dequantized cache that
+    already holds them (speculative verify, chunked prefill): the step after single-query
+    decode, scored against the same quantized keys ([google], the scoring kernel;
+    [inferrs] on prefill speed).
+
+    q: [B, n_q, Hq, d]; k_hat, v_hat: [B, Hkv, T, d]; query head h reads kv head
+    h // (Hq // Hkv).  With T_b cached tokens of sequence b, query i sits at position
+    T_b - n_q + i and attends causally to positions 0 .. T_b - n_q + i:
+      s_t = scale * q . k_hat_t,  LSE = log sum_t exp(s_t),  o = sum_t exp(s_t - LSE) v_hat_t.
+    A query with no position to attend to (T_b - n_q + i < 0) gives o = 0, LSE = -inf.
+    Returns (out [B, n_q, Hq, d], lse [B, n_q, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kh = np.asarray(k_hat, dtype=np.float64)
+    vh = np.asarray(v_hat, dtype=np.float64)
+    bsz, n_q, hq, d = q.shape
+    hkv, t_max = kh.shape[1], kh.shape[2]
+    g = hq // hkv
+    out = np.zeros((bsz, n_q, hq, d))
+    lse = np.full((bsz, n_q, hq), -np.inf)
+    for b in range(bsz):
+        tb = t_max if seq_lens is None else int(seq_lens[b])
+        for i in range(n_q):
+            n_vis = tb - n_q + i + 1  # positions 0 .. tb - n_q + i
+            if n_vis <= 0:
+                continue
+            for h in range(hq):
+                j = h // g
+                s = scale * (kh[b, j, :n_vis] @ q[b, i, h])
+                m = s.max()
+                l_ = m + math.log(np.exp(s - m).sum())
+                out[b, i, h] = (np.exp(s - l_)[:, None] * vh[b, j, :n_vis]).sum(axis=0)
+                lse[b, i, h] = l_
+    return out, lse
+
+
 def sparse_v_borderline(scores, lse, tau: float, rel: float = 1e-3) -> np.ndarray:
     """Rows whose keep decision is within the score tolerance of the threshold.
 

@@ -325,6 +325,51 @@ def test_attention_special_cases(golden_codebooks):
     assert np.allclose(out_l[0], ref[0]) and np.all(np.isneginf(sc_l[0, :, 5:]))
 
 
+def test_multi_query_attention_pins(golden_codebooks):
+    """Multi-query attention: one query position equals single-query decode; query i equals
+    decode over the first T - n_q + i + 1 positions; later positions do not reach earlier
+    queries; and the whole thing matches torch's scaled-dot-product attention (fp64, CPU)
+    with an explicit causal mask."""
+    torch = pytest.importorskip("torch")
+    s, q1, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=41, golden=golden_codebooks)
+    scale = 1 / math.sqrt(D)
+    rng = np.random.default_rng(9)
+    n_q = 5
+    q = rng.standard_normal((2, n_q, 4, D))
+    # n_q = 1 is decode
+    one, lse1 = o.multi_query_attention(q1[:, None], kh, vh, scale)
+    dec, lsed, _ = o.decode_attention(q1, kh, vh, scale)
+    assert np.allclose(one[:, 0], dec, atol=1e-13) and np.allclose(lse1[:, 0], lsed, atol=1e-13)
+    # query i = decode over a prefix; per-sequence lengths, including one shorter than n_q
+    lens = np.array([41, 3])
+    out, lse = o.multi_query_attention(q, kh, vh, scale, seq_lens=lens)
+    for b in range(2):
+        for i in range(n_q):
+            n_vis = int(lens[b]) - n_q + i + 1
+            if n_vis <= 0:
+                assert np.all(out[b, i] == 0.0) and np.all(np.isneginf(lse[b, i]))
+                continue
+            ref, lref, _ = o.decode_attention(q[b:b + 1, i], kh[b:b + 1], vh[b:b + 1], scale,
+                                              seq_lens=np.array([n_vis]))
+            assert np.allclose(out[b, i], ref[0], atol=1e-13) and np.allclose(lse[b, i], lref[0])
+    # causality: changing positions after a query's last one leaves that query unchanged
+    kh2, vh2 = kh.copy(), vh.copy()
+    kh2[:, :, 41 - n_q + 2:] += 5.0
+    vh2[:, :, 41 - n_q + 2:] -= 3.0
+    out2, _ = o.multi_query_attention(q, kh2, vh2, scale)
+    out0, _ = o.multi_query_attention(q, kh, vh, scale)
+    assert np.allclose(out2[:, :2], out0[:, :2], atol=1e-13)
+    assert not np.allclose(out2[:, 2:], out0[:, 2:])
+    # torch SDPA with a boolean causal mask, query head h on kv head h // 2
+    tq_ = torch.from_numpy(q).permute(0, 2, 1, 3)                   # [B, Hq, n_q, d]
+    tk = torch.from_numpy(np.repeat(kh, 2, axis=1))                  # [B, Hq, T, d]
+    tv = torch.from_numpy(np.repeat(vh, 2, axis=1))
+    T = kh.shape[2]
+    mask = torch.arange(T)[None, :] <= (T - n_q + torch.arange(n_q))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq_, tk, tv, attn_mask=mask, scale=scale)
+    assert np.allclose(out0, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
 def test_sparse_v_limits_and_bound(golden_codebooks):
     s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=200, golden=golden_codebooks)
     q = q * 6.0     # sharpen the attention so some rows fall under the threshold
