@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama8k",
-                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k"])
+                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -154,6 +154,8 @@ def main():
 
     if args.workload == "prefill":
         result = bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log)
+    elif w.n_q > 1:
+        result = bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log)
     else:
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
     stream = stream_read_gbs(torch, tq, log)
@@ -351,6 +353,122 @@ def cpu_baseline_decode(w, tau, cache_pair, host_k, host_v, q, signs, np, torch,
             "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
                       f"{ctx} tokens: quantize+pack the appended token, unpack+dequantize+attend; "
                       f"{reps} repetitions"}
+
+
+def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
+    """Speculative verification: a step appends n_q tokens (K and V of every kv head) at the
+    end of each sequence and attends from those n_q positions, causally, over the cache."""
+    batch, hq, hkv, ctx, n_q = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.n_q
+    bk, bv = w.bits_k, w.bits_v
+    per_copy = tq.code_bytes(D, bk, batch, hkv, ctx) + tq.code_bytes(D, bv, batch, hkv, ctx) + 4 * batch * hkv * ctx
+    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    rows = n_q * w.group
+    vgroups = (rows + 7) // 8
+    log(f"[bench] workload={w.name} n_q={n_q} ({rows} query rows per kv head in {vgroups} groups) "
+        f"copies={copies} cache/copy={per_copy / 1e6:.1f} MB ({'eager launches' if args.eager else 'HIP graph replay'})")
+    g = inputs.generate(w, device=dev)
+    k_all, v_all, q = g["k"], g["v"], g["q"].contiguous()
+    caches = []
+    for c in range(copies):
+        kc = tq.PackedCache(batch, hkv, ctx, bk, tq.LAYOUT_ROWS, signs, device=dev)
+        vc = tq.PackedCache(batch, hkv, ctx, bv, tq.LAYOUT_GROUP8, signs, device=dev)
+        tq.quantize_append(kc, k_all[:, : ctx - n_q].contiguous(), 0)
+        tq.quantize_append(vc, v_all[:, : ctx - n_q].contiguous(), 0)
+        caches.append((kc, vc))
+    k_new = k_all[:, ctx - n_q:].contiguous()
+    v_new = v_all[:, ctx - n_q:].contiguous()
+    host_k = k_all[:1].cpu() if not args.no_cpu_baseline else None
+    host_v = v_all[:1].cpu() if not args.no_cpu_baseline else None
+    del k_all, v_all, g
+    bufs = tq.MultiQueryBuffers(batch, n_q, hq, hkv, ctx, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    for kc, vc in caches:
+        tq.quantize_append_kv(kc, vc, k_new, v_new, ctx - n_q)
+    torch.cuda.synchronize()
+
+    def append(i):
+        kc, vc = caches[i % copies]
+        tq.quantize_append_kv(kc, vc, k_new, v_new, ctx - n_q)
+
+    def attend(i):
+        kc, vc = caches[i % copies]
+        tq.decode_attn_multi(kc, vc, q, ctx, scale, buffers=bufs)
+
+    def step(i):
+        append(i)
+        attend(i)
+
+    timer = Timer(torch, args.eager)
+    steps = args.steps
+    ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
+    value = batch * ctx / (ms_per_step / 1e3)
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(attend, max(args.steps, 2 * copies), 2, batches=5)
+    ms_a = timer.per_iteration_ms(append, max(args.steps, 2 * copies), 2)
+    nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
+    achieved = nbytes / (ms_k / 1e3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, attention call {ms_k * 1e3:.1f} us "
+        f"({n_q} positions), append {n_q} tokens (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic")
+    result = {
+        "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16+f32",
+        "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D,
+                   "ctx": ctx, "bits_k": bk, "bits_v": bv, "n_q": n_q, "row_groups": vgroups,
+                   "step": f"append {n_q} tokens (K,V) + causal attention of the {n_q} positions",
+                   "cache_copies": copies, "timing": "eager" if args.eager else "hip graph replay"},
+        "attention_call_us": ms_k * 1e3,
+        "attention_call_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
+        "query_positions_per_s": batch * n_q / (ms_per_step / 1e3),
+        "append_kv_us": ms_a * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": DECODE_KERNEL,
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                     "note": f"algorithmic bytes read the cache once; the kernel reads it once per "
+                             f"group of up to 8 query rows ({vgroups} here)"},
+        "_kernel": "decode_multi",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_multi(w, caches[0], host_k, host_v, q, signs, np, torch, log)
+    return result
+
+
+def cpu_baseline_multi(w, cache_pair, host_k, host_v, q, signs, np, torch, log):
+    """The CPU oracle on a bounded sample: batch element 0, every kv head, the whole context:
+    quantize + pack the n_q appended tokens, then unpack, dequantize and attend causally."""
+    from oracle import tq_oracle as o
+
+    kc, vc = cache_pair
+    ctx, hkv, g, n_q = w.ctx, w.n_kv_heads, w.group, w.n_q
+    s64 = signs.cpu().numpy().astype(np.float64)
+    tabk = o.make_codebook(D, w.bits_k)[:2]
+    tabv = o.make_codebook(D, w.bits_v)[:2]
+    raw_k = [kc.plane_codes(0, h).cpu().numpy() for h in range(hkv)]
+    raw_v = [vc.plane_codes(0, h).cpu().numpy() for h in range(hkv)]
+    nk = [kc.plane_norms(0, h).cpu().numpy() for h in range(hkv)]
+    nv = [vc.plane_norms(0, h).cpu().numpy() for h in range(hkv)]
+    q64 = q[:1].double().cpu().numpy()
+    xk = host_k[0, ctx - n_q:].double().numpy()
+    xv = host_v[0, ctx - n_q:].double().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.quantize(xk, s64, *tabk)
+        o.quantize(xv, s64, *tabv)
+        kh = np.stack([o.dequantize(o.unpack(raw_k[h], ctx, D, w.bits_k, 0), nk[h], s64, tabk[0])
+                       for h in range(hkv)])[None]
+        vh = np.stack([o.dequantize(o.unpack(raw_v[h], ctx, D, w.bits_v, 1), nv[h], s64, tabv[0])
+                       for h in range(hkv)])[None]
+        o.multi_query_attention(q64, kh, vh, 1.0 / math.sqrt(D))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    value = reps * ctx / el
+    log(f"[bench] cpu oracle: {reps} sample steps in {el:.1f} s")
+    return {"value": value, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
+                      f"{ctx} tokens, {n_q} query positions: quantize+pack the appended tokens, "
+                      f"unpack+dequantize+attend; {reps} repetitions"}
 
 
 def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):

@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
                                      i32, vp, i32, f32, f32, vp, vp, vp, vp, sz, vp]
         L.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
         L.tq_decode_workspace_bytes.restype = sz
+        L.tq_decode_attn_multi.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, i32,
+                                           i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.tq_decode_attn_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.tq_decode_attn_multi_workspace_bytes.restype = sz
         L.tq_dequantize.argtypes = [ctypes.POINTER(CacheStruct), i32, i32, vp, i32, vp]
         L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.tq_code_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -64,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_dequantize", "tq_probe_stream_read"):
+                     "tq_decode_attn_multi", "tq_dequantize", "tq_probe_stream_read"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -237,4 +241,43 @@ def decode_attn(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: int, sca
         _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         _dev(buffers.scores, "scores") if buffers.scores is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn")
+    return buffers
+
+
+def decode_attn_multi_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, n_q: int, ctx_len: int) -> int:
+    return int(lib().tq_decode_attn_multi_workspace_bytes(batch, n_q_heads, n_kv_heads, n_q, ctx_len))
+
+
+class MultiQueryBuffers:
+    """Caller-owned outputs and workspace of one multi-query problem shape."""
+
+    def __init__(self, batch, n_q, n_q_heads, n_kv_heads, ctx_len, device="cuda", d=D, want_lse=True):
+        torch = _torch()
+        self.out = torch.empty((batch, n_q, n_q_heads, d), dtype=torch.float32, device=device)
+        self.lse = (torch.empty((batch, n_q, n_q_heads), dtype=torch.float32, device=device)
+                    if want_lse else None)
+        nbytes = decode_attn_multi_workspace_bytes(batch, n_q_heads, n_kv_heads, n_q, ctx_len)
+        if nbytes == 0:
+            raise TQError(TQ_ERR_INVALID_ARG, "tq_decode_attn_multi_workspace_bytes")
+        # zero once: the arrival counters live here and every call leaves them at zero
+        self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.ws_bytes = nbytes
+
+
+def decode_attn_multi(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: int, scale: float,
+                      seq_lens=None, buffers: MultiQueryBuffers | None = None, stream=None):
+    """Attention of the last n_q positions of each sequence (q [B, n_q, Hq, d]) over the packed
+    cache, causal; returns the MultiQueryBuffers holding out [B, n_q, Hq, d] and lse."""
+    bsz, n_q, hq, d = q.shape
+    if buffers is None:
+        buffers = MultiQueryBuffers(bsz, n_q, hq, k_cache.n_kv_heads, ctx_len, device=q.device, d=d)
+    ks, vs = k_cache.struct(), v_cache.struct()
+    sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
+    _check(lib().tq_decode_attn_multi(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, n_q, sl, ctx_len,
+        float(scale), _dev(buffers.out, "out"),
+        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_multi")
     return buffers

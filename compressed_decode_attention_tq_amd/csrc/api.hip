@@ -128,6 +128,29 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
   return w;
 }
 
+MultiQueryShape multi_query_shape(int group, int n_q) {
+  const long rows = (long)group * n_q;
+  const int vgroups = (int)((rows + 7) / 8);
+  return MultiQueryShape{vgroups, (int)((rows + vgroups - 1) / vgroups)};
+}
+
+WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len) {
+  const MultiQueryShape m = multi_query_shape(n_q_heads / n_kv_heads, n_q);
+  const SplitPlan fp = plan_fused(batch, n_kv_heads * m.vgroups, ctx_len);
+  const size_t rows = (size_t)batch * n_q * n_q_heads * fp.n_splits;
+  WorkspaceLayout w{};
+  size_t off = 0;
+  w.counters = off;
+  off = align_up(off + (size_t)batch * n_kv_heads * m.vgroups * sizeof(unsigned), 256);
+  w.fpart_ml = off;
+  off = align_up(off + rows * sizeof(float2), 256);
+  w.fpart_o = off;
+  off = align_up(off + rows * kD * sizeof(float), 256);
+  w.part_ml = w.part_o = w.cand_count = w.cand = off;
+  w.total = off;
+  return w;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -149,6 +172,14 @@ const char *tq_status_string(int status) {
 size_t tq_code_bytes(int d, int bits, int batch, int n_kv_heads, int capacity) {
   if (d < 1 || batch < 1 || n_kv_heads < 1 || capacity < 1 || bits < 1 || bits > 8) return 0;
   return (size_t)batch * n_kv_heads * capacity * (size_t)d * bits / 8;
+}
+
+size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q,
+                                            int ctx_len) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads != 0 ||
+      n_q < 1 || n_q > kMaxQueryPositions || ctx_len < 0)
+    return 0;
+  return workspace_layout_multi(batch, n_q_heads, n_kv_heads, n_q, ctx_len).total;
 }
 
 size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
@@ -244,6 +275,9 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.scale = scale;
   a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
   a.sparse = sparse ? 1 : 0;
+  a.n_q = 1;
+  a.vgroups = 1;
+  a.vg_size = group;
   a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
   a.fplan = sparse ? plan_fused_sparse(k->batch, k->n_kv_heads, ctx_len, a.plan)
                    : plan_fused(k->batch, k->n_kv_heads, ctx_len);
@@ -259,6 +293,59 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
   a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
   return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, int n_q, const int32_t *seq_lens, int ctx_len, float scale,
+                         float *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *hip_stream) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
+      k->signs != v->signs)
+    return TQ_ERR_INVALID_ARG;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  if (n_q < 1 || n_q > kMaxQueryPositions) return TQ_ERR_INVALID_ARG;
+  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
+  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / k->n_kv_heads;
+  const WorkspaceLayout w = workspace_layout_multi(k->batch, n_q_heads, k->n_kv_heads, n_q, ctx_len);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+
+  const MultiQueryShape m = multi_query_shape(group, n_q);
+  DecodeArgs a{};
+  a.k = view_of(k);
+  a.v = view_of(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = ctx_len;
+  a.scale = scale;
+  a.n_q = n_q;
+  a.vgroups = m.vgroups;
+  a.vg_size = m.vg_size;
+  a.fplan = plan_fused(k->batch, k->n_kv_heads * m.vgroups, ctx_len);
+  a.out = out;
+  a.lse = lse;
+  char *ws = static_cast<char *>(workspace);
+  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
+  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
+  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
+  if (!decode_fused_supported(a)) return TQ_ERR_UNSUPPORTED;
+  return hip_status(launch_decode_fused(a, compute_units(), static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

@@ -180,6 +180,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const int g = a.group, S = a.fplan.n_splits, L = a.fplan.split_len;
+  const int n_q = a.n_q, VG = a.vgroups, vgs = a.vg_size;
   const int m_row = lane & 15, quarter = lane >> 4;
   const int pr = lane & 31, half_id = lane >> 5;  // softmax mapping: tokens 2pr, 2pr+1
   const uint32_t kc8 = (uint32_t)(lane & 31) << 3;
@@ -193,13 +194,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   {  // one split of one (batch, kv head) per workgroup
     const int item = blockIdx.x;
     const int split = item % S;
-    const int kvh = (item / S) % a.n_kv_heads;
-    const int b = item / (S * a.n_kv_heads);
+    const int vgi = (item / S) % VG;
+    const int kvh = (item / (S * VG)) % a.n_kv_heads;
+    const int b = item / (S * VG * a.n_kv_heads);
     int T = a.ctx_len;
     if (a.seq_lens != nullptr) T = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.ctx_len));
     const int t_begin = split * L;
     const int t_end = min(t_begin + L, T);
     const int qh0 = kvh * g;  // first query head of the group
+    // Query rows ("heads" of this item): row h is query position f / g, head kvh*g + f % g,
+    // f = vgi * vgs + h; it sees cache positions up to T - n_q + f / g.  For decode (n_q = 1,
+    // one item per kv head) row h is simply head qh0 + h.
+    auto vlive = [&](int h) { return h < vgs && vgi * vgs + h < n_q * g; };
+    auto vrow = [&](int h) -> size_t {  // row of q, out and lse: [batch][n_q][n_q_heads]
+      const int f = vgi * vgs + h, i = f / g;
+      return ((size_t)b * n_q + i) * a.n_q_heads + kvh * g + (f - i * g);
+    };
 
     const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
     const uint32_t span_tok = (uint32_t)n_tiles * kTile;
@@ -237,8 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     for (int i = 0; i < (1 << BK); ++i) kcs[i] = a.k.centroids[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vcs[i] = a.v.centroids[i];
-    const int qhead = qh0 + min(wave, g - 1);
-    const size_t qbase = ((size_t)b * a.n_q_heads + qhead) * kD + 2 * lane;
+    const size_t qbase = vrow(vlive(wave) ? wave : 0) * kD + 2 * lane;
     uint32_t qw0 = 0u, qw1 = 0u;
     if (a.q_dtype == TQ_F32) {
       const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(a.q) + qbase);
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // ---- rotated query group: wave h rotates head h into qrot[h]
     if (wave < NH) {
       float x0 = 0.f, x1 = 0.f;
-      if (wave < g) {
+      if (vlive(wave)) {
         if (a.q_dtype == TQ_F32) {
           x0 = __uint_as_float(qw0);
           x1 = __uint_as_float(qw1);
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     {
       const int head = m_row >> 1;
       const bool lo_row = (m_row & 1) != 0;
-      const bool live = head < NH && head < g;
+      const bool live = head < NH && vlive(head);
       float v[32];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -310,6 +319,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       }
     }
     __syncthreads();  // qrot (wave buffers 0..1) is free for staging from here
+
+    // last visible position of this lane's rows (they differ only with several query
+    // positions; -1 for a row without a query)
+    int vlim[NH2];
+#pragma unroll
+    for (int hh = 0; hh < NH2; ++hh) {
+      const int h = half_id * NH2 + hh;
+      vlim[hh] = vlive(h) ? T - n_q + (vgi * vgs + h) / g : -1;
+    }
 
     // ---- per-lane softmax state: heads half_id*NH2 + hh
     float mr[NH2], lsum[NH2];
@@ -423,6 +441,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
             for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] = -INFINITY;
           }
       }
+      // Rows of later query positions see more of the tile (uniform branch).  A row can then
+      // have no visible token here while its reference is still -inf, where the plain
+      // exponent below would give exp2(-inf - -inf): such tiles take the reference-move
+      // path, whose exponents treat -inf explicitly.
+      bool causal_tile = false;
+      if (n_q > 1 && t0 + kTile > T - n_q + 1) {
+        causal_tile = true;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int hh = 0; hh < NH2; ++hh)
+            if (t0 + 2 * pr + tb > vlim[hh]) sc[tb][hh] = -INFINITY;
+      }
       if constexpr (SPARSE) {
         // exact running maximum of the wave per head, sum relative to it; a token is a
         // candidate when some head's score reaches that maximum + log2(tau).  The maximum
@@ -495,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           p[tb][hh] = __builtin_amdgcn_exp2f(sc[tb][hh] - mr[hh]);
           vmax = fmaxf(vmax, p[tb][hh] * nv[tb]);
         }
-      if (__any(!(vmax <= kAMax))) {
+      if (causal_tile || __any(!(vmax <= kAMax))) {
         // move each head's reference to the tile's largest s + log2||v||, rescale
         float alpha[NH2];
 #pragma unroll
@@ -630,8 +661,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     if constexpr (SPARSE) {
       // the split's (m, l) per query head in natural-log units, and the candidate counts;
       // the value pass and the merge are separate kernels
-      if (wave < NH && wave < g && lane == 0)
-        a.fpart_ml[((size_t)b * a.n_q_heads + qh0 + wave) * S + split] =
+      if (wave < NH && vlive(wave) && lane == 0)
+        a.fpart_ml[vrow(wave) * S + split] =
             make_float2(Mh == -INFINITY ? -INFINITY : Mh * kLn2, Lh);
       for (int i = threadIdx.x; i < n_chunks; i += blockDim.x)
         if (c_first + i < a.plan.n_splits)
@@ -654,8 +685,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
                                                           (oacc[6][2] + oacc[6][3]) * f1, (oacc[7][2] + oacc[7][3]) * f1);
     }
     __syncthreads();
-    const size_t part_row = ((size_t)b * a.n_q_heads + qh0 + wave) * S;  // valid for wave < g
-    if (wave < NH && wave < g) {
+    const bool live_w = wave < NH && vlive(wave);
+    const size_t part_row = vrow(live_w ? wave : 0) * S;  // valid for live_w
+    if (live_w) {
       float2 o = make_float2(0.f, 0.f);
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -672,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     int *flag = reinterpret_cast<int *>(lds + kWBase);
-    unsigned *counter = a.counters + (size_t)b * a.n_kv_heads + kvh;
+    unsigned *counter = a.counters + ((size_t)b * a.n_kv_heads + kvh) * VG + vgi;
     if (threadIdx.x == 0) {
       const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *flag = old == (unsigned)(S - 1) ? 1 : 0;
@@ -680,7 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     __syncthreads();
     const bool last = *flag != 0;
     if (last) {
-      if (wave < NH && wave < g) {
+      if (live_w) {
         // lane s of a chunk holds partial s's (m, l); every lane then sums its two
         // coordinates over the partials, 16 loads in flight at a time
         const float2 *pml = a.fpart_ml + part_row;
@@ -725,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         y1 *= kInvSqrtD;
         if (a.k.signs[2 * lane] < 0) y0 = -y0;
         if (a.k.signs[2 * lane + 1] < 0) y1 = -y1;
-        const size_t orow = (size_t)b * a.n_q_heads + qh0 + wave;
+        const size_t orow = vrow(wave);
         *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
         if (lane == 0 && a.lse != nullptr) a.lse[orow] = M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
         if (a.scores != nullptr) {
@@ -740,7 +772,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 
 template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.group <= 4) decode_fused_kernel<BK, 4, SPARSE><<<grid, kThreads, 0, stream>>>(a);
+  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE><<<grid, kThreads, 0, stream>>>(a);
   else decode_fused_kernel<BK, 8, SPARSE><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -748,21 +780,21 @@ hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
 }  // namespace
 
 bool decode_fused_supported(const DecodeArgs &a) {
-  return !a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.group <= 8 &&
+  return !a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.vg_size <= 8 && a.vg_size >= 1 &&
          a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
          a.fplan.split_len % kTile == 0 && a.counters != nullptr;
 }
 
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream) {
   (void)n_cu;
-  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  const long items = (long)a.batch * a.n_kv_heads * a.vgroups * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   const int grid = (int)items;
   return a.k.bits == 4 ? launch_bk<4, false>(a, grid, stream) : launch_bk<3, false>(a, grid, stream);
 }
 
 bool decode_fused_sparse_supported(const DecodeArgs &a) {
-  return a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.group <= 8 &&
+  return a.sparse && a.n_q == 1 && a.vgroups == 1 && (a.k.bits == 3 || a.k.bits == 4) && a.group <= 8 &&
          a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
          a.plan.split_len % kTile == 0 && a.fplan.split_len % a.plan.split_len == 0 &&
          a.fplan.split_len / a.plan.split_len <= kMaxChunksPerSplit;

@@ -23,6 +23,7 @@ SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len);
 // second pass's splits `p`, about as long as the dense plan's.
 SplitPlan plan_fused_sparse(int batch, int n_kv_heads, int ctx_len, const SplitPlan &p);
 constexpr int kMaxChunksPerSplit = 64;
+constexpr int kMaxQueryPositions = 4096;  // query positions of one multi-query call
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WorkspaceLayout {
@@ -38,6 +39,13 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  bool sparse);
+// Multi-query attention (n_q query positions): the single-launch kernel's counters and
+// partials only.
+struct MultiQueryShape {
+  int vgroups, vg_size;
+};
+MultiQueryShape multi_query_shape(int group, int n_q);
+WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len);
 
 struct DecodeArgs {
   CacheView k, v;
@@ -66,6 +74,9 @@ struct DecodeArgs {
   // fused first pass fpart_ml (fplan splits).
   const float2 *lse_ml;
   int lse_splits;
+  // Query rows of the single-launch kernel: n_q query positions per sequence (1 for decode)
+  // give n_q * group rows per kv head, taken vg_size at a time by `vgroups` work items.
+  int n_q, vgroups, vg_size;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
@@ -76,6 +87,7 @@ hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batc
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+int compute_units();
 bool decode_mfma_supported(const DecodeArgs &a);
 bool decode_fused_supported(const DecodeArgs &a);
 bool decode_fused_sparse_supported(const DecodeArgs &a);

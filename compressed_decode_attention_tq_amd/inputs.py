@@ -62,6 +62,7 @@ class Workload:
     boundary_layers: tuple = ()
     boundary_bits: int = 8
     append: int = 0                            # tokens appended after the prefill
+    n_q: int = 1                               # query positions per sequence (multi-query)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -80,6 +81,9 @@ WORKLOADS = {
                         layers=32, layer_std=(0.5, 3.0), boundary_layers=(0, 1, 30, 31)),
     "ctx131k": Workload("ctx131k", 5, 4, 16, 2, 131072, 4, 2, torch.bfloat16, "normal",
                         tau=1e-4, sink_fraction=0.02, sink_scale=8.0),
+    # speculative verification on the Llama-3-8B-shaped layer: 4 new positions per step
+    "verify8k": Workload("verify8k", 6, 1, 32, 8, 8192, 4, 2, torch.bfloat16, "normal",
+                         head_channel_scales=(0.5, 20.0), append=4, n_q=4),
 }
 
 
@@ -98,8 +102,9 @@ def _draw(dist: str, shape, g: torch.Generator, device) -> torch.Tensor:
 
 
 def generate(w: Workload, device="cpu", batch=None, ctx=None, n_kv_heads=None,
-             n_q_heads=None, layer: int = 0, with_query: bool = True) -> dict:
-    """Draw K, V [batch, ctx, n_kv_heads, d] and q [batch, n_q_heads, d] for one layer.
+             n_q_heads=None, layer: int = 0, with_query: bool = True, n_q=None) -> dict:
+    """Draw K, V [batch, ctx, n_kv_heads, d] and q [batch, n_q_heads, d] for one layer
+    (q [batch, n_q, n_q_heads, d] for a workload or call with n_q > 1).
 
     Shapes default to the workload's; smaller shapes keep the same recipe.
     Draw order: special channels / positions, K, V, scales, q.  Values are
@@ -143,8 +148,10 @@ def generate(w: Workload, device="cpu", batch=None, ctx=None, n_kv_heads=None,
             k[b, sinks[b]] *= w.sink_scale
             v[b, sinks[b]] *= w.sink_scale
     out = {"k": k.to(w.dtype), "v": v.to(w.dtype), "info": info}
+    n_q = w.n_q if n_q is None else n_q
     if with_query:
-        out["q"] = torch.randn((batch, hq, D), generator=g, device=device).to(w.dtype)
+        shape = (batch, hq, D) if n_q == 1 else (batch, n_q, hq, D)
+        out["q"] = torch.randn(shape, generator=g, device=device).to(w.dtype)
     return out
 
 

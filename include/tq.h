@@ -170,6 +170,34 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
 size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  float sparse_v_tau);
 
+/* Attention of n_q new query positions per sequence against the packed cache, which already
+ * holds them (speculative verification of draft tokens, chunked prefill): the same scores,
+ * softmax and rotated-domain value sum as tq_decode_attn ([google] score kernel; [inferrs]
+ * on prefill speed), causal over positions.  With T = seq_lens ? clamp(seq_lens[b], 0,
+ * ctx_len) : ctx_len cached tokens, query i (0 <= i < n_q) of sequence b sits at position
+ * T - n_q + i and attends to positions 0 .. T - n_q + i; a query with no such position gets
+ * o = 0 and LSE = -inf.  Dense only (no Sparse V), no score output.
+ *   k, v       as for tq_decode_attn; keys of 3 or 4 bits and values of 2 bits
+ *              (TQ_ERR_UNSUPPORTED otherwise)
+ *   q          device in [batch][n_q][n_q_heads][d] of q_dtype, 16-byte aligned
+ *   n_q        1 <= n_q <= 4096 (n_q = 1 is tq_decode_attn with sparse_v_tau = 0)
+ *   out        device out [batch][n_q][n_q_heads][d] fp32, 16-byte aligned
+ *   lse        device out [batch][n_q][n_q_heads] fp32 or NULL
+ *   workspace  device scratch of at least tq_decode_attn_multi_workspace_bytes(...) bytes,
+ *              256-byte aligned, zero-filled once before first use (arrival counters that
+ *              every completed call returns to zero); calls sharing it must not overlap.
+ * The n_q * (n_q_heads / n_kv_heads) query rows of a kv head are processed up to 8 at a
+ * time, each group of rows reading the kv head's cache once.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, int n_q, const int32_t *seq_lens, int ctx_len, float scale,
+                         float *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *hip_stream);
+
+/* Workspace bytes tq_decode_attn_multi needs for this problem (0 for invalid arguments). */
+size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q,
+                                            int ctx_len);
+
 /* Reconstruct x_hat = ||x||_fp16 * R^T c[idx] for cache positions
  * [start_pos, start_pos + n_tokens) ([google] unpack kernel; [tq-fwht] §2 invertibility).
  *   out  device out [batch][n_tokens][n_kv_heads][d] of out_dtype, 16-byte aligned

@@ -154,6 +154,37 @@ def test_decode_argument_validation():
     assert _decode(k, v, seq=FAKE + 0x900002) == tq.TQ_ERR_INVALID_ARG
 
 
+def _multi(k, v, q=FAKE + 0x600000, hq=8, n_q=4, seq=None, ctx=512, scale=0.088,
+           out=FAKE + 0x700000, ws=FAKE + 0x800000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = tq.lib().tq_decode_attn_multi_workspace_bytes(k.batch, hq, k.n_kv_heads, max(n_q, 1),
+                                                                 max(ctx, 0)) or 1
+    return tq.lib().tq_decode_attn_multi(ctypes.byref(k), ctypes.byref(v), q, 1, hq, n_q, seq, ctx, scale,
+                                         out, None, ws, ws_bytes, None)
+
+
+def test_multi_query_argument_validation():
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+    wsb = tq.lib().tq_decode_attn_multi_workspace_bytes
+    assert wsb(1, 8, 2, 4, 512) > 0
+    assert wsb(1, 8, 2, 8, 512) > wsb(1, 8, 2, 4, 512)      # more query rows, more partials
+    assert wsb(1, 8, 2, 0, 512) == 0 and wsb(1, 8, 2, 4097, 512) == 0 and wsb(1, 7, 2, 4, 512) == 0
+    assert _multi(k, v, n_q=0) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, n_q=4097) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, ctx=2048) == tq.TQ_ERR_CAPACITY
+    assert _multi(k, v, ctx=-1) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, scale=float("nan")) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    assert _multi(k, v, ws=FAKE + 0x800010) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, out=FAKE + 0x700004) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, v, q=0) == tq.TQ_ERR_INVALID_ARG
+    assert _multi(k, _cache(layout=0, bits=2)) == tq.TQ_ERR_UNSUPPORTED        # V must be GROUP8
+    assert _multi(_cache(layout=0, bits=8), v) == tq.TQ_ERR_UNSUPPORTED        # 8-bit keys: no kernel
+    assert _multi(k, _cache(layout=1, bits=3)) == tq.TQ_ERR_UNSUPPORTED        # 3-bit values: no kernel
+    assert _multi(k, _cache(layout=1, bits=2, n_kv_heads=1)) == tq.TQ_ERR_INVALID_ARG
+
+
 def test_probe_rejects_bad_arguments():
     f = tq.lib().tq_probe_stream_read
     assert f(None, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG

@@ -233,6 +233,63 @@ def test_decode_dense_matches_oracle(case, signs, golden_codebooks):
     _decode_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape)
 
 
+def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens=None, q_dtype=None):
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq, n_q=n_q)
+    kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
+    vc = _new_cache(batch, hkv, cap, 2, 1, signs)
+    _fill(kc, g["k"].to(DEV))
+    _fill(vc, g["v"].to(DEV))
+    q = g["q"] if n_q > 1 else g["q"][:, None]
+    q = q if q_dtype is None else q.to(q_dtype)
+    scale = 1.0 / math.sqrt(128)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    buf = tq.decode_attn_multi(kc, vc, q.to(DEV).contiguous(), ctx, scale, seq_lens=sl)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    kh = parity.oracle_cache_view(kc, s64, golden[bits_k], ctx)
+    vh = parity.oracle_cache_view(vc, s64, golden[2], ctx)
+    out, lse = o.multi_query_attention(parity.to_f64(q), kh, vh, scale, seq_lens=seq_lens)
+    got_lse = buf.lse.cpu().numpy()
+    fin = np.isfinite(lse)
+    assert np.all(np.isneginf(got_lse[~fin]))
+    assert np.allclose(got_lse[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    got = buf.out.cpu().numpy()
+    assert np.all(got[~fin] == 0.0)
+    worst = parity.check_rows(got[fin], out[fin], "multi-query out")
+    _say(f"  worst rel err {worst:.2e}")
+    return buf, out
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, n_q)
+    ("llama8k", 1, 32, 8, 700, 768, 4, 1),
+    ("llama8k", 1, 32, 8, 700, 768, 4, 2),
+    ("llama8k", 1, 32, 8, 700, 768, 4, 4),
+    ("llama8k", 2, 8, 2, 1000, 1024, 4, 7),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 3),
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 5),
+    ("llama8k", 1, 2, 2, 333, 384, 4, 8),
+    ("llama8k", 1, 4, 4, 200, 256, 3, 64),
+])
+def test_multi_query_matches_oracle(case, signs, golden_codebooks):
+    """Several query positions per sequence (speculative verification, chunked prefill):
+    causal attention of each position over the packed cache, rows taken up to 8 at a time."""
+    name, *shape = case
+    _say("multi-query", case)
+    _multi_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape)
+
+
+def test_multi_query_ragged_lengths_and_dtypes(signs, golden_codebooks):
+    """Per-sequence lengths, including one shorter than the number of query positions (its
+    first queries see nothing: o = 0, LSE = -inf) and an empty one; fp32 and fp16 queries."""
+    _say("multi-query ragged")
+    w = inputs.WORKLOADS["llama8k"]
+    _multi_case(w, signs, golden_codebooks, 3, 8, 2, 900, 960, 4, 6, seq_lens=[900, 3, 0])
+    _multi_case(w, signs, golden_codebooks, 2, 8, 2, 300, 320, 4, 3, seq_lens=[129, 300],
+                q_dtype=torch.float32)
+    _multi_case(w, signs, golden_codebooks, 1, 16, 2, 260, 320, 3, 2, q_dtype=torch.float16)
+
+
 def test_decode_seq_lens_and_query_dtypes(signs, golden_codebooks):
     _say("decode seq_lens")
     w = inputs.WORKLOADS["llama8k"]
