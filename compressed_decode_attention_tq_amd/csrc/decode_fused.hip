@@ -31,6 +31,9 @@
 //     partial per query head and bumps a per-(batch, kv head) arrival counter.  The last
 //     workgroup to arrive merges the partials, applies the inverse rotation and writes the
 //     output and log-sum-exp, then clears the counter for the next call.
+//   * Several query positions (speculative verification, a prefill chunk): the query rows
+//     are (position, head) pairs, up to 8 per work item, and each row sees the cache up to
+//     its own position (a mask in the tiles that reach past the first query's position).
 //   * Sparse V first pass (SPARSE): no value loads or products.  Each wave keeps an exact
 //     running maximum per head and writes every token whose score reaches it + log2(tau)
 //     as a candidate record of the second pass's split; the split's (m, l) become partials
