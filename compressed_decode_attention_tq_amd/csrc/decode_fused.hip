@@ -173,7 +173,9 @@ __device__ __forceinline__ float exp2_or_zero(float x, float ref) {
   return (x == -INFINITY || ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - ref);
 }
 
-template <int BK, int NH, bool SPARSE>
+// MULTI: several query positions (a.n_q > 1 or several row groups); a template flag so that
+// single-query decode keeps none of its bookkeeping live across the tile loop.
+template <int BK, int NH, bool SPARSE, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const int g = a.group, S = a.fplan.n_splits, L = a.fplan.split_len;
-  const int n_q = a.n_q, VG = a.vgroups, vgs = a.vg_size;
+  const int n_q = MULTI ? a.n_q : 1, VG = MULTI ? a.vgroups : 1, vgs = MULTI ? a.vg_size : g;
   const int m_row = lane & 15, quarter = lane >> 4;
   const int pr = lane & 31, half_id = lane >> 5;  // softmax mapping: tokens 2pr, 2pr+1
   const uint32_t kc8 = (uint32_t)(lane & 31) << 3;
@@ -208,8 +210,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // Query rows ("heads" of this item): row h is query position f / g, head kvh*g + f % g,
     // f = vgi * vgs + h; it sees cache positions up to T - n_q + f / g.  For decode (n_q = 1,
     // one item per kv head) row h is simply head qh0 + h.
-    auto vlive = [&](int h) { return h < vgs && vgi * vgs + h < n_q * g; };
+    auto vlive = [&](int h) { return MULTI ? h < vgs && vgi * vgs + h < n_q * g : h < g; };
     auto vrow = [&](int h) -> size_t {  // row of q, out and lse: [batch][n_q][n_q_heads]
+      if constexpr (!MULTI) return (size_t)b * a.n_q_heads + qh0 + h;
       const int f = vgi * vgs + h, i = f / g;
       return ((size_t)b * n_q + i) * a.n_q_heads + kvh * g + (f - i * g);
     };
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 #pragma unroll
     for (int hh = 0; hh < NH2; ++hh) {
       const int h = half_id * NH2 + hh;
-      vlim[hh] = vlive(h) ? T - n_q + (vgi * vgs + h) / g : -1;
+      vlim[hh] = MULTI && vlive(h) ? T - n_q + (vgi * vgs + h) / g : -1;
     }
 
     // ---- per-lane softmax state: heads half_id*NH2 + hh
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       // exponent below would give exp2(-inf - -inf): such tiles take the reference-move
       // path, whose exponents treat -inf explicitly.
       bool causal_tile = false;
-      if (n_q > 1 && t0 + kTile > T - n_q + 1) {
+      if (MULTI && t0 + kTile > T - n_q + 1) {
         causal_tile = true;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -773,11 +776,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
+template <int BK, bool SPARSE, bool MULTI>
+hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
+  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8, SPARSE, MULTI><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8, SPARSE><<<grid, kThreads, 0, stream>>>(a);
-  return hipGetLastError();
+  if (!SPARSE && (a.n_q > 1 || a.vgroups > 1)) return launch_nh<BK, false, true>(a, grid, stream);
+  return launch_nh<BK, SPARSE, false>(a, grid, stream);
 }
 
 }  // namespace
