@@ -173,9 +173,83 @@ __device__ __forceinline__ float exp2_or_zero(float x, float ref) {
   return (x == -INFINITY || ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - ref);
 }
 
+// Quantize the token at position t of (batch b, kv head kvh) into the key cache (key) or the
+// value cache: one wave, two coordinates per lane.  The same steps as the quantize kernels
+// ([tq-80] §核心创新: norm, rotation, Lloyd-Max code; [inferrs] §核心技术: Walsh-Hadamard
+// rotation): n = ||x|| (fp32, stored as fp16), u = H (s . x) / (sqrt(d) n) with the butterflies
+// across the wave, code = number of boundaries below u, then the bits of this token in the
+// cache's layout (3/4-bit key rows, 2-bit value groups of 8 tokens, whose other tokens are
+// kept).  `scratch` is 48 bytes of LDS for assembling a 3-bit row.
+template <int BK>
+__device__ void append_token(const DecodeArgs &a, bool key, int b, int kvh, int t, int lane, uint8_t *scratch) {
+  const CacheView &c = key ? a.k : a.v;
+  const void *x = key ? a.xk : a.xv;
+  const size_t xi = ((size_t)b * a.n_kv_heads + kvh) * kD + 2 * lane;
+  float x0, x1;
+  if (a.x_dtype == TQ_F32) {
+    const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(x) + xi);
+    x0 = f.x;
+    x1 = f.y;
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xi);
+    if (a.x_dtype == TQ_BF16) {
+      x0 = __uint_as_float(w << 16);
+      x1 = __uint_as_float(w & 0xffff0000u);
+    } else {
+      x0 = f16((uint16_t)(w & 0xffffu));
+      x1 = f16((uint16_t)(w >> 16));
+    }
+  }
+  float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+  const float n = sqrtf(ss);
+  const float y0 = c.signs[2 * lane] < 0 ? -x0 : x0, y1 = c.signs[2 * lane + 1] < 0 ? -x1 : x1;
+  float u0 = y0 + y1, u1 = y0 - y1;
+  wave_fwht_upper(u0, u1, lane);
+  const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
+  u0 *= inv;
+  u1 *= inv;
+  const int nb = key ? (1 << BK) - 1 : 3;
+  uint32_t c0 = 0u, c1 = 0u;
+  for (int j = 0; j < nb; ++j) {
+    const float tj = c.boundaries[j];
+    c0 += u0 > tj ? 1u : 0u;
+    c1 += u1 > tj ? 1u : 0u;
+  }
+  if (lane == 0) c.norm_plane(b, kvh)[t] = float_to_half_bits(n);
+  uint8_t *plane = c.plane(b, kvh);
+  if (key) {
+    if (BK == 4) {
+      plane[(size_t)t * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
+    } else {  // the 384-bit row, lane l's two codes at bit 6 l
+      uint32_t *words = reinterpret_cast<uint32_t *>(scratch);
+      if (lane < 12) words[lane] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      const uint32_t f = c0 | (c1 << 3);
+      const int bit = 6 * lane, wi = bit >> 5, sh = bit & 31;
+      atomicOr(&words[wi], f << sh);
+      if (sh > 26) atomicOr(&words[wi + 1], f >> (32 - sh));
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      if (lane < 12) reinterpret_cast<uint32_t *>(plane + (size_t)t * 48)[lane] = words[lane];
+    }
+  } else {
+    // value group of 8 tokens: coordinate i of token p at bit 2 (8 i + p); lane l's
+    // coordinates 2l and 2l+1 make up 32-bit word l of the group
+    uint32_t *wp = reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256) + lane;
+    const int p = t & 7, s0 = 8 * (p >> 2) + 2 * (p & 3), s1 = s0 + 16;
+    const uint32_t w = *wp;
+    *wp = (w & ~((3u << s0) | (3u << s1))) | (c0 << s0) | (c1 << s1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are complete
+}
+
 // MULTI: several query positions (a.n_q > 1 or several row groups); a template flag so that
 // single-query decode keeps none of its bookkeeping live across the tile loop.
-template <int BK, int NH, bool SPARSE, bool MULTI>
+// APPEND: the new token of each sequence is quantized into the caches first (a.xk, a.xv).
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
@@ -245,6 +319,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       }
       nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
     };
+
+    if constexpr (APPEND) {
+      // the workgroup whose split holds position T - 1 writes the new token's key (wave 0)
+      // and value (wave 1) before any of its waves reads the cache: the waves of a workgroup
+      // share one CU's vector L1, so stores complete before the barrier are what the loads
+      // after it see
+      if (T >= 1 && T - 1 >= t_begin && T - 1 < t_end) {
+        if (wave < 2) append_token<BK>(a, wave == 0, b, kvh, T - 1, lane, lds + kWBase + 7 * 4096);
+        __syncthreads();
+      }
+    }
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
     // is used until all of them are in flight (a use would make the wave wait right there)
@@ -776,17 +861,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
-template <int BK, bool SPARSE, bool MULTI>
+template <int BK, bool SPARSE, bool MULTI, bool APPEND>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8, SPARSE, MULTI><<<grid, kThreads, 0, stream>>>(a);
+  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (!SPARSE && (a.n_q > 1 || a.vgroups > 1)) return launch_nh<BK, false, true>(a, grid, stream);
-  return launch_nh<BK, SPARSE, false>(a, grid, stream);
+  if (!SPARSE && (a.n_q > 1 || a.vgroups > 1)) return launch_nh<BK, false, true, false>(a, grid, stream);
+  if (!SPARSE && a.xk != nullptr) return launch_nh<BK, false, false, true>(a, grid, stream);
+  return launch_nh<BK, SPARSE, false, false>(a, grid, stream);
 }
 
 }  // namespace

@@ -77,6 +77,10 @@ struct DecodeArgs {
   // Query rows of the single-launch kernel: n_q query positions per sequence (1 for decode)
   // give n_q * group rows per kv head, taken vg_size at a time by `vgroups` work items.
   int n_q, vgroups, vg_size;
+  // Append in the same launch (single-query dense decode): the new token of each sequence,
+  // [batch][1][n_kv_heads][d] of x_dtype, is quantized into position T - 1 first.
+  const void *xk, *xv;
+  int x_dtype;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,

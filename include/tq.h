@@ -170,6 +170,25 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
 size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,
                                  float sparse_v_tau);
 
+/* Append and attend in one call: for every sequence b with T = seq_lens ? clamp(seq_lens[b], 0,
+ * ctx_len) : ctx_len >= 1, quantize its new key xk[b] and value xv[b] into position T - 1 of
+ * the caches (as tq_quantize_append_kv with start_pos = T - 1, n_tokens = 1), then dense
+ * decode attention exactly as tq_decode_attn with sparse_v_tau = 0 and no scores.  One launch
+ * for keys of 3/4 bits, values of 2 bits and n_q_heads / n_kv_heads <= 8 (the workgroup that
+ * owns position T - 1 writes the token first); otherwise the append kernel and then the
+ * decode call, which needs seq_lens == NULL (TQ_ERR_UNSUPPORTED otherwise).
+ *   xk, xv     device in [batch][1][n_kv_heads][d] of x_dtype, 16-byte aligned
+ *   the other arguments as for tq_decode_attn; workspace of tq_decode_workspace_bytes(..., 0)
+ * A decode step needs this one launch instead of two.  The new token's codes follow the
+ * same rule as the append kernels (equal to the oracle's except within 1e-6 of a boundary;
+ * the fp32 rotation is evaluated in another order, so a code within that band can differ
+ * from the append kernel's).
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,
+                          int x_dtype, const void *q, int q_dtype, int n_q_heads,
+                          const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Attention of n_q new query positions per sequence against the packed cache, which already
  * holds them (speculative verification of draft tokens, chunked prefill): the same scores,
  * softmax and rotated-domain value sum as tq_decode_attn ([google] score kernel; [inferrs]

@@ -185,6 +185,29 @@ def test_multi_query_argument_validation():
     assert _multi(k, _cache(layout=1, bits=2, n_kv_heads=1)) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_append_decode_argument_validation():
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+
+    def ad(k, v, xk=FAKE + 0x500000, xv=FAKE + 0x580000, xdt=1, hq=8, seq=None, ctx=512,
+           ws_bytes=None, out=FAKE + 0x700000):
+        if ws_bytes is None:
+            ws_bytes = tq.decode_workspace_bytes(k.batch, hq, k.n_kv_heads, max(ctx, 0), 0.0) or 1
+        return tq.lib().tq_decode_attn_append(ctypes.byref(k), ctypes.byref(v), xk, xv, xdt, FAKE + 0x600000, 1,
+                                              hq, seq, ctx, 0.088, out, None, FAKE + 0x800000, ws_bytes, None)
+
+    assert ad(k, v, xk=0) == tq.TQ_ERR_INVALID_ARG
+    assert ad(k, v, xv=FAKE + 0x580004) == tq.TQ_ERR_INVALID_ARG
+    assert ad(k, v, xdt=7) == tq.TQ_ERR_INVALID_ARG
+    assert ad(k, v, hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert ad(k, v, hq=64) == tq.TQ_ERR_UNSUPPORTED
+    assert ad(k, v, ctx=2048) == tq.TQ_ERR_CAPACITY
+    assert ad(k, v, ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    assert ad(k, v, out=0) == tq.TQ_ERR_INVALID_ARG
+    assert ad(v, k) == tq.TQ_ERR_UNSUPPORTED                                    # layouts swapped
+    # widths without the one-launch kernel take two launches, which need one common position
+    assert ad(_cache(layout=0, bits=8), _cache(layout=1, bits=8), seq=FAKE + 0x900000) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_probe_rejects_bad_arguments():
     f = tq.lib().tq_probe_stream_read
     assert f(None, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG

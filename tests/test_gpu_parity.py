@@ -233,6 +233,73 @@ def test_decode_dense_matches_oracle(case, signs, golden_codebooks):
     _decode_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape)
 
 
+def _append_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, seq_lens=None, x_dtype=None):
+    """Caches hold garbage at each sequence's last position T_b - 1; decode_attn_append must
+    write the new token there (codes and norm as the oracle quantizes it), leave every other
+    position as it was, and attend over the result."""
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
+    k, v = g["k"], g["v"]
+    if x_dtype is not None:
+        k, v = k.to(x_dtype), v.to(x_dtype)
+    lens = [ctx] * batch if seq_lens is None else list(seq_lens)
+    k_pre, v_pre = k.clone(), v.clone()
+    k_new = torch.zeros((batch, 1, hkv, 128), dtype=k.dtype)
+    v_new = torch.zeros((batch, 1, hkv, 128), dtype=v.dtype)
+    for b, tb in enumerate(lens):
+        if tb >= 1:
+            k_new[b, 0], v_new[b, 0] = k[b, tb - 1], v[b, tb - 1]
+            k_pre[b, tb - 1] = k[b, (tb * 7) % ctx] * -3.0       # garbage in the slot to be written
+            v_pre[b, tb - 1] = v[b, (tb * 5) % ctx] * 2.5
+    kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
+    vc = _new_cache(batch, hkv, cap, bits_v, 1, signs)
+    _fill(kc, k_pre.to(DEV))
+    _fill(vc, v_pre.to(DEV))
+    before = {(id(c), b, h): (parity.gpu_plane_codes(c, b, h, cap)[0], parity.gpu_plane_norms(c, b, h, cap))
+              for c in (kc, vc) for b in range(batch) for h in range(hkv)}
+    scale = 1.0 / math.sqrt(128)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    q = g["q"].to(DEV).contiguous()
+    buf = tq.decode_attn_append(kc, vc, k_new.to(DEV).contiguous(), v_new.to(DEV).contiguous(), q, ctx, scale,
+                                seq_lens=sl)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    for cache, xnew, table in ((kc, k_new, golden[bits_k]), (vc, v_new, golden[bits_v])):
+        for b, tb in enumerate(lens):
+            for h in range(hkv):
+                codes0, norms0 = before[(id(cache), b, h)]
+                keep = np.ones(cap, dtype=bool)
+                if tb >= 1:
+                    keep[tb - 1] = False
+                    parity.check_plane(cache, b, h, parity.to_f64(xnew[b, :, h]), tb - 1, s64, table)
+                assert np.array_equal(parity.gpu_plane_codes(cache, b, h, cap)[0][keep], codes0[keep]), (b, h)
+                assert np.array_equal(parity.gpu_plane_norms(cache, b, h, cap)[keep], norms0[keep]), (b, h)
+    kh = parity.oracle_cache_view(kc, s64, golden[bits_k], ctx)
+    vh = parity.oracle_cache_view(vc, s64, golden[bits_v], ctx)
+    out, lse, _ = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=seq_lens)
+    fin = np.isfinite(lse)
+    got_lse = buf.lse.cpu().numpy()
+    assert np.all(np.isneginf(got_lse[~fin]))
+    assert np.allclose(got_lse[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    worst = parity.check_rows(buf.out.cpu().numpy(), out, "append+decode out")
+    _say(f"  worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, bits_v, seq_lens, x dtype)
+    ("llama8k", 1, 32, 8, 700, 768, 4, 2, None, None),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 2, None, None),
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 2, [1500, 1], None),
+    ("llama8k", 3, 8, 2, 520, 576, 3, 2, [520, 0, 9], "f32"),
+    ("llama8k", 2, 4, 4, 300, 320, 4, 2, [257, 64], "f16"),
+    ("llama8k", 1, 8, 2, 333, 384, 8, 3, None, None),      # other widths: two launches
+])
+def test_decode_append_matches_oracle(case, signs, golden_codebooks):
+    name, *shape, xdt = case
+    _say("append + decode", case)
+    xdt = {None: None, "f32": torch.float32, "f16": torch.float16}[xdt]
+    _append_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, x_dtype=xdt)
+
+
 def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens=None, q_dtype=None):
     g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq, n_q=n_q)
     kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
