@@ -70,7 +70,8 @@ def parse():
     p.add_argument("--kernel-us", type=float, default=None, help="average launch time of --kernel")
     p.add_argument("--fetch", default=None)
     p.add_argument("--write", default=None)
-    p.add_argument("--kernel", default=DECODE_KERNEL)
+    p.add_argument("--kernel", default=DECODE_KERNEL,
+                   help="regular expression over the kernel names (template arguments included)")
     p.add_argument("--name", default=None)
     p.add_argument("--command", default="")
     return p.parse_args()
@@ -107,6 +108,13 @@ def decode_bytes(w, bits_k, bits_v, hkv, batch, ctx):
     """Algorithmic bytes of one decode call: packed K and V codes + fp16 norms of every token."""
     per_token_head = (D * bits_k // 8 + 2) + (D * bits_v // 8 + 2)
     return batch * hkv * ctx * per_token_head
+
+
+def append_bytes(w, bits_k, bits_v, hkv, batch):
+    """Algorithmic bytes of appending one token per sequence: its K and V inputs read, packed
+    codes + fp16 norms written."""
+    in_bytes = w.dtype.itemsize
+    return batch * hkv * (2 * D * in_bytes + (D * bits_k // 8 + 2) + (D * bits_v // 8 + 2))
 
 
 def cpu_cores():
@@ -276,23 +284,34 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         kc, vc = caches[i % copies]
         tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
 
-    def step(i):
+    dense_single = tau == 0.0 and bk in (3, 4) and bv == 2 and w.group <= 8
+
+    def append_and_decode(i):  # one launch: the fused kernel writes the new token, then attends
+        kc, vc = caches[i % copies]
+        tq.decode_attn_append(kc, vc, k_new, v_new, q, ctx, scale, buffers=bufs)
+
+    def two_launches(i):
         append(i)
         decode_only(i)
 
+    step = append_and_decode if dense_single else two_launches
     timer = Timer(torch, args.eager)
     steps = args.steps
     ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     kv_tokens = batch * ctx
     value = kv_tokens / (ms_per_step / 1e3)
-    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(decode_only, max(args.steps, 2 * copies), 2, batches=5)
-    ms_a = timer.per_iteration_ms(append, max(args.steps, 2 * copies), 2)
+    n_rep = max(args.steps, 2 * copies)
+    # the roofline kernel: the step's single launch when fused, else the decode call
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step if dense_single else decode_only, n_rep, 2, batches=5)
+    ms_d = timer.per_iteration_ms(decode_only, n_rep, 2) if dense_single else ms_k
+    ms_a = timer.per_iteration_ms(append, n_rep, 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
+    if dense_single:
+        nbytes += append_bytes(w, bk, bv, hkv, batch)
     achieved = nbytes / (ms_k / 1e3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us, decode call {ms_k * 1e3:.1f} us, "
-        f"append (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic")
-
-    dense_single = tau == 0.0 and bk in (3, 4) and bv == 2 and w.group <= 8
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({'one fused launch' if dense_single else 'append + decode'}), "
+        f"decode-only call {ms_d * 1e3:.1f} us, standalone append (K+V) {ms_a * 1e3:.1f} us, "
+        f"roofline launch {ms_k * 1e3:.1f} us = {achieved:.0f} GB/s algorithmic")
     result = {
         "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -300,16 +319,17 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D,
                    "ctx": ctx, "bits_k": bk, "bits_v": bv, "sparse_v_tau": tau,
-                   "step": "append 1 token (K,V) + decode attention", "cache_copies": copies,
+                   "step": ("append 1 token (K,V) + decode attention, one fused launch" if dense_single
+                            else "append 1 token (K,V) + decode attention"), "cache_copies": copies,
                    "timing": "eager" if args.eager else "hip graph replay"},
-        "decode_call_us": ms_k * 1e3,
-        "decode_call_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
+        "decode_call_us": ms_d * 1e3,
         "append_kv_us": ms_a * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": DECODE_KERNEL if dense_single
+                     "kernel": f"{DECODE_KERNEL} (append + attend instance)" if dense_single
                      else "decode attention call (split, Sparse-V and merge kernels)",
-                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3},
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                     "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
         "_kernel": "decode" if dense_single else "decode_sparse",
     }
     if not args.no_cpu_baseline:
@@ -608,7 +628,7 @@ def summarize_traffic(args):
     def weighted(table, counts):
         # every instance of the kernel (e.g. the bit widths of the prefill layers), weighted
         # by its number of dispatches
-        keys = sorted(k for k in table if args.kernel in k and CALIBRATION_KERNEL not in k)
+        keys = sorted(k for k in table if re.search(args.kernel, k) and CALIBRATION_KERNEL not in k)
         if not keys:
             sys.exit(f"no kernel matching {args.kernel!r} in {sorted(table)}")
         n = sum(counts[k] for k in keys)
@@ -629,7 +649,7 @@ def summarize_traffic(args):
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
            "dispatches": {"fetch": df, "write": dw}, "sources_digest": kernel_sources_digest(),
            "command": args.command}
-    kname = "decode" if args.kernel == DECODE_KERNEL else "quantize"
+    kname = "decode" if args.kernel.startswith(DECODE_KERNEL) else "quantize"
     with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{args.workload}.txt"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
@@ -644,7 +664,7 @@ def summarize_instmix(args):
     got = {}
     for n in names:
         means, counts = _counter_means(args.summarize_instmix, n)
-        keys = [k for k in means if args.kernel in k]
+        keys = [k for k in means if re.search(args.kernel, k)]
         if keys:
             tot = sum(counts[k] for k in keys)
             got[n] = sum(means[k] * counts[k] for k in keys) / tot
@@ -659,7 +679,8 @@ def summarize_instmix(args):
         rec["launch_us"] = args.kernel_us
         # SQ_INSTS_VALU includes the matrix instructions, which run on their own unit
         rec["valu_issue_fraction"] = 4.0 * (got["SQ_INSTS_VALU"] - got.get("SQ_INSTS_MFMA", 0.0)) / (1024 * cycles)
-    with open(os.path.join(ROOT, "profiles", f"instmix_{args.kernel}_{args.workload}.txt"), "w") as fh:
+    base = DECODE_KERNEL if args.kernel.startswith(DECODE_KERNEL) else QUANTIZE_KERNEL
+    with open(os.path.join(ROOT, "profiles", f"instmix_{base}_{args.workload}.txt"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
 

@@ -179,26 +179,43 @@ __device__ __forceinline__ float exp2_or_zero(float x, float ref) {
 // rotation): n = ||x|| (fp32, stored as fp16), u = H (s . x) / (sqrt(d) n) with the butterflies
 // across the wave, code = number of boundaries below u, then the bits of this token in the
 // cache's layout (3/4-bit key rows, 2-bit value groups of 8 tokens, whose other tokens are
-// kept).  `scratch` is 48 bytes of LDS for assembling a 3-bit row.
-template <int BK>
-__device__ void append_token(const DecodeArgs &a, bool key, int b, int kvh, int t, int lane, uint8_t *scratch) {
-  const CacheView &c = key ? a.k : a.v;
+// kept).  Two phases, so that the loads are in flight while the wave does other setup work:
+// new_token_load reads the input (and the value word the token shares), new_token_store
+// computes and writes the codes and waits until the stores are complete.
+struct NewToken {
+  uint32_t x0, x1;  // raw input bits: two fp32 words, or one word of two 16-bit values
+  uint32_t vword;   // value cache: the group word that lane's coordinates go into
+};
+
+__device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key, int b, int kvh, int t, int lane) {
   const void *x = key ? a.xk : a.xv;
   const size_t xi = ((size_t)b * a.n_kv_heads + kvh) * kD + 2 * lane;
+  NewToken n{0u, 0u, 0u};
+  if (a.x_dtype == TQ_F32) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(x) + xi);
+    n.x0 = w.x;
+    n.x1 = w.y;
+  } else {
+    n.x0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xi);
+  }
+  if (!key) n.vword = reinterpret_cast<const uint32_t *>(a.v.plane(b, kvh) + (size_t)(t >> 3) * 256)[lane];
+  return n;
+}
+
+template <int BK>
+__device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &in, int b, int kvh, int t, int lane,
+                                uint8_t *scratch) {
+  const CacheView &c = key ? a.k : a.v;
   float x0, x1;
   if (a.x_dtype == TQ_F32) {
-    const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(x) + xi);
-    x0 = f.x;
-    x1 = f.y;
+    x0 = __uint_as_float(in.x0);
+    x1 = __uint_as_float(in.x1);
+  } else if (a.x_dtype == TQ_BF16) {
+    x0 = __uint_as_float(in.x0 << 16);
+    x1 = __uint_as_float(in.x0 & 0xffff0000u);
   } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xi);
-    if (a.x_dtype == TQ_BF16) {
-      x0 = __uint_as_float(w << 16);
-      x1 = __uint_as_float(w & 0xffff0000u);
-    } else {
-      x0 = f16((uint16_t)(w & 0xffffu));
-      x1 = f16((uint16_t)(w >> 16));
-    }
+    x0 = f16((uint16_t)(in.x0 & 0xffffu));
+    x1 = f16((uint16_t)(in.x0 >> 16));
   }
   float ss = x0 * x0 + x1 * x1;
 #pragma unroll
@@ -238,10 +255,9 @@ __device__ void append_token(const DecodeArgs &a, bool key, int b, int kvh, int 
   } else {
     // value group of 8 tokens: coordinate i of token p at bit 2 (8 i + p); lane l's
     // coordinates 2l and 2l+1 make up 32-bit word l of the group
-    uint32_t *wp = reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256) + lane;
     const int p = t & 7, s0 = 8 * (p >> 2) + 2 * (p & 3), s1 = s0 + 16;
-    const uint32_t w = *wp;
-    *wp = (w & ~((3u << s0) | (3u << s1))) | (c0 << s0) | (c1 << s1);
+    reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256)[lane] =
+        (in.vword & ~((3u << s0) | (3u << s1))) | (c0 << s0) | (c1 << s1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are complete
 }
@@ -320,16 +336,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
     };
 
-    if constexpr (APPEND) {
-      // the workgroup whose split holds position T - 1 writes the new token's key (wave 0)
-      // and value (wave 1) before any of its waves reads the cache: the waves of a workgroup
-      // share one CU's vector L1, so stores complete before the barrier are what the loads
-      // after it see
-      if (T >= 1 && T - 1 >= t_begin && T - 1 < t_end) {
-        if (wave < 2) append_token<BK>(a, wave == 0, b, kvh, T - 1, lane, lds + kWBase + 7 * 4096);
-        __syncthreads();
-      }
-    }
+    // APPEND: the workgroup whose split holds position T - 1 writes the new token's key (wave
+    // 6) and value (wave 7) while the other waves set up; the waves of a workgroup share one
+    // CU's vector L1, so stores complete before the first barrier are what every load after
+    // it sees.  The only cache load issued before that barrier is each wave's first key
+    // tile: the wave whose first tile holds T - 1 issues it after the barrier instead.
+    const bool has_new = APPEND && T >= 1 && T - 1 >= t_begin && T - 1 < t_end;
+    const bool appends = has_new && wave >= kWaves - 2;
+    const bool defer_keys = has_new && (T - 1 - t_begin) / kTile == wave;
+    NewToken nt{0u, 0u, 0u};
+    if (appends) nt = new_token_load(a, wave == kWaves - 2, b, kvh, T - 1, lane);
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
     // is used until all of them are in flight (a use would make the wave wait right there)
@@ -348,8 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       qw0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qbase);
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
-    load_keys(wave);
+    if (!defer_keys) load_keys(wave);
     build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
+    if (appends) new_token_store<BK>(a, wave == kWaves - 2, nt, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
     int *chunk_count = reinterpret_cast<int *>(lds + kVBase);
@@ -382,6 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
     }
     __syncthreads();
+    if (defer_keys) load_keys(wave);
     // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
     half8 qop[8];
     {
