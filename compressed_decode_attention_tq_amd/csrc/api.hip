@@ -216,6 +216,9 @@ int tq_quantize_append_kv(const tq_cache *k, const tq_cache *v, const void *xk, 
   if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
   if ((long)start_pos + n_tokens > k->capacity) return TQ_ERR_CAPACITY;
   if (n_tokens == 0) return TQ_OK;
+  if (n_tokens <= kSmallAppendMax)  // decode steps and short drafts: one wave per plane
+    return hip_status(launch_append_small(view_of(k), view_of(v), k->batch, xk, xv, x_dtype, start_pos,
+                                          n_tokens, static_cast<hipStream_t>(hip_stream)));
   return hip_status(launch_quantize_kv(view_of(k), view_of(v), k->batch, xk, xv, x_dtype, start_pos,
                                        n_tokens, static_cast<hipStream_t>(hip_stream)));
 }
@@ -360,7 +363,7 @@ int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, 
   // other code widths: the append kernel, then the decode path (one common position only)
   if (seq_lens != nullptr) return TQ_ERR_UNSUPPORTED;
   if (ctx_len >= 1) {
-    const hipError_t e = launch_quantize_kv(a.k, a.v, k->batch, xk, xv, x_dtype, ctx_len - 1, 1, stream);
+    const hipError_t e = launch_append_small(a.k, a.v, k->batch, xk, xv, x_dtype, ctx_len - 1, 1, stream);
     if (e != hipSuccess) return TQ_ERR_HIP;
   }
   return hip_status(launch_decode(a, stream));

@@ -1,0 +1,218 @@
+// Appending a few tokens to a key cache (row layout) and a value cache (8-token value
+// groups): decode steps and short drafts.  The chunked quantize kernel builds code-search
+// tables in LDS before its first token, a fixed chain of loads and barriers that dominates
+// when only one token per (batch, kv head) arrives.  Here one block owns one (batch, kv head,
+// key or value) plane and one wave of 64 lanes one token, two coordinates per lane, with the
+// transform and the reductions in registers (lanes.h).
+//
+// Steps per token, as in the chunked kernel ([tq-80] §核心创新: norm split off, random
+// rotation, data-independent Lloyd-Max code; [inferrs] §核心技术: Walsh-Hadamard rotation):
+//   n = ||x||_2 in fp32, stored as fp16 (round to nearest even);
+//   u = H (s . x) / (sqrt(d) n);  code_i = #{j : t_j < u_i};
+//   the codes go to their bit positions in the cache's layout (tq.h).
+#include "tq_common.h"
+#include "tq_launch.h"
+#include "lanes.h"
+
+namespace tq {
+namespace {
+
+// input element pair (2 lane, 2 lane + 1) of one token row
+template <int DTYPE>
+__device__ __forceinline__ void load_pair(const void *x, size_t i, float &x0, float &x1) {
+  if constexpr (DTYPE == TQ_F32) {
+    const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(x) + i);
+    x0 = f.x;
+    x1 = f.y;
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + i);
+    if constexpr (DTYPE == TQ_BF16) {
+      x0 = __uint_as_float(w << 16);
+      x1 = __uint_as_float(w & 0xffff0000u);
+    } else {
+      x0 = __half2float(__ushort_as_half((uint16_t)(w & 0xffffu)));
+      x1 = __half2float(__ushort_as_half((uint16_t)(w >> 16)));
+    }
+  }
+}
+
+// codes of coordinates 2 lane, 2 lane + 1 and the norm of one token
+template <int BITS>
+__device__ __forceinline__ void token_codes(const CacheView &c, float x0, float x1, int lane, uint32_t &c0,
+                                            uint32_t &c1, float &n) {
+  n = sqrtf(wave_reduce<false>(x0 * x0 + x1 * x1));
+  const float y0 = c.signs[2 * lane] < 0 ? -x0 : x0, y1 = c.signs[2 * lane + 1] < 0 ? -x1 : x1;
+  float u0 = y0 + y1, u1 = y0 - y1;  // stage 0 of the transform, inside the lane
+  wave_fwht_upper(u0, u1, lane);
+  const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
+  u0 *= inv;
+  u1 *= inv;
+  c0 = 0u;
+  c1 = 0u;
+  for (int j = 0; j < (1 << BITS) - 1; ++j) {
+    const float t = c.boundaries[j];
+    c0 += u0 > t ? 1u : 0u;
+    c1 += u1 > t ? 1u : 0u;
+  }
+}
+
+// Key rows: lane l's two codes are bits [2 BITS l, 2 BITS (l + 1)) of the token's row of
+// 16 BITS bytes; the row is assembled in LDS (4 BITS words) and stored by the first lanes.
+template <int BITS>
+__device__ __forceinline__ void store_row(uint8_t *row, uint32_t c0, uint32_t c1, int lane, uint32_t *words) {
+  constexpr int kWords = 4 * BITS;
+  if (lane < kWords) words[lane] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  const uint32_t f = c0 | (c1 << BITS);
+  const int bit = 2 * BITS * lane, wi = bit >> 5, sh = bit & 31;
+  atomicOr(&words[wi], f << sh);
+  if (sh + 2 * BITS > 32) atomicOr(&words[wi + 1], f >> (32 - sh));
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  if (lane < kWords) reinterpret_cast<uint32_t *>(row)[lane] = words[lane];
+}
+
+// Value groups: coordinate i of token p of a group sits at bit (8 i + p) BITS, so lane l's
+// coordinates 2l and 2l + 1 of all 8 tokens are the 2 BITS bytes at 2 BITS l of the group,
+// which the lane reads, updates for every new token of the group, and writes back.
+template <int BITS>
+struct GroupSlice {
+  uint64_t lo = 0, hi = 0;
+  __device__ void load(const uint8_t *g, int lane) {
+    const uint8_t *p = g + 2 * BITS * lane;
+    if constexpr (BITS == 2) {
+      lo = *reinterpret_cast<const uint32_t *>(p);
+    } else if constexpr (BITS == 3) {
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+      lo = (uint64_t)h[0] | ((uint64_t)h[1] << 16) | ((uint64_t)h[2] << 32);
+    } else if constexpr (BITS == 4) {
+      lo = *reinterpret_cast<const uint64_t *>(p);
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2 *>(p), b = *reinterpret_cast<const uint2 *>(p + 8);
+      lo = (uint64_t)a.x | ((uint64_t)a.y << 32);
+      hi = (uint64_t)b.x | ((uint64_t)b.y << 32);
+    }
+  }
+  __device__ void store(uint8_t *g, int lane) const {
+    uint8_t *p = g + 2 * BITS * lane;
+    if constexpr (BITS == 2) {
+      *reinterpret_cast<uint32_t *>(p) = (uint32_t)lo;
+    } else if constexpr (BITS == 3) {
+      uint16_t *h = reinterpret_cast<uint16_t *>(p);
+      h[0] = (uint16_t)lo;
+      h[1] = (uint16_t)(lo >> 16);
+      h[2] = (uint16_t)(lo >> 32);
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint64_t *>(p) = lo;
+    } else {
+      *reinterpret_cast<uint2 *>(p) = make_uint2((uint32_t)lo, (uint32_t)(lo >> 32));
+      *reinterpret_cast<uint2 *>(p + 8) = make_uint2((uint32_t)hi, (uint32_t)(hi >> 32));
+    }
+  }
+  __device__ void set(int pos, uint32_t code) {  // no field straddles bit 64
+    constexpr uint64_t kMask = (1ull << BITS) - 1ull;
+    if (pos < 64) lo = (lo & ~(kMask << pos)) | ((uint64_t)code << pos);
+    else hi = (hi & ~(kMask << (pos - 64))) | ((uint64_t)code << (pos - 64));
+  }
+};
+
+// Wave j of the block takes token j of the plane: keys write their rows directly; value
+// codes meet in LDS and wave 0 then updates each value group the tokens touch, once.
+struct SmallLds {
+  uint32_t words[kSmallAppendMax][32];  // key row assembly, per wave
+  uint2 codes[kSmallAppendMax][64];     // value codes (coordinates 2 lane, 2 lane + 1)
+};
+
+template <int DTYPE, int BITS, bool KEY>
+__device__ void append_plane(const CacheView &c, const void *x, int b, int h, int start_pos, int n_tokens, int wave,
+                             int lane, SmallLds &sh) {
+  uint8_t *plane = c.plane(b, h);
+  if (wave < n_tokens) {
+    const int t = start_pos + wave;
+    float x0, x1;
+    load_pair<DTYPE>(x, (((size_t)b * n_tokens + wave) * c.n_kv_heads + h) * kD + 2 * lane, x0, x1);
+    uint32_t c0, c1;
+    float n;
+    token_codes<BITS>(c, x0, x1, lane, c0, c1, n);
+    if (lane == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
+    if constexpr (KEY) store_row<BITS>(plane + (size_t)t * (16 * BITS), c0, c1, lane, sh.words[wave]);
+    else sh.codes[wave][lane] = make_uint2(c0, c1);
+  }
+  if constexpr (!KEY) {
+    __syncthreads();
+    if (wave == 0) {
+      GroupSlice<BITS> slice;
+      int group = -1;
+      for (int j = 0; j < n_tokens; ++j) {
+        const int t = start_pos + j;
+        if ((t >> 3) != group) {
+          if (group >= 0) slice.store(plane + (size_t)group * (kD * BITS), lane);
+          group = t >> 3;
+          slice.load(plane + (size_t)group * (kD * BITS), lane);
+        }
+        const uint2 cc = sh.codes[j][lane];
+        slice.set((t & 7) * BITS, cc.x);
+        slice.set((8 + (t & 7)) * BITS, cc.y);
+      }
+      slice.store(plane + (size_t)group * (kD * BITS), lane);
+    }
+  }
+}
+
+// block z < batch * Hkv: key plane (b, h) = (z / Hkv, z % Hkv); the rest: value planes.
+// One wave per token: blockDim = 64 n_tokens.
+template <int DTYPE, int BK, int BV>
+__global__ __launch_bounds__(64 * kSmallAppendMax) void append_small_kernel(CacheView kc, CacheView vc,
+                                                                           const void *__restrict__ xk,
+                                                                           const void *__restrict__ xv,
+                                                                           int start_pos, int n_tokens, int batch) {
+  __shared__ SmallLds sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int planes = batch * kc.n_kv_heads;
+  const int z = blockIdx.x;
+  if (z < planes)
+    append_plane<DTYPE, BK, true>(kc, xk, z / kc.n_kv_heads, z % kc.n_kv_heads, start_pos, n_tokens, wave, lane, sh);
+  else
+    append_plane<DTYPE, BV, false>(vc, xv, (z - planes) / vc.n_kv_heads, (z - planes) % vc.n_kv_heads, start_pos,
+                                   n_tokens, wave, lane, sh);
+}
+
+template <int DTYPE, int BK>
+hipError_t launch_bv(const CacheView &kc, const CacheView &vc, int grid, const void *xk, const void *xv,
+                     int start_pos, int n_tokens, int batch, hipStream_t stream) {
+  switch (vc.bits) {
+    case 2: append_small_kernel<DTYPE, BK, 2><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
+    case 3: append_small_kernel<DTYPE, BK, 3><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
+    case 4: append_small_kernel<DTYPE, BK, 4><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
+    default: append_small_kernel<DTYPE, BK, 8><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DTYPE>
+hipError_t launch_bk(const CacheView &kc, const CacheView &vc, int grid, const void *xk, const void *xv,
+                     int start_pos, int n_tokens, int batch, hipStream_t stream) {
+  switch (kc.bits) {
+    case 2: return launch_bv<DTYPE, 2>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
+    case 3: return launch_bv<DTYPE, 3>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
+    case 4: return launch_bv<DTYPE, 4>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
+    default: return launch_bv<DTYPE, 8>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append_small(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
+                               const void *xv, int x_dtype, int start_pos, int n_tokens, hipStream_t stream) {
+  if (n_tokens < 1 || n_tokens > kSmallAppendMax || kc.layout != TQ_LAYOUT_ROWS || vc.layout != TQ_LAYOUT_GROUP8)
+    return hipErrorInvalidValue;
+  const long grid = 2L * batch * kc.n_kv_heads;
+  if (grid < 1 || grid > 0x7fffffffL) return hipErrorInvalidValue;
+  if (x_dtype == TQ_F32) return launch_bk<TQ_F32>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
+  if (x_dtype == TQ_BF16) return launch_bk<TQ_BF16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
+  return launch_bk<TQ_F16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
+}
+
+}  // namespace tq

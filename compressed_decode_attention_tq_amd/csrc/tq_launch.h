@@ -24,6 +24,7 @@ SplitPlan plan_fused(int batch, int n_kv_heads, int ctx_len);
 SplitPlan plan_fused_sparse(int batch, int n_kv_heads, int ctx_len, const SplitPlan &p);
 constexpr int kMaxChunksPerSplit = 64;
 constexpr int kMaxQueryPositions = 4096;  // query positions of one multi-query call
+constexpr int kSmallAppendMax = 8;        // appends of up to this many tokens take one wave per plane
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WorkspaceLayout {
@@ -88,6 +89,10 @@ hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_d
 hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
                               const void *xv, int x_dtype, int start_pos, int n_tokens,
                               hipStream_t stream);
+// Appends of 1..kSmallAppendMax tokens to a key cache (rows) and a value cache (groups of 8):
+// one wave per (batch, kv head, key or value) plane, the tokens in order.
+hipError_t launch_append_small(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
+                               const void *xv, int x_dtype, int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

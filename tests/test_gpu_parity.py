@@ -113,6 +113,44 @@ def test_quantize_append_kv_equals_two_appends(bits_k, bits_v, dtype, signs, gol
         parity.check_quantize(one[1], parity.to_f64(g["v"]), 0, s64, _table(golden_codebooks, bits_v))
 
 
+@pytest.mark.parametrize("bits_k,bits_v,dtype", [(4, 2, "bf16"), (3, 2, "f32"), (2, 4, "f16"), (8, 3, "bf16"),
+                                                (4, 8, "f32")])
+def test_small_appends_match_oracle(bits_k, bits_v, dtype, signs, golden_codebooks):
+    """Appends of 1..8 tokens (one wave per plane, tokens in order) against the oracle, over
+    ranges that start, end and cross inside 8-token value groups; everything outside the
+    written positions keeps its stale contents."""
+    _say("small appends", bits_k, bits_v, dtype)
+    w = inputs.WORKLOADS["llama8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=61, n_kv_heads=3, with_query=False)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    k, v = g["k"].to(tdt), g["v"].to(tdt)
+    kc, vc = _new_cache(2, 3, 128, bits_k, 0, signs), _new_cache(2, 3, 128, bits_v, 1, signs)
+    for c in (kc, vc):
+        c.codes.fill_(0xA5)
+        c.norms.fill_(0x3C00)
+    edges = [0, 1, 4, 12, 13, 21, 22, 30, 37, 45, 46, 53, 61]
+    for a, e in zip(edges[:-1], edges[1:]):
+        assert 1 <= e - a <= 8
+        tq.quantize_append_kv(kc, vc, k[:, a:e].contiguous().to(DEV), v[:, a:e].contiguous().to(DEV), a)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    parity.check_quantize(kc, parity.to_f64(k), 0, s64, _table(golden_codebooks, bits_k))
+    parity.check_quantize(vc, parity.to_f64(v), 0, s64, _table(golden_codebooks, bits_v))
+    for c, bits in ((kc, bits_k), (vc, bits_v)):
+        for b in range(2):
+            for h in range(3):
+                raw = c.plane_codes(b, h).cpu().numpy()
+                tail = 64 * 16 * bits if c.layout == 1 else 61 * 16 * bits   # past the last group / row
+                assert np.all(raw[tail:] == 0xA5), (b, h)
+                assert np.all(c.plane_norms(b, h)[61:].cpu().numpy() == 0x3C00), (b, h)
+        if c.layout == 1:  # positions 61..63 share the last value group: their codes are kept
+            for b in range(2):
+                for h in range(3):
+                    got = o.unpack(c.plane_codes(b, h).cpu().numpy()[:64 * 16 * bits], 64, 128, bits, 1)
+                    stale = o.unpack(np.full(64 * 16 * bits, 0xA5, dtype=np.uint8), 64, 128, bits, 1)
+                    assert np.array_equal(got[61:], stale[61:]), (b, h)
+
+
 def test_quantize_special_vectors(signs, golden_codebooks):
     """Basis vectors, the all-ones vector (exact ties on the middle boundary) and zeros."""
     _say("special vectors")
