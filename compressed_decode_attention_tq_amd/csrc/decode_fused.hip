@@ -160,7 +160,7 @@ __device__ __forceinline__ float exp2_or_zero(float x, float ref) {
 // cache's layout (3/4-bit key rows, 2-bit value groups of 8 tokens, whose other tokens are
 // kept).  Two phases, so that the loads are in flight while the wave does other setup work:
 // new_token_load reads the input (and the value word the token shares), new_token_store
-// computes and writes the codes and waits until the stores are complete.
+// computes and writes the codes (the caller waits for the stores before reading them back).
 struct NewToken {
   uint32_t x0, x1;  // raw input bits: two fp32 words, or one word of two 16-bit values
   uint32_t vword;   // value cache: the group word that lane's coordinates go into
@@ -236,7 +236,6 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
     reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256)[lane] =
         (in.vword & ~((3u << s0) | (3u << s1))) | (c0 << s0) | (c1 << s1);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are complete
 }
 
 // MULTI: several query positions (a.n_q > 1 or several row groups); a template flag so that
@@ -313,16 +312,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
     };
 
-    // APPEND: the workgroup whose split holds position T - 1 writes the new token's key (wave
-    // 6) and value (wave 7) while the other waves set up; the waves of a workgroup share one
-    // CU's vector L1, so stores complete before the first barrier are what every load after
-    // it sees.  The only cache load issued before that barrier is each wave's first key
-    // tile: the wave whose first tile holds T - 1 issues it after the barrier instead.
+    // APPEND: in the workgroup whose split holds position T - 1, the wave that reads that
+    // position's tile (tiles go to waves round robin) writes the new token's key and value
+    // first.  Only that wave ever loads those bytes, so no other wave waits for the stores:
+    // the writer waits for its own stores to complete after the first barrier and only then
+    // issues its first key tile if that tile holds T - 1; later tiles are loaded later still.
     const bool has_new = APPEND && T >= 1 && T - 1 >= t_begin && T - 1 < t_end;
-    const bool appends = has_new && wave >= kWaves - 2;
-    const bool defer_keys = has_new && (T - 1 - t_begin) / kTile == wave;
-    NewToken nt{0u, 0u, 0u};
-    if (appends) nt = new_token_load(a, wave == kWaves - 2, b, kvh, T - 1, lane);
+    const int new_tile = has_new ? (T - 1 - t_begin) / kTile : -1;
+    const bool appends = has_new && new_tile % kWaves == wave;
+    const bool defer_keys = appends && new_tile == wave;
+    NewToken ntk{0u, 0u, 0u}, ntv{0u, 0u, 0u};
+    if (appends) {
+      ntk = new_token_load(a, true, b, kvh, T - 1, lane);
+      ntv = new_token_load(a, false, b, kvh, T - 1, lane);
+    }
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
     // is used until all of them are in flight (a use would make the wave wait right there)
@@ -343,7 +346,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
     if (!defer_keys) load_keys(wave);
     build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
-    if (appends) new_token_store<BK>(a, wave == kWaves - 2, nt, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
+    // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
+    // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
+    if (appends) {
+      new_token_store<BK>(a, true, ntk, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
+      new_token_store<BK>(a, false, ntv, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
+    }
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
     int *chunk_count = reinterpret_cast<int *>(lds + kVBase);
@@ -376,7 +384,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
     }
     __syncthreads();
-    if (defer_keys) load_keys(wave);
+    if (appends) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the new token's stores are complete
+      if (defer_keys) load_keys(wave);
+    }
     // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
     half8 qop[8];
     {
