@@ -181,7 +181,8 @@ def main():
 class Timer:
     """Time of one iteration of a callable, with HIP events on the current stream.  Exactly
     `n` iterations are timed: they are recorded once into a HIP graph, the graph is replayed
-    once untimed, then once between the events; or (eager) launched directly."""
+    untimed (at least 3 times and 50 ms), then once between the events; or (eager) launched
+    directly."""
 
     def __init__(self, torch, eager):
         self.torch = torch
@@ -213,8 +214,17 @@ class Timer:
             with torch.cuda.graph(graph):
                 for i in range(n):
                     fn(i)
-            graph.replay()
-            torch.cuda.synchronize()
+            # untimed replays first, at least 3 and 50 ms of work: the device idles while the
+            # graph is captured, and the first replays after that run slower
+            t_warm = 0.0
+            for r in range(100):
+                start.record(stream)
+                graph.replay()
+                end.record(stream)
+                torch.cuda.synchronize()
+                t_warm += start.elapsed_time(end)
+                if r >= 2 and t_warm >= 50.0:
+                    break
             for _ in range(batches):
                 start.record(stream)
                 graph.replay()
