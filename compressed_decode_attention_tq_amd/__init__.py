@@ -37,6 +37,16 @@ class CacheStruct(ctypes.Structure):
     ]
 
 
+class PagedCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -64,13 +74,19 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
         L.tq_decode_attn_multi_workspace_bytes.restype = sz
         L.tq_dequantize.argtypes = [ctypes.POINTER(CacheStruct), i32, i32, vp, i32, vp]
+        PP = ctypes.POINTER(PagedCacheStruct)
+        L.tq_paged_quantize_append_kv.argtypes = [PP, PP, vp, vp, i32, vp, i32, vp]
+        L.tq_paged_decode_attn.argtypes = [PP, PP, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.tq_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.tq_paged_decode_workspace_bytes.restype = sz
         L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.tq_code_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.tq_code_bytes.restype = sz
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_dequantize", "tq_probe_stream_read"):
+                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_dequantize", "tq_probe_stream_read",
+                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -304,4 +320,92 @@ def decode_attn_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new,
         _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len, float(scale), _dev(buffers.out, "out"),
         _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_append")
+    return buffers
+
+
+class PagedCache:
+    """One paged K or V cache of one layer: a pool of pages (page_tokens positions of every kv
+    head each) + the block table [batch, max_pages] (int32, -1 = no page) it is read through.
+    The K and V caches of a layer share one block table (pass the K cache's `block_table`)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, page_tokens: int, n_pages: int, max_pages: int,
+                 bits: int, layout: int, signs, block_table=None, device="cuda", d: int = D):
+        torch = _torch()
+        self.d, self.bits, self.layout = d, bits, layout
+        self.batch, self.n_kv_heads, self.page_tokens = batch, n_kv_heads, page_tokens
+        self.n_pages, self.max_pages = n_pages, max_pages
+        self.codes = torch.zeros(n_pages * n_kv_heads * page_tokens * d * bits // 8, dtype=torch.uint8, device=device)
+        self.norms = torch.zeros(n_pages * n_kv_heads * page_tokens, dtype=torch.float16, device=device)
+        self.block_table = (torch.full((batch, max_pages), -1, dtype=torch.int32, device=device)
+                            if block_table is None else block_table)
+        c, t = make_codebook_table(d, bits)
+        self.centroids = torch.from_numpy(c).to(device)
+        self.boundaries = torch.from_numpy(np.concatenate([t, [0.0]]).astype(np.float32)).to(device)
+        if signs.is_cuda and signs.dtype == torch.int8 and signs.is_contiguous():
+            self.signs = signs
+        else:
+            self.signs = signs.to(device=device, dtype=torch.int8).contiguous()
+
+    def struct(self) -> PagedCacheStruct:
+        return PagedCacheStruct(self.d, self.bits, self.layout, self.batch, self.n_kv_heads, self.page_tokens,
+                                self.n_pages, self.max_pages, self.codes.data_ptr(), self.norms.data_ptr(),
+                                self.block_table.data_ptr(), self.centroids.data_ptr(),
+                                self.boundaries.data_ptr(), self.signs.data_ptr())
+
+    def page_codes(self, page: int, h: int):
+        per = self.page_tokens * self.d * self.bits // 8
+        i = page * self.n_kv_heads + h
+        return self.codes[i * per:(i + 1) * per]
+
+    def page_norms(self, page: int, h: int):
+        i = page * self.n_kv_heads + h
+        return self.norms[i * self.page_tokens:(i + 1) * self.page_tokens]
+
+
+def paged_quantize_append_kv(k_cache: PagedCache, v_cache: PagedCache, xk, xv, start_pos, stream=None):
+    """Quantize xk, xv [B, n, Hkv, d] into positions start_pos[b] + j of the paged caches."""
+    for name, cache, x in (("xk", k_cache, xk), ("xv", v_cache, xv)):
+        if x.dim() != 4 or x.shape[0] != cache.batch or x.shape[2] != cache.n_kv_heads or x.shape[3] != cache.d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if xk.shape != xv.shape or xk.dtype != xv.dtype:
+        raise ValueError("xk and xv must have the same shape and dtype")
+    ks, vs = k_cache.struct(), v_cache.struct()
+    _check(lib().tq_paged_quantize_append_kv(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(xk, "xk"), _dev(xv, "xv"), _dtype_code(xk.dtype),
+        _dev(start_pos, "start_pos"), xk.shape[1], _stream_ptr(stream)), "tq_paged_quantize_append_kv")
+
+
+def paged_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_ctx_len: int) -> int:
+    return int(lib().tq_paged_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_ctx_len))
+
+
+class PagedDecodeBuffers:
+    """Caller-owned outputs and workspace of one paged decode problem shape."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, max_ctx_len, device="cuda", d=D, want_lse=True):
+        torch = _torch()
+        self.out = torch.empty((batch, n_q_heads, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=device) if want_lse else None
+        nbytes = paged_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_ctx_len)
+        if nbytes == 0:
+            raise TQError(TQ_ERR_INVALID_ARG, "tq_paged_decode_workspace_bytes")
+        # zero once: the arrival counters live here and every call leaves them at zero
+        self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.ws_bytes = nbytes
+
+
+def paged_decode_attn(k_cache: PagedCache, v_cache: PagedCache, q, seq_lens, max_ctx_len: int, scale: float,
+                      buffers: PagedDecodeBuffers | None = None, stream=None):
+    """Dense decode attention over paged caches; returns the PagedDecodeBuffers (out, lse)."""
+    bsz, hq, d = q.shape
+    if buffers is None:
+        buffers = PagedDecodeBuffers(bsz, hq, k_cache.n_kv_heads, max_ctx_len, device=q.device, d=d)
+    ks, vs = k_cache.struct(), v_cache.struct()
+    _check(lib().tq_paged_decode_attn(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, _dev(seq_lens, "seq_lens"),
+        max_ctx_len, float(scale), _dev(buffers.out, "out"),
+        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn")
     return buffers

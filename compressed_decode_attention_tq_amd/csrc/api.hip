@@ -151,6 +151,79 @@ WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads,
   return w;
 }
 
+SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len) {
+  SplitPlan p = plan_fused(batch, n_kv_heads, ctx_len);
+  if (p.split_len > kPagedMaxSplit) {
+    p.split_len = kPagedMaxSplit;
+    p.n_splits = (ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit;
+  }
+  return p;
+}
+
+WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len) {
+  const SplitPlan fp = plan_fused_paged(batch, n_kv_heads, ctx_len);
+  const size_t rows = (size_t)batch * n_q_heads * fp.n_splits;
+  WorkspaceLayout w{};
+  size_t off = 0;
+  w.counters = off;
+  off = align_up(off + (size_t)batch * n_kv_heads * sizeof(unsigned), 256);
+  w.fpart_ml = off;
+  off = align_up(off + rows * sizeof(float2), 256);
+  w.fpart_o = off;
+  off = align_up(off + rows * kD * sizeof(float), 256);
+  w.part_ml = w.part_o = w.cand_count = w.cand = off;
+  w.total = off;
+  return w;
+}
+
+int check_paged(const tq_paged_cache *c) {
+  if (c == nullptr) return TQ_ERR_INVALID_ARG;
+  if (c->codes == nullptr || c->norms == nullptr || c->block_table == nullptr || c->centroids == nullptr ||
+      c->boundaries == nullptr || c->signs == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned(c->codes, 16) || !aligned(c->norms, 16) || !aligned(c->block_table, 4) ||
+      !aligned(c->centroids, 4) || !aligned(c->boundaries, 4) || !aligned(c->signs, 16))
+    return TQ_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->page_tokens < 1 || c->n_pages < 1 || c->max_pages < 1)
+    return TQ_ERR_INVALID_ARG;
+  if (c->layout != TQ_LAYOUT_ROWS && c->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;
+  if (c->d != kD) return TQ_ERR_UNSUPPORTED;
+  if (!valid_bits(c->bits)) return TQ_ERR_UNSUPPORTED;
+  if (c->page_tokens % kChunk != 0 || c->page_tokens > kMaxCapacity) return TQ_ERR_UNSUPPORTED;
+  // 32-bit offsets in the kernels: pool code bytes below 3 GiB, positions below 2^30
+  const double pool = (double)c->n_pages * c->n_kv_heads * c->page_tokens * kD * c->bits / 8;
+  if (pool >= 3.0 * (1u << 30) || (double)c->max_pages * c->page_tokens >= (double)(1 << 30))
+    return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+// a view of the pool in which plane(page, h) is one page of one kv head
+CacheView view_of_pool(const tq_paged_cache *c) {
+  CacheView v;
+  v.codes = c->codes;
+  v.norms = c->norms;
+  v.centroids = c->centroids;
+  v.boundaries = c->boundaries;
+  v.signs = c->signs;
+  v.bits = c->bits;
+  v.layout = c->layout;
+  v.n_kv_heads = c->n_kv_heads;
+  v.capacity = c->page_tokens;
+  return v;
+}
+
+int check_paged_pair(const tq_paged_cache *k, const tq_paged_cache *v) {
+  int st = check_paged(k);
+  if (st != TQ_OK) return st;
+  st = check_paged(v);
+  if (st != TQ_OK) return st;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->page_tokens != v->page_tokens ||
+      k->n_pages != v->n_pages || k->max_pages != v->max_pages || k->block_table != v->block_table)
+    return TQ_ERR_INVALID_ARG;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -420,6 +493,75 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
   a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
   if (!decode_fused_supported(a)) return TQ_ERR_UNSUPPORTED;
   return hip_status(launch_decode_fused(a, compute_units(), static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_paged_quantize_append_kv(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk,
+                                const void *xv, int x_dtype, const int32_t *start_pos, int n_tokens,
+                                void *hip_stream) {
+  const int st = check_paged_pair(k, v);
+  if (st != TQ_OK) return st;
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  if (start_pos == nullptr || !aligned(start_pos, 4) || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return TQ_OK;
+  if (n_tokens > (1 << 24)) return TQ_ERR_UNSUPPORTED;
+  return hip_status(launch_append_paged(view_of_pool(k), view_of_pool(v), k->block_table, k->max_pages, k->n_pages,
+                                        k->batch, xk, xv, x_dtype, start_pos, n_tokens,
+                                        static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t tq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int max_ctx_len) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads != 0 || max_ctx_len < 0)
+    return 0;
+  return workspace_layout_paged(batch, n_q_heads, n_kv_heads, max_ctx_len).total;
+}
+
+int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, const int32_t *seq_lens, int max_ctx_len, float scale, float *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  const int st = check_paged_pair(k, v);
+  if (st != TQ_OK) return st;
+  if (k->signs != v->signs) return TQ_ERR_INVALID_ARG;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens == nullptr || !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / k->n_kv_heads;
+  if (max_ctx_len < 0 || !std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if ((long)max_ctx_len > (long)k->max_pages * k->page_tokens) return TQ_ERR_CAPACITY;
+  if (group > 8 || (k->bits != 3 && k->bits != 4) || v->bits != 2) return TQ_ERR_UNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout_paged(k->batch, n_q_heads, k->n_kv_heads, max_ctx_len);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+
+  DecodeArgs a{};
+  a.k = view_of_pool(k);
+  a.v = view_of_pool(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = max_ctx_len;
+  a.scale = scale;
+  a.n_q = 1;
+  a.vgroups = 1;
+  a.vg_size = group;
+  a.fplan = plan_fused_paged(k->batch, k->n_kv_heads, max_ctx_len);
+  a.plan = a.fplan;
+  a.out = out;
+  a.lse = lse;
+  char *ws = static_cast<char *>(workspace);
+  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
+  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
+  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
+  a.block_table = k->block_table;
+  a.max_pages = k->max_pages;
+  a.n_pages = k->n_pages;
+  return hip_status(launch_decode_fused_paged(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

@@ -241,9 +241,13 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // MULTI: several query positions (a.n_q > 1 or several row groups); a template flag so that
 // single-query decode keeps none of its bookkeeping live across the tile loop.
 // APPEND: the new token of each sequence is quantized into the caches first (a.xk, a.xv).
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND>
+// PAGED: the caches are page pools found through a.block_table; each tile lies inside one
+// page (pages are whole multiples of 64 tokens), so a tile's loads differ from the
+// contiguous case only by its base offset.
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
+  static_assert(!PAGED || !(SPARSE || MULTI || APPEND), "paged caches: dense single-query decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -284,11 +288,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     };
 
     const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-    const uint32_t span_tok = (uint32_t)n_tiles * kTile;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v.plane(b, kvh) + (size_t)t_begin * 32, span_tok * 32);
-    const __amdgpu_buffer_rsrc_t knrs = make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
-    const __amdgpu_buffer_rsrc_t vnrs = make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    // Buffers: the split's span of one plane, or (paged) the whole pools, whose size the host
+    // keeps below 3 GiB.  tile_tok(tile) is the tile's first position counted in tokens of
+    // the buffer; a tile with no page gets an offset past the end, so it reads zeros.
+    const uint32_t span_tok = PAGED ? (uint32_t)a.n_pages * a.n_kv_heads * a.k.capacity : (uint32_t)n_tiles * kTile;
+    const __amdgpu_buffer_rsrc_t krs =
+        PAGED ? make_rsrc(a.k.codes, span_tok * KROW) : make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
+    const __amdgpu_buffer_rsrc_t vrs =
+        PAGED ? make_rsrc(a.v.codes, span_tok * 32) : make_rsrc(a.v.plane(b, kvh) + (size_t)t_begin * 32, span_tok * 32);
+    const __amdgpu_buffer_rsrc_t knrs =
+        PAGED ? make_rsrc(a.k.norms, span_tok * 2) : make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    const __amdgpu_buffer_rsrc_t vnrs =
+        PAGED ? make_rsrc(a.v.norms, span_tok * 2) : make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    constexpr uint32_t kNoPage = 0xffffffffu;
+    uint32_t page_tok = kNoPage;  // paged: lane i holds tile_tok of the wave's tile wave + 8 i
+    if constexpr (PAGED) {
+      const int tile_i = wave + kWaves * lane;
+      if (tile_i < n_tiles) {
+        const int P = a.k.capacity, t0 = t_begin + tile_i * kTile, slot = t0 / P;
+        const int page = slot < a.max_pages ? a.block_table[(size_t)b * a.max_pages + slot] : -1;
+        if (page >= 0 && page < a.n_pages) page_tok = ((uint32_t)page * a.n_kv_heads + kvh) * P + (t0 - slot * P);
+      }
+    }
+    auto tile_tok = [&](int tile) -> uint32_t {
+      if constexpr (PAGED) return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, (tile - wave) / kWaves);
+      else return (uint32_t)tile * kTile;
+    };
+    auto tile_off = [&](uint32_t tok, uint32_t unit) -> uint32_t {  // bytes; past the end for no page
+      return PAGED && tok == kNoPage ? 0xf0000000u : tok * unit;
+    };
     const uint32_t k_voff = (uint32_t)m_row * KROW + (uint32_t)quarter * (4 * BK);
     const uint32_t v_voff = (uint32_t)quarter * 256u + (uint32_t)m_row * 16u;
     const uint32_t n_voff = (uint32_t)pr * 4u;
@@ -298,7 +326,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     auto load_keys = [&](int tile) {
       // the whole offset is in the vector offset: a tile past the split's end lies outside
       // the buffer's range and reads as zeros without touching memory
-      const uint32_t so = (uint32_t)tile * (kTile * KROW);
+      const uint32_t tok = tile_tok(tile);
+      const uint32_t so = tile_off(tok, KROW);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (BK == 4) {
@@ -309,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = 0u;
         }
       }
-      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
+      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + tile_off(tok, 2), 0, 0);
     };
 
     // APPEND: in the workgroup whose split holds position T - 1, the wave that reads that
@@ -444,12 +473,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       uint32_t vw[2][4];
       uint32_t nvw = 0u;
       if constexpr (!SPARSE) {
+        const uint32_t tok = tile_tok(tile);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + (uint32_t)tile * (kTile * 32) + c * 1024, 0, 0);
+          const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + tile_off(tok, 32) + c * 1024, 0, 0);
           vw[c][0] = w[0]; vw[c][1] = w[1]; vw[c][2] = w[2]; vw[c][3] = w[3];
         }
-        nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff + (uint32_t)tile * (kTile * 2), 0, 0);
+        nvw = __builtin_amdgcn_raw_buffer_load_b32(vnrs, n_voff + tile_off(tok, 2), 0, 0);
       }
 
       // ---- scores: sub-tile s, 16-coordinate chunk m -> key fields 2m, 2m+1 of the quarter
@@ -865,10 +895,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
-template <int BK, bool SPARSE, bool MULTI, bool APPEND>
+template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND><<<grid, kThreads, 0, stream>>>(a);
+  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -900,6 +930,16 @@ bool decode_fused_sparse_supported(const DecodeArgs &a) {
          a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
          a.plan.split_len % kTile == 0 && a.fplan.split_len % a.plan.split_len == 0 &&
          a.fplan.split_len / a.plan.split_len <= kMaxChunksPerSplit;
+}
+
+hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
+  if (a.block_table == nullptr || a.seq_lens == nullptr || a.fplan.split_len > kPagedMaxSplit ||
+      a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity || !decode_fused_supported(a))
+    return hipErrorInvalidValue;
+  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  return a.k.bits == 4 ? launch_nh<4, false, false, false, true>(a, (int)items, stream)
+                       : launch_nh<3, false, false, false, true>(a, (int)items, stream);
 }
 
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream) {

@@ -82,6 +82,11 @@ struct DecodeArgs {
   // [batch][1][n_kv_heads][d] of x_dtype, is quantized into position T - 1 first.
   const void *xk, *xv;
   int x_dtype;
+  // Paged caches (block_table != nullptr): k and v view the page pools, with capacity =
+  // page_tokens so that plane(page, h) is one page of one kv head; position t of sequence b
+  // lies in pool page block_table[b * max_pages + t / page_tokens].
+  const int32_t *block_table;
+  int max_pages, n_pages;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
@@ -90,9 +95,21 @@ hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batc
                               const void *xv, int x_dtype, int start_pos, int n_tokens,
                               hipStream_t stream);
 // Appends of 1..kSmallAppendMax tokens to a key cache (rows) and a value cache (groups of 8):
-// one wave per (batch, kv head, key or value) plane, the tokens in order.
+// one block per (batch, kv head, key or value) plane, one wave per token.
 hipError_t launch_append_small(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
                                const void *xv, int x_dtype, int start_pos, int n_tokens, hipStream_t stream);
+// Appends to paged caches (views of the page pools, capacity = page_tokens): token j of
+// sequence b at position start_pos[b] + j; one block per aligned 8-token window of one
+// (sequence, kv head, key or value), one wave per token.
+hipError_t launch_append_paged(const CacheView &kc, const CacheView &vc, const int32_t *block_table,
+                               int max_pages, int n_pages, int batch, const void *xk, const void *xv,
+                               int x_dtype, const int32_t *start_pos, int n_tokens, hipStream_t stream);
+// Longest split of the paged decode: 64 tiles per wave, so that one lane per tile holds the
+// wave's page offsets.
+constexpr int kPagedMaxSplit = 8 * 64 * 64;
+SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len);
+WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len);
+hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -217,6 +217,71 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
 size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q,
                                             int ctx_len);
 
+/* A paged K or V cache of one layer, the block-table layout of serving engines: the tokens
+ * of every sequence live in fixed-size pages of one shared pool, position t of sequence b
+ * in pool page block_table[b][t / page_tokens] at slot t % page_tokens.  A page holds
+ * page_tokens consecutive positions of every kv head; within one (page, kv head) the codes
+ * follow `layout` exactly as a tq_cache plane of capacity page_tokens does.
+ *   codes        [n_pages][n_kv_heads][page_tokens * d * bits / 8] bytes, 16-byte aligned
+ *   norms        [n_pages][n_kv_heads][page_tokens] fp16 bit patterns, 16-byte aligned
+ *   block_table  device int32 [batch][max_pages], 4-byte aligned; an entry outside
+ *                [0, n_pages) means "no page": appends skip positions that map to it and
+ *                decode reads them as zero codes and norms (never out of the pool)
+ *   centroids, boundaries, signs as for tq_cache.
+ * page_tokens: a positive multiple of 64.  The pool's code bytes must stay below 3 GiB
+ * (32-bit offsets inside the decode kernel).  The K and V caches of a layer share one
+ * block table. */
+typedef struct tq_paged_cache {
+  int32_t d;
+  int32_t bits;
+  int32_t layout;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t page_tokens;
+  int32_t n_pages;
+  int32_t max_pages;
+  uint8_t *codes;
+  uint16_t *norms;
+  const int32_t *block_table;
+  const float *centroids;
+  const float *boundaries;
+  const int8_t *signs;
+} tq_paged_cache;
+
+/* Quantize n_tokens new tokens of every sequence into a paged key cache (ROWS) and value
+ * cache (GROUP8): token j of sequence b goes to position start_pos[b] + j, with the same
+ * steps and codes rule as tq_quantize_append ([tq-80] §核心创新; [inferrs] §核心技术).
+ * Positions below 0, at or past max_pages * page_tokens, or on a "no page" entry are
+ * skipped.  Other positions are left untouched (a value group of 8 tokens is
+ * read-modified-written).  Calls that overlap on one pool race, and so do sequences whose
+ * tables share a page at the same positions.
+ *   xk, xv     device in [batch][n_tokens][n_kv_heads][d] of x_dtype, 16-byte aligned
+ *   start_pos  device int32 [batch], 4-byte aligned
+ * Errors: TQ_ERR_INVALID_ARG (also for mismatched caches or layouts), TQ_ERR_UNSUPPORTED,
+ * TQ_ERR_HIP. */
+int tq_paged_quantize_append_kv(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk,
+                                const void *xv, int x_dtype, const int32_t *start_pos, int n_tokens,
+                                void *hip_stream);
+
+/* Dense decode attention over paged caches: as tq_decode_attn with sparse_v_tau = 0 and no
+ * scores, sequence b attending over positions 0 .. T_b - 1, T_b = clamp(seq_lens[b], 0,
+ * max_ctx_len), its pages found through the block table.  Keys of 3 or 4 bits (ROWS),
+ * values of 2 bits (GROUP8), n_q_heads / n_kv_heads <= 8; otherwise TQ_ERR_UNSUPPORTED.
+ * Same kernel and arithmetic as the contiguous call: equal codes give equal outputs.
+ *   seq_lens     device int32 [batch] (required)
+ *   max_ctx_len  upper bound of the lengths, <= max_pages * page_tokens (TQ_ERR_CAPACITY)
+ *   out, lse     as for tq_decode_attn
+ *   workspace    device scratch of tq_paged_decode_workspace_bytes(...) bytes, 256-byte
+ *                aligned, zero-filled once before first use (arrival counters, left at zero
+ *                by every completed call); calls sharing it must not overlap in time.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, const int32_t *seq_lens, int max_ctx_len, float scale, float *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes tq_paged_decode_attn needs (0 for invalid arguments). */
+size_t tq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int max_ctx_len);
+
 /* Reconstruct x_hat = ||x||_fp16 * R^T c[idx] for cache positions
  * [start_pos, start_pos + n_tokens) ([google] unpack kernel; [tq-fwht] §2 invertibility).
  *   out  device out [batch][n_tokens][n_kv_heads][d] of out_dtype, 16-byte aligned

@@ -208,6 +208,51 @@ def test_append_decode_argument_validation():
     assert ad(_cache(layout=0, bits=8), _cache(layout=1, bits=8), seq=FAKE + 0x900000) == tq.TQ_ERR_UNSUPPORTED
 
 
+def _paged(**kw):
+    base = dict(d=128, bits=4, layout=0, batch=2, n_kv_heads=2, page_tokens=256, n_pages=64, max_pages=16,
+                codes=FAKE, norms=FAKE + 0x1000000, block_table=FAKE + 0x1100000, centroids=FAKE + 0x200000,
+                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000)
+    base.update(kw)
+    return tq.PagedCacheStruct(*(base[f] for f, _ in tq.PagedCacheStruct._fields_))
+
+
+def test_paged_argument_validation():
+    L = tq.lib()
+    k, v = _paged(), _paged(layout=1, bits=2, codes=FAKE + 0x2000000, norms=FAKE + 0x3000000)
+    sp, x = FAKE + 0x900000, FAKE + 0x500000
+
+    def app(k, v, x=x, dt=1, start=sp, n=1):
+        return L.tq_paged_quantize_append_kv(ctypes.byref(k), ctypes.byref(v), x, x + 0x80000, dt, start, n, None)
+
+    assert app(k, v, n=0) == tq.TQ_OK                                   # nothing to do, no launch
+    assert app(k, v, start=0) == tq.TQ_ERR_INVALID_ARG
+    assert app(k, v, start=sp + 2) == tq.TQ_ERR_INVALID_ARG
+    assert app(k, v, n=-1) == tq.TQ_ERR_INVALID_ARG
+    assert app(k, v, dt=5) == tq.TQ_ERR_INVALID_ARG
+    assert app(v, k) == tq.TQ_ERR_INVALID_ARG                            # layouts swapped
+    assert app(_paged(page_tokens=100), v) == tq.TQ_ERR_UNSUPPORTED      # not a multiple of 64
+    assert app(_paged(block_table=0), v) == tq.TQ_ERR_INVALID_ARG
+    assert app(_paged(block_table=FAKE + 0x1100002), v) == tq.TQ_ERR_INVALID_ARG
+    assert app(_paged(max_pages=32), v) == tq.TQ_ERR_INVALID_ARG         # tables differ
+    assert app(_paged(n_pages=1 << 20, page_tokens=64, n_kv_heads=8),
+               _paged(n_pages=1 << 20, page_tokens=64, n_kv_heads=8, layout=1, bits=2)) == tq.TQ_ERR_UNSUPPORTED
+    ws = tq.paged_decode_workspace_bytes(2, 16, 2, 4096)
+    assert ws > 0 and tq.paged_decode_workspace_bytes(2, 15, 2, 4096) == 0
+
+    def dec(k, v, hq=16, seq=sp, ctx=4096, wsb=ws, out=FAKE + 0x700000):
+        return L.tq_paged_decode_attn(ctypes.byref(k), ctypes.byref(v), FAKE + 0x600000, 1, hq, seq, ctx, 0.088,
+                                      out, None, FAKE + 0x800000, wsb, None)
+
+    assert dec(k, v, seq=0) == tq.TQ_ERR_INVALID_ARG                    # lengths are required
+    assert dec(k, v, ctx=4097) == tq.TQ_ERR_CAPACITY                    # 16 pages of 256
+    assert dec(k, v, hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert dec(k, v, hq=64) == tq.TQ_ERR_UNSUPPORTED                    # group 32
+    assert dec(k, v, wsb=16) == tq.TQ_ERR_WORKSPACE
+    assert dec(k, v, out=0) == tq.TQ_ERR_INVALID_ARG
+    assert dec(_paged(bits=8), v) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(k, _paged(layout=1, bits=3)) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_probe_rejects_bad_arguments():
     f = tq.lib().tq_probe_stream_read
     assert f(None, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG

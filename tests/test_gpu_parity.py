@@ -338,6 +338,97 @@ def test_decode_append_matches_oracle(case, signs, golden_codebooks):
     _append_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, x_dtype=xdt)
 
 
+def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtype=None, hole=None, seed=0):
+    """Paged caches with shuffled pages (and optionally one table entry of no page) filled by
+    the paged append (a long call, then a short one with per-sequence starts); the pages,
+    gathered in table order, must hold the oracle's codes, and paged decode must equal the
+    contiguous decode on the gathered cache bit for bit and the oracle within tolerance."""
+    max_ctx = max(seq_lens)
+    max_pages = (max_ctx + page - 1) // page + 1
+    n_pages = batch * max_pages + 3
+    rng = np.random.default_rng(seed)
+    table = torch.tensor(rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages), dtype=torch.int32)
+    if hole is not None:
+        table[hole] = -1
+    kc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, bits_k, 0, signs.to(DEV),
+                       block_table=table.to(DEV).contiguous(), device=DEV)
+    vc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, 2, 1, kc.signs, block_table=kc.block_table, device=DEV)
+    for c in (kc, vc):
+        c.codes.fill_(0xA5)
+        c.norms.fill_(0x3C00)
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=max_ctx, n_kv_heads=hkv, n_q_heads=hq)
+    k, v = g["k"], g["v"]
+    if x_dtype is not None:
+        k, v = k.to(x_dtype), v.to(x_dtype)
+    # every position in one call, then each sequence's last position again (a decode step:
+    # per-sequence starts, T_b = 0 gives start -1, which is skipped)
+    zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
+    tq.paged_quantize_append_kv(kc, vc, k.contiguous().to(DEV), v.contiguous().to(DEV), zeros)
+    last = torch.tensor([tb - 1 for tb in seq_lens], dtype=torch.int32)
+    idx = last.clamp(min=0).long()
+    k1 = k[torch.arange(batch), idx].unsqueeze(1).contiguous()
+    v1 = v[torch.arange(batch), idx].unsqueeze(1).contiguous()
+    tq.paged_quantize_append_kv(kc, vc, k1.to(DEV), v1.to(DEV), last.to(DEV))
+    torch.cuda.synchronize()
+    # the gathered contiguous copy: slot p of sequence b = page table[b, p]
+    cap = max_pages * page
+    kf = _new_cache(batch, hkv, cap, bits_k, 0, signs)
+    vf = _new_cache(batch, hkv, cap, 2, 1, signs)
+    for pc, fc in ((kc, kf), (vc, vf)):
+        per = page * 16 * pc.bits
+        for b in range(batch):
+            for h in range(hkv):
+                dst, dn = fc.plane_codes(b, h), fc.plane_norms(b, h)
+                for slot in range(max_pages):
+                    pg = int(table[b, slot])
+                    if pg < 0:
+                        continue
+                    dst[slot * per:(slot + 1) * per] = pc.page_codes(pg, h)
+                    dn[slot * page:(slot + 1) * page] = pc.page_norms(pg, h)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    lens = list(seq_lens)
+    for fc, x, table_b in ((kf, k, golden[bits_k]), (vf, v, golden[2])):
+        for b in range(batch):
+            for h in range(hkv):
+                upto = max_ctx
+                if hole is not None and hole[0] == b:
+                    upto = min(upto, hole[1] * page)     # positions from the hole on were skipped
+                if upto > 0:
+                    parity.check_plane(fc, b, h, parity.to_f64(x[b, :upto, h]), 0, s64, table_b)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = g["q"].to(DEV).contiguous()
+    scale = 1.0 / math.sqrt(128)
+    got = tq.paged_decode_attn(kc, vc, q, sl, max_ctx, scale)
+    ref = tq.decode_attn(kf, vf, q, max_ctx, scale, seq_lens=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(got.out, ref.out) and torch.equal(got.lse, ref.lse)
+    kh = parity.oracle_cache_view(kf, s64, golden[bits_k], max_ctx)
+    vh = parity.oracle_cache_view(vf, s64, golden[2], max_ctx)
+    out, lse, _ = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=lens)
+    fin = np.isfinite(lse)
+    got_lse = got.lse.cpu().numpy()
+    assert np.all(np.isneginf(got_lse[~fin]))
+    assert np.allclose(got_lse[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    worst = parity.check_rows(got.out.cpu().numpy(), out, "paged decode out")
+    _say(f"  worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, page tokens, seq_lens, bits_k, x dtype, hole)
+    ("llama8k", 3, 32, 8, 64, [700, 1, 333], 4, None, (0, 5)),
+    ("batch32k", 2, 8, 2, 256, [1300, 1024], 3, None, None),
+    ("ctx131k", 2, 16, 2, 128, [1500, 0], 4, None, None),
+    ("llama8k", 2, 4, 4, 64, [64, 65], 4, "f32", None),
+    ("llama8k", 1, 8, 2, 512, [2100], 3, "f16", (0, 3)),
+])
+def test_paged_cache_matches_contiguous_and_oracle(case, signs, golden_codebooks):
+    name, batch, hq, hkv, page, lens, bk, xdt, hole = case
+    _say("paged", case)
+    xdt = {None: None, "f32": torch.float32, "f16": torch.float16}[xdt]
+    _paged_case(inputs.WORKLOADS[name], signs, golden_codebooks, batch, hq, hkv, page, lens, bk, x_dtype=xdt, hole=hole)
+
+
 def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens=None, q_dtype=None):
     g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq, n_q=n_q)
     kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
