@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama8k",
-                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k"])
+                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,6 +164,8 @@ def main():
         result = bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log)
     elif w.n_q > 1:
         result = bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log)
+    elif w.page_tokens > 0:
+        result = bench_paged(args, w, signs, dev, tq, inputs, torch, np, log)
     else:
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
     stream = stream_read_gbs(torch, tq, log)
@@ -383,6 +385,103 @@ def cpu_baseline_decode(w, tau, cache_pair, host_k, host_v, q, signs, np, torch,
             "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
                       f"{ctx} tokens: quantize+pack the appended token, unpack+dequantize+attend; "
                       f"{reps} repetitions"}
+
+
+class _GatheredPlanes:
+    """Batch element 0 of a paged cache as the planes the CPU baseline reads (host-side
+    gather through the block table; not timed)."""
+
+    def __init__(self, cache, table_row, torch):
+        self.cache, self.row, self.torch = cache, [int(p) for p in table_row], torch
+
+    def plane_codes(self, b, h):
+        return self.torch.cat([self.cache.page_codes(p, h) for p in self.row])
+
+    def plane_norms(self, b, h):
+        return self.torch.cat([self.cache.page_norms(p, h) for p in self.row])
+
+
+def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
+    """Decode over paged caches: the batched long-context shape with each sequence's positions
+    in pages of w.page_tokens scattered over the pool in a seeded random order.  A step
+    appends one token per sequence (K and V) through the block table, then paged decode."""
+    batch, hq, hkv, ctx, P = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.page_tokens
+    bk, bv = w.bits_k, w.bits_v
+    max_pages = (ctx + P - 1) // P
+    n_pages = batch * max_pages
+    per_copy = tq.code_bytes(D, bk, n_pages, hkv, P) + tq.code_bytes(D, bv, n_pages, hkv, P) + 4 * n_pages * hkv * P
+    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    log(f"[bench] workload={w.name} pages of {P} tokens, {n_pages} pages, copies={copies} "
+        f"cache/copy={per_copy / 1e6:.1f} MB ({'eager launches' if args.eager else 'HIP graph replay'})")
+    g = inputs.generate(w, device=dev)
+    k_all, v_all, q = g["k"], g["v"], g["q"].contiguous()
+    rng = np.random.default_rng(w.seed)
+    caches = []
+    zeros = torch.zeros(batch, dtype=torch.int32, device=dev)
+    for c in range(copies):
+        table = torch.tensor(rng.permutation(n_pages).reshape(batch, max_pages), dtype=torch.int32, device=dev)
+        kc = tq.PagedCache(batch, hkv, P, n_pages, max_pages, bk, tq.LAYOUT_ROWS, signs, block_table=table, device=dev)
+        vc = tq.PagedCache(batch, hkv, P, n_pages, max_pages, bv, tq.LAYOUT_GROUP8, kc.signs, block_table=table,
+                           device=dev)
+        tq.paged_quantize_append_kv(kc, vc, k_all[:, : ctx - 1].contiguous(), v_all[:, : ctx - 1].contiguous(), zeros)
+        caches.append((kc, vc))
+    k_new = k_all[:, ctx - 1:ctx].contiguous()
+    v_new = v_all[:, ctx - 1:ctx].contiguous()
+    host_k = k_all[:1].cpu() if not args.no_cpu_baseline else None
+    host_v = v_all[:1].cpu() if not args.no_cpu_baseline else None
+    del k_all, v_all, g
+    start = torch.full((batch,), ctx - 1, dtype=torch.int32, device=dev)
+    lens = torch.full((batch,), ctx, dtype=torch.int32, device=dev)
+    bufs = tq.PagedDecodeBuffers(batch, hq, hkv, ctx, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+
+    def append(i):
+        kc, vc = caches[i % copies]
+        tq.paged_quantize_append_kv(kc, vc, k_new, v_new, start)
+
+    def decode_only(i):
+        kc, vc = caches[i % copies]
+        tq.paged_decode_attn(kc, vc, q, lens, ctx, scale, buffers=bufs)
+
+    def step(i):
+        append(i)
+        decode_only(i)
+
+    timer = Timer(torch, args.eager)
+    ms_per_step = timer.per_iteration_ms(step, args.steps, args.warmup)
+    value = batch * ctx / (ms_per_step / 1e3)
+    n_rep = max(args.steps, 2 * copies)
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(decode_only, n_rep, 2, batches=5)
+    ms_a = timer.per_iteration_ms(append, n_rep, 2)
+    nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
+    achieved = nbytes / (ms_k / 1e3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (paged append + paged decode), paged decode call "
+        f"{ms_k * 1e3:.1f} us, paged append (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic")
+    result = {
+        "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16+f32",
+        "data": "synthetic (seeded; shapes and value distributions of the workload; pages in seeded random order)",
+        "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D,
+                   "ctx": ctx, "bits_k": bk, "bits_v": bv, "sparse_v_tau": 0.0, "page_tokens": P,
+                   "step": "paged append 1 token (K,V) + paged decode attention", "cache_copies": copies,
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "decode_call_us": ms_k * 1e3,
+        "append_kv_us": ms_a * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": f"{DECODE_KERNEL} (paged instance)",
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                     "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
+        "_kernel": "decode",
+    }
+    if not args.no_cpu_baseline:
+        kc, vc = caches[0]
+        row = kc.block_table[0].cpu().numpy()
+        gathered = (_GatheredPlanes(kc, row, torch), _GatheredPlanes(vc, row, torch))
+        result["cpu_baseline"] = cpu_baseline_decode(w, 0.0, gathered, host_k, host_v, q, signs, np, torch, log)
+    return result
 
 
 def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):

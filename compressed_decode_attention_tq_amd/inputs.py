@@ -63,6 +63,7 @@ class Workload:
     boundary_bits: int = 8
     append: int = 0                            # tokens appended after the prefill
     n_q: int = 1                               # query positions per sequence (multi-query)
+    page_tokens: int = 0                       # paged cache: positions per page (0 = contiguous)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -84,6 +85,9 @@ WORKLOADS = {
     # speculative verification on the Llama-3-8B-shaped layer: 4 new positions per step
     "verify8k": Workload("verify8k", 6, 1, 32, 8, 8192, 4, 2, torch.bfloat16, "normal",
                          head_channel_scales=(0.5, 20.0), append=4, n_q=4),
+    # the batched long-context shape in a paged cache: 256-token pages, shuffled in the pool
+    "paged32k": Workload("paged32k", 7, 16, 32, 8, 32768, 3, 2, torch.bfloat16, "student5",
+                         outlier_channels=8, outlier_scale=4.0, append=1, page_tokens=256),
 }
 
 
