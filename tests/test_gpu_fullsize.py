@@ -7,7 +7,9 @@ The oracle cannot take whole outputs at these sizes, so sampled outputs are comp
   prefill   a boundary (8/8-bit) layer and a middle (K4/V3) layer of the 32768-token
             cache, two kv-head planes each, against the oracle's quantizer.
 Caches, queries and launches are those of the benchmark: the context minus one token is
-appended, the last token goes through the key-and-value append, then one decode call.
+appended, then the last token goes in with the attention (one fused append-and-attend launch
+for dense decode, the key-and-value append and the decode call for Sparse V); the paged and
+multi-query lines likewise use their benchmark's calls.
 """
 import math
 import sys
@@ -44,11 +46,15 @@ def test_decode_full_size_sampled(workload, tau, golden_codebooks):
     vc = tq.PackedCache(batch, hkv, ctx, w.bits_v, tq.LAYOUT_GROUP8, sd, device=DEV)
     tq.quantize_append(kc, x["k"][:, : ctx - 1].contiguous(), 0)
     tq.quantize_append(vc, x["v"][:, : ctx - 1].contiguous(), 0)
-    tq.quantize_append_kv(kc, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(), ctx - 1)
+    k_new, v_new = x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous()
     q = x["q"].contiguous()
     scale = 1.0 / math.sqrt(128)
     bufs = tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=DEV)
-    tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
+    if tau == 0.0:
+        tq.decode_attn_append(kc, vc, k_new, v_new, q, ctx, scale, buffers=bufs)
+    else:
+        tq.quantize_append_kv(kc, vc, k_new, v_new, ctx - 1)
+        tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
     torch.cuda.synchronize()
     out_g, lse_g = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
     s64 = signs.numpy().astype(np.float64)
@@ -92,3 +98,82 @@ def test_prefill_layer_full_size_sampled(layer, golden_codebooks):
         for cache, xx, bits in ((kc, k, bk), (vc, v, bv)):
             near = parity.check_plane(cache, 0, h, parity.to_f64(xx[0, :, h]), 0, s64, golden_codebooks[bits])
             _say(f"  plane (0,{h}) {bits}-bit: near-boundary coordinates {near}")
+
+
+def test_paged_full_size_sampled(golden_codebooks):
+    """paged32k: the batched long-context shape in 256-token pages in random pool order,
+    filled through the paged append, one more token appended, then paged decode."""
+    w = inputs.WORKLOADS["paged32k"]
+    _say("full-size paged decode")
+    batch, hq, hkv, ctx, g, P = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.group, w.page_tokens
+    signs = inputs.rotation_signs()
+    sd = signs.to(DEV)
+    x = inputs.generate(w, device=DEV)
+    max_pages = ctx // P
+    n_pages = batch * max_pages
+    rng = np.random.default_rng(w.seed)
+    table = torch.tensor(rng.permutation(n_pages).reshape(batch, max_pages), dtype=torch.int32, device=DEV)
+    kc = tq.PagedCache(batch, hkv, P, n_pages, max_pages, w.bits_k, tq.LAYOUT_ROWS, sd, block_table=table,
+                       device=DEV)
+    vc = tq.PagedCache(batch, hkv, P, n_pages, max_pages, w.bits_v, tq.LAYOUT_GROUP8, sd, block_table=table,
+                       device=DEV)
+    zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
+    tq.paged_quantize_append_kv(kc, vc, x["k"][:, : ctx - 1].contiguous(), x["v"][:, : ctx - 1].contiguous(), zeros)
+    tq.paged_quantize_append_kv(kc, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(),
+                                zeros + (ctx - 1))
+    q = x["q"].contiguous()
+    scale = 1.0 / math.sqrt(128)
+    lens = torch.full((batch,), ctx, dtype=torch.int32, device=DEV)
+    got = tq.paged_decode_attn(kc, vc, q, lens, ctx, scale)
+    torch.cuda.synchronize()
+    out_g, lse_g = got.out.cpu().numpy(), got.lse.cpu().numpy()
+    s64 = signs.numpy().astype(np.float64)
+    tab = table.cpu().numpy()
+    for b, h in sorted({(0, 0), (batch - 1, hq - 1), (batch // 2, hq // 2 + 1)}):
+        kvh = h // g
+        planes = []
+        for cache, bits, xx in ((kc, w.bits_k, x["k"]), (vc, w.bits_v, x["v"])):
+            flat = tq.PackedCache(1, 1, ctx, bits, cache.layout, sd, device=DEV)
+            per = P * 16 * bits
+            for slot in range(max_pages):
+                flat.codes[slot * per:(slot + 1) * per] = cache.page_codes(int(tab[b, slot]), kvh)
+                flat.norms[slot * P:(slot + 1) * P] = cache.page_norms(int(tab[b, slot]), kvh)
+            near = parity.check_plane(flat, 0, 0, parity.to_f64(xx[b, :, kvh]), 0, s64, golden_codebooks[bits])
+            _say(f"  plane ({b},{kvh}) {bits}-bit: near-boundary coordinates {near}")
+            planes.append(parity.oracle_plane(flat, 0, 0, s64, golden_codebooks[bits], ctx))
+        q64 = parity.to_f64(q[b, h])
+        out, lse, _ = o.decode_attention(q64[None, None], planes[0][None, None], planes[1][None, None], scale)
+        worst = parity.check_rows(out_g[b, h][None, None], out, f"out[{b},{h}]")
+        assert abs(lse_g[b, h] - lse[0, 0]) <= 1e-3 * max(1.0, abs(lse[0, 0])), (b, h)
+        _say(f"  row ({b},{h}): rel err {worst:.2e}")
+
+
+def test_verify_full_size_sampled(golden_codebooks):
+    """verify8k: 4 positions appended through the key-and-value append, then causal
+    multi-query attention over the 8192-token cache."""
+    w = inputs.WORKLOADS["verify8k"]
+    _say("full-size multi-query")
+    batch, hq, hkv, ctx, g, n_q = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.group, w.n_q
+    signs = inputs.rotation_signs()
+    sd = signs.to(DEV)
+    x = inputs.generate(w, device=DEV)
+    kc = tq.PackedCache(batch, hkv, ctx, w.bits_k, tq.LAYOUT_ROWS, sd, device=DEV)
+    vc = tq.PackedCache(batch, hkv, ctx, w.bits_v, tq.LAYOUT_GROUP8, sd, device=DEV)
+    tq.quantize_append(kc, x["k"][:, : ctx - n_q].contiguous(), 0)
+    tq.quantize_append(vc, x["v"][:, : ctx - n_q].contiguous(), 0)
+    tq.quantize_append_kv(kc, vc, x["k"][:, ctx - n_q:].contiguous(), x["v"][:, ctx - n_q:].contiguous(), ctx - n_q)
+    q = x["q"].contiguous()
+    scale = 1.0 / math.sqrt(128)
+    got = tq.decode_attn_multi(kc, vc, q, ctx, scale)
+    torch.cuda.synchronize()
+    out_g, lse_g = got.out.cpu().numpy(), got.lse.cpu().numpy()
+    s64 = signs.numpy().astype(np.float64)
+    for kvh in (0, hkv - 1):
+        kh = parity.oracle_plane(kc, 0, kvh, s64, golden_codebooks[w.bits_k], ctx)
+        vh = parity.oracle_plane(vc, 0, kvh, s64, golden_codebooks[w.bits_v], ctx)
+        heads = list(range(kvh * g, (kvh + 1) * g))
+        q64 = parity.to_f64(q[0][:, heads])[None]                     # [1, n_q, g, d]
+        out, lse = o.multi_query_attention(q64, kh[None, None], vh[None, None], scale)
+        worst = parity.check_rows(out_g[0][:, heads], out[0], f"multi out kv head {kvh}")
+        assert np.allclose(lse_g[0][:, heads], lse[0], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[0])))
+        _say(f"  kv head {kvh}: rel err {worst:.2e}")
