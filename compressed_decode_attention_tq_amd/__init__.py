@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(PagedCacheStruct)
         L.tq_paged_quantize_append_kv.argtypes = [PP, PP, vp, vp, i32, vp, i32, vp]
         L.tq_paged_decode_attn.argtypes = [PP, PP, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.tq_paged_decode_attn_append.argtypes = [PP, PP, vp, vp, i32, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz,
+                                                  vp]
         L.tq_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.tq_paged_decode_workspace_bytes.restype = sz
         L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
                      "tq_decode_attn_multi", "tq_decode_attn_append", "tq_dequantize", "tq_probe_stream_read",
-                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn"):
+                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -408,4 +410,25 @@ def paged_decode_attn(k_cache: PagedCache, v_cache: PagedCache, q, seq_lens, max
         max_ctx_len, float(scale), _dev(buffers.out, "out"),
         _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn")
+    return buffers
+
+
+def paged_decode_attn_append(k_cache: PagedCache, v_cache: PagedCache, k_new, v_new, q, seq_lens, max_ctx_len: int,
+                             scale: float, buffers: PagedDecodeBuffers | None = None, stream=None):
+    """Quantize k_new, v_new [B, 1, Hkv, d] into position T_b - 1 of the paged caches and
+    attend, in one launch; returns the PagedDecodeBuffers (out, lse)."""
+    bsz, hq, d = q.shape
+    for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
+        if x.dim() != 4 or x.shape[0] != bsz or x.shape[1] != 1 or x.shape[2] != cache.n_kv_heads or x.shape[3] != d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    if buffers is None:
+        buffers = PagedDecodeBuffers(bsz, hq, k_cache.n_kv_heads, max_ctx_len, device=q.device, d=d)
+    ks, vs = k_cache.struct(), v_cache.struct()
+    _check(lib().tq_paged_decode_attn_append(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
+        _dev(q, "q"), _dtype_code(q.dtype), hq, _dev(seq_lens, "seq_lens"), max_ctx_len, float(scale),
+        _dev(buffers.out, "out"), _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn_append")
     return buffers

@@ -516,9 +516,10 @@ size_t tq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads,
   return workspace_layout_paged(batch, n_q_heads, n_kv_heads, max_ctx_len).total;
 }
 
-int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
-                         int n_q_heads, const int32_t *seq_lens, int max_ctx_len, float scale, float *out,
-                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
+static int paged_decode(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk, const void *xv,
+                        int x_dtype, const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens,
+                        int max_ctx_len, float scale, float *out, float *lse, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
   const int st = check_paged_pair(k, v);
   if (st != TQ_OK) return st;
   if (k->signs != v->signs) return TQ_ERR_INVALID_ARG;
@@ -561,7 +562,27 @@ int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const
   a.block_table = k->block_table;
   a.max_pages = k->max_pages;
   a.n_pages = k->n_pages;
+  a.xk = xk;
+  a.xv = xv;
+  a.x_dtype = x_dtype;
   return hip_status(launch_decode_fused_paged(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, const int32_t *seq_lens, int max_ctx_len, float scale, float *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return paged_decode(k, v, nullptr, nullptr, TQ_BF16, q, q_dtype, n_q_heads, seq_lens, max_ctx_len, scale, out,
+                      lse, workspace, workspace_bytes, hip_stream);
+}
+
+int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk, const void *xv,
+                                int x_dtype, const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens,
+                                int max_ctx_len, float scale, float *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *hip_stream) {
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  return paged_decode(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, max_ctx_len, scale, out, lse,
+                      workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

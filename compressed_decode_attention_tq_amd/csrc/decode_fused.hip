@@ -166,7 +166,9 @@ struct NewToken {
   uint32_t vword;   // value cache: the group word that lane's coordinates go into
 };
 
-__device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key, int b, int kvh, int t, int lane) {
+// b: the sequence (input row); pb, pt: the plane (sequence, or pool page) and the position in it
+__device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key, int b, int kvh, int pb, int pt,
+                                                   int lane) {
   const void *x = key ? a.xk : a.xv;
   const size_t xi = ((size_t)b * a.n_kv_heads + kvh) * kD + 2 * lane;
   NewToken n{0u, 0u, 0u};
@@ -177,12 +179,12 @@ __device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key
   } else {
     n.x0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xi);
   }
-  if (!key) n.vword = reinterpret_cast<const uint32_t *>(a.v.plane(b, kvh) + (size_t)(t >> 3) * 256)[lane];
+  if (!key) n.vword = reinterpret_cast<const uint32_t *>(a.v.plane(pb, kvh) + (size_t)(pt >> 3) * 256)[lane];
   return n;
 }
 
 template <int BK>
-__device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &in, int b, int kvh, int t, int lane,
+__device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &in, int pb, int kvh, int t, int lane,
                                 uint8_t *scratch) {
   const CacheView &c = key ? a.k : a.v;
   float x0, x1;
@@ -211,8 +213,8 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
     c0 += u0 > tj ? 1u : 0u;
     c1 += u1 > tj ? 1u : 0u;
   }
-  if (lane == 0) c.norm_plane(b, kvh)[t] = float_to_half_bits(n);
-  uint8_t *plane = c.plane(b, kvh);
+  if (lane == 0) c.norm_plane(pb, kvh)[t] = float_to_half_bits(n);
+  uint8_t *plane = c.plane(pb, kvh);
   if (key) {
     if (BK == 4) {
       plane[(size_t)t * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
@@ -247,7 +249,7 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
-  static_assert(!PAGED || !(SPARSE || MULTI || APPEND), "paged caches: dense single-query decode");
+  static_assert(!PAGED || !(SPARSE || MULTI), "paged caches: dense single-query decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -346,14 +348,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // first.  Only that wave ever loads those bytes, so no other wave waits for the stores:
     // the writer waits for its own stores to complete after the first barrier and only then
     // issues its first key tile if that tile holds T - 1; later tiles are loaded later still.
+    // Paged: the token goes to its slot of the page the table names; with no page there, it
+    // is not written (and its tile reads zeros).
     const bool has_new = APPEND && T >= 1 && T - 1 >= t_begin && T - 1 < t_end;
     const int new_tile = has_new ? (T - 1 - t_begin) / kTile : -1;
-    const bool appends = has_new && new_tile % kWaves == wave;
+    bool appends = has_new && new_tile % kWaves == wave;
+    int new_pb = b, new_pt = T - 1;  // plane and position of the new token
+    if constexpr (PAGED) {
+      if (appends) {
+        const int P = a.k.capacity, slot = (T - 1) / P;
+        new_pb = __builtin_amdgcn_readfirstlane(a.block_table[(size_t)b * a.max_pages + slot]);
+        new_pt = T - 1 - slot * P;
+        appends = new_pb >= 0 && new_pb < a.n_pages;
+      }
+    }
     const bool defer_keys = appends && new_tile == wave;
     NewToken ntk{0u, 0u, 0u}, ntv{0u, 0u, 0u};
     if (appends) {
-      ntk = new_token_load(a, true, b, kvh, T - 1, lane);
-      ntv = new_token_load(a, false, b, kvh, T - 1, lane);
+      ntk = new_token_load(a, true, b, kvh, new_pb, new_pt, lane);
+      ntv = new_token_load(a, false, b, kvh, new_pb, new_pt, lane);
     }
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
@@ -378,8 +391,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
     // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
     if (appends) {
-      new_token_store<BK>(a, true, ntk, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
-      new_token_store<BK>(a, false, ntv, b, kvh, T - 1, lane, lds + kWBase + wave * 4096);
+      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, lds + kWBase + wave * 4096);
+      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, lds + kWBase + wave * 4096);
     }
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
@@ -938,6 +951,9 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  if (a.xk != nullptr)  // append the new token in the same launch
+    return a.k.bits == 4 ? launch_nh<4, false, false, true, true>(a, (int)items, stream)
+                         : launch_nh<3, false, false, true, true>(a, (int)items, stream);
   return a.k.bits == 4 ? launch_nh<4, false, false, false, true>(a, (int)items, stream)
                        : launch_nh<3, false, false, false, true>(a, (int)items, stream);
 }

@@ -279,6 +279,19 @@ int tq_paged_decode_attn(const tq_paged_cache *k, const tq_paged_cache *v, const
                          int n_q_heads, const int32_t *seq_lens, int max_ctx_len, float scale, float *out,
                          float *lse, void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* A paged decode step in one call: the new key and value of every sequence b with
+ * T_b = clamp(seq_lens[b], 0, max_ctx_len) >= 1 are quantized into position T_b - 1 (as
+ * tq_paged_quantize_append_kv with start_pos = T_b - 1, n_tokens = 1, skipped where the
+ * table has no page), then tq_paged_decode_attn runs over positions 0 .. T_b - 1.  One
+ * launch: the wave that reads position T_b - 1 writes it first (as tq_decode_attn_append).
+ *   xk, xv  device in [batch][1][n_kv_heads][d] of x_dtype, 16-byte aligned
+ *   the other arguments as for tq_paged_decode_attn.
+ * Errors: as tq_paged_decode_attn. */
+int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk, const void *xv,
+                                int x_dtype, const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens,
+                                int max_ctx_len, float scale, float *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *hip_stream);
+
 /* Workspace bytes tq_paged_decode_attn needs (0 for invalid arguments). */
 size_t tq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int max_ctx_len);
 

@@ -252,6 +252,15 @@ def test_paged_argument_validation():
     assert dec(_paged(bits=8), v) == tq.TQ_ERR_UNSUPPORTED
     assert dec(k, _paged(layout=1, bits=3)) == tq.TQ_ERR_UNSUPPORTED
 
+    def dec_app(xk=x, xdt=1, wsb=ws):
+        return L.tq_paged_decode_attn_append(ctypes.byref(k), ctypes.byref(v), xk, x + 0x80000, xdt, FAKE + 0x600000,
+                                             1, 16, sp, 4096, 0.088, FAKE + 0x700000, None, FAKE + 0x800000, wsb, None)
+
+    assert dec_app(xk=0) == tq.TQ_ERR_INVALID_ARG
+    assert dec_app(xk=x + 8) == tq.TQ_ERR_INVALID_ARG
+    assert dec_app(xdt=4) == tq.TQ_ERR_INVALID_ARG
+    assert dec_app(wsb=16) == tq.TQ_ERR_WORKSPACE
+
 
 def test_probe_rejects_bad_arguments():
     f = tq.lib().tq_probe_stream_read

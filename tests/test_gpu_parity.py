@@ -338,11 +338,14 @@ def test_decode_append_matches_oracle(case, signs, golden_codebooks):
     _append_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, x_dtype=xdt)
 
 
-def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtype=None, hole=None, seed=0):
+def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtype=None, hole=None, seed=0,
+                fused=False):
     """Paged caches with shuffled pages (and optionally one table entry of no page) filled by
-    the paged append (a long call, then a short one with per-sequence starts); the pages,
-    gathered in table order, must hold the oracle's codes, and paged decode must equal the
-    contiguous decode on the gathered cache bit for bit and the oracle within tolerance."""
+    the paged append (a long call, then a decode step with per-sequence starts: the paged
+    append and paged decode, or, fused, the one-launch paged append-and-attend over a slot
+    that held garbage); the pages, gathered in table order, must hold the oracle's codes,
+    and paged decode must equal the contiguous decode on the gathered cache bit for bit and
+    the oracle within tolerance."""
     max_ctx = max(seq_lens)
     max_pages = (max_ctx + page - 1) // page + 1
     n_pages = batch * max_pages + 3
@@ -363,12 +366,25 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
     # every position in one call, then each sequence's last position again (a decode step:
     # per-sequence starts, T_b = 0 gives start -1, which is skipped)
     zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
-    tq.paged_quantize_append_kv(kc, vc, k.contiguous().to(DEV), v.contiguous().to(DEV), zeros)
+    k_fill, v_fill = k.clone(), v.clone()
+    if fused:  # garbage in each sequence's last slot: the fused step must overwrite it
+        for b, tb in enumerate(seq_lens):
+            if tb >= 1:
+                k_fill[b, tb - 1] = k[b, 0] * -3.0
+                v_fill[b, tb - 1] = v[b, 0] * 2.5
+    tq.paged_quantize_append_kv(kc, vc, k_fill.contiguous().to(DEV), v_fill.contiguous().to(DEV), zeros)
     last = torch.tensor([tb - 1 for tb in seq_lens], dtype=torch.int32)
     idx = last.clamp(min=0).long()
     k1 = k[torch.arange(batch), idx].unsqueeze(1).contiguous()
     v1 = v[torch.arange(batch), idx].unsqueeze(1).contiguous()
-    tq.paged_quantize_append_kv(kc, vc, k1.to(DEV), v1.to(DEV), last.to(DEV))
+    sl = torch.tensor(list(seq_lens), dtype=torch.int32, device=DEV)
+    q = g["q"].to(DEV).contiguous()
+    scale = 1.0 / math.sqrt(128)
+    if fused:
+        got = tq.paged_decode_attn_append(kc, vc, k1.to(DEV), v1.to(DEV), q, sl, max_ctx, scale)
+    else:
+        tq.paged_quantize_append_kv(kc, vc, k1.to(DEV), v1.to(DEV), last.to(DEV))
+        got = tq.paged_decode_attn(kc, vc, q, sl, max_ctx, scale)
     torch.cuda.synchronize()
     # the gathered contiguous copy: slot p of sequence b = page table[b, p]
     cap = max_pages * page
@@ -396,10 +412,6 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
                     upto = min(upto, hole[1] * page)     # positions from the hole on were skipped
                 if upto > 0:
                     parity.check_plane(fc, b, h, parity.to_f64(x[b, :upto, h]), 0, s64, table_b)
-    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    q = g["q"].to(DEV).contiguous()
-    scale = 1.0 / math.sqrt(128)
-    got = tq.paged_decode_attn(kc, vc, q, sl, max_ctx, scale)
     ref = tq.decode_attn(kf, vf, q, max_ctx, scale, seq_lens=sl)
     torch.cuda.synchronize()
     assert torch.equal(got.out, ref.out) and torch.equal(got.lse, ref.lse)
@@ -415,18 +427,22 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
 
 
 @pytest.mark.parametrize("case", [
-    # (workload, batch, hq, hkv, page tokens, seq_lens, bits_k, x dtype, hole)
-    ("llama8k", 3, 32, 8, 64, [700, 1, 333], 4, None, (0, 5)),
-    ("batch32k", 2, 8, 2, 256, [1300, 1024], 3, None, None),
-    ("ctx131k", 2, 16, 2, 128, [1500, 0], 4, None, None),
-    ("llama8k", 2, 4, 4, 64, [64, 65], 4, "f32", None),
-    ("llama8k", 1, 8, 2, 512, [2100], 3, "f16", (0, 3)),
+    # (workload, batch, hq, hkv, page tokens, seq_lens, bits_k, x dtype, hole, fused step)
+    ("llama8k", 3, 32, 8, 64, [700, 1, 333], 4, None, (0, 5), False),
+    ("batch32k", 2, 8, 2, 256, [1300, 1024], 3, None, None, False),
+    ("ctx131k", 2, 16, 2, 128, [1500, 0], 4, None, None, False),
+    ("llama8k", 2, 4, 4, 64, [64, 65], 4, "f32", None, False),
+    ("llama8k", 1, 8, 2, 512, [2100], 3, "f16", (0, 3), False),
+    ("llama8k", 3, 32, 8, 64, [700, 1, 0], 4, None, None, True),
+    ("batch32k", 2, 8, 2, 256, [1300, 513], 3, "f32", (1, 2), True),
+    ("ctx131k", 1, 16, 2, 128, [1500], 4, None, None, True),
 ])
 def test_paged_cache_matches_contiguous_and_oracle(case, signs, golden_codebooks):
-    name, batch, hq, hkv, page, lens, bk, xdt, hole = case
+    name, batch, hq, hkv, page, lens, bk, xdt, hole, fused = case
     _say("paged", case)
     xdt = {None: None, "f32": torch.float32, "f16": torch.float16}[xdt]
-    _paged_case(inputs.WORKLOADS[name], signs, golden_codebooks, batch, hq, hkv, page, lens, bk, x_dtype=xdt, hole=hole)
+    _paged_case(inputs.WORKLOADS[name], signs, golden_codebooks, batch, hq, hkv, page, lens, bk, x_dtype=xdt, hole=hole,
+                fused=fused)
 
 
 def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens=None, q_dtype=None):
