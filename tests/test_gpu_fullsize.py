@@ -102,7 +102,8 @@ def test_prefill_layer_full_size_sampled(layer, golden_codebooks):
 
 def test_paged_full_size_sampled(golden_codebooks):
     """paged32k: the batched long-context shape in 256-token pages in random pool order,
-    filled through the paged append, one more token appended, then paged decode."""
+    filled through the paged append, then the last token appended and attended in the one
+    fused paged launch the benchmark times."""
     w = inputs.WORKLOADS["paged32k"]
     _say("full-size paged decode")
     batch, hq, hkv, ctx, g, P = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.group, w.page_tokens
@@ -119,12 +120,11 @@ def test_paged_full_size_sampled(golden_codebooks):
                        device=DEV)
     zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
     tq.paged_quantize_append_kv(kc, vc, x["k"][:, : ctx - 1].contiguous(), x["v"][:, : ctx - 1].contiguous(), zeros)
-    tq.paged_quantize_append_kv(kc, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(),
-                                zeros + (ctx - 1))
     q = x["q"].contiguous()
     scale = 1.0 / math.sqrt(128)
     lens = torch.full((batch,), ctx, dtype=torch.int32, device=DEV)
-    got = tq.paged_decode_attn(kc, vc, q, lens, ctx, scale)
+    got = tq.paged_decode_attn_append(kc, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(), q,
+                                      lens, ctx, scale)
     torch.cuda.synchronize()
     out_g, lse_g = got.out.cpu().numpy(), got.lse.cpu().numpy()
     s64 = signs.numpy().astype(np.float64)
