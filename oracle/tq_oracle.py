@@ -398,6 +398,30 @@ def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None):
     return out, lse
 
 
+def ip_search(q, codes, norms16, signs, centroids, k: int):
+    """Approximate inner-product nearest-neighbour search with the same quantizer ([tq-80]
+    §技术背景与学术渊源: the method also serves approximate nearest-neighbour search, with
+    higher recall than product quantization and next to no indexing time, the codebook
+    being data-independent).
+
+    q: [Q, d] queries; codes [N, d], norms16 [N]: the quantized database.  The score of
+    database vector t for query j is the inner product with its dequantized vector,
+      s_{j,t} = q_j . x_hat_t,   x_hat_t = n16_t R^T c[codes_t];
+    the result for query j is the min(k, N) indices of largest score in descending score
+    order, equal scores by ascending index.
+    Returns (idx [Q, k'] int64, scores [Q, k'] fp64, all scores [Q, N] fp64)."""
+    xh = dequantize(codes, norms16, signs, centroids)
+    qq = np.asarray(q, dtype=np.float64)
+    s = qq @ xh.T
+    n = xh.shape[0]
+    kk = min(int(k), n)
+    idx = np.zeros((qq.shape[0], kk), dtype=np.int64)
+    for j in range(qq.shape[0]):
+        order = np.lexsort((np.arange(n), -s[j]))   # primary key: -score; then index
+        idx[j] = order[:kk]
+    return idx, np.take_along_axis(s, idx, axis=1), s
+
+
 def sparse_v_borderline(scores, lse, tau: float, rel: float = 1e-3) -> np.ndarray:
     """Rows whose keep decision is within the score tolerance of the threshold.
 

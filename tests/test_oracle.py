@@ -412,3 +412,54 @@ def test_byte_accounting_against_pages():
     assert 1 - (per[4] + per[2]) / (2 * fp16) > fig["k4v2_saving_min"]
     assert abs(1 - (per[3] + per[2]) / (2 * fp16) - fig["k3v2_saving"]) < 0.005
     assert (D * 4 // 8) / fp16 == fig["four_bit_cache_fraction"]
+
+
+# ------------------------------------------------------------------ inner-product search
+
+
+def test_ip_search_pins(golden_codebooks):
+    """Inner-product search: (1) the scores equal the rotated-domain form n16 * (R q) . c[idx]
+    (R orthogonal), computed from the codes without dequantizing; (2) database vectors that
+    are positive multiples of one direction share their codes, so the ranking is that of the
+    stored norms, largest first for a query along the direction and smallest first for its
+    opposite; (3) duplicated vectors tie and come out by ascending index; (4) a brute-force
+    double loop on a tiny case; (5) k beyond N returns all N."""
+    rng = np.random.default_rng(11)
+    d = 128
+    signs = rng.choice([-1.0, 1.0], d)
+    c, t = golden_codebooks[4]
+    x = rng.standard_normal((40, d)) * rng.uniform(0.5, 3.0, (40, 1))
+    codes, n16, _ = o.quantize(x, signs, c, t)
+    q = rng.standard_normal((3, d))
+    idx, sc, s_all = o.ip_search(q, codes, n16, signs, c, 7)
+    rot = (q @ o.rotation_matrix(signs).T)                       # R q per query
+    s_rot = n16.astype(np.float64)[None, :] * (rot @ np.asarray(c, dtype=np.float64)[codes].T)
+    assert np.allclose(s_all, s_rot, rtol=0, atol=1e-11 * np.abs(s_rot).max())
+    # (2) multiples of one direction: lambda_t = 1 + t / 8 is exact in fp16
+    v = rng.standard_normal(d)
+    lam = 1.0 + np.arange(24)[rng.permutation(24)] / 8.0
+    cm, nm, _ = o.quantize(lam[:, None] * v[None, :], signs, c, t)
+    assert np.all(cm == cm[0])
+    i_up, _, _ = o.ip_search(v[None], cm, nm, signs, c, 5)
+    i_dn, _, _ = o.ip_search(-v[None], cm, nm, signs, c, 5)
+    assert list(i_up[0]) == list(np.argsort(-lam)[:5])
+    assert list(i_dn[0]) == list(np.argsort(lam)[:5])
+    # (3) ties: vector 5 repeated at 9 and 17
+    x3 = x.copy()
+    x3[9] = x3[5]
+    x3[17] = x3[5]
+    c3, n3, _ = o.quantize(x3, signs, c, t)
+    qq = x3[5][None]
+    i3, s3, _ = o.ip_search(qq, c3, n3, signs, c, 40)
+    pos = [list(i3[0]).index(j) for j in (5, 9, 17)]
+    assert s3[0][pos[0]] == s3[0][pos[1]] == s3[0][pos[2]]
+    assert pos == sorted(pos) and pos[1] == pos[0] + 1 and pos[2] == pos[1] + 1
+    # (4) brute force
+    xh = o.dequantize(codes[:6], n16[:6], signs, c)
+    qb = q[1]
+    sb = [sum(qb[i] * xh[r][i] for i in range(d)) for r in range(6)]
+    ib, _, _ = o.ip_search(qb[None], codes[:6], n16[:6], signs, c, 4)
+    assert list(ib[0]) == sorted(range(6), key=lambda r: (-sb[r], r))[:4]
+    # (5)
+    i5, _, _ = o.ip_search(q[:1], codes[:3], n16[:3], signs, c, 10)
+    assert i5.shape == (1, 3)
