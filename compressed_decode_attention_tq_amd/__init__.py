@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.tq_paged_decode_attn.argtypes = [PP, PP, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
         L.tq_paged_decode_attn_append.argtypes = [PP, PP, vp, vp, i32, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz,
                                                   vp]
+        L.tq_ip_search.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.tq_ip_search_workspace_bytes.argtypes = [i32, i32, i32]
+        L.tq_ip_search_workspace_bytes.restype = sz
         L.tq_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.tq_paged_decode_workspace_bytes.restype = sz
         L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
@@ -88,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
                      "tq_decode_attn_multi", "tq_decode_attn_append", "tq_dequantize", "tq_probe_stream_read",
-                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append"):
+                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -431,4 +434,37 @@ def paged_decode_attn_append(k_cache: PagedCache, v_cache: PagedCache, k_new, v_
         _dev(q, "q"), _dtype_code(q.dtype), hq, _dev(seq_lens, "seq_lens"), max_ctx_len, float(scale),
         _dev(buffers.out, "out"), _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn_append")
+    return buffers
+
+
+def ip_search_workspace_bytes(n_queries: int, n_vectors: int, top_k: int) -> int:
+    return int(lib().tq_ip_search_workspace_bytes(n_queries, n_vectors, top_k))
+
+
+class SearchBuffers:
+    """Caller-owned outputs and workspace of one inner-product search shape."""
+
+    def __init__(self, n_queries, n_vectors, top_k, device="cuda"):
+        torch = _torch()
+        self.idx = torch.empty((n_queries, top_k), dtype=torch.int32, device=device)
+        self.score = torch.empty((n_queries, top_k), dtype=torch.float32, device=device)
+        nbytes = ip_search_workspace_bytes(n_queries, n_vectors, top_k)
+        if nbytes == 0:
+            raise TQError(TQ_ERR_UNSUPPORTED, "tq_ip_search_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.ws_bytes = nbytes
+
+
+def ip_search(db: PackedCache, q, n_vectors: int, top_k: int, buffers: SearchBuffers | None = None, stream=None):
+    """Top-k inner-product search of q [Q, d] over vectors 0 .. n_vectors - 1 of the database
+    cache (batch 1, one kv head, rows); returns the SearchBuffers (idx, score [Q, top_k])."""
+    nq, d = q.shape
+    if buffers is None:
+        buffers = SearchBuffers(nq, n_vectors, top_k, device=q.device)
+    st = db.struct()
+    _check(lib().tq_ip_search(ctypes.byref(st), _dev(q, "q"), _dtype_code(q.dtype), nq, n_vectors, top_k,
+                              _dev(buffers.idx, "idx"), _dev(buffers.score, "score"), ctypes.c_void_p(buffers.ws_ptr),
+                              buffers.ws_bytes, _stream_ptr(stream)), "tq_ip_search")
     return buffers

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["api.hip", "quantize.hip", "quantize_kv.hip", "append_small.hip", "decode_generic.hip", "decode_mfma.hip", "decode_fused.hip",
+SOURCES = ["api.hip", "quantize.hip", "quantize_kv.hip", "append_small.hip", "ip_search.hip", "decode_generic.hip", "decode_mfma.hip", "decode_fused.hip",
            "probe.hip", "codebook.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -176,6 +176,29 @@ WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads,
   return w;
 }
 
+struct SearchLayout {
+  size_t scores, cand_s, cand_i, total;
+};
+
+SearchLayout search_layout(int n_q, int n, int k) {
+  const size_t n_cand = (size_t)((n + kSearchChunk - 1) / kSearchChunk) * k;
+  SearchLayout w{};
+  size_t off = 0;
+  w.scores = off;
+  off = align_up(off + (size_t)n_q * n * sizeof(float), 256);
+  w.cand_s = off;
+  off = align_up(off + (size_t)n_q * n_cand * sizeof(float), 256);
+  w.cand_i = off;
+  off = align_up(off + (size_t)n_q * n_cand * sizeof(int32_t), 256);
+  w.total = off;
+  return w;
+}
+
+bool search_shape_ok(int n_q, int n, int k) {
+  return n_q >= 1 && n_q <= 65535 * 8 && n >= 1 && k >= 1 && k <= kSearchMaxK &&
+         (long)((n + kSearchChunk - 1) / kSearchChunk) * k <= kSearchChunk;
+}
+
 int check_paged(const tq_paged_cache *c) {
   if (c == nullptr) return TQ_ERR_INVALID_ARG;
   if (c->codes == nullptr || c->norms == nullptr || c->block_table == nullptr || c->centroids == nullptr ||
@@ -583,6 +606,32 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
     return TQ_ERR_INVALID_ARG;
   return paged_decode(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, max_ctx_len, scale, out, lse,
                       workspace, workspace_bytes, hip_stream);
+}
+
+size_t tq_ip_search_workspace_bytes(int n_queries, int n_vectors, int top_k) {
+  if (!search_shape_ok(n_queries, n_vectors, top_k)) return 0;
+  return search_layout(n_queries, n_vectors, top_k).total;
+}
+
+int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, int n_vectors, int top_k,
+                 int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  const int st = check_cache(db);
+  if (st != TQ_OK) return st;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out_idx == nullptr || out_score == nullptr || !aligned(out_idx, 4) || !aligned(out_score, 4))
+    return TQ_ERR_INVALID_ARG;
+  if (n_queries < 1 || n_vectors < 1 || top_k < 1) return TQ_ERR_INVALID_ARG;
+  if (db->batch != 1 || db->n_kv_heads != 1 || db->layout != TQ_LAYOUT_ROWS || (db->bits != 3 && db->bits != 4))
+    return TQ_ERR_UNSUPPORTED;
+  if (n_vectors > db->capacity) return TQ_ERR_CAPACITY;
+  if (!search_shape_ok(n_queries, n_vectors, top_k)) return TQ_ERR_UNSUPPORTED;
+  const SearchLayout w = search_layout(n_queries, n_vectors, top_k);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  return hip_status(launch_ip_search(view_of(db), q, q_dtype, n_queries, n_vectors, top_k, out_idx, out_score,
+                                     reinterpret_cast<float *>(ws + w.scores), reinterpret_cast<float *>(ws + w.cand_s),
+                                     reinterpret_cast<int32_t *>(ws + w.cand_i), static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

@@ -110,6 +110,13 @@ constexpr int kPagedMaxSplit = 8 * 64 * 64;
 SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len);
 WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len);
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
+// Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
+// db, 3- or 4-bit rows), then the k best per query.  scores [n_q][n], cand_s / cand_i
+// [n_q][ceil(n / 8192) * k] are caller scratch.
+hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
+                            float *out_score, float *scores, float *cand_s, int32_t *cand_i, hipStream_t stream);
+constexpr int kSearchChunk = 8192;
+constexpr int kSearchMaxK = 64;
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -164,3 +164,26 @@ def layer_bits(w: Workload, layer: int) -> tuple:
     if layer in w.boundary_layers:
         return w.boundary_bits, w.boundary_bits
     return w.bits_k, w.bits_v
+
+
+# Inner-product search: a database of n vectors drawn around `centers` cluster centres
+# (centre N(0, 1) plus N(0, spread^2) noise, the shape of an embedding collection) and
+# queries drawn the same way around random centres.  No public search benchmark is
+# available offline; this stands in for one.
+SEARCH = {
+    "search1m": dict(seed=8, n=1 << 20, n_queries=8, top_k=10, bits=4, centers=1024, spread=0.5,
+                     dtype=torch.bfloat16),
+}
+
+
+def generate_search(spec: dict, device="cpu", n=None, n_queries=None) -> dict:
+    """Database x [n, d] and queries [n_queries, d] (fp32 drawn, rounded to spec dtype)."""
+    n = spec["n"] if n is None else n
+    nq = spec["n_queries"] if n_queries is None else n_queries
+    g = torch.Generator(device=device).manual_seed(spec["seed"] * 1000)
+    centers = torch.randn((spec["centers"], D), generator=g, device=device)
+    which = torch.randint(0, spec["centers"], (n,), generator=g, device=device)
+    x = centers[which] + spec["spread"] * torch.randn((n, D), generator=g, device=device)
+    qc = torch.randint(0, spec["centers"], (nq,), generator=g, device=device)
+    q = centers[qc] + spec["spread"] * torch.randn((nq, D), generator=g, device=device)
+    return {"x": x.to(spec["dtype"]), "q": q.to(spec["dtype"])}

@@ -292,6 +292,25 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
                                 int max_ctx_len, float scale, float *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *hip_stream);
 
+/* Approximate inner-product nearest-neighbour search with the same quantizer ([tq-80]
+ * §技术背景与学术渊源): the database is plane (batch 0, kv head 0) of `db` (batch = 1,
+ * n_kv_heads = 1, ROWS layout, 3- or 4-bit codes, vectors 0 .. n_vectors - 1 quantized by
+ * tq_quantize_append).  For query j the score of vector t is the inner product with its
+ * dequantized vector, s = q_j . x_hat_t = n16_t (R q_j) . c[idx_t]; the result is the top_k
+ * indices of largest score, descending, equal scores by ascending index, with their scores
+ * (fp32, as the decode kernels compute them: within 1e-3 relative of the exact value).
+ *   q          device in [n_queries][d] of q_dtype
+ *   out_idx    device out int32 [n_queries][top_k] (-1 past n_vectors)
+ *   out_score  device out fp32 [n_queries][top_k] (-inf past n_vectors)
+ *   workspace  device scratch of tq_ip_search_workspace_bytes(...) bytes, 256-byte aligned
+ * 1 <= top_k <= 64 and ceil(n_vectors / 8192) * top_k <= 8192, else TQ_ERR_UNSUPPORTED.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, int n_vectors, int top_k,
+                 int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes tq_ip_search needs (0 for invalid arguments). */
+size_t tq_ip_search_workspace_bytes(int n_queries, int n_vectors, int top_k);
+
 /* Workspace bytes tq_paged_decode_attn needs (0 for invalid arguments). */
 size_t tq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int max_ctx_len);
 

@@ -262,6 +262,30 @@ def test_paged_argument_validation():
     assert dec_app(wsb=16) == tq.TQ_ERR_WORKSPACE
 
 
+def test_ip_search_argument_validation():
+    L = tq.lib()
+    db = _cache(batch=1, n_kv_heads=1, capacity=65536)
+    ws = tq.ip_search_workspace_bytes(4, 65536, 10)
+    assert ws > 0
+    assert tq.ip_search_workspace_bytes(4, 65536, 65) == 0          # top_k above 64
+    assert tq.ip_search_workspace_bytes(4, 2 << 20, 64) == 0        # 256 chunks x 64 candidates
+
+    def srch(db=db, nq=4, n=65536, k=10, wsb=ws, out=FAKE + 0x700000, qdt=1):
+        return L.tq_ip_search(ctypes.byref(db), FAKE + 0x600000, qdt, nq, n, k, out, FAKE + 0x780000,
+                              FAKE + 0x800000, wsb, None)
+
+    assert srch(n=65537) == tq.TQ_ERR_CAPACITY
+    assert srch(k=0) == tq.TQ_ERR_INVALID_ARG
+    assert srch(k=65) == tq.TQ_ERR_UNSUPPORTED
+    assert srch(nq=0) == tq.TQ_ERR_INVALID_ARG
+    assert srch(wsb=16) == tq.TQ_ERR_WORKSPACE
+    assert srch(out=0) == tq.TQ_ERR_INVALID_ARG
+    assert srch(qdt=3) == tq.TQ_ERR_INVALID_ARG
+    assert srch(db=_cache(batch=2, n_kv_heads=1, capacity=65536)) == tq.TQ_ERR_UNSUPPORTED
+    assert srch(db=_cache(batch=1, n_kv_heads=1, capacity=65536, bits=2)) == tq.TQ_ERR_UNSUPPORTED
+    assert srch(db=_cache(batch=1, n_kv_heads=1, capacity=65536, layout=1)) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_probe_rejects_bad_arguments():
     f = tq.lib().tq_probe_stream_read
     assert f(None, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG

@@ -567,3 +567,68 @@ def test_stream_read_probe_runs():
     tq.probe_stream_read(buf, sink)
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
+
+
+# ------------------------------------------------------------------ inner-product search
+
+
+def _search_case(signs, golden, n, nq, k, bits, q_dtype=None, dup=False, seed=0):
+    spec = dict(inputs.SEARCH["search1m"])
+    spec["seed"] = 20 + seed
+    g = inputs.generate_search(spec, device="cpu", n=n, n_queries=nq)
+    x, q = g["x"], g["q"]
+    if dup:  # exact duplicates: equal codes, equal scores, ascending indices
+        x[7] = x[3]
+        x[n - 1] = x[3]
+        q[0] = x[3]
+    if q_dtype is not None:
+        q = q.to(q_dtype)
+    cap = (n + 63) // 64 * 64
+    db = _new_cache(1, 1, cap, bits, 0, signs)
+    _fill(db, x[None, :, None, :].contiguous().to(DEV))
+    res = tq.ip_search(db, q.to(DEV).contiguous(), n, k)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    c, _ = golden[bits]
+    codes, _ = parity.gpu_plane_codes(db, 0, 0, cap)
+    n16 = parity.gpu_plane_norms(db, 0, 0, n).astype(np.float16)
+    idx_o, sc_o, s_all = o.ip_search(parity.to_f64(q), codes[:n], n16, s64, c, k)
+    idx_g, sc_g = res.idx.cpu().numpy(), res.score.cpu().numpy()
+    kk = min(k, n)
+    for j in range(nq):
+        tol = 1e-3 * np.abs(s_all[j]).max()
+        got = idx_g[j, :kk]
+        assert np.all(got >= 0) and len(set(got.tolist())) == kk, (j, got)
+        # scores of the returned vectors, and the order the GPU gave them
+        assert np.all(np.abs(sc_g[j, :kk] - s_all[j][got]) <= tol), j
+        assert np.all(np.diff(sc_g[j, :kk]) <= 0), j
+        for a in range(kk - 1):
+            if sc_g[j, a] == sc_g[j, a + 1]:
+                assert got[a] < got[a + 1], (j, a)
+        # the set: everything clearly above the k-th oracle score is found, nothing clearly
+        # below it is returned (near-ties may go either way)
+        kth = sc_o[j, kk - 1]
+        assert np.all(s_all[j][got] >= kth - 2 * tol), j
+        must = np.nonzero(s_all[j] > kth + 2 * tol)[0]
+        assert set(must.tolist()) <= set(got.tolist()), j
+        if k > n:
+            assert np.all(idx_g[j, n:] == -1) and np.all(np.isneginf(sc_g[j, n:]))
+    if dup:
+        got0 = idx_g[0, :kk].tolist()
+        assert got0[:3] == [3, 7, n - 1] and sc_g[0, 0] == sc_g[0, 1] == sc_g[0, 2]
+    return idx_g
+
+
+@pytest.mark.parametrize("case", [
+    # (n vectors, queries, top_k, bits, q dtype, duplicates)
+    (20000, 11, 10, 4, None, False),
+    (20000, 8, 64, 3, None, False),
+    (9000, 3, 5, 4, "f32", True),
+    (40, 2, 64, 4, None, False),          # fewer vectors than k
+    (8192, 1, 1, 3, "f16", False),
+])
+def test_ip_search_matches_oracle(case, signs, golden_codebooks):
+    n, nq, k, bits, qdt, dup = case
+    _say("ip search", case)
+    qdt = {None: None, "f32": torch.float32, "f16": torch.float16}[qdt]
+    _search_case(signs, golden_codebooks, n, nq, k, bits, q_dtype=qdt, dup=dup)
