@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama8k",
-                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k"])
+                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k", "search1m"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -150,15 +150,27 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    if args.workload in inputs.SEARCH:
+        digest = kernel_sources_digest()
+        result = bench_search(args, inputs.SEARCH[args.workload], inputs.rotation_signs().to(dev), dev, tq, inputs,
+                              torch, np, log)
+        stream = stream_read_gbs(torch, tq, log)
+        result["roofline"]["stream_read_gbs"] = stream
+        result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
+        result.pop("_kernel", None)
+        result["sources_digest"] = digest
+        print(json.dumps(result), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     tau = w.tau if args.tau is None else args.tau
     if args.workload == "batch32k" and args.tau is None:
         tau = 0.0          # reported dense by default; pass --tau 1e-4 for Sparse V
     signs = inputs.rotation_signs().to(dev)
     digest = kernel_sources_digest()
-
-    def log(*a):
-        print(*a, file=sys.stderr, flush=True)
 
     if args.workload == "prefill":
         result = bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log)
@@ -485,6 +497,84 @@ def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
         gathered = (_GatheredPlanes(kc, row, torch), _GatheredPlanes(vc, row, torch))
         result["cpu_baseline"] = cpu_baseline_decode(w, 0.0, gathered, host_k, host_v, q, signs, np, torch, log)
     return result
+
+
+def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):
+    """Inner-product nearest-neighbour search: a step is one tq_ip_search call for the
+    queries over the whole quantized database (score, chunk top-k and merge kernels)."""
+    n, nq, k, bits = spec["n"], spec["n_queries"], spec["top_k"], spec["bits"]
+    per_copy = tq.code_bytes(D, bits, 1, 1, n) + 2 * n
+    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    log(f"[bench] search n={n} queries={nq} top_k={k} bits={bits} copies={copies} db/copy={per_copy / 1e6:.1f} MB "
+        f"({'eager launches' if args.eager else 'HIP graph replay'})")
+    g = inputs.generate_search(spec, device=dev)
+    x, q = g["x"], g["q"].contiguous()
+    dbs = []
+    for c in range(copies):
+        db = tq.PackedCache(1, 1, n, bits, tq.LAYOUT_ROWS, signs, device=dev)
+        tq.quantize_append(db, x[None, :, None, :].contiguous(), 0)
+        dbs.append(db)
+    bufs = tq.SearchBuffers(nq, n, k, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        tq.ip_search(dbs[i % copies], q, n, k, buffers=bufs)
+
+    timer = Timer(torch, args.eager)
+    ms_per_step = timer.per_iteration_ms(step, args.steps, args.warmup)
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step, max(args.steps, 2 * copies), 2, batches=5)
+    nbytes = per_copy  # the packed database, read once per call
+    achieved = nbytes / (ms_k / 1e3) / 1e9
+    # recall@k against exact inner-product search over the unquantized vectors (measurement only)
+    step(0)
+    exact = torch.topk(q.float() @ x.float().T, k, dim=1).indices
+    got = bufs.idx.long()
+    recall = float(sum(len(set(got[j].tolist()) & set(exact[j].tolist())) for j in range(nq)) / (nq * k))
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({nq} queries over {n} vectors), {achieved:.0f} GB/s of packed "
+        f"database, recall@{k} vs exact search {recall:.3f}")
+    result = {
+        "metric": METRIC, "value": nq / (ms_per_step / 1e3), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16+f32",
+        "data": "synthetic (seeded clustered vectors standing in for a search benchmark)",
+        "config": {"workload": "search1m", "n_vectors": n, "n_queries": nq, "top_k": k, "bits": bits, "d": D,
+                   "step": "inner-product search: scores + top-k per query", "cache_copies": copies,
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "recall_at_k_vs_exact": recall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "search call (ip_score_kernel, topk_chunk_kernel, topk_merge_kernel)",
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                     "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_search(spec, dbs[0], q, signs, np, torch, log)
+    return result
+
+
+def cpu_baseline_search(spec, db, q, signs, np, torch, log):
+    """The CPU oracle on a bounded sample: one query over the first 65536 database vectors,
+    scaled to queries/s over the whole database (the work is linear in its size)."""
+    from oracle import tq_oracle as o
+
+    n, bits, sample = spec["n"], spec["bits"], 65536
+    s64 = signs.cpu().numpy().astype(np.float64)
+    c, _, _ = o.make_codebook(D, bits)[:3]
+    codes = o.unpack(db.plane_codes(0, 0)[: sample * 16 * bits].cpu().numpy(), sample, D, bits, 0)
+    n16 = db.plane_norms(0, 0)[:sample].cpu().numpy().astype(np.float16)
+    q64 = q[:1].double().cpu().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.ip_search(q64, codes, n16, s64, c, spec["top_k"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    value = reps * sample / n / el
+    log(f"[bench] cpu oracle: {reps} sample searches in {el:.1f} s")
+    return {"value": value, "unit": "queries/s", "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"1 query over the first {sample} of {n} vectors, scaled to the whole database; "
+                      f"{reps} repetitions"}
 
 
 def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):

@@ -177,3 +177,30 @@ def test_verify_full_size_sampled(golden_codebooks):
         worst = parity.check_rows(out_g[0][:, heads], out[0], f"multi out kv head {kvh}")
         assert np.allclose(lse_g[0][:, heads], lse[0], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[0])))
         _say(f"  kv head {kvh}: rel err {worst:.2e}")
+
+
+def test_search_full_size(golden_codebooks):
+    """search1m: 8 queries over 2^20 quantized vectors, the benchmark's call; the oracle ranks
+    the whole database from the GPU-written codes and norms."""
+    spec = inputs.SEARCH["search1m"]
+    _say("full-size search")
+    n, nq, k, bits = spec["n"], spec["n_queries"], spec["top_k"], spec["bits"]
+    signs = inputs.rotation_signs()
+    g = inputs.generate_search(spec, device=DEV)
+    db = tq.PackedCache(1, 1, n, bits, tq.LAYOUT_ROWS, signs.to(DEV), device=DEV)
+    tq.quantize_append(db, g["x"][None, :, None, :].contiguous(), 0)
+    res = tq.ip_search(db, g["q"].contiguous(), n, k)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    c, _ = golden_codebooks[bits]
+    codes = o.unpack(db.plane_codes(0, 0).cpu().numpy(), n, 128, bits, 0)
+    n16 = db.plane_norms(0, 0).cpu().numpy().astype(np.float16)
+    idx_o, sc_o, s_all = o.ip_search(parity.to_f64(g["q"]), codes, n16, s64, c, k)
+    idx_g, sc_g = res.idx.cpu().numpy(), res.score.cpu().numpy()
+    for j in range(nq):
+        tol = 1e-3 * np.abs(s_all[j]).max()
+        assert np.all(np.abs(sc_g[j] - s_all[j][idx_g[j]]) <= tol), j
+        kth = sc_o[j, k - 1]
+        assert np.all(s_all[j][idx_g[j]] >= kth - 2 * tol), j
+        assert set(np.nonzero(s_all[j] > kth + 2 * tol)[0].tolist()) <= set(idx_g[j].tolist()), j
+        _say(f"  query {j}: {len(set(idx_g[j].tolist()) & set(idx_o[j].tolist()))}/{k} of the oracle's top {k}")
