@@ -9,10 +9,11 @@
 //                     group of 8) against the database, on matrix cores: queries are the
 //                     rows of v_mfma_f32_16x16x32_f16 (fp16 value and remainder rows, as in
 //                     the decode kernel), 16 database vectors its columns; written to HBM.
-//   topk_chunk_kernel per (query, chunk of kChunkScores scores): the chunk's k best, found
-//                     by a radix select in LDS, written in index order.
-//   topk_merge_kernel per query: the same selection over the chunks' candidates, then the
-//                     k results ranked by descending score, ties by ascending index.
+//   topk_chunk_kernel per (query, chunk of kChunkScores scores): the chunk's k best, highest
+//                     score first, equal scores by lowest index: each wave takes the best of
+//                     its slice k times (wave-wide max, then min index), then one wave does
+//                     the same over the waves' results.
+//   topk_merge_kernel per query: the same selection over the chunks' candidates.
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
@@ -130,142 +131,146 @@ __global__ __launch_bounds__(64 * kScoreWaves) void ip_score_kernel(CacheView db
   }
 }
 
-// Order-preserving unsigned key of a float: a larger float has a larger key.
+// Order-preserving unsigned key of a float: a larger float has a larger key, and every
+// finite score has a key above 0, which marks an empty or taken slot.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-
-// Block prefix sum (exclusive) of one count per thread; returns the thread's offset and
-// leaves the total in *total.
-__device__ int block_exclusive_scan(int v, int *tmp, int *total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopkThreads; off <<= 1) {
-    const int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
-  }
-  const int incl = tmp[tid];
-  *total = tmp[kTopkThreads - 1];
-  __syncthreads();
-  return incl - v;
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Selects the k best of cnt (score, index) pairs staged in index order in LDS and writes them
-// in that order to out_s / out_i (k entries; missing ones as -inf / -1).  Radix select of the
-// k-th largest key, 8 bits at a time from the top; among keys equal to it the lowest staged
-// positions are taken.  Each thread owns a contiguous run of staged entries.
-__device__ void block_topk(const float *sc, const int32_t *ix, int cnt, int k, float *out_s, int32_t *out_i,
-                           int *hist, int *tmp) {
-  const int tid = threadIdx.x;
-  const int per = (cnt + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(tid * per, cnt), hi = min(lo + per, cnt);
-  const int kk = min(k, cnt);
-  uint32_t prefix = 0u, mask = 0u;
-  int remaining = kk;  // how many still to take at or below the current prefix
-  for (int digit = 3; digit >= 0 && kk > 0; --digit) {
-    for (int b = tid; b < 256; b += kTopkThreads) hist[b] = 0;
-    __syncthreads();
-    for (int i = lo; i < hi; ++i) {
-      const uint32_t key = order_key(sc[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> (8 * digit)) & 0xffu], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {  // the digit holding the remaining-th largest
-      int above = 0, b = 255;
-      for (; b > 0; --b) {
-        if (above + hist[b] >= remaining) break;
-        above += hist[b];
+// Wave-wide integer max / min with the lane exchanges of lanes.h: DPP quad permutes and row
+// rotations within 16 lanes, then the permlane swaps of rows and halves.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_int(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : (uint32_t)min((int)a, (int)b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor4, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor8, 0xF, 0xF, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_int<true>(v); }
+__device__ __forceinline__ int wave_min_i32(int v) { return (int)wave_reduce_int<false>((uint32_t)v); }
+
+// The k best of the entries a wave holds (kPer per lane: key, index), best first: highest
+// key, then lowest index.  Each round the wave's best is found from the lanes' own bests;
+// only the lane that gave it up looks at its entries again.  Results go to out_k / out_i
+// (k slots; 0 / -1 once the entries run out).
+template <int kPer>
+__device__ void wave_select(uint32_t (&key)[kPer], int (&idx)[kPer], int k, int lane, uint32_t *out_k, int *out_i) {
+  uint32_t bk = 0u;
+  int bi = 0x7fffffff;
+  auto lane_best = [&]() {
+    bk = 0u;
+    bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (key[j] > bk || (key[j] == bk && key[j] != 0u && idx[j] < bi)) {
+        bk = key[j];
+        bi = idx[j];
       }
-      tmp[kTopkThreads] = b;
-      tmp[kTopkThreads + 1] = remaining - above;
+  };
+  lane_best();
+  for (int r = 0; r < k; ++r) {
+    const uint32_t mk = wave_max_u32(bk);
+    const int mi = wave_min_i32(bk == mk ? bi : 0x7fffffff);
+    if (lane == 0) {
+      out_k[r] = mk;
+      out_i[r] = mk == 0u ? -1 : mi;
     }
-    __syncthreads();
-    prefix |= (uint32_t)tmp[kTopkThreads] << (8 * digit);
-    mask |= 0xffu << (8 * digit);
-    remaining = tmp[kTopkThreads + 1];
-    __syncthreads();
-  }
-  // keys above the k-th are all taken; of the keys equal to it, the first `remaining`
-  int n_eq = 0;
-  for (int i = lo; i < hi; ++i) n_eq += (kk > 0 && order_key(sc[i]) == prefix) ? 1 : 0;
-  int tot_eq;
-  int eq_rank = block_exclusive_scan(n_eq, tmp, &tot_eq);
-  int n_take = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    if (kk > 0 && (key > prefix || (key == prefix && eq_rank++ < remaining))) ++n_take;
-  }
-  int tot_take;
-  int pos = block_exclusive_scan(n_take, tmp, &tot_take);
-  eq_rank = block_exclusive_scan(n_eq, tmp, &tot_eq);
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    if (kk > 0 && (key > prefix || (key == prefix && eq_rank++ < remaining))) {
-      out_s[pos] = sc[i];
-      out_i[pos] = ix[i];
-      ++pos;
+    if (mk == 0u) continue;
+    if (bk == mk && bi == mi) {  // the one lane that held it
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (key[j] == mk && idx[j] == mi) key[j] = 0u;
+      lane_best();
     }
   }
-  for (int i = tot_take + tid; i < k; i += kTopkThreads) {
-    out_s[i] = -INFINITY;
-    out_i[i] = -1;
+}
+
+constexpr int kSelWaves = kTopkThreads / 64;
+constexpr int kSelPer = kChunkScores / kTopkThreads;  // entries per lane
+
+// Block top-k of n (key, index) entries read by `get` (i -> {key, index}), best first, into
+// out_k / out_i (k slots): every wave selects from its slice, then wave 0 from the waves' k
+// bests each.
+template <typename Get>
+__device__ void block_select(int n, int k, Get get, uint32_t *wk, int *wi, uint32_t *out_k, int *out_i) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {
+    uint32_t key[kSelPer];
+    int idx[kSelPer];
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int i = (wave * kSelPer + j) * 64 + lane;  // coalesced: lanes take neighbours
+      key[j] = 0u;
+      idx[j] = 0x7fffffff;
+      if (i < n) get(i, key[j], idx[j]);
+    }
+    wave_select<kSelPer>(key, idx, k, lane, wk + wave * kSearchMaxK, wi + wave * kSearchMaxK);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kPer2 = kSelWaves * kSearchMaxK / 64;
+    uint32_t key[kPer2];
+    int idx[kPer2];
+#pragma unroll
+    for (int j = 0; j < kPer2; ++j) {
+      const int e = j * 64 + lane, w = e / kSearchMaxK, r = e % kSearchMaxK;
+      key[j] = r < k ? wk[w * kSearchMaxK + r] : 0u;
+      idx[j] = r < k ? wi[w * kSearchMaxK + r] : 0x7fffffff;
+      if (key[j] == 0u) idx[j] = 0x7fffffff;
+    }
+    wave_select<kPer2>(key, idx, k, lane, out_k, out_i);
   }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(const float *__restrict__ scores, int n, int k,
                                                                  float *cand_s, int32_t *cand_i, int n_chunks) {
-  __shared__ float sc[kChunkScores];
-  __shared__ int32_t ix[kChunkScores];
-  __shared__ int hist[256];
-  __shared__ int tmp[kTopkThreads + 2];
+  __shared__ uint32_t wk[kSelWaves * kSearchMaxK];
+  __shared__ int wi[kSelWaves * kSearchMaxK];
+  __shared__ uint32_t ok[kSearchMaxK];
+  __shared__ int oi[kSearchMaxK];
   const int chunk = blockIdx.x, j = blockIdx.y;
   const int base = chunk * kChunkScores, cnt = min(kChunkScores, n - base);
-  for (int i = threadIdx.x; i < cnt; i += kTopkThreads) {
-    sc[i] = scores[(size_t)j * n + base + i];
-    ix[i] = base + i;
-  }
+  const float *row = scores + (size_t)j * n + base;
+  block_select(cnt, k, [&](int i, uint32_t &key, int &idx) { key = order_key(row[i]); idx = base + i; }, wk, wi, ok,
+               oi);
   __syncthreads();
   const size_t o = ((size_t)j * n_chunks + chunk) * k;
-  block_topk(sc, ix, cnt, k, cand_s + o, cand_i + o, hist, tmp);
+  for (int r = threadIdx.x; r < k; r += kTopkThreads) {
+    cand_s[o + r] = ok[r] == 0u ? -INFINITY : key_value(ok[r]);
+    cand_i[o + r] = oi[r];
+  }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(const float *__restrict__ cand_s,
                                                                  const int32_t *__restrict__ cand_i, int n_cand, int k,
                                                                  int32_t *out_idx, float *out_score) {
-  __shared__ float sc[kChunkScores];
-  __shared__ int32_t ix[kChunkScores];
-  __shared__ float bs[64];
-  __shared__ int32_t bi[64];
-  __shared__ int hist[256];
-  __shared__ int tmp[kTopkThreads + 2];
+  __shared__ uint32_t wk[kSelWaves * kSearchMaxK];
+  __shared__ int wi[kSelWaves * kSearchMaxK];
+  __shared__ uint32_t ok[kSearchMaxK];
+  __shared__ int oi[kSearchMaxK];
   const int j = blockIdx.x;
-  // chunks' candidates in chunk order: every chunk's list is in index order, so the staging
-  // is in index order (the empty slots, -inf with index -1, sort last)
-  for (int i = threadIdx.x; i < n_cand; i += kTopkThreads) {
-    sc[i] = cand_s[(size_t)j * n_cand + i];
-    ix[i] = cand_i[(size_t)j * n_cand + i];
-  }
+  const float *cs = cand_s + (size_t)j * n_cand;
+  const int32_t *ci = cand_i + (size_t)j * n_cand;
+  block_select(n_cand, k,
+               [&](int i, uint32_t &key, int &idx) {
+                 idx = ci[i];
+                 key = idx < 0 ? 0u : order_key(cs[i]);  // an empty candidate slot
+                 if (idx < 0) idx = 0x7fffffff;
+               },
+               wk, wi, ok, oi);
   __syncthreads();
-  block_topk(sc, ix, n_cand, k, bs, bi, hist, tmp);
-  __syncthreads();
-  // rank the k results: descending score, ascending index on ties (no index -1 is ever
-  // ahead of a real one, since its score is -inf)
-  for (int a = threadIdx.x; a < k; a += kTopkThreads) {
-    const float s = bs[a];
-    const int32_t id = bi[a];
-    int rank = 0;
-    for (int b = 0; b < k; ++b) {
-      const float t = bs[b];
-      const int32_t tb = bi[b];
-      const bool ahead = t > s || (t == s && ((tb >= 0 && (id < 0 || tb < id)) || (tb == id && b < a)));
-      rank += ahead ? 1 : 0;
-    }
-    out_idx[(size_t)j * k + rank] = id;
-    out_score[(size_t)j * k + rank] = s;
+  for (int r = threadIdx.x; r < k; r += kTopkThreads) {  // already best first
+    out_idx[(size_t)j * k + r] = oi[r];
+    out_score[(size_t)j * k + r] = ok[r] == 0u ? -INFINITY : key_value(ok[r]);
   }
 }
 
