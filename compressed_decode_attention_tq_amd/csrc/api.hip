@@ -177,26 +177,27 @@ WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads,
 }
 
 struct SearchLayout {
-  size_t scores, cand_s, cand_i, total;
+  size_t cand_s0, cand_i0, cand_s1, cand_i1, total;
 };
 
 SearchLayout search_layout(int n_q, int n, int k) {
-  const size_t n_cand = (size_t)((n + kSearchChunk - 1) / kSearchChunk) * k;
+  const size_t n_cand = (size_t)n_q * ((n + kSearchBlock - 1) / kSearchBlock) * k;
   SearchLayout w{};
   size_t off = 0;
-  w.scores = off;
-  off = align_up(off + (size_t)n_q * n * sizeof(float), 256);
-  w.cand_s = off;
-  off = align_up(off + (size_t)n_q * n_cand * sizeof(float), 256);
-  w.cand_i = off;
-  off = align_up(off + (size_t)n_q * n_cand * sizeof(int32_t), 256);
+  w.cand_s0 = off;
+  off = align_up(off + n_cand * sizeof(float), 256);
+  w.cand_i0 = off;
+  off = align_up(off + n_cand * sizeof(int32_t), 256);
+  w.cand_s1 = off;
+  off = align_up(off + n_cand * sizeof(float), 256);
+  w.cand_i1 = off;
+  off = align_up(off + n_cand * sizeof(int32_t), 256);
   w.total = off;
   return w;
 }
 
 bool search_shape_ok(int n_q, int n, int k) {
-  return n_q >= 1 && n_q <= 65535 * 8 && n >= 1 && k >= 1 && k <= kSearchMaxK &&
-         (long)((n + kSearchChunk - 1) / kSearchChunk) * k <= kSearchChunk;
+  return n_q >= 1 && n_q <= 65535 * 8 && n >= 1 && k >= 1 && k <= kSearchMaxK;
 }
 
 int check_paged(const tq_paged_cache *c) {
@@ -630,8 +631,9 @@ int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, 
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);
   return hip_status(launch_ip_search(view_of(db), q, q_dtype, n_queries, n_vectors, top_k, out_idx, out_score,
-                                     reinterpret_cast<float *>(ws + w.scores), reinterpret_cast<float *>(ws + w.cand_s),
-                                     reinterpret_cast<int32_t *>(ws + w.cand_i), static_cast<hipStream_t>(hip_stream)));
+                                     reinterpret_cast<float *>(ws + w.cand_s0), reinterpret_cast<int32_t *>(ws + w.cand_i0),
+                                     reinterpret_cast<float *>(ws + w.cand_s1), reinterpret_cast<int32_t *>(ws + w.cand_i1),
+                                     static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

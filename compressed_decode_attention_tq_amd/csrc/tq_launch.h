@@ -111,11 +111,12 @@ SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len);
 WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len);
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
 // Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
-// db, 3- or 4-bit rows), then the k best per query.  scores [n_q][n], cand_s / cand_i
-// [n_q][ceil(n / 8192) * k] are caller scratch.
+// db, 3- or 4-bit rows), then the k best per query.  Two candidate buffers (ping-pong for the
+// merge levels), each [n_q][ceil(n / kSearchBlock) * k] score + index, are caller scratch.
 hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
-                            float *out_score, float *scores, float *cand_s, int32_t *cand_i, hipStream_t stream);
-constexpr int kSearchChunk = 8192;
+                            float *out_score, float *cand_s0, int32_t *cand_i0, float *cand_s1, int32_t *cand_i1,
+                            hipStream_t stream);
+constexpr int kSearchBlock = 2048;
 constexpr int kSearchMaxK = 64;
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);

@@ -303,7 +303,7 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
  *   out_idx    device out int32 [n_queries][top_k] (-1 past n_vectors)
  *   out_score  device out fp32 [n_queries][top_k] (-inf past n_vectors)
  *   workspace  device scratch of tq_ip_search_workspace_bytes(...) bytes, 256-byte aligned
- * 1 <= top_k <= 64 and ceil(n_vectors / 8192) * top_k <= 8192, else TQ_ERR_UNSUPPORTED.
+ * 1 <= top_k <= 64, else TQ_ERR_UNSUPPORTED.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, int n_vectors, int top_k,
                  int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, void *hip_stream);

@@ -268,7 +268,7 @@ def test_ip_search_argument_validation():
     ws = tq.ip_search_workspace_bytes(4, 65536, 10)
     assert ws > 0
     assert tq.ip_search_workspace_bytes(4, 65536, 65) == 0          # top_k above 64
-    assert tq.ip_search_workspace_bytes(4, 2 << 20, 64) == 0        # 256 chunks x 64 candidates
+    assert tq.ip_search_workspace_bytes(4, 2 << 20, 64) > 0         # several merge levels
 
     def srch(db=db, nq=4, n=65536, k=10, wsb=ws, out=FAKE + 0x700000, qdt=1):
         return L.tq_ip_search(ctypes.byref(db), FAKE + 0x600000, qdt, nq, n, k, out, FAKE + 0x780000,

@@ -626,6 +626,7 @@ def _search_case(signs, golden, n, nq, k, bits, q_dtype=None, dup=False, seed=0)
     (9000, 3, 5, 4, "f32", True),
     (40, 2, 64, 4, None, False),          # fewer vectors than k
     (8192, 1, 1, 3, "f16", False),
+    (300000, 3, 64, 4, None, False),      # 147 blocks x 64 candidates: two merge levels
 ])
 def test_ip_search_matches_oracle(case, signs, golden_codebooks):
     n, nq, k, bits, qdt, dup = case
