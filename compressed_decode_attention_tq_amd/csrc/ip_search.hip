@@ -13,7 +13,9 @@
 //                     highest score first, equal scores by lowest index, by taking the best
 //                     k times (wave-wide max of the key, then min index).
 //   topk_merge_kernel per query, kChunkScores candidates per block to k, repeated until one
-//                     block holds them all (one level for up to 2^20 vectors at k = 16).
+//                     block holds them all (two levels for 2^20 vectors at k = 10).  Small
+//                     slices keep each lane's share short: a round's cost is one lane
+//                     re-scanning its entries.
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
@@ -27,7 +29,7 @@ typedef _Float16 half8s __attribute__((ext_vector_type(8)));
 typedef float floatx4s __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreWaves = 8;
-constexpr int kChunkScores = 8192;  // candidates per merge block
+constexpr int kChunkScores = 1024;  // candidates per merge block
 constexpr int kBlockTokens = kSearchBlock;  // database vectors per score workgroup (scores kept in LDS)
 constexpr int kTopkThreads = 256;
 

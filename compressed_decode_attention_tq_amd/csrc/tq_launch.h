@@ -116,7 +116,7 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
                             float *out_score, float *cand_s0, int32_t *cand_i0, float *cand_s1, int32_t *cand_i1,
                             hipStream_t stream);
-constexpr int kSearchBlock = 2048;
+constexpr int kSearchBlock = 1024;
 constexpr int kSearchMaxK = 64;
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
