@@ -26,7 +26,9 @@ Readings of points the pages leave open (each is listed in the design notes):
     round-to-nearest-even value; a zero vector gives u = 0;
   * packing is an LSB-first bit stream (see `code_bit_positions`);
   * Sparse V keeps row t for head h iff the final normalised softmax weight
-    p_{h,t} >= tau, without renormalisation.
+    p_{h,t} >= tau, without renormalisation;
+  * inner-product search ranks database vectors by q . x_hat (their dequantized
+    vectors), descending, equal scores by ascending index.
 
 Parity status: every function here is pinned by a test in tests/ against
 closed forms, a library routine or brute force, except the end-to-end outputs
