@@ -99,6 +99,57 @@ __device__ void wave_select(uint32_t (&key)[kPer], int (&idx)[kPer], int k, int 
   }
 }
 
+// The k best of kPer entries per lane, as wave_select, with a prefilter: the k-th largest of
+// the 64 lane maxima is a lower bound of the k-th largest entry (k lanes hold an entry at
+// least that large), so only entries at or above it can be among the k best.  When at most
+// 64 pass, they are compacted through `scratch` (64 keys + 64 indices of LDS) to one per lane
+// and the rounds no longer re-scan kPer entries; otherwise the plain selection runs.
+template <int kPer>
+__device__ void wave_select_pruned(uint32_t (&key)[kPer], int (&idx)[kPer], int k, int lane, uint32_t *scratch,
+                                   uint32_t *out_k, int *out_i) {
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) lm = max(lm, key[j]);
+  uint32_t v = lm, theta = 0u;
+  for (int r = 0; r < k && r < 64; ++r) {  // the k-th largest lane maximum
+    theta = wave_max_u32(v);
+    const uint64_t at = __ballot(v == theta);
+    if (lane == __ffsll((unsigned long long)at) - 1) v = 0u;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) cnt += (key[j] != 0u && key[j] >= theta) ? 1 : 0;
+  // exclusive prefix of the counts over the lanes
+  int incl = cnt;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  const int total = __shfl(incl, 63);
+  if (total > 64) {  // many entries tie with the bound: select over all of them
+    wave_select<kPer>(key, idx, k, lane, out_k, out_i);
+    return;
+  }
+  int pos = incl - cnt;
+  uint32_t *sk = scratch;
+  int *si = reinterpret_cast<int *>(scratch + 64);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (key[j] != 0u && key[j] >= theta) {
+      sk[pos] = key[j];
+      si[pos] = idx[j];
+      ++pos;
+    }
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  uint32_t k1[1] = {lane < total ? sk[lane] : 0u};
+  int i1[1] = {lane < total ? si[lane] : 0x7fffffff};
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+  wave_select<1>(k1, i1, k, lane, out_k, out_i);
+}
+
 constexpr int kSelWaves = kTopkThreads / 64;
 constexpr int kSelPer = kChunkScores / kTopkThreads;  // entries per lane
 
@@ -252,7 +303,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void ip_score_kernel(CacheView db
     }
     uint32_t *ok = reinterpret_cast<uint32_t *>(&sc[wave][0]);  // this wave's row is free now
     int *oi = reinterpret_cast<int *>(&sc[wave][kSearchMaxK]);
-    wave_select<kPer>(key, idx, k, lane, ok, oi);
+    wave_select_pruned<kPer>(key, idx, k, lane, reinterpret_cast<uint32_t *>(&sc[wave][2 * kSearchMaxK]), ok, oi);
     const size_t o = ((size_t)(q0 + wave) * gridDim.x + blockIdx.x) * k;
     for (int r = lane; r < k; r += 64) {
       cand_s[o + r] = ok[r] == 0u ? -INFINITY : key_value(ok[r]);
