@@ -174,15 +174,16 @@ size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int c
  * ctx_len) : ctx_len >= 1, quantize its new key xk[b] and value xv[b] into position T - 1 of
  * the caches (as tq_quantize_append_kv with start_pos = T - 1, n_tokens = 1), then dense
  * decode attention exactly as tq_decode_attn with sparse_v_tau = 0 and no scores.  One launch
- * for keys of 3/4 bits, values of 2 bits and n_q_heads / n_kv_heads <= 8 (the workgroup that
- * owns position T - 1 writes the token first); otherwise the append kernel and then the
+ * for keys of 3/4 bits, values of 2 bits and n_q_heads / n_kv_heads <= 8 (the wave that
+ * reads position T - 1 writes the token first); otherwise the append kernel and then the
  * decode call, which needs seq_lens == NULL (TQ_ERR_UNSUPPORTED otherwise).
  *   xk, xv     device in [batch][1][n_kv_heads][d] of x_dtype, 16-byte aligned
  *   the other arguments as for tq_decode_attn; workspace of tq_decode_workspace_bytes(..., 0)
  * A decode step needs this one launch instead of two.  The new token's codes follow the
- * same rule as the append kernels (equal to the oracle's except within 1e-6 of a boundary;
- * the fp32 rotation is evaluated in another order, so a code within that band can differ
- * from the append kernel's).
+ * same rule as the append kernels (equal to the oracle's except within 1e-6 of a boundary).
+ * The arithmetic is that of the append path for up to 8 tokens; the chunked path for longer
+ * appends evaluates the fp32 rotation in another order, so a code within that band can
+ * differ from it.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,
                           int x_dtype, const void *q, int q_dtype, int n_q_heads,
