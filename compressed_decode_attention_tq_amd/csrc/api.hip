@@ -123,6 +123,12 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
     off = align_up(off + units * sizeof(int), 256);
     w.cand = off;
     off = align_up(off + units * (size_t)p.split_len * (1 + g) * sizeof(float), 256);
+    const SplitPlan dp = plan_fused(batch, n_kv_heads, ctx_len);
+    const size_t vheads = (size_t)batch * n_q_heads * dp.n_splits;
+    w.vpart_ml = off;
+    off = align_up(off + vheads * sizeof(float2), 256);
+    w.vpart_o = off;
+    off = align_up(off + vheads * kD * sizeof(float), 256);
   }
   w.total = off;
   return w;
@@ -392,6 +398,10 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
   a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
   a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
   a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
+  if (a.sparse) {
+    a.vpart_ml = reinterpret_cast<float2 *>(ws + w.vpart_ml);
+    a.vpart_o = reinterpret_cast<float *>(ws + w.vpart_o);
+  }
   return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
 

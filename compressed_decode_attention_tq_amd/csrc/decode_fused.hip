@@ -246,10 +246,14 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // PAGED: the caches are page pools found through a.block_table; each tile lies inside one
 // page (pages are whole multiples of 64 tokens), so a tile's loads differ from the
 // contiguous case only by its base offset.
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED>
+// VMASK: Sparse V's value pass after the key pass: the dense kernel, with the value operand
+// P' of a row whose final weight exp(s - LSE) is below tau set to zero (LSE merged from the
+// key pass's partials a.lse_ml); the softmax sum still counts every row.
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PAGED || !(SPARSE || MULTI), "paged caches: dense single-query decode");
+  static_assert(!VMASK || !(SPARSE || MULTI || APPEND || PAGED), "masked value pass: dense decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -425,11 +429,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       const float qs = a.scale * kInvSqrtD * kLog2e;
       *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
     }
+    float *thr_lds = reinterpret_cast<float *>(lds + kWBase + 4096 + 64);  // [NH], set-up only
+    if constexpr (VMASK) {  // head `wave`: threshold on s (log2 units) = (LSE + ln tau) log2 e
+      if (wave < NH) {
+        float m = -INFINITY, l = 0.f;
+        if (vlive(wave)) {
+          const float2 *ml = a.lse_ml + vrow(wave) * a.lse_splits;
+          for (int k = lane; k < a.lse_splits; k += 64) m = fmaxf(m, ml[k].x);
+          m = wave_reduce<true>(m);
+          if (m != -INFINITY)
+            for (int k = lane; k < a.lse_splits; k += 64)
+              if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - m);
+          l = wave_reduce<false>(l);
+        }
+        if (lane == 0) thr_lds[wave] = m == -INFINITY ? INFINITY : (m + __logf(l) + a.ln_tau) * kLog2e;
+      }
+    }
     __syncthreads();
     if (appends) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the new token's stores are complete
       if (defer_keys) load_keys(wave);
     }
+    float vthr[NH2];
+#pragma unroll
+    for (int hh = 0; hh < NH2; ++hh) vthr[hh] = VMASK ? thr_lds[half_id * NH2 + hh] : -INFINITY;
     // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
     half8 qop[8];
     {
@@ -616,6 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         }
         // token 2pr + tb is a candidate if either head half flags it; records are
         // {token, g scores (natural log)} at consecutive slots of the tile's second-pass split
+        if (a.cand == nullptr) { cand0 = false; cand1 = false; }  // key pass for the LSE only
         const uint64_t b0 = __ballot(cand0), b1 = __ballot(cand1);
         const uint32_t c0 = (uint32_t)b0 | (uint32_t)(b0 >> 32);
         const uint32_t c1 = (uint32_t)b1 | (uint32_t)(b1 >> 32);
@@ -716,7 +740,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 #pragma unroll
       for (int hh = 0; hh < NH2; ++hh) {
         const int h = half_id * NH2 + hh;
-        const float v0 = p[0][hh] * nv[0], v1 = p[1][hh] * nv[1];
+        float v0 = p[0][hh] * nv[0], v1 = p[1][hh] * nv[1];
+        if constexpr (VMASK) {  // Sparse V: rows under the final-weight threshold add no value
+          if (!(sc[0][hh] >= vthr[hh])) v0 = 0.f;
+          if (!(sc[1][hh] >= vthr[hh])) v1 = 0.f;
+        }
         half2v hi, lo;
         hi[0] = (_Float16)v0;
         hi[1] = (_Float16)v1;
@@ -804,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       if (wave < NH && vlive(wave) && lane == 0)
         a.fpart_ml[vrow(wave) * S + split] =
             make_float2(Mh == -INFINITY ? -INFINITY : Mh * kLn2, Lh);
-      for (int i = threadIdx.x; i < n_chunks; i += blockDim.x)
+      for (int i = threadIdx.x; i < n_chunks && a.cand_count != nullptr; i += blockDim.x)
         if (c_first + i < a.plan.n_splits)
           a.cand_count[((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + c_first + i] = chunk_count[i];
       return;
@@ -908,10 +936,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
-template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false>
+template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED><<<grid, kThreads, 0, stream>>>(a);
+  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK><<<grid, kThreads, 0, stream>>>(a);
+  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -956,6 +984,14 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
                          : launch_nh<3, false, false, true, true>(a, (int)items, stream);
   return a.k.bits == 4 ? launch_nh<4, false, false, false, true>(a, (int)items, stream)
                        : launch_nh<3, false, false, false, true>(a, (int)items, stream);
+}
+
+hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {
+  if (!decode_fused_supported(a) || a.lse_ml == nullptr || a.lse_splits < 1) return hipErrorInvalidValue;
+  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  return a.k.bits == 4 ? launch_nh<4, false, false, false, false, true>(a, (int)items, stream)
+                       : launch_nh<3, false, false, false, false, true>(a, (int)items, stream);
 }
 
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream) {

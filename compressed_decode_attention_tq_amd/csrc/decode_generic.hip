@@ -498,6 +498,24 @@ hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
   dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
   hipError_t e;
+  // Sparse V on matrix cores, two launches: the key pass (no candidate records) for each
+  // row's LSE, then the dense kernel with the rows under the final-weight threshold masked
+  // out of the value product; it merges its splits itself.  (Values of 2 bits.)
+  DecodeArgs v2 = a;
+  v2.sparse = 0;
+  v2.lse_ml = a.fpart_ml;
+  v2.lse_splits = a.fplan.n_splits;
+  v2.fplan = plan_fused(a.batch, a.n_kv_heads, a.ctx_len);
+  v2.fpart_ml = a.vpart_ml;
+  v2.fpart_o = a.vpart_o;
+  if (a.sparse && decode_fused_sparse_supported(a) && a.vpart_ml != nullptr && decode_fused_supported(v2)) {
+    DecodeArgs k1 = a;
+    k1.cand = nullptr;
+    k1.cand_count = nullptr;
+    e = launch_decode_fused_sparse(k1, stream);
+    if (e != hipSuccess) return e;
+    return launch_decode_fused_vmask(v2, stream);
+  }
   if (decode_fused_sparse_supported(a)) {  // key-only fused first pass
     a.lse_ml = a.fpart_ml;
     a.lse_splits = a.fplan.n_splits;

@@ -35,6 +35,8 @@ struct WorkspaceLayout {
   size_t part_o;      // float  [batch][n_q_heads][n_splits][128] rotated-domain sums
   size_t cand_count;  // int    [batch][n_kv_heads][n_splits]      Sparse-V candidates
   size_t cand;        // float  [batch][n_kv_heads][n_splits][split_len][1 + g]
+  size_t vpart_ml;    // Sparse V, masked value pass: float2 [batch][n_q_heads][dense fused splits]
+  size_t vpart_o;     //   and float [batch][n_q_heads][dense fused splits][128]
   size_t total;
 };
 
@@ -87,6 +89,10 @@ struct DecodeArgs {
   // lies in pool page block_table[b * max_pages + t / page_tokens].
   const int32_t *block_table;
   int max_pages, n_pages;
+  // Sparse V, masked value pass (the dense fused kernel after the key pass): its own
+  // partials; a.lse_ml / a.lse_splits are the key pass's (m, l) per split
+  float2 *vpart_ml;
+  float *vpart_o;
 };
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
@@ -126,6 +132,9 @@ bool decode_mfma_supported(const DecodeArgs &a);
 bool decode_fused_supported(const DecodeArgs &a);
 bool decode_fused_sparse_supported(const DecodeArgs &a);
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream);
+// Sparse V's masked value pass: the dense single-launch kernel over the dense plan (a.fplan,
+// partials a.fpart_ml / a.fpart_o) with the key pass's partials in a.lse_ml.
+hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int n_cu, hipStream_t stream);
 
