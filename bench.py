@@ -351,7 +351,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": f"{DECODE_KERNEL} (append + attend instance)" if dense_single
-                     else "decode attention call (split, Sparse-V and merge kernels)",
+                     else "decode attention call (Sparse V: key pass + masked value pass on matrix cores where the widths allow)",
                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
                      "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
         "_kernel": "decode" if dense_single else "decode_sparse",
