@@ -736,6 +736,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         }
       }
 
+      if constexpr (VMASK) {  // no row of the tile reaches its head's threshold: no value work
+        bool kept = false;
+#pragma unroll
+        for (int hh = 0; hh < NH2; ++hh) kept |= sc[0][hh] >= vthr[hh] || sc[1][hh] >= vthr[hh];
+        if (!__any(kept)) return;
+      }
+
       // ---- P' = p * ||v||: fp16 row 2h and remainder row 2h+1, token pair per 32-bit write
 #pragma unroll
       for (int hh = 0; hh < NH2; ++hh) {
@@ -921,8 +928,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         wave_fwht_upper(y0, y1, lane);
         y0 *= kInvSqrtD;
         y1 *= kInvSqrtD;
-        if (a.k.signs[2 * lane] < 0) y0 = -y0;
-        if (a.k.signs[2 * lane + 1] < 0) y1 = -y1;
+        if (sgn & 0x80u) y0 = -y0;  // the sign bytes loaded at set-up
+        if (sgn & 0x8000u) y1 = -y1;
         const size_t orow = vrow(wave);
         *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
         if (lane == 0 && a.lse != nullptr) a.lse[orow] = M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
