@@ -798,7 +798,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, std::true_type{});
     if (tile < n_tiles) tile_body(tile, std::false_type{});
 
-    // ---- combine the 8 waves of the split.  Round 1: (m, l) per head.
+    // ---- combine the 8 waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
+    //      the start of the key-table region (free once every wave is past its tiles), so
+    //      that round 2 can write the staging buffers while other waves still read them.
     float ltot[NH2];
 #pragma unroll
     for (int hh = 0; hh < NH2; ++hh) ltot[hh] = half_sum(lsum[hh]);
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     if (pr == 0) {
 #pragma unroll
       for (int hh = 0; hh < NH2; ++hh)
-        *reinterpret_cast<float2 *>(wbuf + (half_id * NH2 + hh) * 8) = make_float2(mr[hh], ltot[hh]);
+        *reinterpret_cast<float2 *>(lds + wave * 64 + (half_id * NH2 + hh) * 8) = make_float2(mr[hh], ltot[hh]);
     }
     __syncthreads();
     // scale of this wave's value rows (heads 2q, 2q+1) and, for the summing phase, the
@@ -817,18 +819,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       float M0 = -INFINITY, M1 = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float *src = reinterpret_cast<const float *>(lds + kWBase + w * 4096);
+        const float *src = reinterpret_cast<const float *>(lds + w * 64);
         M0 = fmaxf(M0, src[2 * h0]);
         M1 = fmaxf(M1, src[2 * (h0 + 1)]);
         if (wave < NH) Mh = fmaxf(Mh, src[2 * wave]);
       }
-      const float *own = reinterpret_cast<const float *>(wbuf);
+      const float *own = reinterpret_cast<const float *>(lds + wave * 64);
       f0 = exp2_or_zero(own[2 * h0], M0);
       f1 = exp2_or_zero(own[2 * (h0 + 1)], M1);
       if (wave < NH) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float *src = reinterpret_cast<const float *>(lds + kWBase + w * 4096);
+          const float *src = reinterpret_cast<const float *>(lds + w * 64);
           Lh += src[2 * wave + 1] * exp2_or_zero(src[2 * wave], Mh);
         }
       }
@@ -844,7 +846,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           a.cand_count[((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + c_first + i] = chunk_count[i];
       return;
     }
-    __syncthreads();
     // Round 2: scaled O rows of this wave, [head][128] fp32 (hi and remainder rows summed)
     if (NH == 8 || quarter < 2) {
       const int h0 = 2 * quarter;
