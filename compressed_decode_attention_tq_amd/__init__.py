@@ -152,6 +152,54 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, want, name):
+    """Raise ValueError unless tensor t has exactly the shape `want` (checked before any launch:
+    the kernels index caller buffers with the call's sizes, not the buffers')."""
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the call needs {tuple(want)}")
+
+
+def _check_query(q, cache, n_dims, what):
+    if q.dim() != n_dims:
+        raise ValueError(f"{what}: q must have {n_dims} dimensions, got shape {tuple(q.shape)}")
+    if q.shape[0] != cache.batch:
+        raise ValueError(f"{what}: q has batch {q.shape[0]}, the caches hold {cache.batch} sequences")
+    if q.shape[-1] != cache.d:
+        raise ValueError(f"{what}: q has head dim {q.shape[-1]}, the caches {cache.d}")
+    if q.shape[-2] % cache.n_kv_heads != 0:
+        raise ValueError(f"{what}: {q.shape[-2]} query heads is not a multiple of {cache.n_kv_heads} kv heads")
+
+
+def _check_seq_lens(seq_lens, batch, what, required=False):
+    if seq_lens is None:
+        if required:
+            raise ValueError(f"{what}: seq_lens is required")
+        return
+    torch = _torch()
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (batch,):
+        raise ValueError(f"{what}: seq_lens must be int32 of shape ({batch},), got {seq_lens.dtype} "
+                         f"{tuple(seq_lens.shape)}")
+
+
+def _check_outputs(buffers, out_shape, lse_shape, what, scores_shape=None):
+    torch = _torch()
+    _shape(buffers.out, out_shape, f"{what}: out")
+    if buffers.out.dtype != torch.float32:
+        raise ValueError(f"{what}: out must be float32")
+    lse = getattr(buffers, "lse", None)
+    if lse is not None:
+        _shape(lse, lse_shape, f"{what}: lse")
+        if lse.dtype != torch.float32:
+            raise ValueError(f"{what}: lse must be float32")
+    scores = getattr(buffers, "scores", None)
+    if scores is not None:
+        if scores_shape is None:
+            raise ValueError(f"{what}: this call writes no scores")
+        _shape(scores, scores_shape, f"{what}: scores")
+        if scores.dtype != torch.float32:
+            raise ValueError(f"{what}: scores must be float32")
+
+
 class PackedCache:
     """One K or V cache of one layer: packed codes + fp16 norms + codebook + signs (device)."""
 
@@ -252,10 +300,13 @@ def decode_attn(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: int, sca
                 tau: float = 0.0, seq_lens=None, buffers: DecodeBuffers | None = None,
                 want_scores: bool = False, stream=None):
     """Decode attention; returns the DecodeBuffers holding out [B, Hq, d], lse and scores."""
+    _check_query(q, k_cache, 3, "decode_attn")
     bsz, hq, d = q.shape
+    _check_seq_lens(seq_lens, bsz, "decode_attn")
     if buffers is None:
         buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, tau, device=q.device,
                                 d=d, want_scores=want_scores)
+    _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "decode_attn", scores_shape=(bsz, hq, ctx_len))
     ks, vs = k_cache.struct(), v_cache.struct()
     sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
     _check(lib().tq_decode_attn(
@@ -293,9 +344,12 @@ def decode_attn_multi(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: in
                       seq_lens=None, buffers: MultiQueryBuffers | None = None, stream=None):
     """Attention of the last n_q positions of each sequence (q [B, n_q, Hq, d]) over the packed
     cache, causal; returns the MultiQueryBuffers holding out [B, n_q, Hq, d] and lse."""
+    _check_query(q, k_cache, 4, "decode_attn_multi")
     bsz, n_q, hq, d = q.shape
+    _check_seq_lens(seq_lens, bsz, "decode_attn_multi")
     if buffers is None:
         buffers = MultiQueryBuffers(bsz, n_q, hq, k_cache.n_kv_heads, ctx_len, device=q.device, d=d)
+    _check_outputs(buffers, (bsz, n_q, hq, d), (bsz, n_q, hq), "decode_attn_multi")
     ks, vs = k_cache.struct(), v_cache.struct()
     sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
     _check(lib().tq_decode_attn_multi(
@@ -310,14 +364,17 @@ def decode_attn_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new,
                        scale: float, seq_lens=None, buffers: DecodeBuffers | None = None, stream=None):
     """Quantize k_new, v_new [B, 1, Hkv, d] into position T_b - 1 of each sequence, then dense
     decode attention (one launch where the fused kernel applies); returns the DecodeBuffers."""
+    _check_query(q, k_cache, 3, "decode_attn_append")
     bsz, hq, d = q.shape
     for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
         if x.dim() != 4 or x.shape[0] != bsz or x.shape[1] != 1 or x.shape[2] != cache.n_kv_heads or x.shape[3] != d:
             raise ValueError(f"{name} has shape {tuple(x.shape)}")
     if k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must have the same dtype")
+    _check_seq_lens(seq_lens, bsz, "decode_attn_append")
     if buffers is None:
         buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, 0.0, device=q.device, d=d)
+    _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "decode_attn_append")
     ks, vs = k_cache.struct(), v_cache.struct()
     sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
     _check(lib().tq_decode_attn_append(
@@ -404,9 +461,12 @@ class PagedDecodeBuffers:
 def paged_decode_attn(k_cache: PagedCache, v_cache: PagedCache, q, seq_lens, max_ctx_len: int, scale: float,
                       buffers: PagedDecodeBuffers | None = None, stream=None):
     """Dense decode attention over paged caches; returns the PagedDecodeBuffers (out, lse)."""
+    _check_query(q, k_cache, 3, "paged_decode_attn")
     bsz, hq, d = q.shape
+    _check_seq_lens(seq_lens, bsz, "paged_decode_attn", required=True)
     if buffers is None:
         buffers = PagedDecodeBuffers(bsz, hq, k_cache.n_kv_heads, max_ctx_len, device=q.device, d=d)
+    _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "paged_decode_attn")
     ks, vs = k_cache.struct(), v_cache.struct()
     _check(lib().tq_paged_decode_attn(
         ctypes.byref(ks), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, _dev(seq_lens, "seq_lens"),
@@ -420,14 +480,17 @@ def paged_decode_attn_append(k_cache: PagedCache, v_cache: PagedCache, k_new, v_
                              scale: float, buffers: PagedDecodeBuffers | None = None, stream=None):
     """Quantize k_new, v_new [B, 1, Hkv, d] into position T_b - 1 of the paged caches and
     attend, in one launch; returns the PagedDecodeBuffers (out, lse)."""
+    _check_query(q, k_cache, 3, "paged_decode_attn_append")
     bsz, hq, d = q.shape
     for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
         if x.dim() != 4 or x.shape[0] != bsz or x.shape[1] != 1 or x.shape[2] != cache.n_kv_heads or x.shape[3] != d:
             raise ValueError(f"{name} has shape {tuple(x.shape)}")
     if k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must have the same dtype")
+    _check_seq_lens(seq_lens, bsz, "paged_decode_attn_append", required=True)
     if buffers is None:
         buffers = PagedDecodeBuffers(bsz, hq, k_cache.n_kv_heads, max_ctx_len, device=q.device, d=d)
+    _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "paged_decode_attn_append")
     ks, vs = k_cache.struct(), v_cache.struct()
     _check(lib().tq_paged_decode_attn_append(
         ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
@@ -460,9 +523,13 @@ class SearchBuffers:
 def ip_search(db: PackedCache, q, n_vectors: int, top_k: int, buffers: SearchBuffers | None = None, stream=None):
     """Top-k inner-product search of q [Q, d] over vectors 0 .. n_vectors - 1 of the database
     cache (batch 1, one kv head, rows); returns the SearchBuffers (idx, score [Q, top_k])."""
+    if q.dim() != 2 or q.shape[1] != db.d:
+        raise ValueError(f"ip_search: q has shape {tuple(q.shape)}")
     nq, d = q.shape
     if buffers is None:
         buffers = SearchBuffers(nq, n_vectors, top_k, device=q.device)
+    _shape(buffers.idx, (nq, top_k), "ip_search: idx")
+    _shape(buffers.score, (nq, top_k), "ip_search: score")
     st = db.struct()
     _check(lib().tq_ip_search(ctypes.byref(st), _dev(q, "q"), _dtype_code(q.dtype), nq, n_vectors, top_k,
                               _dev(buffers.idx, "idx"), _dev(buffers.score, "score"), ctypes.c_void_p(buffers.ws_ptr),

@@ -253,7 +253,11 @@ def quantize(x, signs, centroids, boundaries, method: str = "boundaries"):
 
 
 def near_boundary_mask(u, boundaries, band: float = 1e-6) -> np.ndarray:
-    """Coordinates whose rotated value lies within `band` of a boundary."""
+    """Coordinates whose rotated value lies within `band` of a boundary.
+
+    The band is an absolute distance in unit-vector coordinates, |u_i - t_j| <= band for
+    some boundary t_j (the plain reading of "within 1e-6 of a codebook boundary"), taken
+    on the oracle's fp64 u.  A code on either side of such a boundary is accepted."""
     u = np.asarray(u, dtype=np.float64)
     t = np.asarray(boundaries, dtype=np.float64)
     return (np.abs(u[..., None] - t) <= band).any(axis=-1)
@@ -324,7 +328,7 @@ def dequantize(codes, norms16, signs, centroids) -> np.ndarray:
     return n[..., None] * unrotate(c, signs)
 
 
-def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 0.0):
+def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 0.0, valid=None):
     """Decode attention over a dequantized cache, one query per (batch, head).
 
     q: [B, Hq, d]; k_hat, v_hat: [B, Hkv, T, d]; query head h reads kv head
@@ -334,7 +338,13 @@ def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 
     with keep_t = (p_t >= tau) for Sparse V ([inferrs] §Sparse V: V rows of
     low attention weight are skipped) and keep_t = 1 when tau == 0.  The
     denominator always counts every row (no renormalisation).
-    Returns (out [B, Hq, d], lse [B, Hq], scores [B, Hq, T] with -inf past T_b).
+    valid: optional bool [B, T]; a position with valid[b, t] False is not part of
+    sequence b's context (a paged cache's position whose block-table entry names no
+    page, [inferrs] §二 PagedAttention: only allocated pages hold tokens): it is left out
+    of the softmax entirely, as if the position were absent.  A row with no valid
+    position gives o = 0 and LSE = -inf.
+    Returns (out [B, Hq, d], lse [B, Hq], scores [B, Hq, T] with -inf past T_b and at
+    positions that are not valid).
     """
     q = np.asarray(q, dtype=np.float64)
     kh = np.asarray(k_hat, dtype=np.float64)
@@ -351,15 +361,19 @@ def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 
             j = h // g
             if tb == 0:
                 continue
-            s = scale * (kh[b, j, :tb] @ q[b, h])
+            live = np.ones(tb, dtype=bool) if valid is None else np.asarray(valid[b][:tb], dtype=bool)
+            if not live.any():
+                continue
+            pos = np.nonzero(live)[0]
+            s = scale * (kh[b, j, pos] @ q[b, h])
             m = s.max()
             ssum = np.exp(s - m).sum()
             l_ = m + math.log(ssum)
             p = np.exp(s - l_)
-            keep = p >= tau if tau > 0 else np.ones(tb, dtype=bool)
-            out[b, h] = (p[keep, None] * vh[b, j, :tb][keep]).sum(axis=0)
+            keep = p >= tau if tau > 0 else np.ones(pos.size, dtype=bool)
+            out[b, h] = (p[keep, None] * vh[b, j, pos][keep]).sum(axis=0)
             lse[b, h] = l_
-            scores[b, h, :tb] = s
+            scores[b, h, pos] = s
     return out, lse, scores
 
 
@@ -431,7 +445,10 @@ def sparse_v_borderline(scores, lse, tau: float, rel: float = 1e-3) -> np.ndarra
     is acceptable there.
     """
     s = np.asarray(scores, dtype=np.float64)
-    finite = np.isfinite(s)
-    smax = np.where(finite, np.abs(s), 0.0).max(axis=-1, keepdims=True)
-    thr = np.asarray(lse)[..., None] + math.log(tau)
-    return finite & (np.abs(s - thr) <= rel * smax)
+    thr = np.asarray(lse, dtype=np.float64)[..., None] + math.log(tau)
+    # only finite scores against a finite threshold are compared: a row with no tokens
+    # (LSE = -inf, every score -inf) has no borderline entry, and no -inf - -inf is formed
+    finite = np.isfinite(s) & np.isfinite(thr)
+    smax = np.where(np.isfinite(s), np.abs(s), 0.0).max(axis=-1, keepdims=True)
+    dist = np.abs(np.where(finite, s, 0.0) - np.where(finite, thr, 0.0))
+    return finite & (dist <= rel * smax)

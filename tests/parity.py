@@ -121,7 +121,8 @@ def check_scores(got, ref, seq_lens):
 def sparse_allowance(scores, lse, v_hat, tau, group):
     """sum over borderline rows of p_t ||v_hat_t|| per (b, h): either decision is allowed."""
     border = o.sparse_v_borderline(scores, lse, tau, REL)
-    p = np.exp(np.where(np.isfinite(scores), scores - lse[..., None], -np.inf))
+    ok = np.isfinite(scores) & np.isfinite(lse)[..., None]
+    p = np.where(ok, np.exp(np.where(ok, scores, 0.0) - np.where(ok, lse[..., None], 0.0)), 0.0)
     vn = np.linalg.norm(v_hat, axis=-1)                # [B, Hkv, T]
     vn_q = np.repeat(vn, group, axis=1)                # [B, Hq, T]
     return (p * border * vn_q).sum(-1), int(border.sum())

@@ -293,3 +293,47 @@ def test_probe_rejects_bad_arguments():
     assert f(FAKE + 8, 1 << 20, FAKE, None) == tq.TQ_ERR_INVALID_ARG
     assert f(FAKE, 1000, FAKE, None) == tq.TQ_ERR_INVALID_ARG
     assert f(FAKE, 0, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_binding_rejects_buffers_of_another_shape():
+    """The binding checks caller-supplied output buffers, q and seq_lens against the call's
+    (batch, query heads, context) before any launch: the kernels write scores with the call's
+    ctx_len as row stride, so a buffer made for a shorter context must be refused.  Runs on
+    CPU tensors: every check here comes before the device-pointer checks."""
+    torch = pytest.importorskip("torch")
+    signs = torch.ones(128, dtype=torch.int8)
+    kc = tq.PackedCache(2, 2, 256, 4, tq.LAYOUT_ROWS, signs, device="cpu")
+    vc = tq.PackedCache(2, 2, 256, 2, tq.LAYOUT_GROUP8, signs, device="cpu")
+    q = torch.zeros(2, 8, 128)
+    short = tq.DecodeBuffers(2, 8, 2, 128, 0.0, device="cpu", want_scores=True)
+    with pytest.raises(ValueError, match="scores"):
+        tq.decode_attn(kc, vc, q, 256, 0.1, buffers=short)
+    other_heads = tq.DecodeBuffers(2, 4, 2, 256, 0.0, device="cpu")
+    with pytest.raises(ValueError, match="out"):
+        tq.decode_attn(kc, vc, q, 256, 0.1, buffers=other_heads)
+    with pytest.raises(ValueError, match="batch"):
+        tq.decode_attn(kc, vc, torch.zeros(3, 8, 128), 256, 0.1)
+    with pytest.raises(ValueError, match="seq_lens"):
+        tq.decode_attn(kc, vc, q, 256, 0.1, seq_lens=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="seq_lens"):
+        tq.decode_attn(kc, vc, q, 256, 0.1, seq_lens=torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="kv heads"):
+        tq.decode_attn(kc, vc, torch.zeros(2, 7, 128), 256, 0.1)
+    new = torch.zeros(2, 1, 2, 128)
+    with pytest.raises(ValueError, match="out"):
+        tq.decode_attn_append(kc, vc, new, new, q, 256, 0.1, buffers=other_heads)
+    mq = tq.MultiQueryBuffers(2, 3, 8, 2, 256, device="cpu")
+    with pytest.raises(ValueError, match="out"):
+        tq.decode_attn_multi(kc, vc, torch.zeros(2, 4, 8, 128), 256, 0.1, buffers=mq)
+    pk = tq.PagedCache(2, 2, 64, 8, 4, 4, tq.LAYOUT_ROWS, signs, device="cpu")
+    pv = tq.PagedCache(2, 2, 64, 8, 4, 2, tq.LAYOUT_GROUP8, signs, block_table=pk.block_table, device="cpu")
+    pb = tq.PagedDecodeBuffers(1, 8, 2, 256, device="cpu")
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out"):
+        tq.paged_decode_attn(pk, pv, q, lens, 256, 0.1, buffers=pb)
+    with pytest.raises(ValueError, match="seq_lens"):
+        tq.paged_decode_attn(pk, pv, q, None, 256, 0.1)
+    # a correctly shaped call gets past every shape check and stops at the device check
+    ok = tq.DecodeBuffers(2, 8, 2, 256, 0.0, device="cpu", want_scores=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        tq.decode_attn(kc, vc, q, 256, 0.1, buffers=ok)

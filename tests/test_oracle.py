@@ -370,6 +370,38 @@ def test_multi_query_attention_pins(golden_codebooks):
     assert np.allclose(out0, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
 
 
+def test_attention_excluded_positions_equal_removed_positions(golden_codebooks):
+    """Positions that are not part of the context (valid = False) behave exactly as if they
+    had been removed from the cache: the result equals attention over the compacted cache,
+    and differs from attending to them as zero vectors (which would add exp(0 - LSE)
+    to the denominator)."""
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=200, golden=golden_codebooks)
+    scale = 1 / math.sqrt(D)
+    bsz, T = kh.shape[0], kh.shape[2]
+    valid = np.ones((bsz, T), dtype=bool)
+    valid[0, 64:128] = False          # a missing page in the middle of sequence 0
+    valid[-1, :64] = False            # and the first page of the last sequence
+    out, lse, sc = o.decode_attention(q, kh, vh, scale, valid=valid)
+    for b in range(bsz):
+        keep = np.nonzero(valid[b])[0]
+        ref, rlse, rsc = o.decode_attention(q[b:b + 1], kh[b:b + 1][:, :, keep], vh[b:b + 1][:, :, keep], scale)
+        assert np.allclose(out[b], ref[0], rtol=1e-13, atol=1e-15)
+        assert np.allclose(lse[b], rlse[0], rtol=1e-13)
+        assert np.all(np.isneginf(sc[b][:, ~valid[b]]))
+        assert np.allclose(sc[b][:, keep], rsc[0], rtol=1e-13)
+    zeroed_k, zeroed_v = kh.copy(), vh.copy()
+    zeroed_k[0, :, 64:128] = 0.0
+    zeroed_v[0, :, 64:128] = 0.0
+    as_zero, zlse, _ = o.decode_attention(q, zeroed_k, zeroed_v, scale)
+    assert np.all(zlse[0] > lse[0])
+    # no valid position at all: o = 0, LSE = -inf; with seq_lens the two rules combine
+    none, nlse, _ = o.decode_attention(q, kh, vh, scale, valid=np.zeros((bsz, T), dtype=bool))
+    assert np.all(none == 0.0) and np.all(np.isneginf(nlse))
+    part, plse, _ = o.decode_attention(q, kh, vh, scale, seq_lens=[100] * bsz, valid=valid)
+    ref0, rl0, _ = o.decode_attention(q[:1], kh[:1][:, :, :64], vh[:1][:, :, :64], scale)
+    assert np.allclose(part[0], ref0[0], rtol=1e-13, atol=1e-15) and np.allclose(plse[0], rl0[0])
+
+
 def test_sparse_v_limits_and_bound(golden_codebooks):
     s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=200, golden=golden_codebooks)
     q = q * 6.0     # sharpen the attention so some rows fall under the threshold
@@ -389,6 +421,67 @@ def test_sparse_v_limits_and_bound(golden_codebooks):
             bound = (p[b, h] * dropped[b, h] * np.linalg.norm(vh[b, h // g], axis=1)).sum()
             assert np.linalg.norm(sparse[b, h] - dense[b, h]) <= bound + 1e-12
     assert dropped.any() and (~dropped).any()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_near_boundary_band_is_absolute_and_inclusive(bits, golden_codebooks):
+    """The band that excuses a code mismatch: |u - t_j| <= 1e-6 in unit-vector units.
+    Constructed values at +-0.5e-6 and +-1.5e-6 of every boundary, plus exactly on it, so a
+    band read as relative (|u - t| <= 1e-6 |t|), a strict '<' or a wider band each fails."""
+    c, t = golden_codebooks[bits]
+    band = 1e-6
+    inside = np.concatenate([t - 0.5 * band, t + 0.5 * band, t])
+    outside = np.concatenate([t - 1.5 * band, t + 1.5 * band])
+    # the cells are far wider than the band: no constructed value is near a second boundary
+    assert np.min(np.diff(t)) > 100 * band
+    assert np.all(o.near_boundary_mask(inside, t, band))
+    assert not np.any(o.near_boundary_mask(outside, t, band))
+    # a value at exactly band + a small margin is outside; exactly at the edge is inside
+    # (both chosen so the fp64 distance is exact: a boundary with a short mantissa)
+    edge = np.array([0.0 + band, 0.0 - band, 0.0 + 2 * band])
+    assert list(o.near_boundary_mask(edge, t, band)) == [True, True, False]
+    # the centroids themselves are half a cell away: never flagged
+    assert not np.any(o.near_boundary_mask(c, t, band))
+    # shapes: the mask keeps the leading axes of u
+    u = np.stack([inside[:4], outside[:4]])
+    assert o.near_boundary_mask(u, t, band).tolist() == [[True] * 4, [False] * 4]
+
+
+def test_sparse_v_borderline_band_sign_and_empty_rows():
+    """Rows whose keep decision is within the score tolerance: |s - (LSE + ln tau)| <=
+    1e-3 max|s|.  Scores are placed at +-0.5 and +-1.5 times the tolerance around the
+    threshold; a sign slip in ln tau, an absolute 1e-3 band or a band on |s| alone fails."""
+    rel, tau = 1e-3, 1e-4
+    lse = np.array([[3.0, -2.0]])
+    thr = lse + math.log(tau)              # about -6.21 and -11.21
+    smax = np.array([[40.0, 25.0]])       # one large score per row sets max|s|
+    tol = rel * smax
+    offs = np.array([-1.5, -0.5, 0.0, 0.5, 1.5])
+    rows = np.zeros((1, 2, 6))
+    for h in range(2):
+        rows[0, h, :5] = thr[0, h] + offs * tol[0, h]
+        rows[0, h, 5] = smax[0, h]
+    got = o.sparse_v_borderline(rows, lse, tau, rel)
+    want = np.array([False, True, True, True, False, False])
+    assert got.tolist() == [[want.tolist(), want.tolist()]]
+    # the band scales with the row's largest |s|, not with 1e-3 alone: at +-0.5 tol = 0.02
+    # (row 0) an absolute 1e-3 band would flag nothing
+    assert 0.5 * tol[0, 0] > 10 * rel
+    # the threshold sits below the LSE (ln tau < 0): the mirror image LSE - ln tau is far
+    mirror = lse[..., None] - math.log(tau) + np.zeros((1, 2, 1))
+    assert not o.sparse_v_borderline(np.concatenate([mirror, rows[..., 5:]], -1), lse, tau, rel).any()
+    # the flagged rows are exactly those whose weight exp(s - LSE) lies within a factor
+    # exp(tol) of tau
+    p = np.exp(rows - lse[..., None])
+    near = np.abs(np.log(p / tau)) <= tol[..., None] * (1 + 1e-9)
+    assert np.array_equal(near, got)
+    # rows with no tokens (LSE = -inf, every score -inf) and -inf entries of a live row are
+    # never borderline, and no invalid operation is formed
+    mixed = np.array([[[-np.inf] * 6, [-np.inf, thr[0, 1], 1.0, -np.inf, 2.0, -np.inf]]])
+    mlse = np.array([[-np.inf, lse[0, 1]]])
+    with np.errstate(all="raise"):
+        m = o.sparse_v_borderline(mixed, mlse, tau, rel)
+    assert m.tolist() == [[[False] * 6, [False, True, False, False, False, False]]]
 
 
 def _page_figures():
