@@ -296,7 +296,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
     // Buffers: the split's span of one plane, or (paged) the whole pools, whose size the host
     // keeps below 3 GiB.  tile_tok(tile) is the tile's first position counted in tokens of
-    // the buffer; a tile with no page gets an offset past the end, so it reads zeros.
+    // the buffer; a tile with no page gets an offset past the end, so its loads read zeros
+    // without touching memory, and its positions are masked out of the softmax.
     const uint32_t span_tok = PAGED ? (uint32_t)a.n_pages * a.n_kv_heads * a.k.capacity : (uint32_t)n_tiles * kTile;
     const __amdgpu_buffer_rsrc_t krs =
         PAGED ? make_rsrc(a.k.codes, span_tok * KROW) : make_rsrc(a.k.plane(b, kvh) + (size_t)t_begin * KROW, span_tok * KROW);
@@ -506,10 +507,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     auto tile_body = [&](int tile, auto prefetch_tag) {
       constexpr bool PREFETCH = decltype(prefetch_tag)::value;
       const int t0 = t_begin + tile * kTile;
+      const uint32_t tok = tile_tok(tile);
       uint32_t vw[2][4];
       uint32_t nvw = 0u;
       if constexpr (!SPARSE) {
-        const uint32_t tok = tile_tok(tile);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const auto w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + tile_off(tok, 32) + c * 1024, 0, 0);
@@ -609,6 +610,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       // exponent below would give exp2(-inf - -inf): such tiles take the reference-move
       // path, whose exponents treat -inf explicitly.
       bool causal_tile = false;
+      // Paged: a tile on a table entry of no page is not part of the sequence; its positions
+      // leave the softmax (score -inf).  Like a causal tile it may meet a -inf reference, so it
+      // takes the reference-move path (uniform branch).
+      if (PAGED && tok == kNoPage) {
+        causal_tile = true;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] = -INFINITY;
+      }
       if (MULTI && t0 + kTile > T - n_q + 1) {
         causal_tile = true;
 #pragma unroll

@@ -226,8 +226,11 @@ size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_h
  *   codes        [n_pages][n_kv_heads][page_tokens * d * bits / 8] bytes, 16-byte aligned
  *   norms        [n_pages][n_kv_heads][page_tokens] fp16 bit patterns, 16-byte aligned
  *   block_table  device int32 [batch][max_pages], 4-byte aligned; an entry outside
- *                [0, n_pages) means "no page": appends skip positions that map to it and
- *                decode reads them as zero codes and norms (never out of the pool)
+ *                [0, n_pages) means "no page": those positions are not part of the sequence
+ *                ([inferrs] §二: tokens live only in allocated pages).  Appends skip them and
+ *                decode leaves them out of the softmax (no score, no value; nothing is read
+ *                outside the pool); a sequence with no position on a page gets o = 0 and
+ *                LSE = -inf
  *   centroids, boundaries, signs as for tq_cache.
  * page_tokens: a positive multiple of 64.  The pool's code bytes must stay below 3 GiB
  * (32-bit offsets inside the decode kernel).  The K and V caches of a layer share one
@@ -268,7 +271,10 @@ int tq_paged_quantize_append_kv(const tq_paged_cache *k, const tq_paged_cache *v
  * scores, sequence b attending over positions 0 .. T_b - 1, T_b = clamp(seq_lens[b], 0,
  * max_ctx_len), its pages found through the block table.  Keys of 3 or 4 bits (ROWS),
  * values of 2 bits (GROUP8), n_q_heads / n_kv_heads <= 8; otherwise TQ_ERR_UNSUPPORTED.
- * Same kernel and arithmetic as the contiguous call: equal codes give equal outputs.
+ * Positions on a "no page" entry below T_b are left out of the softmax (see
+ * tq_paged_cache).  Same kernel and arithmetic as the contiguous call: a sequence whose
+ * positions 0 .. T_b - 1 all lie on pages gets the output the contiguous call gives for
+ * equal codes, bit for bit.
  *   seq_lens     device int32 [batch] (required)
  *   max_ctx_len  upper bound of the lengths, <= max_pages * page_tokens (TQ_ERR_CAPACITY)
  *   out, lse     as for tq_decode_attn

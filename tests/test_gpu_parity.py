@@ -218,7 +218,7 @@ def test_dequantize_matches_oracle(layout, signs, golden_codebooks):
 
 
 def _decode_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, tau=0.0,
-                 seq_lens=None, q_dtype=None, scale=None):
+                 seq_lens=None, q_dtype=None, scale=None, want_caches=False):
     g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
     kc = _new_cache(batch, hkv, cap, bits_k, 0, signs)
     vc = _new_cache(batch, hkv, cap, bits_v, 1, signs)
@@ -244,14 +244,38 @@ def _decode_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, tau
         allowance, nb = parity.sparse_allowance(scores, lse, vh, tau, hq // hkv)
     worst = parity.check_rows(buf.out.cpu().numpy(), out, "decode out", allowance=allowance)
     _say(f"  worst rel err {worst:.2e} borderline {nb}")
+    if want_caches:
+        return buf, out, (kc, vc, g)
     return buf, out
 
 
 def test_decode_tiny_workload(signs, golden_codebooks):
-    """The smallest workload exactly as stated: 1 kv head, 1 query head, 1024 fp32 tokens."""
+    """The smallest workload exactly as stated: 1 kv head, 1 query head, 1024 fp32 tokens with
+    4 outlier channels x10, K 4-bit and V 2-bit, fp32 query, scale 1/sqrt(128), no Sparse V.
+    Every code and norm of the 1024 keys and values is checked against the oracle's own
+    quantization (code mismatches allowed only within 1e-6 of a boundary, counted), then the
+    attention against the oracle on the GPU-written cache, and end to end against the oracle
+    on its own cache."""
     _say("decode tiny")
     w = inputs.WORKLOADS["tiny"]
-    _decode_case(w, signs, golden_codebooks, 1, 1, 1, 1024, 1024, 4, 2)
+    buf, out, (kc, vc, g) = _decode_case(w, signs, golden_codebooks, 1, 1, 1, 1024, 1024, 4, 2,
+                                         want_caches=True)
+    s64 = signs.numpy().astype(np.float64)
+    k64, v64 = parity.to_f64(g["k"]), parity.to_f64(g["v"])
+    near_k = parity.check_quantize(kc, k64, 0, s64, golden_codebooks[4])
+    near_v = parity.check_quantize(vc, v64, 0, s64, golden_codebooks[2])
+    _say(f"  tiny: near-boundary coordinates K {near_k} / {1024 * 128}, V {near_v} / {1024 * 128}")
+    # end to end: the oracle quantizes, packs and attends on its own; the GPU output may differ
+    # from it only through near-boundary codes (none are expected at this size)
+    ck, tk = golden_codebooks[4]
+    cv, tv = golden_codebooks[2]
+    codes_k, n_k, _ = o.quantize(k64[0, :, 0], s64, ck, tk)
+    codes_v, n_v, _ = o.quantize(v64[0, :, 0], s64, cv, tv)
+    kh = o.dequantize(o.unpack(o.pack(codes_k, 4, 0), 1024, 128, 4, 0), n_k, s64, ck)[None, None]
+    vh = o.dequantize(o.unpack(o.pack(codes_v, 2, 1), 1024, 128, 2, 1), n_v, s64, cv)[None, None]
+    e2e, _, _ = o.decode_attention(parity.to_f64(g["q"]), kh, vh, 1.0 / math.sqrt(128))
+    if near_k == 0 and near_v == 0:
+        parity.check_rows(buf.out.cpu().numpy(), e2e, "tiny end to end")
 
 
 @pytest.mark.parametrize("case", [
@@ -340,19 +364,22 @@ def test_decode_append_matches_oracle(case, signs, golden_codebooks):
 
 def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtype=None, hole=None, seed=0,
                 fused=False):
-    """Paged caches with shuffled pages (and optionally one table entry of no page) filled by
+    """Paged caches with shuffled pages (and optionally table entries of no page) filled by
     the paged append (a long call, then a decode step with per-sequence starts: the paged
     append and paged decode, or, fused, the one-launch paged append-and-attend over a slot
-    that held garbage); the pages, gathered in table order, must hold the oracle's codes,
-    and paged decode must equal the contiguous decode on the gathered cache bit for bit and
-    the oracle within tolerance."""
+    that held garbage); the pages, gathered in table order, must hold the oracle's codes.
+    A position on a table entry of no page is not part of its sequence ([inferrs] §二,
+    PagedAttention: tokens live only in allocated pages): the oracle leaves it out of the
+    softmax.  Paged decode must equal the oracle within tolerance, and, for every sequence
+    without such a hole, the contiguous decode on the gathered cache bit for bit."""
+    holes = [] if hole is None else ([hole] if isinstance(hole[0], int) else list(hole))
     max_ctx = max(seq_lens)
     max_pages = (max_ctx + page - 1) // page + 1
     n_pages = batch * max_pages + 3
     rng = np.random.default_rng(seed)
     table = torch.tensor(rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages), dtype=torch.int32)
-    if hole is not None:
-        table[hole] = -1
+    for hb, hs in holes:
+        table[hb, hs] = -1
     kc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, bits_k, 0, signs.to(DEV),
                        block_table=table.to(DEV).contiguous(), device=DEV)
     vc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, 2, 1, kc.signs, block_table=kc.block_table, device=DEV)
@@ -404,20 +431,26 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
     torch.cuda.synchronize()
     s64 = signs.numpy().astype(np.float64)
     lens = list(seq_lens)
+    valid = np.ones((batch, max_ctx), dtype=bool)     # positions on a page of the table
+    for b in range(batch):
+        for slot in range(max_pages):
+            if int(table[b, slot]) < 0:
+                valid[b, slot * page:(slot + 1) * page] = False
     for fc, x, table_b in ((kf, k, golden[bits_k]), (vf, v, golden[2])):
         for b in range(batch):
-            for h in range(hkv):
-                upto = max_ctx
-                if hole is not None and hole[0] == b:
-                    upto = min(upto, hole[1] * page)     # positions from the hole on were skipped
-                if upto > 0:
-                    parity.check_plane(fc, b, h, parity.to_f64(x[b, :upto, h]), 0, s64, table_b)
+            # each run of positions on allocated pages holds the oracle's codes (the appends
+            # skipped the positions with no page)
+            edges = np.flatnonzero(np.diff(np.concatenate(([0], valid[b].astype(np.int8), [0]))))
+            for a, e in zip(edges[0::2], edges[1::2]):
+                for h in range(hkv):
+                    parity.check_plane(fc, b, h, parity.to_f64(x[b, a:e, h]), int(a), s64, table_b)
     ref = tq.decode_attn(kf, vf, q, max_ctx, scale, seq_lens=sl)
     torch.cuda.synchronize()
-    assert torch.equal(got.out, ref.out) and torch.equal(got.lse, ref.lse)
+    whole = [b for b in range(batch) if valid[b, :max(lens[b], 0)].all()]
+    assert torch.equal(got.out[whole], ref.out[whole]) and torch.equal(got.lse[whole], ref.lse[whole])
     kh = parity.oracle_cache_view(kf, s64, golden[bits_k], max_ctx)
     vh = parity.oracle_cache_view(vf, s64, golden[2], max_ctx)
-    out, lse, _ = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=lens)
+    out, lse, _ = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=lens, valid=valid)
     fin = np.isfinite(lse)
     got_lse = got.lse.cpu().numpy()
     assert np.all(np.isneginf(got_lse[~fin]))
@@ -436,6 +469,10 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
     ("llama8k", 3, 32, 8, 64, [700, 1, 0], 4, None, None, True),
     ("batch32k", 2, 8, 2, 256, [1300, 513], 3, "f32", (1, 2), True),
     ("ctx131k", 1, 16, 2, 128, [1500], 4, None, None, True),
+    # a sequence with no page at all (o = 0, LSE = -inf) beside one with two holes, the new
+    # token of the fused step falling into a hole
+    ("llama8k", 3, 16, 4, 64, [300, 450, 129], 4, None, [(0, s) for s in range(6)] + [(1, 1), (1, 7), (2, 2)], True),
+    ("batch32k", 2, 8, 2, 64, [640, 200], 3, "f16", [(0, 0), (0, 9), (1, 3)], False),
 ])
 def test_paged_cache_matches_contiguous_and_oracle(case, signs, golden_codebooks):
     name, batch, hq, hkv, page, lens, bk, xdt, hole, fused = case
