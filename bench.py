@@ -9,9 +9,13 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   prefill:          quantize a 32-layer cache of 32768 tokens (K and V of every layer).
 Inputs are resident in HBM before the timed region.  Decode workloads rotate over enough
 copies of the cache (one per step, like the layers of a model) that the reads come from
-HBM rather than the 256 MB Infinity Cache.  The steps are recorded once into a HIP graph
-and the graph is replayed, so the timed region holds GPU work only (no Python launch
-overhead between kernels); --eager times plain launches instead.
+HBM rather than the 256 MB Infinity Cache, and every timed batch starts cold: right
+before it, a streaming read of 1 GiB of other data evicts the Infinity Cache and the L2s,
+so no copy the timed steps read is still cached from the untimed replays.  The steps are
+recorded once into a HIP graph and the graph is replayed, so the timed region holds GPU
+work only (no Python launch overhead between kernels); --eager times plain launches
+instead.  The default workload is the batched long-context decode (batch 16, 32 query
+heads, 8 kv heads, 32768 tokens, K3/V2), the largest decode configuration.
 
 Prints one JSON line: the throughput, the roofline of the dominant kernel (the single
 decode-attention kernel, or quantize for prefill) timed with HIP events on the stream the
@@ -56,7 +60,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llama8k",
+    p.add_argument("--workload", default="batch32k",
                    choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k", "search1m"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
@@ -73,6 +77,11 @@ def parse():
     p.add_argument("--kernel", default=DECODE_KERNEL,
                    help="regular expression over the kernel names (template arguments included)")
     p.add_argument("--name", default=None)
+    p.add_argument("--record", default=None,
+                   help="traffic record name (profiles/traffic_<record>_<workload>.txt); default decode or quantize")
+    p.add_argument("--sum-instances", action="store_true",
+                   help="traffic per step = sum over the matching kernels (one dispatch each per step), "
+                        "e.g. Sparse V's key pass and value pass")
     p.add_argument("--command", default="")
     return p.parse_args()
 
@@ -118,12 +127,35 @@ def append_bytes(w, bits_k, bits_v, hkv, batch):
 
 
 def cpu_cores():
+    """Host cores this process may run on (its affinity set)."""
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_context():
+    """The BLAS thread count (the oracle's dense-rotation matrix products may use that many
+    threads; the rest of the oracle is single-threaded NumPy) and the CPU model string."""
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        n = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        return int(n)
+        blas = max((int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=None)
     except Exception:
-        return len(os.sched_getaffinity(0))
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"blas_threads": blas, "cpu_model": model}
+
+
+def with_cpu_context(rec):
+    rec.update(cpu_context())
+    return rec
 
 
 def main():
@@ -137,6 +169,11 @@ def main():
     if args.summarize_instmix:
         summarize_instmix(args)
         return
+    try:  # the oracle's BLAS calls use at most the cores this process may run on
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=cpu_cores(), user_api="blas")
+    except Exception:
+        pass
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): it measures the single-GPU "
               "kernel; the path would shard by (batch, kv head) with no exchange.", file=sys.stderr)
@@ -198,9 +235,10 @@ class Timer:
     untimed (at least 3 times and 50 ms), then once between the events; or (eager) launched
     directly."""
 
-    def __init__(self, torch, eager):
+    def __init__(self, torch, eager, flush=None):
         self.torch = torch
         self.eager = eager
+        self.flush = flush  # run (untimed) before every timed batch: leaves the caches cold
 
     def per_iteration_ms(self, fn, n, warmup):
         return self.per_iteration_stats(fn, n, warmup, batches=1)[0]
@@ -217,6 +255,7 @@ class Timer:
         times = []
         if self.eager:
             for _ in range(batches):
+                self._cold()
                 start.record(stream)
                 for i in range(n):
                     fn(i)
@@ -240,6 +279,7 @@ class Timer:
                 if r >= 2 and t_warm >= 50.0:
                     break
             for _ in range(batches):
+                self._cold()
                 start.record(stream)
                 graph.replay()
                 end.record(stream)
@@ -248,6 +288,11 @@ class Timer:
             del graph
         times.sort()
         return times[len(times) // 2], times[0], times[-1]
+
+    def _cold(self):
+        if self.flush is not None:
+            self.flush()
+        self.torch.cuda.synchronize()
 
 
 def stream_read_gbs(torch, tq, log):
@@ -272,6 +317,19 @@ def stream_read_gbs(torch, tq, log):
     log(f"[bench] streaming-read probe: {gbs:.0f} GB/s")
     del bufs
     return gbs
+
+
+def cache_flush(torch, tq):
+    """A callable that streams 1 GiB of unrelated data through the read path (the library's
+    plain read kernel): more than the 256 MB Infinity Cache plus the 8 L2s, so whatever the
+    benchmark read before is evicted and the next timed batch reads its inputs from HBM."""
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def flush():
+        tq.probe_stream_read(buf, sink)
+
+    return flush
 
 
 def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
@@ -319,7 +377,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         decode_only(i)
 
     step = append_and_decode if dense_single else two_launches
-    timer = Timer(torch, args.eager)
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
     steps = args.steps
     ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     kv_tokens = batch * ctx
@@ -330,8 +388,20 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     ms_d = timer.per_iteration_ms(decode_only, n_rep, 2) if dense_single else ms_k
     ms_a = timer.per_iteration_ms(append, n_rep, 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
+    sparse_info = None
     if dense_single:
         nbytes += append_bytes(w, bk, bv, hkv, batch)
+    elif tau > 0:
+        # Sparse V: the keys of every token plus the value rows that some head of the group
+        # keeps (p = exp(s - LSE) >= tau), counted from this call's own scores and LSE
+        kept, kept_tiles, n_tiles = sparse_kept_rows(tq, torch, caches[0], q, ctx, scale, tau, batch, hq, hkv, dev)
+        k_bytes = batch * hkv * ctx * (D * bk // 8 + 2)
+        nbytes = k_bytes + kept * (D * bv // 8 + 2)
+        sparse_info = {"kept_value_rows": kept, "kept_value_rows_frac": kept / (batch * hkv * ctx),
+                       "tiles_with_kept_row_frac": kept_tiles / n_tiles, "key_bytes": k_bytes,
+                       "dense_bytes": decode_bytes(w, bk, bv, hkv, batch, ctx)}
+        log(f"[bench] Sparse V: {kept} of {batch * hkv * ctx} value rows kept by a group "
+            f"({100 * kept / (batch * hkv * ctx):.2f}%), {100 * kept_tiles / n_tiles:.1f}% of 64-token tiles hold one")
     achieved = nbytes / (ms_k / 1e3) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us ({'one fused launch' if dense_single else 'append + decode'}), "
         f"decode-only call {ms_d * 1e3:.1f} us, standalone append (K+V) {ms_a * 1e3:.1f} us, "
@@ -356,9 +426,31 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
                      "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
         "_kernel": "decode" if dense_single else "decode_sparse",
     }
+    if sparse_info is not None:
+        result["roofline"]["bytes_note"] = ("algorithmic bytes: every key (codes + norm) plus the value rows "
+                                            "kept by the union of the group's heads")
+        result["sparse_v"] = sparse_info
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(w, tau, caches[0], host_k, host_v, q, signs, np, torch, log)
     return result
+
+
+def sparse_kept_rows(tq, torch, cache_pair, q, ctx, scale, tau, batch, hq, hkv, dev):
+    """Value rows a Sparse-V call must read: (batch, kv head, position) triples that some
+    query head of the group keeps (p = exp(s - LSE) >= tau), and the 64-token tiles that
+    hold at least one of them, from one call's score and LSE outputs (measurement only)."""
+    kc, vc = cache_pair
+    b2 = tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=dev, want_scores=True)
+    tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=b2)
+    torch.cuda.synchronize()
+    g = hq // hkv
+    keep = (torch.exp(b2.scores - b2.lse[..., None]) >= tau).view(batch, hkv, g, ctx).any(dim=2)
+    n_tiles = batch * hkv * ((ctx + 63) // 64)
+    pad = (-ctx) % 64
+    tiles = torch.nn.functional.pad(keep, (0, pad)).view(batch, hkv, -1, 64).any(dim=-1)
+    kept, kept_tiles = int(keep.sum()), int(tiles.sum())
+    del b2
+    return kept, kept_tiles, n_tiles
 
 
 def cpu_baseline_decode(w, tau, cache_pair, host_k, host_v, q, signs, np, torch, log):
@@ -393,10 +485,10 @@ def cpu_baseline_decode(w, tau, cache_pair, host_k, host_v, q, signs, np, torch,
             break
     value = reps * ctx / el
     log(f"[bench] cpu oracle: {reps} sample steps in {el:.1f} s")
-    return {"value": value, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
+    return with_cpu_context({"value": value, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
             "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
                       f"{ctx} tokens: quantize+pack the appended token, unpack+dequantize+attend; "
-                      f"{reps} repetitions"}
+                      f"{reps} repetitions"})
 
 
 class _GatheredPlanes:
@@ -460,7 +552,7 @@ def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
         kc, vc = caches[i % copies]
         tq.paged_decode_attn_append(kc, vc, k_new, v_new, q, lens, ctx, scale, buffers=bufs)
 
-    timer = Timer(torch, args.eager)
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
     ms_per_step = timer.per_iteration_ms(step, args.steps, args.warmup)
     value = batch * ctx / (ms_per_step / 1e3)
     n_rep = max(args.steps, 2 * copies)
@@ -520,7 +612,7 @@ def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):
     def step(i):
         tq.ip_search(dbs[i % copies], q, n, k, buffers=bufs)
 
-    timer = Timer(torch, args.eager)
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
     ms_per_step = timer.per_iteration_ms(step, args.steps, args.warmup)
     ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step, max(args.steps, 2 * copies), 2, batches=5)
     nbytes = per_copy  # the packed database, read once per call
@@ -572,9 +664,9 @@ def cpu_baseline_search(spec, db, q, signs, np, torch, log):
             break
     value = reps * sample / n / el
     log(f"[bench] cpu oracle: {reps} sample searches in {el:.1f} s")
-    return {"value": value, "unit": "queries/s", "cores": cpu_cores(), "kind": "oracle",
+    return with_cpu_context({"value": value, "unit": "queries/s", "cores": cpu_cores(), "kind": "oracle",
             "sample": f"1 query over the first {sample} of {n} vectors, scaled to the whole database; "
-                      f"{reps} repetitions"}
+                      f"{reps} repetitions"})
 
 
 def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
@@ -620,7 +712,7 @@ def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
         append(i)
         attend(i)
 
-    timer = Timer(torch, args.eager)
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
     steps = args.steps
     ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     value = batch * ctx / (ms_per_step / 1e3)
@@ -687,10 +779,10 @@ def cpu_baseline_multi(w, cache_pair, host_k, host_v, q, signs, np, torch, log):
             break
     value = reps * ctx / el
     log(f"[bench] cpu oracle: {reps} sample steps in {el:.1f} s")
-    return {"value": value, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
+    return with_cpu_context({"value": value, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
             "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
                       f"{ctx} tokens, {n_q} query positions: quantize+pack the appended tokens, "
-                      f"unpack+dequantize+attend; {reps} repetitions"}
+                      f"unpack+dequantize+attend; {reps} repetitions"})
 
 
 def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
@@ -714,7 +806,7 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
         for (kc, vc), (k, v) in zip(caches, xs):
             tq.quantize_append_kv(kc, vc, k, v, 0)
 
-    timer = Timer(torch, args.eager)
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
     steps = max(1, args.steps // 20)
     ms_per_step = timer.per_iteration_ms(step, steps, max(1, args.warmup // 20))
     tokens = layers * ctx
@@ -752,9 +844,9 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
             el = time.perf_counter() - t0
             if el > 10.0 or reps >= 100:
                 break
-        result["cpu_baseline"] = {"value": reps * 1024 / el, "unit": result["unit"], "cores": cpu_cores(),
-                                  "kind": "oracle",
-                                  "sample": f"layer 5, 1024 positions x {hkv} kv heads, K4/V3, quantize+pack, {reps} reps"}
+        result["cpu_baseline"] = with_cpu_context({
+            "value": reps * 1024 / el, "unit": result["unit"], "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"layer 5, 1024 positions x {hkv} kv heads, K4/V3, quantize+pack, {reps} reps"})
     return result
 
 
@@ -836,8 +928,15 @@ def summarize_traffic(args):
         n = sum(counts[k] for k in keys)
         return keys, sum(table[k] * counts[k] for k in keys) / n, {k: counts[k] for k in keys}
 
-    kf, mf, df = weighted(fetch, nf)
-    kw, mw, dw = weighted(write, nw)
+    def summed(table, counts):
+        keys = sorted(k for k in table if re.search(args.kernel, k) and CALIBRATION_KERNEL not in k)
+        if not keys:
+            sys.exit(f"no kernel matching {args.kernel!r} in {sorted(table)}")
+        return keys, sum(table[k] for k in keys), {k: counts[k] for k in keys}
+
+    agg = summed if args.sum_instances else weighted
+    kf, mf, df = agg(fetch, nf)
+    kw, mw, dw = agg(write, nw)
     cf, cw = pick(fetch, CALIBRATION_KERNEL), pick(write, CALIBRATION_KERNEL)
     scale_f = COPY_BYTES / (fetch[cf] * 1024.0)
     scale_w = COPY_BYTES / (write[cw] * 1024.0)
@@ -850,8 +949,9 @@ def summarize_traffic(args):
            "copy_bytes": COPY_BYTES, "fetch_scale": scale_f, "write_scale": scale_w,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
            "dispatches": {"fetch": df, "write": dw}, "sources_digest": kernel_sources_digest(),
+           "per_step": "sum of the matching kernels" if args.sum_instances else "dispatch-weighted mean",
            "command": args.command}
-    kname = "decode" if args.kernel.startswith(DECODE_KERNEL) else "quantize"
+    kname = args.record or ("decode" if args.kernel.startswith(DECODE_KERNEL) else "quantize")
     with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{args.workload}.txt"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
