@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn_append.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp, i32,
                                             vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
         L.tq_decode_attn_multi_workspace_bytes.restype = sz
+        L.tq_decode_attn_append_noalloc.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp,
+                                                    vp, i32, vp, i32, i32, vp, i32, f32, vp, vp, vp]
         L.tq_dequantize.argtypes = [ctypes.POINTER(CacheStruct), i32, i32, vp, i32, vp]
         PP = ctypes.POINTER(PagedCacheStruct)
         L.tq_paged_quantize_append_kv.argtypes = [PP, PP, vp, vp, i32, vp, i32, vp]
@@ -90,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_dequantize", "tq_probe_stream_read",
+                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
                      "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search"):
             getattr(L, name).restype = i32
         _lib = L
@@ -383,6 +385,35 @@ def decode_attn_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new,
         _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_append")
     return buffers
+
+
+def decode_attn_append_noalloc(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new, q, ctx_len: int,
+                               scale: float, seq_lens=None, out=None, lse=None, stream=None):
+    """decode_attn_append through the allocation-free entry point: the library's static
+    scratch replaces the workspace.  out [B, Hq, d] and lse [B, Hq] (float32, device) may be
+    given by the caller; returns (out, lse)."""
+    torch = _torch()
+    _check_query(q, k_cache, 3, "decode_attn_append_noalloc")
+    bsz, hq, d = q.shape
+    for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
+        if x.dim() != 4 or x.shape[0] != bsz or x.shape[1] != 1 or x.shape[2] != cache.n_kv_heads or x.shape[3] != d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    _check_seq_lens(seq_lens, bsz, "decode_attn_append_noalloc")
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    _shape(out, (bsz, hq, d), "decode_attn_append_noalloc: out")
+    _shape(lse, (bsz, hq), "decode_attn_append_noalloc: lse")
+    ks, vs = k_cache.struct(), v_cache.struct()
+    sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
+    _check(lib().tq_decode_attn_append_noalloc(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
+        _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len, float(scale), _dev(out, "out"), _dev(lse, "lse"),
+        _stream_ptr(stream)), "tq_decode_attn_append_noalloc")
+    return out, lse
 
 
 class PagedCache:

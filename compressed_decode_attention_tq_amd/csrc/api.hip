@@ -254,6 +254,52 @@ int check_paged_pair(const tq_paged_cache *k, const tq_paged_cache *v) {
   return TQ_OK;
 }
 
+int setup_decode_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                        const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len,
+                        float scale, float *out, float *lse, DecodeArgs &a, WorkspaceLayout &w) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
+      k->signs != v->signs)
+    return TQ_ERR_INVALID_ARG;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / k->n_kv_heads;
+  if (group > 16) return TQ_ERR_UNSUPPORTED;
+  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
+  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  w = workspace_layout(k->batch, n_q_heads, k->n_kv_heads, ctx_len, false);
+  a = DecodeArgs{};
+  a.k = view_of(k);
+  a.v = view_of(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = ctx_len;
+  a.scale = scale;
+  a.n_q = 1;
+  a.vgroups = 1;
+  a.vg_size = group;
+  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
+  a.fplan = plan_fused(k->batch, k->n_kv_heads, ctx_len);
+  a.out = out;
+  a.lse = lse;
+  return TQ_OK;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -409,49 +455,13 @@ int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, 
                           int x_dtype, const void *q, int q_dtype, int n_q_heads,
                           const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *hip_stream) {
-  int st = check_cache(k);
+  DecodeArgs a{};
+  WorkspaceLayout w{};
+  const int st = setup_decode_append(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, out,
+                                     lse, a, w);
   if (st != TQ_OK) return st;
-  st = check_cache(v);
-  if (st != TQ_OK) return st;
-  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
-      k->signs != v->signs)
-    return TQ_ERR_INVALID_ARG;
-  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
-  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
-    return TQ_ERR_INVALID_ARG;
-  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
-  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
-  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
-  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
-  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
-  const int group = n_q_heads / k->n_kv_heads;
-  if (group > 16) return TQ_ERR_UNSUPPORTED;
-  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
-  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
-  const WorkspaceLayout w = workspace_layout(k->batch, n_q_heads, k->n_kv_heads, ctx_len, false);
   if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
-
-  DecodeArgs a{};
-  a.k = view_of(k);
-  a.v = view_of(v);
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.batch = k->batch;
-  a.n_q_heads = n_q_heads;
-  a.n_kv_heads = k->n_kv_heads;
-  a.group = group;
-  a.seq_lens = seq_lens;
-  a.ctx_len = ctx_len;
-  a.scale = scale;
-  a.n_q = 1;
-  a.vgroups = 1;
-  a.vg_size = group;
-  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
-  a.fplan = plan_fused(k->batch, k->n_kv_heads, ctx_len);
-  a.out = out;
-  a.lse = lse;
   char *ws = static_cast<char *>(workspace);
   a.part_ml = reinterpret_cast<float2 *>(ws + w.part_ml);
   a.part_o = reinterpret_cast<float *>(ws + w.part_o);

@@ -971,11 +971,12 @@ hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_fused_supported(const DecodeArgs &a) {
+bool decode_fused_shape_ok(const DecodeArgs &a) {
   return !a.sparse && (a.k.bits == 3 || a.k.bits == 4) && a.v.bits == 2 && a.vg_size <= 8 && a.vg_size >= 1 &&
-         a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 &&
-         a.fplan.split_len % kTile == 0 && a.counters != nullptr;
+         a.k.layout == TQ_LAYOUT_ROWS && a.v.layout == TQ_LAYOUT_GROUP8 && a.fplan.split_len % kTile == 0;
 }
+
+bool decode_fused_supported(const DecodeArgs &a) { return decode_fused_shape_ok(a) && a.counters != nullptr; }
 
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream) {
   (void)n_cu;

@@ -130,12 +130,20 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 int compute_units();
 bool decode_mfma_supported(const DecodeArgs &a);
 bool decode_fused_supported(const DecodeArgs &a);
+// The single-launch kernel covers these widths and shapes (the workspace aside).
+bool decode_fused_shape_ok(const DecodeArgs &a);
 bool decode_fused_sparse_supported(const DecodeArgs &a);
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream);
 // Sparse V's masked value pass: the dense single-launch kernel over the dense plan (a.fplan,
 // partials a.fpart_ml / a.fpart_o) with the key pass's partials in a.lse_ml.
 hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream);
+// Validation and argument set-up shared by tq_decode_attn_append and its allocation-free
+// variant: fills `a` (everything but the workspace pointers) and the workspace layout `w`;
+// returns a tq_status.
+int setup_decode_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                        const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len,
+                        float scale, float *out, float *lse, DecodeArgs &a, WorkspaceLayout &w);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int n_cu, hipStream_t stream);
 
 }  // namespace tq

@@ -190,6 +190,25 @@ int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, 
                           const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* tq_decode_attn_append for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same one-launch decode
+ * step with the same arguments and results, except that there is no workspace argument.  Its
+ * scratch (arrival counters and per-split partials) is a static device array of the library,
+ * 8 MiB per GPU, kept until the process ends; the first call on a GPU clears its counter
+ * region with a kernel on hip_stream and every completed call leaves it at zero.  The call
+ * allocates nothing.
+ *   Limits: keys of 3 or 4 bits, values of 2 bits, n_q_heads / n_kv_heads <= 8 (the one-launch
+ *   path; TQ_ERR_UNSUPPORTED otherwise); batch * n_kv_heads <= 16384 and
+ *   batch * n_q_heads * splits * 520 bytes of partials within the rest of the 8 MiB
+ *   (TQ_ERR_WORKSPACE otherwise; splits is about 256 / (batch * n_kv_heads), at least 1).
+ *   Every call on one GPU uses the same scratch: calls that overlap in time on one GPU race,
+ *   so order them (one stream, or events).
+ * Errors: as tq_decode_attn_append, and TQ_ERR_HIP if the scratch cannot be located. */
+int tq_decode_attn_append_noalloc(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,
+                                  int x_dtype, const void *q, int q_dtype, int n_q_heads,
+                                  const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse,
+                                  void *hip_stream);
+
 /* Attention of n_q new query positions per sequence against the packed cache, which already
  * holds them (speculative verification of draft tokens, chunked prefill): the same scores,
  * softmax and rotated-domain value sum as tq_decode_attn ([google] score kernel; [inferrs]

@@ -208,6 +208,30 @@ def test_append_decode_argument_validation():
     assert ad(_cache(layout=0, bits=8), _cache(layout=1, bits=8), seq=FAKE + 0x900000) == tq.TQ_ERR_UNSUPPORTED
 
 
+def test_noalloc_decode_step_argument_validation():
+    """The allocation-free decode step validates like tq_decode_attn_append, refuses the widths
+    of the two-launch path, and refuses problems beyond its static scratch, all before any HIP
+    call."""
+    def na(k, v, xk=FAKE + 0x500000, hq=8, ctx=512, out=FAKE + 0x700000):
+        return tq.lib().tq_decode_attn_append_noalloc(ctypes.byref(k), ctypes.byref(v), xk, FAKE + 0x580000, 1,
+                                                      FAKE + 0x600000, 1, hq, None, ctx, 0.088, out, None, None)
+
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+    assert na(k, v, xk=0) == tq.TQ_ERR_INVALID_ARG
+    assert na(k, v, out=FAKE + 0x700004) == tq.TQ_ERR_INVALID_ARG
+    assert na(k, v, hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert na(k, v, ctx=2048) == tq.TQ_ERR_CAPACITY
+    assert na(v, k) == tq.TQ_ERR_UNSUPPORTED
+    assert na(_cache(layout=0, bits=8), _cache(layout=1, bits=8)) == tq.TQ_ERR_UNSUPPORTED
+    assert na(k, v, hq=32) == tq.TQ_ERR_UNSUPPORTED                        # group 16: two-launch path only
+    # more (batch, kv head) counters than the static scratch holds
+    big_k, big_v = _cache(layout=0, batch=4096, n_kv_heads=8), _cache(layout=1, bits=2, batch=4096, n_kv_heads=8)
+    assert na(big_k, big_v, hq=64) == tq.TQ_ERR_WORKSPACE
+    # partials beyond the rest of the 8 MiB: 2048 sequences x 64 query heads x 1 split x 520 bytes
+    mid_k, mid_v = _cache(layout=0, batch=2048, n_kv_heads=8), _cache(layout=1, bits=2, batch=2048, n_kv_heads=8)
+    assert na(mid_k, mid_v, hq=64) == tq.TQ_ERR_WORKSPACE
+
+
 def _paged(**kw):
     base = dict(d=128, bits=4, layout=0, batch=2, n_kv_heads=2, page_tokens=256, n_pages=64, max_pages=16,
                 codes=FAKE, norms=FAKE + 0x1000000, block_table=FAKE + 0x1100000, centroids=FAKE + 0x200000,
