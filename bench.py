@@ -61,7 +61,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="batch32k",
-                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k", "search1m"])
+                   choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k", "search1m",
+                            "qjl8k"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,6 +216,8 @@ def main():
         result = bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log)
     elif w.page_tokens > 0:
         result = bench_paged(args, w, signs, dev, tq, inputs, torch, np, log)
+    elif w.extra.get("qjl_m"):
+        result = bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log)
     else:
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
     stream = stream_read_gbs(torch, tq, log)
@@ -589,6 +592,122 @@ def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
         gathered = (_GatheredPlanes(kc, row, torch), _GatheredPlanes(vc, row, torch))
         result["cpu_baseline"] = cpu_baseline_decode(w, 0.0, gathered, host_k, host_v, q, signs, np, torch, log)
     return result
+
+
+def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
+    """QJL keys: a step appends one token per (batch, kv head), the key with its sign sketch and
+    the value as usual, then decode attention with QJL-corrected scores (the generic kernel)."""
+    batch, hq, hkv, ctx = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx
+    bk, bv, m = w.bits_k, w.bits_v, w.extra["qjl_m"]
+    k_row = D * bk // 8 + 2 + m // 8 + 2       # codes + norm + sign bits + residual norm
+    v_row = D * bv // 8 + 2
+    per_copy = batch * hkv * ctx * (k_row + v_row)
+    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    log(f"[bench] workload={w.name} QJL keys ({bk}-bit codes + {m} sign bits) copies={copies} "
+        f"cache/copy={per_copy / 1e6:.1f} MB ({'eager launches' if args.eager else 'HIP graph replay'})")
+    g = inputs.generate(w, device=dev)
+    k_all, v_all, q = g["k"], g["v"], g["q"].contiguous()
+    proj = inputs.qjl_projection(m)
+    caches = []
+    for c in range(copies):
+        kc = tq.PackedCache(batch, hkv, ctx, bk, tq.LAYOUT_ROWS, signs, device=dev)
+        vc = tq.PackedCache(batch, hkv, ctx, bv, tq.LAYOUT_GROUP8, signs, device=dev)
+        sk = tq.QjlSketch(kc, proj, device=dev)
+        tq.qjl_quantize_append(kc, sk, k_all[:, : ctx - 1].contiguous(), 0)
+        tq.quantize_append(vc, v_all[:, : ctx - 1].contiguous(), 0)
+        caches.append((kc, sk, vc))
+    k_new = k_all[:, ctx - 1:ctx].contiguous()
+    v_new = v_all[:, ctx - 1:ctx].contiguous()
+    host_k = k_all[:1, ctx - 1].cpu() if not args.no_cpu_baseline else None
+    del k_all, v_all, g
+    bufs = tq.DecodeBuffers(batch, hq, hkv, ctx, 0.0, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+
+    def append(i):
+        kc, sk, vc = caches[i % copies]
+        tq.qjl_quantize_append(kc, sk, k_new, ctx - 1)
+        tq.quantize_append(vc, v_new, ctx - 1)
+
+    def attend(i):
+        kc, sk, vc = caches[i % copies]
+        tq.qjl_decode_attn(kc, sk, vc, q, ctx, scale, buffers=bufs)
+
+    def step(i):
+        append(i)
+        attend(i)
+
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
+    ms_per_step = timer.per_iteration_ms(step, args.steps, args.warmup)
+    n_rep = max(args.steps, 2 * copies)
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(attend, n_rep, 2, batches=5)
+    ms_a = timer.per_iteration_ms(append, n_rep, 2)
+    nbytes = batch * hkv * ctx * (k_row + v_row)
+    achieved = nbytes / (ms_k / 1e3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, QJL decode call {ms_k * 1e3:.1f} us = {achieved:.0f} GB/s, "
+        f"append (QJL key + value) {ms_a * 1e3:.1f} us")
+    result = {
+        "metric": METRIC, "value": batch * ctx / (ms_per_step / 1e3), "unit": "KV-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; shapes and value distributions of the workload; seeded Gaussian sketch)",
+        "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D, "ctx": ctx,
+                   "bits_k": bk, "qjl_sketch_rows": m, "bits_v": bv,
+                   "step": "QJL key + value append (1 token) + decode attention with QJL-corrected scores",
+                   "cache_copies": copies, "timing": "eager" if args.eager else "hip graph replay"},
+        "decode_call_us": ms_k * 1e3, "append_us": ms_a * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "QJL decode call (decode_split_generic + decode_merge, fp32 vector ALU)",
+                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                     "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
+                     "bytes_note": f"per (token, kv head): key {k_row} B (codes, norm, sign bits, residual norm), "
+                                   f"value {v_row} B"},
+        "_kernel": "decode_qjl",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_qjl(w, caches[0], host_k, q, signs, proj, np, log)
+    return result
+
+
+def cpu_baseline_qjl(w, cache, host_k, q, signs, proj, np, log):
+    """The CPU oracle on a bounded sample: batch element 0, every kv head, the whole context:
+    QJL-quantize the appended key, then unpack the codes and sign bits, form the effective keys
+    and attend."""
+    from oracle import tq_oracle as o
+
+    kc, sk, vc = cache
+    ctx, hkv, g, m = w.ctx, w.n_kv_heads, w.group, w.extra["qjl_m"]
+    s64 = signs.cpu().numpy().astype(np.float64)
+    p64 = proj.numpy().astype(np.float64)
+    tabk = o.make_codebook(D, w.bits_k)[:2]
+    tabv = o.make_codebook(D, w.bits_v)[:2]
+    raw_k = [kc.plane_codes(0, h).cpu().numpy() for h in range(hkv)]
+    raw_s = [sk.plane_bits(0, h).cpu().numpy() for h in range(hkv)]
+    raw_v = [vc.plane_codes(0, h).cpu().numpy() for h in range(hkv)]
+    nk = [kc.plane_norms(0, h).cpu().numpy() for h in range(hkv)]
+    rk = [sk.plane_res_norms(0, h).cpu().numpy() for h in range(hkv)]
+    nv = [vc.plane_norms(0, h).cpu().numpy() for h in range(hkv)]
+    q64 = q[:1].double().cpu().numpy()
+    xk = host_k[0].double().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.qjl_quantize(xk, s64, *tabk, p64)
+        kh = np.stack([o.qjl_dequantize(o.unpack(raw_k[h], ctx, D, w.bits_k, 0), nk[h],
+                                        o.unpack(raw_s[h], ctx, m, 1, 0).astype(bool), rk[h], s64, tabk[0], p64)
+                       for h in range(hkv)])[None]
+        vh = np.stack([o.dequantize(o.unpack(raw_v[h], ctx, D, w.bits_v, 1), nv[h], s64, tabv[0])
+                       for h in range(hkv)])[None]
+        o.decode_attention(q64, kh, vh, 1.0 / math.sqrt(D))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    log(f"[bench] cpu oracle: {reps} sample steps in {el:.1f} s")
+    return with_cpu_context({"value": reps * ctx / el, "unit": "KV-tokens/s", "cores": cpu_cores(), "kind": "oracle",
+                             "sample": f"batch element 0 of {w.batch}, all {hkv} kv heads / {hkv * g} query heads, "
+                                       f"{ctx} tokens: QJL-quantize the appended key, unpack codes and sign bits, "
+                                       f"effective keys, attend; {reps} repetitions"})
 
 
 def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):

@@ -37,6 +37,11 @@ class CacheStruct(ctypes.Structure):
     ]
 
 
+class QjlSketchStruct(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("bits", ctypes.c_void_p), ("res_norms", ctypes.c_void_p),
+                ("proj", ctypes.c_void_p)]
+
+
 class PagedCacheStruct(ctypes.Structure):
     _fields_ = [
         ("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("layout", ctypes.c_int32),
@@ -82,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.tq_paged_decode_attn_append.argtypes = [PP, PP, vp, vp, i32, vp, i32, i32, vp, i32, f32, vp, vp, vp, sz,
                                                   vp]
         L.tq_ip_search.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        QP = ctypes.POINTER(QjlSketchStruct)
+        L.tq_qjl_quantize_append.argtypes = [ctypes.POINTER(CacheStruct), QP, vp, i32, i32, i32, vp]
+        L.tq_qjl_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), QP, ctypes.POINTER(CacheStruct), vp, i32, i32,
+                                         vp, i32, f32, f32, vp, vp, vp, vp, sz, vp]
         L.tq_ip_search_workspace_bytes.argtypes = [i32, i32, i32]
         L.tq_ip_search_workspace_bytes.restype = sz
         L.tq_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -93,7 +102,8 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
                      "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
-                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search"):
+                     "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search",
+                     "tq_qjl_quantize_append", "tq_qjl_decode_attn"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -414,6 +424,65 @@ def decode_attn_append_noalloc(k_cache: PackedCache, v_cache: PackedCache, k_new
         _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len, float(scale), _dev(out, "out"), _dev(lse, "lse"),
         _stream_ptr(stream)), "tq_decode_attn_append_noalloc")
     return out, lse
+
+
+class QjlSketch:
+    """The QJL sign sketch beside a key cache (device): bits [batch, n_kv_heads, capacity, m/8]
+    uint8, residual norms [batch, n_kv_heads, capacity] fp16, and the sketch matrix S [m, d]
+    fp32 (drawn by the caller)."""
+
+    def __init__(self, key_cache: PackedCache, proj, device="cuda"):
+        torch = _torch()
+        self.m = int(proj.shape[0])
+        c = key_cache
+        self.bits = torch.zeros(c.batch * c.n_kv_heads * c.capacity * self.m // 8, dtype=torch.uint8, device=device)
+        self.res_norms = torch.zeros(c.batch * c.n_kv_heads * c.capacity, dtype=torch.float16, device=device)
+        self.proj = proj.to(device=device, dtype=torch.float32).contiguous()
+        self.capacity, self.n_kv_heads = c.capacity, c.n_kv_heads
+
+    def struct(self) -> QjlSketchStruct:
+        return QjlSketchStruct(self.m, self.bits.data_ptr(), self.res_norms.data_ptr(), self.proj.data_ptr())
+
+    def plane_bits(self, b: int, h: int):
+        per = self.capacity * self.m // 8
+        i = b * self.n_kv_heads + h
+        return self.bits[i * per:(i + 1) * per]
+
+    def plane_res_norms(self, b: int, h: int):
+        i = b * self.n_kv_heads + h
+        return self.res_norms[i * self.capacity:(i + 1) * self.capacity]
+
+
+def qjl_quantize_append(k_cache: PackedCache, sketch: QjlSketch, x, start_pos: int, stream=None):
+    """QJL keys: quantize x [batch, n_tokens, n_kv_heads, d] into the key cache (codes, norms)
+    and the sketch (sign bits, residual norms) at positions start_pos .. start_pos+n_tokens."""
+    if x.dim() != 4 or x.shape[0] != k_cache.batch or x.shape[2] != k_cache.n_kv_heads or x.shape[3] != k_cache.d:
+        raise ValueError(f"x has shape {tuple(x.shape)}")
+    st, ss = k_cache.struct(), sketch.struct()
+    _check(lib().tq_qjl_quantize_append(ctypes.byref(st), ctypes.byref(ss), _dev(x, "x"), _dtype_code(x.dtype),
+                                        start_pos, x.shape[1], _stream_ptr(stream)), "tq_qjl_quantize_append")
+
+
+def qjl_decode_attn(k_cache: PackedCache, sketch: QjlSketch, v_cache: PackedCache, q, ctx_len: int, scale: float,
+                    tau: float = 0.0, seq_lens=None, buffers: DecodeBuffers | None = None, want_scores: bool = False,
+                    stream=None):
+    """Decode attention with QJL-corrected scores; returns the DecodeBuffers (out, lse, scores)."""
+    _check_query(q, k_cache, 3, "qjl_decode_attn")
+    bsz, hq, d = q.shape
+    _check_seq_lens(seq_lens, bsz, "qjl_decode_attn")
+    if buffers is None:
+        buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, tau, device=q.device, d=d,
+                                want_scores=want_scores)
+    _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "qjl_decode_attn", scores_shape=(bsz, hq, ctx_len))
+    ks, ss, vs = k_cache.struct(), sketch.struct(), v_cache.struct()
+    sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
+    _check(lib().tq_qjl_decode_attn(
+        ctypes.byref(ks), ctypes.byref(ss), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len,
+        float(scale), float(tau), _dev(buffers.out, "out"),
+        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        _dev(buffers.scores, "scores") if buffers.scores is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_qjl_decode_attn")
+    return buffers
 
 
 class PagedCache:

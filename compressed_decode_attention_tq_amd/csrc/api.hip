@@ -254,6 +254,79 @@ int check_paged_pair(const tq_paged_cache *k, const tq_paged_cache *v) {
   return TQ_OK;
 }
 
+int check_sketch(const tq_qjl_sketch *s) {
+  if (s == nullptr || s->bits == nullptr || s->res_norms == nullptr || s->proj == nullptr) return TQ_ERR_INVALID_ARG;
+  if (!aligned(s->bits, 16) || !aligned(s->res_norms, 2) || !aligned(s->proj, 4)) return TQ_ERR_INVALID_ARG;
+  if (s->m != kD) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+int setup_decode(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype, int n_q_heads,
+                 const int32_t *seq_lens, int ctx_len, float scale, float sparse_v_tau, float *out, float *lse,
+                 float *scores, void *workspace, size_t workspace_bytes, DecodeArgs &a) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
+      k->signs != v->signs)
+    return TQ_ERR_INVALID_ARG;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (scores != nullptr && !aligned(scores, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / k->n_kv_heads;
+  if (group > 16) return TQ_ERR_UNSUPPORTED;
+  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
+  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if (!(sparse_v_tau >= 0.f && sparse_v_tau < 1.f)) return TQ_ERR_INVALID_ARG;
+  const bool sparse = sparse_v_tau > 0.f;
+  const WorkspaceLayout w = workspace_layout(k->batch, n_q_heads, k->n_kv_heads, ctx_len, sparse);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+
+  a = DecodeArgs{};
+  a.k = view_of(k);
+  a.v = view_of(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = ctx_len;
+  a.scale = scale;
+  a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
+  a.sparse = sparse ? 1 : 0;
+  a.n_q = 1;
+  a.vgroups = 1;
+  a.vg_size = group;
+  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
+  a.fplan = sparse ? plan_fused_sparse(k->batch, k->n_kv_heads, ctx_len, a.plan)
+                   : plan_fused(k->batch, k->n_kv_heads, ctx_len);
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  char *ws = static_cast<char *>(workspace);
+  a.part_ml = reinterpret_cast<float2 *>(ws + w.part_ml);
+  a.part_o = reinterpret_cast<float *>(ws + w.part_o);
+  a.cand_count = reinterpret_cast<int *>(ws + w.cand_count);
+  a.cand = reinterpret_cast<float *>(ws + w.cand);
+  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
+  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
+  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
+  if (a.sparse) {
+    a.vpart_ml = reinterpret_cast<float2 *>(ws + w.vpart_ml);
+    a.vpart_o = reinterpret_cast<float *>(ws + w.vpart_o);
+  }
+  return TQ_OK;
+}
+
 int setup_decode_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
                         const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len,
                         float scale, float *out, float *lse, DecodeArgs &a, WorkspaceLayout &w) {
@@ -388,67 +461,51 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
                    int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
                    float sparse_v_tau, float *out, float *lse, float *scores, void *workspace,
                    size_t workspace_bytes, void *hip_stream) {
+  DecodeArgs a{};
+  const int st = setup_decode(k, v, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, sparse_v_tau, out, lse, scores,
+                              workspace, workspace_bytes, a);
+  if (st != TQ_OK) return st;
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void *x, int x_dtype, int start_pos,
+                           int n_tokens, void *hip_stream) {
   int st = check_cache(k);
   if (st != TQ_OK) return st;
-  st = check_cache(v);
+  st = check_sketch(s);
   if (st != TQ_OK) return st;
-  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity ||
-      k->signs != v->signs)
-    return TQ_ERR_INVALID_ARG;
-  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_UNSUPPORTED;
-  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
-  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
-  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
-  if (scores != nullptr && !aligned(scores, 4)) return TQ_ERR_INVALID_ARG;
-  if (seq_lens != nullptr && !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
-  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
-  const int group = n_q_heads / k->n_kv_heads;
-  if (group > 16) return TQ_ERR_UNSUPPORTED;
-  if (ctx_len < 0) return TQ_ERR_INVALID_ARG;
-  if (ctx_len > k->capacity) return TQ_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
-  if (!(sparse_v_tau >= 0.f && sparse_v_tau < 1.f)) return TQ_ERR_INVALID_ARG;
-  const bool sparse = sparse_v_tau > 0.f;
-  const WorkspaceLayout w = workspace_layout(k->batch, n_q_heads, k->n_kv_heads, ctx_len, sparse);
-  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
-  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
-
-  DecodeArgs a{};
+  if (k->layout != TQ_LAYOUT_ROWS) return TQ_ERR_INVALID_ARG;
+  if (x == nullptr || !aligned(x, 16) || !valid_dtype(x_dtype)) return TQ_ERR_INVALID_ARG;
+  if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if ((long)start_pos + n_tokens > k->capacity) return TQ_ERR_CAPACITY;
+  if (n_tokens == 0) return TQ_OK;
+  QjlQuantArgs a{};
   a.k = view_of(k);
-  a.v = view_of(v);
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.batch = k->batch;
-  a.n_q_heads = n_q_heads;
-  a.n_kv_heads = k->n_kv_heads;
-  a.group = group;
-  a.seq_lens = seq_lens;
-  a.ctx_len = ctx_len;
-  a.scale = scale;
-  a.ln_tau = sparse ? std::log(sparse_v_tau) : 0.f;
-  a.sparse = sparse ? 1 : 0;
-  a.n_q = 1;
-  a.vgroups = 1;
-  a.vg_size = group;
-  a.plan = plan_splits(k->batch, k->n_kv_heads, ctx_len, group);
-  a.fplan = sparse ? plan_fused_sparse(k->batch, k->n_kv_heads, ctx_len, a.plan)
-                   : plan_fused(k->batch, k->n_kv_heads, ctx_len);
-  a.out = out;
-  a.lse = lse;
-  a.scores = scores;
-  char *ws = static_cast<char *>(workspace);
-  a.part_ml = reinterpret_cast<float2 *>(ws + w.part_ml);
-  a.part_o = reinterpret_cast<float *>(ws + w.part_o);
-  a.cand_count = reinterpret_cast<int *>(ws + w.cand_count);
-  a.cand = reinterpret_cast<float *>(ws + w.cand);
-  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
-  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
-  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
-  if (a.sparse) {
-    a.vpart_ml = reinterpret_cast<float2 *>(ws + w.vpart_ml);
-    a.vpart_o = reinterpret_cast<float *>(ws + w.vpart_o);
-  }
-  return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)));
+  a.bits = s->bits;
+  a.res_norms = s->res_norms;
+  a.proj = s->proj;
+  a.x = x;
+  a.x_dtype = x_dtype;
+  a.start_pos = start_pos;
+  a.n_tokens = n_tokens;
+  return hip_status(launch_qjl_quantize(a, k->batch, static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cache *v, const void *q, int q_dtype,
+                       int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale, float sparse_v_tau,
+                       float *out, float *lse, float *scores, void *workspace, size_t workspace_bytes,
+                       void *hip_stream) {
+  int st = check_sketch(ks);
+  if (st != TQ_OK) return st;
+  DecodeArgs a{};
+  st = setup_decode(k, v, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, sparse_v_tau, out, lse, scores, workspace,
+                    workspace_bytes, a);
+  if (st != TQ_OK) return st;
+  a.qjl_bits = ks->bits;
+  a.qjl_rnorm = ks->res_norms;
+  a.qjl_proj = ks->proj;
+  a.qjl_m = ks->m;
+  return hip_status(launch_decode_generic(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,

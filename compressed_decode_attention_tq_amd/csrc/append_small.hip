@@ -13,65 +13,10 @@
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
+#include "wave_quant.h"
 
 namespace tq {
 namespace {
-
-// input element pair (2 lane, 2 lane + 1) of one token row
-template <int DTYPE>
-__device__ __forceinline__ void load_pair(const void *x, size_t i, float &x0, float &x1) {
-  if constexpr (DTYPE == TQ_F32) {
-    const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(x) + i);
-    x0 = f.x;
-    x1 = f.y;
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + i);
-    if constexpr (DTYPE == TQ_BF16) {
-      x0 = __uint_as_float(w << 16);
-      x1 = __uint_as_float(w & 0xffff0000u);
-    } else {
-      x0 = __half2float(__ushort_as_half((uint16_t)(w & 0xffffu)));
-      x1 = __half2float(__ushort_as_half((uint16_t)(w >> 16)));
-    }
-  }
-}
-
-// codes of coordinates 2 lane, 2 lane + 1 and the norm of one token
-template <int BITS>
-__device__ __forceinline__ void token_codes(const CacheView &c, float x0, float x1, int lane, uint32_t &c0,
-                                            uint32_t &c1, float &n) {
-  n = sqrtf(wave_reduce<false>(x0 * x0 + x1 * x1));
-  const float y0 = c.signs[2 * lane] < 0 ? -x0 : x0, y1 = c.signs[2 * lane + 1] < 0 ? -x1 : x1;
-  float u0 = y0 + y1, u1 = y0 - y1;  // stage 0 of the transform, inside the lane
-  wave_fwht_upper(u0, u1, lane);
-  const float inv = n > 0.f ? 1.0f / (n * 11.313708498984761f) : 0.f;
-  u0 *= inv;
-  u1 *= inv;
-  c0 = 0u;
-  c1 = 0u;
-  for (int j = 0; j < (1 << BITS) - 1; ++j) {
-    const float t = c.boundaries[j];
-    c0 += u0 > t ? 1u : 0u;
-    c1 += u1 > t ? 1u : 0u;
-  }
-}
-
-// Key rows: lane l's two codes are bits [2 BITS l, 2 BITS (l + 1)) of the token's row of
-// 16 BITS bytes; the row is assembled in LDS (4 BITS words) and stored by the first lanes.
-template <int BITS>
-__device__ __forceinline__ void store_row(uint8_t *row, uint32_t c0, uint32_t c1, int lane, uint32_t *words) {
-  constexpr int kWords = 4 * BITS;
-  if (lane < kWords) words[lane] = 0u;
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("" ::: "memory");
-  const uint32_t f = c0 | (c1 << BITS);
-  const int bit = 2 * BITS * lane, wi = bit >> 5, sh = bit & 31;
-  atomicOr(&words[wi], f << sh);
-  if (sh + 2 * BITS > 32) atomicOr(&words[wi + 1], f >> (32 - sh));
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("" ::: "memory");
-  if (lane < kWords) reinterpret_cast<uint32_t *>(row)[lane] = words[lane];
-}
 
 // Value groups: coordinate i of token p of a group sits at bit (8 i + p) BITS, so lane l's
 // coordinates 2l and 2l + 1 of all 8 tokens are the 2 BITS bytes at 2 BITS l of the group,
@@ -134,7 +79,8 @@ __device__ void append_plane(const CacheView &c, const void *x, int b, int h, in
     load_pair<DTYPE>(x, (((size_t)b * n_tokens + wave) * c.n_kv_heads + h) * kD + 2 * lane, x0, x1);
     uint32_t c0, c1;
     float n;
-    token_codes<BITS>(c, x0, x1, lane, c0, c1, n);
+    float h0, h1;
+    token_codes<BITS>(c, x0, x1, lane, c0, c1, n, h0, h1);
     if (lane == 0) c.norm_plane(b, h)[t] = float_to_half_bits(n);
     if constexpr (KEY) store_row<BITS>(plane + (size_t)t * (16 * BITS), c0, c1, lane, sh.words[wave]);
     else sh.codes[wave][lane] = make_uint2(c0, c1);
@@ -201,7 +147,8 @@ __device__ void append_window(const CacheView &c, const void *x, const int32_t *
     load_pair<DTYPE>(x, (((size_t)b * n_tokens + j) * c.n_kv_heads + h) * kD + 2 * lane, x0, x1);
     uint32_t c0, c1;
     float n;
-    token_codes<BITS>(c, x0, x1, lane, c0, c1, n);
+    float h0, h1;
+    token_codes<BITS>(c, x0, x1, lane, c0, c1, n, h0, h1);
     if (lane == 0) c.norm_plane(page, h)[pos] = float_to_half_bits(n);
     if constexpr (KEY) store_row<BITS>(plane + (size_t)pos * (16 * BITS), c0, c1, lane, sh.words[wave]);
     else sh.codes[wave][lane] = make_uint2(c0, c1);

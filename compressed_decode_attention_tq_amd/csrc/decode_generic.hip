@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
   const bool sparse = a.sparse != 0;
 
   __shared__ float qt[16][kD];
+  __shared__ float pq[16][kD];  // QJL keys: S qt[j], the sketch of each scaled rotated query
   __shared__ float lutK[256], lutV[256];
   __shared__ float pbuf[16][256];
   __shared__ float nvs[256];
@@ -69,6 +70,19 @@ __global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
   for (int i = tid; i < (1 << bk); i += blockDim.x) lutK[i] = a.k.centroids[i];
   for (int i = tid; i < (1 << bv); i += blockDim.x) lutV[i] = a.v.centroids[i];
   load_rotated_queries(a, b, kvh, qt);
+  const bool qjl = a.qjl_m > 0;
+  if (qjl) {  // ([google] §第二步：QJL) pq[j][r] = sum_i S[r][i] qt[j][i]
+    for (int e = tid; e < g * kD; e += blockDim.x) {
+      const int j = e / kD, r = e % kD;
+      const float *row = a.qjl_proj + (size_t)r * kD;
+      float acc = 0.f;
+      for (int i = 0; i < kD; ++i) acc = fmaf(row[i], qt[j][i], acc);
+      pq[j][r] = acc;
+    }
+    __syncthreads();
+  }
+  // sqrt(pi / 2) / m: the sign sketch's estimate of the residual's inner product is unbiased
+  const float qjl_kappa = qjl ? 1.2533141373155003f / (float)a.qjl_m : 0.f;
 
   float m_run[4], l_run[4];
 #pragma unroll
@@ -110,6 +124,26 @@ __global__ __launch_bounds__(256) void decode_split_generic(DecodeArgs a) {
       const float nk = half_bits_to_float(knorm[t]);
 #pragma unroll
       for (int j = 0; j < 16; ++j) d[j] *= nk;
+      if (qjl) {
+        // QJL correction: kappa ||r|| sum_r (S qt[j])_r (2 bit_r - 1), the unbiased estimate of
+        // the residual's share of the score ([google] _prod_score_kernel: the score against
+        // the codes plus the sign-sketch term)
+        const size_t unit = (size_t)b * a.n_kv_heads + kvh;
+        const uint4 sb = *reinterpret_cast<const uint4 *>(a.qjl_bits + (unit * a.k.capacity + t) * (kD / 8));
+        const uint32_t wv[4] = {sb.x, sb.y, sb.z, sb.w};
+        float e[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) e[j] = 0.f;
+        for (int r = 0; r < kD; ++r) {
+          const bool on = (wv[r >> 5] >> (r & 31)) & 1u;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (j < g) e[j] += on ? pq[j][r] : -pq[j][r];
+        }
+        const float rk = qjl_kappa * half_bits_to_float(a.qjl_rnorm[unit * a.k.capacity + t]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) d[j] = fmaf(rk, e[j], d[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -493,6 +527,19 @@ int compute_units() {
   return cached[dev];
 }
 
+// After a split pass: the Sparse-V second pass (if a.sparse), then the LSE merge of the splits.
+static hipError_t finish_split_decode(const DecodeArgs &a, dim3 grid_split, hipStream_t stream) {
+  if (a.sparse) {
+    if (a.group <= 4) launch_sparse_v<4>(a, grid_split, stream);
+    else if (a.group <= 8) launch_sparse_v<8>(a, grid_split, stream);
+    else launch_sparse_v<16>(a, grid_split, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  decode_merge<<<dim3(a.n_q_heads, a.batch), 128 * kMergeGroups, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
   if (decode_fused_supported(args)) return launch_decode_fused(args, compute_units(), stream);
   DecodeArgs a = args;
@@ -526,20 +573,22 @@ hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
     if (decode_mfma_supported(a)) {
       e = launch_decode_mfma(a, compute_units(), stream);
     } else {
-      decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
-      e = hipGetLastError();
+      return launch_decode_generic(a, stream);
     }
   }
   if (e != hipSuccess) return e;
-  if (a.sparse) {
-    if (a.group <= 4) launch_sparse_v<4>(a, grid_split, stream);
-    else if (a.group <= 8) launch_sparse_v<8>(a, grid_split, stream);
-    else launch_sparse_v<16>(a, grid_split, stream);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  decode_merge<<<dim3(a.n_q_heads, a.batch), 128 * kMergeGroups, 0, stream>>>(a);
-  return hipGetLastError();
+  return finish_split_decode(a, grid_split, stream);
+}
+
+hipError_t launch_decode_generic(const DecodeArgs &args, hipStream_t stream) {
+  DecodeArgs a = args;
+  a.lse_ml = a.part_ml;
+  a.lse_splits = a.plan.n_splits;
+  const dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
+  decode_split_generic<<<grid_split, 256, 0, stream>>>(a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return finish_split_decode(a, grid_split, stream);
 }
 
 }  // namespace tq

@@ -1,0 +1,103 @@
+// QJL residual variant of the key quantizer ([google] "Google 最新極限壓縮算法…", §第二步：QJL
+// —— 1 bit 清理殘差, and its mlx-vlm kernel list: _qjl_score_kernel, _prod_score_kernel;
+// [tq-80] "TurboQuant：让大模型本地推理内存占用降低80%的KV缓存压缩技术" §技术背景与学术渊源).
+//
+// After the rotate-and-code stage, one bit per row of a Gaussian matrix S records the sign of
+// the projection of the stage's error, so that inner products with the key (attention scores)
+// are unbiased.  Per token, one wave of 64 lanes, two coordinates per lane:
+//   n = ||x||, h = H (s . x) (lanes.h butterflies), code_i = #{j : t_j < h_i / (sqrt(d) n)}
+//   (the same steps as the small-append kernels, wave_quant.h);
+//   r_i = h_i / sqrt(d) - n16 c[code_i]       the error of the reconstruction the decoder
+//                                             makes (n16 = the stored fp16 norm), rotated domain
+//   ||r|| -> fp16;  z = S r;  bit j = (z_j >= 0), LSB first in a 16-byte row per token.
+// S^T sits in LDS with a row pitch of 129 floats (66 KB), so both the transposing copy and
+// the reads are free of bank conflicts: lane l reads row i at column l (and l + 64) while the
+// residual coordinate r_i is a broadcast; lane l forms z_l and z_{l+64} and two ballots give
+// the 128 bits.
+#include "tq_common.h"
+#include "tq_launch.h"
+#include "lanes.h"
+#include "wave_quant.h"
+
+namespace tq {
+namespace {
+
+constexpr int kQjlTokens = 64;  // tokens per block (16 per wave)
+constexpr int kPitch = kD + 1;   // LDS row pitch of S^T
+constexpr float kInvSqrtD = 0.08838834764831845f;
+
+template <int DTYPE, int BITS>
+__global__ __launch_bounds__(256) void qjl_quantize_kernel(QjlQuantArgs a) {
+  __shared__ float st[kD * kPitch];  // S^T: st[i * kPitch + j] = S[j][i]
+  __shared__ __align__(16) float res[4][kD];
+  __shared__ uint32_t words[4][4 * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  for (int e = threadIdx.x; e < kD * kD; e += blockDim.x) st[(e & (kD - 1)) * kPitch + (e >> 7)] = a.proj[e];
+  __syncthreads();
+  const CacheView &c = a.k;
+  uint8_t *plane = c.plane(b, h);
+  uint16_t *norms = c.norm_plane(b, h);
+  const size_t unit = (size_t)b * c.n_kv_heads + h;
+  uint8_t *bits = a.bits + unit * (size_t)c.capacity * (kD / 8);
+  uint16_t *rnorms = a.res_norms + unit * (size_t)c.capacity;
+  const int j_end = min(a.n_tokens, (int)(blockIdx.x + 1) * kQjlTokens);
+  for (int j = blockIdx.x * kQjlTokens + wave; j < j_end; j += 4) {
+    const int t = a.start_pos + j;
+    float x0, x1, n, h0, h1;
+    load_pair<DTYPE>(a.x, (((size_t)b * a.n_tokens + j) * c.n_kv_heads + h) * kD + 2 * lane, x0, x1);
+    uint32_t c0, c1;
+    token_codes<BITS>(c, x0, x1, lane, c0, c1, n, h0, h1);
+    const uint16_t n16 = float_to_half_bits(n);
+    const float nf = half_bits_to_float(n16);
+    const float r0 = h0 * kInvSqrtD - nf * c.centroids[c0];
+    const float r1 = h1 * kInvSqrtD - nf * c.centroids[c1];
+    const float rn = sqrtf(wave_reduce<false>(r0 * r0 + r1 * r1));
+    *reinterpret_cast<float2 *>(&res[wave][2 * lane]) = make_float2(r0, r1);
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    float z_lo = 0.f, z_hi = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < kD; ++i) {
+      const float ri = res[wave][i];
+      z_lo = fmaf(st[i * kPitch + lane], ri, z_lo);
+      z_hi = fmaf(st[i * kPitch + lane + 64], ri, z_hi);
+    }
+    const uint64_t b_lo = __ballot(z_lo >= 0.f), b_hi = __ballot(z_hi >= 0.f);
+    if (lane < 4) {
+      const uint64_t w = lane < 2 ? b_lo : b_hi;
+      reinterpret_cast<uint32_t *>(bits + (size_t)t * (kD / 8))[lane] = (uint32_t)(w >> (32 * (lane & 1)));
+    }
+    if (lane == 0) {
+      norms[t] = n16;
+      rnorms[t] = float_to_half_bits(rn);
+    }
+    store_row<BITS>(plane + (size_t)t * (16 * BITS), c0, c1, lane, words[wave]);
+    // the residual buffer is read by every lane above before the next token overwrites it
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
+}
+
+template <int DTYPE>
+hipError_t launch_dtype(const QjlQuantArgs &a, dim3 grid, hipStream_t stream) {
+  switch (a.k.bits) {
+    case 2: qjl_quantize_kernel<DTYPE, 2><<<grid, 256, 0, stream>>>(a); break;
+    case 3: qjl_quantize_kernel<DTYPE, 3><<<grid, 256, 0, stream>>>(a); break;
+    case 4: qjl_quantize_kernel<DTYPE, 4><<<grid, 256, 0, stream>>>(a); break;
+    default: qjl_quantize_kernel<DTYPE, 8><<<grid, 256, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t stream) {
+  if (a.n_tokens < 1 || a.k.layout != TQ_LAYOUT_ROWS) return hipErrorInvalidValue;
+  const dim3 grid((a.n_tokens + kQjlTokens - 1) / kQjlTokens, a.k.n_kv_heads, batch);
+  if (a.x_dtype == TQ_F32) return launch_dtype<TQ_F32>(a, grid, stream);
+  if (a.x_dtype == TQ_BF16) return launch_dtype<TQ_BF16>(a, grid, stream);
+  return launch_dtype<TQ_F16>(a, grid, stream);
+}
+
+}  // namespace tq

@@ -93,7 +93,30 @@ struct DecodeArgs {
   // partials; a.lse_ml / a.lse_splits are the key pass's (m, l) per split
   float2 *vpart_ml;
   float *vpart_o;
+  // QJL keys (qjl_m > 0, the generic kernel only): beside the key codes, the sign sketch of each
+  // key's residual, [batch][n_kv_heads][capacity][qjl_m / 8] bytes, its fp16 norms
+  // [batch][n_kv_heads][capacity], and the sketch matrix S [qjl_m][d] fp32
+  const uint8_t *qjl_bits;
+  const uint16_t *qjl_rnorm;
+  const float *qjl_proj;
+  int qjl_m;
 };
+
+// QJL key quantization: the key cache k (ROWS) gets the codes and norms, bits / res_norms the
+// sign sketch of each token's residual and its fp16 norm, from S = proj [128][d] fp32.
+struct QjlQuantArgs {
+  CacheView k;
+  uint8_t *bits;
+  uint16_t *res_norms;
+  const float *proj;
+  const void *x;
+  int x_dtype;
+  int start_pos, n_tokens;
+};
+hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t stream);
+// The generic split kernel, the Sparse-V second pass (if a.sparse) and the split merge: any code
+// width, group <= 16, and the only path that takes QJL keys.
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_quantize(const CacheView &c, int batch, const void *x, int x_dtype,
                            int start_pos, int n_tokens, hipStream_t stream);

@@ -20,6 +20,8 @@ Workloads (d = 128 everywhere):
   ctx131k batch 4, 16/2 heads (group 8), 131072 tokens, bf16 N(0,1), 2% of the
           token positions of each sequence x8 in K and V (attention sinks),
           seed 5, K 4-bit / V 2-bit, Sparse V tau 1e-4.
+  qjl8k   as llama8k (seed 9) with QJL keys: 3-bit codes plus a 128-row Gaussian sign
+          sketch of the residual (sketch matrix from seed 10), V 2-bit.
 """
 from __future__ import annotations
 
@@ -37,6 +39,16 @@ def rotation_signs(d: int = D, seed: int = SIGN_SEED) -> torch.Tensor:
     g = torch.Generator(device="cpu").manual_seed(seed)
     bits = torch.randint(0, 2, (d,), generator=g)
     return (1 - 2 * bits).to(torch.int8)
+
+
+QJL_SEED = 10
+
+
+def qjl_projection(m: int = D, d: int = D, seed: int = QJL_SEED) -> torch.Tensor:
+    """Gaussian sketch matrix S [m, d] (fp32, CPU) with i.i.d. N(0, 1) entries, for the QJL
+    residual variant; drawn here and passed in (the library has no random generator)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn((m, d), generator=g, dtype=torch.float32)
 
 
 @dataclass
@@ -88,6 +100,10 @@ WORKLOADS = {
     # the batched long-context shape in a paged cache: 256-token pages, shuffled in the pool
     "paged32k": Workload("paged32k", 7, 16, 32, 8, 32768, 3, 2, torch.bfloat16, "student5",
                          outlier_channels=8, outlier_scale=4.0, append=1, page_tokens=256),
+    # the Llama-3-8B-shaped layer with QJL keys: 3-bit codes plus a 128-bit sign sketch of the
+    # residual (4 bits per coordinate in all), 2-bit values
+    "qjl8k": Workload("qjl8k", 9, 1, 32, 8, 8192, 3, 2, torch.bfloat16, "normal",
+                      head_channel_scales=(0.5, 20.0), append=1, extra={"qjl_m": 128}),
 }
 
 

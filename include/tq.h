@@ -99,6 +99,25 @@ typedef struct tq_cache {
   const int8_t *signs;
 } tq_cache;
 
+/* The QJL sign sketch that accompanies a key cache in the residual variant ([google] §第二步：
+ * QJL —— 1 bit 清理殘差: one bit per sketch row of a Johnson-Lindenstrauss projection of the
+ * first stage's error removes the bias of inner products, i.e. of attention scores).  For the
+ * key at (b, h, t) with codes idx, stored norm n16 and r = R x - n16 c[idx] (rotated domain):
+ *   bits       device [batch][n_kv_heads][capacity][m / 8] bytes, 16-byte aligned; bit j (LSB
+ *              first) of a row is 1 iff (S r)_j >= 0
+ *   res_norms  device [batch][n_kv_heads][capacity] fp16 bit patterns of ||r||, 2-byte aligned
+ *   proj       device [m][d] fp32: the Gaussian matrix S, i.i.d. N(0, 1) entries drawn by the
+ *              caller (the library has no random generator), 4-byte aligned
+ *   m          sketch rows; m must equal d (128): one bit per coordinate
+ * The key cache itself (tq_cache, ROWS layout) holds the first stage's codes and norms; with
+ * bits = b - 1 the key costs b bits per coordinate plus two fp16 norms. */
+typedef struct tq_qjl_sketch {
+  int32_t m;
+  uint8_t *bits;
+  uint16_t *res_norms;
+  const float *proj;
+} tq_qjl_sketch;
+
 /* Lloyd-Max codebook for the marginal density of one coordinate of a random unit
  * vector in R^d, f(x) proportional to (1 - x^2)^((d-3)/2) on [-1, 1] ([tq-80] §核心创新:
  * rotated coordinates are Beta distributed; the codebook is data-independent and
@@ -165,6 +184,32 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
                    int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
                    float sparse_v_tau, float *out, float *lse, float *scores, void *workspace,
                    size_t workspace_bytes, void *hip_stream);
+
+/* QJL residual variant, quantize: as tq_quantize_append into the key cache k (ROWS layout), and
+ * for each token the sign sketch of its residual and the residual's norm into s ([google]
+ * §第二步：QJL; [tq-80] §技术背景与学术渊源):
+ *   r = R x - n16 c[idx] (rotated domain, n16 the stored fp16 norm), ||r|| -> fp16 (nearest
+ *   even), bit j = ((S r)_j >= 0) with (S r)_j summed in fp32.
+ * A sign bit equals the one computed in exact arithmetic except where |(S r)_j| is within
+ * about 1e-5 ||S_j|| ||r|| of zero (fp32 rounding).  Positions outside the range are kept.
+ * Errors: TQ_ERR_INVALID_ARG (also for a GROUP8 key cache), TQ_ERR_UNSUPPORTED (m != d),
+ * TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void *x, int x_dtype,
+                           int start_pos, int n_tokens, void *hip_stream);
+
+/* QJL residual variant, decode attention: tq_decode_attn with every score corrected by the key's
+ * sign sketch ([google] _prod_score_kernel: the score against the codes plus the QJL term),
+ *   s_t = scale ( ||k_t||_fp16 (R q) . c_K[idx_t]
+ *                 + sqrt(pi/2) / m ||r_t||_fp16 (S R q) . (2 bits_t - 1) ),
+ * an unbiased estimate of scale q . k_t over the draw of S, followed by the same softmax,
+ * Sparse V, value sum and inverse rotation.  Arguments as tq_decode_attn plus ks, the sketch of
+ * the keys in k; the workspace is tq_decode_workspace_bytes(...).  Any code widths, groups up
+ * to 16 (fp32 vector arithmetic).
+ * Errors: as tq_decode_attn, and TQ_ERR_INVALID_ARG / TQ_ERR_UNSUPPORTED for the sketch. */
+int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cache *v, const void *q,
+                       int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,
+                       float sparse_v_tau, float *out, float *lse, float *scores, void *workspace,
+                       size_t workspace_bytes, void *hip_stream);
 
 /* Workspace bytes tq_decode_attn needs for this problem (0 for invalid arguments). */
 size_t tq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int ctx_len,

@@ -37,6 +37,7 @@ oracle for those values).
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -172,12 +173,15 @@ def codebook_distortion(d: int, centroids) -> float:
 # Rotation  ([inferrs] §核心技术; [tq-fwht] §2 FWHT 预处理)
 # ---------------------------------------------------------------------------
 
+@functools.lru_cache(maxsize=None)
 def hadamard(d: int) -> np.ndarray:
-    """Sylvester-ordered Hadamard matrix, H[i, j] = (-1)^popcount(i & j)."""
+    """Sylvester-ordered Hadamard matrix, H[i, j] = (-1)^popcount(i & j).  Built once per d
+    (entry by entry) and returned read-only."""
     h = np.empty((d, d), dtype=np.float64)
     for i in range(d):
         for j in range(d):
             h[i, j] = -1.0 if bin(i & j).count("1") % 2 else 1.0
+    h.setflags(write=False)
     return h
 
 
@@ -436,6 +440,82 @@ def ip_search(q, codes, norms16, signs, centroids, k: int):
         order = np.lexsort((np.arange(n), -s[j]))   # primary key: -score; then index
         idx[j] = order[:kk]
     return idx, np.take_along_axis(s, idx, axis=1), s
+
+
+# ---------------------------------------------------------------------------
+# QJL residual variant  ([google] §第二步：QJL —— 1 bit 清理殘差 and the mlx-vlm kernel list
+# (_qjl_score_kernel, _prod_score_kernel); [tq-80] §技术背景与学术渊源 (QJL, a residual
+# correction built on the Johnson-Lindenstrauss lemma))
+# ---------------------------------------------------------------------------
+
+def qjl_scale(m: int) -> float:
+    """kappa = sqrt(pi / 2) / m, the factor that makes the sign sketch's inner-product estimate
+    unbiased: for a Gaussian row s ~ N(0, I), E[sign(s . r) (s . q)] = sqrt(2 / pi) (q . r) / ||r||,
+    so sqrt(pi / 2) ||r|| / m sum_j sign((S r)_j) (S q)_j has mean q . r.  No sketch (m = 0)
+    gives no correction."""
+    return math.sqrt(math.pi / 2.0) / m if m > 0 else 0.0
+
+
+def qjl_quantize(x, signs, centroids, boundaries, proj):
+    """Quantize head vectors x[..., d] with the QJL residual variant.
+
+    [google] §第二步: after the first stage (here the (b-1)-bit rotate-and-code path of
+    `quantize`), one bit per sketch coordinate records the sign of a Johnson-Lindenstrauss
+    projection of the remaining error, which removes the bias of inner products (attention
+    scores).  Steps:
+      codes, n16, u = quantize(x)                      the MSE stage
+      r = R x - n16 c[codes]                           residual of the reconstruction the
+                                                       decoder makes, in the rotated domain
+      rn16 = fp16(||r||)                               its norm, stored as fp16
+      z = S r  (S: [m, d] Gaussian, an input)          the sketch
+      sigma_j = 1 if z_j >= 0 else 0                   one bit per row of S
+    Returns (codes, n16, sigma bool [..., m], rn16, u, z, ||r|| fp64)."""
+    codes, n16, u = quantize(x, signs, centroids, boundaries)
+    c = np.asarray(centroids, dtype=np.float64)
+    y = rotate(x, signs)
+    r = y - np.asarray(n16, dtype=np.float64)[..., None] * c[codes]
+    rn = np.sqrt(np.sum(r * r, axis=-1))
+    z = r @ np.asarray(proj, dtype=np.float64).T
+    return codes, n16, z >= 0.0, fp16_round(rn), u, z, rn
+
+
+def qjl_dequantize(codes, norms16, sigma, res_norms16, signs, centroids, proj) -> np.ndarray:
+    """The effective key of the QJL estimate: the vector k_hat with q . k_hat equal to the
+    estimate of q . x for every q,
+      k_hat = n16 R^T c[codes] + kappa rn16 R^T S^T (2 sigma - 1),   kappa = sqrt(pi/2) / m.
+    (The estimate is linear in q, so attention over these keys is attention with the
+    QJL-corrected scores.)"""
+    s_mat = np.asarray(proj, dtype=np.float64)
+    m = s_mat.shape[0]
+    base = dequantize(codes, norms16, signs, centroids)
+    if m == 0:
+        return base
+    pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0
+    corr = qjl_scale(m) * np.asarray(res_norms16, dtype=np.float64)[..., None] * (pm @ s_mat)
+    return base + unrotate(corr, signs)
+
+
+def qjl_inner_product(q, codes, norms16, sigma, res_norms16, signs, centroids, proj) -> np.ndarray:
+    """Estimate of q . x from the QJL code of x, computed in the rotated domain as the
+    score kernels do ([google] _prod_score_kernel: MSE part plus QJL correction):
+      n16 (R q) . c[codes] + kappa rn16 (S R q) . (2 sigma - 1)."""
+    qr = rotate(q, signs)
+    c = np.asarray(centroids, dtype=np.float64)[np.asarray(codes)]
+    s_mat = np.asarray(proj, dtype=np.float64)
+    mse = np.asarray(norms16, dtype=np.float64) * np.sum(qr * c, axis=-1)
+    if s_mat.shape[0] == 0:
+        return mse
+    pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0
+    return mse + qjl_scale(s_mat.shape[0]) * np.asarray(res_norms16, dtype=np.float64) * np.sum(
+        (qr @ s_mat.T) * pm, axis=-1)
+
+
+def qjl_near_zero_mask(z, r_norm, proj, band: float = 1e-5) -> np.ndarray:
+    """Sketch coordinates whose projection is within `band` of zero relative to its natural
+    scale, |z_j| <= band ||S_j|| ||r|| (|cos| of the angle between row j and r): there a sign
+    computed in fp32 may differ from the fp64 one, and either bit is accepted."""
+    rows = np.linalg.norm(np.asarray(proj, dtype=np.float64), axis=-1)
+    return np.abs(np.asarray(z)) <= band * rows * np.asarray(r_norm, dtype=np.float64)[..., None]
 
 
 def sparse_v_borderline(scores, lse, tau: float, rel: float = 1e-3) -> np.ndarray:

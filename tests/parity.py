@@ -126,3 +126,47 @@ def sparse_allowance(scores, lse, v_hat, tau, group):
     vn = np.linalg.norm(v_hat, axis=-1)                # [B, Hkv, T]
     vn_q = np.repeat(vn, group, axis=1)                # [B, Hq, T]
     return (p * border * vn_q).sum(-1), int(border.sum())
+
+
+def check_qjl_plane(cache, sketch, b, h, x64, start, signs, table, proj64):
+    """QJL keys of plane (b, h) at positions [start, start + n): codes and norms as
+    check_plane; on every token whose codes all equal the oracle's, the sign bits equal the
+    oracle's except where the projection is within 1e-5 ||S_j|| ||r|| of zero, and the fp16
+    residual norm is within 1e-3 relative.  (A code flip inside the boundary band moves the
+    residual by a centroid step and so may move many of its signs: such tokens are counted.)
+    Returns (near-boundary coordinates, near-zero sign bits, tokens with a code flip)."""
+    c, t = table
+    n = x64.shape[0]
+    near = check_plane(cache, b, h, x64, start, signs, table)
+    codes_g, _ = gpu_plane_codes(cache, b, h, start + n)
+    codes_g = codes_g[start:start + n]
+    codes_o, n16_o, sig_o, rn16_o, u, z, rn = o.qjl_quantize(x64, signs, c, t, proj64)
+    m = proj64.shape[0]
+    raw = sketch.plane_bits(b, h).cpu().numpy()[: (start + n) * m // 8]
+    sig_g = o.unpack(raw, start + n, m, 1, o.LAYOUT_ROWS)[start:].astype(bool)
+    same = np.all(codes_g == codes_o, axis=-1)
+    zero_band = o.qjl_near_zero_mask(z, rn, proj64, 1e-5)
+    bad = (sig_g != sig_o) & ~zero_band & same[:, None]
+    assert not bad.any(), (b, h, np.argwhere(bad)[:5])
+    rn_g = sketch.plane_res_norms(b, h)[start:start + n].cpu().numpy().astype(np.float64)
+    ref = rn16_o.astype(np.float64)
+    ok = np.abs(rn_g - ref) <= REL * np.abs(ref) + 1e-30
+    assert np.all(ok | ~same), (b, h, np.argwhere(~ok & same)[:5])
+    return near, int((zero_band & same[:, None]).sum()), int((~same).sum())
+
+
+def oracle_qjl_view(cache, sketch, signs, table, proj64, n_tokens):
+    """Effective QJL keys [batch, n_kv_heads, n_tokens, d] computed by the oracle from the
+    GPU-written codes, norms, sign bits and residual norms."""
+    c, _ = table
+    m = proj64.shape[0]
+    out = np.zeros((cache.batch, cache.n_kv_heads, n_tokens, cache.d))
+    for b in range(cache.batch):
+        for h in range(cache.n_kv_heads):
+            codes, _ = gpu_plane_codes(cache, b, h, n_tokens)
+            n16 = gpu_plane_norms(cache, b, h, n_tokens).astype(np.float16)
+            raw = sketch.plane_bits(b, h).cpu().numpy()[: n_tokens * m // 8]
+            sig = o.unpack(raw, n_tokens, m, 1, o.LAYOUT_ROWS).astype(bool)
+            rn16 = sketch.plane_res_norms(b, h)[:n_tokens].cpu().numpy().astype(np.float16)
+            out[b, h] = o.qjl_dequantize(codes, n16, sig, rn16, signs, c, proj64)
+    return out

@@ -232,6 +232,42 @@ def test_noalloc_decode_step_argument_validation():
     assert na(mid_k, mid_v, hq=64) == tq.TQ_ERR_WORKSPACE
 
 
+def test_qjl_argument_validation():
+    """The QJL calls check the sketch (pointers, alignment, m = d) and the key cache's layout
+    before any HIP call."""
+    L = tq.lib()
+
+    def sk(**kw):
+        base = dict(m=128, bits=FAKE + 0xA00000, res_norms=FAKE + 0xB00000, proj=FAKE + 0xC00000)
+        base.update(kw)
+        return tq.QjlSketchStruct(base["m"], base["bits"], base["res_norms"], base["proj"])
+
+    k = _cache(layout=0, bits=3)
+    x = FAKE + 0x500000
+    quant = lambda kk, ss, start=0, n=16: L.tq_qjl_quantize_append(ctypes.byref(kk), ctypes.byref(ss), x, 1, start, n,
+                                                                   None)
+    assert quant(k, sk(m=64)) == tq.TQ_ERR_UNSUPPORTED
+    assert quant(k, sk(bits=0)) == tq.TQ_ERR_INVALID_ARG
+    assert quant(k, sk(bits=FAKE + 8)) == tq.TQ_ERR_INVALID_ARG
+    assert quant(k, sk(res_norms=FAKE + 1)) == tq.TQ_ERR_INVALID_ARG
+    assert quant(_cache(layout=1, bits=3), sk()) == tq.TQ_ERR_INVALID_ARG
+    assert quant(k, sk(), start=1020, n=16) == tq.TQ_ERR_CAPACITY
+    assert quant(k, sk(), n=0) == tq.TQ_OK
+    v = _cache(layout=1, bits=2)
+    ws = tq.decode_workspace_bytes(1, 8, 2, 512, 0.0)
+
+    def dec(ss, hq=8, ctx=512, tau=0.0, wsb=ws):
+        return L.tq_qjl_decode_attn(ctypes.byref(k), ctypes.byref(ss), ctypes.byref(v), FAKE + 0x600000, 1, hq, None,
+                                    ctx, 0.088, tau, FAKE + 0x700000, None, None, FAKE + 0x800000, wsb, None)
+
+    assert dec(sk(m=0)) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(sk(proj=0)) == tq.TQ_ERR_INVALID_ARG
+    assert dec(sk(), hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert dec(sk(), ctx=4096) == tq.TQ_ERR_CAPACITY
+    assert dec(sk(), wsb=16) == tq.TQ_ERR_WORKSPACE
+    assert dec(sk(), tau=1.5) == tq.TQ_ERR_INVALID_ARG
+
+
 def _paged(**kw):
     base = dict(d=128, bits=4, layout=0, batch=2, n_kv_heads=2, page_tokens=256, n_pages=64, max_pages=16,
                 codes=FAKE, norms=FAKE + 0x1000000, block_table=FAKE + 0x1100000, centroids=FAKE + 0x200000,

@@ -1,0 +1,106 @@
+"""GPU parity of the QJL residual variant ([google] §第二步：QJL: a 1-bit Johnson-Lindenstrauss
+sketch of the first stage's error, for unbiased attention scores): the quantize kernel's codes,
+sign bits and residual norms against the oracle's, and decode attention with QJL-corrected
+scores against the oracle's attention over its effective keys, on the GPU-written cache."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import compressed_decode_attention_tq_amd as tq  # noqa: E402
+from compressed_decode_attention_tq_amd import inputs  # noqa: E402
+from oracle import tq_oracle as o  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("bits,dtype,n_tok,start", [(3, "bf16", 200, 0), (2, "f32", 130, 7), (4, "f16", 64, 64),
+                                                    (8, "bf16", 70, 1), (3, "f32", 1, 100)])
+def test_qjl_quantize_matches_oracle(bits, dtype, n_tok, start, golden_codebooks):
+    _say("qjl quantize", bits, dtype, n_tok, start)
+    w = inputs.WORKLOADS["qjl8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=n_tok, n_kv_heads=3, with_query=False)
+    x = g["k"].to({"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[dtype])
+    signs = inputs.rotation_signs()
+    proj = inputs.qjl_projection()
+    cap = ((start + n_tok + 63) // 64) * 64
+    kc = tq.PackedCache(2, 3, cap, bits, tq.LAYOUT_ROWS, signs.to(DEV), device=DEV)
+    sk = tq.QjlSketch(kc, proj, device=DEV)
+    kc.codes.fill_(0x5A)
+    sk.bits.fill_(0xC3)
+    tq.qjl_quantize_append(kc, sk, x.to(DEV).contiguous(), start)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    p64 = proj.numpy().astype(np.float64)
+    x64 = parity.to_f64(x)
+    tot = [0, 0, 0]
+    for b in range(2):
+        for h in range(3):
+            r = parity.check_qjl_plane(kc, sk, b, h, x64[b, :, h], start, s64, golden_codebooks[bits], p64)
+            tot = [a + c for a, c in zip(tot, r)]
+            if start > 0:  # positions before the range keep their stale sign bits
+                before = sk.plane_bits(b, h)[: start * 16].cpu().numpy()
+                assert np.all(before == 0xC3)
+    _say(f"  near-boundary coords {tot[0]}, near-zero sign bits {tot[1]}, tokens with a code flip {tot[2]}")
+
+
+def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, seq_lens=None):
+    _say("qjl decode", name, batch, hq, hkv, ctx, bits_k, tau, seq_lens)
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
+    signs = inputs.rotation_signs()
+    sd = signs.to(DEV)
+    proj = inputs.qjl_projection()
+    kc = tq.PackedCache(batch, hkv, cap, bits_k, tq.LAYOUT_ROWS, sd, device=DEV)
+    vc = tq.PackedCache(batch, hkv, cap, 2, tq.LAYOUT_GROUP8, sd, device=DEV)
+    sk = tq.QjlSketch(kc, proj, device=DEV)
+    tq.qjl_quantize_append(kc, sk, g["k"].to(DEV).contiguous(), 0)
+    tq.quantize_append(vc, g["v"].to(DEV).contiguous(), 0)
+    scale = 1.0 / math.sqrt(128)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    buf = tq.qjl_decode_attn(kc, sk, vc, g["q"].to(DEV).contiguous(), ctx, scale, tau=tau, seq_lens=sl,
+                             want_scores=True)
+    torch.cuda.synchronize()
+    s64 = signs.numpy().astype(np.float64)
+    p64 = proj.numpy().astype(np.float64)
+    kh = parity.oracle_qjl_view(kc, sk, s64, golden[bits_k], p64, ctx)
+    vh = parity.oracle_cache_view(vc, s64, golden[2], ctx)
+    out, lse, scores = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=seq_lens, tau=tau)
+    parity.check_scores(buf.scores.cpu().numpy(), scores, seq_lens)
+    fin = np.isfinite(lse)
+    got_lse = buf.lse.cpu().numpy()
+    assert np.all(np.isneginf(got_lse[~fin]))
+    assert np.allclose(got_lse[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    allowance, nb = None, 0
+    if tau > 0:
+        allowance, nb = parity.sparse_allowance(scores, lse, vh, tau, hq // hkv)
+    worst = parity.check_rows(buf.out.cpu().numpy(), out, "qjl decode out", allowance=allowance)
+    # the correction is not a no-op: the same codes without the sketch give other scores
+    kh_mse = parity.oracle_cache_view(kc, s64, golden[bits_k], ctx)
+    _, _, mse_scores = o.decode_attention(parity.to_f64(g["q"]), kh_mse, vh, scale, seq_lens=seq_lens)
+    diff = np.nanmax(np.abs(np.where(np.isfinite(scores), scores - mse_scores, 0.0)))
+    assert diff > 1e-2 * np.nanmax(np.abs(np.where(np.isfinite(scores), scores, 0.0)))
+    _say(f"  worst rel err {worst:.2e} borderline {nb}")
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, tau, seq_lens)
+    ("qjl8k", 1, 32, 8, 700, 768, 3, 0.0, None),
+    ("qjl8k", 2, 8, 2, 1000, 1024, 2, 0.0, [1000, 333]),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 1e-4, None),
+    ("ctx131k", 1, 16, 2, 900, 960, 4, 1e-4, [900]),
+    ("qjl8k", 3, 16, 1, 300, 320, 3, 0.0, [300, 0, 1]),
+])
+def test_qjl_decode_matches_oracle(case, golden_codebooks):
+    name, batch, hq, hkv, ctx, cap, bk, tau, sl = case
+    _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bk, golden_codebooks, tau=tau, seq_lens=sl)

@@ -484,6 +484,122 @@ def test_sparse_v_borderline_band_sign_and_empty_rows():
     assert m.tolist() == [[[False] * 6, [False, True, False, False, False, False]]]
 
 
+# ----------------------------------------------------------------- QJL residual variant
+
+
+def _qjl_case(golden, bits=1, seed=5):
+    """One vector with outlier channels and a query correlated with it, so that the MSE
+    stage's inner product is visibly biased (the reconstruction shrinks toward the centre)."""
+    rng = np.random.default_rng(seed)
+    s = _signs()
+    x = rng.standard_normal(D)
+    x[[3, 40, 77]] *= 8.0
+    q = x + 0.5 * rng.standard_normal(D)
+    c, t = golden[bits]
+    return s, x, q, c, t
+
+
+def _qjl_draws(s, x, q, c, t, n, seed):
+    """The estimate of q . x for n independent Gaussian sketches S (m = d)."""
+    rng = np.random.default_rng(seed)
+    est = np.empty(n)
+    for i in range(n):
+        proj = rng.standard_normal((D, D))
+        codes, n16, sig, rn16, _, _, _ = o.qjl_quantize(x, s, c, t, proj)
+        est[i] = o.qjl_inner_product(q, codes, n16, sig, rn16, s, c, proj)
+    return est
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_qjl_estimate_is_unbiased_over_sketches(bits, golden_codebooks):
+    """E_S[estimate] = q . x: the sign sketch with kappa = sqrt(pi/2)/m removes the MSE stage's
+    bias (Monte Carlo over 3000 sketches; a constant of sqrt(2/pi), 1, or a missing ||r||
+    misses by hundreds of standard errors).  The only bias left is the fp16 rounding of ||r||."""
+    s, x, q, c, t = _qjl_case(golden_codebooks, bits)
+    exact = float(q @ x)
+    codes, n16, _, rn16, _, _, rn = o.qjl_quantize(x, s, c, t, np.zeros((0, D)))
+    mse_only = float(q @ o.dequantize(codes, n16, s, c))
+    est = _qjl_draws(s, x, q, c, t, 3000, seed=11 + bits)
+    se = est.std(ddof=1) / math.sqrt(est.size)
+    resid_ip = exact - float(q @ o.dequantize(codes, n16, s, c))
+    fp16_bias = abs(resid_ip) * abs(float(rn16) / rn - 1.0)
+    assert abs(est.mean() - exact) <= 4.0 * se + fp16_bias
+    assert abs(mse_only - exact) >= 50.0 * se          # the bias QJL removes is large here
+
+
+def test_qjl_variance_matches_closed_form(golden_codebooks):
+    """Var_S[estimate] = (pi/2) rn16^2 / m (||Rq||^2 - (2/pi) ((Rq) . r / ||r||)^2): the variance
+    of one sign-times-projection term, summed over m independent rows and scaled by kappa rn16.
+    It pins the 1/m scaling and the ||r|| factor; the bound (pi/2) ||r||^2 ||q||^2 / m holds."""
+    s, x, q, c, t = _qjl_case(golden_codebooks, 2, seed=7)
+    codes, n16, _, rn16, _, _, rn = o.qjl_quantize(x, s, c, t, np.zeros((0, D)))
+    r = o.rotate(x, s) - float(n16) * c[codes]
+    qr = o.rotate(q, s)
+    rn16 = float(rn16)
+    var_exact = (math.pi / 2) * rn16 ** 2 / D * (qr @ qr - (2 / math.pi) * (qr @ r / rn) ** 2)
+    est = _qjl_draws(s, x, q, c, t, 6000, seed=21)
+    ratio = est.var(ddof=1) / var_exact
+    assert 0.92 < ratio < 1.08, ratio
+    assert var_exact <= (math.pi / 2) * rn16 ** 2 * (q @ q) / D
+
+
+def test_qjl_without_sketch_is_the_mse_path(golden_codebooks):
+    """m = 0: no correction, the (b-1)-bit rotate-and-code path of quantize / dequantize."""
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=20, golden=golden_codebooks)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, D))
+    tk = golden_codebooks[4][1]
+    empty = np.zeros((0, D))
+    codes, n16, sig, rn16, u, z, rn = o.qjl_quantize(x, s, ck, tk, empty)
+    c2, n2, u2 = o.quantize(x, s, ck, tk)
+    assert np.array_equal(codes, c2) and np.array_equal(n16, n2) and sig.shape == (6, 0)
+    assert np.array_equal(o.qjl_dequantize(codes, n16, sig, rn16, s, ck, empty), o.dequantize(codes, n16, s, ck))
+    qq = rng.standard_normal((6, D))
+    assert np.allclose(o.qjl_inner_product(qq, codes, n16, sig, rn16, s, ck, empty),
+                       np.sum(qq * o.dequantize(codes, n16, s, ck), axis=-1), rtol=1e-12, atol=1e-12)
+
+
+def test_qjl_routes_residual_and_special_vectors(golden_codebooks):
+    """Two routes to the same estimate (the effective key in the original domain, and the
+    rotated-domain sum the score kernels take); ||r|| equals ||x - x_hat|| of the dequantized
+    MSE stage; the zero vector gives r = 0, every sign bit 1 and no correction; the sign bits
+    pack as numpy.packbits (little bit order) does."""
+    s = _signs()
+    rng = np.random.default_rng(9)
+    c, t = golden_codebooks[3]
+    proj = rng.standard_normal((D, D))
+    x = rng.standard_normal((5, D)) * np.array([1.0, 3.0, 0.2, 10.0, 1.0])[:, None]
+    x[4] = 0.0
+    codes, n16, sig, rn16, u, z, rn = o.qjl_quantize(x, s, c, t, proj)
+    xh = o.dequantize(codes, n16, s, c)
+    assert np.allclose(rn, np.linalg.norm(x - xh, axis=-1), rtol=1e-12, atol=1e-12)
+    assert rn[4] == 0.0 and rn16[4] == 0.0 and sig[4].all()
+    qq = rng.standard_normal((5, D))
+    k_eff = o.qjl_dequantize(codes, n16, sig, rn16, s, c, proj)
+    direct = o.qjl_inner_product(qq, codes, n16, sig, rn16, s, c, proj)
+    assert np.allclose(np.sum(qq * k_eff, axis=-1), direct, rtol=1e-12, atol=1e-12)
+    assert np.allclose(k_eff[4], 0.0)
+    # the correction is kappa rn16 S^T (2 sigma - 1) in the rotated domain
+    corr = o.rotate(k_eff - xh, s)
+    assert np.allclose(corr[:4], (math.sqrt(math.pi / 2) / D) * rn16[:4, None].astype(np.float64)
+                       * ((2.0 * sig[:4] - 1.0) @ proj), rtol=1e-12, atol=1e-12)
+    packed = o.pack(sig[:4].astype(np.int64), 1, o.LAYOUT_ROWS)
+    assert np.array_equal(packed, np.packbits(sig[:4].reshape(-1), bitorder="little"))
+    assert packed.size == 4 * D // 8
+
+
+def test_qjl_near_zero_band(golden_codebooks):
+    """A sign bit may differ only where the projection is within 1e-5 ||S_j|| ||r|| of zero."""
+    proj = np.ones((4, D)) * np.array([1.0, 2.0, 0.5, 4.0])[:, None]     # row norms sqrt(D) x
+    rows = np.linalg.norm(proj, axis=-1)
+    rnorm = np.array([2.0, 0.5])
+    band = 1e-5
+    z = np.stack([rows * rnorm[0] * band * np.array([0.5, -0.5, 1.0, 0.0]),
+                  rows * rnorm[1] * band * np.array([1.5, -1.5, -2.0, 0.9])])
+    got = o.qjl_near_zero_mask(z, rnorm, proj, band)
+    assert got.tolist() == [[True, True, True, True], [False, False, False, True]]
+
+
 def _page_figures():
     out = {}
     with open(os.path.join(GOLDEN, "pages_format_figures.txt")) as fh:
