@@ -123,12 +123,14 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
     off = align_up(off + units * sizeof(int), 256);
     w.cand = off;
     off = align_up(off + units * (size_t)p.split_len * (1 + g) * sizeof(float), 256);
-    const SplitPlan dp = plan_fused(batch, n_kv_heads, ctx_len);
+    const SplitPlan dp = plan_fused_paged(batch, n_kv_heads, ctx_len);  // value pass: <= 64 tiles per wave
     const size_t vheads = (size_t)batch * n_q_heads * dp.n_splits;
     w.vpart_ml = off;
     off = align_up(off + vheads * sizeof(float2), 256);
     w.vpart_o = off;
     off = align_up(off + vheads * kD * sizeof(float), 256);
+    w.tile_max = off;
+    off = align_up(off + (size_t)batch * n_q_heads * ((ctx_len + 63) / 64) * sizeof(float), 256);
   }
   w.total = off;
   return w;
@@ -323,6 +325,8 @@ int setup_decode(const tq_cache *k, const tq_cache *v, const void *q, int q_dtyp
   if (a.sparse) {
     a.vpart_ml = reinterpret_cast<float2 *>(ws + w.vpart_ml);
     a.vpart_o = reinterpret_cast<float *>(ws + w.vpart_o);
+    a.tile_max = reinterpret_cast<float *>(ws + w.tile_max);
+    a.tile_stride = (ctx_len + 63) / 64;
   }
   return TQ_OK;
 }

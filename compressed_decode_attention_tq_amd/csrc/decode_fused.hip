@@ -246,9 +246,12 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // PAGED: the caches are page pools found through a.block_table; each tile lies inside one
 // page (pages are whole multiples of 64 tokens), so a tile's loads differ from the
 // contiguous case only by its base offset.
-// VMASK: Sparse V's value pass after the key pass: the dense kernel, with the value operand
-// P' of a row whose final weight exp(s - LSE) is below tau set to zero (LSE merged from the
-// key pass's partials a.lse_ml); the softmax sum still counts every row.
+// VMASK: Sparse V's value pass after the key pass.  The final LSE of every head is merged from
+// the key pass's partials (a.lse_ml) at set-up, so the pass needs no running softmax: p =
+// exp(s - LSE) is the final weight, and a row with p < tau adds nothing (no renormalisation).
+// A wave visits only the tiles whose largest score (a.tile_max, written by the key pass)
+// reaches some head's threshold LSE + ln tau: it loads keys and values of those tiles alone.
+// Partials are then already normalised: the merge sums them and writes the key pass's LSE.
 template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
@@ -391,7 +394,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       qw0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qbase);
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
-    if (!defer_keys) load_keys(wave);
+    if (!defer_keys && !VMASK) load_keys(wave);
+    // VMASK: the maxima of the wave's tiles (lane k: tile wave + 8 k) for every head of the group,
+    // loaded now so that only the comparison waits for the thresholds
+    float tmx[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) tmx[h] = -INFINITY;
+    if constexpr (VMASK) {
+      const int tile_k = wave + kWaves * lane;
+      if (tile_k < n_tiles) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          if (vlive(h)) tmx[h] = a.tile_max[vrow(h) * a.tile_stride + (t_begin >> 6) + tile_k];
+      }
+    }
     build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
     // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
@@ -430,8 +446,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       const float qs = a.scale * kInvSqrtD * kLog2e;
       *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
     }
-    float *thr_lds = reinterpret_cast<float *>(lds + kWBase + 4096 + 64);  // [NH], set-up only
-    if constexpr (VMASK) {  // head `wave`: threshold on s (log2 units) = (LSE + ln tau) log2 e
+    // VMASK, set-up only: [0, NH) thresholds on s (log2 units) = (LSE + ln tau) log2 e, [8, 8 + NH)
+    // the LSE in log2 units (the fixed softmax reference of the pass)
+    float *thr_lds = reinterpret_cast<float *>(lds + kWBase + 4096 + 64);
+    float lse_own = -INFINITY;  // VMASK: natural-log LSE of head `wave`
+    if constexpr (VMASK) {
       if (wave < NH) {
         float m = -INFINITY, l = 0.f;
         if (vlive(wave)) {
@@ -443,7 +462,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
               if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - m);
           l = wave_reduce<false>(l);
         }
-        if (lane == 0) thr_lds[wave] = m == -INFINITY ? INFINITY : (m + __logf(l) + a.ln_tau) * kLog2e;
+        lse_own = m == -INFINITY ? -INFINITY : m + __logf(l);
+        if (lane == 0) {
+          thr_lds[wave] = m == -INFINITY ? INFINITY : (lse_own + a.ln_tau) * kLog2e;
+          thr_lds[8 + wave] = lse_own * kLog2e;
+        }
       }
     }
     __syncthreads();
@@ -451,9 +474,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the new token's stores are complete
       if (defer_keys) load_keys(wave);
     }
-    float vthr[NH2];
+    float vthr[NH2], vref[NH2];
 #pragma unroll
-    for (int hh = 0; hh < NH2; ++hh) vthr[hh] = VMASK ? thr_lds[half_id * NH2 + hh] : -INFINITY;
+    for (int hh = 0; hh < NH2; ++hh) {
+      vthr[hh] = VMASK ? thr_lds[half_id * NH2 + hh] : -INFINITY;
+      vref[hh] = VMASK ? thr_lds[8 + half_id * NH2 + hh] : -INFINITY;
+    }
+    // VMASK: bit k of `need` = tile wave + 8 k holds a score that reaches some head's threshold
+    uint64_t need = 0;
+    if constexpr (VMASK) {
+      bool nd = false;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) nd |= tmx[h] >= thr_lds[h];
+      need = __ballot(nd);
+    }
     // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
     half8 qop[8];
     {
@@ -495,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // ---- per-lane softmax state: heads half_id*NH2 + hh
     float mr[NH2], lsum[NH2];
 #pragma unroll
-    for (int hh = 0; hh < NH2; ++hh) { mr[hh] = -INFINITY; lsum[hh] = 0.f; }
+    for (int hh = 0; hh < NH2; ++hh) { mr[hh] = vref[hh]; lsum[hh] = 0.f; }
     floatx4 oacc[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -504,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     // one tile; PREFETCH issues the key loads of the wave's next tile.  The last tile is
     // peeled off so that the loads are never conditional inside the loop body: a load
     // issued on one path only would make every later wait cover it as well.
-    auto tile_body = [&](int tile, auto prefetch_tag) {
+    auto tile_body = [&](int tile, int next_tile, auto prefetch_tag) {
       constexpr bool PREFETCH = decltype(prefetch_tag)::value;
       const int t0 = t_begin + tile * kTile;
       const uint32_t tok = tile_tok(tile);
@@ -559,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         __builtin_amdgcn_sched_barrier(0);
       }
       const uint32_t nk_pair = nkw;
-      if (PREFETCH) load_keys(tile + kWaves);
+      if (PREFETCH) load_keys(next_tile);
 
       // lane holds rows 4q..4q+3 (heads 2q, 2q+1; fp16 and remainder rows) of token 16s+m_row
       if (NH == 8 || quarter < 2) {
@@ -639,6 +673,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
 #pragma unroll
         for (int hh = 0; hh < NH2; ++hh) {
           const float z = half_max(fmaxf(sc[0][hh], sc[1][hh]));
+          if (a.tile_max != nullptr && pr == 0 && half_id * NH2 + hh < g)  // the tile's largest score
+            a.tile_max[vrow(half_id * NH2 + hh) * a.tile_stride + (t0 >> 6)] = z;
           const float m_new = fmaxf(mr[hh], z);
           lsum[hh] = lsum[hh] * exp2_or_zero(mr[hh], m_new) + exp2_or_zero(sc[0][hh], m_new) +
                      exp2_or_zero(sc[1][hh], m_new);
@@ -701,7 +737,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           p[tb][hh] = __builtin_amdgcn_exp2f(sc[tb][hh] - mr[hh]);
           vmax = fmaxf(vmax, p[tb][hh] * nv[tb]);
         }
-      if (causal_tile || __any(!(vmax <= kAMax))) {
+      // (VMASK: the reference is the final LSE, so p <= 1 and never moves; P' is clamped to the
+      // fp16 range below)
+      if (!VMASK && (causal_tile || __any(!(vmax <= kAMax)))) {
         // move each head's reference to the tile's largest s + log2||v||, rescale
         float alpha[NH2];
 #pragma unroll
@@ -731,8 +769,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           oacc[n][2] *= a1; oacc[n][3] *= a1;
         }
       }
+      if constexpr (!VMASK) {
 #pragma unroll
-      for (int hh = 0; hh < NH2; ++hh) lsum[hh] += p[0][hh] + p[1][hh];
+        for (int hh = 0; hh < NH2; ++hh) lsum[hh] += p[0][hh] + p[1][hh];
+      }
 
       if (a.scores != nullptr) {
 #pragma unroll
@@ -760,8 +800,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         const int h = half_id * NH2 + hh;
         float v0 = p[0][hh] * nv[0], v1 = p[1][hh] * nv[1];
         if constexpr (VMASK) {  // Sparse V: rows under the final-weight threshold add no value
-          if (!(sc[0][hh] >= vthr[hh])) v0 = 0.f;
-          if (!(sc[1][hh] >= vthr[hh])) v1 = 0.f;
+          v0 = sc[0][hh] >= vthr[hh] ? fminf(v0, 65504.f) : 0.f;
+          v1 = sc[1][hh] >= vthr[hh] ? fminf(v1, 65504.f) : 0.f;
         }
         half2v hi, lo;
         hi[0] = (_Float16)v0;
@@ -805,9 +845,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    int tile = wave;
-    for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, std::true_type{});
-    if (tile < n_tiles) tile_body(tile, std::false_type{});
+    if constexpr (VMASK) {  // the needed tiles only, the next one's keys prefetched
+      uint64_t rem = need;
+      if (rem != 0) {
+        int tile = wave + kWaves * (int)__builtin_ctzll(rem);
+        rem &= rem - 1;
+        load_keys(tile);
+        while (rem != 0) {
+          const int next = wave + kWaves * (int)__builtin_ctzll(rem);
+          rem &= rem - 1;
+          tile_body(tile, next, std::true_type{});
+          tile = next;
+        }
+        tile_body(tile, 0, std::false_type{});
+      }
+    } else {
+      int tile = wave;
+      for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, tile + kWaves, std::true_type{});
+      if (tile < n_tiles) tile_body(tile, 0, std::false_type{});
+    }
 
     // ---- combine the 8 waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
     //      the start of the key-table region (free once every wave is past its tiles), so
@@ -932,8 +988,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
             }
           }
           l = wave_reduce<false>(l);
-          o0 /= l;
-          o1 /= l;
+          if constexpr (!VMASK) {  // (VMASK partials are final weights already)
+            o0 /= l;
+            o1 /= l;
+          }
         }
         // inverse rotation: x = s * (H y) / sqrt(128)
         float y0 = o0 + o1, y1 = o0 - o1;
@@ -944,7 +1002,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
         if (sgn & 0x8000u) y1 = -y1;
         const size_t orow = vrow(wave);
         *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
-        if (lane == 0 && a.lse != nullptr) a.lse[orow] = M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
+        if (lane == 0 && a.lse != nullptr)
+          a.lse[orow] = VMASK ? lse_own : M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
         if (a.scores != nullptr) {
           float *row = a.scores + orow * a.ctx_len;
           for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;

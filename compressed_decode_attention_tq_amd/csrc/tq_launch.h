@@ -35,8 +35,9 @@ struct WorkspaceLayout {
   size_t part_o;      // float  [batch][n_q_heads][n_splits][128] rotated-domain sums
   size_t cand_count;  // int    [batch][n_kv_heads][n_splits]      Sparse-V candidates
   size_t cand;        // float  [batch][n_kv_heads][n_splits][split_len][1 + g]
-  size_t vpart_ml;    // Sparse V, masked value pass: float2 [batch][n_q_heads][dense fused splits]
-  size_t vpart_o;     //   and float [batch][n_q_heads][dense fused splits][128]
+  size_t vpart_ml;    // Sparse V, masked value pass: float2 [batch][n_q_heads][value-pass splits]
+  size_t vpart_o;     //   and float [batch][n_q_heads][value-pass splits][128]
+  size_t tile_max;    // Sparse V: float [batch][n_q_heads][ceil(ctx_len / 64)] per-tile maxima
   size_t total;
 };
 
@@ -93,6 +94,11 @@ struct DecodeArgs {
   // partials; a.lse_ml / a.lse_splits are the key pass's (m, l) per split
   float2 *vpart_ml;
   float *vpart_o;
+  // Sparse V: the key pass writes the largest scaled score (log2 units) of every (batch, query
+  // head, 64-token tile) to tile_max[(b * n_q_heads + h) * tile_stride + t / 64]; the value pass
+  // visits only the tiles whose maximum reaches some head's threshold
+  float *tile_max;
+  int tile_stride;
   // QJL keys (qjl_m > 0, the generic kernel only): beside the key codes, the sign sketch of each
   // key's residual, [batch][n_kv_heads][capacity][qjl_m / 8] bytes, its fp16 norms
   // [batch][n_kv_heads][capacity], and the sketch matrix S [qjl_m][d] fp32
