@@ -123,7 +123,7 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
     off = align_up(off + units * sizeof(int), 256);
     w.cand = off;
     off = align_up(off + units * (size_t)p.split_len * (1 + g) * sizeof(float), 256);
-    const SplitPlan dp = plan_fused_paged(batch, n_kv_heads, ctx_len);  // value pass: <= 64 tiles per wave
+    const SplitPlan dp = plan_fused_vmask(batch, n_kv_heads, ctx_len);  // value pass: <= 64 tiles per split
     const size_t vheads = (size_t)batch * n_q_heads * dp.n_splits;
     w.vpart_ml = off;
     off = align_up(off + vheads * sizeof(float2), 256);
@@ -164,6 +164,15 @@ SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len) {
   if (p.split_len > kPagedMaxSplit) {
     p.split_len = kPagedMaxSplit;
     p.n_splits = (ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit;
+  }
+  return p;
+}
+
+SplitPlan plan_fused_vmask(int batch, int n_kv_heads, int ctx_len) {
+  SplitPlan p = plan_fused(batch, n_kv_heads, ctx_len);
+  if (p.split_len > kVmaskMaxSplit) {
+    p.split_len = kVmaskMaxSplit;
+    p.n_splits = (ctx_len + kVmaskMaxSplit - 1) / kVmaskMaxSplit;
   }
   return p;
 }

@@ -395,13 +395,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
     if (!defer_keys && !VMASK) load_keys(wave);
-    // VMASK: the maxima of the wave's tiles (lane k: tile wave + 8 k) for every head of the group,
-    // loaded now so that only the comparison waits for the thresholds
+    // VMASK: a split of at most 64 tiles is shared out by need (lane k looks at tile k); a longer
+    // one (at most 64 tiles per wave) keeps the round-robin tiles (lane k: tile wave + 8 k), where
+    // most tiles are needed anyway.  The maxima of those tiles for every head of the group are
+    // loaded now, so that only the comparison waits for the thresholds.
+    const bool by_need = n_tiles <= 64;
     float tmx[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) tmx[h] = -INFINITY;
     if constexpr (VMASK) {
-      const int tile_k = wave + kWaves * lane;
+      const int tile_k = by_need ? lane : wave + kWaves * lane;
       if (tile_k < n_tiles) {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -480,14 +483,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       vthr[hh] = VMASK ? thr_lds[half_id * NH2 + hh] : -INFINITY;
       vref[hh] = VMASK ? thr_lds[8 + half_id * NH2 + hh] : -INFINITY;
     }
-    // VMASK: bit k of `need` = tile wave + 8 k holds a score that reaches some head's threshold
+    // VMASK: the needed tiles (a score reaches some head's threshold).  By need, the k-th needed
+    // tile of the split goes to wave k mod 8, so that a wave gets at most one more than another,
+    // and bit k of `need` is tile k; round robin, bit k is tile wave + 8 k.
     uint64_t need = 0;
     if constexpr (VMASK) {
       bool nd = false;
 #pragma unroll
       for (int h = 0; h < NH; ++h) nd |= tmx[h] >= thr_lds[h];
-      need = __ballot(nd);
+      const uint64_t all = __ballot(nd);
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(all >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)all, 0u));
+      need = by_need ? __ballot(nd && (rank & (kWaves - 1)) == wave) : all;
     }
+    auto need_tile = [&](int bit) { return by_need ? bit : wave + kWaves * bit; };
     // operand rows: 2h = fp16 part of head h, 2h+1 = remainder; rows >= 2*NH are zero
     half8 qop[8];
     {
@@ -845,14 +853,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    if constexpr (VMASK) {  // the needed tiles only, the next one's keys prefetched
+    if constexpr (VMASK) {  // the wave's needed tiles only, the next one's keys prefetched
       uint64_t rem = need;
       if (rem != 0) {
-        int tile = wave + kWaves * (int)__builtin_ctzll(rem);
+        int tile = need_tile((int)__builtin_ctzll(rem));
         rem &= rem - 1;
         load_keys(tile);
         while (rem != 0) {
-          const int next = wave + kWaves * (int)__builtin_ctzll(rem);
+          const int next = need_tile((int)__builtin_ctzll(rem));
           rem &= rem - 1;
           tile_body(tile, next, std::true_type{});
           tile = next;
@@ -1066,7 +1074,10 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {
-  if (!decode_fused_supported(a) || a.lse_ml == nullptr || a.lse_splits < 1) return hipErrorInvalidValue;
+  // one lane per tile decides which tiles a wave needs: at most 64 tiles per wave
+  if (!decode_fused_supported(a) || a.lse_ml == nullptr || a.lse_splits < 1 || a.tile_max == nullptr ||
+      a.fplan.split_len > kVmaskMaxSplit)
+    return hipErrorInvalidValue;
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   return a.k.bits == 4 ? launch_nh<4, false, false, false, false, true>(a, (int)items, stream)

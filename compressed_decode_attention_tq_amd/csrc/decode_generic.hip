@@ -552,7 +552,7 @@ hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
   v2.sparse = 0;
   v2.lse_ml = a.fpart_ml;
   v2.lse_splits = a.fplan.n_splits;
-  v2.fplan = plan_fused_paged(a.batch, a.n_kv_heads, a.ctx_len);  // at most 64 tiles per wave
+  v2.fplan = plan_fused_vmask(a.batch, a.n_kv_heads, a.ctx_len);  // at most 64 tiles per split
   v2.fpart_ml = a.vpart_ml;
   v2.fpart_o = a.vpart_o;
   if (a.sparse && decode_fused_sparse_supported(a) && a.vpart_ml != nullptr && a.tile_max != nullptr &&

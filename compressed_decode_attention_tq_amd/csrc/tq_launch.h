@@ -143,6 +143,10 @@ hipError_t launch_append_paged(const CacheView &kc, const CacheView &vc, const i
 // wave's page offsets.
 constexpr int kPagedMaxSplit = 8 * 64 * 64;
 SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len);
+// Splits of Sparse V's value pass: the dense plan with at most 64 tiles per wave (8 * 64 * 64
+// tokens per split), so that one lane per tile decides which tiles a wave needs.
+constexpr int kVmaskMaxSplit = 8 * 64 * 64;
+SplitPlan plan_fused_vmask(int batch, int n_kv_heads, int ctx_len);
 WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len);
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
 // Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
