@@ -252,14 +252,23 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // A wave visits only the tiles whose largest score (a.tile_max, written by the key pass)
 // reaches some head's threshold LSE + ln tau: it loads keys and values of those tiles alone.
 // Partials are then already normalised: the merge sums them and writes the key pass's LSE.
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false>
-__global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
+// RECORDS (with SPARSE): the key pass also writes candidate records for the record-based second
+// pass; without, it writes only the (m, l) partials and the per-tile maxima the masked value
+// pass reads.
+// The key pass without records needs only the key table and the score staging: its LDS is the
+// 64 KB table plus 2 KB per wave (80 KB).  (Two such workgroups per CU, 4 waves per SIMD at 128
+// VGPRs, made the pass slower: 22 -> 28 us on the 131072-token workload, with spills.)
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false, bool RECORDS = true>
+__device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PAGED || !(SPARSE || MULTI), "paged caches: dense single-query decode");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND || PAGED), "masked value pass: dense decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
+  constexpr uint32_t WBASE = KEYS_ONLY ? kVBase : kWBase;  // per-wave staging buffers
+  constexpr uint32_t WSTRIDE = KEYS_ONLY ? 2048u : 4096u;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KEYS_ONLY ? kVBase + kWaves * 2048 : kLdsBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
@@ -269,10 +278,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   const int pr = lane & 31, half_id = lane >> 5;  // softmax mapping: tokens 2pr, 2pr+1
   const uint32_t kc8 = (uint32_t)(lane & 31) << 3;
   const uint32_t vc8 = ((uint32_t)(lane & 31) << 3) | kVBase;
-  uint8_t *wbuf = lds + kWBase + wave * 4096;
-  float *qrot = reinterpret_cast<float *>(lds + kWBase);  // [NH][128] between tiles
+  uint8_t *wbuf = lds + WBASE + wave * WSTRIDE;
+  float *qrot = reinterpret_cast<float *>(lds + WBASE);  // [NH][128] between tiles
 
-  if (NH == 4)  // P' rows 8..15 stay zero for the whole launch
+  if (!SPARSE && NH == 4)  // P' rows 8..15 stay zero for the whole launch
     *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 
   {  // one split of one (batch, kv head) per workgroup
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
     int *chunk_count = reinterpret_cast<int *>(lds + kVBase);
     const int c_first = SPARSE ? t_begin / a.plan.split_len : 0;
     const int n_chunks = SPARSE ? a.fplan.split_len / a.plan.split_len : 0;
-    if (SPARSE && (int)threadIdx.x < n_chunks) chunk_count[threadIdx.x] = 0;
+    if (SPARSE && RECORDS && (int)threadIdx.x < n_chunks) chunk_count[threadIdx.x] = 0;
 
     // ---- rotated query group: wave h rotates head h into qrot[h]
     if (wave < NH) {
@@ -687,14 +696,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
           lsum[hh] = lsum[hh] * exp2_or_zero(mr[hh], m_new) + exp2_or_zero(sc[0][hh], m_new) +
                      exp2_or_zero(sc[1][hh], m_new);
           mr[hh] = m_new;
-          if (half_id * NH2 + hh < g) {
+          if (RECORDS && half_id * NH2 + hh < g) {
             cand0 |= sc[0][hh] != -INFINITY && sc[0][hh] >= m_new + log2_tau;
             cand1 |= sc[1][hh] != -INFINITY && sc[1][hh] >= m_new + log2_tau;
           }
         }
         // token 2pr + tb is a candidate if either head half flags it; records are
         // {token, g scores (natural log)} at consecutive slots of the tile's second-pass split
-        if (a.cand == nullptr) { cand0 = false; cand1 = false; }  // key pass for the LSE only
+        if (!RECORDS || a.cand == nullptr) { cand0 = false; cand1 = false; }  // key pass for the LSE only
         const uint64_t b0 = __ballot(cand0), b1 = __ballot(cand1);
         const uint32_t c0 = (uint32_t)b0 | (uint32_t)(b0 >> 32);
         const uint32_t c1 = (uint32_t)b1 | (uint32_t)(b1 >> 32);
@@ -916,7 +925,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
       if (wave < NH && vlive(wave) && lane == 0)
         a.fpart_ml[vrow(wave) * S + split] =
             make_float2(Mh == -INFINITY ? -INFINITY : Mh * kLn2, Lh);
-      for (int i = threadIdx.x; i < n_chunks && a.cand_count != nullptr; i += blockDim.x)
+      for (int i = threadIdx.x; RECORDS && i < n_chunks && a.cand_count != nullptr; i += blockDim.x)
         if (c_first + i < a.plan.n_splits)
           a.cand_count[((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + c_first + i] = chunk_count[i];
       return;
@@ -1022,10 +1031,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a)
   }
 }
 
-template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false>
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS>
+__global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
+  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS>(a);
+}
+
+template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
-  if (a.vg_size <= 4) decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK><<<grid, kThreads, 0, stream>>>(a);
-  else decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK><<<grid, kThreads, 0, stream>>>(a);
+  if (a.vg_size <= 4) {
+    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS><<<grid, kThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1087,6 +1104,9 @@ hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream) {
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  if (a.cand == nullptr)  // the LSE and tile maxima only (before the masked value pass)
+    return a.k.bits == 4 ? launch_nh<4, true, false, false, false, false, false>(a, (int)items, stream)
+                         : launch_nh<3, true, false, false, false, false, false>(a, (int)items, stream);
   return a.k.bits == 4 ? launch_bk<4, true>(a, (int)items, stream) : launch_bk<3, true>(a, (int)items, stream);
 }
 
