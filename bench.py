@@ -983,7 +983,7 @@ def calibrate_copy(torch, log):
 
 def _short(name: str) -> str:
     n = name.replace("void ", "").replace("tq::(anonymous namespace)::", "")
-    return n.split("(")[0][:60]
+    return n.split("(")[0][:90]
 
 
 def summarize_stats(args):
@@ -993,9 +993,9 @@ def summarize_stats(args):
         sys.exit(f"no kernel_stats.csv under {args.summarize_stats}")
     rows = list(csv.DictReader(open(files[0])))
     lines = [f"# {args.name}", "", f"command: {args.command}", "",
-             f"{'kernel':60s} {'calls':>7s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} {'total %':>8s}"]
+             f"{'kernel':90s} {'calls':>7s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} {'total %':>8s}"]
     for r in rows:
-        lines.append(f"{_short(r['Name']):60s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+        lines.append(f"{_short(r['Name']):90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
     out = "\n".join(lines) + "\n"
     with open(os.path.join(ROOT, "profiles", f"{args.name}.txt"), "w") as fh:
