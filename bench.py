@@ -49,6 +49,7 @@ METRIC = "compressed-KV decode attention KV-tokens/s & HBM GB/s; quantize tokens
 HBM_PEAK_GBS = 8000.0
 D = 128
 COPY_BYTES = 512 << 20
+MAX_COPIES = 256   # small workloads are launch-bound; more copies only lengthen the set-up
 CALIBRATION_COPIES = 5
 CALIBRATION_KERNEL = "copyBuffer"   # the HIP runtime's device-to-device copy kernel
 DECODE_KERNEL = "decode_fused_kernel"
@@ -340,7 +341,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     bk, bv = w.bits_k, w.bits_v
     cap = ctx
     per_copy = tq.code_bytes(D, bk, batch, hkv, cap) + tq.code_bytes(D, bv, batch, hkv, cap) + 4 * batch * hkv * cap
-    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
     log(f"[bench] workload={w.name} tau={tau} copies={copies} cache/copy={per_copy / 1e6:.1f} MB "
         f"({'eager launches' if args.eager else 'HIP graph replay'})")
     g = inputs.generate(w, device=dev)
@@ -517,7 +518,7 @@ def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
     max_pages = (ctx + P - 1) // P
     n_pages = batch * max_pages
     per_copy = tq.code_bytes(D, bk, n_pages, hkv, P) + tq.code_bytes(D, bv, n_pages, hkv, P) + 4 * n_pages * hkv * P
-    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
     log(f"[bench] workload={w.name} pages of {P} tokens, {n_pages} pages, copies={copies} "
         f"cache/copy={per_copy / 1e6:.1f} MB ({'eager launches' if args.eager else 'HIP graph replay'})")
     g = inputs.generate(w, device=dev)
@@ -602,7 +603,7 @@ def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
     k_row = D * bk // 8 + 2 + m // 8 + 2       # codes + norm + sign bits + residual norm
     v_row = D * bv // 8 + 2
     per_copy = batch * hkv * ctx * (k_row + v_row)
-    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
     log(f"[bench] workload={w.name} QJL keys ({bk}-bit codes + {m} sign bits) copies={copies} "
         f"cache/copy={per_copy / 1e6:.1f} MB ({'eager launches' if args.eager else 'HIP graph replay'})")
     g = inputs.generate(w, device=dev)
@@ -715,7 +716,7 @@ def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):
     queries over the whole quantized database (score, chunk top-k and merge kernels)."""
     n, nq, k, bits = spec["n"], spec["n_queries"], spec["top_k"], spec["bits"]
     per_copy = tq.code_bytes(D, bits, 1, 1, n) + 2 * n
-    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
     log(f"[bench] search n={n} queries={nq} top_k={k} bits={bits} copies={copies} db/copy={per_copy / 1e6:.1f} MB "
         f"({'eager launches' if args.eager else 'HIP graph replay'})")
     g = inputs.generate_search(spec, device=dev)
@@ -794,7 +795,7 @@ def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
     batch, hq, hkv, ctx, n_q = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx, w.n_q
     bk, bv = w.bits_k, w.bits_v
     per_copy = tq.code_bytes(D, bk, batch, hkv, ctx) + tq.code_bytes(D, bv, batch, hkv, ctx) + 4 * batch * hkv * ctx
-    copies = args.copies or max(1, math.ceil(600e6 / per_copy))
+    copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
     rows = n_q * w.group
     vgroups = (rows + 7) // 8
     log(f"[bench] workload={w.name} n_q={n_q} ({rows} query rows per kv head in {vgroups} groups) "

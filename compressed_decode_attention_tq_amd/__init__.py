@@ -8,6 +8,7 @@ There is no CPU fallback: if libtq.so has not been built, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import numpy as np
@@ -120,6 +121,12 @@ def _check(status: int, what: str):
 
 def make_codebook_table(d: int, bits: int):
     """Host call: fp32 (centroids[2^bits], boundaries[2^bits - 1]) as numpy arrays."""
+    c, t = _codebook_table(d, bits)
+    return c.copy(), t.copy()
+
+
+@functools.lru_cache(maxsize=None)
+def _codebook_table(d: int, bits: int):
     c = np.zeros(1 << bits, dtype=np.float32)
     t = np.zeros(max((1 << bits) - 1, 1), dtype=np.float32)
     _check(lib().tq_make_codebook_table(d, bits, c.ctypes.data, t.ctypes.data), "tq_make_codebook_table")
