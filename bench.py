@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 METRIC = "compressed-KV decode attention KV-tokens/s & HBM GB/s; quantize tokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 matrix peak of the MI355X
 D = 128
 COPY_BYTES = 512 << 20
 MAX_COPIES = 256   # small workloads are launch-bound; more copies only lengthen the set-up
@@ -63,7 +64,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="batch32k",
                    choices=["tiny", "llama8k", "batch32k", "prefill", "ctx131k", "verify8k", "paged32k", "search1m",
-                            "qjl8k"])
+                            "qjl8k", "chunk8k"])
     p.add_argument("--tau", type=float, default=None, help="Sparse-V threshold (default: workload's)")
     p.add_argument("--copies", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -223,7 +224,8 @@ def main():
         result = bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log)
     stream = stream_read_gbs(torch, tq, log)
     result["roofline"]["stream_read_gbs"] = stream
-    result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
+    if result["roofline"]["unit"] == "GB/s":
+        result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
     traffic = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
     launches = result.pop("_launches", 1)  # traffic per step when a step is several launches
     result["roofline"]["traffic"] = None if traffic is None else traffic * launches
@@ -840,8 +842,14 @@ def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
     ms_a = timer.per_iteration_ms(append, max(args.steps, 2 * copies), 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
     achieved = nbytes / (ms_k / 1e3) / 1e9
+    # causal (query row, visible token) pairs: QK and PV take 2 d multiply-adds per pair
+    pairs = batch * hq * sum(max(ctx - n_q + i + 1, 0) for i in range(n_q))
+    flops = 4 * D * pairs
+    tflops = flops / (ms_k / 1e3) / 1e12
+    prefill = vgroups >= 8
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, attention call {ms_k * 1e3:.1f} us "
-        f"({n_q} positions), append {n_q} tokens (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic")
+        f"({n_q} positions), append {n_q} tokens (K+V) {ms_a * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic, "
+        f"{tflops:.1f} TFLOP/s algorithmic")
     result = {
         "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -855,11 +863,21 @@ def bench_multi_query(args, w, signs, dev, tq, inputs, torch, np, log):
         "attention_call_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
         "query_positions_per_s": batch * n_q / (ms_per_step / 1e3),
         "append_kv_us": ms_a * 1e3,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": DECODE_KERNEL,
-                     "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
-                     "note": f"algorithmic bytes read the cache once; the kernel reads it once per "
-                             f"group of up to 8 query rows ({vgroups} here)"},
+        "roofline": ({"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                      "kernel": DECODE_KERNEL + " (prefill: 8 row groups per workgroup)",
+                      "flops_per_launch": flops, "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
+                      "hbm_gbs": achieved,
+                      "note": f"algorithmic flops: 4 d per causal (query row, token) pair; the products run on "
+                              f"fp16 matrix cores with hi/lo operand splits (about 4x the algorithmic products); "
+                              f"the cache is read from memory once per workgroup of 8 row groups "
+                              f"({(vgroups + 7) // 8} per kv head here)"}
+                     if prefill else
+                     {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": DECODE_KERNEL,
+                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3, "tflops": tflops,
+                      "note": f"algorithmic bytes read the cache once; the kernel reads it once per "
+                              f"group of up to 8 query rows ({vgroups} here)"}),
         "_kernel": "decode_multi",
     }
     if not args.no_cpu_baseline:

@@ -139,12 +139,19 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
 MultiQueryShape multi_query_shape(int group, int n_q) {
   const long rows = (long)group * n_q;
   const int vgroups = (int)((rows + 7) / 8);
-  return MultiQueryShape{vgroups, (int)((rows + vgroups - 1) / vgroups)};
+  return MultiQueryShape{vgroups, (int)((rows + vgroups - 1) / vgroups), vgroups >= kPrefillMinGroups};
+}
+
+// Splits of a multi-query call: one work item per (batch, kv head, row group, split), or with
+// prefill one per (batch, kv head, 8 row groups, split).
+SplitPlan plan_multi(int batch, int n_kv_heads, const MultiQueryShape &m, int ctx_len) {
+  const int items = m.prefill ? (m.vgroups + 7) / 8 : m.vgroups;
+  return plan_fused(batch, n_kv_heads * items, ctx_len);
 }
 
 WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len) {
   const MultiQueryShape m = multi_query_shape(n_q_heads / n_kv_heads, n_q);
-  const SplitPlan fp = plan_fused(batch, n_kv_heads * m.vgroups, ctx_len);
+  const SplitPlan fp = plan_multi(batch, n_kv_heads, m, ctx_len);
   const size_t rows = (size_t)batch * n_q * n_q_heads * fp.n_splits;
   WorkspaceLayout w{};
   size_t off = 0;
@@ -598,7 +605,8 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
   a.n_q = n_q;
   a.vgroups = m.vgroups;
   a.vg_size = m.vg_size;
-  a.fplan = plan_fused(k->batch, k->n_kv_heads * m.vgroups, ctx_len);
+  a.prefill = m.prefill ? 1 : 0;
+  a.fplan = plan_multi(k->batch, k->n_kv_heads, m, ctx_len);
   a.out = out;
   a.lse = lse;
   char *ws = static_cast<char *>(workspace);

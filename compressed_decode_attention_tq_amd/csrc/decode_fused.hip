@@ -258,9 +258,17 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // The key pass without records needs only the key table and the score staging: its LDS is the
 // 64 KB table plus 2 KB per wave (80 KB).  (Two such workgroups per CU, 4 waves per SIMD at 128
 // VGPRs, made the pass slower: 22 -> 28 us on the 131072-token workload, with spills.)
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false, bool RECORDS = true>
+// PREFILL (with MULTI): several query positions with many row groups per kv head (a prefill
+// chunk).  The 8 waves of a workgroup take 8 row groups, not 8 slices of the tiles: every wave
+// walks all tiles of the split for its own rows, so the workgroup reads each tile of keys and
+// values from memory once for up to 64 query rows (the other waves find it in L2).  Each wave
+// keeps its own softmax, writes its own partials and merges its row group's splits when it is
+// the last to arrive; there is no combine across waves.
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false, bool RECORDS = true,
+          bool PREFILL = false>
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
+  static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !PAGED && !VMASK), "prefill: dense multi-query only");
   static_assert(!PAGED || !(SPARSE || MULTI), "paged caches: dense single-query decode");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND || PAGED), "masked value pass: dense decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
@@ -286,10 +294,13 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
 
   {  // one split of one (batch, kv head) per workgroup
     const int item = blockIdx.x;
+    const int VGB = PREFILL ? (VG + kWaves - 1) / kWaves : VG;  // items per (batch, kv head, split)
     const int split = item % S;
-    const int vgi = (item / S) % VG;
-    const int kvh = (item / (S * VG)) % a.n_kv_heads;
-    const int b = item / (S * VG * a.n_kv_heads);
+    const int vgb = (item / S) % VGB;
+    const int vgi = PREFILL ? vgb * kWaves + wave : vgb;  // PREFILL: each wave its own row group
+    const int kvh = (item / (S * VGB)) % a.n_kv_heads;
+    const int b = item / (S * VGB * a.n_kv_heads);
+    const bool wave_on = !PREFILL || vgi < VG;
     int T = a.ctx_len;
     if (a.seq_lens != nullptr) T = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.ctx_len));
     const int t_begin = split * L;
@@ -393,17 +404,21 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     for (int i = 0; i < (1 << BK); ++i) kcs[i] = a.k.centroids[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vcs[i] = a.v.centroids[i];
-    const size_t qbase = vrow(vlive(wave) ? wave : 0) * kD + 2 * lane;
+    // (PREFILL: each wave loads its own rows when it rotates them; a wave past the last row group
+    // has no row to read)
     uint32_t qw0 = 0u, qw1 = 0u;
-    if (a.q_dtype == TQ_F32) {
-      const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(a.q) + qbase);
-      qw0 = w.x;
-      qw1 = w.y;
-    } else {
-      qw0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qbase);
+    if constexpr (!PREFILL) {
+      const size_t qbase = vrow(vlive(wave) ? wave : 0) * kD + 2 * lane;
+      if (a.q_dtype == TQ_F32) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(a.q) + qbase);
+        qw0 = w.x;
+        qw1 = w.y;
+      } else {
+        qw0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qbase);
+      }
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
-    if (!defer_keys && !VMASK) load_keys(wave);
+    if (!defer_keys && !VMASK) load_keys(PREFILL ? 0 : wave);
     // VMASK: a split of at most 64 tiles is shared out by need (lane k looks at tile k); a longer
     // one (at most 64 tiles per wave) keeps the round-robin tiles (lane k: tile wave + 8 k), where
     // most tiles are needed anyway.  The maxima of those tiles for every head of the group are
@@ -434,19 +449,20 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     const int n_chunks = SPARSE ? a.fplan.split_len / a.plan.split_len : 0;
     if (SPARSE && RECORDS && (int)threadIdx.x < n_chunks) chunk_count[threadIdx.x] = 0;
 
-    // ---- rotated query group: wave h rotates head h into qrot[h]
-    if (wave < NH) {
+    // ---- rotated query group: wave h rotates head h into qrot[h] (PREFILL: every wave rotates
+    //      its own rows into its own buffer)
+    auto rotate_row = [&](bool live, uint32_t w0, uint32_t w1, float *dst) {
       float x0 = 0.f, x1 = 0.f;
-      if (vlive(wave)) {
+      if (live) {
         if (a.q_dtype == TQ_F32) {
-          x0 = __uint_as_float(qw0);
-          x1 = __uint_as_float(qw1);
+          x0 = __uint_as_float(w0);
+          x1 = __uint_as_float(w1);
         } else if (a.q_dtype == TQ_BF16) {
-          x0 = __uint_as_float(qw0 << 16);
-          x1 = __uint_as_float(qw0 & 0xffff0000u);
+          x0 = __uint_as_float(w0 << 16);
+          x1 = __uint_as_float(w0 & 0xffff0000u);
         } else {
-          x0 = f16((uint16_t)(qw0 & 0xffffu));
-          x1 = f16((uint16_t)(qw0 >> 16));
+          x0 = f16((uint16_t)(w0 & 0xffffu));
+          x1 = f16((uint16_t)(w0 >> 16));
         }
         if (sgn & 0x80u) x0 = -x0;
         if (sgn & 0x8000u) x1 = -x1;
@@ -456,7 +472,26 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       x1 = y1;
       wave_fwht_upper(x0, x1, lane);
       const float qs = a.scale * kInvSqrtD * kLog2e;
-      *reinterpret_cast<float2 *>(qrot + wave * kD + 2 * lane) = make_float2(x0 * qs, x1 * qs);
+      *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(x0 * qs, x1 * qs);
+    };
+    if constexpr (PREFILL) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        uint32_t w0 = 0u, w1 = 0u;
+        if (vlive(h)) {
+          const size_t qi = vrow(h) * kD + 2 * lane;
+          if (a.q_dtype == TQ_F32) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(a.q) + qi);
+            w0 = w.x;
+            w1 = w.y;
+          } else {
+            w0 = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.q) + qi);
+          }
+        }
+        rotate_row(vlive(h), w0, w1, reinterpret_cast<float *>(wbuf) + h * kD);
+      }
+    } else if (wave < NH) {
+      rotate_row(vlive(wave), qw0, qw1, qrot + wave * kD);
     }
     // VMASK, set-up only: [0, NH) thresholds on s (log2 units) = (LSE + ln tau) log2 e, [8, 8 + NH)
     // the LSE in log2 units (the fixed softmax reference of the pass)
@@ -514,7 +549,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       float v[32];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        float4 f = live ? *reinterpret_cast<const float4 *>(qrot + head * kD + 32 * quarter + 4 * r)
+        const float *qsrc = PREFILL ? reinterpret_cast<const float *>(wbuf) : qrot;
+        float4 f = live ? *reinterpret_cast<const float4 *>(qsrc + head * kD + 32 * quarter + 4 * r)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
         v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
       }
@@ -876,10 +912,122 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         }
         tile_body(tile, 0, std::false_type{});
       }
+    } else if constexpr (PREFILL) {  // every tile of the split, for this wave's rows
+      if (wave_on && n_tiles > 0) {
+        int tile = 0;
+        for (; tile + 1 < n_tiles; ++tile) tile_body(tile, tile + 1, std::true_type{});
+        tile_body(tile, 0, std::false_type{});
+      }
     } else {
       int tile = wave;
       for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, tile + kWaves, std::true_type{});
       if (tile < n_tiles) tile_body(tile, 0, std::false_type{});
+    }
+
+    // The last workgroup (PREFILL: the last wave) of a (batch, kv head, row group) merges the
+    // splits of row h: LSE merge of the partials, inverse rotation, output and LSE.
+    auto merge_row = [&](int h) {
+      // lane s of a chunk holds partial s's (m, l); every lane then sums its two
+      // coordinates over the partials, 16 loads in flight at a time
+      const size_t prow = vrow(h) * S;
+      const float2 *pml = a.fpart_ml + prow;
+      const float2 *pof = reinterpret_cast<const float2 *>(a.fpart_o + prow * kD) + lane;
+      float M = -INFINITY;
+      for (int s0 = 0; s0 < S; s0 += 64)
+        if (s0 + lane < S) M = fmaxf(M, load_coherent(pml + s0 + lane).x);
+      M = wave_reduce<true>(M);
+      float l = 0.f, o0 = 0.f, o1 = 0.f;
+      if (M != -INFINITY) {
+        for (int s0 = 0; s0 < S; s0 += 64) {
+          float w = 0.f;
+          if (s0 + lane < S) {
+            const float2 ml = load_coherent(pml + s0 + lane);
+            w = exp2_or_zero(ml.x, M);
+            l += ml.y * w;
+          }
+          const int n = min(64, S - s0);
+          for (int s = 0; s < n; s += 16) {
+            float2 o[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              o[u] = s + u < n ? load_coherent(pof + (size_t)(s0 + s + u) * (kD / 2)) : make_float2(0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+              o0 += o[u].x * wu;
+              o1 += o[u].y * wu;
+            }
+          }
+        }
+        l = wave_reduce<false>(l);
+        if constexpr (!VMASK) {  // (VMASK partials are final weights already)
+          o0 /= l;
+          o1 /= l;
+        }
+      }
+      // inverse rotation: x = s * (H y) / sqrt(128)
+      float y0 = o0 + o1, y1 = o0 - o1;
+      wave_fwht_upper(y0, y1, lane);
+      y0 *= kInvSqrtD;
+      y1 *= kInvSqrtD;
+      if (sgn & 0x80u) y0 = -y0;  // the sign bytes loaded at set-up
+      if (sgn & 0x8000u) y1 = -y1;
+      const size_t orow = vrow(h);
+      *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
+      if (lane == 0 && a.lse != nullptr)
+        a.lse[orow] = VMASK ? lse_own : M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
+      if (a.scores != nullptr) {
+        float *row = a.scores + orow * a.ctx_len;
+        for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;
+      }    };
+
+    if constexpr (PREFILL) {
+      // ---- this wave's rows alone: partials (m, l, O) per row, then its own arrival
+      float ltot[NH2];
+#pragma unroll
+      for (int hh = 0; hh < NH2; ++hh) ltot[hh] = half_sum(lsum[hh]);
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      if (NH == 8 || quarter < 2) {  // O rows [head][128] fp32 (hi and remainder rows summed)
+        const int h0 = 2 * quarter;
+        float *dst0 = reinterpret_cast<float *>(wbuf) + h0 * kD + 8 * m_row;
+        float *dst1 = dst0 + kD;
+        *reinterpret_cast<float4 *>(dst0) = make_float4(oacc[0][0] + oacc[0][1], oacc[1][0] + oacc[1][1],
+                                                        oacc[2][0] + oacc[2][1], oacc[3][0] + oacc[3][1]);
+        *reinterpret_cast<float4 *>(dst0 + 4) = make_float4(oacc[4][0] + oacc[4][1], oacc[5][0] + oacc[5][1],
+                                                            oacc[6][0] + oacc[6][1], oacc[7][0] + oacc[7][1]);
+        *reinterpret_cast<float4 *>(dst1) = make_float4(oacc[0][2] + oacc[0][3], oacc[1][2] + oacc[1][3],
+                                                        oacc[2][2] + oacc[2][3], oacc[3][2] + oacc[3][3]);
+        *reinterpret_cast<float4 *>(dst1 + 4) = make_float4(oacc[4][2] + oacc[4][3], oacc[5][2] + oacc[5][3],
+                                                            oacc[6][2] + oacc[6][3], oacc[7][2] + oacc[7][3]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      if (!wave_on) return;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        if (!vlive(h)) continue;
+        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr[h % NH2]), (h / NH2) * 32));
+        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ltot[h % NH2]), (h / NH2) * 32));
+        const size_t prow = vrow(h) * S + split;
+        const float2 o = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(wbuf) + h * kD + 2 * lane);
+        store_coherent(reinterpret_cast<float2 *>(a.fpart_o + prow * kD) + lane, o);
+        if (lane == 0) store_coherent(a.fpart_ml + prow, make_float2(mh, lh));
+      }
+      // arrival of this wave's row group; the ordering is the workgroup arrival's below, for one
+      // wave (its own vmcnt covers all of its partial stores)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      unsigned *counter = a.counters + ((size_t)b * a.n_kv_heads + kvh) * VG + vgi;
+      unsigned old = 0u;
+      if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old == (unsigned)(S - 1)) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          if (vlive(h)) merge_row(h);
+        if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
     }
 
     // ---- combine the 8 waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
@@ -983,81 +1131,32 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     const bool last = *flag != 0;
     if (last) {
       if (live_w) {
-        // lane s of a chunk holds partial s's (m, l); every lane then sums its two
-        // coordinates over the partials, 16 loads in flight at a time
-        const float2 *pml = a.fpart_ml + part_row;
-        const float2 *pof = reinterpret_cast<const float2 *>(a.fpart_o + part_row * kD) + lane;
-        float M = -INFINITY;
-        for (int s0 = 0; s0 < S; s0 += 64)
-          if (s0 + lane < S) M = fmaxf(M, load_coherent(pml + s0 + lane).x);
-        M = wave_reduce<true>(M);
-        float l = 0.f, o0 = 0.f, o1 = 0.f;
-        if (M != -INFINITY) {
-          for (int s0 = 0; s0 < S; s0 += 64) {
-            float w = 0.f;
-            if (s0 + lane < S) {
-              const float2 ml = load_coherent(pml + s0 + lane);
-              w = exp2_or_zero(ml.x, M);
-              l += ml.y * w;
-            }
-            const int n = min(64, S - s0);
-            for (int s = 0; s < n; s += 16) {
-              float2 o[16];
-#pragma unroll
-              for (int u = 0; u < 16; ++u)
-                o[u] = s + u < n ? load_coherent(pof + (size_t)(s0 + s + u) * (kD / 2)) : make_float2(0.f, 0.f);
-#pragma unroll
-              for (int u = 0; u < 16; ++u) {
-                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
-                o0 += o[u].x * wu;
-                o1 += o[u].y * wu;
-              }
-            }
-          }
-          l = wave_reduce<false>(l);
-          if constexpr (!VMASK) {  // (VMASK partials are final weights already)
-            o0 /= l;
-            o1 /= l;
-          }
-        }
-        // inverse rotation: x = s * (H y) / sqrt(128)
-        float y0 = o0 + o1, y1 = o0 - o1;
-        wave_fwht_upper(y0, y1, lane);
-        y0 *= kInvSqrtD;
-        y1 *= kInvSqrtD;
-        if (sgn & 0x80u) y0 = -y0;  // the sign bytes loaded at set-up
-        if (sgn & 0x8000u) y1 = -y1;
-        const size_t orow = vrow(wave);
-        *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
-        if (lane == 0 && a.lse != nullptr)
-          a.lse[orow] = VMASK ? lse_own : M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
-        if (a.scores != nullptr) {
-          float *row = a.scores + orow * a.ctx_len;
-          for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;
-        }
+        merge_row(wave);
       }
       if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS>
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS, bool PREFILL>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
-  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS>(a);
+  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL>(a);
 }
 
-template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true>
+template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true,
+          bool PREFILL = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
   if (a.vg_size <= 4) {
-    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS><<<grid, kThreads, 0, stream>>>(a);
+    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL><<<grid, kThreads, 0, stream>>>(a);
   } else {
-    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS><<<grid, kThreads, 0, stream>>>(a);
+    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL><<<grid, kThreads, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
 
 template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
+  if (!SPARSE && a.prefill) return launch_nh<BK, false, true, false, false, false, true, true>(a, grid, stream);
   if (!SPARSE && (a.n_q > 1 || a.vgroups > 1)) return launch_nh<BK, false, true, false>(a, grid, stream);
   if (!SPARSE && a.xk != nullptr) return launch_nh<BK, false, false, true>(a, grid, stream);
   return launch_nh<BK, SPARSE, false, false>(a, grid, stream);
@@ -1074,7 +1173,9 @@ bool decode_fused_supported(const DecodeArgs &a) { return decode_fused_shape_ok(
 
 hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream) {
   (void)n_cu;
-  const long items = (long)a.batch * a.n_kv_heads * a.vgroups * a.fplan.n_splits;
+  // prefill: one workgroup per 8 row groups (one per wave)
+  const long vg_items = a.prefill ? (a.vgroups + kWaves - 1) / kWaves : a.vgroups;
+  const long items = (long)a.batch * a.n_kv_heads * vg_items * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   const int grid = (int)items;
   return a.k.bits == 4 ? launch_bk<4, false>(a, grid, stream) : launch_bk<3, false>(a, grid, stream);

@@ -47,7 +47,9 @@ WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int c
 // partials only.
 struct MultiQueryShape {
   int vgroups, vg_size;
+  bool prefill;  // vgroups >= 8: row groups by wave (see DecodeArgs::prefill)
 };
+constexpr int kPrefillMinGroups = 8;
 MultiQueryShape multi_query_shape(int group, int n_q);
 WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len);
 
@@ -81,6 +83,9 @@ struct DecodeArgs {
   // Query rows of the single-launch kernel: n_q query positions per sequence (1 for decode)
   // give n_q * group rows per kv head, taken vg_size at a time by `vgroups` work items.
   int n_q, vgroups, vg_size;
+  // several query positions with at least 8 row groups per kv head (a prefill chunk): a
+  // workgroup's 8 waves take 8 row groups over the same split
+  int prefill;
   // Append in the same launch (single-query dense decode): the new token of each sequence,
   // [batch][1][n_kv_heads][d] of x_dtype, is quantized into position T - 1 first.
   const void *xk, *xv;

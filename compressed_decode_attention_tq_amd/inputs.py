@@ -97,6 +97,9 @@ WORKLOADS = {
     # speculative verification on the Llama-3-8B-shaped layer: 4 new positions per step
     "verify8k": Workload("verify8k", 6, 1, 32, 8, 8192, 4, 2, torch.bfloat16, "normal",
                          head_channel_scales=(0.5, 20.0), append=4, n_q=4),
+    # a prefill chunk on the Llama-3-8B-shaped layer: 512 new positions at the end of 8192
+    "chunk8k": Workload("chunk8k", 11, 1, 32, 8, 8192, 4, 2, torch.bfloat16, "normal",
+                        head_channel_scales=(0.5, 20.0), append=512, n_q=512),
     # the batched long-context shape in a paged cache: 256-token pages, shuffled in the pool
     "paged32k": Workload("paged32k", 7, 16, 32, 8, 32768, 3, 2, torch.bfloat16, "student5",
                          outlier_channels=8, outlier_scale=4.0, append=1, page_tokens=256),

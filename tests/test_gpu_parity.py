@@ -519,6 +519,11 @@ def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_len
     ("ctx131k", 2, 16, 2, 1500, 1536, 4, 5),
     ("llama8k", 1, 2, 2, 333, 384, 4, 8),
     ("llama8k", 1, 4, 4, 200, 256, 3, 64),
+    # prefill chunks (8 or more row groups of 8 rows per kv head: a workgroup's waves take
+    # different row groups over the same tiles)
+    ("llama8k", 1, 8, 2, 1400, 1408, 4, 256),
+    ("batch32k", 2, 16, 2, 900, 960, 3, 96),
+    ("ctx131k", 1, 16, 2, 700, 704, 4, 33),
 ])
 def test_multi_query_matches_oracle(case, signs, golden_codebooks):
     """Several query positions per sequence (speculative verification, chunked prefill):
@@ -537,6 +542,9 @@ def test_multi_query_ragged_lengths_and_dtypes(signs, golden_codebooks):
     _multi_case(w, signs, golden_codebooks, 2, 8, 2, 300, 320, 4, 3, seq_lens=[129, 300],
                 q_dtype=torch.float32)
     _multi_case(w, signs, golden_codebooks, 1, 16, 2, 260, 320, 3, 2, q_dtype=torch.float16)
+    # a prefill chunk longer than one sequence (its first queries see nothing) and an empty one
+    _multi_case(w, signs, golden_codebooks, 3, 8, 2, 700, 704, 4, 80, seq_lens=[700, 50, 0],
+                q_dtype=torch.float32)
 
 
 def test_decode_seq_lens_and_query_dtypes(signs, golden_codebooks):
