@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.tq_ip_search_workspace_bytes.restype = sz
         L.tq_paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.tq_paged_decode_workspace_bytes.restype = sz
+        L.tq_paged_decode_attn_ext.argtypes = [PP, PP, vp, i32, i32, i32, vp, i32, f32, f32, vp, vp, vp, sz, vp]
+        L.tq_paged_decode_ext_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, f32]
+        L.tq_paged_decode_ext_workspace_bytes.restype = sz
         L.tq_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.tq_code_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.tq_code_bytes.restype = sz
@@ -104,7 +107,7 @@ def lib() -> ctypes.CDLL:
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
                      "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
                      "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search",
-                     "tq_qjl_quantize_append", "tq_qjl_decode_attn"):
+                     "tq_qjl_quantize_append", "tq_qjl_decode_attn", "tq_paged_decode_attn_ext"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -548,6 +551,11 @@ def paged_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, ma
     return int(lib().tq_paged_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_ctx_len))
 
 
+def paged_decode_ext_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, n_q: int, max_ctx_len: int,
+                                     tau: float = 0.0) -> int:
+    return int(lib().tq_paged_decode_ext_workspace_bytes(batch, n_q_heads, n_kv_heads, n_q, max_ctx_len, tau))
+
+
 class PagedDecodeBuffers:
     """Caller-owned outputs and workspace of one paged decode problem shape."""
 
@@ -604,6 +612,47 @@ def paged_decode_attn_append(k_cache: PagedCache, v_cache: PagedCache, k_new, v_
         _dev(q, "q"), _dtype_code(q.dtype), hq, _dev(seq_lens, "seq_lens"), max_ctx_len, float(scale),
         _dev(buffers.out, "out"), _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn_append")
+    return buffers
+
+
+class PagedExtBuffers:
+    """Caller-owned outputs and workspace of tq_paged_decode_attn_ext: out [B, n_q, Hq, d] (or
+    [B, Hq, d] for one position), lse, and the workspace."""
+
+    def __init__(self, batch, n_q, n_q_heads, n_kv_heads, max_ctx_len, tau=0.0, device="cuda", d=D):
+        torch = _torch()
+        shape = (batch, n_q_heads) if n_q == 1 else (batch, n_q, n_q_heads)
+        self.out = torch.empty(shape + (d,), dtype=torch.float32, device=device)
+        self.lse = torch.empty(shape, dtype=torch.float32, device=device)
+        nbytes = paged_decode_ext_workspace_bytes(batch, n_q_heads, n_kv_heads, n_q, max_ctx_len, tau)
+        if nbytes == 0:
+            raise TQError(TQ_ERR_INVALID_ARG, "tq_paged_decode_ext_workspace_bytes")
+        # zero once: the arrival counters live here and every call leaves them at zero
+        self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.ws_bytes = nbytes
+
+
+def paged_decode_attn_ext(k_cache: PagedCache, v_cache: PagedCache, q, seq_lens, max_ctx_len: int, scale: float,
+                          tau: float = 0.0, buffers: PagedExtBuffers | None = None, stream=None):
+    """Paged attention of several query positions (q [B, n_q, Hq, d], causal) or Sparse V with one
+    position (q [B, Hq, d], tau > 0); returns the PagedExtBuffers (out, lse)."""
+    _check_query(q, k_cache, 3 if q.dim() == 3 else 4, "paged_decode_attn_ext")
+    if q.dim() == 3:
+        (bsz, hq, d), n_q = q.shape, 1
+    else:
+        bsz, n_q, hq, d = q.shape
+    _check_seq_lens(seq_lens, bsz, "paged_decode_attn_ext", required=True)
+    if buffers is None:
+        buffers = PagedExtBuffers(bsz, n_q, hq, k_cache.n_kv_heads, max_ctx_len, tau, device=q.device, d=d)
+    shape = (bsz, hq) if n_q == 1 else (bsz, n_q, hq)
+    _check_outputs(buffers, shape + (d,), shape, "paged_decode_attn_ext")
+    ks, vs = k_cache.struct(), v_cache.struct()
+    _check(lib().tq_paged_decode_attn_ext(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(q, "q"), _dtype_code(q.dtype), hq, n_q, _dev(seq_lens, "seq_lens"),
+        max_ctx_len, float(scale), float(tau), _dev(buffers.out, "out"), _dev(buffers.lse, "lse"),
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_paged_decode_attn_ext")
     return buffers
 
 

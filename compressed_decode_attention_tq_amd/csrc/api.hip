@@ -200,6 +200,41 @@ WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads,
   return w;
 }
 
+WorkspaceLayout workspace_layout_paged_ext(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len,
+                                          bool sparse) {
+  WorkspaceLayout w{};
+  size_t off = 0;
+  w.counters = off;
+  if (!sparse) {  // several query positions: one row group per work item (no prefill mode over pages)
+    MultiQueryShape m = multi_query_shape(n_q_heads / n_kv_heads, n_q);
+    m.prefill = false;
+    SplitPlan fp = plan_multi(batch, n_kv_heads, m, ctx_len);
+    if (fp.split_len > kPagedMaxSplit) fp = SplitPlan{(ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit, kPagedMaxSplit};
+    const size_t rows = (size_t)batch * n_q * n_q_heads * fp.n_splits;
+    off = align_up(off + (size_t)batch * n_kv_heads * m.vgroups * sizeof(unsigned), 256);
+    w.fpart_ml = off;
+    off = align_up(off + rows * sizeof(float2), 256);
+    w.fpart_o = off;
+    off = align_up(off + rows * kD * sizeof(float), 256);
+    w.part_ml = w.part_o = w.cand_count = w.cand = w.vpart_ml = w.vpart_o = w.tile_max = off;
+  } else {  // Sparse V: the key pass's (m, l) partials, the value pass's partials, the tile maxima
+    const SplitPlan kp = plan_fused_paged(batch, n_kv_heads, ctx_len);
+    const SplitPlan vp = plan_fused_vmask(batch, n_kv_heads, ctx_len);
+    off = align_up(off + (size_t)batch * n_kv_heads * sizeof(unsigned), 256);
+    w.fpart_ml = off;
+    off = align_up(off + (size_t)batch * n_q_heads * kp.n_splits * sizeof(float2), 256);
+    w.fpart_o = w.part_ml = w.part_o = w.cand_count = w.cand = off;
+    w.vpart_ml = off;
+    off = align_up(off + (size_t)batch * n_q_heads * vp.n_splits * sizeof(float2), 256);
+    w.vpart_o = off;
+    off = align_up(off + (size_t)batch * n_q_heads * vp.n_splits * kD * sizeof(float), 256);
+    w.tile_max = off;
+    off = align_up(off + (size_t)batch * n_q_heads * ((ctx_len + 63) / 64) * sizeof(float), 256);
+  }
+  w.total = off;
+  return w;
+}
+
 struct SearchLayout {
   size_t cand_s0, cand_i0, cand_s1, cand_i1, total;
 };
@@ -705,6 +740,93 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
     return TQ_ERR_INVALID_ARG;
   return paged_decode(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, max_ctx_len, scale, out, lse,
                       workspace, workspace_bytes, hip_stream);
+}
+
+size_t tq_paged_decode_ext_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q, int max_ctx_len,
+                                           float sparse_v_tau) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads != 0 || max_ctx_len < 0 ||
+      n_q < 1 || n_q > kMaxQueryPositions || !(sparse_v_tau >= 0.f && sparse_v_tau < 1.f) ||
+      (sparse_v_tau > 0.f && n_q != 1))
+    return 0;
+  return workspace_layout_paged_ext(batch, n_q_heads, n_kv_heads, n_q, max_ctx_len, sparse_v_tau > 0.f).total;
+}
+
+int tq_paged_decode_attn_ext(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
+                             int n_q_heads, int n_q, const int32_t *seq_lens, int max_ctx_len, float scale,
+                             float sparse_v_tau, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  const int st = check_paged_pair(k, v);
+  if (st != TQ_OK) return st;
+  if (k->signs != v->signs) return TQ_ERR_INVALID_ARG;
+  if (q == nullptr || !aligned(q, 16) || !valid_dtype(q_dtype)) return TQ_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return TQ_ERR_INVALID_ARG;
+  if (seq_lens == nullptr || !aligned(seq_lens, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  if (n_q < 1 || n_q > kMaxQueryPositions) return TQ_ERR_INVALID_ARG;
+  if (max_ctx_len < 0 || !std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  if (!(sparse_v_tau >= 0.f && sparse_v_tau < 1.f)) return TQ_ERR_INVALID_ARG;
+  if ((long)max_ctx_len > (long)k->max_pages * k->page_tokens) return TQ_ERR_CAPACITY;
+  const int group = n_q_heads / k->n_kv_heads;
+  const bool sparse = sparse_v_tau > 0.f;
+  if (group > 8 || (k->bits != 3 && k->bits != 4) || v->bits != 2 || (sparse && n_q != 1)) return TQ_ERR_UNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout_paged_ext(k->batch, n_q_heads, k->n_kv_heads, n_q, max_ctx_len, sparse);
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+
+  DecodeArgs a{};
+  a.k = view_of_pool(k);
+  a.v = view_of_pool(v);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = k->n_kv_heads;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.ctx_len = max_ctx_len;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  char *ws = static_cast<char *>(workspace);
+  a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
+  a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
+  a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
+  a.block_table = k->block_table;
+  a.max_pages = k->max_pages;
+  a.n_pages = k->n_pages;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (!sparse) {
+    MultiQueryShape m = multi_query_shape(group, n_q);
+    m.prefill = false;
+    a.n_q = n_q;
+    a.vgroups = m.vgroups;
+    a.vg_size = m.vg_size;
+    a.fplan = plan_multi(k->batch, k->n_kv_heads, m, max_ctx_len);
+    if (a.fplan.split_len > kPagedMaxSplit)
+      a.fplan = SplitPlan{(max_ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit, kPagedMaxSplit};
+    a.plan = a.fplan;
+    return hip_status(launch_decode_fused_paged(a, stream));
+  }
+  // Sparse V: key pass (LSE partials and tile maxima), then the masked value pass
+  a.n_q = 1;
+  a.vgroups = 1;
+  a.vg_size = group;
+  a.sparse = 1;
+  a.ln_tau = std::log(sparse_v_tau);
+  a.fplan = plan_fused_paged(k->batch, k->n_kv_heads, max_ctx_len);
+  a.plan = a.fplan;
+  a.tile_max = reinterpret_cast<float *>(ws + w.tile_max);
+  a.tile_stride = (max_ctx_len + 63) / 64;
+  DecodeArgs vp = a;
+  vp.sparse = 0;
+  vp.lse_ml = a.fpart_ml;
+  vp.lse_splits = a.fplan.n_splits;
+  vp.fplan = plan_fused_vmask(k->batch, k->n_kv_heads, max_ctx_len);
+  vp.plan = vp.fplan;
+  vp.fpart_ml = reinterpret_cast<float2 *>(ws + w.vpart_ml);
+  vp.fpart_o = reinterpret_cast<float *>(ws + w.vpart_o);
+  return hip_status(launch_decode_fused_paged_sparse(a, vp, stream));
 }
 
 size_t tq_ip_search_workspace_bytes(int n_queries, int n_vectors, int top_k) {

@@ -269,8 +269,9 @@ template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !PAGED && !VMASK), "prefill: dense multi-query only");
-  static_assert(!PAGED || !(SPARSE || MULTI), "paged caches: dense single-query decode");
-  static_assert(!VMASK || !(SPARSE || MULTI || APPEND || PAGED), "masked value pass: dense decode");
+  static_assert(!PAGED || !(PREFILL || (SPARSE && RECORDS) || (MULTI && APPEND)),
+                "paged caches: decode, its append, several query positions, Sparse V's two passes");
+  static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
@@ -331,9 +332,12 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     const __amdgpu_buffer_rsrc_t vnrs =
         PAGED ? make_rsrc(a.v.norms, span_tok * 2) : make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
     constexpr uint32_t kNoPage = 0xffffffffu;
-    uint32_t page_tok = kNoPage;  // paged: lane i holds tile_tok of the wave's tile wave + 8 i
+    // A value-pass split of at most 64 tiles is shared out by need (lane k: tile k, see VMASK
+    // below); every other split keeps the round-robin tiles (lane i: tile wave + 8 i).
+    const bool by_need = VMASK && n_tiles <= 64;
+    uint32_t page_tok = kNoPage;  // paged: lane i holds tile_tok of its tile in the mapping above
     if constexpr (PAGED) {
-      const int tile_i = wave + kWaves * lane;
+      const int tile_i = by_need ? lane : wave + kWaves * lane;
       if (tile_i < n_tiles) {
         const int P = a.k.capacity, t0 = t_begin + tile_i * kTile, slot = t0 / P;
         const int page = slot < a.max_pages ? a.block_table[(size_t)b * a.max_pages + slot] : -1;
@@ -341,7 +345,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       }
     }
     auto tile_tok = [&](int tile) -> uint32_t {
-      if constexpr (PAGED) return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, (tile - wave) / kWaves);
+      if constexpr (PAGED)
+        return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, by_need ? tile : (tile - wave) / kWaves);
       else return (uint32_t)tile * kTile;
     };
     auto tile_off = [&](uint32_t tok, uint32_t unit) -> uint32_t {  // bytes; past the end for no page
@@ -423,7 +428,6 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // one (at most 64 tiles per wave) keeps the round-robin tiles (lane k: tile wave + 8 k), where
     // most tiles are needed anyway.  The maxima of those tiles for every head of the group are
     // loaded now, so that only the comparison waits for the thresholds.
-    const bool by_need = n_tiles <= 64;
     float tmx[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) tmx[h] = -INFINITY;
@@ -1190,8 +1194,15 @@ bool decode_fused_sparse_supported(const DecodeArgs &a) {
 
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
   if (a.block_table == nullptr || a.seq_lens == nullptr || a.fplan.split_len > kPagedMaxSplit ||
-      a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity || !decode_fused_supported(a))
+      a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity || !decode_fused_supported(a) || a.prefill)
     return hipErrorInvalidValue;
+  if (a.n_q > 1 || a.vgroups > 1) {  // several query positions (one row group per work item)
+    if (a.xk != nullptr) return hipErrorInvalidValue;
+    const long items = (long)a.batch * a.n_kv_heads * a.vgroups * a.fplan.n_splits;
+    if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+    return a.k.bits == 4 ? launch_nh<4, false, true, false, true>(a, (int)items, stream)
+                         : launch_nh<3, false, true, false, true>(a, (int)items, stream);
+  }
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   if (a.xk != nullptr)  // append the new token in the same launch
@@ -1199,6 +1210,26 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
                          : launch_nh<3, false, false, true, true>(a, (int)items, stream);
   return a.k.bits == 4 ? launch_nh<4, false, false, false, true>(a, (int)items, stream)
                        : launch_nh<3, false, false, false, true>(a, (int)items, stream);
+}
+
+// Sparse V over paged caches: the key pass without records, then the masked value pass, both
+// reading the pages through the block table (splits of at most kPagedMaxSplit tokens).
+hipError_t launch_decode_fused_paged_sparse(const DecodeArgs &key_pass, const DecodeArgs &value_pass,
+                                            hipStream_t stream) {
+  const DecodeArgs &a = key_pass, &v = value_pass;
+  if (a.block_table == nullptr || a.seq_lens == nullptr || a.fplan.split_len > kPagedMaxSplit ||
+      v.fplan.split_len > kVmaskMaxSplit || a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity ||
+      (a.k.bits != 3 && a.k.bits != 4) || a.v.bits != 2 || a.vg_size > 8 || a.tile_max == nullptr ||
+      v.lse_ml == nullptr || v.counters == nullptr)
+    return hipErrorInvalidValue;
+  const long items_k = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  const long items_v = (long)v.batch * v.n_kv_heads * v.fplan.n_splits;
+  if (items_k < 1 || items_k > 0x7fffffffL || items_v < 1 || items_v > 0x7fffffffL) return hipErrorInvalidValue;
+  hipError_t e = a.k.bits == 4 ? launch_nh<4, true, false, false, true, false, false>(a, (int)items_k, stream)
+                               : launch_nh<3, true, false, false, true, false, false>(a, (int)items_k, stream);
+  if (e != hipSuccess) return e;
+  return v.k.bits == 4 ? launch_nh<4, false, false, false, true, true>(v, (int)items_v, stream)
+                       : launch_nh<3, false, false, false, true, true>(v, (int)items_v, stream);
 }
 
 hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {

@@ -154,6 +154,11 @@ constexpr int kVmaskMaxSplit = 8 * 64 * 64;
 SplitPlan plan_fused_vmask(int batch, int n_kv_heads, int ctx_len);
 WorkspaceLayout workspace_layout_paged(int batch, int n_q_heads, int n_kv_heads, int ctx_len);
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_fused_paged_sparse(const DecodeArgs &key_pass, const DecodeArgs &value_pass,
+                                            hipStream_t stream);
+// Workspace of the paged calls with several query positions or Sparse V (tau > 0).
+WorkspaceLayout workspace_layout_paged_ext(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len, bool sparse);
+SplitPlan plan_multi(int batch, int n_kv_heads, const MultiQueryShape &m, int ctx_len);
 // Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
 // db, 3- or 4-bit rows), then the k best per query.  Two candidate buffers (ping-pong for the
 // merge levels), each [n_q][ceil(n / kSearchBlock) * k] score + index, are caller scratch.

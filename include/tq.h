@@ -363,6 +363,31 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
                                 int max_ctx_len, float scale, float *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *hip_stream);
 
+/* Paged caches, several query positions or Sparse V: tq_paged_decode_attn extended as
+ *   n_q > 1 (sparse_v_tau = 0): the attention of tq_decode_attn_multi ([google] score kernel;
+ *     [inferrs] on prefill speed) over paged caches: with T_b = clamp(seq_lens[b], 0,
+ *     max_ctx_len), query i of sequence b sits at position T_b - n_q + i and attends causally;
+ *     q [batch][n_q][n_q_heads][d], out [batch][n_q][n_q_heads][d], lse [batch][n_q][n_q_heads];
+ *   n_q = 1, sparse_v_tau in (0, 1): the Sparse V rule of tq_decode_attn ([inferrs] §Sparse V;
+ *     keep_t = exp(s_t - LSE) >= tau, no renormalisation) over paged caches;
+ *   n_q = 1, sparse_v_tau = 0: tq_paged_decode_attn.
+ * Positions on a "no page" entry leave the softmax (see tq_paged_cache).  Keys of 3 or 4 bits,
+ * values of 2 bits, n_q_heads / n_kv_heads <= 8, 1 <= n_q <= 4096; Sparse V with n_q = 1 only
+ * (TQ_ERR_UNSUPPORTED otherwise).  Equal codes give the outputs of the contiguous calls for
+ * sequences without holes.
+ *   workspace  tq_paged_decode_ext_workspace_bytes(...) bytes, 256-byte aligned, zero-filled once
+ *              before first use (arrival counters every completed call leaves at zero); calls
+ *              sharing it must not overlap in time.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_paged_decode_attn_ext(const tq_paged_cache *k, const tq_paged_cache *v, const void *q, int q_dtype,
+                             int n_q_heads, int n_q, const int32_t *seq_lens, int max_ctx_len, float scale,
+                             float sparse_v_tau, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/* Workspace bytes tq_paged_decode_attn_ext needs (0 for invalid arguments). */
+size_t tq_paged_decode_ext_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q, int max_ctx_len,
+                                           float sparse_v_tau);
+
 /* Approximate inner-product nearest-neighbour search with the same quantizer ([tq-80]
  * §技术背景与学术渊源): the database is plane (batch 0, kv head 0) of `db` (batch = 1,
  * n_kv_heads = 1, ROWS layout, 3- or 4-bit codes, vectors 0 .. n_vectors - 1 quantized by

@@ -381,7 +381,7 @@ def decode_attention(q, k_hat, v_hat, scale: float, seq_lens=None, tau: float = 
     return out, lse, scores
 
 
-def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None):
+def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None, valid=None):
     """Attention of n_q new query positions per sequence over a dequantized cache that
     already holds them (speculative verify, chunked prefill): the step after single-query
     decode, scored against the same quantized keys ([google], the scoring kernel;
@@ -392,6 +392,9 @@ def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None):
     T_b - n_q + i and attends causally to positions 0 .. T_b - n_q + i:
       s_t = scale * q . k_hat_t,  LSE = log sum_t exp(s_t),  o = sum_t exp(s_t - LSE) v_hat_t.
     A query with no position to attend to (T_b - n_q + i < 0) gives o = 0, LSE = -inf.
+    valid: optional bool [B, T]; positions with valid[b, t] False are not part of the sequence
+    (a paged cache's positions on a table entry of no page, as in `decode_attention`) and are
+    left out of every query's softmax.
     Returns (out [B, n_q, Hq, d], lse [B, n_q, Hq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -408,12 +411,15 @@ def multi_query_attention(q, k_hat, v_hat, scale: float, seq_lens=None):
             n_vis = tb - n_q + i + 1  # positions 0 .. tb - n_q + i
             if n_vis <= 0:
                 continue
+            pos = np.arange(n_vis) if valid is None else np.nonzero(np.asarray(valid[b][:n_vis], dtype=bool))[0]
+            if pos.size == 0:
+                continue
             for h in range(hq):
                 j = h // g
-                s = scale * (kh[b, j, :n_vis] @ q[b, i, h])
+                s = scale * (kh[b, j, pos] @ q[b, i, h])
                 m = s.max()
                 l_ = m + math.log(np.exp(s - m).sum())
-                out[b, i, h] = (np.exp(s - l_)[:, None] * vh[b, j, :n_vis]).sum(axis=0)
+                out[b, i, h] = (np.exp(s - l_)[:, None] * vh[b, j, pos]).sum(axis=0)
                 lse[b, i, h] = l_
     return out, lse
 

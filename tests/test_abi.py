@@ -322,6 +322,42 @@ def test_paged_argument_validation():
     assert dec_app(wsb=16) == tq.TQ_ERR_WORKSPACE
 
 
+def test_paged_ext_argument_validation():
+    """tq_paged_decode_attn_ext: several positions or Sparse V (not both), the same page,
+    width and workspace rules as the paged decode."""
+    L = tq.lib()
+    k, v = _paged(), _paged(layout=1, bits=2, codes=FAKE + 0x2000000, norms=FAKE + 0x3000000)
+    sp = FAKE + 0x900000
+    ws_multi = tq.paged_decode_ext_workspace_bytes(2, 16, 2, 4, 4096)
+    ws_sparse = tq.paged_decode_ext_workspace_bytes(2, 16, 2, 1, 4096, 1e-4)
+    assert ws_multi > 0 and ws_sparse > 0
+    assert tq.paged_decode_ext_workspace_bytes(2, 16, 2, 4, 4096, 1e-4) == 0   # not both
+    assert tq.paged_decode_ext_workspace_bytes(2, 16, 2, 0, 4096) == 0
+    assert tq.paged_decode_ext_workspace_bytes(2, 16, 2, 1, 4096, 1.0) == 0
+    assert tq.paged_decode_ext_workspace_bytes(2, 15, 2, 1, 4096) == 0
+
+    def ext(k=k, v=v, hq=16, n_q=4, seq=sp, ctx=4096, tau=0.0, wsb=ws_multi, ws=FAKE + 0x800000, q=FAKE + 0x600000):
+        return L.tq_paged_decode_attn_ext(ctypes.byref(k), ctypes.byref(v), q, 1, hq, n_q, seq, ctx, 0.088, tau,
+                                          FAKE + 0x700000, None, ws, wsb, None)
+
+    assert ext(seq=0) == tq.TQ_ERR_INVALID_ARG                          # lengths are required
+    assert ext(ctx=4097) == tq.TQ_ERR_CAPACITY                          # 16 pages of 256
+    assert ext(n_q=0) == tq.TQ_ERR_INVALID_ARG
+    assert ext(n_q=1 << 20) == tq.TQ_ERR_INVALID_ARG
+    assert ext(hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert ext(hq=64) == tq.TQ_ERR_UNSUPPORTED                          # group 32
+    assert ext(tau=1e-4) == tq.TQ_ERR_UNSUPPORTED                       # Sparse V takes one position
+    assert ext(n_q=1, tau=1.0) == tq.TQ_ERR_INVALID_ARG
+    assert ext(n_q=1, tau=float("nan")) == tq.TQ_ERR_INVALID_ARG
+    assert ext(n_q=1, tau=1e-4, wsb=ws_sparse - 1) == tq.TQ_ERR_WORKSPACE
+    assert ext(wsb=ws_multi - 1) == tq.TQ_ERR_WORKSPACE
+    assert ext(ws=FAKE + 0x800010) == tq.TQ_ERR_INVALID_ARG             # not 256-aligned
+    assert ext(q=FAKE + 0x600002) == tq.TQ_ERR_INVALID_ARG
+    assert ext(k=_paged(bits=8)) == tq.TQ_ERR_UNSUPPORTED
+    assert ext(v=_paged(layout=1, bits=3)) == tq.TQ_ERR_UNSUPPORTED
+    assert ext(v=k) == tq.TQ_ERR_INVALID_ARG                            # layouts
+
+
 def test_ip_search_argument_validation():
     L = tq.lib()
     db = _cache(batch=1, n_kv_heads=1, capacity=65536)

@@ -362,6 +362,34 @@ def test_decode_append_matches_oracle(case, signs, golden_codebooks):
     _append_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape, x_dtype=xdt)
 
 
+def _gather_pages(kc, vc, table, signs, max_ctx):
+    """The contiguous copy of paged caches (slot p of sequence b = pool page table[b, p]) and
+    the mask of positions that lie on a page of the table."""
+    batch, max_pages = table.shape
+    page, hkv = kc.page_tokens, kc.n_kv_heads
+    cap = max_pages * page
+    kf = _new_cache(batch, hkv, cap, kc.bits, 0, signs)
+    vf = _new_cache(batch, hkv, cap, vc.bits, 1, signs)
+    for pc, fc in ((kc, kf), (vc, vf)):
+        per = page * 16 * pc.bits
+        for b in range(batch):
+            for h in range(hkv):
+                dst, dn = fc.plane_codes(b, h), fc.plane_norms(b, h)
+                for slot in range(max_pages):
+                    pg = int(table[b, slot])
+                    if pg < 0:
+                        continue
+                    dst[slot * per:(slot + 1) * per] = pc.page_codes(pg, h)
+                    dn[slot * page:(slot + 1) * page] = pc.page_norms(pg, h)
+    torch.cuda.synchronize()
+    valid = np.ones((batch, max_ctx), dtype=bool)
+    for b in range(batch):
+        for slot in range(max_pages):
+            if int(table[b, slot]) < 0:
+                valid[b, slot * page:(slot + 1) * page] = False
+    return kf, vf, valid
+
+
 def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtype=None, hole=None, seed=0,
                 fused=False):
     """Paged caches with shuffled pages (and optionally table entries of no page) filled by
@@ -413,29 +441,9 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
         tq.paged_quantize_append_kv(kc, vc, k1.to(DEV), v1.to(DEV), last.to(DEV))
         got = tq.paged_decode_attn(kc, vc, q, sl, max_ctx, scale)
     torch.cuda.synchronize()
-    # the gathered contiguous copy: slot p of sequence b = page table[b, p]
-    cap = max_pages * page
-    kf = _new_cache(batch, hkv, cap, bits_k, 0, signs)
-    vf = _new_cache(batch, hkv, cap, 2, 1, signs)
-    for pc, fc in ((kc, kf), (vc, vf)):
-        per = page * 16 * pc.bits
-        for b in range(batch):
-            for h in range(hkv):
-                dst, dn = fc.plane_codes(b, h), fc.plane_norms(b, h)
-                for slot in range(max_pages):
-                    pg = int(table[b, slot])
-                    if pg < 0:
-                        continue
-                    dst[slot * per:(slot + 1) * per] = pc.page_codes(pg, h)
-                    dn[slot * page:(slot + 1) * page] = pc.page_norms(pg, h)
-    torch.cuda.synchronize()
+    kf, vf, valid = _gather_pages(kc, vc, table, signs, max_ctx)
     s64 = signs.numpy().astype(np.float64)
     lens = list(seq_lens)
-    valid = np.ones((batch, max_ctx), dtype=bool)     # positions on a page of the table
-    for b in range(batch):
-        for slot in range(max_pages):
-            if int(table[b, slot]) < 0:
-                valid[b, slot * page:(slot + 1) * page] = False
     for fc, x, table_b in ((kf, k, golden[bits_k]), (vf, v, golden[2])):
         for b in range(batch):
             # each run of positions on allocated pages holds the oracle's codes (the appends
@@ -480,6 +488,91 @@ def test_paged_cache_matches_contiguous_and_oracle(case, signs, golden_codebooks
     xdt = {None: None, "f32": torch.float32, "f16": torch.float16}[xdt]
     _paged_case(inputs.WORKLOADS[name], signs, golden_codebooks, batch, hq, hkv, page, lens, bk, x_dtype=xdt, hole=hole,
                 fused=fused)
+
+
+def _paged_ext_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, n_q=1, tau=0.0, holes=(), seed=0,
+                    q_dtype=None):
+    """Paged attention of several query positions, or paged Sparse V, through
+    tq_paged_decode_attn_ext: shuffled pages (some table entries naming no page) filled by the
+    paged append; the result must equal the oracle on the gathered cache with the positions of
+    no page left out (multi_query_attention / decode_attention with tau), and, for several
+    positions, the contiguous multi-query call on the gathered cache bit for bit on every
+    sequence without a hole whenever both calls split the context alike."""
+    max_ctx = max(seq_lens)
+    max_pages = (max_ctx + page - 1) // page + 1
+    n_pages = batch * max_pages + 3
+    rng = np.random.default_rng(seed)
+    table = torch.tensor(rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages), dtype=torch.int32)
+    for hb, hs in holes:
+        table[hb, hs] = -1
+    kc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, bits_k, 0, signs.to(DEV),
+                       block_table=table.to(DEV).contiguous(), device=DEV)
+    vc = tq.PagedCache(batch, hkv, page, n_pages, max_pages, 2, 1, kc.signs, block_table=kc.block_table, device=DEV)
+    for c in (kc, vc):
+        c.codes.fill_(0xA5)
+        c.norms.fill_(0x3C00)
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=max_ctx, n_kv_heads=hkv, n_q_heads=hq, n_q=n_q)
+    zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
+    tq.paged_quantize_append_kv(kc, vc, g["k"].contiguous().to(DEV), g["v"].contiguous().to(DEV), zeros)
+    q = g["q"] if q_dtype is None else g["q"].to(q_dtype)
+    qd = q.to(DEV).contiguous()
+    sl = torch.tensor(list(seq_lens), dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    got = tq.paged_decode_attn_ext(kc, vc, qd, sl, max_ctx, scale, tau=tau)
+    torch.cuda.synchronize()
+    kf, vf, valid = _gather_pages(kc, vc, table, signs, max_ctx)
+    s64 = signs.numpy().astype(np.float64)
+    lens = list(seq_lens)
+    kh = parity.oracle_cache_view(kf, s64, golden[bits_k], max_ctx)
+    vh = parity.oracle_cache_view(vf, s64, golden[2], max_ctx)
+    whole = [b for b in range(batch) if valid[b, :max(lens[b], 0)].all()]
+    allowance, nb = None, 0
+    if n_q > 1:
+        vgroups = -(-(hq // hkv) * n_q // 8)
+        if vgroups < 8:  # the contiguous call takes the same splits (no prefill mode)
+            ref = tq.decode_attn_multi(kf, vf, qd, max_ctx, scale, seq_lens=sl)
+            torch.cuda.synchronize()
+            assert torch.equal(got.out[whole], ref.out[whole]) and torch.equal(got.lse[whole], ref.lse[whole])
+        out, lse = o.multi_query_attention(parity.to_f64(q), kh, vh, scale, seq_lens=lens, valid=valid)
+    else:
+        out, lse, scores = o.decode_attention(parity.to_f64(q), kh, vh, scale, seq_lens=lens, tau=tau, valid=valid)
+        if tau > 0:
+            allowance, nb = parity.sparse_allowance(scores, lse, vh, tau, hq // hkv)
+    fin = np.isfinite(lse)
+    got_lse = got.lse.cpu().numpy()
+    got_out = got.out.cpu().numpy()
+    assert np.all(np.isneginf(got_lse[~fin])) and np.all(got_out[~fin] == 0.0)
+    assert np.allclose(got_lse[fin], lse[fin], rtol=0, atol=1e-3 * np.maximum(1, np.abs(lse[fin])))
+    worst = parity.check_rows(got_out, out, "paged ext out", allowance=allowance)
+    _say(f"  worst rel err {worst:.2e} borderline {nb}")
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, page tokens, seq_lens, bits_k, n_q, tau, holes)
+    ("llama8k", 3, 32, 8, 64, [700, 5, 333], 4, 4, 0.0, [(0, 5)]),
+    ("batch32k", 2, 8, 2, 256, [1300, 1024], 3, 7, 0.0, []),
+    ("ctx131k", 2, 16, 2, 128, [1500, 0], 4, 3, 0.0, [(0, 0), (0, 11)]),
+    # a chunk of 96 positions (12 row groups per kv head) whose last page is missing
+    ("llama8k", 1, 8, 2, 64, [1400], 4, 96, 0.0, [(0, 21)]),
+    ("llama8k", 2, 16, 4, 64, [300, 450], 3, 2, 0.0, [(0, s) for s in range(5)] + [(1, 1)]),
+    # Sparse V over pages
+    ("ctx131k", 2, 16, 2, 128, [1500, 900], 4, 1, 1e-4, []),
+    ("batch32k", 2, 8, 2, 256, [1300, 513], 3, 1, 1e-3, [(1, 1)]),
+    ("llama8k", 3, 16, 4, 64, [300, 450, 129], 4, 1, 1e-2, [(0, s) for s in range(6)] + [(1, 1), (1, 6)]),
+    ("ctx131k", 1, 16, 2, 64, [4000], 4, 1, 1e-3, [(0, 3), (0, 40)]),
+])
+def test_paged_multi_query_and_sparse_v(case, signs, golden_codebooks):
+    name, batch, hq, hkv, page, lens, bk, n_q, tau, holes = case
+    _say("paged ext", case)
+    _paged_ext_case(inputs.WORKLOADS[name], signs, golden_codebooks, batch, hq, hkv, page, lens, bk, n_q=n_q,
+                    tau=tau, holes=holes)
+
+
+def test_paged_ext_query_dtypes(signs, golden_codebooks):
+    _say("paged ext dtypes")
+    w = inputs.WORKLOADS["llama8k"]
+    _paged_ext_case(w, signs, golden_codebooks, 2, 8, 2, 64, [640, 200], 4, n_q=3, q_dtype=torch.float32)
+    _paged_ext_case(w, signs, golden_codebooks, 2, 8, 2, 64, [640, 200], 4, tau=1e-3, q_dtype=torch.float16)
 
 
 def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens=None, q_dtype=None):

@@ -402,6 +402,32 @@ def test_attention_excluded_positions_equal_removed_positions(golden_codebooks):
     assert np.allclose(part[0], ref0[0], rtol=1e-13, atol=1e-15) and np.allclose(plse[0], rl0[0])
 
 
+def test_multi_query_excluded_positions_equal_decode_over_prefix(golden_codebooks):
+    """Several query positions with positions left out (paged holes): query i equals
+    single-query decode over its own prefix with the same positions left out."""
+    s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=120, golden=golden_codebooks)
+    scale = 1 / math.sqrt(D)
+    bsz, T = kh.shape[0], kh.shape[2]
+    n_q = 6
+    rng = np.random.default_rng(5)
+    qm = rng.standard_normal((bsz, n_q, q.shape[1], D))
+    valid = np.ones((bsz, T), dtype=bool)
+    valid[0, 10:40] = False
+    valid[1, 100:] = False                         # the last positions, some queries' own
+    out, lse = o.multi_query_attention(qm, kh, vh, scale, valid=valid)
+    for b in range(bsz):
+        for i in range(n_q):
+            n_vis = T - n_q + i + 1
+            ref, rl, _ = o.decode_attention(qm[b:b + 1, i], kh[b:b + 1], vh[b:b + 1], scale, seq_lens=[n_vis],
+                                            valid=valid[b:b + 1])
+            assert np.allclose(out[b, i], ref[0], rtol=1e-12, atol=1e-14)
+            assert np.allclose(lse[b, i], rl[0], rtol=1e-12)
+    # without a mask it is the unmasked attention
+    full, _ = o.multi_query_attention(qm, kh, vh, scale)
+    same, _ = o.multi_query_attention(qm, kh, vh, scale, valid=np.ones((bsz, T), dtype=bool))
+    assert np.array_equal(full, same)
+
+
 def test_sparse_v_limits_and_bound(golden_codebooks):
     s, q, kc, kn, vc, vn, kh, vh, ck, cv = _small_cache(T=200, golden=golden_codebooks)
     q = q * 6.0     # sharpen the attention so some rows fall under the threshold
