@@ -599,7 +599,8 @@ def bench_paged(args, w, signs, dev, tq, inputs, torch, np, log):
 
 def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
     """QJL keys: a step appends one token per (batch, kv head), the key with its sign sketch and
-    the value as usual, then decode attention with QJL-corrected scores (the generic kernel)."""
+    the value as usual, then decode attention with QJL-corrected scores (one launch of the fused
+    kernel: the query's sketch and the sign products on matrix cores)."""
     batch, hq, hkv, ctx = w.batch, w.n_q_heads, w.n_kv_heads, w.ctx
     bk, bv, m = w.bits_k, w.bits_v, w.extra["qjl_m"]
     k_row = D * bk // 8 + 2 + m // 8 + 2       # codes + norm + sign bits + residual norm
@@ -652,7 +653,7 @@ def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
     result = {
         "metric": METRIC, "value": batch * ctx / (ms_per_step / 1e3), "unit": "KV-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16+f32",
         "data": "synthetic (seeded; shapes and value distributions of the workload; seeded Gaussian sketch)",
         "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D, "ctx": ctx,
                    "bits_k": bk, "qjl_sketch_rows": m, "bits_v": bv,
@@ -661,7 +662,7 @@ def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
         "decode_call_us": ms_k * 1e3, "append_us": ms_a * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "QJL decode call (decode_split_generic + decode_merge, fp32 vector ALU)",
+                     "kernel": "decode_fused_kernel (QJL: sign products against the query's sketch)",
                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
                      "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3],
                      "bytes_note": f"per (token, kv head): key {k_row} B (codes, norm, sign bits, residual norm), "

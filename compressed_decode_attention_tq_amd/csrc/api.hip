@@ -309,7 +309,7 @@ int check_paged_pair(const tq_paged_cache *k, const tq_paged_cache *v) {
 
 int check_sketch(const tq_qjl_sketch *s) {
   if (s == nullptr || s->bits == nullptr || s->res_norms == nullptr || s->proj == nullptr) return TQ_ERR_INVALID_ARG;
-  if (!aligned(s->bits, 16) || !aligned(s->res_norms, 2) || !aligned(s->proj, 4)) return TQ_ERR_INVALID_ARG;
+  if (!aligned(s->bits, 16) || !aligned(s->res_norms, 2) || !aligned(s->proj, 16)) return TQ_ERR_INVALID_ARG;
   if (s->m != kD) return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }
@@ -560,7 +560,10 @@ int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cach
   a.qjl_rnorm = ks->res_norms;
   a.qjl_proj = ks->proj;
   a.qjl_m = ks->m;
-  return hip_status(launch_decode_generic(a, static_cast<hipStream_t>(hip_stream)));
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  // 3-bit codes, 2-bit values, groups up to 8, no Sparse V: one launch on matrix cores
+  if (decode_fused_qjl_supported(a)) return hip_status(launch_decode_fused_qjl(a, stream));
+  return hip_status(launch_decode_generic(a, stream));
 }
 
 int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv,

@@ -62,7 +62,9 @@ constexpr float kNvFloor = 1e-20f;  // ||v|| used for the range test of an all-z
 constexpr int kRsrcWord3 = 0x00020000;
 
 // LDS map (bytes):
-//   [0, 64K)      K table: entry e at e*256 + copy*8 (copy < 32)
+//   [0, 64K)      K table: entry e at e*256 + copy*8 (copy < 32); 3-bit keys use entries < 64
+//                 only, [0, 16K), and QJL keys put the sign table in [16K, 48K): entry e (a
+//                 byte of sign bits) at 16K + e*128 + copy*16 (copy < 8), eight fp16 +/-1
 //   [64K, 128K)   V table: entry e at 64K + e*256 + copy*8
 //   [128K, 160K)  one 4 KB buffer per wave:
 //                   [0, 2K)  scores of the tile, [32 token pairs][2 head halves][2][NH/2]
@@ -74,6 +76,7 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr uint32_t kVBase = 64 * 1024;
 constexpr uint32_t kWBase = 128 * 1024;
 constexpr uint32_t kPBase = 2048;
+constexpr uint32_t kSgnBase = 16 * 1024;
 
 __device__ __forceinline__ uint2 lds_u64(const uint8_t *lds, uint32_t addr) {
   return *reinterpret_cast<const uint2 *>(lds + addr);
@@ -126,14 +129,30 @@ __device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 
   uint8_t *row = lds + w * 256 + copy * 8;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    uint32_t c1;
-    if (BK == 4) c1 = khl[k];
-    else c1 = (w >> 3) ? khl[(2 * k + 1) & 7] : khl[(2 * k) & 7];
-    uint2 kv;
-    kv.x = (c0 & 0xffffu) | (c1 << 16);
-    kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
-    *reinterpret_cast<uint2 *>(row + k * 4096) = kv;
+    if (BK == 4 || k < 4) {  // a 3-bit key field has 6 bits: entries < 64
+      uint32_t c1;
+      if (BK == 4) c1 = khl[k];
+      else c1 = (w >> 3) ? khl[(2 * k + 1) & 7] : khl[(2 * k) & 7];
+      uint2 kv;
+      kv.x = (c0 & 0xffffu) | (c1 << 16);
+      kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
+      *reinterpret_cast<uint2 *>(row + k * 4096) = kv;
+    }
     if (VTAB) *reinterpret_cast<uint2 *>(row + kVBase + k * 4096) = make_uint2(vlo, vh[k & 3] | (vh[(k >> 2) & 3] << 16));
+  }
+}
+
+// QJL sign table: entry e holds fp16 (2 bit_k - 1) for bits k = 0..7 of e (bit set: +1), eight
+// copies so that the 8 lanes of one 128-byte LDS pass read distinct banks.
+__device__ __forceinline__ void build_sign_table(uint8_t *lds) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + kThreads * i, e = idx >> 3, copy = idx & 7;
+    uint32_t wd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wd[j] = ((e >> (2 * j)) & 1 ? 0x3C00u : 0xBC00u) | ((e >> (2 * j + 1)) & 1 ? 0x3C000000u : 0xBC000000u);
+    *reinterpret_cast<uint4 *>(lds + kSgnBase + e * 128 + copy * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 }
 
@@ -265,13 +284,15 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // keeps its own softmax, writes its own partials and merges its row group's splits when it is
 // the last to arrive; there is no combine across waves.
 template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false, bool RECORDS = true,
-          bool PREFILL = false>
+          bool PREFILL = false, bool QJL = false>
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !PAGED && !VMASK), "prefill: dense multi-query only");
   static_assert(!PAGED || !(PREFILL || (SPARSE && RECORDS) || (MULTI && APPEND)),
                 "paged caches: decode, its append, several query positions, Sparse V's two passes");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
+  static_assert(!QJL || (BK == 3 && !(SPARSE || MULTI || APPEND || PAGED || VMASK || PREFILL)),
+                "QJL keys: 3-bit codes, dense single-query decode");
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
@@ -331,6 +352,10 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         PAGED ? make_rsrc(a.k.norms, span_tok * 2) : make_rsrc(a.k.norm_plane(b, kvh) + t_begin, span_tok * 2);
     const __amdgpu_buffer_rsrc_t vnrs =
         PAGED ? make_rsrc(a.v.norms, span_tok * 2) : make_rsrc(a.v.norm_plane(b, kvh) + t_begin, span_tok * 2);
+    // QJL: the split's sign rows (16 bytes per token) and residual norms
+    const size_t qjl_row = QJL ? ((size_t)b * a.n_kv_heads + kvh) * a.k.capacity + t_begin : 0;
+    const __amdgpu_buffer_rsrc_t sbrs = make_rsrc(QJL ? a.qjl_bits + qjl_row * 16 : nullptr, QJL ? span_tok * 16 : 0);
+    const __amdgpu_buffer_rsrc_t rnrs = make_rsrc(QJL ? a.qjl_rnorm + qjl_row : nullptr, QJL ? span_tok * 2 : 0);
     constexpr uint32_t kNoPage = 0xffffffffu;
     // A value-pass split of at most 64 tiles is shared out by need (lane k: tile k, see VMASK
     // below); every other split keeps the round-robin tiles (lane i: tile wave + 8 i).
@@ -358,6 +383,10 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
 
     uint32_t kw[4][4];
     uint32_t nkw = 0;
+    // QJL, per sub-tile s: the sign bits 32 quarter .. 32 quarter + 31 of token 16 s + m_row (the
+    // lane's B-operand column), and that token's key norm and residual norm
+    uint32_t sgw[4] = {0u, 0u, 0u, 0u};
+    uint16_t nq16[4] = {0, 0, 0, 0}, rq16[4] = {0, 0, 0, 0};
     auto load_keys = [&](int tile) {
       // the whole offset is in the vector offset: a tile past the split's end lies outside
       // the buffer's range and reads as zeros without touching memory
@@ -373,7 +402,17 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           kw[s][0] = w[0]; kw[s][1] = w[1]; kw[s][2] = w[2]; kw[s][3] = 0u;
         }
       }
-      nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + tile_off(tok, 2), 0, 0);
+      if constexpr (QJL) {
+        const uint32_t t16 = (uint32_t)tile * kTile + (uint32_t)m_row;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          sgw[s] = __builtin_amdgcn_raw_buffer_load_b32(sbrs, (t16 + 16 * s) * 16 + (uint32_t)quarter * 4, 0, 0);
+          nq16[s] = __builtin_amdgcn_raw_buffer_load_b16(knrs, (t16 + 16 * s) * 2, 0, 0);
+          rq16[s] = __builtin_amdgcn_raw_buffer_load_b16(rnrs, (t16 + 16 * s) * 2, 0, 0);
+        }
+      } else {
+        nkw = __builtin_amdgcn_raw_buffer_load_b32(knrs, n_voff + tile_off(tok, 2), 0, 0);
+      }
     };
 
     // APPEND: in the workgroup whose split holds position T - 1, the wave that reads that
@@ -423,6 +462,14 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       }
     }
     const uint16_t sgn = *reinterpret_cast<const uint16_t *>(a.k.signs + 2 * lane);
+    // QJL: wave w computes sketch rows j = 16 w .. 16 w + 15 of the query group; the lane loads
+    // S[j][32 quarter .. 32 quarter + 31], j = 16 w + m_row (its B-operand column)
+    float4 srow[8];
+    if constexpr (QJL) {
+      const float4 *src = reinterpret_cast<const float4 *>(a.qjl_proj + (size_t)(16 * wave + m_row) * kD + 32 * quarter);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) srow[m] = src[m];
+    }
     if (!defer_keys && !VMASK) load_keys(PREFILL ? 0 : wave);
     // VMASK: a split of at most 64 tiles is shared out by need (lane k looks at tile k); a longer
     // one (at most 64 tiles per wave) keeps the round-robin tiles (lane k: tile wave + 8 k), where
@@ -440,6 +487,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       }
     }
     build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
+    if constexpr (QJL) build_sign_table(lds);
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
     // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
     if (appends) {
@@ -572,7 +620,55 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         qop[m][6] = part[4 * m + 2]; qop[m][7] = part[4 * m + 3];
       }
     }
-    __syncthreads();  // qrot (wave buffers 0..1) is free for staging from here
+    // QJL: the query sketch pq[h][j] = sqrt(pi/2)/m (S R q~)_j on matrix cores: the query
+    // operands above against S^T (each element split into its fp16 value and remainder, in the
+    // {hi, hi, lo, lo} order of the key operands), 8 products per wave for its 16 rows of S.
+    // Lane (m_row, quarter) gets heads 2 quarter, 2 quarter + 1 of row j; pq goes to wave
+    // buffers 2..3, then comes back as the A operands of the sign products, rows as for qop
+    // (2h the fp16 part of head h, 2h+1 the remainder); K step kk of the lane's quarter covers
+    // signs 32 quarter + 8 kk .. + 7, byte kk of the lane's sign word.
+    half8 sop[4];
+    if constexpr (QJL) {
+      float *pq_lds = reinterpret_cast<float *>(lds + kWBase + 2 * 4096);  // [NH][128]
+      floatx4 pacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float f[4] = {srow[m].x, srow[m].y, srow[m].z, srow[m].w};
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (_Float16)f[e];
+          lo[e] = (_Float16)(f[e] - (float)hi[e]);
+        }
+        half8 sb;
+        sb[0] = hi[0]; sb[1] = hi[1]; sb[2] = lo[0]; sb[3] = lo[1];
+        sb[4] = hi[2]; sb[5] = hi[3]; sb[6] = lo[2]; sb[7] = lo[3];
+        pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[m], sb, pacc, 0, 0, 0);
+      }
+      constexpr float kQjlKappa = 1.2533141373155003f / (float)kD;  // sqrt(pi/2) / m, m = d
+      if (2 * quarter < NH) {
+        const int j = 16 * wave + m_row;
+        pq_lds[(2 * quarter) * kD + j] = kQjlKappa * (pacc[0] + pacc[1]);
+        pq_lds[(2 * quarter + 1) * kD + j] = kQjlKappa * (pacc[2] + pacc[3]);
+      }
+      __syncthreads();
+      const int head = m_row >> 1;
+      const bool lo_row = (m_row & 1) != 0;
+      const bool live = head < NH && vlive(head);
+      const float *src = pq_lds + (live ? head : 0) * kD + 32 * quarter;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float4 f0 = live ? *reinterpret_cast<const float4 *>(src + 8 * kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 f1 = live ? *reinterpret_cast<const float4 *>(src + 8 * kk + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 hi = (_Float16)v[e];
+          sop[kk][e] = lo_row ? (_Float16)(v[e] - (float)hi) : hi;
+        }
+      }
+    }
+    __syncthreads();  // qrot (wave buffers 0..1) and pq (2..3) are free for staging from here
 
     // last visible position of this lane's rows (they differ only with several query
     // positions; -1 for a row without a query)
@@ -649,6 +745,35 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[m], bop[m & 1][s], acc[s], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // QJL: the sign-sketch products, acc2 = pq . (2 bits - 1) per row and token, and the two
+      // norms of the lane's tokens, taken before the prefetch overwrites them
+      floatx4 acc2[4];
+      float nqf[4], rqf[4];
+      if constexpr (QJL) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          acc2[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+          nqf[s] = f16(nq16[s]);
+          rqf[s] = f16(rq16[s]);
+        }
+        const uint32_t c16 = kSgnBase + (uint32_t)(lane & 7) * 16u;
+        auto sign_operand = [&](int kk, int s) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(lds + c16 + ((sgw[s] >> (8 * kk)) & 0xffu) * 128u);
+          half8 bo;
+          __builtin_memcpy(&bo, &w, 16);
+          return bo;
+        };
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          half8 sb[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sb[s] = sign_operand(kk, s);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc2[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sop[kk], sb[s], acc2[s], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       const uint32_t nk_pair = nkw;
       if (PREFETCH) load_keys(next_tile);
 
@@ -657,7 +782,10 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int tok = 16 * s + m_row, p2 = tok >> 1, tb = tok & 1;
-          const float2 sv = make_float2(acc[s][0] + acc[s][1], acc[s][2] + acc[s][3]);
+          float2 sv = make_float2(acc[s][0] + acc[s][1], acc[s][2] + acc[s][3]);
+          if constexpr (QJL)  // ||k|| (R q).c + ||r|| pq.(2 bits - 1), the token's whole score
+            sv = make_float2(fmaf(rqf[s], acc2[s][0] + acc2[s][1], nqf[s] * sv.x),
+                             fmaf(rqf[s], acc2[s][2] + acc2[s][3], nqf[s] * sv.y));
           uint32_t off;
           if (NH == 4) off = score_unit<4>(p2, quarter) + tb * 8;
           else off = score_unit<8>(p2, 2 * (quarter >> 1) + tb) + (quarter & 1) * 8;
@@ -684,10 +812,12 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       nk[1] = f16((uint16_t)(nk_pair >> 16));
       nv[0] = fmaxf(f16((uint16_t)(nvw & 0xffffu)), kNvFloor);
       nv[1] = fmaxf(f16((uint16_t)(nvw >> 16)), kNvFloor);
+      if constexpr (!QJL) {  // (QJL scores carry their norms already)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] *= nk[tb];
+          for (int hh = 0; hh < NH2; ++hh) sc[tb][hh] *= nk[tb];
+      }
       if (t0 + kTile > t_end) {  // ragged last tile of the split (uniform branch)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -1142,18 +1272,21 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   }
 }
 
-template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS, bool PREFILL>
+template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS, bool PREFILL,
+          bool QJL>
 __global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
-  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL>(a);
+  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>(a);
 }
 
 template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true,
-          bool PREFILL = false>
+          bool PREFILL = false, bool QJL = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
   if (a.vg_size <= 4) {
-    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL><<<grid, kThreads, 0, stream>>>(a);
+    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>
+        <<<grid, kThreads, 0, stream>>>(a);
   } else {
-    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL><<<grid, kThreads, 0, stream>>>(a);
+    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>
+        <<<grid, kThreads, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
@@ -1230,6 +1363,19 @@ hipError_t launch_decode_fused_paged_sparse(const DecodeArgs &key_pass, const De
   if (e != hipSuccess) return e;
   return v.k.bits == 4 ? launch_nh<4, false, false, false, true, true>(v, (int)items_v, stream)
                        : launch_nh<3, false, false, false, true, true>(v, (int)items_v, stream);
+}
+
+bool decode_fused_qjl_supported(const DecodeArgs &a) {
+  return decode_fused_supported(a) && a.k.bits == 3 && a.n_q == 1 && a.vgroups == 1 && a.xk == nullptr &&
+         a.block_table == nullptr && a.qjl_bits != nullptr && a.qjl_rnorm != nullptr && a.qjl_proj != nullptr &&
+         a.qjl_m == kD;
+}
+
+hipError_t launch_decode_fused_qjl(const DecodeArgs &a, hipStream_t stream) {
+  if (!decode_fused_qjl_supported(a)) return hipErrorInvalidValue;
+  const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  return launch_nh<3, false, false, false, false, false, true, false, true>(a, (int)items, stream);
 }
 
 hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {

@@ -10,10 +10,10 @@
 //   r_i = h_i / sqrt(d) - n16 c[code_i]       the error of the reconstruction the decoder
 //                                             makes (n16 = the stored fp16 norm), rotated domain
 //   ||r|| -> fp16;  z = S r;  bit j = (z_j >= 0), LSB first in a 16-byte row per token.
-// S^T sits in LDS with a row pitch of 129 floats (66 KB), so both the transposing copy and
-// the reads are free of bank conflicts: lane l reads row i at column l (and l + 64) while the
-// residual coordinate r_i is a broadcast; lane l forms z_l and z_{l+64} and two ballots give
-// the 128 bits.
+// Longer appends: S^T sits in LDS with a row pitch of 129 floats (66 KB), so both the
+// transposing copy and the reads are free of bank conflicts: lane l reads row i at column l
+// (and l + 64) while the residual coordinate r_i is a broadcast; lane l forms z_l and z_{l+64}
+// and two ballots give the 128 bits.  Up to 8 tokens: the kernel below.
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
@@ -33,7 +33,19 @@ __global__ __launch_bounds__(256) void qjl_quantize_kernel(QjlQuantArgs a) {
   __shared__ uint32_t words[4][4 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
-  for (int e = threadIdx.x; e < kD * kD; e += blockDim.x) st[(e & (kD - 1)) * kPitch + (e >> 7)] = a.proj[e];
+  {  // S^T into LDS: the thread's 16 float4 loads all go out before the first store
+    float4 f[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) f[k] = reinterpret_cast<const float4 *>(a.proj)[threadIdx.x + 256 * k];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = 4 * (threadIdx.x + 256 * k), j = e >> 7, i = e & (kD - 1);
+      st[i * kPitch + j] = f[k].x;
+      st[(i + 1) * kPitch + j] = f[k].y;
+      st[(i + 2) * kPitch + j] = f[k].z;
+      st[(i + 3) * kPitch + j] = f[k].w;
+    }
+  }
   __syncthreads();
   const CacheView &c = a.k;
   uint8_t *plane = c.plane(b, h);
@@ -79,8 +91,86 @@ __global__ __launch_bounds__(256) void qjl_quantize_kernel(QjlQuantArgs a) {
   }
 }
 
+// A few tokens (a decode step): the sketch rows are shared out instead of S being staged.  Block
+// (chunk, h, b) is one wave that handles rows j = 16 chunk .. 16 chunk + 15 of every token of the
+// call; lane l holds S[16 chunk + l / 4][32 (l % 4) .. + 31] in registers, forms that quarter of
+// (S r)_j against the residual (a broadcast from LDS) and the quad adds the quarters.  Every
+// block quantizes the token itself (the same steps as above); chunk 0 stores the codes and both
+// norms, each chunk its 16 sign bits.
+constexpr int kQjlSmallMax = 8;   // tokens per call for this kernel
+constexpr int kQjlChunks = kD / 16;
+
+template <int DTYPE, int BITS>
+__global__ __launch_bounds__(64) void qjl_append_small_kernel(QjlQuantArgs a) {
+  __shared__ __align__(16) float res[kD];
+  __shared__ uint32_t words[4 * 8];
+  const int lane = threadIdx.x, chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int q = lane & 3;
+  float4 srow[8];
+  const float4 *src = reinterpret_cast<const float4 *>(a.proj + (size_t)(16 * chunk + (lane >> 2)) * kD + 32 * q);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) srow[m] = src[m];
+  const CacheView &c = a.k;
+  uint8_t *plane = c.plane(b, h);
+  uint16_t *norms = c.norm_plane(b, h);
+  const size_t unit = (size_t)b * c.n_kv_heads + h;
+  uint8_t *bits = a.bits + unit * (size_t)c.capacity * (kD / 8);
+  uint16_t *rnorms = a.res_norms + unit * (size_t)c.capacity;
+  for (int j = 0; j < a.n_tokens; ++j) {
+    const int t = a.start_pos + j;
+    float x0, x1, n, h0, h1;
+    load_pair<DTYPE>(a.x, (((size_t)b * a.n_tokens + j) * c.n_kv_heads + h) * kD + 2 * lane, x0, x1);
+    uint32_t c0, c1;
+    token_codes<BITS>(c, x0, x1, lane, c0, c1, n, h0, h1);
+    const uint16_t n16 = float_to_half_bits(n);
+    const float nf = half_bits_to_float(n16);
+    const float r0 = h0 * kInvSqrtD - nf * c.centroids[c0];
+    const float r1 = h1 * kInvSqrtD - nf * c.centroids[c1];
+    *reinterpret_cast<float2 *>(&res[2 * lane]) = make_float2(r0, r1);
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    float z = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float4 r4 = *reinterpret_cast<const float4 *>(&res[32 * q + 4 * m]);
+      z = fmaf(srow[m].x, r4.x, z);
+      z = fmaf(srow[m].y, r4.y, z);
+      z = fmaf(srow[m].z, r4.z, z);
+      z = fmaf(srow[m].w, r4.w, z);
+    }
+    z += dpp_mov<kDppQuadXor1>(z);
+    z += dpp_mov<kDppQuadXor2>(z);
+    const uint64_t ball = __ballot(z >= 0.f);
+    uint32_t sb = 0u;  // bit i: row 16 chunk + i, read from lane 4 i
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sb |= (uint32_t)((ball >> (4 * i)) & 1u) << i;
+    if (lane == 0) reinterpret_cast<uint16_t *>(bits + (size_t)t * (kD / 8))[chunk] = (uint16_t)sb;
+    if (chunk == 0) {
+      const float rn = sqrtf(wave_reduce<false>(r0 * r0 + r1 * r1));
+      if (lane == 0) {
+        norms[t] = n16;
+        rnorms[t] = float_to_half_bits(rn);
+      }
+      store_row<BITS>(plane + (size_t)t * (16 * BITS), c0, c1, lane, words);
+    }
+    // every lane has read the residual before the next token overwrites it
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
+}
+
 template <int DTYPE>
 hipError_t launch_dtype(const QjlQuantArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.n_tokens <= kQjlSmallMax) {
+    const dim3 g2(kQjlChunks, grid.y, grid.z);
+    switch (a.k.bits) {
+      case 2: qjl_append_small_kernel<DTYPE, 2><<<g2, 64, 0, stream>>>(a); break;
+      case 3: qjl_append_small_kernel<DTYPE, 3><<<g2, 64, 0, stream>>>(a); break;
+      case 4: qjl_append_small_kernel<DTYPE, 4><<<g2, 64, 0, stream>>>(a); break;
+      default: qjl_append_small_kernel<DTYPE, 8><<<g2, 64, 0, stream>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   switch (a.k.bits) {
     case 2: qjl_quantize_kernel<DTYPE, 2><<<grid, 256, 0, stream>>>(a); break;
     case 3: qjl_quantize_kernel<DTYPE, 3><<<grid, 256, 0, stream>>>(a); break;

@@ -104,9 +104,9 @@ struct DecodeArgs {
   // visits only the tiles whose maximum reaches some head's threshold
   float *tile_max;
   int tile_stride;
-  // QJL keys (qjl_m > 0, the generic kernel only): beside the key codes, the sign sketch of each
-  // key's residual, [batch][n_kv_heads][capacity][qjl_m / 8] bytes, its fp16 norms
-  // [batch][n_kv_heads][capacity], and the sketch matrix S [qjl_m][d] fp32
+  // QJL keys (qjl_m > 0): beside the key codes, the sign sketch of each key's residual,
+  // [batch][n_kv_heads][capacity][qjl_m / 8] bytes, its fp16 norms [batch][n_kv_heads][capacity],
+  // and the sketch matrix S [qjl_m][d] fp32
   const uint8_t *qjl_bits;
   const uint16_t *qjl_rnorm;
   const float *qjl_proj;
@@ -125,6 +125,10 @@ struct QjlQuantArgs {
   int start_pos, n_tokens;
 };
 hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t stream);
+// QJL decode on matrix cores (3-bit codes, 2-bit values, groups up to 8, no Sparse V): the fused
+// kernel with the query's sketch and the sign-sketch products.
+bool decode_fused_qjl_supported(const DecodeArgs &a);
+hipError_t launch_decode_fused_qjl(const DecodeArgs &a, hipStream_t stream);
 // The generic split kernel, the Sparse-V second pass (if a.sparse) and the split merge: any code
 // width, group <= 16, and the only path that takes QJL keys.
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t stream);

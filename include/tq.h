@@ -107,7 +107,7 @@ typedef struct tq_cache {
  *              first) of a row is 1 iff (S r)_j >= 0
  *   res_norms  device [batch][n_kv_heads][capacity] fp16 bit patterns of ||r||, 2-byte aligned
  *   proj       device [m][d] fp32: the Gaussian matrix S, i.i.d. N(0, 1) entries drawn by the
- *              caller (the library has no random generator), 4-byte aligned
+ *              caller (the library has no random generator), 16-byte aligned
  *   m          sketch rows; m must equal d (128): one bit per coordinate
  * The key cache itself (tq_cache, ROWS layout) holds the first stage's codes and norms; with
  * bits = b - 1 the key costs b bits per coordinate plus two fp16 norms. */
@@ -203,8 +203,10 @@ int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void
  *                 + sqrt(pi/2) / m ||r_t||_fp16 (S R q) . (2 bits_t - 1) ),
  * an unbiased estimate of scale q . k_t over the draw of S, followed by the same softmax,
  * Sparse V, value sum and inverse rotation.  Arguments as tq_decode_attn plus ks, the sketch of
- * the keys in k; the workspace is tq_decode_workspace_bytes(...).  Any code widths, groups up
- * to 16 (fp32 vector arithmetic).
+ * the keys in k; the workspace is tq_decode_workspace_bytes(...).  Keys of 3 bits, values of 2
+ * bits, groups up to 8 and no Sparse V run in one launch on matrix cores (the query's sketch
+ * S R q and the sign products as fp16 matrix operands, the signs exact as +/-1); any other
+ * widths, groups up to 16 and Sparse V take the fp32 vector kernels.
  * Errors: as tq_decode_attn, and TQ_ERR_INVALID_ARG / TQ_ERR_UNSUPPORTED for the sketch. */
 int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cache *v, const void *q,
                        int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,

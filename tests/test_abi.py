@@ -262,6 +262,7 @@ def test_qjl_argument_validation():
 
     assert dec(sk(m=0)) == tq.TQ_ERR_UNSUPPORTED
     assert dec(sk(proj=0)) == tq.TQ_ERR_INVALID_ARG
+    assert dec(sk(proj=FAKE + 0xC00004)) == tq.TQ_ERR_INVALID_ARG     # S is read 16 bytes at a time
     assert dec(sk(), hq=7) == tq.TQ_ERR_INVALID_ARG
     assert dec(sk(), ctx=4096) == tq.TQ_ERR_CAPACITY
     assert dec(sk(), wsb=16) == tq.TQ_ERR_WORKSPACE

@@ -25,7 +25,10 @@ def _say(*a):
 
 
 @pytest.mark.parametrize("bits,dtype,n_tok,start", [(3, "bf16", 200, 0), (2, "f32", 130, 7), (4, "f16", 64, 64),
-                                                    (8, "bf16", 70, 1), (3, "f32", 1, 100)])
+                                                    (8, "bf16", 70, 1), (3, "f32", 1, 100),
+                                                    # up to 8 tokens: sketch rows shared out over workgroups
+                                                    (4, "bf16", 8, 33), (2, "f16", 3, 0), (8, "f32", 5, 60),
+                                                    (3, "bf16", 9, 20)])
 def test_qjl_quantize_matches_oracle(bits, dtype, n_tok, start, golden_codebooks):
     _say("qjl quantize", bits, dtype, n_tok, start)
     w = inputs.WORKLOADS["qjl8k"]
@@ -54,8 +57,8 @@ def test_qjl_quantize_matches_oracle(bits, dtype, n_tok, start, golden_codebooks
     _say(f"  near-boundary coords {tot[0]}, near-zero sign bits {tot[1]}, tokens with a code flip {tot[2]}")
 
 
-def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, seq_lens=None):
-    _say("qjl decode", name, batch, hq, hkv, ctx, bits_k, tau, seq_lens)
+def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, seq_lens=None, q_dtype=None):
+    _say("qjl decode", name, batch, hq, hkv, ctx, bits_k, tau, seq_lens, q_dtype)
     w = inputs.WORKLOADS[name]
     g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
     signs = inputs.rotation_signs()
@@ -68,14 +71,15 @@ def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, se
     tq.quantize_append(vc, g["v"].to(DEV).contiguous(), 0)
     scale = 1.0 / math.sqrt(128)
     sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
-    buf = tq.qjl_decode_attn(kc, sk, vc, g["q"].to(DEV).contiguous(), ctx, scale, tau=tau, seq_lens=sl,
+    q = g["q"] if q_dtype is None else g["q"].to(q_dtype)
+    buf = tq.qjl_decode_attn(kc, sk, vc, q.to(DEV).contiguous(), ctx, scale, tau=tau, seq_lens=sl,
                              want_scores=True)
     torch.cuda.synchronize()
     s64 = signs.numpy().astype(np.float64)
     p64 = proj.numpy().astype(np.float64)
     kh = parity.oracle_qjl_view(kc, sk, s64, golden[bits_k], p64, ctx)
     vh = parity.oracle_cache_view(vc, s64, golden[2], ctx)
-    out, lse, scores = o.decode_attention(parity.to_f64(g["q"]), kh, vh, scale, seq_lens=seq_lens, tau=tau)
+    out, lse, scores = o.decode_attention(parity.to_f64(q), kh, vh, scale, seq_lens=seq_lens, tau=tau)
     parity.check_scores(buf.scores.cpu().numpy(), scores, seq_lens)
     fin = np.isfinite(lse)
     got_lse = buf.lse.cpu().numpy()
@@ -87,9 +91,11 @@ def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, se
     worst = parity.check_rows(buf.out.cpu().numpy(), out, "qjl decode out", allowance=allowance)
     # the correction is not a no-op: the same codes without the sketch give other scores
     kh_mse = parity.oracle_cache_view(kc, s64, golden[bits_k], ctx)
-    _, _, mse_scores = o.decode_attention(parity.to_f64(g["q"]), kh_mse, vh, scale, seq_lens=seq_lens)
-    diff = np.nanmax(np.abs(np.where(np.isfinite(scores), scores - mse_scores, 0.0)))
-    assert diff > 1e-2 * np.nanmax(np.abs(np.where(np.isfinite(scores), scores, 0.0)))
+    _, _, mse_scores = o.decode_attention(parity.to_f64(q), kh_mse, vh, scale, seq_lens=seq_lens)
+    live = np.isfinite(scores)
+    if live.any():
+        diff = np.max(np.abs(scores[live] - mse_scores[live]))
+        assert diff > 1e-2 * np.max(np.abs(scores[live]))
     _say(f"  worst rel err {worst:.2e} borderline {nb}")
 
 
@@ -100,7 +106,19 @@ def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, se
     ("batch32k", 2, 8, 2, 1300, 1344, 3, 1e-4, None),
     ("ctx131k", 1, 16, 2, 900, 960, 4, 1e-4, [900]),
     ("qjl8k", 3, 16, 1, 300, 320, 3, 0.0, [300, 0, 1]),
+    # 3-bit codes, groups up to 8, no Sparse V: the matrix-core kernel (sign products on fp16
+    # +/-1 operands against the query's sketch)
+    ("qjl8k", 2, 16, 2, 1000, 1024, 3, 0.0, [1000, 1]),
+    ("qjl8k", 3, 8, 2, 640, 640, 3, 0.0, [640, 0, 65]),
+    ("ctx131k", 1, 16, 2, 2000, 2048, 3, 0.0, None),
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 0.0, None),
+    ("qjl8k", 1, 12, 4, 4100, 4160, 3, 0.0, None),
 ])
 def test_qjl_decode_matches_oracle(case, golden_codebooks):
     name, batch, hq, hkv, ctx, cap, bk, tau, sl = case
     _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bk, golden_codebooks, tau=tau, seq_lens=sl)
+
+
+def test_qjl_decode_query_dtypes(golden_codebooks):
+    _qjl_decode_case("qjl8k", 2, 8, 2, 500, 512, 3, golden_codebooks, q_dtype=torch.float32)
+    _qjl_decode_case("qjl8k", 2, 8, 2, 500, 512, 3, golden_codebooks, q_dtype=torch.float16, seq_lens=[500, 77])
