@@ -95,8 +95,9 @@ __device__ __forceinline__ uint32_t score_unit(int pr, int u) {
   return (uint32_t)pr * 64u + ((uint32_t)(u ^ ((pr >> 2) & 3)) << 4);
 }
 // P' staging: 16-byte unit `unit` (tokens 8*unit .. 8*unit+7) of row `row`.
+template <uint32_t PB = kPBase>
 __device__ __forceinline__ uint32_t pst_off(int row, int unit) {
-  return kPBase + (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
+  return PB + (uint32_t)row * 128u + ((uint32_t)(unit ^ ((row >> 1) & 7)) << 4);
 }
 
 // Code tables, built from the centroids each thread holds in registers.  Thread (w, copy),
@@ -116,7 +117,11 @@ __device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 
   uint32_t vh[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) vh[i] = h16(vcs[i]);
+  if (threadIdx.x >= kThreads) return;  // (12-wave workgroups: the first 8 waves build them)
   const int w = threadIdx.x >> 5, copy = threadIdx.x & 31;
+  // (3-bit keys: the second code of entry 16k + w is 2k or 2k + 1 by bit 3 of w; a bitwise
+  // select, so that the compiler does not turn it into a scratch-memory array index)
+  const uint32_t odd = 0u - (uint32_t)((w >> 3) & 1);
   uint32_t c0 = 0u, vlo0 = 0u, vlo1 = 0u;
 #pragma unroll
   for (int i = 0; i < NK; ++i) c0 = (w & (NK - 1)) == i ? khl[i] : c0;
@@ -132,7 +137,7 @@ __device__ __forceinline__ void build_tables(uint8_t *lds, const float (&kcs)[1 
     if (BK == 4 || k < 4) {  // a 3-bit key field has 6 bits: entries < 64
       uint32_t c1;
       if (BK == 4) c1 = khl[k];
-      else c1 = (w >> 3) ? khl[(2 * k + 1) & 7] : khl[(2 * k) & 7];
+      else c1 = (khl[(2 * k + 1) & 7] & odd) | (khl[(2 * k) & 7] & ~odd);
       uint2 kv;
       kv.x = (c0 & 0xffffu) | (c1 << 16);
       kv.y = (c0 >> 16) | (c1 & 0xffff0000u);
@@ -284,7 +289,7 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // keeps its own softmax, writes its own partials and merges its row group's splits when it is
 // the last to arrive; there is no combine across waves.
 template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK = false, bool RECORDS = true,
-          bool PREFILL = false, bool QJL = false>
+          bool PREFILL = false, bool QJL = false, int W = kWaves>
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !PAGED && !VMASK), "prefill: dense multi-query only");
@@ -293,12 +298,21 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
   static_assert(!QJL || (BK == 3 && !(SPARSE || MULTI || APPEND || PAGED || VMASK || PREFILL)),
                 "QJL keys: 3-bit codes, dense single-query decode");
+  // W = 12 (three waves per SIMD) for groups of up to 4 heads in plain single-query decode:
+  // 2 KB wave buffers (scores [0, 1K), P' rows 0..7 [1K, 2K)) and a shared zero block for P'
+  // rows 8..15, behind the tables
+  static_assert(W == kWaves || (W == 12 && NH == 4 && !(SPARSE || MULTI || PAGED || VMASK || PREFILL || QJL)),
+                "12 waves: plain decode of groups up to 4 heads");
+  constexpr int NT = 64 * W;                          // threads of the workgroup
+  constexpr uint32_t PB = W == 12 ? 1024u : kPBase;   // P' staging inside a wave buffer
+  constexpr uint32_t kZeroBase = kWBase + 12 * 2048;  // (W = 12) 1 KB of zeros
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
   constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
   constexpr uint32_t WBASE = KEYS_ONLY ? kVBase : kWBase;  // per-wave staging buffers
-  constexpr uint32_t WSTRIDE = KEYS_ONLY ? 2048u : 4096u;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KEYS_ONLY ? kVBase + kWaves * 2048 : kLdsBytes];
+  constexpr uint32_t WSTRIDE = KEYS_ONLY || W == 12 ? 2048u : 4096u;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KEYS_ONLY ? kVBase + kWaves * 2048
+                                                      : W == 12 ? kZeroBase + 1024 : kLdsBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
@@ -311,8 +325,11 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   uint8_t *wbuf = lds + WBASE + wave * WSTRIDE;
   float *qrot = reinterpret_cast<float *>(lds + WBASE);  // [NH][128] between tiles
 
-  if (!SPARSE && NH == 4)  // P' rows 8..15 stay zero for the whole launch
+  if constexpr (W == 12) {  // the zero block that P' rows 8..15 read
+    if (wave == 0) *reinterpret_cast<uint4 *>(lds + kZeroBase + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+  } else if (!SPARSE && NH == 4) {  // P' rows 8..15 stay zero for the whole launch
     *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   {  // one split of one (batch, kv head) per workgroup
     const int item = blockIdx.x;
@@ -424,7 +441,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // is not written (and its tile reads zeros).
     const bool has_new = APPEND && T >= 1 && T - 1 >= t_begin && T - 1 < t_end;
     const int new_tile = has_new ? (T - 1 - t_begin) / kTile : -1;
-    bool appends = has_new && new_tile % kWaves == wave;
+    bool appends = has_new && new_tile % W == wave;
     int new_pb = b, new_pt = T - 1;  // plane and position of the new token
     if constexpr (PAGED) {
       if (appends) {
@@ -491,8 +508,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
     // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
     if (appends) {
-      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, lds + kWBase + wave * 4096);
-      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, lds + kWBase + wave * 4096);
+      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, lds + kWBase + wave * WSTRIDE);
+      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, lds + kWBase + wave * WSTRIDE);
     }
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
@@ -996,8 +1013,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         lo[0] = (_Float16)(v0 - (float)hi[0]);
         lo[1] = (_Float16)(v1 - (float)hi[1]);
         const uint32_t sub = (uint32_t)(pr & 3) * 4u;
-        *reinterpret_cast<half2v *>(wbuf + pst_off(2 * h, pr >> 2) + sub) = hi;
-        *reinterpret_cast<half2v *>(wbuf + pst_off(2 * h + 1, pr >> 2) + sub) = lo;
+        *reinterpret_cast<half2v *>(wbuf + pst_off<PB>(2 * h, pr >> 2) + sub) = hi;
+        *reinterpret_cast<half2v *>(wbuf + pst_off<PB>(2 * h + 1, pr >> 2) + sub) = lo;
       }
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
@@ -1005,7 +1022,9 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       // ---- O[row][coord] += P'[row][token] V[token][coord]
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint4 pa = *reinterpret_cast<const uint4 *>(wbuf + pst_off(m_row, 4 * c + quarter));
+        const uint8_t *pa_src = W == 12 && m_row >= 8 ? lds + kZeroBase + lane * 16
+                                                      : wbuf + pst_off<PB>(m_row, 4 * c + quarter);
+        const uint4 pa = *reinterpret_cast<const uint4 *>(pa_src);
         half8 aop;
         __builtin_memcpy(&aop, &pa, 16);
         auto value_operand = [&](int n) {
@@ -1054,7 +1073,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       }
     } else {
       int tile = wave;
-      for (; tile + kWaves < n_tiles; tile += kWaves) tile_body(tile, tile + kWaves, std::true_type{});
+      for (; tile + W < n_tiles; tile += W) tile_body(tile, tile + W, std::true_type{});
       if (tile < n_tiles) tile_body(tile, 0, std::false_type{});
     }
 
@@ -1184,7 +1203,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       const int h0 = NH == 8 ? 2 * quarter : 2 * (quarter & 1);
       float M0 = -INFINITY, M1 = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float *src = reinterpret_cast<const float *>(lds + w * 64);
         M0 = fmaxf(M0, src[2 * h0]);
         M1 = fmaxf(M1, src[2 * (h0 + 1)]);
@@ -1195,7 +1214,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       f1 = exp2_or_zero(own[2 * (h0 + 1)], M1);
       if (wave < NH) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
           const float *src = reinterpret_cast<const float *>(lds + w * 64);
           Lh += src[2 * wave + 1] * exp2_or_zero(src[2 * wave], Mh);
         }
@@ -1232,8 +1251,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     if (live_w) {
       float2 o = make_float2(0.f, 0.f);
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float2 x = *reinterpret_cast<const float2 *>(lds + kWBase + w * 4096 + (wave * kD + 2 * lane) * 4);
+      for (int w = 0; w < W; ++w) {
+        const float2 x = *reinterpret_cast<const float2 *>(lds + kWBase + w * WSTRIDE + (wave * kD + 2 * lane) * 4);
         o.x += x.x;
         o.y += x.y;
       }
@@ -1273,19 +1292,31 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
 }
 
 template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool VMASK, bool RECORDS, bool PREFILL,
-          bool QJL>
-__global__ __launch_bounds__(kThreads, 1) void decode_fused_kernel(DecodeArgs a) {
-  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>(a);
+          bool QJL, int W>
+__global__ __launch_bounds__(64 * W, 1) void decode_fused_kernel(DecodeArgs a) {
+  decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, W>(a);
 }
+
+// Splits of at least this many tokens run plain decode of up to 4 heads per kv head with 12
+// waves per workgroup; shorter ones (a wave would have few tiles) keep 8.
+constexpr int kWide12MinSplit = 48 * kTile;
 
 template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true,
           bool PREFILL = false, bool QJL = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
+  constexpr bool kCan12 = !(SPARSE || MULTI || PAGED || VMASK || PREFILL || QJL);
   if (a.vg_size <= 4) {
-    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>
+    if constexpr (kCan12) {
+      if (a.fplan.split_len >= kWide12MinSplit) {
+        decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, 12>
+            <<<grid, 64 * 12, 0, stream>>>(a);
+        return hipGetLastError();
+      }
+    }
+    decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, kWaves>
         <<<grid, kThreads, 0, stream>>>(a);
   } else {
-    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL>
+    decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, kWaves>
         <<<grid, kThreads, 0, stream>>>(a);
   }
   return hipGetLastError();

@@ -288,6 +288,9 @@ def test_decode_tiny_workload(signs, golden_codebooks):
     ("llama8k", 1, 2, 2, 333, 384, 8, 8),
     ("llama8k", 1, 4, 2, 64, 64, 2, 4),
     ("llama8k", 1, 16, 1, 500, 512, 4, 2),
+    # 256 (batch, kv head) planes with splits of 3072+ tokens: 12 waves per workgroup
+    ("batch32k", 32, 32, 8, 3100, 3136, 3, 2),
+    ("llama8k", 32, 16, 8, 3200, 3200, 4, 2),
 ])
 def test_decode_dense_matches_oracle(case, signs, golden_codebooks):
     name, *shape = case
@@ -354,6 +357,9 @@ def _append_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, seq
     ("llama8k", 3, 8, 2, 520, 576, 3, 2, [520, 0, 9], "f32"),
     ("llama8k", 2, 4, 4, 300, 320, 4, 2, [257, 64], "f16"),
     ("llama8k", 1, 8, 2, 333, 384, 8, 3, None, None),      # other widths: two launches
+    # 12 waves per workgroup (splits of 3072+ tokens), ragged lengths: the new token lands in
+    # various waves' tiles, one sequence is empty
+    ("batch32k", 32, 32, 8, 3100, 3136, 3, 2, [3100 - 37 * i for i in range(31)] + [0], None),
 ])
 def test_decode_append_matches_oracle(case, signs, golden_codebooks):
     name, *shape, xdt = case
