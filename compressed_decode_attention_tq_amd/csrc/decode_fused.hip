@@ -298,20 +298,24 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
   static_assert(!QJL || (BK == 3 && !(SPARSE || MULTI || APPEND || PAGED || VMASK || PREFILL)),
                 "QJL keys: 3-bit codes, dense single-query decode");
-  // W = 12 (three waves per SIMD) for groups of up to 4 heads in plain single-query decode:
-  // 2 KB wave buffers (scores [0, 1K), P' rows 0..7 [1K, 2K)) and a shared zero block for P'
-  // rows 8..15, behind the tables
-  static_assert(W == kWaves || (W == 12 && NH == 4 && !(SPARSE || MULTI || PAGED || VMASK || PREFILL || QJL)),
-                "12 waves: plain decode of groups up to 4 heads");
-  constexpr int NT = 64 * W;                          // threads of the workgroup
+  constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
+  // More waves per workgroup for single-query decode, paged or not, with long splits:
+  //   W = 12 (three per SIMD), groups of up to 4 heads, values too: 2 KB wave buffers (scores
+  //     [0, 1K), P' rows 0..7 [1K, 2K)) and a shared zero block for P' rows 8..15, behind the
+  //     tables;
+  //   the key-only first pass of Sparse V (2 KB wave buffers already): W = 16 for groups of
+  //     up to 4 heads, W = 12 for up to 8.
+  static_assert(W == kWaves ||
+                    (!(MULTI || VMASK || PREFILL || QJL) &&
+                     ((W == 12 && NH == 4 && !SPARSE) || (KEYS_ONLY && ((W == 16 && NH == 4) || (W == 12 && NH == 8))))),
+                "wider workgroups: single-query decode with long splits");
   constexpr uint32_t PB = W == 12 ? 1024u : kPBase;   // P' staging inside a wave buffer
   constexpr uint32_t kZeroBase = kWBase + 12 * 2048;  // (W = 12) 1 KB of zeros
   constexpr int NH2 = NH / 2;      // heads per softmax lane
   constexpr int KROW = 16 * BK;    // key bytes per token
-  constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
   constexpr uint32_t WBASE = KEYS_ONLY ? kVBase : kWBase;  // per-wave staging buffers
   constexpr uint32_t WSTRIDE = KEYS_ONLY || W == 12 ? 2048u : 4096u;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KEYS_ONLY ? kVBase + kWaves * 2048
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KEYS_ONLY ? kVBase + W * 2048
                                                       : W == 12 ? kZeroBase + 1024 : kLdsBytes];
 
   const int lane = threadIdx.x & 63;
@@ -325,7 +329,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   uint8_t *wbuf = lds + WBASE + wave * WSTRIDE;
   float *qrot = reinterpret_cast<float *>(lds + WBASE);  // [NH][128] between tiles
 
-  if constexpr (W == 12) {  // the zero block that P' rows 8..15 read
+  if constexpr (W == 12 && !KEYS_ONLY) {  // the zero block that P' rows 8..15 read
     if (wave == 0) *reinterpret_cast<uint4 *>(lds + kZeroBase + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
   } else if (!SPARSE && NH == 4) {  // P' rows 8..15 stay zero for the whole launch
     *reinterpret_cast<uint4 *>(wbuf + kPBase + 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
@@ -375,11 +379,11 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     const __amdgpu_buffer_rsrc_t rnrs = make_rsrc(QJL ? a.qjl_rnorm + qjl_row : nullptr, QJL ? span_tok * 2 : 0);
     constexpr uint32_t kNoPage = 0xffffffffu;
     // A value-pass split of at most 64 tiles is shared out by need (lane k: tile k, see VMASK
-    // below); every other split keeps the round-robin tiles (lane i: tile wave + 8 i).
+    // below); every other split keeps the round-robin tiles (lane i: tile wave + W i).
     const bool by_need = VMASK && n_tiles <= 64;
     uint32_t page_tok = kNoPage;  // paged: lane i holds tile_tok of its tile in the mapping above
     if constexpr (PAGED) {
-      const int tile_i = by_need ? lane : wave + kWaves * lane;
+      const int tile_i = by_need ? lane : wave + W * lane;
       if (tile_i < n_tiles) {
         const int P = a.k.capacity, t0 = t_begin + tile_i * kTile, slot = t0 / P;
         const int page = slot < a.max_pages ? a.block_table[(size_t)b * a.max_pages + slot] : -1;
@@ -388,7 +392,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     }
     auto tile_tok = [&](int tile) -> uint32_t {
       if constexpr (PAGED)
-        return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, by_need ? tile : (tile - wave) / kWaves);
+        return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, by_need ? tile : (tile - wave) / W);
       else return (uint32_t)tile * kTile;
     };
     auto tile_off = [&](uint32_t tok, uint32_t unit) -> uint32_t {  // bytes; past the end for no page
@@ -1022,7 +1026,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       // ---- O[row][coord] += P'[row][token] V[token][coord]
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint8_t *pa_src = W == 12 && m_row >= 8 ? lds + kZeroBase + lane * 16
+        const uint8_t *pa_src = W == 12 && !KEYS_ONLY && m_row >= 8 ? lds + kZeroBase + lane * 16
                                                       : wbuf + pst_off<PB>(m_row, 4 * c + quarter);
         const uint4 pa = *reinterpret_cast<const uint4 *>(pa_src);
         half8 aop;
@@ -1297,25 +1301,36 @@ __global__ __launch_bounds__(64 * W, 1) void decode_fused_kernel(DecodeArgs a) {
   decode_fused_body<BK, NH, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, W>(a);
 }
 
-// Splits of at least this many tokens run plain decode of up to 4 heads per kv head with 12
-// waves per workgroup; shorter ones (a wave would have few tiles) keep 8.
-constexpr int kWide12MinSplit = 48 * kTile;
+// Splits of at least this many tokens run single-query decode with wider workgroups (12
+// waves for up to 4 heads per kv head; the key-only pass 16 or 12); shorter ones (a wave
+// would have few tiles) keep 8.
+constexpr int kWideMinSplit = 48 * kTile;
 
 template <int BK, bool SPARSE, bool MULTI, bool APPEND, bool PAGED = false, bool VMASK = false, bool RECORDS = true,
           bool PREFILL = false, bool QJL = false>
 hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
-  constexpr bool kCan12 = !(SPARSE || MULTI || PAGED || VMASK || PREFILL || QJL);
+  constexpr bool kKeysOnly = SPARSE && !RECORDS;
+  constexpr bool kCanWide = !(MULTI || VMASK || PREFILL || QJL) && (!SPARSE || kKeysOnly);
+  const bool wide = kCanWide && a.fplan.split_len >= kWideMinSplit;
   if (a.vg_size <= 4) {
-    if constexpr (kCan12) {
-      if (a.fplan.split_len >= kWide12MinSplit) {
-        decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, 12>
-            <<<grid, 64 * 12, 0, stream>>>(a);
+    if constexpr (kCanWide) {
+      if (wide) {
+        constexpr int W4 = kKeysOnly ? 16 : 12;
+        decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, W4>
+            <<<grid, 64 * W4, 0, stream>>>(a);
         return hipGetLastError();
       }
     }
     decode_fused_kernel<BK, 4, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, kWaves>
         <<<grid, kThreads, 0, stream>>>(a);
   } else {
+    if constexpr (kCanWide && kKeysOnly) {
+      if (wide) {
+        decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, 12>
+            <<<grid, 64 * 12, 0, stream>>>(a);
+        return hipGetLastError();
+      }
+    }
     decode_fused_kernel<BK, 8, SPARSE, MULTI, APPEND, PAGED, VMASK, RECORDS, PREFILL, QJL, kWaves>
         <<<grid, kThreads, 0, stream>>>(a);
   }

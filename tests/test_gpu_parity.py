@@ -487,6 +487,9 @@ def _paged_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, x_dtyp
     # token of the fused step falling into a hole
     ("llama8k", 3, 16, 4, 64, [300, 450, 129], 4, None, [(0, s) for s in range(6)] + [(1, 1), (1, 7), (2, 2)], True),
     ("batch32k", 2, 8, 2, 64, [640, 200], 3, "f16", [(0, 0), (0, 9), (1, 3)], False),
+    # splits of 3072+ tokens over pages: 12 waves per workgroup, plain and fused step
+    ("batch32k", 32, 32, 8, 256, [3200] * 30 + [1500, 0], 3, None, [(3, 2)], False),
+    ("llama8k", 32, 16, 8, 256, [3200 - 50 * i for i in range(32)], 4, None, [(5, 12)], True),
 ])
 def test_paged_cache_matches_contiguous_and_oracle(case, signs, golden_codebooks):
     name, batch, hq, hkv, page, lens, bk, xdt, hole, fused = case
@@ -566,6 +569,8 @@ def _paged_ext_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, n_
     ("batch32k", 2, 8, 2, 256, [1300, 513], 3, 1, 1e-3, [(1, 1)]),
     ("llama8k", 3, 16, 4, 64, [300, 450, 129], 4, 1, 1e-2, [(0, s) for s in range(6)] + [(1, 1), (1, 6)]),
     ("ctx131k", 1, 16, 2, 64, [4000], 4, 1, 1e-3, [(0, 3), (0, 40)]),
+    # long splits: the paged key pass with 12 waves (8-head groups)
+    ("ctx131k", 32, 64, 8, 256, [3200] * 31 + [700], 4, 1, 1e-4, [(2, 4)]),
 ])
 def test_paged_multi_query_and_sparse_v(case, signs, golden_codebooks):
     name, batch, hq, hkv, page, lens, bk, n_q, tau, holes = case
@@ -672,6 +677,9 @@ def test_decode_empty_context(signs, golden_codebooks):
     ("llama8k", 1, 2, 2, 333, 384, 8, 8, 1e-3),
     ("ctx131k", 1, 16, 1, 600, 640, 4, 3, 1e-3),
     ("llama8k", 1, 6, 2, 500, 512, 4, 4, 1e-3),
+    # splits of 3072+ tokens: the key pass runs 16 waves (4-head groups) or 12 (8-head groups)
+    ("batch32k", 32, 32, 8, 3100, 3136, 3, 2, 1e-3),
+    ("ctx131k", 32, 64, 8, 3100, 3136, 4, 2, 1e-4),
 ])
 def test_decode_sparse_v_matches_oracle(case, signs, golden_codebooks):
     name, *shape, tau = case
