@@ -475,6 +475,9 @@ int tq_quantize_append(const tq_cache *c, const void *x, int x_dtype, int start_
   if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
   if ((long)start_pos + n_tokens > c->capacity) return TQ_ERR_CAPACITY;
   if (n_tokens == 0) return TQ_OK;
+  if (n_tokens <= kSmallAppendMax)  // decode steps and short drafts: one wave per token
+    return hip_status(launch_append_small_one(view_of(c), c->batch, x, x_dtype, start_pos, n_tokens,
+                                              static_cast<hipStream_t>(hip_stream)));
   return hip_status(launch_quantize(view_of(c), c->batch, x, x_dtype, start_pos, n_tokens,
                                     static_cast<hipStream_t>(hip_stream)));
 }

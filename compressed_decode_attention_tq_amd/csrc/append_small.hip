@@ -106,18 +106,20 @@ __device__ void append_plane(const CacheView &c, const void *x, int b, int h, in
   }
 }
 
-// block z < batch * Hkv: key plane (b, h) = (z / Hkv, z % Hkv); the rest: value planes.
-// One wave per token: blockDim = 64 n_tokens.
+// block z = z0 + blockIdx.x < batch * Hkv: key plane (b, h) = (z / Hkv, z % Hkv); the rest:
+// value planes (z0 = batch * Hkv and kc = vc appends to one value cache alone).  One wave per
+// token: blockDim = 64 n_tokens.
 template <int DTYPE, int BK, int BV>
 __global__ __launch_bounds__(64 * kSmallAppendMax) void append_small_kernel(CacheView kc, CacheView vc,
                                                                            const void *__restrict__ xk,
                                                                            const void *__restrict__ xv,
-                                                                           int start_pos, int n_tokens, int batch) {
+                                                                           int start_pos, int n_tokens, int batch,
+                                                                           int z0) {
   __shared__ SmallLds sh;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int planes = batch * kc.n_kv_heads;
-  const int z = blockIdx.x;
+  const int z = z0 + (int)blockIdx.x;
   if (z < planes)
     append_plane<DTYPE, BK, true>(kc, xk, z / kc.n_kv_heads, z % kc.n_kv_heads, start_pos, n_tokens, wave, lane, sh);
   else
@@ -225,24 +227,24 @@ void launch_paged1(const CacheView &kc, const CacheView &vc, const PagedLaunch &
 
 template <int DTYPE, int BK>
 hipError_t launch_bv(const CacheView &kc, const CacheView &vc, int grid, const void *xk, const void *xv,
-                     int start_pos, int n_tokens, int batch, hipStream_t stream) {
+                     int start_pos, int n_tokens, int batch, int z0, hipStream_t stream) {
   switch (vc.bits) {
-    case 2: append_small_kernel<DTYPE, BK, 2><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
-    case 3: append_small_kernel<DTYPE, BK, 3><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
-    case 4: append_small_kernel<DTYPE, BK, 4><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
-    default: append_small_kernel<DTYPE, BK, 8><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch); break;
+    case 2: append_small_kernel<DTYPE, BK, 2><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch, z0); break;
+    case 3: append_small_kernel<DTYPE, BK, 3><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch, z0); break;
+    case 4: append_small_kernel<DTYPE, BK, 4><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch, z0); break;
+    default: append_small_kernel<DTYPE, BK, 8><<<grid, 64 * n_tokens, 0, stream>>>(kc, vc, xk, xv, start_pos, n_tokens, batch, z0); break;
   }
   return hipGetLastError();
 }
 
 template <int DTYPE>
 hipError_t launch_bk(const CacheView &kc, const CacheView &vc, int grid, const void *xk, const void *xv,
-                     int start_pos, int n_tokens, int batch, hipStream_t stream) {
+                     int start_pos, int n_tokens, int batch, int z0, hipStream_t stream) {
   switch (kc.bits) {
-    case 2: return launch_bv<DTYPE, 2>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
-    case 3: return launch_bv<DTYPE, 3>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
-    case 4: return launch_bv<DTYPE, 4>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
-    default: return launch_bv<DTYPE, 8>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, stream);
+    case 2: return launch_bv<DTYPE, 2>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, z0, stream);
+    case 3: return launch_bv<DTYPE, 3>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, z0, stream);
+    case 4: return launch_bv<DTYPE, 4>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, z0, stream);
+    default: return launch_bv<DTYPE, 8>(kc, vc, grid, xk, xv, start_pos, n_tokens, batch, z0, stream);
   }
 }
 
@@ -269,9 +271,21 @@ hipError_t launch_append_small(const CacheView &kc, const CacheView &vc, int bat
     return hipErrorInvalidValue;
   const long grid = 2L * batch * kc.n_kv_heads;
   if (grid < 1 || grid > 0x7fffffffL) return hipErrorInvalidValue;
-  if (x_dtype == TQ_F32) return launch_bk<TQ_F32>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
-  if (x_dtype == TQ_BF16) return launch_bk<TQ_BF16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
-  return launch_bk<TQ_F16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, stream);
+  if (x_dtype == TQ_F32) return launch_bk<TQ_F32>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, 0, stream);
+  if (x_dtype == TQ_BF16) return launch_bk<TQ_BF16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, 0, stream);
+  return launch_bk<TQ_F16>(kc, vc, (int)grid, xk, xv, start_pos, n_tokens, batch, 0, stream);
+}
+
+hipError_t launch_append_small_one(const CacheView &c, int batch, const void *x, int x_dtype, int start_pos,
+                                   int n_tokens, hipStream_t stream) {
+  if (n_tokens < 1 || n_tokens > kSmallAppendMax) return hipErrorInvalidValue;
+  const long planes = (long)batch * c.n_kv_heads;
+  if (planes < 1 || planes > 0x3fffffffL) return hipErrorInvalidValue;
+  // the key path for a row cache (blocks 0 .. planes - 1), the value path for a group cache
+  const int z0 = c.layout == TQ_LAYOUT_ROWS ? 0 : (int)planes;
+  if (x_dtype == TQ_F32) return launch_bk<TQ_F32>(c, c, (int)planes, x, x, start_pos, n_tokens, batch, z0, stream);
+  if (x_dtype == TQ_BF16) return launch_bk<TQ_BF16>(c, c, (int)planes, x, x, start_pos, n_tokens, batch, z0, stream);
+  return launch_bk<TQ_F16>(c, c, (int)planes, x, x, start_pos, n_tokens, batch, z0, stream);
 }
 
 }  // namespace tq

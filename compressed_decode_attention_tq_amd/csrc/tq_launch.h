@@ -142,6 +142,9 @@ hipError_t launch_quantize_kv(const CacheView &kc, const CacheView &vc, int batc
 // one block per (batch, kv head, key or value) plane, one wave per token.
 hipError_t launch_append_small(const CacheView &kc, const CacheView &vc, int batch, const void *xk,
                                const void *xv, int x_dtype, int start_pos, int n_tokens, hipStream_t stream);
+// The same for one cache (x is [batch][n_tokens][n_kv_heads][d]): its layout picks the path.
+hipError_t launch_append_small_one(const CacheView &c, int batch, const void *x, int x_dtype, int start_pos,
+                                   int n_tokens, hipStream_t stream);
 // Appends to paged caches (views of the page pools, capacity = page_tokens): token j of
 // sequence b at position start_pos[b] + j; one block per aligned 8-token window of one
 // (sequence, kv head, key or value), one wave per token.

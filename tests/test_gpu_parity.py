@@ -113,13 +113,16 @@ def test_quantize_append_kv_equals_two_appends(bits_k, bits_v, dtype, signs, gol
         parity.check_quantize(one[1], parity.to_f64(g["v"]), 0, s64, _table(golden_codebooks, bits_v))
 
 
-@pytest.mark.parametrize("bits_k,bits_v,dtype", [(4, 2, "bf16"), (3, 2, "f32"), (2, 4, "f16"), (8, 3, "bf16"),
-                                                (4, 8, "f32")])
-def test_small_appends_match_oracle(bits_k, bits_v, dtype, signs, golden_codebooks):
+@pytest.mark.parametrize("bits_k,bits_v,dtype,single", [(4, 2, "bf16", False), (3, 2, "f32", False),
+                                                       (2, 4, "f16", False), (8, 3, "bf16", False),
+                                                       (4, 8, "f32", False), (3, 2, "bf16", True),
+                                                       (4, 3, "f16", True), (8, 2, "f32", True)])
+def test_small_appends_match_oracle(bits_k, bits_v, dtype, single, signs, golden_codebooks):
     """Appends of 1..8 tokens (one wave per plane, tokens in order) against the oracle, over
     ranges that start, end and cross inside 8-token value groups; everything outside the
-    written positions keeps its stale contents."""
-    _say("small appends", bits_k, bits_v, dtype)
+    written positions keeps its stale contents.  `single`: each cache through its own
+    tq_quantize_append call (the same kernel, one cache)."""
+    _say("small appends", bits_k, bits_v, dtype, single)
     w = inputs.WORKLOADS["llama8k"]
     g = inputs.generate(w, device="cpu", batch=2, ctx=61, n_kv_heads=3, with_query=False)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
@@ -131,7 +134,11 @@ def test_small_appends_match_oracle(bits_k, bits_v, dtype, signs, golden_codeboo
     edges = [0, 1, 4, 12, 13, 21, 22, 30, 37, 45, 46, 53, 61]
     for a, e in zip(edges[:-1], edges[1:]):
         assert 1 <= e - a <= 8
-        tq.quantize_append_kv(kc, vc, k[:, a:e].contiguous().to(DEV), v[:, a:e].contiguous().to(DEV), a)
+        if single:
+            tq.quantize_append(kc, k[:, a:e].contiguous().to(DEV), a)
+            tq.quantize_append(vc, v[:, a:e].contiguous().to(DEV), a)
+        else:
+            tq.quantize_append_kv(kc, vc, k[:, a:e].contiguous().to(DEV), v[:, a:e].contiguous().to(DEV), a)
     torch.cuda.synchronize()
     s64 = signs.numpy().astype(np.float64)
     parity.check_quantize(kc, parity.to_f64(k), 0, s64, _table(golden_codebooks, bits_k))
