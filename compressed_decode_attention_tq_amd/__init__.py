@@ -34,7 +34,7 @@ class CacheStruct(ctypes.Structure):
         ("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
-        ("boundaries", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+        ("boundaries", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("table_scale", ctypes.c_float),
     ]
 
 
@@ -50,6 +50,7 @@ class PagedCacheStruct(ctypes.Structure):
         ("n_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
         ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+        ("table_scale", ctypes.c_float),
     ]
 
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.tq_make_codebook_table.argtypes = [i32, i32, vp, vp]
+        L.tq_value_table_scale.argtypes = [vp, i32]
+        L.tq_value_table_scale.restype = f32
         L.tq_quantize_append.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, vp]
         L.tq_quantize_append_kv.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp,
                                             i32, i32, i32, vp]
@@ -134,6 +137,12 @@ def _codebook_table(d: int, bits: int):
     t = np.zeros(max((1 << bits) - 1, 1), dtype=np.float32)
     _check(lib().tq_make_codebook_table(d, bits, c.ctypes.data, t.ctypes.data), "tq_make_codebook_table")
     return c, t[: (1 << bits) - 1]
+
+
+def value_table_scale(centroids) -> float:
+    """Host call: the table_scale for a cache with these fp32 centroids (1.0 when none applies)."""
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    return float(lib().tq_value_table_scale(c.ctypes.data, int(c.size)))
 
 
 def code_bytes(d: int, bits: int, batch: int, n_kv_heads: int, capacity: int) -> int:
@@ -236,6 +245,7 @@ class PackedCache:
         c, t = make_codebook_table(d, bits)
         self.centroids = torch.from_numpy(c).to(device)
         self.boundaries = torch.from_numpy(np.concatenate([t, [0.0]]).astype(np.float32)).to(device)
+        self.table_scale = value_table_scale(c)
         if signs.is_cuda and signs.dtype == torch.int8 and signs.is_contiguous():
             self.signs = signs          # shared: the K and V caches of a layer use one sign vector
         else:
@@ -244,7 +254,7 @@ class PackedCache:
     def struct(self) -> CacheStruct:
         return CacheStruct(self.d, self.bits, self.layout, self.batch, self.n_kv_heads, self.capacity,
                            self.codes.data_ptr(), self.norms.data_ptr(), self.centroids.data_ptr(),
-                           self.boundaries.data_ptr(), self.signs.data_ptr())
+                           self.boundaries.data_ptr(), self.signs.data_ptr(), self.table_scale)
 
     def plane_codes(self, b: int, h: int):
         per = self.capacity * self.d * self.bits // 8
@@ -513,6 +523,7 @@ class PagedCache:
         c, t = make_codebook_table(d, bits)
         self.centroids = torch.from_numpy(c).to(device)
         self.boundaries = torch.from_numpy(np.concatenate([t, [0.0]]).astype(np.float32)).to(device)
+        self.table_scale = value_table_scale(c)
         if signs.is_cuda and signs.dtype == torch.int8 and signs.is_contiguous():
             self.signs = signs
         else:
@@ -522,7 +533,7 @@ class PagedCache:
         return PagedCacheStruct(self.d, self.bits, self.layout, self.batch, self.n_kv_heads, self.page_tokens,
                                 self.n_pages, self.max_pages, self.codes.data_ptr(), self.norms.data_ptr(),
                                 self.block_table.data_ptr(), self.centroids.data_ptr(),
-                                self.boundaries.data_ptr(), self.signs.data_ptr())
+                                self.boundaries.data_ptr(), self.signs.data_ptr(), self.table_scale)
 
     def page_codes(self, page: int, h: int):
         per = self.page_tokens * self.d * self.bits // 8

@@ -31,6 +31,7 @@ int check_cache(const tq_cache *c) {
   if (c->d != kD) return TQ_ERR_UNSUPPORTED;
   if (!valid_bits(c->bits)) return TQ_ERR_UNSUPPORTED;
   if (c->capacity % kChunk != 0 || c->capacity > kMaxCapacity) return TQ_ERR_UNSUPPORTED;
+  if (!(c->table_scale == 0.f || (c->table_scale >= 1.f && c->table_scale <= 2.f))) return TQ_ERR_INVALID_ARG;
   return TQ_OK;
 }
 
@@ -45,6 +46,7 @@ CacheView view_of(const tq_cache *c) {
   v.layout = c->layout;
   v.n_kv_heads = c->n_kv_heads;
   v.capacity = c->capacity;
+  v.table_scale = c->table_scale > 0.f ? c->table_scale : 1.f;
   return v;
 }
 
@@ -273,6 +275,7 @@ int check_paged(const tq_paged_cache *c) {
   if (c->d != kD) return TQ_ERR_UNSUPPORTED;
   if (!valid_bits(c->bits)) return TQ_ERR_UNSUPPORTED;
   if (c->page_tokens % kChunk != 0 || c->page_tokens > kMaxCapacity) return TQ_ERR_UNSUPPORTED;
+  if (!(c->table_scale == 0.f || (c->table_scale >= 1.f && c->table_scale <= 2.f))) return TQ_ERR_INVALID_ARG;
   // 32-bit offsets in the kernels: pool code bytes below 3 GiB, positions below 2^30
   const double pool = (double)c->n_pages * c->n_kv_heads * c->page_tokens * kD * c->bits / 8;
   if (pool >= 3.0 * (1u << 30) || (double)c->max_pages * c->page_tokens >= (double)(1 << 30))
@@ -292,6 +295,7 @@ CacheView view_of_pool(const tq_paged_cache *c) {
   v.layout = c->layout;
   v.n_kv_heads = c->n_kv_heads;
   v.capacity = c->page_tokens;
+  v.table_scale = c->table_scale > 0.f ? c->table_scale : 1.f;
   return v;
 }
 

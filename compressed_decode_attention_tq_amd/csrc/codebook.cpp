@@ -132,6 +132,31 @@ bool increasing(const std::vector<double> &c) {
 
 }  // namespace
 
+extern "C" float tq_value_table_scale(const float *c, int n_levels) {
+  if (c == nullptr || n_levels != 4) return 1.f;
+  const double a = c[2], b = c[3];
+  if (!(a > 0.0) || !(b > a) || c[1] != -c[2] || c[0] != -c[3]) return 1.f;
+  const double r = b / a;
+  if (!(r < 2047.0)) return 1.f;
+  // convergents p_k / q_k of r: p_k = a_k p_{k-1} + p_{k-2}, the same for q
+  double p0 = 1.0, q0 = 0.0, p1 = std::floor(r), q1 = 1.0, x = r - p1;
+  for (int k = 0; k < 64 && x > 1e-12; ++k) {
+    x = 1.0 / x;
+    const double ak = std::floor(x);
+    x -= ak;
+    const double p2 = ak * p1 + p0, q2 = ak * q1 + q0;
+    if (p2 > 2047.0) break;
+    p0 = p1;
+    q0 = q1;
+    p1 = p2;
+    q1 = q2;
+  }
+  // q 2^j in [a, 2a)
+  const double qj = q1 * std::exp2(std::floor(std::log2(a / q1)));
+  const double s = (qj < a ? 2.0 * qj : qj) / a;
+  return (float)s;
+}
+
 extern "C" int tq_make_codebook_table(int d, int bits, float *centroids, float *boundaries) {
   if (centroids == nullptr || boundaries == nullptr || d < 4) return TQ_ERR_INVALID_ARG;
   if (bits < 1 || bits > 8) return TQ_ERR_UNSUPPORTED;

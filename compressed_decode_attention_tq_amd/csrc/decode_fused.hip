@@ -507,7 +507,13 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           if (vlive(h)) tmx[h] = a.tile_max[vrow(h) * a.tile_stride + (t_begin >> 6) + tile_k];
       }
     }
-    build_tables<BK, !SPARSE>(lds, kcs, vcs);  // read only after the barriers below
+    // value centroids scaled by the cache's table scale, chosen so that the fp16 table holds
+    // them almost exactly (taken off the output at merge)
+    const float vscale = SPARSE ? 1.f : a.v.table_scale;
+    float vcs_s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vcs_s[i] = vcs[i] * vscale;
+    build_tables<BK, !SPARSE>(lds, kcs, vcs_s);  // read only after the barriers below
     if constexpr (QJL) build_sign_table(lds);
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
     // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
@@ -1117,10 +1123,10 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           }
         }
         l = wave_reduce<false>(l);
-        if constexpr (!VMASK) {  // (VMASK partials are final weights already)
-          o0 /= l;
-          o1 /= l;
-        }
+        // (VMASK partials are final weights already); the value table's scale comes off here
+        const float norm = VMASK ? 1.f / a.v.table_scale : 1.f / (a.v.table_scale * l);
+        o0 *= norm;
+        o1 *= norm;
       }
       // inverse rotation: x = s * (H y) / sqrt(128)
       float y0 = o0 + o1, y1 = o0 - o1;

@@ -24,6 +24,7 @@ struct CacheView {
   int layout;
   int n_kv_heads;
   int capacity;
+  float table_scale;  // value centroids in the fp16 operand table are scaled by this (1: none)
   __host__ __device__ size_t code_plane_bytes() const { return (size_t)capacity * kD * bits / 8; }
   __device__ uint8_t *plane(int b, int h) const {
     return codes + ((size_t)b * n_kv_heads + h) * code_plane_bytes();

@@ -84,6 +84,11 @@ enum tq_layout { TQ_LAYOUT_ROWS = 0, TQ_LAYOUT_GROUP8 = 1 };
  *               -boundaries[j] and boundaries[L/2-1] = 0 (L = 1 << bits)
  *   signs       [d] int8, each +1 or -1, 16-byte aligned: the diagonal of the rotation
  *               (shared by the K and V caches of a layer)
+ *   table_scale 0 (none), or a factor s in [1, 2] that the matrix-core decode kernels apply
+ *               to the value centroids of their fp16 operand table and take off the output
+ *               again; tq_value_table_scale() gives one for which a 4-level codebook is held
+ *               almost exactly in fp16 (about 1e-6 relative instead of 2^-12).  Only a value
+ *               cache's is read.  Results do not depend on it beyond that rounding.
  * capacity must be a positive multiple of 64. */
 typedef struct tq_cache {
   int32_t d;
@@ -97,6 +102,7 @@ typedef struct tq_cache {
   const float *centroids;
   const float *boundaries;
   const int8_t *signs;
+  float table_scale;
 } tq_cache;
 
 /* The QJL sign sketch that accompanies a key cache in the residual variant ([google] §第二步：
@@ -127,6 +133,13 @@ typedef struct tq_qjl_sketch {
  *   boundaries  host out [(1 << bits) - 1], midpoints of adjacent centroids
  * Errors: TQ_ERR_INVALID_ARG (null pointer, d < 4), TQ_ERR_UNSUPPORTED (bits outside 1..8). */
 int tq_make_codebook_table(int d, int bits, float *centroids, float *boundaries);
+
+/* Host only: the table_scale for a cache with these centroids (host memory, n_levels of
+ * them).  For a symmetric 4-level codebook {-b, -a, a, b}: with p/q the best convergent of the
+ * continued fraction of b/a whose p is below 2048, s = q 2^j / a in [1, 2), so that s a = q 2^j
+ * and s b = p 2^j up to that convergent's error are both fp16 values.  1 for any other
+ * codebook (no scale).  Never fails. */
+float tq_value_table_scale(const float *centroids, int n_levels);
 
 /* Quantize n_tokens new tokens of every (batch, kv head) into cache positions
  * [start_pos, start_pos + n_tokens) ([tq-80] §核心创新; [inferrs] §核心技术):
@@ -297,7 +310,7 @@ size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_h
  *                decode leaves them out of the softmax (no score, no value; nothing is read
  *                outside the pool); a sequence with no position on a page gets o = 0 and
  *                LSE = -inf
- *   centroids, boundaries, signs as for tq_cache.
+ *   centroids, boundaries, signs, table_scale as for tq_cache.
  * page_tokens: a positive multiple of 64.  The pool's code bytes must stay below 3 GiB
  * (32-bit offsets inside the decode kernel).  The K and V caches of a layer share one
  * block table. */
@@ -316,6 +329,7 @@ typedef struct tq_paged_cache {
   const float *centroids;
   const float *boundaries;
   const int8_t *signs;
+  float table_scale;
 } tq_paged_cache;
 
 /* Quantize n_tokens new tokens of every sequence into a paged key cache (ROWS) and value

@@ -40,6 +40,33 @@ def test_host_codebook_equals_oracle_table(bits, golden_codebooks):
     assert np.array_equal(t, gt.astype(np.float32))
 
 
+def test_value_table_scale_makes_both_magnitudes_fp16_exact():
+    """tq_value_table_scale: for the 2-bit tables, s in [1, 2) makes s a an fp16 value and
+    leaves s b off an fp16 value by no more than the best rational approximation p/q of b/a with
+    p < 2048 allows (brute force over every q), far below fp16's 2^-12; any other codebook
+    gets 1."""
+    for d in (64, 128, 256, 512):
+        c, _ = tq.make_codebook_table(d, 2)
+        s = tq.value_table_scale(c)
+        assert 1.0 <= s < 2.0
+        a, b = float(np.float32(c[2])), float(np.float32(c[3]))
+        r = b / a
+        best = min(abs(r - round(r * q) / q) / r for q in range(1, 2048) if round(r * q) <= 2047)
+        sa, sb = np.float32(s) * np.float32(a), np.float32(s) * np.float32(b)
+        assert abs(float(np.float16(sa)) - float(sa)) <= 1e-7 * float(sa), d
+        assert abs(float(np.float16(sb)) - float(sb)) <= (best + 2e-7) * float(sb), (d, best)
+        assert best < 2.0 ** -12
+    assert tq.value_table_scale(tq.make_codebook_table(128, 3)[0]) == 1.0
+    assert tq.value_table_scale(np.array([-0.2, -0.05, 0.04, 0.2], np.float32)) == 1.0   # not symmetric
+    assert tq.value_table_scale(np.array([-3.0, -1.0, 1.0, 3.0], np.float32)) == 1.0     # both exact already
+    assert tq.value_table_scale(np.array([-0.3, -0.1, 0.1, 0.3], np.float32)) == 1.25    # 3/1: s a = 1/8
+
+
+def test_cache_table_scale_validation():
+    for bad in (-1.0, 0.5, 2.5, float("nan"), float("inf")):
+        assert _quant(_cache(table_scale=bad)) == tq.TQ_ERR_INVALID_ARG, bad
+
+
 def test_codebook_argument_errors():
     c = np.zeros(16, np.float32)
     L = tq.lib()
@@ -68,11 +95,11 @@ FAKE = 0x7F0000000000
 def _cache(**kw):
     base = dict(d=128, bits=4, layout=0, batch=1, n_kv_heads=2, capacity=1024,
                 codes=FAKE, norms=FAKE + 0x100000, centroids=FAKE + 0x200000,
-                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000)
+                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000, table_scale=0.0)
     base.update(kw)
     return tq.CacheStruct(base["d"], base["bits"], base["layout"], base["batch"], base["n_kv_heads"],
                           base["capacity"], base["codes"], base["norms"], base["centroids"],
-                          base["boundaries"], base["signs"])
+                          base["boundaries"], base["signs"], base["table_scale"])
 
 
 def _quant(cache, x=FAKE + 0x500000, dtype=1, start=0, n=16):
@@ -272,7 +299,7 @@ def test_qjl_argument_validation():
 def _paged(**kw):
     base = dict(d=128, bits=4, layout=0, batch=2, n_kv_heads=2, page_tokens=256, n_pages=64, max_pages=16,
                 codes=FAKE, norms=FAKE + 0x1000000, block_table=FAKE + 0x1100000, centroids=FAKE + 0x200000,
-                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000)
+                boundaries=FAKE + 0x300000, signs=FAKE + 0x400000, table_scale=0.0)
     base.update(kw)
     return tq.PagedCacheStruct(*(base[f] for f, _ in tq.PagedCacheStruct._fields_))
 
@@ -295,6 +322,7 @@ def test_paged_argument_validation():
     assert app(_paged(block_table=0), v) == tq.TQ_ERR_INVALID_ARG
     assert app(_paged(block_table=FAKE + 0x1100002), v) == tq.TQ_ERR_INVALID_ARG
     assert app(_paged(max_pages=32), v) == tq.TQ_ERR_INVALID_ARG         # tables differ
+    assert app(k, _paged(layout=1, bits=2, table_scale=3.0)) == tq.TQ_ERR_INVALID_ARG
     assert app(_paged(n_pages=1 << 20, page_tokens=64, n_kv_heads=8),
                _paged(n_pages=1 << 20, page_tokens=64, n_kv_heads=8, layout=1, bits=2)) == tq.TQ_ERR_UNSUPPORTED
     ws = tq.paged_decode_workspace_bytes(2, 16, 2, 4096)
