@@ -962,7 +962,7 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": QUANTIZE_KERNEL + " (32 launches per step, K and V of one layer each)",
-                     "bytes_per_launch": (in_bytes + out_bytes) / (2 * layers)},
+                     "bytes_per_launch": (in_bytes + out_bytes) / layers},
         "_kernel": "quantize",
         "_launches": layers,
     }
