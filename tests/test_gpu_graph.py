@@ -19,16 +19,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("workload,tau", [("llama8k", 0.0), ("ctx131k", 0.0), ("batch32k", 1e-4)])
-def test_graph_replays_match_eager(workload, tau):
-    print("graph", workload, tau, flush=True)
+@pytest.mark.parametrize("workload,tau,batch,ctx", [
+    ("llama8k", 0.0, 2, 2048 + 37), ("ctx131k", 0.0, 2, 2048 + 37), ("batch32k", 1e-4, 2, 2048 + 37),
+    # splits of 3072+ tokens: 12 waves per workgroup (dense), 16 and 12 in the key pass
+    ("batch32k", 0.0, 32, 3100), ("batch32k", 1e-4, 32, 3100), ("ctx131k", 1e-4, 64, 6200),
+])
+def test_graph_replays_match_eager(workload, tau, batch, ctx):
+    print("graph", workload, tau, batch, ctx, flush=True)
     sys.stdout.flush()
     w = inputs.WORKLOADS[workload]
-    batch, hkv, ctx = 2, w.n_kv_heads, 2048 + 37
+    hkv = w.n_kv_heads
     hq = hkv * w.group
     g = inputs.generate(w, device=DEV, batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
     signs = inputs.rotation_signs().to(DEV)
-    cap = 2112
+    cap = (ctx + 63) // 64 * 64 + 64
     caches = []
     for _ in range(2):
         kc = tq.PackedCache(batch, hkv, cap, w.bits_k, tq.LAYOUT_ROWS, signs, device=DEV)

@@ -715,6 +715,19 @@ def test_decode_is_deterministic(signs):
         b = tq.decode_attn(kc, vc, q, 900, 0.0884, tau=tau).out.clone()
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+    # 256 planes, splits of 3072+ tokens: the 12-wave decode and the 16-wave key pass
+    w = inputs.WORKLOADS["batch32k"]
+    g = inputs.generate(w, device="cpu", batch=32, ctx=3100, n_kv_heads=8, n_q_heads=32)
+    kc = _new_cache(32, 8, 3136, 3, 0, signs)
+    vc = _new_cache(32, 8, 3136, 2, 1, signs)
+    _fill(kc, g["k"].to(DEV))
+    _fill(vc, g["v"].to(DEV))
+    q = g["q"].to(DEV)
+    for tau in (0.0, 1e-3):
+        a = tq.decode_attn(kc, vc, q, 3100, 0.0884, tau=tau).out.clone()
+        b = tq.decode_attn(kc, vc, q, 3100, 0.0884, tau=tau).out.clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
 
 
 def test_stream_read_probe_runs():
