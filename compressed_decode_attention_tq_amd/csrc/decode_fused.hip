@@ -336,13 +336,24 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   }
 
   {  // one split of one (batch, kv head) per workgroup
-    const int item = blockIdx.x;
     const int VGB = PREFILL ? (VG + kWaves - 1) / kWaves : VG;  // items per (batch, kv head, split)
-    const int split = item % S;
-    const int vgb = (item / S) % VGB;
+    // Work item -> (unit u = (b, kv head, split), row-group item vgb).  With several row-group
+    // items per unit they read the same tiles: workgroups are dealt to the 8 XCDs round robin
+    // by their index, so the items of one unit get indices congruent to u mod 8 (all on one
+    // XCD, whose L2 then serves the repeated reads): item = (vgb * G + u / 8) * 8 + u % 8,
+    // G = ceil(units / 8), indices past the last unit idle.
+    int u = blockIdx.x, vgb = 0;
+    if (VGB > 1) {
+      const int units = a.batch * a.n_kv_heads * S, G = (units + 7) / 8;
+      const int lo = (int)blockIdx.x & 7, hi = (int)blockIdx.x >> 3;
+      vgb = hi / G;
+      u = (hi - vgb * G) * 8 + lo;
+      if (u >= units || vgb >= VGB) return;  // (uniform: before any barrier or store)
+    }
+    const int split = u % S;
     const int vgi = PREFILL ? vgb * kWaves + wave : vgb;  // PREFILL: each wave its own row group
-    const int kvh = (item / (S * VGB)) % a.n_kv_heads;
-    const int b = item / (S * VGB * a.n_kv_heads);
+    const int kvh = (u / S) % a.n_kv_heads;
+    const int b = u / (S * a.n_kv_heads);
     const bool wave_on = !PREFILL || vgi < VG;
     int T = a.ctx_len;
     if (a.seq_lens != nullptr) T = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.ctx_len));
@@ -1364,7 +1375,9 @@ hipError_t launch_decode_fused(const DecodeArgs &a, int n_cu, hipStream_t stream
   (void)n_cu;
   // prefill: one workgroup per 8 row groups (one per wave)
   const long vg_items = a.prefill ? (a.vgroups + kWaves - 1) / kWaves : a.vgroups;
-  const long items = (long)a.batch * a.n_kv_heads * vg_items * a.fplan.n_splits;
+  const long units = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  // several row-group items per unit: units padded to a multiple of 8 (XCD grouping)
+  const long items = vg_items > 1 ? vg_items * ((units + 7) / 8) * 8 : units;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
   const int grid = (int)items;
   return a.k.bits == 4 ? launch_bk<4, false>(a, grid, stream) : launch_bk<3, false>(a, grid, stream);
@@ -1383,7 +1396,8 @@ hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   if (a.n_q > 1 || a.vgroups > 1) {  // several query positions (one row group per work item)
     if (a.xk != nullptr) return hipErrorInvalidValue;
-    const long items = (long)a.batch * a.n_kv_heads * a.vgroups * a.fplan.n_splits;
+    const long units = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+    const long items = a.vgroups > 1 ? (long)a.vgroups * ((units + 7) / 8) * 8 : units;
     if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
     return a.k.bits == 4 ? launch_nh<4, false, true, false, true>(a, (int)items, stream)
                          : launch_nh<3, false, true, false, true>(a, (int)items, stream);
