@@ -1006,16 +1006,41 @@ def _short(name: str) -> str:
     return n.split("(")[0][:90]
 
 
+def _trace_medians(d):
+    """Median duration (ns) per kernel from the run's kernel trace (csv, or csv.gz), if kept."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv*"), recursive=True)
+    if not files:
+        return {}
+    import gzip
+    opener = gzip.open if files[0].endswith(".gz") else open
+    durs = {}
+    with opener(files[0], "rt") as fh:
+        for r in csv.DictReader(fh):
+            durs.setdefault(_short(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for k, v in durs.items():
+        v.sort()
+        out[k] = v[len(v) // 2]
+    return out
+
+
 def summarize_stats(args):
-    """Kernel table of a `rocprofv3 --kernel-trace --stats --output-format csv` run."""
+    """Kernel table of a `rocprofv3 --kernel-trace --stats --output-format csv` run: calls, mean,
+    median (from the kernel trace: the mean also counts the slower first replays after a graph
+    capture or a cache flush), min, max and share of the time."""
     files = glob.glob(os.path.join(args.summarize_stats, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         sys.exit(f"no kernel_stats.csv under {args.summarize_stats}")
     rows = list(csv.DictReader(open(files[0])))
+    med = _trace_medians(args.summarize_stats)
     lines = [f"# {args.name}", "", f"command: {args.command}", "",
-             f"{'kernel':90s} {'calls':>7s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} {'total %':>8s}"]
+             f"{'kernel':90s} {'calls':>7s} {'avg us':>10s} {'median us':>10s} {'min us':>10s} {'max us':>10s} "
+             f"{'total %':>8s}"]
     for r in rows:
-        lines.append(f"{_short(r['Name']):90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+        m = med.get(_short(r["Name"]))
+        ms = f"{m / 1e3:10.2f}" if m is not None else f"{'-':>10s}"
+        lines.append(f"{_short(r['Name']):90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {ms} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
     out = "\n".join(lines) + "\n"
     with open(os.path.join(ROOT, "profiles", f"{args.name}.txt"), "w") as fh:
