@@ -9,7 +9,9 @@
 //
 //   * Work unit: one workgroup (8 waves, all 160 KB of LDS, so one resident per CU) owns one
 //     contiguous split of one (batch, kv head) context; the plan makes about one split per
-//     CU.  The waves take the split's 64-token tiles in turn.
+//     CU.  The waves take the split's 64-token tiles in turn.  Long splits take wider
+//     workgroups: 12 waves for groups of up to 4 heads (2 KB wave buffers, 153 KB of LDS),
+//     and in the key-only pass 16 (4 heads) or 12 (8 heads).
 //   * The query group is rotated once per split: wave h applies the signs and the
 //     Walsh-Hadamard butterflies to head h (two coordinates per lane, lane exchanges for the
 //     upper six stages) and leaves R q in LDS for all waves.
@@ -27,7 +29,7 @@
 //     reference of a head only moves when a tile would push p * ||v|| past the fp16 range,
 //     so the value accumulator is rarely rescaled.  The value product takes P' = p * ||v||
 //     split the same way into a fp16 row and a remainder row.
-//   * End of split: the 8 waves combine (m, l, O) through LDS; the workgroup writes one
+//   * End of split: the waves combine (m, l, O) through LDS; the workgroup writes one
 //     partial per query head and bumps a per-(batch, kv head) arrival counter.  The last
 //     workgroup to arrive merges the partials, applies the inverse rotation and writes the
 //     output and log-sum-exp, then clears the counter for the next call.
@@ -35,9 +37,11 @@
 //     are (position, head) pairs, up to 8 per work item, and each row sees the cache up to
 //     its own position (a mask in the tiles that reach past the first query's position).
 //   * Sparse V first pass (SPARSE): no value loads or products.  Each wave keeps an exact
-//     running maximum per head and writes every token whose score reaches it + log2(tau)
-//     as a candidate record of the second pass's split; the split's (m, l) become partials
-//     for the second pass and the merge (separate kernels).
+//     running maximum per head and writes the largest score of each of its tiles per head;
+//     the split's (m, l) become the partials the masked value pass (VMASK) merges into each
+//     head's final LSE, and that pass visits only the tiles whose maximum reaches some head's
+//     threshold.  (With RECORDS, the key pass also writes every token whose score reaches its
+//     wave's running maximum + log2(tau) as a candidate record for the vector second pass.)
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
@@ -280,8 +284,9 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
 // pass; without, it writes only the (m, l) partials and the per-tile maxima the masked value
 // pass reads.
 // The key pass without records needs only the key table and the score staging: its LDS is the
-// 64 KB table plus 2 KB per wave (80 KB).  (Two such workgroups per CU, 4 waves per SIMD at 128
-// VGPRs, made the pass slower: 22 -> 28 us on the 131072-token workload, with spills.)
+// 64 KB table plus 2 KB per wave (80 KB with 8 waves).  (Two such workgroups per CU, 4 waves per
+// SIMD at 128 VGPRs forced, made the pass slower: 22 -> 28 us on the 131072-token workload, with
+// spills; one workgroup of 16 or 12 waves at the VGPRs the pass needs anyway made it faster.)
 // PREFILL (with MULTI): several query positions with many row groups per kv head (a prefill
 // chunk).  The 8 waves of a workgroup take 8 row groups, not 8 slices of the tiles: every wave
 // walks all tiles of the split for its own rows, so the workgroup reads each tile of keys and
@@ -1204,7 +1209,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       return;
     }
 
-    // ---- combine the 8 waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
+    // ---- combine the waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
     //      the start of the key-table region (free once every wave is past its tiles), so
     //      that round 2 can write the staging buffers while other waves still read them.
     float ltot[NH2];
