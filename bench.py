@@ -201,7 +201,7 @@ def main():
         stream = stream_read_gbs(torch, tq, log)
         result["roofline"]["stream_read_gbs"] = stream
         result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
-        result.pop("_kernel", None)
+        result["roofline"]["traffic"] = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
         result["sources_digest"] = digest
         print(json.dumps(result), flush=True)
         return
@@ -716,7 +716,7 @@ def cpu_baseline_qjl(w, cache, host_k, q, signs, proj, np, log):
 
 def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):
     """Inner-product nearest-neighbour search: a step is one tq_ip_search call for the
-    queries over the whole quantized database (score, chunk top-k and merge kernels)."""
+    queries over the whole quantized database (scores with block top-k, then the final top-k)."""
     n, nq, k, bits = spec["n"], spec["n_queries"], spec["top_k"], spec["bits"]
     per_copy = tq.code_bytes(D, bits, 1, 1, n) + 2 * n
     copies = args.copies or min(MAX_COPIES, max(1, math.ceil(600e6 / per_copy)))
@@ -758,9 +758,10 @@ def bench_search(args, spec, signs, dev, tq, inputs, torch, np, log):
         "recall_at_k_vs_exact": recall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "search call (ip_score_kernel, topk_chunk_kernel, topk_merge_kernel)",
+                     "kernel": "search call (ip_score_kernel, topk_final_kernel)",
                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
                      "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
+        "_kernel": "ip_search",
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_search(spec, dbs[0], q, signs, np, torch, log)

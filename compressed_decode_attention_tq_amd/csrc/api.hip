@@ -238,21 +238,17 @@ WorkspaceLayout workspace_layout_paged_ext(int batch, int n_q_heads, int n_kv_he
 }
 
 struct SearchLayout {
-  size_t cand_s0, cand_i0, cand_s1, cand_i1, total;
+  size_t cand, bnd, total;
 };
 
 SearchLayout search_layout(int n_q, int n, int k) {
-  const size_t n_cand = (size_t)n_q * ((n + kSearchBlock - 1) / kSearchBlock) * k;
+  const size_t blocks = (size_t)n_q * ((n + kSearchBlock - 1) / kSearchBlock);
   SearchLayout w{};
   size_t off = 0;
-  w.cand_s0 = off;
-  off = align_up(off + n_cand * sizeof(float), 256);
-  w.cand_i0 = off;
-  off = align_up(off + n_cand * sizeof(int32_t), 256);
-  w.cand_s1 = off;
-  off = align_up(off + n_cand * sizeof(float), 256);
-  w.cand_i1 = off;
-  off = align_up(off + n_cand * sizeof(int32_t), 256);
+  w.cand = off;
+  off = align_up(off + blocks * k * sizeof(uint64_t), 256);
+  w.bnd = off;
+  off = align_up(off + blocks * sizeof(uint2), 256);
   w.total = off;
   return w;
 }
@@ -860,9 +856,8 @@ int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, 
   if (workspace == nullptr || !aligned(workspace, 256)) return TQ_ERR_INVALID_ARG;
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);
-  return hip_status(launch_ip_search(view_of(db), q, q_dtype, n_queries, n_vectors, top_k, out_idx, out_score,
-                                     reinterpret_cast<float *>(ws + w.cand_s0), reinterpret_cast<int32_t *>(ws + w.cand_i0),
-                                     reinterpret_cast<float *>(ws + w.cand_s1), reinterpret_cast<int32_t *>(ws + w.cand_i1),
+  const SearchState state{reinterpret_cast<uint64_t *>(ws + w.cand), reinterpret_cast<uint2 *>(ws + w.bnd)};
+  return hip_status(launch_ip_search(view_of(db), q, q_dtype, n_queries, n_vectors, top_k, out_idx, out_score, state,
                                      static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -5,22 +5,23 @@
 // the packed keys without the softmax ([google], the scoring kernel).
 //
 // Launches:
-//   ip_score_kernel   the scores of up to 8 queries (one workgroup row of blockIdx.y per
-//                     group of 8) against kBlockTokens database vectors per workgroup, on
-//                     matrix cores: queries are the rows of v_mfma_f32_16x16x32_f16 (fp16
-//                     value and remainder rows, as in the decode kernel), 16 vectors its
-//                     columns.  The scores stay in LDS; wave h then takes query h's k best,
-//                     highest score first, equal scores by lowest index, by taking the best
-//                     k times (wave-wide max of the key, then min index).
-//   topk_merge_kernel per query, kChunkScores candidates per block to k, repeated until one
-//                     block holds them all (two levels for 2^20 vectors at k = 10).  Small
-//                     slices keep each lane's share short: a round's cost is one lane
-//                     re-scanning its entries.
+//   ip_score_kernel    workgroup x of query group y (up to 8 queries) scores kBlockTokens
+//                      database vectors on matrix cores: the queries are the rows of
+//                      v_mfma_f32_16x16x32_f16 (fp16 value and remainder rows, as in the
+//                      decode kernel), 16 vectors its columns.  The scores stay in LDS; wave h
+//                      then ranks query h's: the k-th largest of its 64 lane maxima bounds the
+//                      block's k-th best from below, the (normally few) scores reaching it are
+//                      sorted across the lanes, and the first k are the block's candidates.
+//   topk_final_kernel  one workgroup per query.  Two keys that k scores reach bound the
+//                      query's k-th best from below: the largest block k-th best, and the k-th
+//                      largest of the lanes' maxima over block bests.  Only candidates reaching
+//                      the larger bound are ranked; normally at most 64, sorted at once.
+// Ranking order everywhere: higher score first, equal scores by lower index, as one 64-bit
+// unsigned comparison of key << 32 | ~index, sorted across a wave's lanes by a bitonic network
+// of lane exchanges; longer lists are kept to their best 64 by merging sorted runs.
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
-
-#include <utility>
 
 namespace tq {
 namespace {
@@ -29,9 +30,10 @@ typedef _Float16 half8s __attribute__((ext_vector_type(8)));
 typedef float floatx4s __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreWaves = 8;
-constexpr int kChunkScores = 1024;  // candidates per merge block
 constexpr int kBlockTokens = kSearchBlock;  // database vectors per score workgroup (scores kept in LDS)
-constexpr int kTopkThreads = 256;
+constexpr int kFinalWaves = 16;  // waves of the final workgroup
+constexpr int kFinalRows = 12;   // candidate rows of 64 in flight per wave
+constexpr int kBoundLoads = 16;  // block bounds in flight per lane
 
 __device__ __forceinline__ uint16_t h16s(float x) { return __half_as_ushort(__float2half_rn(x)); }
 __device__ __forceinline__ float f16s(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -46,157 +48,103 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Wave-wide integer max / min with the lane exchanges of lanes.h: DPP quad permutes and row
+// Wave-wide unsigned max with the lane exchanges of lanes.h: DPP quad permutes and row
 // rotations within 16 lanes, then the permlane swaps of rows and halves.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_int(uint32_t v) {
-  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : (uint32_t)min((int)a, (int)b); };
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor4, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor8, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor4, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor8, 0xF, 0xF, false));
   const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = op(r16[0], r16[1]);
+  v = max(r16[0], r16[1]);
   const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return op(r32[0], r32[1]);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_int<true>(v); }
-__device__ __forceinline__ int wave_min_i32(int v) { return (int)wave_reduce_int<false>((uint32_t)v); }
-
-// The k best of the entries a wave holds (kPer per lane: key, index), best first: highest
-// key, then lowest index.  Each round the wave's best is found from the lanes' own bests;
-// only the lane that gave it up looks at its entries again.  Results go to out_k / out_i
-// (k slots; 0 / -1 once the entries run out).
-template <int kPer>
-__device__ void wave_select(uint32_t (&key)[kPer], int (&idx)[kPer], int k, int lane, uint32_t *out_k, int *out_i) {
-  uint32_t bk = 0u;
-  int bi = 0x7fffffff;
-  auto lane_best = [&]() {
-    bk = 0u;
-    bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (key[j] > bk || (key[j] == bk && key[j] != 0u && idx[j] < bi)) {
-        bk = key[j];
-        bi = idx[j];
-      }
-  };
-  lane_best();
-  for (int r = 0; r < k; ++r) {
-    const uint32_t mk = wave_max_u32(bk);
-    const int mi = wave_min_i32(bk == mk ? bi : 0x7fffffff);
-    if (lane == 0) {
-      out_k[r] = mk;
-      out_i[r] = mk == 0u ? -1 : mi;
-    }
-    if (mk == 0u) continue;
-    if (bk == mk && bi == mi) {  // the one lane that held it
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (key[j] == mk && idx[j] == mi) key[j] = 0u;
-      lane_best();
-    }
-  }
+  return max(r32[0], r32[1]);
 }
 
-// The k best of kPer entries per lane, as wave_select, with a prefilter: the k-th largest of
-// the 64 lane maxima is a lower bound of the k-th largest entry (k lanes hold an entry at
-// least that large), so only entries at or above it can be among the k best.  When at most
-// 64 pass, they are compacted through `scratch` (64 keys + 64 indices of LDS) to one per lane
-// and the rounds no longer re-scan kPer entries; otherwise the plain selection runs.
-template <int kPer>
-__device__ void wave_select_pruned(uint32_t (&key)[kPer], int (&idx)[kPer], int k, int lane, uint32_t *scratch,
-                                   uint32_t *out_k, int *out_i) {
-  uint32_t lm = 0u;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) lm = max(lm, key[j]);
-  uint32_t v = lm, theta = 0u;
-  for (int r = 0; r < k && r < 64; ++r) {  // the k-th largest lane maximum
-    theta = wave_max_u32(v);
-    const uint64_t at = __ballot(v == theta);
-    if (lane == __ffsll((unsigned long long)at) - 1) v = 0u;
-  }
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) cnt += (key[j] != 0u && key[j] >= theta) ? 1 : 0;
-  // exclusive prefix of the counts over the lanes
-  int incl = cnt;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int o = __shfl_up(incl, m);
-    if (lane >= m) incl += o;
-  }
-  const int total = __shfl(incl, 63);
-  if (total > 64) {  // many entries tie with the bound: select over all of them
-    wave_select<kPer>(key, idx, k, lane, out_k, out_i);
-    return;
-  }
-  int pos = incl - cnt;
-  uint32_t *sk = scratch;
-  int *si = reinterpret_cast<int *>(scratch + 64);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (key[j] != 0u && key[j] >= theta) {
-      sk[pos] = key[j];
-      si[pos] = idx[j];
-      ++pos;
-    }
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("" ::: "memory");
-  uint32_t k1[1] = {lane < total ? sk[lane] : 0u};
-  int i1[1] = {lane < total ? si[lane] : 0x7fffffff};
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("" ::: "memory");
-  wave_select<1>(k1, i1, k, lane, out_k, out_i);
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-constexpr int kSelWaves = kTopkThreads / 64;
-constexpr int kSelPer = kChunkScores / kTopkThreads;  // entries per lane
+// Ranking across the 64 lanes of a wave, one entry per lane as the 64-bit value
+// key << 32 | ~index: entry a comes before b when its key is larger, or the keys are equal and
+// its index smaller, which is a > b as unsigned integers.  0 is an empty entry (key 0 marks no
+// vector), after every other.
+__device__ __forceinline__ uint64_t rank_entry(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint32_t)~idx;
+}
+__device__ __forceinline__ int entry_index(uint64_t e) { return (int)~(uint32_t)e; }
+__device__ __forceinline__ uint32_t entry_key(uint64_t e) { return (uint32_t)(e >> 32); }
 
-// Block top-k of n (key, index) entries read by `get` (i -> {key, index}), best first, into
-// out_k / out_i (k slots): every wave selects from its slice, then wave 0 from the waves' k
-// bests each.
-template <typename Get>
-__device__ void block_select(int n, int k, Get get, uint32_t *wk, int *wi, uint32_t *out_k, int *out_i) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  {
-    uint32_t key[kSelPer];
-    int idx[kSelPer];
-#pragma unroll
-    for (int j = 0; j < kSelPer; ++j) {
-      const int i = (wave * kSelPer + j) * 64 + lane;  // coalesced: lanes take neighbours
-      key[j] = 0u;
-      idx[j] = 0x7fffffff;
-      if (i < n) get(i, key[j], idx[j]);
-    }
-    wave_select<kSelPer>(key, idx, k, lane, wk + wave * kSearchMaxK, wi + wave * kSearchMaxK);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    constexpr int kPer2 = kSelWaves * kSearchMaxK / 64;
-    uint32_t key[kPer2];
-    int idx[kPer2];
-#pragma unroll
-    for (int j = 0; j < kPer2; ++j) {
-      const int e = j * 64 + lane, w = e / kSearchMaxK, r = e % kSearchMaxK;
-      key[j] = r < k ? wk[w * kSearchMaxK + r] : 0u;
-      idx[j] = r < k ? wi[w * kSearchMaxK + r] : 0x7fffffff;
-      if (key[j] == 0u) idx[j] = 0x7fffffff;
-    }
-    wave_select<kPer2>(key, idx, k, lane, out_k, out_i);
+// the value of lane (lane xor M), for 32- and 64-bit entries
+template <int M, typename T>
+__device__ __forceinline__ T lane_xor_t(T v, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return __float_as_uint(lane_xor<M>(__uint_as_float(v), lane));
+  } else {
+    const uint32_t lo = __float_as_uint(lane_xor<M>(__uint_as_float((uint32_t)v), lane));
+    const uint32_t hi = __float_as_uint(lane_xor<M>(__uint_as_float((uint32_t)(v >> 32)), lane));
+    return ((uint64_t)hi << 32) | lo;
   }
 }
+// One compare-exchange stage of a bitonic network: blocks of SIZE lanes, partner lane
+// (lane xor M).  The lower lane of a pair keeps the larger value in blocks that run in rank
+// order (lane 0 first, largest first), the smaller in the others; REV reverses the network's
+// final order.
+template <int SIZE, int M, bool REV, typename T>
+__device__ __forceinline__ void bitonic_step(T &v, int lane) {
+  const T p = lane_xor_t<M>(v, lane);
+  const bool up = ((lane & SIZE) == 0) != REV;  // SIZE = 64: every lane in one block
+  const bool larger = ((lane & M) == 0) == up;
+  v = ((p > v) == larger) ? p : v;
+}
+// Bitonic merge of a bitonic sequence of 64 values into rank order (REV: reversed).
+template <bool REV, typename T>
+__device__ __forceinline__ void bitonic_merge64(T &v, int lane) {
+  bitonic_step<64, 32, REV>(v, lane);
+  bitonic_step<64, 16, REV>(v, lane);
+  bitonic_step<64, 8, REV>(v, lane);
+  bitonic_step<64, 4, REV>(v, lane);
+  bitonic_step<64, 2, REV>(v, lane);
+  bitonic_step<64, 1, REV>(v, lane);
+}
+// Sort 64 values into rank order (REV: reversed), 21 compare-exchange stages.
+template <bool REV, typename T>
+__device__ __forceinline__ void bitonic_sort64(T &v, int lane) {
+  bitonic_step<2, 1, REV>(v, lane);
+  bitonic_step<4, 2, REV>(v, lane);
+  bitonic_step<4, 1, REV>(v, lane);
+  bitonic_step<8, 4, REV>(v, lane);
+  bitonic_step<8, 2, REV>(v, lane);
+  bitonic_step<8, 1, REV>(v, lane);
+  bitonic_step<16, 8, REV>(v, lane);
+  bitonic_step<16, 4, REV>(v, lane);
+  bitonic_step<16, 2, REV>(v, lane);
+  bitonic_step<16, 1, REV>(v, lane);
+  bitonic_step<32, 16, REV>(v, lane);
+  bitonic_step<32, 8, REV>(v, lane);
+  bitonic_step<32, 4, REV>(v, lane);
+  bitonic_step<32, 2, REV>(v, lane);
+  bitonic_step<32, 1, REV>(v, lane);
+  bitonic_merge64<REV>(v, lane);
+}
+// The best 64 of two ranked lists, ranked: v in rank order, r in reversed order.  Lane l's
+// larger of (a_l, b_63-l) leaves the best 64 as a bitonic sequence.
+__device__ __forceinline__ void merge_best64(uint64_t &v, uint64_t r, int lane) {
+  v = r > v ? r : v;
+  bitonic_merge64<false, uint64_t>(v, lane);
+}
 
+// Workgroup x of query group y scores vectors [x kBlockTokens, (x + 1) kBlockTokens) into LDS,
+// then wave h takes the k best of query h's scores (best first) as the block's candidates:
+// cand [query][block][k] rank entries (0: no vector), bnd [query][block] the keys of the k-th
+// and the best.
 // Table entry e of two codes a = e mod L, b = e div L (L = 2^BK): {hi(c_a) | hi(c_b) << 16,
 // lo(c_a) | lo(c_b) << 16}, hi = the fp16 value of the centroid and lo = the fp16 remainder.
 // A byte of 4-bit codes (a 6-bit field of 3-bit codes) is one entry: coordinates 2j, 2j+1.
 template <int BK>
-// Workgroup x of query group y scores vectors [x kBlockTokens, (x + 1) kBlockTokens) into LDS,
-// then wave h takes the k best of query h's scores (best first) as the block's candidates
-// cand_s / cand_i [query][block][k].
 __global__ __launch_bounds__(64 * kScoreWaves) void ip_score_kernel(CacheView db, const void *__restrict__ q,
-                                                                   int q_dtype, int n_q, int n, int k, float *cand_s,
-                                                                   int32_t *cand_i) {
+                                                                   int q_dtype, int n_q, int n, int k,
+                                                                   uint64_t *cand, uint2 *bnd) {
   constexpr int L = 1 << BK, KROW = 16 * BK;
   constexpr int kTilesPerBlock = kBlockTokens / 16;
   __shared__ uint2 tab[L * L];
@@ -292,81 +240,201 @@ __global__ __launch_bounds__(64 * kScoreWaves) void ip_score_kernel(CacheView db
   if (wave < nq) {  // the block's k best for query q0 + wave; vectors past n hold no entry
     constexpr int kPer = kBlockTokens / 64;
     const int t0 = blockIdx.x * kBlockTokens;
-    uint32_t key[kPer];
-    int idx[kPer];
+    uint32_t key[kPer];  // entry j of a lane is vector t0 + 64 j + lane
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int c = j * 64 + lane;
-      const bool live = t0 + c < n;
-      key[j] = live ? order_key(sc[wave][c]) : 0u;
-      idx[j] = live ? t0 + c : 0x7fffffff;
+      key[j] = t0 + c < n ? order_key(sc[wave][c]) : 0u;
     }
-    uint32_t *ok = reinterpret_cast<uint32_t *>(&sc[wave][0]);  // this wave's row is free now
-    int *oi = reinterpret_cast<int *>(&sc[wave][kSearchMaxK]);
-    wave_select_pruned<kPer>(key, idx, k, lane, reinterpret_cast<uint32_t *>(&sc[wave][2 * kSearchMaxK]), ok, oi);
-    const size_t o = ((size_t)(q0 + wave) * gridDim.x + blockIdx.x) * k;
-    for (int r = lane; r < k; r += 64) {
-      cand_s[o + r] = ok[r] == 0u ? -INFINITY : key_value(ok[r]);
-      cand_i[o + r] = oi[r];
+    const size_t o = (size_t)(q0 + wave) * gridDim.x + blockIdx.x;
+    // The k-th largest lane maximum is reached by k entries (one per lane), so no entry below
+    // it is among the k best; normally at most 64 reach it, and one sort ranks them.
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lm = max(lm, key[j]);
+    bitonic_sort64<false>(lm, lane);
+    const uint32_t theta = max((uint32_t)__builtin_amdgcn_readlane((int)lm, k - 1), 1u);
+    float mine = 0.f;  // entries of this lane that reach the bound (a per-lane count keeps the
+                       // ballot masks of the compaction below out of scalar registers)
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += key[j] >= theta ? 1.f : 0.f;
+    const int n_pass = (int)wave_reduce<false>(mine);  // exact: at most 1024
+    uint64_t *slot = reinterpret_cast<uint64_t *>(&sc[wave][0]);  // this wave's row is free now
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    uint64_t v;  // the block's ranked entries, one per lane; lane r < k holds the r-th best
+    if (n_pass <= 64) {
+      int at = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const bool pass = key[j] >= theta;
+        const uint64_t m = __ballot(pass);
+        if (pass) slot[at + lanes_below(m)] = rank_entry(key[j], t0 + j * 64 + lane);
+        at += __popcll(m);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __asm__ volatile("" ::: "memory");
+      v = lane < n_pass ? slot[lane] : 0ull;
+      bitonic_sort64<false>(v, lane);
+    } else {  // many entries tie with the bound: rank the scores 64 at a time, keep the best 64
+      v = 0ull;
+#pragma unroll 1
+      for (int j = 0; j < kPer; ++j) {
+        const int c = j * 64 + lane;
+        const uint32_t kc = t0 + c < n ? order_key(sc[wave][c]) : 0u;
+        uint64_t r = kc >= theta ? rank_entry(kc, t0 + c) : 0ull;
+        bitonic_sort64<true>(r, lane);
+        merge_best64(v, r, lane);
+      }
     }
+    if (lane < k) cand[o * k + lane] = v;  // 0 past the last vector
+    const uint32_t vk = entry_key(v);
+    if (lane == 0)
+      bnd[o] = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)vk, k - 1),
+                          (uint32_t)__builtin_amdgcn_readlane((int)vk, 0));
   }
 }
 
+// Workgroup j ranks query j's candidates (`blocks` blocks of k) into out_idx / out_score [j][k].
+__global__ __launch_bounds__(64 * kFinalWaves) void topk_final_kernel(const uint64_t *__restrict__ cand,
+                                                                     const uint2 *__restrict__ bnd, int blocks,
+                                                                     int k, int32_t *out_idx, float *out_score) {
+  __shared__ int passed[kFinalWaves];
+  __shared__ uint64_t stage[kFinalWaves][kFinalRows * 64];  // a wave's passing entries of one batch
+  __shared__ uint64_t lists[kFinalWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = blockIdx.x;
 
-// Block (x, query j) takes candidates [x kChunkScores, ...) of the query's n_cand and writes
-// their k best, best first, to out_s / out_i [query][gridDim.x][k].
-__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(const float *__restrict__ cand_s,
-                                                                 const int32_t *__restrict__ cand_i, int n_cand, int k,
-                                                                 int32_t *out_idx, float *out_score) {
-  __shared__ uint32_t wk[kSelWaves * kSearchMaxK];
-  __shared__ int wi[kSelWaves * kSearchMaxK];
-  __shared__ uint32_t ok[kSearchMaxK];
-  __shared__ int oi[kSearchMaxK];
-  const int j = blockIdx.y;
-  const int base = blockIdx.x * kChunkScores;
-  const float *cs = cand_s + (size_t)j * n_cand + base;
-  const int32_t *ci = cand_i + (size_t)j * n_cand + base;
-  block_select(min(kChunkScores, n_cand - base), k,
-               [&](int i, uint32_t &key, int &idx) {
-                 idx = ci[i];
-                 key = idx < 0 ? 0u : order_key(cs[i]);  // an empty candidate slot
-                 if (idx < 0) idx = 0x7fffffff;
-               },
-               wk, wi, ok, oi);
-  __syncthreads();
-  const size_t o = ((size_t)j * gridDim.x + blockIdx.x) * k;
-  for (int r = threadIdx.x; r < k; r += kTopkThreads) {  // already best first
-    out_idx[o + r] = oi[r];
-    out_score[o + r] = ok[r] == 0u ? -INFINITY : key_value(ok[r]);
+  // wave w ranks candidate rows w, w + kFinalWaves, ... (64 entries each); the first rows'
+  // loads go out before those of the bound
+  const uint64_t *c = cand + (size_t)j * blocks * k;
+  const int total = blocks * k;
+  uint64_t e[kFinalRows];
+  auto load_rows = [&](int r0) {
+#pragma unroll
+    for (int t = 0; t < kFinalRows; ++t) {
+      const int i = (r0 + t * kFinalWaves) * 64 + lane;
+      e[t] = i < total ? c[i] : 0ull;
+    }
+  };
+  load_rows(wave);
+
+  // The bound, in every wave alike (no exchange between waves): a key that k scores of the
+  // query reach bounds its k-th best from below, and only entries at or above it (and not
+  // empty) can be among the k best.  Two such keys: the largest block k-th best, and the k-th
+  // largest of the lanes' maxima over block bests (each lane's maximum is the best of a block
+  // of its own, so k blocks reach it).
+  uint32_t mk = 0u, mb = 0u;
+  for (int b0 = 0; b0 < blocks; b0 += 64 * kBoundLoads) {  // lane l takes blocks l, l + 64, ...
+    uint2 v[kBoundLoads];
+#pragma unroll
+    for (int t = 0; t < kBoundLoads; ++t) {
+      const int b = b0 + t * 64 + lane;
+      v[t] = b < blocks ? bnd[(size_t)j * blocks + b] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int t = 0; t < kBoundLoads; ++t) {
+      mk = max(mk, v[t].x);
+      mb = max(mb, v[t].y);
+    }
+  }
+  mk = wave_max_u32(mk);
+  bitonic_sort64<false>(mb, lane);
+  const uint32_t lim = max(max(mk, 1u), (uint32_t)__builtin_amdgcn_readlane((int)mb, k - 1));
+  const uint64_t floor = (uint64_t)lim << 32;
+
+  if (total <= kFinalWaves * kFinalRows * 64) {  // every candidate is loaded: count those passing
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < kFinalRows; ++t) cnt += __popcll(__ballot(e[t] >= floor));
+    if (lane == 0) passed[wave] = cnt;
+    __syncthreads();
+    int n_pass = 0, at = 0;
+#pragma unroll
+    for (int w = 0; w < kFinalWaves; ++w) {
+      at += w < wave ? passed[w] : 0;
+      n_pass += passed[w];
+    }
+    if (n_pass <= 64) {  // the usual case: one sort of all of them
+      uint64_t *slots = &stage[0][0];
+#pragma unroll
+      for (int t = 0; t < kFinalRows; ++t) {
+        const bool pass = e[t] >= floor;
+        const uint64_t bm = __ballot(pass);
+        if (pass) slots[at + lanes_below(bm)] = e[t];
+        at += __popcll(bm);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint64_t v = lane < n_pass ? slots[lane] : 0ull;
+        bitonic_sort64<false>(v, lane);
+        if (lane < k) {
+          out_idx[(size_t)j * k + lane] = v == 0ull ? -1 : entry_index(v);
+          out_score[(size_t)j * k + lane] = v == 0ull ? -INFINITY : key_value(entry_key(v));
+        }
+      }
+      return;
+    }
+  }
+
+  // a wave's running best 64, in rank order: each batch's passing entries are compacted into
+  // the wave's LDS stage, then ranked 64 at a time (one copy of the sort code, in a loop) and
+  // merged in
+  uint64_t best = 0ull;
+  uint64_t *st = stage[wave];
+  for (int r0 = wave; r0 * 64 < total; r0 += kFinalWaves * kFinalRows) {
+    if (r0 != wave) load_rows(r0);
+    int n_st = 0;
+#pragma unroll
+    for (int t = 0; t < kFinalRows; ++t) {
+      const bool pass = e[t] >= floor;
+      const uint64_t bm = __ballot(pass);
+      if (pass) st[n_st + lanes_below(bm)] = e[t];
+      n_st += __popcll(bm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+#pragma unroll 1
+    for (int c0 = 0; c0 < n_st; c0 += 64) {
+      uint64_t v = c0 + lane < n_st ? st[c0 + lane] : 0ull;
+      bitonic_sort64<true>(v, lane);
+      merge_best64(best, v, lane);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
+
+  // merge the waves' lists pairwise: wave w takes wave w + s's list, reversed
+  lists[wave][lane] = best;
+#pragma unroll 1
+  for (int s = 1; s < kFinalWaves; s <<= 1) {
+    __syncthreads();
+    if ((wave & (2 * s - 1)) == 0) {
+      merge_best64(best, lists[wave + s][63 - lane], lane);
+      lists[wave][lane] = best;
+    }
+  }
+  if (wave == 0 && lane < k) {
+    out_idx[(size_t)j * k + lane] = best == 0ull ? -1 : entry_index(best);
+    out_score[(size_t)j * k + lane] = best == 0ull ? -INFINITY : key_value(entry_key(best));
   }
 }
 
 }  // namespace
 
 hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
-                            float *out_score, float *cand_s0, int32_t *cand_i0, float *cand_s1, int32_t *cand_i1,
-                            hipStream_t stream) {
+                            float *out_score, const SearchState &st, hipStream_t stream) {
   const int blocks = (n + kBlockTokens - 1) / kBlockTokens;
-  const dim3 g1(blocks, (n_q + 7) / 8);
-  if (db.bits == 4) ip_score_kernel<4><<<g1, 64 * kScoreWaves, 0, stream>>>(db, q, q_dtype, n_q, n, k, cand_s0, cand_i0);
-  else ip_score_kernel<3><<<g1, 64 * kScoreWaves, 0, stream>>>(db, q, q_dtype, n_q, n, k, cand_s0, cand_i0);
+  const dim3 grid(blocks, (n_q + 7) / 8);
+  if (db.bits == 4)
+    ip_score_kernel<4><<<grid, 64 * kScoreWaves, 0, stream>>>(db, q, q_dtype, n_q, n, k, st.cand, st.bnd);
+  else
+    ip_score_kernel<3><<<grid, 64 * kScoreWaves, 0, stream>>>(db, q, q_dtype, n_q, n, k, st.cand, st.bnd);
   hipError_t e = hipGetLastError();
-  // merge levels: each block reduces kChunkScores candidates to k, until one block is left
-  long n_cand = (long)blocks * k;
-  float *src_s = cand_s0, *dst_s = cand_s1;
-  int32_t *src_i = cand_i0, *dst_i = cand_i1;
-  while (e == hipSuccess) {
-    const int groups = (int)((n_cand + kChunkScores - 1) / kChunkScores);
-    const bool last = groups == 1;
-    topk_merge_kernel<<<dim3(groups, n_q), kTopkThreads, 0, stream>>>(src_s, src_i, (int)n_cand, k,
-                                                                     last ? out_idx : dst_i, last ? out_score : dst_s);
-    e = hipGetLastError();
-    if (last) break;
-    n_cand = (long)groups * k;
-    std::swap(src_s, dst_s);
-    std::swap(src_i, dst_i);
-  }
-  return e;
+  if (e != hipSuccess) return e;
+  topk_final_kernel<<<n_q, 64 * kFinalWaves, 0, stream>>>(st.cand, st.bnd, blocks, k, out_idx, out_score);
+  return hipGetLastError();
 }
 
 }  // namespace tq

@@ -166,14 +166,19 @@ hipError_t launch_decode_fused_paged_sparse(const DecodeArgs &key_pass, const De
 // Workspace of the paged calls with several query positions or Sparse V (tau > 0).
 WorkspaceLayout workspace_layout_paged_ext(int batch, int n_q_heads, int n_kv_heads, int n_q, int ctx_len, bool sparse);
 SplitPlan plan_multi(int batch, int n_kv_heads, const MultiQueryShape &m, int ctx_len);
-// Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
-// db, 3- or 4-bit rows), then the k best per query.  Two candidate buffers (ping-pong for the
-// merge levels), each [n_q][ceil(n / kSearchBlock) * k] score + index, are caller scratch.
-hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
-                            float *out_score, float *cand_s0, int32_t *cand_i0, float *cand_s1, int32_t *cand_i1,
-                            hipStream_t stream);
 constexpr int kSearchBlock = 1024;
 constexpr int kSearchMaxK = 64;
+// Inner-product search candidates in caller scratch: cand [n_q][blocks][k] rank entries
+// (order key << 32 | ~index), bnd [n_q][blocks] the keys of each block's k-th best and best,
+// blocks = ceil(n / kSearchBlock).
+struct SearchState {
+  uint64_t *cand;
+  uint2 *bnd;
+};
+// Inner-product search: scores of n_q queries against n database vectors (plane (0, 0) of
+// db, 3- or 4-bit rows), each block's k best, then the k best per query.
+hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int n_q, int n, int k, int32_t *out_idx,
+                            float *out_score, const SearchState &st, hipStream_t stream);
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

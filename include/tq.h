@@ -415,6 +415,11 @@ size_t tq_paged_decode_ext_workspace_bytes(int batch, int n_q_heads, int n_kv_he
  *   out_idx    device out int32 [n_queries][top_k] (-1 past n_vectors)
  *   out_score  device out fp32 [n_queries][top_k] (-inf past n_vectors)
  *   workspace  device scratch of tq_ip_search_workspace_bytes(...) bytes, 256-byte aligned
+ *              (per-block candidates; no initial contents needed).  A workspace sized for
+ *              (n_queries, n_vectors, top_k) serves any smaller call.
+ * Two launches on hip_stream: each workgroup scores 1024 vectors for up to 8 queries and keeps
+ * each query's k best; then one workgroup per query ranks the candidates that reach the
+ * largest block k-th best.
  * 1 <= top_k <= 64, else TQ_ERR_UNSUPPORTED.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_ip_search(const tq_cache *db, const void *q, int q_dtype, int n_queries, int n_vectors, int top_k,

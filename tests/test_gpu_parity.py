@@ -749,7 +749,9 @@ def _search_case(signs, golden, n, nq, k, bits, q_dtype=None, dup=False, seed=0)
     spec["seed"] = 20 + seed
     g = inputs.generate_search(spec, device="cpu", n=n, n_queries=nq)
     x, q = g["x"], g["q"]
-    if dup:  # exact duplicates: equal codes, equal scores, ascending indices
+    if dup == "all":  # every vector the same: every block ties, the lowest indices win
+        x[:] = x[0]
+    elif dup:  # exact duplicates: equal codes, equal scores, ascending indices
         x[7] = x[3]
         x[n - 1] = x[3]
         q[0] = x[3]
@@ -785,7 +787,10 @@ def _search_case(signs, golden, n, nq, k, bits, q_dtype=None, dup=False, seed=0)
         assert set(must.tolist()) <= set(got.tolist()), j
         if k > n:
             assert np.all(idx_g[j, n:] == -1) and np.all(np.isneginf(sc_g[j, n:]))
-    if dup:
+    if dup == "all":
+        assert np.all(idx_g[:, :kk] == np.arange(kk)[None, :])
+        assert np.all(sc_g[:, :kk] == sc_g[:, :1])
+    elif dup:
         got0 = idx_g[0, :kk].tolist()
         assert got0[:3] == [3, 7, n - 1] and sc_g[0, 0] == sc_g[0, 1] == sc_g[0, 2]
     return idx_g
@@ -798,10 +803,34 @@ def _search_case(signs, golden, n, nq, k, bits, q_dtype=None, dup=False, seed=0)
     (9000, 3, 5, 4, "f32", True),
     (40, 2, 64, 4, None, False),          # fewer vectors than k
     (8192, 1, 1, 3, "f16", False),
-    (300000, 3, 64, 4, None, False),      # 147 blocks x 64 candidates: two merge levels
+    (300000, 3, 64, 4, None, False),      # 293 blocks x 64 candidates
+    (20000, 2, 64, 4, None, "all"),       # all tied: 20 blocks x 64 candidates pass the bound
+    (70000, 9, 7, 3, "f16", "all"),       # all tied, two query groups
+    (300000, 1, 64, 4, None, "all"),      # all tied: 18752 candidates reach the bound
 ])
 def test_ip_search_matches_oracle(case, signs, golden_codebooks):
     n, nq, k, bits, qdt, dup = case
     _say("ip search", case)
     qdt = {None: None, "f32": torch.float32, "f16": torch.float16}[qdt]
     _search_case(signs, golden_codebooks, n, nq, k, bits, q_dtype=qdt, dup=dup)
+
+
+def test_ip_search_repeated_calls_share_workspace(signs):
+    """The search state in the workspace returns to zero after every call: calls in a row on
+    one set of buffers (a smaller database second, then the first again) give the outputs of
+    calls on fresh buffers, bit for bit."""
+    _say("ip search repeated calls")
+    spec = dict(inputs.SEARCH["search1m"])
+    n, nq, k = 150000, 12, 16
+    g = inputs.generate_search(spec, device="cpu", n=n, n_queries=nq)
+    cap = (n + 63) // 64 * 64
+    db = _new_cache(1, 1, cap, 4, 0, signs)
+    _fill(db, g["x"][None, :, None, :].contiguous().to(DEV))
+    q = g["q"].to(DEV).contiguous()
+    shared = tq.SearchBuffers(nq, n, k, device=DEV)
+    for m in (n, 33333, n):
+        fresh = tq.ip_search(db, q, m, k)
+        tq.ip_search(db, q, m, k, buffers=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(fresh.idx, shared.idx) and torch.equal(fresh.score, shared.score), m
+        assert int(fresh.idx.max()) < m
