@@ -203,6 +203,8 @@ def main():
         result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / stream
         result["roofline"]["traffic"] = traffic_from_profiles(args.workload, result.pop("_kernel"), digest)
         result["sources_digest"] = digest
+        if args.calibrate_copy:
+            calibrate_copy(torch, log)
         print(json.dumps(result), flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
