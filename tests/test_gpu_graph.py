@@ -2,8 +2,9 @@
 
 The decode kernel keeps per-(batch, kv head) arrival counters in the caller's workspace and
 clears them itself, and no call of the path records a memset, so a graph of append + decode
-steps can be replayed any number of times.  Each replay is checked against the eager result
-with eager work and synchronisations in between.
+steps can be replayed any number of times.  The search keeps only per-block candidates in its
+workspace, rewritten by every call.  Each replay is checked against the eager result with eager
+work and synchronisations in between.
 """
 import math
 import sys
@@ -74,3 +75,48 @@ def test_graph_replays_match_eager(workload, tau, batch, ctx):
         step(0)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(bufs[0].out, eager[0][0])
+
+
+@pytest.mark.parametrize("n,nq,k", [(300000, 11, 10), (70000, 8, 64)])
+def test_search_graph_replays_match_eager(n, nq, k):
+    """Inner-product search (score kernel, then the final ranking) recorded into a graph over
+    two databases, replayed with eager searches of a third in between."""
+    print("graph search", n, nq, k, flush=True)
+    spec = dict(inputs.SEARCH["search1m"])
+    g = inputs.generate_search(spec, device=DEV, n=n, n_queries=nq)
+    signs = inputs.rotation_signs().to(DEV)
+    cap = (n + 63) // 64 * 64
+    dbs = []
+    for c in range(3):
+        db = tq.PackedCache(1, 1, cap, 4, tq.LAYOUT_ROWS, signs, device=DEV)
+        x = g["x"] if c == 0 else g["x"].flip(0).contiguous() if c == 1 else (g["x"] * 0.5).contiguous()
+        tq.quantize_append(db, x[None, :, None, :].contiguous(), 0)
+        dbs.append(db)
+    q = g["q"].contiguous()
+    bufs = [tq.SearchBuffers(nq, n, k, device=DEV) for _ in range(2)]
+    extra = tq.SearchBuffers(nq, n, k, device=DEV)
+    for i in range(2):
+        tq.ip_search(dbs[i], q, n, k, buffers=bufs[i])
+    tq.ip_search(dbs[2], q, n, k, buffers=extra)
+    torch.cuda.synchronize()
+    eager = [(b.idx.clone(), b.score.clone()) for b in bufs]
+    eager_extra = extra.idx.clone()
+    assert not torch.equal(eager[0][0], eager[1][0])  # the two databases rank differently
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(2):
+            tq.ip_search(dbs[i], q, n, k, buffers=bufs[i])
+    for rep in range(3):
+        for b in bufs:
+            b.idx.fill_(-7)
+            b.score.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(bufs):
+            assert torch.equal(b.idx, eager[i][0]), f"replay {rep}, database {i}: idx differs"
+            assert torch.equal(b.score, eager[i][1]), f"replay {rep}, database {i}: score differs"
+        tq.ip_search(dbs[2], q, n, k, buffers=extra)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(extra.idx, eager_extra)
