@@ -597,12 +597,18 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         float m = -INFINITY, l = 0.f;
         if (vlive(wave)) {
           const float2 *ml = a.lse_ml + vrow(wave) * a.lse_splits;
-          for (int k = lane; k < a.lse_splits; k += 64) m = fmaxf(m, ml[k].x);
-          m = wave_reduce<true>(m);
-          if (m != -INFINITY)
-            for (int k = lane; k < a.lse_splits; k += 64)
-              if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - m);
-          l = wave_reduce<false>(l);
+          if (a.lse_splits <= 64) {  // one partial per lane, loaded once for both reductions
+            const float2 v = lane < a.lse_splits ? ml[lane] : make_float2(-INFINITY, 0.f);
+            m = wave_reduce<true>(v.x);
+            l = wave_reduce<false>(m != -INFINITY && v.x != -INFINITY ? v.y * __expf(v.x - m) : 0.f);
+          } else {
+            for (int k = lane; k < a.lse_splits; k += 64) m = fmaxf(m, ml[k].x);
+            m = wave_reduce<true>(m);
+            if (m != -INFINITY)
+              for (int k = lane; k < a.lse_splits; k += 64)
+                if (ml[k].x != -INFINITY) l += ml[k].y * __expf(ml[k].x - m);
+            l = wave_reduce<false>(l);
+          }
         }
         lse_own = m == -INFINITY ? -INFINITY : m + __logf(l);
         if (lane == 0) {
