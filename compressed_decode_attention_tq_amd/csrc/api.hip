@@ -168,6 +168,15 @@ WorkspaceLayout workspace_layout_multi(int batch, int n_q_heads, int n_kv_heads,
   return w;
 }
 
+// Splits of a paged multi-query call: those of the contiguous call, capped so that a wave's
+// page offsets fit its lanes (one tile per lane; in prefill mode every wave walks every tile).
+SplitPlan plan_paged_multi(int batch, int n_kv_heads, const MultiQueryShape &m, int ctx_len) {
+  SplitPlan fp = plan_multi(batch, n_kv_heads, m, ctx_len);
+  const int cap = m.prefill ? kPagedPrefillMaxSplit : kPagedMaxSplit;
+  if (fp.split_len > cap) fp = SplitPlan{(ctx_len + cap - 1) / cap, cap};
+  return fp;
+}
+
 SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len) {
   SplitPlan p = plan_fused(batch, n_kv_heads, ctx_len);
   if (p.split_len > kPagedMaxSplit) {
@@ -207,11 +216,9 @@ WorkspaceLayout workspace_layout_paged_ext(int batch, int n_q_heads, int n_kv_he
   WorkspaceLayout w{};
   size_t off = 0;
   w.counters = off;
-  if (!sparse) {  // several query positions: one row group per work item (no prefill mode over pages)
-    MultiQueryShape m = multi_query_shape(n_q_heads / n_kv_heads, n_q);
-    m.prefill = false;
-    SplitPlan fp = plan_multi(batch, n_kv_heads, m, ctx_len);
-    if (fp.split_len > kPagedMaxSplit) fp = SplitPlan{(ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit, kPagedMaxSplit};
+  if (!sparse) {  // several query positions (a long chunk in prefill mode, as without pages)
+    const MultiQueryShape m = multi_query_shape(n_q_heads / n_kv_heads, n_q);
+    const SplitPlan fp = plan_paged_multi(batch, n_kv_heads, m, ctx_len);
     const size_t rows = (size_t)batch * n_q * n_q_heads * fp.n_splits;
     off = align_up(off + (size_t)batch * n_kv_heads * m.vgroups * sizeof(unsigned), 256);
     w.fpart_ml = off;
@@ -803,14 +810,12 @@ int tq_paged_decode_attn_ext(const tq_paged_cache *k, const tq_paged_cache *v, c
   a.n_pages = k->n_pages;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (!sparse) {
-    MultiQueryShape m = multi_query_shape(group, n_q);
-    m.prefill = false;
+    const MultiQueryShape m = multi_query_shape(group, n_q);
     a.n_q = n_q;
     a.vgroups = m.vgroups;
     a.vg_size = m.vg_size;
-    a.fplan = plan_multi(k->batch, k->n_kv_heads, m, max_ctx_len);
-    if (a.fplan.split_len > kPagedMaxSplit)
-      a.fplan = SplitPlan{(max_ctx_len + kPagedMaxSplit - 1) / kPagedMaxSplit, kPagedMaxSplit};
+    a.prefill = m.prefill ? 1 : 0;
+    a.fplan = plan_paged_multi(k->batch, k->n_kv_heads, m, max_ctx_len);
     a.plan = a.fplan;
     return hip_status(launch_decode_fused_paged(a, stream));
   }

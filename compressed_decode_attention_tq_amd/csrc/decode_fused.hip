@@ -297,9 +297,9 @@ template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool
           bool PREFILL = false, bool QJL = false, int W = kWaves>
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
-  static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !PAGED && !VMASK), "prefill: dense multi-query only");
-  static_assert(!PAGED || !(PREFILL || (SPARSE && RECORDS) || (MULTI && APPEND)),
-                "paged caches: decode, its append, several query positions, Sparse V's two passes");
+  static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !VMASK), "prefill: dense multi-query only");
+  static_assert(!PAGED || !((SPARSE && RECORDS) || (MULTI && APPEND)),
+                "paged caches: decode, its append, several query positions (prefill chunks too), Sparse V's two passes");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
   static_assert(!QJL || (BK == 3 && !(SPARSE || MULTI || APPEND || PAGED || VMASK || PREFILL)),
                 "QJL keys: 3-bit codes, dense single-query decode");
@@ -397,9 +397,12 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // A value-pass split of at most 64 tiles is shared out by need (lane k: tile k, see VMASK
     // below); every other split keeps the round-robin tiles (lane i: tile wave + W i).
     const bool by_need = VMASK && n_tiles <= 64;
+    // lane k holds tile k's page offset where a wave may visit any tile of its split (shared
+    // by need, or prefill: every wave walks all of at most 64 tiles)
+    const bool by_tile = by_need || PREFILL;
     uint32_t page_tok = kNoPage;  // paged: lane i holds tile_tok of its tile in the mapping above
     if constexpr (PAGED) {
-      const int tile_i = by_need ? lane : wave + W * lane;
+      const int tile_i = by_tile ? lane : wave + W * lane;
       if (tile_i < n_tiles) {
         const int P = a.k.capacity, t0 = t_begin + tile_i * kTile, slot = t0 / P;
         const int page = slot < a.max_pages ? a.block_table[(size_t)b * a.max_pages + slot] : -1;
@@ -408,7 +411,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     }
     auto tile_tok = [&](int tile) -> uint32_t {
       if constexpr (PAGED)
-        return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, by_need ? tile : (tile - wave) / W);
+        return (uint32_t)__builtin_amdgcn_readlane((int)page_tok, by_tile ? tile : (tile - wave) / W);
       else return (uint32_t)tile * kTile;
     };
     auto tile_off = [&](uint32_t tok, uint32_t unit) -> uint32_t {  // bytes; past the end for no page
@@ -1403,8 +1406,18 @@ bool decode_fused_sparse_supported(const DecodeArgs &a) {
 
 hipError_t launch_decode_fused_paged(const DecodeArgs &a, hipStream_t stream) {
   if (a.block_table == nullptr || a.seq_lens == nullptr || a.fplan.split_len > kPagedMaxSplit ||
-      a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity || !decode_fused_supported(a) || a.prefill)
+      a.k.capacity % kTile != 0 || a.v.capacity != a.k.capacity || !decode_fused_supported(a) ||
+      (a.prefill && a.fplan.split_len > kPagedPrefillMaxSplit))
     return hipErrorInvalidValue;
+  if (a.prefill) {  // a chunk of positions: one workgroup per 8 row groups (one per wave)
+    if (a.xk != nullptr) return hipErrorInvalidValue;
+    const long vg_items = (a.vgroups + kWaves - 1) / kWaves;
+    const long units = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+    const long items = vg_items > 1 ? vg_items * ((units + 7) / 8) * 8 : units;
+    if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+    return a.k.bits == 4 ? launch_nh<4, false, true, false, true, false, true, true>(a, (int)items, stream)
+                         : launch_nh<3, false, true, false, true, false, true, true>(a, (int)items, stream);
+  }
   if (a.n_q > 1 || a.vgroups > 1) {  // several query positions (one row group per work item)
     if (a.xk != nullptr) return hipErrorInvalidValue;
     const long units = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;

@@ -152,8 +152,9 @@ hipError_t launch_append_paged(const CacheView &kc, const CacheView &vc, const i
                                int max_pages, int n_pages, int batch, const void *xk, const void *xv,
                                int x_dtype, const int32_t *start_pos, int n_tokens, hipStream_t stream);
 // Longest split of the paged decode: 64 tiles per wave, so that one lane per tile holds the
-// wave's page offsets.
+// wave's page offsets.  In prefill mode every wave walks every tile of its split: 64 tiles.
 constexpr int kPagedMaxSplit = 8 * 64 * 64;
+constexpr int kPagedPrefillMaxSplit = 64 * 64;
 SplitPlan plan_fused_paged(int batch, int n_kv_heads, int ctx_len);
 // Splits of Sparse V's value pass: the dense plan with at most 64 tiles per wave (8 * 64 * 64
 // tokens per split), so that one lane per tile decides which tiles a wave needs.

@@ -389,8 +389,11 @@ int tq_paged_decode_attn_append(const tq_paged_cache *k, const tq_paged_cache *v
  *   n_q = 1, sparse_v_tau = 0: tq_paged_decode_attn.
  * Positions on a "no page" entry leave the softmax (see tq_paged_cache).  Keys of 3 or 4 bits,
  * values of 2 bits, n_q_heads / n_kv_heads <= 8, 1 <= n_q <= 4096; Sparse V with n_q = 1 only
- * (TQ_ERR_UNSUPPORTED otherwise).  Equal codes give the outputs of the contiguous calls for
- * sequences without holes.
+ * (TQ_ERR_UNSUPPORTED otherwise).  A chunk of 8 or more groups of 8 query rows per kv head
+ * runs in prefill mode, as without pages: the 8 waves of a workgroup take 8 row groups and
+ * walk the same tiles, in splits of at most 4096 tokens (one page offset per lane).  Equal
+ * codes give the outputs of the contiguous calls, bit for bit, for sequences without holes
+ * wherever both calls split the context alike (always up to 4096 tokens).
  *   workspace  tq_paged_decode_ext_workspace_bytes(...) bytes, 256-byte aligned, zero-filled once
  *              before first use (arrival counters every completed call leaves at zero); calls
  *              sharing it must not overlap in time.

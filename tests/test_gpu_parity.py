@@ -544,8 +544,7 @@ def _paged_ext_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, n_
     whole = [b for b in range(batch) if valid[b, :max(lens[b], 0)].all()]
     allowance, nb = None, 0
     if n_q > 1:
-        vgroups = -(-(hq // hkv) * n_q // 8)
-        if vgroups < 8:  # the contiguous call takes the same splits (no prefill mode)
+        if max_ctx <= 4096:  # the contiguous call takes the same splits (prefill mode or not)
             ref = tq.decode_attn_multi(kf, vf, qd, max_ctx, scale, seq_lens=sl)
             torch.cuda.synchronize()
             assert torch.equal(got.out[whole], ref.out[whole]) and torch.equal(got.lse[whole], ref.lse[whole])
@@ -568,8 +567,13 @@ def _paged_ext_case(w, signs, golden, batch, hq, hkv, page, seq_lens, bits_k, n_
     ("llama8k", 3, 32, 8, 64, [700, 5, 333], 4, 4, 0.0, [(0, 5)]),
     ("batch32k", 2, 8, 2, 256, [1300, 1024], 3, 7, 0.0, []),
     ("ctx131k", 2, 16, 2, 128, [1500, 0], 4, 3, 0.0, [(0, 0), (0, 11)]),
-    # a chunk of 96 positions (12 row groups per kv head) whose last page is missing
+    # a chunk of 96 positions (48 row groups per kv head: prefill mode) whose last page is missing
     ("llama8k", 1, 8, 2, 64, [1400], 4, 96, 0.0, [(0, 21)]),
+    # prefill mode over pages: contexts past 4096 tokens (capped splits), 8-head groups, 3-bit
+    # keys, holes, and row groups past the last one in a workgroup
+    ("llama8k", 2, 8, 2, 128, [6000, 4500], 4, 64, 0.0, [(1, 7)]),
+    ("batch32k", 2, 16, 2, 256, [5000, 2100], 3, 20, 0.0, []),
+    ("ctx131k", 1, 16, 2, 64, [3000], 4, 9, 0.0, []),       # equals the contiguous call bit for bit
     ("llama8k", 2, 16, 4, 64, [300, 450], 3, 2, 0.0, [(0, s) for s in range(5)] + [(1, 1)]),
     # Sparse V over pages
     ("ctx131k", 2, 16, 2, 128, [1500, 900], 4, 1, 1e-4, []),
