@@ -786,7 +786,7 @@ def cpu_baseline_search(spec, db, q, signs, np, torch, log):
         o.ip_search(q64, codes, n16, s64, c, spec["top_k"])
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 50:
+        if el > 10.0 or reps >= 1000:  # about 10 s of CPU work
             break
     value = reps * sample / n / el
     log(f"[bench] cpu oracle: {reps} sample searches in {el:.1f} s")
