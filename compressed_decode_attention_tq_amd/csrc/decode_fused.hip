@@ -847,7 +847,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
       float sc[2][NH2];  // [token bit][head slot]
-      if (NH == 4) {
+      if constexpr (NH == 4) {
         const float4 r = *reinterpret_cast<const float4 *>(wbuf + score_unit<4>(pr, half_id));
         sc[0][0] = r.x; sc[0][1] = r.y; sc[1][0] = r.z; sc[1][1] = r.w;
       } else {
