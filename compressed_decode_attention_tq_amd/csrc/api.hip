@@ -573,6 +573,20 @@ int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cach
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   // 3-bit codes, 2-bit values, groups up to 8, no Sparse V: one launch on matrix cores
   if (decode_fused_qjl_supported(a)) return hip_status(launch_decode_fused_qjl(a, stream));
+  if (a.sparse) {  // with Sparse V: the key pass for the LSE, then the masked value pass
+    DecodeArgs k1 = a;
+    k1.cand = nullptr;
+    k1.cand_count = nullptr;
+    DecodeArgs v2 = a;
+    v2.sparse = 0;
+    v2.lse_ml = a.fpart_ml;
+    v2.lse_splits = a.fplan.n_splits;
+    v2.fplan = plan_fused_vmask(a.batch, a.n_kv_heads, a.ctx_len);  // at most 64 tiles per split
+    v2.fpart_ml = a.vpart_ml;
+    v2.fpart_o = a.vpart_o;
+    if (decode_fused_qjl_sparse_supported(k1) && decode_fused_supported(v2))
+      return hip_status(launch_decode_fused_qjl_sparse(k1, v2, stream));
+  }
   return hip_status(launch_decode_generic(a, stream));
 }
 

@@ -42,6 +42,9 @@
 //     head's final LSE, and that pass visits only the tiles whose maximum reaches some head's
 //     threshold.  (With RECORDS, the key pass also writes every token whose score reaches its
 //     wave's running maximum + log2(tau) as a candidate record for the vector second pass.)
+//   * QJL keys (QJL, 3-bit codes): every score adds the sign-sketch term, the query's sketch
+//     against fp16 +/-1 sign operands on matrix cores; dense decode, or Sparse V's key pass
+//     and masked value pass.
 #include "tq_common.h"
 #include "tq_launch.h"
 #include "lanes.h"
@@ -301,8 +304,8 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(!PAGED || !((SPARSE && RECORDS) || (MULTI && APPEND)),
                 "paged caches: decode, its append, several query positions (prefill chunks too), Sparse V's two passes");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
-  static_assert(!QJL || (BK == 3 && !(SPARSE || MULTI || APPEND || PAGED || VMASK || PREFILL)),
-                "QJL keys: 3-bit codes, dense single-query decode");
+  static_assert(!QJL || (BK == 3 && !(MULTI || APPEND || PAGED || PREFILL || (SPARSE && RECORDS))),
+                "QJL keys: 3-bit codes, single-query decode, dense or Sparse V's two passes");
   constexpr bool KEYS_ONLY = SPARSE && !RECORDS;
   // More waves per workgroup for single-query decode, paged or not, with long splits:
   //   W = 12 (three per SIMD), groups of up to 4 heads, values too: 2 KB wave buffers (scores
@@ -681,7 +684,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // signs 32 quarter + 8 kk .. + 7, byte kk of the lane's sign word.
     half8 sop[4];
     if constexpr (QJL) {
-      float *pq_lds = reinterpret_cast<float *>(lds + kWBase + 2 * 4096);  // [NH][128]
+      float *pq_lds = reinterpret_cast<float *>(lds + WBASE + 2 * WSTRIDE);  // [NH][128], wave buffers 2..3
       floatx4 pacc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -1459,6 +1462,28 @@ bool decode_fused_qjl_supported(const DecodeArgs &a) {
   return decode_fused_supported(a) && a.k.bits == 3 && a.n_q == 1 && a.vgroups == 1 && a.xk == nullptr &&
          a.block_table == nullptr && a.qjl_bits != nullptr && a.qjl_rnorm != nullptr && a.qjl_proj != nullptr &&
          a.qjl_m == kD;
+}
+
+bool decode_fused_qjl_sparse_supported(const DecodeArgs &a) {
+  return decode_fused_sparse_supported(a) && a.k.bits == 3 && a.v.bits == 2 && a.xk == nullptr &&
+         a.block_table == nullptr && a.qjl_bits != nullptr && a.qjl_rnorm != nullptr && a.qjl_proj != nullptr &&
+         a.qjl_m == kD && a.cand == nullptr && a.tile_max != nullptr;
+}
+
+// Sparse V with QJL keys: the key pass (LSE partials and tile maxima, QJL-corrected scores),
+// then the masked value pass, which recomputes the QJL scores of the tiles it needs.
+hipError_t launch_decode_fused_qjl_sparse(const DecodeArgs &key_pass, const DecodeArgs &value_pass,
+                                          hipStream_t stream) {
+  const DecodeArgs &a = key_pass, &v = value_pass;
+  if (!decode_fused_qjl_sparse_supported(a) || !decode_fused_supported(v) || v.lse_ml == nullptr ||
+      v.lse_splits < 1 || v.tile_max == nullptr || v.fplan.split_len > kVmaskMaxSplit)
+    return hipErrorInvalidValue;
+  const long items_k = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
+  const long items_v = (long)v.batch * v.n_kv_heads * v.fplan.n_splits;
+  if (items_k < 1 || items_k > 0x7fffffffL || items_v < 1 || items_v > 0x7fffffffL) return hipErrorInvalidValue;
+  const hipError_t e = launch_nh<3, true, false, false, false, false, false, false, true>(a, (int)items_k, stream);
+  if (e != hipSuccess) return e;
+  return launch_nh<3, false, false, false, false, true, true, false, true>(v, (int)items_v, stream);
 }
 
 hipError_t launch_decode_fused_qjl(const DecodeArgs &a, hipStream_t stream) {

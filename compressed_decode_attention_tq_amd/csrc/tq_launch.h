@@ -129,6 +129,11 @@ hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t str
 // kernel with the query's sketch and the sign-sketch products.
 bool decode_fused_qjl_supported(const DecodeArgs &a);
 hipError_t launch_decode_fused_qjl(const DecodeArgs &a, hipStream_t stream);
+// QJL decode with Sparse V on matrix cores: key_pass as for the key-only fused pass (no
+// candidate records), value_pass the masked value pass over the key pass's partials.
+bool decode_fused_qjl_sparse_supported(const DecodeArgs &a);
+hipError_t launch_decode_fused_qjl_sparse(const DecodeArgs &key_pass, const DecodeArgs &value_pass,
+                                          hipStream_t stream);
 // The generic split kernel, the Sparse-V second pass (if a.sparse) and the split merge: any code
 // width, group <= 16, and the only path that takes QJL keys.
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t stream);

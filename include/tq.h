@@ -217,9 +217,10 @@ int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void
  * an unbiased estimate of scale q . k_t over the draw of S, followed by the same softmax,
  * Sparse V, value sum and inverse rotation.  Arguments as tq_decode_attn plus ks, the sketch of
  * the keys in k; the workspace is tq_decode_workspace_bytes(...).  Keys of 3 bits, values of 2
- * bits, groups up to 8 and no Sparse V run in one launch on matrix cores (the query's sketch
- * S R q and the sign products as fp16 matrix operands, the signs exact as +/-1); any other
- * widths, groups up to 16 and Sparse V take the fp32 vector kernels.
+ * bits and groups up to 8 run on matrix cores (the query's sketch S R q and the sign products
+ * as fp16 matrix operands, the signs exact as +/-1): one launch, or with Sparse V the key pass
+ * and the masked value pass; any other widths and groups up to 16 take the fp32 vector
+ * kernels.
  * Errors: as tq_decode_attn, and TQ_ERR_INVALID_ARG / TQ_ERR_UNSUPPORTED for the sketch. */
 int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cache *v, const void *q,
                        int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale,

@@ -120,3 +120,56 @@ def test_search_graph_replays_match_eager(n, nq, k):
         tq.ip_search(dbs[2], q, n, k, buffers=extra)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(extra.idx, eager_extra)
+
+
+@pytest.mark.parametrize("tau,hq", [(0.0, 16), (1e-4, 16), (1e-3, 8)])
+def test_qjl_graph_replays_match_eager(tau, hq):
+    """QJL decode (one launch, or Sparse V's key pass and masked value pass) recorded into a
+    graph over two caches, replayed with eager calls in between."""
+    print("graph qjl", tau, hq, flush=True)
+    w = inputs.WORKLOADS["qjl8k"]
+    batch, hkv, ctx = 2, 2, 3000
+    g = inputs.generate(w, device=DEV, batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
+    signs = inputs.rotation_signs().to(DEV)
+    proj = inputs.qjl_projection()
+    cap = (ctx + 63) // 64 * 64
+    caches = []
+    for c in range(2):
+        kc = tq.PackedCache(batch, hkv, cap, 3, tq.LAYOUT_ROWS, signs, device=DEV)
+        vc = tq.PackedCache(batch, hkv, cap, 2, tq.LAYOUT_GROUP8, signs, device=DEV)
+        sk = tq.QjlSketch(kc, proj, device=DEV)
+        k = g["k"] if c == 0 else g["k"].flip(1).contiguous()
+        tq.qjl_quantize_append(kc, sk, k.contiguous(), 0)
+        tq.quantize_append(vc, g["v"].contiguous(), 0)
+        caches.append((kc, sk, vc))
+    q = g["q"].contiguous()
+    sl = torch.tensor([ctx, ctx - 777], dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    bufs = [tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=DEV) for _ in caches]
+
+    def step(i):
+        kc, sk, vc = caches[i]
+        tq.qjl_decode_attn(kc, sk, vc, q, ctx, scale, tau=tau, seq_lens=sl, buffers=bufs[i])
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    eager = [(b.out.clone(), b.lse.clone()) for b in bufs]
+    assert not torch.equal(eager[0][0], eager[1][0])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(2):
+            step(i)
+    for rep in range(3):
+        for b in bufs:
+            b.out.fill_(float("nan"))
+            b.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(bufs):
+            assert torch.equal(b.out, eager[i][0]), f"replay {rep}, cache {i}: out differs"
+            assert torch.equal(b.lse, eager[i][1]), f"replay {rep}, cache {i}: lse differs"
+        step(0)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(bufs[0].out, eager[0][0])

@@ -113,6 +113,12 @@ def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, se
     ("ctx131k", 1, 16, 2, 2000, 2048, 3, 0.0, None),
     ("batch32k", 2, 8, 2, 1300, 1344, 3, 0.0, None),
     ("qjl8k", 1, 12, 4, 4100, 4160, 3, 0.0, None),
+    # Sparse V on matrix cores: the key pass (QJL scores, LSE partials, tile maxima), then the
+    # masked value pass recomputing the QJL scores of the tiles it needs
+    ("qjl8k", 2, 16, 2, 1000, 1024, 3, 1e-3, [1000, 1]),
+    ("ctx131k", 1, 16, 2, 5000, 5056, 3, 1e-4, None),
+    ("qjl8k", 3, 8, 2, 640, 640, 3, 1e-2, [640, 0, 65]),
+    ("batch32k", 1, 8, 2, 3100, 3136, 3, 1e-4, None),
 ])
 def test_qjl_decode_matches_oracle(case, golden_codebooks):
     name, batch, hq, hkv, ctx, cap, bk, tau, sl = case
