@@ -50,6 +50,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 matrix peak of the MI355X
 D = 128
 COPY_BYTES = 512 << 20
+STEADY_STEPS = 32  # back-to-back steps of the warm steady-state figure
 MAX_COPIES = 256   # small workloads are launch-bound; more copies only lengthen the set-up
 CALIBRATION_COPIES = 5
 CALIBRATION_KERNEL = "copyBuffer"   # the HIP runtime's device-to-device copy kernel
@@ -361,6 +362,7 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     v_new = v_all[:, ctx - 1:ctx].contiguous()
     host_k = k_all[:1].cpu() if not args.no_cpu_baseline else None
     host_v = v_all[:1].cpu() if not args.no_cpu_baseline else None
+    prefill = prefill_quantize_stats(args, w, caches, k_all, v_all, tq, torch, log)
     del k_all, v_all, g
     bufs = tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=dev, want_lse=True)
     scale = 1.0 / math.sqrt(D)
@@ -395,6 +397,9 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step if dense_single else decode_only, n_rep, 2, batches=5)
     ms_d = timer.per_iteration_ms(decode_only, n_rep, 2) if dense_single else ms_k
     ms_a = timer.per_iteration_ms(append, n_rep, 2)
+    # steady state of a decode loop over a resident cache: 32 back-to-back steps on one copy,
+    # caches warm (a small context stays in the L2s and the 256 MB last-level cache)
+    ms_ss = Timer(torch, args.eager, None).per_iteration_ms(lambda i: step(0), STEADY_STEPS, 2)
     nbytes = decode_bytes(w, bk, bv, hkv, batch, ctx)
     sparse_info = None
     if dense_single:
@@ -426,6 +431,9 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
                    "timing": "eager" if args.eager else "hip graph replay"},
         "decode_call_us": ms_d * 1e3,
         "append_kv_us": ms_a * 1e3,
+        "steady_state": {"us_per_step": ms_ss * 1e3, "kv_tokens_per_s": kv_tokens / (ms_ss / 1e3),
+                         "note": f"{STEADY_STEPS} back-to-back steps on one cache copy, caches warm"},
+        "prefill_quantize": prefill,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": f"{DECODE_KERNEL} (append + attend instance)" if dense_single
@@ -441,6 +449,28 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(w, tau, caches[0], host_k, host_v, q, signs, np, torch, log)
     return result
+
+
+def prefill_quantize_stats(args, w, caches, k_all, v_all, tq, torch, log):
+    """The whole context of every sequence quantized into the caches in one K-and-V call
+    (tq_quantize_append_kv at position 0): HBM-cold, rotated over the cache copies."""
+    batch, hkv, ctx, bk, bv = w.batch, w.n_kv_heads, w.ctx, w.bits_k, w.bits_v
+    k_all, v_all = k_all.contiguous(), v_all.contiguous()
+
+    def fill(i):
+        kc, vc = caches[i % len(caches)]
+        tq.quantize_append_kv(kc, vc, k_all, v_all, 0)
+
+    timer = Timer(torch, args.eager, cache_flush(torch, tq))
+    ms = timer.per_iteration_ms(fill, max(4, 2 * len(caches)), 1)
+    vectors = 2 * batch * ctx * hkv
+    nbytes = vectors * D * k_all.element_size() + batch * ctx * hkv * ((D * bk // 8 + 2) + (D * bv // 8 + 2))
+    log(f"[bench] prefill quantize of the whole cache: {ms * 1e3:.1f} us for {vectors} vectors "
+        f"({nbytes / (ms / 1e3) / 1e9:.0f} GB/s)")
+    return {"us": ms * 1e3, "tokens_per_s": batch * ctx / (ms / 1e3), "vectors_per_s": vectors / (ms / 1e3),
+            "vectors": vectors, "bytes": nbytes, "gbs": nbytes / (ms / 1e3) / 1e9,
+            "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "note": "every sequence's whole context, K and V of all kv heads, one tq_quantize_append_kv call"}
 
 
 def sparse_kept_rows(tq, torch, cache_pair, q, ctx, scale, tau, batch, hq, hkv, dev):
@@ -969,6 +999,12 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
         "_kernel": "quantize",
         "_launches": layers,
     }
+    mix = recorded_instmix("quantize_kv_kernel", w.name)
+    if mix is not None:
+        result["roofline"]["valu_issue_fraction"] = {
+            "value": mix.get("valu_issue_fraction"), "per_wave": mix.get("per_wave"),
+            "record": f"profiles/instmix_quantize_kv_kernel_{w.name}.txt",
+            "note": "vector-instruction issue cycles (4 per wave64 instruction) over the recorded launch time"}
     if not args.no_cpu_baseline:
         from oracle import tq_oracle as o
         s64 = signs.cpu().numpy().astype(np.float64)
@@ -990,6 +1026,16 @@ def bench_prefill(args, w, signs, dev, tq, inputs, torch, np, log):
             "value": reps * 1024 / el, "unit": result["unit"], "cores": cpu_cores(), "kind": "oracle",
             "sample": f"layer 5, 1024 positions x {hkv} kv heads, K4/V3, quantize+pack, {reps} reps"})
     return result
+
+
+def recorded_instmix(kernel, workload):
+    """The committed instruction-mix record of a kernel (rocprofv3 counters), or None."""
+    path = os.path.join(ROOT, "profiles", f"instmix_{kernel}_{workload}.txt")
+    try:
+        with open(path) as fh:
+            return json.load(fh)
+    except (OSError, ValueError):
+        return None
 
 
 def calibrate_copy(torch, log):
