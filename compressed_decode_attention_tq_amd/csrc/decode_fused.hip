@@ -1119,37 +1119,64 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // splits of row h: LSE merge of the partials, inverse rotation, output and LSE.
     auto merge_row = [&](int h) {
       // lane s of a chunk holds partial s's (m, l); every lane then sums its two
-      // coordinates over the partials, 16 loads in flight at a time
+      // coordinates over the partials, 16 loads in flight at a time.  With at most 64 partials
+      // (one per lane) each (m, l) is loaded once and the first 16 coordinate loads go out
+      // with it, before the maximum is known: one memory round trip where the general loop
+      // takes three.  Both add the partials in the same order.
       const size_t prow = vrow(h) * S;
       const float2 *pml = a.fpart_ml + prow;
       const float2 *pof = reinterpret_cast<const float2 *>(a.fpart_o + prow * kD) + lane;
-      float M = -INFINITY;
-      for (int s0 = 0; s0 < S; s0 += 64)
-        if (s0 + lane < S) M = fmaxf(M, load_coherent(pml + s0 + lane).x);
-      M = wave_reduce<true>(M);
-      float l = 0.f, o0 = 0.f, o1 = 0.f;
-      if (M != -INFINITY) {
-        for (int s0 = 0; s0 < S; s0 += 64) {
-          float w = 0.f;
-          if (s0 + lane < S) {
-            const float2 ml = load_coherent(pml + s0 + lane);
-            w = exp2_or_zero(ml.x, M);
-            l += ml.y * w;
+      float o0 = 0.f, o1 = 0.f;
+      auto load_o = [&](float2 (&o)[16], int base, int n) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          o[u] = base + u < n ? load_coherent(pof + (size_t)(base + u) * (kD / 2)) : make_float2(0.f, 0.f);
+      };
+      auto add_o = [&](const float2 (&o)[16], float w, int lane0) {  // partial lane0 + u is lane lane0 + u's
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), lane0 + u));
+          o0 += o[u].x * wu;
+          o1 += o[u].y * wu;
+        }
+      };
+      float M = -INFINITY, l = 0.f;
+      if (S <= 64) {
+        const float2 ml = lane < S ? load_coherent(pml + lane) : make_float2(-INFINITY, 0.f);
+        float2 o[16];
+        load_o(o, 0, S);
+        M = wave_reduce<true>(ml.x);
+        if (M != -INFINITY) {
+          const float w = exp2_or_zero(ml.x, M);
+          l = ml.y * w;
+          add_o(o, w, 0);
+          for (int s = 16; s < S; s += 16) {
+            load_o(o, s, S);
+            add_o(o, w, s);
           }
-          const int n = min(64, S - s0);
-          for (int s = 0; s < n; s += 16) {
-            float2 o[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-              o[u] = s + u < n ? load_coherent(pof + (size_t)(s0 + s + u) * (kD / 2)) : make_float2(0.f, 0.f);
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-              const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
-              o0 += o[u].x * wu;
-              o1 += o[u].y * wu;
+        }
+      } else {
+        for (int s0 = 0; s0 < S; s0 += 64)
+          if (s0 + lane < S) M = fmaxf(M, load_coherent(pml + s0 + lane).x);
+        M = wave_reduce<true>(M);
+        if (M != -INFINITY) {
+          for (int s0 = 0; s0 < S; s0 += 64) {
+            float w = 0.f;
+            if (s0 + lane < S) {
+              const float2 ml = load_coherent(pml + s0 + lane);
+              w = exp2_or_zero(ml.x, M);
+              l += ml.y * w;
+            }
+            const int n = min(64, S - s0);
+            for (int s = 0; s < n; s += 16) {
+              float2 o[16];
+              load_o(o, s0 + s, s0 + n);
+              add_o(o, w, s);
             }
           }
         }
+      }
+      if (M != -INFINITY) {
         l = wave_reduce<false>(l);
         // (VMASK partials are final weights already); the value table's scale comes off here
         const float norm = VMASK ? 1.f / a.v.table_scale : 1.f / (a.v.table_scale * l);
