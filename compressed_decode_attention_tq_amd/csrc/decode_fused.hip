@@ -1248,9 +1248,10 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       return;
     }
 
-    // ---- combine the waves of the split.  Round 1: (m, l) per head, 64 bytes per wave at
+    // ---- combine the waves of the split.  First pass: (m, l) per head, 64 bytes per wave at
     //      the start of the key-table region (free once every wave is past its tiles), so
-    //      that round 2 can write the staging buffers while other waves still read them.
+    //      that the second pass can write the staging buffers while other waves still read
+    //      them.
     float ltot[NH2];
 #pragma unroll
     for (int hh = 0; hh < NH2; ++hh) ltot[hh] = half_sum(lsum[hh]);
@@ -1296,7 +1297,7 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           a.cand_count[((size_t)b * a.n_kv_heads + kvh) * a.plan.n_splits + c_first + i] = chunk_count[i];
       return;
     }
-    // Round 2: scaled O rows of this wave, [head][128] fp32 (hi and remainder rows summed)
+    // Second pass: scaled O rows of this wave, [head][128] fp32 (hi and remainder rows summed)
     if (NH == 8 || quarter < 2) {
       const int h0 = 2 * quarter;
       float *dst0 = reinterpret_cast<float *>(wbuf) + h0 * kD + 8 * m_row;
