@@ -1115,6 +1115,32 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       if (tile < n_tiles) tile_body(tile, 0, std::false_type{});
     }
 
+    // Row h's output from its reference M, total l and rotated-domain sums (o0, o1) of the
+    // lane's coordinates 2 lane, 2 lane + 1: normalise, inverse rotation, output and LSE.
+    auto finish_row = [&](int h, float M, float l, float o0, float o1) {
+      if (M != -INFINITY) {
+        // (VMASK partials are final weights already); the value table's scale comes off here
+        const float norm = VMASK ? 1.f / a.v.table_scale : 1.f / (a.v.table_scale * l);
+        o0 *= norm;
+        o1 *= norm;
+      }
+      // inverse rotation: x = s * (H y) / sqrt(128)
+      float y0 = o0 + o1, y1 = o0 - o1;
+      wave_fwht_upper(y0, y1, lane);
+      y0 *= kInvSqrtD;
+      y1 *= kInvSqrtD;
+      if (sgn & 0x80u) y0 = -y0;  // the sign bytes loaded at set-up
+      if (sgn & 0x8000u) y1 = -y1;
+      const size_t orow = vrow(h);
+      *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
+      if (lane == 0 && a.lse != nullptr)
+        a.lse[orow] = VMASK ? lse_own : M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
+      if (a.scores != nullptr) {
+        float *row = a.scores + orow * a.ctx_len;
+        for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;
+      }
+    };
+
     // The last workgroup (PREFILL: the last wave) of a (batch, kv head, row group) merges the
     // splits of row h: LSE merge of the partials, inverse rotation, output and LSE.
     auto merge_row = [&](int h) {
@@ -1176,31 +1202,13 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
           }
         }
       }
-      if (M != -INFINITY) {
-        l = wave_reduce<false>(l);
-        // (VMASK partials are final weights already); the value table's scale comes off here
-        const float norm = VMASK ? 1.f / a.v.table_scale : 1.f / (a.v.table_scale * l);
-        o0 *= norm;
-        o1 *= norm;
-      }
-      // inverse rotation: x = s * (H y) / sqrt(128)
-      float y0 = o0 + o1, y1 = o0 - o1;
-      wave_fwht_upper(y0, y1, lane);
-      y0 *= kInvSqrtD;
-      y1 *= kInvSqrtD;
-      if (sgn & 0x80u) y0 = -y0;  // the sign bytes loaded at set-up
-      if (sgn & 0x8000u) y1 = -y1;
-      const size_t orow = vrow(h);
-      *reinterpret_cast<float2 *>(a.out + orow * kD + 2 * lane) = make_float2(y0, y1);
-      if (lane == 0 && a.lse != nullptr)
-        a.lse[orow] = VMASK ? lse_own : M == -INFINITY ? -INFINITY : (M + __log2f(l)) * kLn2;
-      if (a.scores != nullptr) {
-        float *row = a.scores + orow * a.ctx_len;
-        for (int t = T + lane; t < a.ctx_len; t += 64) row[t] = -INFINITY;
-      }    };
+      if (M != -INFINITY) l = wave_reduce<false>(l);
+      finish_row(h, M, l, o0, o1);
+    };
 
     if constexpr (PREFILL) {
-      // ---- this wave's rows alone: partials (m, l, O) per row, then its own arrival
+      // ---- this wave's rows alone: partials (m, l, O) per row, then its own arrival (with a
+      //      single split, the rows' outputs directly)
       float ltot[NH2];
 #pragma unroll
       for (int hh = 0; hh < NH2; ++hh) ltot[hh] = half_sum(lsum[hh]);
@@ -1222,6 +1230,17 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
       __builtin_amdgcn_wave_barrier();
       __asm__ volatile("" ::: "memory");
       if (!wave_on) return;
+      if (S == 1) {  // the wave saw the whole context: no partials, no arrival, no merge
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          if (!vlive(h)) continue;
+          const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr[h % NH2]), (h / NH2) * 32));
+          const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ltot[h % NH2]), (h / NH2) * 32));
+          const float2 o = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(wbuf) + h * kD + 2 * lane);
+          finish_row(h, mh, lh, o.x, o.y);
+        }
+        return;
+      }
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         if (!vlive(h)) continue;

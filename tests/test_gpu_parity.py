@@ -639,6 +639,10 @@ def _multi_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_len
     ("llama8k", 1, 8, 2, 1400, 1408, 4, 256),
     ("batch32k", 2, 16, 2, 900, 960, 3, 96),
     ("ctx131k", 1, 16, 2, 700, 704, 4, 33),
+    # prefill chunks over one split (contexts of at most 512 tokens): each wave writes its rows'
+    # outputs itself, with no partials and no merge
+    ("llama8k", 1, 8, 2, 500, 512, 4, 64),
+    ("batch32k", 2, 16, 2, 448, 448, 3, 40),
 ])
 def test_multi_query_matches_oracle(case, signs, golden_codebooks):
     """Several query positions per sequence (speculative verification, chunked prefill):
@@ -660,6 +664,8 @@ def test_multi_query_ragged_lengths_and_dtypes(signs, golden_codebooks):
     # a prefill chunk longer than one sequence (its first queries see nothing) and an empty one
     _multi_case(w, signs, golden_codebooks, 3, 8, 2, 700, 704, 4, 80, seq_lens=[700, 50, 0],
                 q_dtype=torch.float32)
+    # the same over one split (the rows' outputs written without partials)
+    _multi_case(w, signs, golden_codebooks, 3, 8, 2, 480, 512, 4, 80, seq_lens=[480, 50, 0])
 
 
 def test_decode_seq_lens_and_query_dtypes(signs, golden_codebooks):
