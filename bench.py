@@ -660,10 +660,9 @@ def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
     scale = 1.0 / math.sqrt(D)
     torch.cuda.synchronize()
 
-    def append(i):
+    def append(i):  # keys (codes and sketch) and values in one launch
         kc, sk, vc = caches[i % copies]
-        tq.qjl_quantize_append(kc, sk, k_new, ctx - 1)
-        tq.quantize_append(vc, v_new, ctx - 1)
+        tq.qjl_quantize_append_kv(kc, sk, vc, k_new, v_new, ctx - 1)
 
     def attend(i):
         kc, sk, vc = caches[i % copies]
@@ -689,7 +688,8 @@ def bench_qjl(args, w, signs, dev, tq, inputs, torch, np, log):
         "data": "synthetic (seeded; shapes and value distributions of the workload; seeded Gaussian sketch)",
         "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D, "ctx": ctx,
                    "bits_k": bk, "qjl_sketch_rows": m, "bits_v": bv,
-                   "step": "QJL key + value append (1 token) + decode attention with QJL-corrected scores",
+                   "step": "QJL key + value append (1 token, one launch) + decode attention with QJL-corrected "
+                           "scores",
                    "cache_copies": copies, "timing": "eager" if args.eager else "hip graph replay"},
         "decode_call_us": ms_k * 1e3, "append_us": ms_a * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.tq_ip_search.argtypes = [ctypes.POINTER(CacheStruct), vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         QP = ctypes.POINTER(QjlSketchStruct)
         L.tq_qjl_quantize_append.argtypes = [ctypes.POINTER(CacheStruct), QP, vp, i32, i32, i32, vp]
+        L.tq_qjl_quantize_append_kv.argtypes = [ctypes.POINTER(CacheStruct), QP, ctypes.POINTER(CacheStruct), vp, vp,
+                                                i32, i32, i32, vp]
         L.tq_qjl_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), QP, ctypes.POINTER(CacheStruct), vp, i32, i32,
                                          vp, i32, f32, f32, vp, vp, vp, vp, sz, vp]
         L.tq_ip_search_workspace_bytes.argtypes = [i32, i32, i32]
@@ -110,7 +112,8 @@ def lib() -> ctypes.CDLL:
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
                      "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
                      "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search",
-                     "tq_qjl_quantize_append", "tq_qjl_decode_attn", "tq_paged_decode_attn_ext"):
+                     "tq_qjl_quantize_append", "tq_qjl_quantize_append_kv", "tq_qjl_decode_attn",
+                     "tq_paged_decode_attn_ext"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -481,6 +484,22 @@ def qjl_quantize_append(k_cache: PackedCache, sketch: QjlSketch, x, start_pos: i
     st, ss = k_cache.struct(), sketch.struct()
     _check(lib().tq_qjl_quantize_append(ctypes.byref(st), ctypes.byref(ss), _dev(x, "x"), _dtype_code(x.dtype),
                                         start_pos, x.shape[1], _stream_ptr(stream)), "tq_qjl_quantize_append")
+
+
+def qjl_quantize_append_kv(k_cache: PackedCache, sketch: QjlSketch, v_cache: PackedCache, xk, xv, start_pos: int,
+                           stream=None):
+    """QJL keys and plain values of one step: xk into the key cache and its sketch, xv
+    [batch, n_tokens, n_kv_heads, d] into the value cache, positions start_pos .. +n_tokens (one
+    launch for up to 8 tokens)."""
+    for name, x in (("xk", xk), ("xv", xv)):
+        if x.dim() != 4 or x.shape[0] != k_cache.batch or x.shape[2] != k_cache.n_kv_heads or x.shape[3] != k_cache.d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if xk.shape != xv.shape or xk.dtype != xv.dtype:
+        raise ValueError(f"xk {tuple(xk.shape)} {xk.dtype} and xv {tuple(xv.shape)} {xv.dtype} differ")
+    ks, ss, vs = k_cache.struct(), sketch.struct(), v_cache.struct()
+    _check(lib().tq_qjl_quantize_append_kv(ctypes.byref(ks), ctypes.byref(ss), ctypes.byref(vs), _dev(xk, "xk"),
+                                           _dev(xv, "xv"), _dtype_code(xk.dtype), start_pos, xk.shape[1],
+                                           _stream_ptr(stream)), "tq_qjl_quantize_append_kv")
 
 
 def qjl_decode_attn(k_cache: PackedCache, sketch: QjlSketch, v_cache: PackedCache, q, ctx_len: int, scale: float,

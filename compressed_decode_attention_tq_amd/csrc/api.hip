@@ -556,6 +556,39 @@ int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void
   return hip_status(launch_qjl_quantize(a, k->batch, static_cast<hipStream_t>(hip_stream)));
 }
 
+int tq_qjl_quantize_append_kv(const tq_cache *k, const tq_qjl_sketch *s, const tq_cache *v, const void *xk,
+                              const void *xv, int x_dtype, int start_pos, int n_tokens, void *hip_stream) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_sketch(s);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->layout != TQ_LAYOUT_ROWS || v->layout != TQ_LAYOUT_GROUP8) return TQ_ERR_INVALID_ARG;
+  if (k->batch != v->batch || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity)
+    return TQ_ERR_INVALID_ARG;
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  if (start_pos < 0 || n_tokens < 0) return TQ_ERR_INVALID_ARG;
+  if ((long)start_pos + n_tokens > k->capacity) return TQ_ERR_CAPACITY;
+  if (n_tokens == 0) return TQ_OK;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  QjlQuantArgs a{};
+  a.k = view_of(k);
+  a.bits = s->bits;
+  a.res_norms = s->res_norms;
+  a.proj = s->proj;
+  a.x = xk;
+  a.x_dtype = x_dtype;
+  a.start_pos = start_pos;
+  a.n_tokens = n_tokens;
+  if (n_tokens <= kSmallAppendMax && k->batch <= 65535 && k->n_kv_heads <= 65535)  // a decode step: one launch
+    return hip_status(launch_qjl_quantize_kv_small(a, view_of(v), xv, k->batch, stream));
+  st = hip_status(launch_qjl_quantize(a, k->batch, stream));
+  if (st != TQ_OK) return st;
+  return hip_status(launch_quantize(view_of(v), v->batch, xv, x_dtype, start_pos, n_tokens, stream));
+}
+
 int tq_qjl_decode_attn(const tq_cache *k, const tq_qjl_sketch *ks, const tq_cache *v, const void *q, int q_dtype,
                        int n_q_heads, const int32_t *seq_lens, int ctx_len, float scale, float sparse_v_tau,
                        float *out, float *lse, float *scores, void *workspace, size_t workspace_bytes,

@@ -18,6 +18,7 @@
 #include "tq_launch.h"
 #include "lanes.h"
 #include "wave_quant.h"
+#include "append_plane.h"
 
 namespace tq {
 namespace {
@@ -101,10 +102,8 @@ constexpr int kQjlSmallMax = 8;   // tokens per call for this kernel
 constexpr int kQjlChunks = kD / 16;
 
 template <int DTYPE, int BITS>
-__global__ __launch_bounds__(64) void qjl_append_small_kernel(QjlQuantArgs a) {
-  __shared__ __align__(16) float res[kD];
-  __shared__ uint32_t words[4 * 8];
-  const int lane = threadIdx.x, chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__device__ void qjl_append_small_body(const QjlQuantArgs &a, int chunk, int h, int b, int lane, float *res,
+                                      uint32_t *words) {
   const int q = lane & 3;
   float4 srow[8];
   const float4 *src = reinterpret_cast<const float4 *>(a.proj + (size_t)(16 * chunk + (lane >> 2)) * kD + 32 * q);
@@ -159,6 +158,53 @@ __global__ __launch_bounds__(64) void qjl_append_small_kernel(QjlQuantArgs a) {
   }
 }
 
+template <int DTYPE, int BITS>
+__global__ __launch_bounds__(64) void qjl_append_small_kernel(QjlQuantArgs a) {
+  __shared__ __align__(16) float res[kD];
+  __shared__ uint32_t words[4 * 8];
+  qjl_append_small_body<DTYPE, BITS>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, res, words);
+}
+
+// Keys (with their sketch) and values of up to 8 tokens in one launch: blocks x < kQjlChunks of
+// (x, h, b) are the key blocks above (their first wave; the block has one wave per token for the
+// value blocks' sake), block x = kQjlChunks appends the tokens' values to plane (b, h) as the
+// small-append kernel does (one wave per token, then one update per 8-token value group).
+template <int DTYPE, int BK, int BV>
+__global__ __launch_bounds__(64 * kSmallAppendMax) void qjl_append_kv_small_kernel(QjlQuantArgs a, CacheView vc,
+                                                                                  const void *__restrict__ xv) {
+  __shared__ __align__(16) float res[kD];
+  __shared__ uint32_t words[4 * 8];
+  __shared__ SmallLds sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < kQjlChunks) {
+    if (wave == 0) qjl_append_small_body<DTYPE, BK>(a, blockIdx.x, blockIdx.y, blockIdx.z, lane, res, words);
+    return;  // (no block-wide barrier on this path)
+  }
+  append_plane<DTYPE, BV, false>(vc, xv, blockIdx.z, blockIdx.y, a.start_pos, a.n_tokens, wave, lane, sh);
+}
+
+template <int DTYPE, int BK>
+void launch_kv_small_bv(const QjlQuantArgs &a, const CacheView &vc, const void *xv, dim3 grid, hipStream_t stream) {
+  const int threads = 64 * a.n_tokens;
+  switch (vc.bits) {
+    case 2: qjl_append_kv_small_kernel<DTYPE, BK, 2><<<grid, threads, 0, stream>>>(a, vc, xv); break;
+    case 3: qjl_append_kv_small_kernel<DTYPE, BK, 3><<<grid, threads, 0, stream>>>(a, vc, xv); break;
+    case 4: qjl_append_kv_small_kernel<DTYPE, BK, 4><<<grid, threads, 0, stream>>>(a, vc, xv); break;
+    default: qjl_append_kv_small_kernel<DTYPE, BK, 8><<<grid, threads, 0, stream>>>(a, vc, xv); break;
+  }
+}
+
+template <int DTYPE>
+void launch_kv_small(const QjlQuantArgs &a, const CacheView &vc, const void *xv, dim3 grid, hipStream_t stream) {
+  switch (a.k.bits) {
+    case 2: launch_kv_small_bv<DTYPE, 2>(a, vc, xv, grid, stream); break;
+    case 3: launch_kv_small_bv<DTYPE, 3>(a, vc, xv, grid, stream); break;
+    case 4: launch_kv_small_bv<DTYPE, 4>(a, vc, xv, grid, stream); break;
+    default: launch_kv_small_bv<DTYPE, 8>(a, vc, xv, grid, stream); break;
+  }
+}
+
 template <int DTYPE>
 hipError_t launch_dtype(const QjlQuantArgs &a, dim3 grid, hipStream_t stream) {
   if (a.n_tokens <= kQjlSmallMax) {
@@ -181,6 +227,18 @@ hipError_t launch_dtype(const QjlQuantArgs &a, dim3 grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_qjl_quantize_kv_small(const QjlQuantArgs &a, const CacheView &vc, const void *xv, int batch,
+                                       hipStream_t stream) {
+  if (a.n_tokens < 1 || a.n_tokens > kQjlSmallMax || a.n_tokens > kSmallAppendMax || a.k.layout != TQ_LAYOUT_ROWS ||
+      vc.layout != TQ_LAYOUT_GROUP8 || batch < 1 || batch > 65535 || a.k.n_kv_heads > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid(kQjlChunks + 1, a.k.n_kv_heads, batch);
+  if (a.x_dtype == TQ_F32) launch_kv_small<TQ_F32>(a, vc, xv, grid, stream);
+  else if (a.x_dtype == TQ_BF16) launch_kv_small<TQ_BF16>(a, vc, xv, grid, stream);
+  else launch_kv_small<TQ_F16>(a, vc, xv, grid, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t stream) {
   if (a.n_tokens < 1 || a.k.layout != TQ_LAYOUT_ROWS) return hipErrorInvalidValue;

@@ -125,6 +125,10 @@ struct QjlQuantArgs {
   int start_pos, n_tokens;
 };
 hipError_t launch_qjl_quantize(const QjlQuantArgs &a, int batch, hipStream_t stream);
+// QJL keys and plain values of 1..8 tokens in one launch: a.k (with the sketch) as
+// launch_qjl_quantize, the value cache vc (groups of 8) from xv as launch_append_small.
+hipError_t launch_qjl_quantize_kv_small(const QjlQuantArgs &a, const CacheView &vc, const void *xv, int batch,
+                                       hipStream_t stream);
 // QJL decode on matrix cores (3-bit codes, 2-bit values, groups up to 8, no Sparse V): the fused
 // kernel with the query's sketch and the sign-sketch products.
 bool decode_fused_qjl_supported(const DecodeArgs &a);

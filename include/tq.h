@@ -210,6 +210,17 @@ int tq_decode_attn(const tq_cache *k, const tq_cache *v, const void *q, int q_dt
 int tq_qjl_quantize_append(const tq_cache *k, const tq_qjl_sketch *s, const void *x, int x_dtype,
                            int start_pos, int n_tokens, void *hip_stream);
 
+/* QJL residual variant, keys and values of one step: tq_qjl_quantize_append(k, s, xk, ...) and
+ * tq_quantize_append(v, xv, ...) over the same positions, with the same results, in one launch
+ * for up to 8 tokens (a decode step; two launches for longer ranges).
+ *   k, s       the key cache (ROWS) and its sketch, as for tq_qjl_quantize_append
+ *   v          the value cache (GROUP8), same batch, n_kv_heads and capacity as k
+ *   xk, xv     device in [batch][n_tokens][n_kv_heads][d] of x_dtype, 16-byte aligned
+ * Errors: TQ_ERR_INVALID_ARG (also for other layouts or mismatched caches), TQ_ERR_UNSUPPORTED,
+ * TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+int tq_qjl_quantize_append_kv(const tq_cache *k, const tq_qjl_sketch *s, const tq_cache *v, const void *xk,
+                              const void *xv, int x_dtype, int start_pos, int n_tokens, void *hip_stream);
+
 /* QJL residual variant, decode attention: tq_decode_attn with every score corrected by the key's
  * sign sketch ([google] _prod_score_kernel: the score against the codes plus the QJL term),
  *   s_t = scale ( ||k_t||_fp16 (R q) . c_K[idx_t]

@@ -280,6 +280,23 @@ def test_qjl_argument_validation():
     assert quant(_cache(layout=1, bits=3), sk()) == tq.TQ_ERR_INVALID_ARG
     assert quant(k, sk(), start=1020, n=16) == tq.TQ_ERR_CAPACITY
     assert quant(k, sk(), n=0) == tq.TQ_OK
+    vg = _cache(layout=1, bits=2)
+
+    def kv(kk, ss, vv, start=0, n=16, xv=FAKE + 0x580000):
+        return L.tq_qjl_quantize_append_kv(ctypes.byref(kk), ctypes.byref(ss), ctypes.byref(vv), x, xv, 1, start, n,
+                                           None)
+
+    assert kv(k, sk(), vg, n=0) == tq.TQ_OK
+    assert kv(k, sk(m=64), vg) == tq.TQ_ERR_UNSUPPORTED
+    assert kv(k, sk(bits=FAKE + 8), vg) == tq.TQ_ERR_INVALID_ARG
+    assert kv(k, sk(), _cache(layout=0, bits=2)) == tq.TQ_ERR_INVALID_ARG          # values in groups of 8
+    assert kv(_cache(layout=1, bits=3), sk(), vg) == tq.TQ_ERR_INVALID_ARG         # keys in rows
+    assert kv(k, sk(), _cache(layout=1, bits=2, batch=2)) == tq.TQ_ERR_INVALID_ARG  # caches disagree
+    assert kv(k, sk(), _cache(layout=1, bits=2, capacity=2048)) == tq.TQ_ERR_INVALID_ARG
+    assert kv(k, sk(), vg, xv=FAKE + 4) == tq.TQ_ERR_INVALID_ARG                   # misaligned input
+    assert kv(k, sk(), vg, xv=0) == tq.TQ_ERR_INVALID_ARG
+    assert kv(k, sk(), vg, start=1020, n=16) == tq.TQ_ERR_CAPACITY
+    assert kv(k, sk(), vg, start=-1, n=1) == tq.TQ_ERR_INVALID_ARG
     v = _cache(layout=1, bits=2)
     ws = tq.decode_workspace_bytes(1, 8, 2, 512, 0.0)
 

@@ -224,7 +224,7 @@ def test_chunk_full_size_sampled(golden_codebooks):
 
 def test_qjl_full_size_sampled(golden_codebooks):
     """qjl8k: 8191 keys through the QJL quantize and values through the quantize, the last token
-    through the step's own appends (the small kernels), then the QJL decode on matrix cores
+    through the step's own append (keys and values in one launch), then the QJL decode on matrix cores
     with scores; three kv heads' query heads against the oracle's attention over its effective
     keys from the GPU-written codes, sign bits and norms, and the new key against the oracle's
     QJL quantizer."""
@@ -240,8 +240,8 @@ def test_qjl_full_size_sampled(golden_codebooks):
     sk = tq.QjlSketch(kc, proj, device=DEV)
     tq.qjl_quantize_append(kc, sk, x["k"][:, : ctx - 1].contiguous(), 0)
     tq.quantize_append(vc, x["v"][:, : ctx - 1].contiguous(), 0)
-    tq.qjl_quantize_append(kc, sk, x["k"][:, ctx - 1:].contiguous(), ctx - 1)
-    tq.quantize_append(vc, x["v"][:, ctx - 1:].contiguous(), ctx - 1)
+    tq.qjl_quantize_append_kv(kc, sk, vc, x["k"][:, ctx - 1:].contiguous(), x["v"][:, ctx - 1:].contiguous(),
+                              ctx - 1)
     q = x["q"].contiguous()
     scale = 1.0 / math.sqrt(128)
     got = tq.qjl_decode_attn(kc, sk, vc, q, ctx, scale, want_scores=True)

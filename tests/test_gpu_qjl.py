@@ -57,6 +57,42 @@ def test_qjl_quantize_matches_oracle(bits, dtype, n_tok, start, golden_codebooks
     _say(f"  near-boundary coords {tot[0]}, near-zero sign bits {tot[1]}, tokens with a code flip {tot[2]}")
 
 
+@pytest.mark.parametrize("bk,bv,dtype,n_tok,start", [(3, 2, "bf16", 1, 8191), (3, 2, "f32", 3, 6), (4, 3, "f16", 8, 37),
+                                                     (2, 4, "bf16", 5, 0), (3, 2, "bf16", 20, 3)])
+def test_qjl_append_kv_equals_separate_calls(bk, bv, dtype, n_tok, start, golden_codebooks):
+    """The key-and-value call (one launch up to 8 tokens, two launches beyond) writes exactly the
+    bytes of tq_qjl_quantize_append on the keys and tq_quantize_append on the values: codes, norms,
+    sign bits, residual norms and every value group, including groups the range only partly
+    covers (their other tokens kept).  The separate calls themselves are checked against the
+    oracle above and in the small-append tests."""
+    _say("qjl append kv", bk, bv, dtype, n_tok, start)
+    w = inputs.WORKLOADS["qjl8k"]
+    g = inputs.generate(w, device="cpu", batch=2, ctx=n_tok, n_kv_heads=3, with_query=False)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[dtype]
+    xk, xv = g["k"].to(dt).to(DEV).contiguous(), g["v"].to(dt).to(DEV).contiguous()
+    signs = inputs.rotation_signs().to(DEV)
+    proj = inputs.qjl_projection()
+    cap = ((start + n_tok + 63) // 64) * 64
+    out = []
+    for fused in (False, True):
+        kc = tq.PackedCache(2, 3, cap, bk, tq.LAYOUT_ROWS, signs, device=DEV)
+        vc = tq.PackedCache(2, 3, cap, bv, tq.LAYOUT_GROUP8, signs, device=DEV)
+        sk = tq.QjlSketch(kc, proj, device=DEV)
+        for t, v in ((kc.codes, 0x5A), (kc.norms, 7), (vc.codes, 0xA5), (vc.norms, 9), (sk.bits, 0xC3),
+                     (sk.res_norms, 11)):
+            t.fill_(v)
+        if fused:
+            tq.qjl_quantize_append_kv(kc, sk, vc, xk, xv, start)
+        else:
+            tq.qjl_quantize_append(kc, sk, xk, start)
+            tq.quantize_append(vc, xv, start)
+        torch.cuda.synchronize()
+        out.append([t.clone() for t in (kc.codes, kc.norms, vc.codes, vc.norms, sk.bits, sk.res_norms)])
+    for name, a, b in zip(("key codes", "key norms", "value codes", "value norms", "sign bits", "residual norms"),
+                          *out):
+        assert torch.equal(a, b), name
+
+
 def _qjl_decode_case(name, batch, hq, hkv, ctx, cap, bits_k, golden, tau=0.0, seq_lens=None, q_dtype=None):
     _say("qjl decode", name, batch, hq, hkv, ctx, bits_k, tau, seq_lens, q_dtype)
     w = inputs.WORKLOADS[name]
