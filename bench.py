@@ -376,26 +376,30 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         kc, vc = caches[i % copies]
         tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs)
 
-    dense_single = tau == 0.0 and bk in (3, 4) and bv == 2 and w.group <= 8
+    # matrix-core widths: the step is one call that appends inside the attention: dense, one
+    # launch; Sparse V, the key pass (which writes the new token first) and the value pass
+    fused_step = bk in (3, 4) and bv == 2 and w.group <= 8
+    dense_single = fused_step and tau == 0.0
 
-    def append_and_decode(i):  # one launch: the fused kernel writes the new token, then attends
+    def append_and_decode(i):
         kc, vc = caches[i % copies]
-        tq.decode_attn_append(kc, vc, k_new, v_new, q, ctx, scale, buffers=bufs)
+        tq.decode_attn_append(kc, vc, k_new, v_new, q, ctx, scale, buffers=bufs, tau=tau)
 
     def two_launches(i):
         append(i)
         decode_only(i)
 
-    step = append_and_decode if dense_single else two_launches
+    step = append_and_decode if fused_step else two_launches
     timer = Timer(torch, args.eager, cache_flush(torch, tq))
     steps = args.steps
     ms_per_step = timer.per_iteration_ms(step, steps, args.warmup)
     kv_tokens = batch * ctx
     value = kv_tokens / (ms_per_step / 1e3)
     n_rep = max(args.steps, 2 * copies)
-    # the roofline kernel: the step's single launch when fused, else the decode call
-    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step if dense_single else decode_only, n_rep, 2, batches=5)
-    ms_d = timer.per_iteration_ms(decode_only, n_rep, 2) if dense_single else ms_k
+    # the roofline launches: the step's call when fused (dense: one launch; Sparse V: the key pass
+    # with the append and the value pass), else the decode call
+    ms_k, ms_k_min, ms_k_max = timer.per_iteration_stats(step if fused_step else decode_only, n_rep, 2, batches=5)
+    ms_d = timer.per_iteration_ms(decode_only, n_rep, 2) if fused_step else ms_k
     ms_a = timer.per_iteration_ms(append, n_rep, 2)
     # steady state of a decode loop over a resident cache: 32 back-to-back steps on one copy,
     # caches warm (a small context stays in the L2s and the 256 MB last-level cache)
@@ -410,13 +414,16 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         kept, kept_tiles, n_tiles = sparse_kept_rows(tq, torch, caches[0], q, ctx, scale, tau, batch, hq, hkv, dev)
         k_bytes = batch * hkv * ctx * (D * bk // 8 + 2)
         nbytes = k_bytes + kept * (D * bv // 8 + 2)
+        if fused_step:
+            nbytes += append_bytes(w, bk, bv, hkv, batch)
         sparse_info = {"kept_value_rows": kept, "kept_value_rows_frac": kept / (batch * hkv * ctx),
                        "tiles_with_kept_row_frac": kept_tiles / n_tiles, "key_bytes": k_bytes,
                        "dense_bytes": decode_bytes(w, bk, bv, hkv, batch, ctx)}
         log(f"[bench] Sparse V: {kept} of {batch * hkv * ctx} value rows kept by a group "
             f"({100 * kept / (batch * hkv * ctx):.2f}%), {100 * kept_tiles / n_tiles:.1f}% of 64-token tiles hold one")
     achieved = nbytes / (ms_k / 1e3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({'one fused launch' if dense_single else 'append + decode'}), "
+    how = 'one fused launch' if dense_single else 'key pass with the append + value pass' if fused_step else 'append + decode'
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({how}), "
         f"decode-only call {ms_d * 1e3:.1f} us, standalone append (K+V) {ms_a * 1e3:.1f} us, "
         f"roofline launch {ms_k * 1e3:.1f} us = {achieved:.0f} GB/s algorithmic")
     result = {
@@ -427,7 +434,8 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         "config": {"workload": w.name, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "d": D,
                    "ctx": ctx, "bits_k": bk, "bits_v": bv, "sparse_v_tau": tau,
                    "step": ("append 1 token (K,V) + decode attention, one fused launch" if dense_single
-                            else "append 1 token (K,V) + decode attention"), "cache_copies": copies,
+                            else "append 1 token (K,V) in Sparse V's key pass, then the masked value pass"
+                            if fused_step else "append 1 token (K,V) + decode attention"), "cache_copies": copies,
                    "timing": "eager" if args.eager else "hip graph replay"},
         "decode_call_us": ms_d * 1e3,
         "append_kv_us": ms_a * 1e3,
@@ -437,14 +445,16 @@ def bench_decode(args, w, tau, signs, dev, tq, inputs, torch, np, log):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": f"{DECODE_KERNEL} (append + attend instance)" if dense_single
-                     else "decode attention call (Sparse V: key pass + masked value pass on matrix cores where the widths allow)",
+                     else f"{DECODE_KERNEL}: Sparse V's key pass (with the append) + masked value pass" if fused_step
+                     else "decode attention call (Sparse V: key pass + masked value pass)",
                      "bytes_per_launch": nbytes, "launch_us": ms_k * 1e3,
                      "launch_us_min_max": [ms_k_min * 1e3, ms_k_max * 1e3]},
         "_kernel": "decode" if dense_single else "decode_sparse",
     }
     if sparse_info is not None:
         result["roofline"]["bytes_note"] = ("algorithmic bytes: every key (codes + norm) plus the value rows "
-                                            "kept by the union of the group's heads")
+                                            "kept by the union of the group's heads"
+                                            + (", plus the appended token's input and codes" if fused_step else ""))
         result["sparse_v"] = sparse_info
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(w, tau, caches[0], host_k, host_v, q, signs, np, torch, log)

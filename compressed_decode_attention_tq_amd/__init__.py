@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.tq_decode_attn_append.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp, i32,
                                             vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.tq_decode_attn_append_sparse.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp,
+                                                   i32, vp, i32, i32, vp, i32, f32, f32, vp, vp, vp, sz, vp]
         L.tq_decode_attn_multi_workspace_bytes.restype = sz
         L.tq_decode_attn_append_noalloc.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp,
                                                     vp, i32, vp, i32, i32, vp, i32, f32, vp, vp, vp]
@@ -110,7 +112,8 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
+                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_sparse",
+                     "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
                      "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search",
                      "tq_qjl_quantize_append", "tq_qjl_quantize_append_kv", "tq_qjl_decode_attn",
                      "tq_paged_decode_attn_ext"):
@@ -396,9 +399,12 @@ def decode_attn_multi(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: in
 
 
 def decode_attn_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new, q, ctx_len: int,
-                       scale: float, seq_lens=None, buffers: DecodeBuffers | None = None, stream=None):
-    """Quantize k_new, v_new [B, 1, Hkv, d] into position T_b - 1 of each sequence, then dense
-    decode attention (one launch where the fused kernel applies); returns the DecodeBuffers."""
+                       scale: float, seq_lens=None, buffers: DecodeBuffers | None = None, stream=None,
+                       tau: float = 0.0):
+    """Quantize k_new, v_new [B, 1, Hkv, d] into position T_b - 1 of each sequence, then decode
+    attention: dense (one launch where the fused kernel applies), or with Sparse V at tau > 0
+    (the new token written by the key pass where it runs on matrix cores); returns the
+    DecodeBuffers (sized for tau)."""
     _check_query(q, k_cache, 3, "decode_attn_append")
     bsz, hq, d = q.shape
     for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
@@ -408,15 +414,18 @@ def decode_attn_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new,
         raise ValueError("k_new and v_new must have the same dtype")
     _check_seq_lens(seq_lens, bsz, "decode_attn_append")
     if buffers is None:
-        buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, 0.0, device=q.device, d=d)
+        buffers = DecodeBuffers(bsz, hq, k_cache.n_kv_heads, ctx_len, tau, device=q.device, d=d)
     _check_outputs(buffers, (bsz, hq, d), (bsz, hq), "decode_attn_append")
     ks, vs = k_cache.struct(), v_cache.struct()
     sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
-    _check(lib().tq_decode_attn_append(
-        ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
-        _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len, float(scale), _dev(buffers.out, "out"),
-        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
-        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_append")
+    head = (ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
+            _dev(q, "q"), _dtype_code(q.dtype), hq, sl, ctx_len, float(scale))
+    tail = (_dev(buffers.out, "out"), _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+            ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream))
+    if tau == 0.0:
+        _check(lib().tq_decode_attn_append(*head, *tail), "tq_decode_attn_append")
+    else:
+        _check(lib().tq_decode_attn_append_sparse(*head, float(tau), *tail), "tq_decode_attn_append_sparse")
     return buffers
 
 

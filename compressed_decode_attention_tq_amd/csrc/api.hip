@@ -658,6 +658,39 @@ int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, 
   return hip_status(launch_decode(a, stream));
 }
 
+int tq_decode_attn_append_sparse(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                                 const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len,
+                                 float scale, float sparse_v_tau, float *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream) {
+  if (!(sparse_v_tau >= 0.f && sparse_v_tau < 1.f)) return TQ_ERR_INVALID_ARG;
+  if (sparse_v_tau == 0.f)
+    return tq_decode_attn_append(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, out, lse,
+                                 workspace, workspace_bytes, hip_stream);
+  DecodeArgs chk{};
+  WorkspaceLayout w{};
+  int st = setup_decode_append(k, v, xk, xv, x_dtype, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, out, lse,
+                               chk, w);  // the append's checks
+  if (st != TQ_OK) return st;
+  DecodeArgs a{};
+  st = setup_decode(k, v, q, q_dtype, n_q_heads, seq_lens, ctx_len, scale, sparse_v_tau, out, lse, nullptr, workspace,
+                    workspace_bytes, a);
+  if (st != TQ_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  DecodeArgs k1 = a;  // the key pass writes each sequence's new token at T - 1 first
+  k1.xk = xk;
+  k1.xv = xv;
+  k1.x_dtype = x_dtype;
+  hipError_t e = launch_sparse_two_pass(k1, stream);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  // other code widths or groups: the append kernel, then the decode call (one common position)
+  if (seq_lens != nullptr) return TQ_ERR_UNSUPPORTED;
+  if (ctx_len >= 1) {
+    e = launch_append_small(a.k, a.v, k->batch, xk, xv, x_dtype, ctx_len - 1, 1, stream);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+  }
+  return hip_status(launch_decode(a, stream));
+}
+
 int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
                          int n_q_heads, int n_q, const int32_t *seq_lens, int ctx_len, float scale,
                          float *out, float *lse, void *workspace, size_t workspace_bytes,

@@ -538,10 +538,14 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     build_tables<BK, !SPARSE>(lds, kcs, vcs_s);  // read only after the barriers below
     if constexpr (QJL) build_sign_table(lds);
     // 3-bit rows are assembled in the first 48 bytes of the wave's own buffer: during set-up
-    // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's)
+    // no other wave writes there (the rotated query's rows 1.. start at byte 512 of wave 0's).
+    // The key-only pass has 2 KB buffers, where the rotated query of 8 heads covers those of
+    // waves 0 and 1: there the rows go behind the 16 KB table of 3-bit keys, a region the pass
+    // does not use.
     if (appends) {
-      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, lds + kWBase + wave * WSTRIDE);
-      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, lds + kWBase + wave * WSTRIDE);
+      uint8_t *ascr = KEYS_ONLY ? lds + 16 * 1024 + wave * 64 : lds + kWBase + wave * WSTRIDE;
+      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, ascr);
+      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, ascr);
     }
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
@@ -1554,6 +1558,10 @@ hipError_t launch_decode_fused_vmask(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_fused_sparse(const DecodeArgs &a, hipStream_t stream) {
   const long items = (long)a.batch * a.n_kv_heads * a.fplan.n_splits;
   if (items < 1 || items > 0x7fffffffL) return hipErrorInvalidValue;
+  if (a.cand == nullptr && a.xk != nullptr)  // the same, the decode step's new token written first
+    return a.k.bits == 4 ? launch_nh<4, true, false, true, false, false, false>(a, (int)items, stream)
+                         : launch_nh<3, true, false, true, false, false, false>(a, (int)items, stream);
+  if (a.xk != nullptr) return hipErrorInvalidValue;  // (appends go with the key-only pass alone)
   if (a.cand == nullptr)  // the LSE and tile maxima only (before the masked value pass)
     return a.k.bits == 4 ? launch_nh<4, true, false, false, false, false, false>(a, (int)items, stream)
                          : launch_nh<3, true, false, false, false, false, false>(a, (int)items, stream);

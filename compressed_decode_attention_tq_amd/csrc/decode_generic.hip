@@ -540,29 +540,38 @@ static hipError_t finish_split_decode(const DecodeArgs &a, dim3 grid_split, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
-  if (decode_fused_supported(args)) return launch_decode_fused(args, compute_units(), stream);
-  DecodeArgs a = args;
-  dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
-  hipError_t e;
+hipError_t launch_sparse_two_pass(const DecodeArgs &a, hipStream_t stream) {
   // Sparse V on matrix cores, two launches: the key pass (no candidate records) for each
   // row's LSE, then the dense kernel with the rows under the final-weight threshold masked
-  // out of the value product; it merges its splits itself.  (Values of 2 bits.)
+  // out of the value product; it merges its splits itself.  (Values of 2 bits.)  With a.xk
+  // set, the key pass first writes the decode step's new key and value.
   DecodeArgs v2 = a;
   v2.sparse = 0;
+  v2.xk = v2.xv = nullptr;
   v2.lse_ml = a.fpart_ml;
   v2.lse_splits = a.fplan.n_splits;
   v2.fplan = plan_fused_vmask(a.batch, a.n_kv_heads, a.ctx_len);  // at most 64 tiles per split
   v2.fpart_ml = a.vpart_ml;
   v2.fpart_o = a.vpart_o;
-  if (a.sparse && decode_fused_sparse_supported(a) && a.vpart_ml != nullptr && a.tile_max != nullptr &&
-      decode_fused_supported(v2)) {
-    DecodeArgs k1 = a;
-    k1.cand = nullptr;
-    k1.cand_count = nullptr;
-    e = launch_decode_fused_sparse(k1, stream);
-    if (e != hipSuccess) return e;
-    return launch_decode_fused_vmask(v2, stream);
+  if (!(a.sparse && decode_fused_sparse_supported(a) && a.vpart_ml != nullptr && a.tile_max != nullptr &&
+        decode_fused_supported(v2)))
+    return hipErrorNotSupported;
+  DecodeArgs k1 = a;
+  k1.cand = nullptr;
+  k1.cand_count = nullptr;
+  const hipError_t e = launch_decode_fused_sparse(k1, stream);
+  if (e != hipSuccess) return e;
+  return launch_decode_fused_vmask(v2, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs &args, hipStream_t stream) {
+  if (decode_fused_supported(args)) return launch_decode_fused(args, compute_units(), stream);
+  DecodeArgs a = args;
+  dim3 grid_split(a.plan.n_splits, a.n_kv_heads, a.batch);
+  hipError_t e;
+  if (a.sparse) {
+    e = launch_sparse_two_pass(a, stream);
+    if (e != hipErrorNotSupported) return e;
   }
   if (decode_fused_sparse_supported(a)) {  // key-only fused first pass
     a.lse_ml = a.fpart_ml;

@@ -192,6 +192,10 @@ hipError_t launch_ip_search(const CacheView &db, const void *q, int q_dtype, int
 hipError_t launch_dequantize(const CacheView &c, int batch, void *out, int out_dtype,
                              int start_pos, int n_tokens, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Sparse V's two matrix-core passes (key pass, masked value pass); with a.xk set the key pass
+// first writes the decode step's new token.  hipErrorNotSupported, with nothing launched,
+// where that path does not apply (other widths, groups above 8).
+hipError_t launch_sparse_two_pass(const DecodeArgs &a, hipStream_t stream);
 int compute_units();
 bool decode_mfma_supported(const DecodeArgs &a);
 bool decode_fused_supported(const DecodeArgs &a);

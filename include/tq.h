@@ -262,6 +262,22 @@ int tq_decode_attn_append(const tq_cache *k, const tq_cache *v, const void *xk, 
                           const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Append and attend with Sparse V ([inferrs] §Sparse V): as tq_decode_attn_append, then decode
+ * attention exactly as tq_decode_attn at sparse_v_tau (no scores).  sparse_v_tau = 0 is
+ * tq_decode_attn_append.  For tau in (0, 1) with keys of 3/4 bits, values of 2 bits and
+ * n_q_heads / n_kv_heads <= 8, the new token goes in with Sparse V's first pass (the wave that
+ * reads position T - 1 writes the key and value first), so the step is the key pass and the
+ * masked value pass, two launches; otherwise the append kernel and the decode call, which
+ * needs seq_lens == NULL (TQ_ERR_UNSUPPORTED otherwise).
+ *   sparse_v_tau  0 or a threshold in (0, 1)
+ *   workspace     tq_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, ctx_len, sparse_v_tau)
+ *   the other arguments as for tq_decode_attn_append
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_decode_attn_append_sparse(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                                 const void *q, int q_dtype, int n_q_heads, const int32_t *seq_lens, int ctx_len,
+                                 float scale, float sparse_v_tau, float *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream);
+
 /* tq_decode_attn_append for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same one-launch decode
  * step with the same arguments and results, except that there is no workspace argument.  Its

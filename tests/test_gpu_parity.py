@@ -357,6 +357,65 @@ def _append_case(w, signs, golden, batch, hq, hkv, ctx, cap, bits_k, bits_v, seq
 
 
 @pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, bits_v, tau, seq_lens)
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 2, 1e-4, [1500, 1]),            # 8-wave key pass
+    # 256 planes with splits of 3072+ tokens: the 16-wave (4-head groups) and 12-wave (8-head
+    # groups) key passes, 3-bit rows assembled behind the 3-bit table; ragged, one empty
+    ("batch32k", 32, 32, 8, 3100, 3136, 3, 2, 1e-3, [3100 - 37 * i for i in range(31)] + [0]),
+    ("ctx131k", 32, 64, 8, 3100, 3136, 4, 2, 1e-4, [3100 - 41 * i for i in range(31)] + [0]),
+    ("batch32k", 32, 64, 8, 3100, 3136, 3, 2, 1e-3, [3100 - 43 * i for i in range(31)] + [0]),
+    ("llama8k", 1, 8, 2, 333, 384, 8, 8, 1e-3, None),                    # other widths: two launches
+])
+def test_decode_append_sparse_equals_append_then_decode(case, signs, golden_codebooks):
+    """Sparse V with the decode step's append (tq_decode_attn_append_sparse): the key pass writes
+    each sequence's new key and value at T_b - 1 before reading that tile.  The caches must hold
+    exactly the bytes the dense append-and-attend call writes, and the outputs and LSE must equal
+    those of tq_decode_attn at the same tau on those caches (itself checked against the oracle
+    in the Sparse V tests)."""
+    name, batch, hq, hkv, ctx, cap, bk, bv, tau, seq_lens = case
+    _say("append + sparse decode", case)
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq)
+    lens = [ctx] * batch if seq_lens is None else list(seq_lens)
+    k_new = torch.zeros((batch, 1, hkv, 128), dtype=g["k"].dtype)
+    v_new = torch.zeros((batch, 1, hkv, 128), dtype=g["v"].dtype)
+    for b, tb in enumerate(lens):
+        if tb >= 1:
+            k_new[b, 0], v_new[b, 0] = g["k"][b, tb - 1], g["v"][b, tb - 1]
+    k_new, v_new = k_new.to(DEV).contiguous(), v_new.to(DEV).contiguous()
+    scale = 1.0 / math.sqrt(128)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    q = g["q"].to(DEV).contiguous()
+    caches = []
+    for _ in range(2):
+        kc = _new_cache(batch, hkv, cap, bk, 0, signs)
+        vc = _new_cache(batch, hkv, cap, bv, 1, signs)
+        _fill(kc, (g["k"] * -0.5).to(DEV))  # stale contents at every T_b - 1
+        _fill(vc, (g["v"] * 1.5).to(DEV))
+        _fill(kc, g["k"][:, : ctx - 1].to(DEV).contiguous())
+        _fill(vc, g["v"][:, : ctx - 1].to(DEV).contiguous())
+        caches.append((kc, vc))
+    (ka, va), (kb, vb) = caches
+    got = tq.decode_attn_append(ka, va, k_new, v_new, q, ctx, scale, seq_lens=sl, tau=tau)
+    if seq_lens is None:  # the reference append: the small-append kernel at the common position
+        tq.quantize_append_kv(kb, vb, k_new, v_new, ctx - 1)
+    else:  # the dense append-and-attend call writes each sequence's token at T_b - 1
+        tq.decode_attn_append(kb, vb, k_new, v_new, q, ctx, scale, seq_lens=sl)
+    ref = tq.decode_attn(kb, vb, q, ctx, scale, tau=tau, seq_lens=sl)
+    torch.cuda.synchronize()
+    for what, x, y in (("key codes", ka.codes, kb.codes), ("key norms", ka.norms, kb.norms),
+                       ("value codes", va.codes, vb.codes), ("value norms", va.norms, vb.norms)):
+        assert torch.equal(x, y), what
+    d_out = (got.out - ref.out).abs().max().item()
+    scale_out = ref.out.abs().max().item()
+    fin = torch.isfinite(ref.lse)
+    assert torch.equal(torch.isfinite(got.lse), fin)
+    d_lse = (got.lse[fin] - ref.lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
+    _say(f"  max |out diff| {d_out:.2e} (of {scale_out:.2e}), max |lse diff| {d_lse:.2e}")
+    assert d_out <= 1e-6 * max(scale_out, 1e-30) and d_lse <= 1e-6 * max(1.0, ref.lse[fin].abs().max().item())
+
+
+@pytest.mark.parametrize("case", [
     # (workload, batch, hq, hkv, ctx, cap, bits_k, bits_v, seq_lens, x dtype)
     ("llama8k", 1, 32, 8, 700, 768, 4, 2, None, None),
     ("batch32k", 2, 8, 2, 1300, 1344, 3, 2, None, None),
