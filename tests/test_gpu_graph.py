@@ -20,13 +20,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("workload,tau,batch,ctx", [
-    ("llama8k", 0.0, 2, 2048 + 37), ("ctx131k", 0.0, 2, 2048 + 37), ("batch32k", 1e-4, 2, 2048 + 37),
+@pytest.mark.parametrize("workload,tau,batch,ctx,fused", [
+    ("llama8k", 0.0, 2, 2048 + 37, False), ("ctx131k", 0.0, 2, 2048 + 37, False),
+    ("batch32k", 1e-4, 2, 2048 + 37, False),
     # splits of 3072+ tokens: 12 waves per workgroup (dense), 16 and 12 in the key pass
-    ("batch32k", 0.0, 32, 3100), ("batch32k", 1e-4, 32, 3100), ("ctx131k", 1e-4, 64, 6200),
+    ("batch32k", 0.0, 32, 3100, False), ("batch32k", 1e-4, 32, 3100, False), ("ctx131k", 1e-4, 64, 6200, False),
+    # the decode step as one call: append inside the dense launch, or inside Sparse V's key pass
+    ("llama8k", 0.0, 2, 2048 + 37, True), ("ctx131k", 1e-4, 2, 2048 + 37, True), ("batch32k", 1e-4, 32, 3100, True),
 ])
-def test_graph_replays_match_eager(workload, tau, batch, ctx):
-    print("graph", workload, tau, batch, ctx, flush=True)
+def test_graph_replays_match_eager(workload, tau, batch, ctx, fused):
+    print("graph", workload, tau, batch, ctx, fused, flush=True)
     sys.stdout.flush()
     w = inputs.WORKLOADS[workload]
     hkv = w.n_kv_heads
@@ -49,6 +52,9 @@ def test_graph_replays_match_eager(workload, tau, batch, ctx):
 
     def step(i):
         kc, vc = caches[i]
+        if fused:
+            tq.decode_attn_append(kc, vc, k_new, v_new, q, ctx, scale, buffers=bufs[i], tau=tau)
+            return
         tq.quantize_append(kc, k_new, ctx - 1)
         tq.quantize_append(vc, v_new, ctx - 1)
         tq.decode_attn(kc, vc, q, ctx, scale, tau=tau, buffers=bufs[i])
@@ -124,8 +130,9 @@ def test_search_graph_replays_match_eager(n, nq, k):
 
 @pytest.mark.parametrize("tau,hq", [(0.0, 16), (1e-4, 16), (1e-3, 8)])
 def test_qjl_graph_replays_match_eager(tau, hq):
-    """QJL decode (one launch, or Sparse V's key pass and masked value pass) recorded into a
-    graph over two caches, replayed with eager calls in between."""
+    """The QJL decode step (the key-and-value append in one launch, then the decode: one launch,
+    or Sparse V's key pass and masked value pass) recorded into a graph over two caches,
+    replayed with eager calls in between."""
     print("graph qjl", tau, hq, flush=True)
     w = inputs.WORKLOADS["qjl8k"]
     batch, hkv, ctx = 2, 2, 3000
@@ -147,8 +154,12 @@ def test_qjl_graph_replays_match_eager(tau, hq):
     scale = 1.0 / math.sqrt(128)
     bufs = [tq.DecodeBuffers(batch, hq, hkv, ctx, tau, device=DEV) for _ in caches]
 
-    def step(i):
+    k_new = g["k"][:, ctx - 1:].contiguous()
+    v_new = g["v"][:, ctx - 1:].contiguous()
+
+    def step(i):  # the decode step: keys (with their sketch) and values in one launch, then attend
         kc, sk, vc = caches[i]
+        tq.qjl_quantize_append_kv(kc, sk, vc, k_new, v_new, ctx - 1)
         tq.qjl_decode_attn(kc, sk, vc, q, ctx, scale, tau=tau, seq_lens=sl, buffers=bufs[i])
 
     for i in range(2):
