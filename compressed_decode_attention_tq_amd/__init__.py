@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_workspace_bytes.restype = sz
         L.tq_decode_attn_multi.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, i32,
                                            i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.tq_decode_attn_multi_append.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp,
+                                                  i32, vp, i32, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
         L.tq_decode_attn_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.tq_decode_attn_append.argtypes = [ctypes.POINTER(CacheStruct), ctypes.POINTER(CacheStruct), vp, vp, i32,
                                             vp, i32, i32, vp, i32, f32, vp, vp, vp, sz, vp]
@@ -112,7 +114,8 @@ def lib() -> ctypes.CDLL:
         L.tq_status_string.argtypes = [i32]
         L.tq_status_string.restype = ctypes.c_char_p
         for name in ("tq_make_codebook_table", "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_attn",
-                     "tq_decode_attn_multi", "tq_decode_attn_append", "tq_decode_attn_append_sparse",
+                     "tq_decode_attn_multi", "tq_decode_attn_multi_append", "tq_decode_attn_append",
+                     "tq_decode_attn_append_sparse",
                      "tq_decode_attn_append_noalloc", "tq_dequantize", "tq_probe_stream_read",
                      "tq_paged_quantize_append_kv", "tq_paged_decode_attn", "tq_paged_decode_attn_append", "tq_ip_search",
                      "tq_qjl_quantize_append", "tq_qjl_quantize_append_kv", "tq_qjl_decode_attn",
@@ -395,6 +398,32 @@ def decode_attn_multi(k_cache: PackedCache, v_cache: PackedCache, q, ctx_len: in
         float(scale), _dev(buffers.out, "out"),
         _dev(buffers.lse, "lse") if buffers.lse is not None else None,
         ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_multi")
+    return buffers
+
+
+def decode_attn_multi_append(k_cache: PackedCache, v_cache: PackedCache, k_new, v_new, q, ctx_len: int, scale: float,
+                             seq_lens=None, buffers: MultiQueryBuffers | None = None, stream=None):
+    """Quantize k_new, v_new [B, n_q, Hkv, d] into positions T_b - n_q .. T_b - 1, then
+    decode_attn_multi for q [B, n_q, Hq, d] (one launch for up to 8 positions); returns the
+    MultiQueryBuffers."""
+    _check_query(q, k_cache, 4, "decode_attn_multi_append")
+    bsz, n_q, hq, d = q.shape
+    for name, cache, x in (("k_new", k_cache, k_new), ("v_new", v_cache, v_new)):
+        if x.dim() != 4 or x.shape[0] != bsz or x.shape[1] != n_q or x.shape[2] != cache.n_kv_heads or x.shape[3] != d:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    _check_seq_lens(seq_lens, bsz, "decode_attn_multi_append")
+    if buffers is None:
+        buffers = MultiQueryBuffers(bsz, n_q, hq, k_cache.n_kv_heads, ctx_len, device=q.device, d=d)
+    _check_outputs(buffers, (bsz, n_q, hq, d), (bsz, n_q, hq), "decode_attn_multi_append")
+    ks, vs = k_cache.struct(), v_cache.struct()
+    sl = _dev(seq_lens, "seq_lens") if seq_lens is not None else None
+    _check(lib().tq_decode_attn_multi_append(
+        ctypes.byref(ks), ctypes.byref(vs), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new.dtype),
+        _dev(q, "q"), _dtype_code(q.dtype), hq, n_q, sl, ctx_len, float(scale), _dev(buffers.out, "out"),
+        _dev(buffers.lse, "lse") if buffers.lse is not None else None,
+        ctypes.c_void_p(buffers.ws_ptr), buffers.ws_bytes, _stream_ptr(stream)), "tq_decode_attn_multi_append")
     return buffers
 
 

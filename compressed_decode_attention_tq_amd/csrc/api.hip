@@ -691,10 +691,10 @@ int tq_decode_attn_append_sparse(const tq_cache *k, const tq_cache *v, const voi
   return hip_status(launch_decode(a, stream));
 }
 
-int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
-                         int n_q_heads, int n_q, const int32_t *seq_lens, int ctx_len, float scale,
-                         float *out, float *lse, void *workspace, size_t workspace_bytes,
-                         void *hip_stream) {
+// Validation and arguments of a multi-query call (everything but the append inputs).
+static int setup_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype, int n_q_heads, int n_q,
+                       const int32_t *seq_lens, int ctx_len, float scale, float *out, float *lse, void *workspace,
+                       size_t workspace_bytes, DecodeArgs &a) {
   int st = check_cache(k);
   if (st != TQ_OK) return st;
   st = check_cache(v);
@@ -718,7 +718,7 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
 
   const MultiQueryShape m = multi_query_shape(group, n_q);
-  DecodeArgs a{};
+  a = DecodeArgs{};
   a.k = view_of(k);
   a.v = view_of(v);
   a.q = q;
@@ -741,8 +741,46 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
   a.counters = reinterpret_cast<unsigned *>(ws + w.counters);
   a.fpart_ml = reinterpret_cast<float2 *>(ws + w.fpart_ml);
   a.fpart_o = reinterpret_cast<float *>(ws + w.fpart_o);
-  if (!decode_fused_supported(a)) return TQ_ERR_UNSUPPORTED;
+  return decode_fused_supported(a) ? TQ_OK : TQ_ERR_UNSUPPORTED;
+}
+
+
+int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, int q_dtype,
+                         int n_q_heads, int n_q, const int32_t *seq_lens, int ctx_len, float scale,
+                         float *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *hip_stream) {
+  DecodeArgs a{};
+  const int st = setup_multi(k, v, q, q_dtype, n_q_heads, n_q, seq_lens, ctx_len, scale, out, lse, workspace,
+                             workspace_bytes, a);
+  if (st != TQ_OK) return st;
   return hip_status(launch_decode_fused(a, compute_units(), static_cast<hipStream_t>(hip_stream)));
+}
+
+int tq_decode_attn_multi_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                                const void *q, int q_dtype, int n_q_heads, int n_q, const int32_t *seq_lens,
+                                int ctx_len, float scale, float *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *hip_stream) {
+  if (xk == nullptr || xv == nullptr || !aligned(xk, 16) || !aligned(xv, 16) || !valid_dtype(x_dtype))
+    return TQ_ERR_INVALID_ARG;
+  DecodeArgs a{};
+  const int st = setup_multi(k, v, q, q_dtype, n_q_heads, n_q, seq_lens, ctx_len, scale, out, lse, workspace,
+                             workspace_bytes, a);
+  if (st != TQ_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (n_q <= kMultiAppendMax && !a.prefill) {  // one launch: the new tokens written, then attended
+    a.xk = xk;
+    a.xv = xv;
+    a.x_dtype = x_dtype;
+    return hip_status(launch_decode_fused(a, compute_units(), stream));
+  }
+  // a prefill chunk or more than 8 positions: the append kernels, then the attention (one
+  // common position for the chunk)
+  if (seq_lens != nullptr || ctx_len < n_q) return TQ_ERR_UNSUPPORTED;
+  const hipError_t e = n_q <= kSmallAppendMax
+                           ? launch_append_small(a.k, a.v, k->batch, xk, xv, x_dtype, ctx_len - n_q, n_q, stream)
+                           : launch_quantize_kv(a.k, a.v, k->batch, xk, xv, x_dtype, ctx_len - n_q, n_q, stream);
+  if (e != hipSuccess) return TQ_ERR_HIP;
+  return hip_status(launch_decode_fused(a, compute_units(), stream));
 }
 
 int tq_paged_quantize_append_kv(const tq_paged_cache *k, const tq_paged_cache *v, const void *xk,

@@ -197,11 +197,12 @@ struct NewToken {
   uint32_t vword;   // value cache: the group word that lane's coordinates go into
 };
 
-// b: the sequence (input row); pb, pt: the plane (sequence, or pool page) and the position in it
+// b: the sequence; j: the token among the sequence's nt new tokens (input [batch][nt][kv heads][d]);
+// pb, pt: the plane (sequence, or pool page) and the position in it
 __device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key, int b, int kvh, int pb, int pt,
-                                                   int lane) {
+                                                   int lane, int j = 0, int nt = 1) {
   const void *x = key ? a.xk : a.xv;
-  const size_t xi = ((size_t)b * a.n_kv_heads + kvh) * kD + 2 * lane;
+  const size_t xi = (((size_t)b * nt + j) * a.n_kv_heads + kvh) * kD + 2 * lane;
   NewToken n{0u, 0u, 0u};
   if (a.x_dtype == TQ_F32) {
     const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(x) + xi);
@@ -214,9 +215,12 @@ __device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key
   return n;
 }
 
+// vatomic (values, several new tokens of one group from different waves): the token's two
+// 2-bit fields of the group word are cleared and set with atomics, which commute with the other
+// tokens' (disjoint fields), instead of a store of the word loaded before.
 template <int BK>
 __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &in, int pb, int kvh, int t, int lane,
-                                uint8_t *scratch) {
+                                uint8_t *scratch, bool vatomic = false) {
   const CacheView &c = key ? a.k : a.v;
   float x0, x1;
   if (a.x_dtype == TQ_F32) {
@@ -266,8 +270,14 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
     // value group of 8 tokens: coordinate i of token p at bit 2 (8 i + p); lane l's
     // coordinates 2l and 2l+1 make up 32-bit word l of the group
     const int p = t & 7, s0 = 8 * (p >> 2) + 2 * (p & 3), s1 = s0 + 16;
-    reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256)[lane] =
-        (in.vword & ~((3u << s0) | (3u << s1))) | (c0 << s0) | (c1 << s1);
+    const uint32_t mask = (3u << s0) | (3u << s1), bits = (c0 << s0) | (c1 << s1);
+    uint32_t *word = reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256) + lane;
+    if (vatomic) {
+      atomicAnd(word, ~mask);
+      atomicOr(word, bits);
+    } else {
+      *word = (in.vword & ~mask) | bits;
+    }
   }
 }
 
@@ -301,6 +311,7 @@ template <int BK, int NH, bool SPARSE, bool MULTI, bool APPEND, bool PAGED, bool
 __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
   static_assert(NH == 4 || NH == 8, "NH heads of two rows each must fit 16 rows");
   static_assert(!PREFILL || (MULTI && !SPARSE && !APPEND && !VMASK), "prefill: dense multi-query only");
+  static_assert(!(MULTI && APPEND) || (!SPARSE && !PAGED), "several new tokens: dense, contiguous caches");
   static_assert(!PAGED || !((SPARSE && RECORDS) || (MULTI && APPEND)),
                 "paged caches: decode, its append, several query positions (prefill chunks too), Sparse V's two passes");
   static_assert(!VMASK || !(SPARSE || MULTI || APPEND), "masked value pass: single-query decode");
@@ -477,11 +488,37 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         appends = new_pb >= 0 && new_pb < a.n_pages;
       }
     }
-    const bool defer_keys = appends && new_tile == wave;
+    bool defer_keys = appends && new_tile == wave;
     NewToken ntk{0u, 0u, 0u}, ntv{0u, 0u, 0u};
-    if (appends) {
+    if (!MULTI && appends) {
       ntk = new_token_load(a, true, b, kvh, new_pb, new_pt, lane);
       ntv = new_token_load(a, false, b, kvh, new_pb, new_pt, lane);
+    }
+    // MULTI: the n_q new tokens of the sequence go to positions T - n_q .. T - 1 (those >= 0) of
+    // this split; token j goes in through wave j mod W (bit j of `mine`), so the tokens are
+    // quantized side by side.  Their value fields are set with atomics (tokens of one group
+    // touch disjoint fields of the same words); every appending wave waits for its writes before
+    // the set-up barrier, and a wave whose first tile holds a new token loads it after that
+    // barrier.  With several row groups per kv head each item writes the same bytes again.
+    constexpr int MT = MULTI && APPEND ? kMultiAppendMax : 1;
+    uint32_t mine = 0u;
+    NewToken mk[MT], mv[MT];
+    if constexpr (MULTI && APPEND) {
+      defer_keys = false;
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const int p = T - n_q + j;
+        mk[j] = mv[j] = NewToken{0u, 0u, 0u};
+        if (j < n_q && p >= 0 && p >= t_begin && p < t_end) {
+          if ((p - t_begin) / kTile == wave) defer_keys = true;
+          if (j % W == wave) {
+            mine |= 1u << j;
+            mk[j] = new_token_load(a, true, b, kvh, b, p, lane, j, n_q);
+            mv[j] = new_token_load(a, false, b, kvh, b, p, lane, j, n_q);
+          }
+        }
+      }
+      appends = mine != 0u;
     }
 
     // the small loads the setup needs go out first, then the wave's first key tile; nothing
@@ -544,8 +581,18 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     // does not use.
     if (appends) {
       uint8_t *ascr = KEYS_ONLY ? lds + 16 * 1024 + wave * 64 : lds + kWBase + wave * WSTRIDE;
-      new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, ascr);
-      new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, ascr);
+      if constexpr (MULTI && APPEND) {
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          if (!((mine >> j) & 1u)) continue;
+          const int p = T - n_q + j;
+          new_token_store<BK>(a, true, mk[j], b, kvh, p, lane, ascr);
+          new_token_store<BK>(a, false, mv[j], b, kvh, p, lane, ascr, true);
+        }
+      } else {
+        new_token_store<BK>(a, true, ntk, new_pb, kvh, new_pt, lane, ascr);
+        new_token_store<BK>(a, false, ntv, new_pb, kvh, new_pt, lane, ascr);
+      }
     }
     // Sparse V: candidate count of each second-pass split this split covers (LDS atomics;
     // the value-table region is free in that mode)
@@ -627,8 +674,12 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
         }
       }
     }
+    // MULTI: every appending wave's writes are complete before the barrier (vmcnt(0) covers the
+    // wave's own stores and atomics); the deferred tile is loaded after it
+    if (MULTI && APPEND && appends) __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (appends) {
+    if (appends || defer_keys) {  // (MULTI: the tokens of a deferred tile may come from other waves,
+                                  // all written before the barrier above)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the new token's stores are complete
       if (defer_keys) load_keys(wave);
     }
@@ -1425,6 +1476,10 @@ hipError_t launch_nh(const DecodeArgs &a, int grid, hipStream_t stream) {
 template <int BK, bool SPARSE>
 hipError_t launch_bk(const DecodeArgs &a, int grid, hipStream_t stream) {
   if (!SPARSE && a.prefill) return launch_nh<BK, false, true, false, false, false, true, true>(a, grid, stream);
+  if (!SPARSE && (a.n_q > 1 || a.vgroups > 1) && a.xk != nullptr) {
+    if (a.n_q > kMultiAppendMax) return hipErrorInvalidValue;
+    return launch_nh<BK, false, true, true>(a, grid, stream);  // the n_q new tokens written first
+  }
   if (!SPARSE && (a.n_q > 1 || a.vgroups > 1)) return launch_nh<BK, false, true, false>(a, grid, stream);
   if (!SPARSE && a.xk != nullptr) return launch_nh<BK, false, false, true>(a, grid, stream);
   return launch_nh<BK, SPARSE, false, false>(a, grid, stream);

@@ -25,6 +25,7 @@ SplitPlan plan_fused_sparse(int batch, int n_kv_heads, int ctx_len, const SplitP
 constexpr int kMaxChunksPerSplit = 64;
 constexpr int kMaxQueryPositions = 4096;  // query positions of one multi-query call
 constexpr int kSmallAppendMax = 8;        // appends of up to this many tokens take one wave per plane
+constexpr int kMultiAppendMax = 8;        // new tokens the multi-query launch writes itself
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WorkspaceLayout {

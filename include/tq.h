@@ -321,6 +321,22 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
                          float *out, float *lse, void *workspace, size_t workspace_bytes,
                          void *hip_stream);
 
+/* Append and attend for several positions (speculative verification: the draft's tokens): the n_q
+ * new keys and values of each sequence, xk, xv [batch][n_q][n_kv_heads][d] of x_dtype, are
+ * quantized into positions T_b - n_q .. T_b - 1 (those >= 0; T_b as for tq_decode_attn_multi),
+ * then tq_decode_attn_multi runs over the result.  Up to 8 positions (outside the prefill mode)
+ * take one launch: the wave that reads a new token's tile writes it first, one store per value
+ * group word for all of its new tokens; the codes follow the same rule as the append kernels.
+ * Longer chunks take the append kernels and then the attention, which needs seq_lens == NULL
+ * and n_q <= ctx_len (TQ_ERR_UNSUPPORTED otherwise).
+ *   the other arguments as for tq_decode_attn_multi (workspace of
+ *   tq_decode_attn_multi_workspace_bytes)
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_decode_attn_multi_append(const tq_cache *k, const tq_cache *v, const void *xk, const void *xv, int x_dtype,
+                                const void *q, int q_dtype, int n_q_heads, int n_q, const int32_t *seq_lens,
+                                int ctx_len, float scale, float *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *hip_stream);
+
 /* Workspace bytes tq_decode_attn_multi needs for this problem (0 for invalid arguments). */
 size_t tq_decode_attn_multi_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int n_q,
                                             int ctx_len);

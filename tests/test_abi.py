@@ -212,6 +212,31 @@ def test_multi_query_argument_validation():
     assert _multi(k, _cache(layout=1, bits=2, n_kv_heads=1)) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_multi_query_append_argument_validation():
+    """The multi-query append-and-attend call checks the new tokens' inputs, then everything the
+    multi-query call checks, before any HIP call."""
+    k, v = _cache(layout=0), _cache(layout=1, bits=2)
+
+    def call(xk=FAKE + 0x500000, xv=FAKE + 0x580000, xdt=1, n_q=4, ctx=512, seq=None, hq=8, ws_bytes=None):
+        wsb = ws_bytes if ws_bytes is not None else (
+            tq.lib().tq_decode_attn_multi_workspace_bytes(1, hq, 2, max(n_q, 1), max(ctx, 0)) or 1)
+        return tq.lib().tq_decode_attn_multi_append(ctypes.byref(k), ctypes.byref(v), xk, xv, xdt, FAKE + 0x600000, 1,
+                                                   hq, n_q, seq, ctx, 0.088, FAKE + 0x700000, None,
+                                                   FAKE + 0x800000, wsb, None)
+
+    assert call(xk=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(xv=FAKE + 4) == tq.TQ_ERR_INVALID_ARG          # misaligned input
+    assert call(xdt=7) == tq.TQ_ERR_INVALID_ARG                # no such dtype
+    assert call(n_q=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(ctx=2048) == tq.TQ_ERR_CAPACITY
+    assert call(hq=7) == tq.TQ_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    # a prefill chunk (64 positions at 4 heads per kv head) takes the two-launch path, which needs
+    # one common length and at least n_q positions
+    assert call(n_q=64, seq=FAKE + 0x900000) == tq.TQ_ERR_UNSUPPORTED
+    assert call(n_q=64, ctx=32) == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_append_decode_argument_validation():
     k, v = _cache(layout=0), _cache(layout=1, bits=2)
 

@@ -711,6 +711,78 @@ def test_multi_query_matches_oracle(case, signs, golden_codebooks):
     _multi_case(inputs.WORKLOADS[name], signs, golden_codebooks, *shape)
 
 
+@pytest.mark.parametrize("case", [
+    # (workload, batch, hq, hkv, ctx, cap, bits_k, n_q, seq_lens)
+    ("llama8k", 2, 32, 8, 1000, 1024, 4, 4, None),     # 16 rows per kv head: two work items
+    ("llama8k", 1, 32, 8, 1026, 1088, 4, 4, None),     # new tokens on both sides of a tile edge
+    ("llama8k", 1, 32, 8, 1004, 1024, 4, 8, None),     # 8 tokens over two value groups of one tile
+    ("batch32k", 2, 8, 2, 1300, 1344, 3, 5, None),     # 3-bit rows
+    ("ctx131k", 2, 16, 2, 1500, 1536, 4, 3, None),     # 8-head groups
+    ("llama8k", 4, 8, 2, 900, 960, 4, 4, [900, 863, 3, 0]),   # ragged: a short and an empty sequence
+    ("llama8k", 1, 8, 2, 700, 704, 4, 64, None),       # a prefill chunk: append kernel, then attention
+])
+def test_multi_query_append_equals_append_then_attend(case, signs, golden_codebooks):
+    """tq_decode_attn_multi_append writes each sequence's n_q new tokens at T_b - n_q .. T_b - 1
+    (those >= 0) and attends: the caches must hold exactly the bytes of the append kernels at
+    those positions (every other byte unchanged) and the outputs and LSE must equal
+    tq_decode_attn_multi on them (itself checked against the oracle above)."""
+    name, batch, hq, hkv, ctx, cap, bk, n_q, seq_lens = case
+    _say("multi-query append", case)
+    w = inputs.WORKLOADS[name]
+    g = inputs.generate(w, device="cpu", batch=batch, ctx=ctx, n_kv_heads=hkv, n_q_heads=hq, n_q=n_q)
+    lens = [ctx] * batch if seq_lens is None else list(seq_lens)
+    k_new = torch.zeros((batch, n_q, hkv, 128), dtype=g["k"].dtype)
+    v_new = torch.zeros((batch, n_q, hkv, 128), dtype=g["v"].dtype)
+    for b, tb in enumerate(lens):
+        for j in range(n_q):
+            p = tb - n_q + j
+            if p >= 0:
+                k_new[b, j], v_new[b, j] = g["k"][b, p], g["v"][b, p]
+    k_new, v_new = k_new.to(DEV).contiguous(), v_new.to(DEV).contiguous()
+    scale = 1.0 / math.sqrt(128)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    q = g["q"].to(DEV).contiguous()
+
+    def filled(bsz, kx, vx):
+        kc = _new_cache(bsz, hkv, cap, bk, 0, signs)
+        vc = _new_cache(bsz, hkv, cap, 2, 1, signs)
+        _fill(kc, (kx * -0.5).to(DEV))  # stale contents at the positions to be written
+        _fill(vc, (vx * 1.5).to(DEV))
+        _fill(kc, kx[:, : ctx - n_q].to(DEV).contiguous())
+        _fill(vc, vx[:, : ctx - n_q].to(DEV).contiguous())
+        return kc, vc
+
+    ka, va = filled(batch, g["k"], g["v"])
+    got = tq.decode_attn_multi_append(ka, va, k_new, v_new, q, ctx, scale, seq_lens=sl)
+    torch.cuda.synchronize()
+    # reference caches: each sequence's tokens through the append kernels into a cache of its own
+    kb, vb = filled(batch, g["k"], g["v"])
+    for b, tb in enumerate(lens):
+        j0 = max(0, n_q - tb)
+        if tb == 0 or j0 >= n_q:
+            continue
+        k1, v1 = filled(1, g["k"][b:b + 1], g["v"][b:b + 1])
+        tq.quantize_append_kv(k1, v1, k_new[b:b + 1, j0:].contiguous(), v_new[b:b + 1, j0:].contiguous(),
+                              tb - n_q + j0)
+        torch.cuda.synchronize()
+        for h in range(hkv):
+            for big, one in ((kb, k1), (vb, v1)):
+                big.plane_codes(b, h).copy_(one.plane_codes(0, h))
+                big.plane_norms(b, h).copy_(one.plane_norms(0, h))
+    ref = tq.decode_attn_multi(kb, vb, q, ctx, scale, seq_lens=sl)
+    torch.cuda.synchronize()
+    for what, x, y in (("key codes", ka.codes, kb.codes), ("key norms", ka.norms, kb.norms),
+                       ("value codes", va.codes, vb.codes), ("value norms", va.norms, vb.norms)):
+        assert torch.equal(x, y), what
+    d_out = (got.out - ref.out).abs().max().item()
+    fin = torch.isfinite(ref.lse)
+    assert torch.equal(torch.isfinite(got.lse), fin)
+    d_lse = (got.lse[fin] - ref.lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
+    _say(f"  max |out diff| {d_out:.2e}, max |lse diff| {d_lse:.2e}")
+    assert d_out <= 1e-6 * max(ref.out.abs().max().item(), 1e-30)
+    assert d_lse <= 1e-6 * max(1.0, ref.lse[fin].abs().max().item() if bool(fin.any()) else 1.0)
+
+
 def test_multi_query_ragged_lengths_and_dtypes(signs, golden_codebooks):
     """Per-sequence lengths, including one shorter than the number of query positions (its
     first queries see nothing: o = 0, LSE = -inf) and an empty one; fp32 and fp16 queries."""
