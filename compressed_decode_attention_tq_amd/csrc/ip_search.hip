@@ -28,6 +28,7 @@ namespace {
 
 typedef _Float16 half8s __attribute__((ext_vector_type(8)));
 typedef float floatx4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreWaves = 8;
 constexpr int kBlockTokens = kSearchBlock;  // database vectors per score workgroup (scores kept in LDS)
@@ -202,11 +203,14 @@ __global__ __launch_bounds__(64 * kScoreWaves) void ip_score_kernel(CacheView db
     if (live) {
       const uint8_t *src = plane + (size_t)t * KROW + quarter * (4 * BK);
       if (BK == 4) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(src);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        // each code word is read once: streaming (nt) loads, 1% faster on a 1M-vector scan
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
       } else {
         const uint32_t *p = reinterpret_cast<const uint32_t *>(src);
-        w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
+        w[0] = __builtin_nontemporal_load(p);
+        w[1] = __builtin_nontemporal_load(p + 1);
+        w[2] = __builtin_nontemporal_load(p + 2);
       }
       nrm = f16s(norms[t]);
     }
