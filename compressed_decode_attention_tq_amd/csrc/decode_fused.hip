@@ -220,8 +220,11 @@ __device__ __forceinline__ NewToken new_token_load(const DecodeArgs &a, bool key
 }
 
 // vatomic (values, several new tokens of one group from different waves): the token's two
-// 2-bit fields of the group word are cleared and set with atomics, which commute with the other
-// tokens' (disjoint fields), instead of a store of the word loaded before.
+// 2-bit fields of the group word are replaced with compare-and-swap, which keeps the other
+// tokens' fields (disjoint, possibly written meanwhile) instead of storing the word loaded
+// before.  Each swap writes the word with the token's fields already final: the work items of
+// other row groups append the same tokens into the same words while this one may read them, so
+// a field must never pass through a cleared state (an and-then-or pair would expose one).
 template <int BK>
 __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &in, int pb, int kvh, int t, int lane,
                                 uint8_t *scratch, bool vatomic = false) {
@@ -277,8 +280,14 @@ __device__ void new_token_store(const DecodeArgs &a, bool key, const NewToken &i
     const uint32_t mask = (3u << s0) | (3u << s1), bits = (c0 << s0) | (c1 << s1);
     uint32_t *word = reinterpret_cast<uint32_t *>(plane + (size_t)(t >> 3) * 256) + lane;
     if (vatomic) {
-      atomicAnd(word, ~mask);
-      atomicOr(word, bits);
+      // each failed swap means another writer's swap succeeded, and every writer swaps once:
+      // the loop ends after at most as many rounds as there are writers of the word
+      uint32_t old = in.vword;
+      for (;;) {
+        const uint32_t seen = atomicCAS(word, old, (old & ~mask) | bits);
+        if (seen == old) break;
+        old = seen;
+      }
     } else {
       *word = (in.vword & ~mask) | bits;
     }
@@ -500,10 +509,11 @@ __device__ __forceinline__ void decode_fused_body(const DecodeArgs &a) {
     }
     // MULTI: the n_q new tokens of the sequence go to positions T - n_q .. T - 1 (those >= 0) of
     // this split; token j goes in through wave j mod W (bit j of `mine`), so the tokens are
-    // quantized side by side.  Their value fields are set with atomics (tokens of one group
-    // touch disjoint fields of the same words); every appending wave waits for its writes before
-    // the set-up barrier, and a wave whose first tile holds a new token loads it after that
-    // barrier.  With several row groups per kv head each item writes the same bytes again.
+    // quantized side by side.  Their value fields are set with compare-and-swap (tokens of one
+    // group touch disjoint fields of the same words); every appending wave waits for its writes
+    // before the set-up barrier, and a wave whose first tile holds a new token loads it after
+    // that barrier.  With several row groups per kv head each item writes the same bytes again,
+    // every write already final, so a reader sees the same bytes whichever write it follows.
     constexpr int MT = MULTI && APPEND ? kMultiAppendMax : 1;
     uint32_t mine = 0u;
     NewToken mk[MT], mv[MT];
