@@ -325,10 +325,12 @@ int tq_decode_attn_multi(const tq_cache *k, const tq_cache *v, const void *q, in
  * new keys and values of each sequence, xk, xv [batch][n_q][n_kv_heads][d] of x_dtype, are
  * quantized into positions T_b - n_q .. T_b - 1 (those >= 0; T_b as for tq_decode_attn_multi),
  * then tq_decode_attn_multi runs over the result.  Up to 8 positions (outside the prefill mode)
- * take one launch: the wave that reads a new token's tile writes it first, one store per value
- * group word for all of its new tokens; the codes follow the same rule as the append kernels.
- * Longer chunks take the append kernels and then the attention, which needs seq_lens == NULL
- * and n_q <= ctx_len (TQ_ERR_UNSUPPORTED otherwise).
+ * take one launch: in every work item whose split holds new tokens, they are quantized side by
+ * side (token j by wave j mod the item's wave count), key rows and norms stored whole and each
+ * token's value fields replaced by compare-and-swap, all before the item reads its tiles; the
+ * codes follow the same rule as the append kernels.  Longer chunks take the append kernels and
+ * then the attention, which needs seq_lens == NULL and n_q <= ctx_len (TQ_ERR_UNSUPPORTED
+ * otherwise).  The caches are written in place: calls that overlap on the same caches race.
  *   the other arguments as for tq_decode_attn_multi (workspace of
  *   tq_decode_attn_multi_workspace_bytes)
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
